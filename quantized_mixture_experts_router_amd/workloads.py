@@ -1,0 +1,133 @@
+"""Seeded synthetic QMoE workloads.
+
+This module only draws random inputs; it contains none of the operator's
+arithmetic (no routing, no dequantisation, no matmul).  Both the HIP path and
+the CPU oracle consume the same host arrays it returns.
+
+Shapes follow the QMoE WebGPU manifest (page "com.microsoft.QMoE manifest",
+``inputs``): input (T, H) or (B, S, H) float32; router_probs (T, E) float32;
+fc1_experts_weights (E, fusion*I, H/pack) uint8; fc1_scales (E, fusion*I) or
+(E, fusion*I, H/bs) float32; fc2_experts_weights (E, H, I/pack) uint8;
+fc2_scales (E, H) or (E, H, I/bs) float32, with pack = 2 for 4-bit codes and
+fusion = 2 for interleaved SwiGLU.
+
+Draw order (fixed, one ``numpy.random.default_rng(seed)`` per workload):
+input ~ N(0, 1); router logits ~ N(0, sigma) (plus the Zipf bias
+-2*ln(rank) with rank = e + 1 where requested); fc1 bytes U{0..255};
+fc1 scales U[a, b]; fc2 bytes U{0..255}; fc2 scales U[a, b].  Uniform bytes
+are uniform 4-bit nibbles as well, so one recipe serves both widths.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, asdict
+from typing import Optional, Tuple
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    input_shape: Tuple[int, ...]   # (T, H) or (B, S, H)
+    experts: int
+    inter: int
+    k: int
+    bits: int
+    block_size: int                # 0 = column-wise scales
+    activation: str                # "relu" | "swiglu"
+    scale_range: Tuple[float, float]
+    logit_sigma: float = 1.0
+    zipf_bias: bool = False
+    seed: int = 0
+    alpha: float = 1.0
+    beta: float = 0.0
+
+    @property
+    def hidden(self) -> int:
+        return self.input_shape[-1]
+
+    @property
+    def tokens(self) -> int:
+        t = 1
+        for d in self.input_shape[:-1]:
+            t *= d
+        return t
+
+    @property
+    def fusion(self) -> int:
+        return 2 if self.activation == "swiglu" else 1
+
+    @property
+    def pack(self) -> int:
+        return 2 if self.bits == 4 else 1
+
+    def attrs(self) -> dict:
+        return dict(k=self.k, expert_weight_bits=self.bits, block_size=self.block_size,
+                    activation_type=self.activation,
+                    swiglu_fusion=1 if self.activation == "swiglu" else 0,
+                    activation_alpha=self.alpha, activation_beta=self.beta,
+                    normalize_routing_weights=0, routing="qmoe")
+
+    def describe(self) -> dict:
+        d = asdict(self)
+        d["tokens"] = self.tokens
+        return d
+
+
+# The five measured workloads: a tiny ReLU int8 case, a Mixtral-like int4
+# decode step, the same experts at prefill length, a fine-grained 64-expert
+# layer with Zipf-skewed routing, and a 128-expert int8 layer.
+WORKLOADS = {
+    "tiny": Workload("tiny", (8, 64), 4, 128, 1, 8, 0, "relu", (0.005, 0.02)),
+    "decode": Workload("decode", (16, 4096), 8, 14336, 2, 4, 64, "swiglu", (0.002, 0.01)),
+    "prefill": Workload("prefill", (2, 2048, 4096), 8, 14336, 2, 4, 128, "swiglu", (0.002, 0.01)),
+    "fine": Workload("fine", (2048, 2048), 64, 1408, 6, 4, 32, "swiglu", (0.002, 0.01),
+                     zipf_bias=True),
+    "large_e": Workload("large_e", (4, 2048, 4096), 128, 1536, 8, 8, 0, "swiglu",
+                        (0.001, 0.005), logit_sigma=1.5),
+}
+
+
+def shapes(w: Workload) -> dict:
+    T, H, E, I = w.tokens, w.hidden, w.experts, w.inter
+    F = w.fusion * I
+    d = {
+        "input": tuple(w.input_shape),
+        "router_probs": (T, E),
+        "fc1_experts_weights": (E, F, H // w.pack),
+        "fc2_experts_weights": (E, H, I // w.pack),
+    }
+    if w.block_size:
+        d["fc1_scales"] = (E, F, H // w.block_size)
+        d["fc2_scales"] = (E, H, I // w.block_size)
+    else:
+        d["fc1_scales"] = (E, F)
+        d["fc2_scales"] = (E, H)
+    return d
+
+
+def generate(w: Workload, seed: Optional[int] = None) -> dict:
+    """Draw every input of workload ``w`` in the fixed order documented above."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    s = shapes(w)
+    a, b = w.scale_range
+    x = rng.standard_normal(s["input"], dtype=np.float32)
+    logits = (rng.standard_normal(s["router_probs"], dtype=np.float64) * w.logit_sigma)
+    if w.zipf_bias:
+        rank = np.arange(1, w.experts + 1, dtype=np.float64)
+        logits = logits + (-2.0 * np.log(rank))[None, :]
+    logits = logits.astype(np.float32)
+    fc1 = rng.integers(0, 256, size=s["fc1_experts_weights"], dtype=np.uint8)
+    fc1_s = rng.uniform(a, b, size=s["fc1_scales"]).astype(np.float32)
+    fc2 = rng.integers(0, 256, size=s["fc2_experts_weights"], dtype=np.uint8)
+    fc2_s = rng.uniform(a, b, size=s["fc2_scales"]).astype(np.float32)
+    return {"input": x, "router_probs": logits, "fc1_experts_weights": fc1,
+            "fc1_scales": fc1_s, "fc2_experts_weights": fc2, "fc2_scales": fc2_s}
+
+
+def random_case(rng: np.random.Generator, *, tokens_shape, hidden, experts, inter, k, bits,
+                block_size, activation, scale_range=(0.005, 0.02), logit_sigma=1.0) -> tuple:
+    """A small random case for sweeps; returns (Workload, arrays)."""
+    w = Workload("sweep", tuple(tokens_shape) + (hidden,), experts, inter, k, bits, block_size,
+                 activation, scale_range, logit_sigma=logit_sigma)
+    return w, generate(w, seed=int(rng.integers(0, 2**31 - 1)))
