@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""QMoE layer benchmark on one AMD Instinct MI355X (gfx950).
+
+One step = one full qmoe_forward (router, permutation, operand prep, FC1 +
+activation, FC2, combine) over one batch of seeded synthetic input already
+resident in HBM.  Default workload: the Mixtral-like int4 decode layer
+(16 tokens x hidden 4096, 8 experts, inter 14336, k = 2, interleaved SwiGLU,
+block size 64).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+The roofline object describes the dominant kernel (FC1 or FC2, whichever is
+slower), timed with HIP events recorded on the launch stream around that
+kernel over K further steps; its algorithmic bytes and FLOPs are counted from
+the shapes (packed weights and scales of the experts that receive a slot,
+activations in and out).  The CPU baseline times the float64 oracle on the
+host cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+F16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense f16 matrix peak, TFLOP/s
+METRIC = "QMoE layer tokens/s + achieved HBM GB/s vs peak (int4 decode & prefill)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stage-timing", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_work(w, counts):
+    """Algorithmic bytes and FLOPs of the FC1 and FC2 kernels for one call."""
+    import numpy as np
+    used = int(np.count_nonzero(counts))
+    T, H, E, I, k = w.tokens, w.hidden, w.experts, w.inter, w.k
+    S = T * k
+    F = w.fusion * I
+    nb1 = H // w.block_size if w.block_size else 1
+    nb2 = I // w.block_size if w.block_size else 1
+    w1 = used * (F * H // w.pack + F * nb1 * 4)
+    w2 = used * (H * I // w.pack + H * nb2 * 4)
+    fc1 = dict(bytes=w1 + T * H * 4 + S * I * 4, flops=2.0 * S * F * H, weight_bytes=w1, used_experts=used)
+    fc2 = dict(bytes=w2 + S * I * 4 + S * H * 4, flops=2.0 * S * H * I, weight_bytes=w2, used_experts=used)
+    return fc1, fc2
+
+
+def roofline_for(work, ms):
+    intensity = work["flops"] / work["bytes"]
+    ridge = F16_DENSE_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        ach = work["bytes"] / (ms * 1e-3) / 1e9
+        return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4))
+    ach = work["flops"] / (ms * 1e-3) / 1e12
+    return dict(bound="mfma", achieved=round(ach, 1), peak=F16_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=round(ach / F16_DENSE_PEAK_TFLOPS, 4))
+
+
+def stage_times(qm, call_debug, steps):
+    """Average per-stage durations (ms) from HIP events recorded by the library."""
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    evs = []
+    for _ in range(5):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e)
+    sums = [0.0] * 4
+    for _ in range(steps):
+        call_debug([e.value for e in evs])
+        assert hip.hipEventSynchronize(evs[4]) == 0
+        for i in range(4):
+            ms = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[i], evs[i + 1]) == 0
+            sums[i] += ms.value
+    for e in evs:
+        hip.hipEventDestroy(e)
+    return dict(zip(("routing", "fc1", "fc2", "combine"), [s / steps for s in sums]))
+
+
+def cpu_baseline(w, arrs):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: numpy runs single threaded loops
+        threads = 1
+    attrs = w.attrs()
+    if w.tokens <= 16:
+        ids = list(range(w.tokens))
+        sample = f"all {w.tokens} tokens of the workload (every used expert dequantised once)"
+    else:
+        ids = list(range(4))
+        sample = "first 4 tokens of the workload (oracle.qmoe_tokens: their experts dequantised once)"
+    t0 = time.perf_counter()
+    oracle.qmoe_tokens(ids, *arrs.values(), attrs=attrs)
+    dt = time.perf_counter() - t0
+    return dict(value=round(len(ids) / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=sample, seconds=round(dt, 2))
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the kernel source now in the tree; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    ent = rec.get(kernel_key)
+    if not ent:
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gemm.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return ent.get("bytes") if ent.get("gemm_sha") == h else None
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every run here uses a single MI355X); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import quantized_mixture_experts_router_amd as qm
+    from quantized_mixture_experts_router_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    arrs = W.generate(w)
+    torch.cuda.set_device(0)
+    d = {k: torch.from_numpy(v).cuda() for k, v in arrs.items()}
+    ins = [d[k] for k in ("input", "router_probs", "fc1_experts_weights", "fc1_scales", "fc2_experts_weights",
+                          "fc2_scales")]
+    attrs = qm.make_attrs(w.attrs())
+    out = torch.empty_like(d["input"])
+    need = qm.qmoe_workspace_size(*ins, attrs)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        qm.qmoe_forward(*ins, attrs, out, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = w.tokens * args.steps / elapsed
+
+    # routing counts (for the algorithmic work of the used experts)
+    counts_t = torch.empty(w.experts, dtype=torch.int32, device="cuda")
+    qm.qmoe_forward(*ins, attrs, out, ws, stream, debug={"counts": counts_t})
+    torch.cuda.synchronize()
+    counts = counts_t.cpu().numpy()
+    fc1_work, fc2_work = kernel_work(w, counts)
+
+    roofline = None
+    stages = None
+    if not args.no_stage_timing:
+        def call_debug(events):
+            qm.qmoe_forward(*ins, attrs, out, ws, stream, debug={"events": events})
+        stages = stage_times(qm, call_debug, args.steps)
+        key = "fc1" if stages["fc1"] >= stages["fc2"] else "fc2"
+        work = fc1_work if key == "fc1" else fc2_work
+        roofline = roofline_for(work, stages[key])
+        roofline["kernel"] = f"qmoe_gemm ({key.upper()}, {'SwiGLU' if w.activation == 'swiglu' else 'ReLU'} "\
+                             f"epilogue)" if key == "fc1" else "qmoe_gemm (FC2, slot-row store)"
+        roofline["avg_ms"] = round(stages[key], 5)
+        roofline["algorithmic_bytes"] = int(work["bytes"])
+        roofline["algorithmic_flops"] = work["flops"]
+        roofline["traffic"] = traffic_for(f"{args.workload}:{key}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, arrs)
+
+    total_bytes = fc1_work["bytes"] + fc2_work["bytes"]
+    total_flops = fc1_work["flops"] + fc2_work["flops"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 operands (fp32 activations as hi+lo f16), fp32 accumulate",
+        "data": "synthetic (seeded numpy draws per workload recipe; weights random uint8)",
+        "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden, "experts": w.experts,
+                   "inter": w.inter, "k": w.k, "bits": w.bits, "block_size": w.block_size,
+                   "activation": w.activation, "input_shape": list(w.input_shape)},
+        "layer_hbm_gbs": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "layer_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "stage_ms": {k: round(v, 5) for k, v in stages.items()} if stages else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * qmoe.h -- C ABI of the QMoE routed expert FFN for AMD Instinct gfx950.
+ *
+ * The operator (QMoE WebGPU manifest: description, inputs, outputs,
+ * attributes) takes float32 token activations x [T, H] (or [B, S, H]),
+ * float32 router logits [T, E], raw uint8-packed FC1/FC2 expert weights with
+ * float32 scales, and returns float32 output of x's shape:
+ *
+ *   sel[t]    = indices of the k largest logits of row t, largest first,
+ *               equal logits ordered by ascending expert index
+ *   w[t, s]   = softmax over the k selected logits           (QMoE routing)
+ *             | softmax over all E logits taken at sel[t, s],
+ *               renormalised iff normalize_routing_weights   (MoE routing)
+ *   W[e]      = (q - mid) * scale, mid = 8 (4-bit) / 128 (8-bit);
+ *               4-bit bytes hold the even code in the low nibble
+ *   h         = x[t] . W1[e]^T                (FC1, rows = fusion * I)
+ *   a         = relu(h)  |  g * sigmoid(alpha * g) * (u + beta),
+ *               g = h[2j], u = h[2j+1]        (interleaved SwiGLU)
+ *   out[t]    = sum_s w[t, s] * (a . W2[sel[t, s]]^T)
+ *
+ * FC1 and FC2 are each a GroupedMatMul (ONNX GroupedMatMul-29, Summary) over
+ * dequantised weights.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are described by qmoe_tensor: a pointer, a dtype code, a rank and
+ *    up to three dims, row-major and contiguous.  For qmoe_validate and
+ *    qmoe_workspace_size the pointers are not dereferenced; for qmoe_forward
+ *    they are DEVICE pointers on the current HIP device.
+ *  - The caller owns every buffer.  The library allocates nothing, never
+ *    synchronises, and enqueues all work on the caller's stream.
+ *  - A non-OK status means nothing was enqueued and the output is untouched.
+ *    On QMOE_OK every output element is written by work enqueued on stream.
+ *  - Inputs that are finite are in contract; NaN/inf in x or logits, and
+ *    |x| or |activation| at or above 65504 (the f16 range used by the matrix
+ *    cores), are out of contract and produce unspecified (but bounded-time)
+ *    results.
+ *  - Entry points hold no global mutable state; calls on different streams
+ *    with different workspaces may overlap.
+ */
+#ifndef QMOE_H_
+#define QMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMOE_ABI_VERSION 1
+
+typedef enum {
+  QMOE_OK = 0,
+  QMOE_ERR_NULL = 1,        /* a required pointer argument is NULL            */
+  QMOE_ERR_SHAPE = 2,       /* ranks/dims violate the manifest's shape rules  */
+  QMOE_ERR_ATTR = 3,        /* attribute value outside the accepted set       */
+  QMOE_ERR_UNSUPPORTED = 4, /* standard value this library does not implement */
+  QMOE_ERR_WORKSPACE = 5,   /* workspace smaller than qmoe_workspace_size     */
+  QMOE_ERR_HIP = 6,         /* a HIP launch or device query failed            */
+  QMOE_ERR_DTYPE = 7,       /* tensor dtype code differs from the contract    */
+  QMOE_ERR_ALIGN = 8        /* a device pointer is not 16-byte aligned        */
+} qmoe_status;
+
+typedef enum { QMOE_F32 = 1, QMOE_U8 = 2 } qmoe_dtype;
+
+typedef enum { QMOE_ACT_RELU = 0, QMOE_ACT_SWIGLU = 1 } qmoe_activation;
+
+typedef enum {
+  QMOE_ROUTE_QMOE = 0, /* softmax over the k selected logits (QMoE manifest)      */
+  QMOE_ROUTE_MOE = 1   /* softmax over all logits before top-k (float MoE README) */
+} qmoe_routing;
+
+typedef struct {
+  const void* data;  /* device pointer for qmoe_forward; unused by validation */
+  int32_t dtype;     /* qmoe_dtype */
+  int32_t rank;      /* 1..3 */
+  int64_t dims[3];   /* row-major extents; dims[i] for i >= rank are ignored */
+} qmoe_tensor;
+
+/* Attributes of the QMoE manifest (key "attributes"), defaults in brackets. */
+typedef struct {
+  int32_t k;                         /* [1]  experts per token, 1 <= k <= E      */
+  int32_t expert_weight_bits;        /* [4]  4 or 8                               */
+  int32_t block_size;                /* [0]  0 = column-wise scales; else a power
+                                             of two >= 16 dividing H and I        */
+  int32_t activation_type;           /* [RELU] qmoe_activation                    */
+  int32_t swiglu_fusion;             /* [0]  0 with relu, 1 with swiglu; 2 is
+                                             QMOE_ERR_UNSUPPORTED                 */
+  float activation_alpha;            /* [1]  SwiGLU gate sigmoid slope            */
+  float activation_beta;             /* [0]  added to the SwiGLU linear branch    */
+  int32_t normalize_routing_weights; /* [0]  0 or 1; only the MoE routing mode
+                                             reads it                             */
+  int32_t routing;                   /* [QMOE_ROUTE_QMOE] qmoe_routing            */
+  int32_t use_sparse_mixer;          /* [0]  1 is QMOE_ERR_UNSUPPORTED            */
+  int32_t weights_prepacked;         /* [-1] -1 or 0; 1 is QMOE_ERR_UNSUPPORTED   */
+  int32_t quant_type;                /* [0]  0 = "int"; others UNSUPPORTED        */
+} qmoe_attrs;
+
+/* Stage boundaries at which qmoe_forward_debug records events. */
+#define QMOE_STAGE_EVENTS 5
+
+/* Optional outputs for parity checks and timing.  Any field may be NULL.
+ * Device buffers: topk_idx, topk_w [T*k] (row t, slot s at t*k+s); counts
+ * [E]; offsets [E+1]; perm [T*k] (slot id t*k+s at each expert-sorted
+ * position, stable within an expert).
+ * events: caller-created hipEvent_t handles recorded on the stream at
+ *   [0] before the router, [1] after the routing front end (router,
+ *   permutation, operand preparation), [2] after FC1, [3] after FC2,
+ *   [4] after the combine (before any debug copy).  Events are only recorded
+ *   when T > 0 and I > 0. */
+typedef struct {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  void* events[QMOE_STAGE_EVENTS];
+} qmoe_debug;
+
+/* Library ABI version (QMOE_ABI_VERSION of the build). */
+int32_t qmoe_abi_version(void);
+
+/* Fill *a with the manifest defaults listed above.  a must not be NULL. */
+void qmoe_attrs_default(qmoe_attrs* a);
+
+/* Check shapes, dtypes and attributes against the manifest's derive rules
+ * (quantContract: activationSupported, routingModeSupported, rawWeightLayout,
+ * quantShapeOk with quantBlockSizeOk and quantScalesOk, 1 <= k <= E).  Pure
+ * host code; never touches a device.  output may describe the output tensor
+ * (must equal input's shape) or be NULL to skip that check. */
+qmoe_status qmoe_validate(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                          const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_scales,
+                          const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_scales,
+                          const qmoe_tensor* output, const qmoe_attrs* attrs);
+
+/* Bytes of device workspace qmoe_forward needs for these shapes (validates
+ * first).  *bytes receives the size; it is 0 when T == 0.  With I == 0 only
+ * the (small) routing part is needed. */
+qmoe_status qmoe_workspace_size(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                                const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_scales,
+                                const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_scales,
+                                const qmoe_attrs* attrs, size_t* bytes);
+
+/* Enqueue the whole operator on stream (a hipStream_t; NULL = the null
+ * stream).  Device pointers: input, router_probs, scales 4-byte aligned;
+ * input, weights and output 16-byte aligned (QMOE_ERR_ALIGN otherwise).
+ * workspace: device memory of at least qmoe_workspace_size bytes, 256-byte
+ * aligned, exclusively owned by this call until the stream reaches it.  The
+ * output must not alias any input. */
+qmoe_status qmoe_forward(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                         const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_scales,
+                         const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_scales,
+                         const qmoe_attrs* attrs, const qmoe_tensor* output,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* As qmoe_forward, and also copies the routing stages' results to the
+ * non-NULL device buffers of *debug (debug may be NULL). */
+qmoe_status qmoe_forward_debug(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                               const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_scales,
+                               const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_scales,
+                               const qmoe_attrs* attrs, const qmoe_tensor* output,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               const qmoe_debug* debug);
+
+/* Static, human-readable name of a status code. */
+const char* qmoe_status_string(qmoe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H_ */

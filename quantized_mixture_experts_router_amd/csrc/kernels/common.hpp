@@ -1,0 +1,105 @@
+// Device helpers shared by the QMoE kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Activation operand layout ("A rows").
+//
+// The matrix cores take f16 operands.  An fp32 activation v is carried as two
+// f16 values, hi = f16(v) and lo = f16(v - hi), so hi + lo keeps about 22
+// significant bits; each product runs twice (hi, then lo) into one fp32
+// accumulator.  Weights are exact small integers in f16, so the only rounding
+// is fp32 accumulation and the lo residual.
+//
+// A row holds Kp codes (Kp a multiple of 128, zero padded).  Codes are stored
+// in groups of 8: 16 bytes of hi halves then 16 bytes of lo halves, so one
+// 32-byte group is what a lane feeds to one matrix instruction.  Inside a
+// group of 8 the storage order follows how the weight unpacker emits codes:
+//   8-bit: natural order;
+//   4-bit: storage slot i holds logical code kPerm4[i] (pairs (0,4),(1,5),...)
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int perm4_of_slot(int i) { return (i >> 1) | ((i & 1) << 2); }
+__host__ __device__ constexpr int slot4_of_code(int c) { return ((c & 3) << 1) | (c >> 2); }
+
+template <int BITS>
+__device__ __forceinline__ int storage_of_code(int j) {
+  if constexpr (BITS == 4) return (j & ~7) | slot4_of_code(j & 7);
+  else return j;
+}
+template <int BITS>
+__device__ __forceinline__ int code_of_storage(int q) {
+  if constexpr (BITS == 4) return (q & ~7) | perm4_of_slot(q & 7);
+  else return q;
+}
+
+// Split fp32 into f16 hi + lo.
+__device__ __forceinline__ void split_f16(float v, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)v;
+  lo = (_Float16)(v - (float)hi);
+}
+
+// ---------------------------------------------------------------------------
+// Weight unpacking: raw packed bytes -> exact f16 values (q - mid).
+//
+// f16 with exponent field 25 (0x6400 = 1024.0) has unit spacing on [1024,
+// 2048), so OR-ing an integer q < 1024 into the mantissa gives exactly
+// 1024 + q; one packed f16 subtract of (1024 + mid) leaves q - mid exactly.
+// A nibble left in bits 4..7 of a half gives 1024 + 16 q, undone by a packed
+// multiply-add with 1/16 (exact: powers of two).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+
+// 8 four-bit codes of one little-endian dword (code j in bits 4j..4j+3) ->
+// f16x8 in storage order (0,4,1,5,2,6,3,7), each value q - 8.
+__device__ __forceinline__ f16x8 unpack4(uint32_t d) {
+  const f16x2 bias = {(_Float16)-1032.f, (_Float16)-1032.f};   // -(1024 + 8)
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2 bias16 = {(_Float16)-72.f, (_Float16)-72.f};     // -(64 + 8)
+  const uint32_t d8 = d >> 8;
+  f16x2 p0 = as_h2((d & 0x000F000Fu) | 0x64006400u) + bias;                    // codes 0, 4
+  f16x2 p1 = as_h2((d & 0x00F000F0u) | 0x64006400u) * sixteenth + bias16;      // codes 1, 5
+  f16x2 p2 = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + bias;                   // codes 2, 6
+  f16x2 p3 = as_h2((d8 & 0x00F000F0u) | 0x64006400u) * sixteenth + bias16;     // codes 3, 7
+  f16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// 4 eight-bit codes (byte j = code j) -> two f16x2 in natural order, q - 128.
+__device__ __forceinline__ void unpack8(uint32_t d, f16x2& a, f16x2& b) {
+  const f16x2 bias = {(_Float16)-1152.f, (_Float16)-1152.f};   // -(1024 + 128)
+  // v_perm_b32 selector bytes: 0..3 pick from src1 (d), 4..7 from src0 (0x64646464)
+  a = as_h2(__builtin_amdgcn_perm(0x64646464u, d, 0x04010400u)) + bias;  // bytes 0, 1
+  b = as_h2(__builtin_amdgcn_perm(0x64646464u, d, 0x04030402u)) + bias;  // bytes 2, 3
+}
+
+__device__ __forceinline__ f16x8 unpack8x2(uint32_t d0, uint32_t d1) {
+  f16x2 a, b, c, e;
+  unpack8(d0, a, b);
+  unpack8(d1, c, e);
+  f16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = e[0]; r[7] = e[1];
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Wave-wide helpers.
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+}  // namespace qmoe

@@ -1,0 +1,50 @@
+// Launch functions of the QMoE kernels (host side; enqueue only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+hipError_t launch_router(const float* logits, int T, int E, int k, int routing, int normalize, int* topk_idx,
+                         float* topk_w, hipStream_t st);
+
+hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchunks, int bm, int* hist,
+                          int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st);
+
+hipError_t launch_prep_a(int bits, const float* x, int T, int H, int kp, uint8_t* xa, uint8_t* act, int S, int I,
+                         int kp2, hipStream_t st);
+
+// Grouped quantised GEMM over expert-sorted rows.
+//   FC1: rows are tokens (via perm / k), weights fc1 [E][F][K/pack], output act rows.
+//   FC2: rows are act rows in sorted order, weights fc2 [E][H][I/pack], output slot rows.
+struct GemmArgs {
+  const uint8_t* wq;    // packed weights [E][N][kb]
+  const float* ws;      // scales [E][N] or [E][N][nblk]
+  const uint8_t* a;     // operand rows (f16 hi/lo groups), row stride a_stride bytes
+  const int* a_map;     // FC1: perm (sorted position -> slot); FC2: nullptr (row = position)
+  int a_div;            // FC1: k (slot -> token)
+  long a_stride;
+  const int* tiles;     // [max_tiles][4] = expert, first position, rows, 0
+  const int* ntiles;
+  int N, K, kb, nblk, bs;
+  // epilogue
+  uint8_t* act;         // FC1 output rows, stride act_stride bytes
+  long act_stride;
+  float* slot_out;      // FC2 output [S][N] by slot id
+  const int* perm;      // FC2: sorted position -> slot
+  float alpha, beta;
+};
+
+enum { EPI_RELU = 0, EPI_SWIGLU = 1, EPI_STORE = 2 };
+
+hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& g, int max_tiles, hipStream_t st);
+
+hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, float* out,
+                          hipStream_t st);
+
+hipError_t launch_fill_zero(float* out, long n, hipStream_t st);
+
+hipError_t launch_copy_i32(const int* src, int* dst, long n, hipStream_t st);
+hipError_t launch_copy_f32(const float* src, float* dst, long n, hipStream_t st);
+
+}  // namespace qmoe

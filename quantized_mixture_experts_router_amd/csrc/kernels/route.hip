@@ -1,0 +1,299 @@
+// Routing front end of the QMoE operator:
+//   qmoe_router        top-k selection and routing weights, one wavefront per token
+//   qmoe_hist          per-chunk expert histogram of the selected slots
+//   qmoe_scan          per-expert counts, exclusive offsets, chunk bases, M-tile table
+//   qmoe_scatter       stable expert-sorted slot order (perm)
+//   qmoe_prep_a        fp32 tokens -> f16 hi/lo operand rows (see common.hpp)
+//
+// Routing follows the QMoE WebGPU manifest (description: softmax over the
+// selected top-k logits; attributeDescriptions.normalize_routing_weights) and
+// the float MoE README (Description: softmax over all logits before top-k,
+// optional renormalisation).  The permutation is the manifest's group stage
+// (variants quant_grouped_routed, pass group_stage: expert-grouped slot list
+// and M-tile metadata), made stable so that it is deterministic.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.h"
+
+namespace qmoe {
+
+// Total order used for selection: larger logit first, then lower index.
+// NaN is mapped to -inf so that every token still selects k experts.
+__device__ __forceinline__ bool key_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// One wavefront per token; each lane holds logits e = lane + 64 * j.
+template <int V>
+__global__ void __launch_bounds__(256) qmoe_router(const float* __restrict__ logits, int T, int E, int k,
+                                                   int routing, int normalize, int* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  float v[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int e = lane + 64 * j;
+    float x = e < E ? row[e] : -INFINITY;
+    v[j] = (x != x) ? -INFINITY : x;
+  }
+  // k rounds: each picks the best key strictly after the previous pick.
+  float pv = INFINITY;
+  int pi = -1;
+  float my_val = 0.f;  // lane r keeps pick number r (k <= 64 * V handled below)
+  float v0 = 0.f;
+  float sum_sel = 0.f;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && key_before(pv, pi, v[j], e) && key_before(v[j], e, bv, bi)) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (key_before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    bi = min(max(bi, 0), E - 1);  // always a valid expert index
+    pv = bv;
+    pi = bi;
+    if (r == 0) v0 = bv;
+    const float ex = expf(bv - v0);  // identical in every lane
+    sum_sel += ex;
+    if (lane == 0) topk_idx[(size_t)t * k + r] = bi;
+    if (lane == (r & 63)) {
+      if (r < 64) my_val = ex;
+      else topk_w[(size_t)t * k + r] = ex;  // picks beyond 64 wait in the output buffer
+    }
+  }
+  float denom = sum_sel;
+  if (routing == 1 && !normalize) {
+    // Full softmax over all experts, taken at the selection.
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      if (lane + 64 * j < E) part += expf(v[j] - v0);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    denom = part;
+  }
+  // MoE with normalisation reduces to the selected-logit softmax.
+  if (lane < k) topk_w[(size_t)t * k + lane] = my_val / denom;
+  for (int r = 64 + lane; r < k; r += 64) {
+    const float ex = topk_w[(size_t)t * k + r];
+    topk_w[(size_t)t * k + r] = ex / denom;
+  }
+}
+
+// Histogram of selected experts over chunks of `chunk` consecutive slots.
+__global__ void __launch_bounds__(256) qmoe_hist(const int* __restrict__ topk_idx, int S, int E, int chunk,
+                                                 int* __restrict__ hist) {
+  extern __shared__ int cnt[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int s0 = blockIdx.x * chunk;
+  const int s1 = min(S, s0 + chunk);
+  for (int s = s0 + threadIdx.x; s < s1; s += blockDim.x) atomicAdd(&cnt[topk_idx[s]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Single block: counts, offsets, per-chunk bases and the M-tile table.
+// tiles[4*i .. 4*i+3] = (expert, first sorted position, rows, 0); ntiles[0] = count.
+__global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nchunks, int E, int S, int bm,
+                                                  int* __restrict__ counts, int* __restrict__ offsets,
+                                                  int* __restrict__ tiles, int* __restrict__ ntiles) {
+  __shared__ int s_cnt[1024];
+  __shared__ int s_tiles[1024];
+  __shared__ int s_warp[16];
+  __shared__ int s_warp2[16];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E) {
+    for (int ch = 0; ch < nchunks; ++ch) {
+      int* h = hist + (size_t)ch * E + e;
+      const int v = *h;
+      *h = c;  // exclusive prefix over chunks
+      c += v;
+    }
+    counts[e] = c;
+  }
+  const int nt = (c + bm - 1) / bm;
+  // Block-wide inclusive scans of counts and tile counts (wave scan, then wave totals).
+  int inc = c, inct = nt;
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int a = __shfl_up(inc, off);
+    const int b = __shfl_up(inct, off);
+    if (lane >= off) {
+      inc += a;
+      inct += b;
+    }
+  }
+  if (lane == 63) {
+    s_warp[w] = inc;
+    s_warp2[w] = inct;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0, b = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int x = s_warp[i], y = s_warp2[i];
+      s_warp[i] = a;
+      s_warp2[i] = b;
+      a += x;
+      b += y;
+    }
+  }
+  __syncthreads();
+  const int off_e = inc - c + s_warp[w];
+  const int tile0 = inct - nt + s_warp2[w];
+  if (e < E) {
+    s_cnt[e] = off_e;
+    s_tiles[e] = tile0;
+    offsets[e] = off_e;
+    for (int ch = 0; ch < nchunks; ++ch) hist[(size_t)ch * E + e] += off_e;
+    for (int i = 0; i < nt; ++i) {
+      int* tp = tiles + 4 * (tile0 + i);
+      tp[0] = e;
+      tp[1] = off_e + i * bm;
+      tp[2] = min(bm, c - i * bm);
+      tp[3] = 0;
+    }
+  }
+  if (e == E - 1) {
+    offsets[E] = S;
+    ntiles[0] = tile0 + nt;
+  }
+}
+
+// Stable scatter: slot s (expert e) goes to base[chunk][e] + (number of slots
+// of the same chunk with expert e and a smaller slot id).
+__global__ void __launch_bounds__(256) qmoe_scatter(const int* __restrict__ topk_idx, const int* __restrict__ hist,
+                                                    int S, int E, int chunk, int* __restrict__ perm) {
+  extern __shared__ int sm[];
+  int* base = sm;          // [E]
+  int* wcnt = sm + E;      // [4][E]
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += 256) base[e] = hist[(size_t)blockIdx.x * E + e];
+  const int s0 = blockIdx.x * chunk;
+  const int s1 = min(S, s0 + chunk);
+  for (int r0 = s0; r0 < s1; r0 += 256) {
+    for (int i = threadIdx.x; i < 4 * E; i += 256) wcnt[i] = 0;
+    __syncthreads();
+    const int s = r0 + threadIdx.x;
+    const bool valid = s < s1;
+    const int e = valid ? topk_idx[s] : -1;
+    // rank among lower lanes of this wave with the same expert
+    unsigned long long todo = __ballot(valid);
+    int rank = 0;
+    while (todo) {
+      const int leader = __ffsll((long long)todo) - 1;
+      const int le = __shfl(e, leader);
+      const unsigned long long m = __ballot(valid && e == le);
+      if (e == le) rank = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == leader) wcnt[w * E + le] = __popcll(m);
+      todo &= ~m;
+    }
+    __syncthreads();
+    if (valid) {
+      int pos = base[e] + rank;
+      for (int ww = 0; ww < w; ++ww) pos += wcnt[ww * E + e];
+      perm[pos] = s;
+    }
+    __syncthreads();
+    for (int ee = threadIdx.x; ee < E; ee += 256)
+      base[ee] += wcnt[ee] + wcnt[E + ee] + wcnt[2 * E + ee] + wcnt[3 * E + ee];
+    __syncthreads();
+  }
+}
+
+// fp32 token rows -> f16 hi/lo operand rows (storage order of common.hpp),
+// zero padded to kp codes.  One thread per group of 8 codes.  When act_pad is
+// given, also zero the padding columns [I, kp2) of every act row.
+template <int BITS>
+__global__ void __launch_bounds__(256) qmoe_prep_a(const float* __restrict__ x, int T, int H, int kp,
+                                                   uint8_t* __restrict__ xa, uint8_t* __restrict__ act,
+                                                   int S, int I, int kp2) {
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long groups = (long)T * (kp / 8);
+  if (gid < groups) {
+    const int t = gid / (kp / 8);
+    const int g = gid % (kp / 8);
+    f16x8 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = code_of_storage<BITS>(g * 8 + i);
+      const float v = c < H ? x[(size_t)t * H + c] : 0.f;
+      _Float16 h, l;
+      split_f16(v, h, l);
+      hi[i] = h;
+      lo[i] = l;
+    }
+    uint8_t* dst = xa + (size_t)t * kp * 4 + (size_t)g * 32;
+    *(f16x8*)dst = hi;
+    *(f16x8*)(dst + 16) = lo;
+  }
+  if (act != nullptr) {
+    // padding groups of act rows: storage groups covering codes >= I
+    const int g0 = I / 8;  // first group that may hold codes >= I
+    const int pg = kp2 / 8 - g0;
+    const long pid = gid - groups;
+    if (pid >= 0 && pid < (long)S * pg) {
+      const int p = pid / pg;
+      const int g = g0 + pid % pg;
+      uint8_t* dst = act + (size_t)p * kp2 * 4 + (size_t)g * 32;
+      // codes < I in a partial group are written later by FC1; zero the rest now
+      // (FC1 writes only valid codes, so a full clear of the group is safe
+      // because FC1 runs after this kernel on the same stream)
+      *(f16x8*)dst = f16x8{};
+      *(f16x8*)(dst + 16) = f16x8{};
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_router(const float* logits, int T, int E, int k, int routing, int normalize, int* topk_idx,
+                         float* topk_w, hipStream_t st) {
+  const dim3 grid((T + 3) / 4), block(256);
+  const int V = (E + 63) / 64;
+  if (V <= 1) hipLaunchKernelGGL(qmoe_router<1>, grid, block, 0, st, logits, T, E, k, routing, normalize, topk_idx, topk_w);
+  else if (V <= 2) hipLaunchKernelGGL(qmoe_router<2>, grid, block, 0, st, logits, T, E, k, routing, normalize, topk_idx, topk_w);
+  else if (V <= 4) hipLaunchKernelGGL(qmoe_router<4>, grid, block, 0, st, logits, T, E, k, routing, normalize, topk_idx, topk_w);
+  else if (V <= 8) hipLaunchKernelGGL(qmoe_router<8>, grid, block, 0, st, logits, T, E, k, routing, normalize, topk_idx, topk_w);
+  else hipLaunchKernelGGL(qmoe_router<16>, grid, block, 0, st, logits, T, E, k, routing, normalize, topk_idx, topk_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchunks, int bm, int* hist,
+                          int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st) {
+  hipLaunchKernelGGL(qmoe_hist, dim3(nchunks), dim3(256), E * sizeof(int), st, topk_idx, S, E, chunk, hist);
+  hipLaunchKernelGGL(qmoe_scan, dim3(1), dim3(1024), 0, st, hist, nchunks, E, S, bm, counts, offsets, tiles, ntiles);
+  hipLaunchKernelGGL(qmoe_scatter, dim3(nchunks), dim3(256), 5 * E * sizeof(int), st, topk_idx, hist, S, E, chunk, perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_a(int bits, const float* x, int T, int H, int kp, uint8_t* xa, uint8_t* act, int S, int I,
+                         int kp2, hipStream_t st) {
+  long work = (long)T * (kp / 8);
+  if (act) work += (long)S * (kp2 / 8 - I / 8);
+  const dim3 grid((work + 255) / 256), block(256);
+  if (bits == 4) hipLaunchKernelGGL(qmoe_prep_a<4>, grid, block, 0, st, x, T, H, kp, xa, act, S, I, kp2);
+  else hipLaunchKernelGGL(qmoe_prep_a<8>, grid, block, 0, st, x, T, H, kp, xa, act, S, I, kp2);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,217 @@
+// C ABI entry points of the QMoE library (declared in include/qmoe.h).
+//
+// qmoe_forward enqueues, on the caller's stream:
+//   router -> permutation (histogram, scan, stable scatter) -> operand prep ->
+//   FC1 + activation -> FC2 -> combine
+// with every intermediate in the caller's workspace.  It allocates nothing and
+// never synchronises.
+#include <hip/hip_runtime.h>
+
+#include "kernels/launch.h"
+#include "qmoe.h"
+#include "qmoe_plan.h"
+
+using namespace qmoe;
+
+namespace {
+
+bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t numel(const qmoe_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->rank; ++i) n *= t->dims[i];
+  return n;
+}
+
+#define QMOE_TRY_HIP(expr)                      \
+  do {                                          \
+    if ((expr) != hipSuccess) return QMOE_ERR_HIP; \
+  } while (0)
+
+qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, const qmoe_tensor* fc1w,
+                         const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
+                         const qmoe_attrs* attrs, const qmoe_tensor* output, void* workspace, size_t ws_bytes,
+                         void* stream, const qmoe_debug* dbg) {
+  if (!output) return QMOE_ERR_NULL;
+  Dims d;
+  qmoe_status st = validate(input, router, fc1w, fc1s, fc2w, fc2s, output, attrs, &d);
+  if (st != QMOE_OK) return st;
+  Plan p;
+  make_plan(d, &p);
+  if (d.T == 0) return QMOE_OK;
+
+  // Required device pointers and their alignment.
+  const qmoe_tensor* all[] = {input, router, fc1w, fc1s, fc2w, fc2s, output};
+  for (const qmoe_tensor* t : all)
+    if (numel(t) > 0 && t->data == nullptr) return QMOE_ERR_NULL;
+  if (!aligned_to(input->data, 16) || !aligned_to(output->data, 16) || !aligned_to(fc1w->data, 16) ||
+      !aligned_to(fc2w->data, 16) || !aligned_to(router->data, 4) || !aligned_to(fc1s->data, 4) ||
+      !aligned_to(fc2s->data, 4))
+    return QMOE_ERR_ALIGN;
+  if (p.bytes > 0) {
+    if (workspace == nullptr) return QMOE_ERR_NULL;
+    if (ws_bytes < p.bytes) return QMOE_ERR_WORKSPACE;
+    if (!aligned_to(workspace, 256)) return QMOE_ERR_ALIGN;
+  }
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* out = static_cast<float*>(const_cast<void*>(output->data));
+  const int T = (int)d.T, H = (int)d.H, E = (int)d.E, I = (int)d.I, k = (int)d.k, S = (int)p.S;
+
+  if (d.I == 0) {
+    // Variant quant_zero_inter of the manifest: every output element is zero.
+    QMOE_TRY_HIP(launch_fill_zero(out, (long)d.T * d.H, s));
+    if (!dbg) return QMOE_OK;
+  }
+  int* topk_idx = reinterpret_cast<int*>(ws + p.off_topk_idx);
+  float* topk_w = reinterpret_cast<float*>(ws + p.off_topk_w);
+  int* counts = reinterpret_cast<int*>(ws + p.off_counts);
+  int* offsets = reinterpret_cast<int*>(ws + p.off_offsets);
+  int* perm = reinterpret_cast<int*>(ws + p.off_perm);
+  int* tiles = reinterpret_cast<int*>(ws + p.off_tiles);
+  int* ntiles = reinterpret_cast<int*>(ws + p.off_ntiles);
+  int* hist = reinterpret_cast<int*>(ws + p.off_hist);
+  uint8_t* xa = ws + p.off_xa;
+  uint8_t* act = ws + p.off_act;
+  float* slot = reinterpret_cast<float*>(ws + p.off_slot);
+
+  auto mark = [&](int i) -> hipError_t {
+    if (dbg && d.I > 0 && dbg->events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(dbg->events[i]), s);
+    return hipSuccess;
+  };
+  QMOE_TRY_HIP(mark(0));
+  QMOE_TRY_HIP(launch_router(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize, topk_idx,
+                             topk_w, s));
+  QMOE_TRY_HIP(launch_permute(topk_idx, S, E, (int)p.chunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets, perm,
+                              tiles, ntiles, s));
+  if (d.I > 0) {
+    QMOE_TRY_HIP(launch_prep_a(d.bits, static_cast<const float*>(input->data), T, H, (int)p.kp1, xa, act, S, I,
+                               (int)p.kp2, s));
+    QMOE_TRY_HIP(mark(1));
+    GemmArgs g1{};
+    g1.wq = static_cast<const uint8_t*>(fc1w->data);
+    g1.ws = static_cast<const float*>(fc1s->data);
+    g1.a = xa;
+    g1.a_map = perm;
+    g1.a_div = k;
+    g1.a_stride = 4 * p.kp1;
+    g1.tiles = tiles;
+    g1.ntiles = ntiles;
+    g1.N = (int)d.F;
+    g1.K = H;
+    g1.kb = (int)(d.H / d.pack);
+    g1.nblk = (int)d.nb1;
+    g1.bs = (int)d.bs;
+    g1.act = act;
+    g1.act_stride = 4 * p.kp2;
+    g1.alpha = d.alpha;
+    g1.beta = d.beta;
+    QMOE_TRY_HIP(launch_gemm(d.bits, d.act == QMOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU, p.mt, p.aligned, g1,
+                             (int)p.max_tiles, s));
+    QMOE_TRY_HIP(mark(2));
+    GemmArgs g2{};
+    g2.wq = static_cast<const uint8_t*>(fc2w->data);
+    g2.ws = static_cast<const float*>(fc2s->data);
+    g2.a = act;
+    g2.a_map = nullptr;
+    g2.a_div = 1;
+    g2.a_stride = 4 * p.kp2;
+    g2.tiles = tiles;
+    g2.ntiles = ntiles;
+    g2.N = H;
+    g2.K = I;
+    g2.kb = (int)(d.I / d.pack);
+    g2.nblk = (int)d.nb2;
+    g2.bs = (int)d.bs;
+    g2.slot_out = slot;
+    g2.perm = perm;
+    QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
+    QMOE_TRY_HIP(mark(3));
+    QMOE_TRY_HIP(launch_combine(slot, topk_w, T, k, H, out, s));
+    QMOE_TRY_HIP(mark(4));
+  }
+  if (dbg) {
+    if (dbg->topk_idx) QMOE_TRY_HIP(launch_copy_i32(topk_idx, dbg->topk_idx, S, s));
+    if (dbg->topk_w) QMOE_TRY_HIP(launch_copy_f32(topk_w, dbg->topk_w, S, s));
+    if (dbg->counts) QMOE_TRY_HIP(launch_copy_i32(counts, dbg->counts, E, s));
+    if (dbg->offsets) QMOE_TRY_HIP(launch_copy_i32(offsets, dbg->offsets, E + 1, s));
+    if (dbg->perm) QMOE_TRY_HIP(launch_copy_i32(perm, dbg->perm, S, s));
+  }
+  return QMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qmoe_abi_version(void) { return QMOE_ABI_VERSION; }
+
+void qmoe_attrs_default(qmoe_attrs* a) {
+  if (!a) return;
+  a->k = 1;
+  a->expert_weight_bits = 4;
+  a->block_size = 0;
+  a->activation_type = QMOE_ACT_RELU;
+  a->swiglu_fusion = 0;
+  a->activation_alpha = 1.f;
+  a->activation_beta = 0.f;
+  a->normalize_routing_weights = 0;
+  a->routing = QMOE_ROUTE_QMOE;
+  a->use_sparse_mixer = 0;
+  a->weights_prepacked = -1;
+  a->quant_type = 0;
+}
+
+qmoe_status qmoe_validate(const qmoe_tensor* input, const qmoe_tensor* router_probs, const qmoe_tensor* fc1w,
+                          const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
+                          const qmoe_tensor* output, const qmoe_attrs* attrs) {
+  Dims d;
+  return validate(input, router_probs, fc1w, fc1s, fc2w, fc2s, output, attrs, &d);
+}
+
+qmoe_status qmoe_workspace_size(const qmoe_tensor* input, const qmoe_tensor* router_probs, const qmoe_tensor* fc1w,
+                                const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
+                                const qmoe_attrs* attrs, size_t* bytes) {
+  if (!bytes) return QMOE_ERR_NULL;
+  Dims d;
+  qmoe_status st = validate(input, router_probs, fc1w, fc1s, fc2w, fc2s, nullptr, attrs, &d);
+  if (st != QMOE_OK) return st;
+  Plan p;
+  make_plan(d, &p);
+  *bytes = p.bytes;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_forward(const qmoe_tensor* input, const qmoe_tensor* router_probs, const qmoe_tensor* fc1w,
+                         const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
+                         const qmoe_attrs* attrs, const qmoe_tensor* output, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return forward_impl(input, router_probs, fc1w, fc1s, fc2w, fc2s, attrs, output, workspace, workspace_bytes,
+                      stream, nullptr);
+}
+
+qmoe_status qmoe_forward_debug(const qmoe_tensor* input, const qmoe_tensor* router_probs, const qmoe_tensor* fc1w,
+                               const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
+                               const qmoe_attrs* attrs, const qmoe_tensor* output, void* workspace,
+                               size_t workspace_bytes, void* stream, const qmoe_debug* debug) {
+  return forward_impl(input, router_probs, fc1w, fc1s, fc2w, fc2s, attrs, output, workspace, workspace_bytes,
+                      stream, debug);
+}
+
+const char* qmoe_status_string(qmoe_status s) {
+  switch (s) {
+    case QMOE_OK: return "ok";
+    case QMOE_ERR_NULL: return "null pointer";
+    case QMOE_ERR_SHAPE: return "shape violates the operator contract";
+    case QMOE_ERR_ATTR: return "attribute value outside the accepted set";
+    case QMOE_ERR_UNSUPPORTED: return "standard value not implemented by this library";
+    case QMOE_ERR_WORKSPACE: return "workspace too small";
+    case QMOE_ERR_HIP: return "HIP launch failed";
+    case QMOE_ERR_DTYPE: return "tensor dtype differs from the contract";
+    case QMOE_ERR_ALIGN: return "pointer misaligned";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// Contract validation and workspace planning for the QMoE operator.
+//
+// Every clause follows the QMoE WebGPU manifest: `attributeConstraints`,
+// `typeConstraints`, and the `derive` booleans activationSupported,
+// routingModeSupported, rawWeightLayout, inputOutputShapeOk,
+// quantBlockSizeOk, quantScalesOk, quantShapeOk and quantContract.
+#include "qmoe_plan.h"
+
+namespace qmoe {
+namespace {
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool rank_ok(const qmoe_tensor* t, int r) { return t->rank == r; }
+
+}  // namespace
+
+qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const qmoe_tensor* fc1w,
+                     const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
+                     const qmoe_tensor* output, const qmoe_attrs* a, Dims* d) {
+  if (!input || !router || !fc1w || !fc1s || !fc2w || !fc2s || !a || !d) return QMOE_ERR_NULL;
+
+  // Standard attribute values this library does not implement.
+  if (a->quant_type != 0) return QMOE_ERR_UNSUPPORTED;
+  if (a->use_sparse_mixer == 1) return QMOE_ERR_UNSUPPORTED;
+  if (a->use_sparse_mixer != 0) return QMOE_ERR_ATTR;
+  if (a->weights_prepacked == 1) return QMOE_ERR_UNSUPPORTED;
+  if (a->weights_prepacked != -1 && a->weights_prepacked != 0) return QMOE_ERR_ATTR;
+  if (a->swiglu_fusion == 2) return QMOE_ERR_UNSUPPORTED;
+  // attributeConstraints
+  if (a->expert_weight_bits != 4 && a->expert_weight_bits != 8) return QMOE_ERR_ATTR;
+  if (a->normalize_routing_weights != 0 && a->normalize_routing_weights != 1) return QMOE_ERR_ATTR;
+  if (a->routing != QMOE_ROUTE_QMOE && a->routing != QMOE_ROUTE_MOE) return QMOE_ERR_ATTR;
+  // activationSupported
+  const bool relu = a->activation_type == QMOE_ACT_RELU && a->swiglu_fusion == 0;
+  const bool swiglu = a->activation_type == QMOE_ACT_SWIGLU && a->swiglu_fusion == 1;
+  if (!relu && !swiglu) return QMOE_ERR_ATTR;
+  // quantBlockSizeOk, attribute part
+  const int64_t bs = a->block_size;
+  if (bs < 0 || (bs != 0 && (bs < 16 || !is_pow2(bs)))) return QMOE_ERR_ATTR;
+
+  // typeConstraints: T = float32, T1 = uint8, T2 = float32
+  if (input->dtype != QMOE_F32 || router->dtype != QMOE_F32 || fc1w->dtype != QMOE_U8 ||
+      fc2w->dtype != QMOE_U8 || fc1s->dtype != QMOE_F32 || fc2s->dtype != QMOE_F32)
+    return QMOE_ERR_DTYPE;
+  if (output && output->dtype != QMOE_F32) return QMOE_ERR_DTYPE;
+
+  // inputOutputShapeOk
+  if (input->rank != 2 && input->rank != 3) return QMOE_ERR_SHAPE;
+  for (int i = 0; i < input->rank; ++i)
+    if (input->dims[i] < 0) return QMOE_ERR_SHAPE;
+  const int64_t H = input->dims[input->rank - 1];
+  if (H <= 0) return QMOE_ERR_SHAPE;
+  int64_t T = 1;
+  for (int i = 0; i < input->rank - 1; ++i) T *= input->dims[i];
+  if (output) {
+    if (output->rank != input->rank) return QMOE_ERR_SHAPE;
+    for (int i = 0; i < input->rank; ++i)
+      if (output->dims[i] != input->dims[i]) return QMOE_ERR_SHAPE;
+  }
+
+  const int bits = a->expert_weight_bits;
+  const int pack = bits == 4 ? 2 : 1;
+  const int fusion = swiglu ? 2 : 1;
+
+  // quantShapeOk
+  if (!rank_ok(router, 2) || !rank_ok(fc1w, 3) || !rank_ok(fc2w, 3)) return QMOE_ERR_SHAPE;
+  const int64_t E = router->dims[1];
+  if (router->dims[0] != T || E < 0) return QMOE_ERR_SHAPE;
+  if (fc1w->dims[0] != E || fc2w->dims[0] != E) return QMOE_ERR_SHAPE;
+  const int64_t F = fc1w->dims[1];
+  if (F < 0 || F % fusion != 0) return QMOE_ERR_SHAPE;
+  const int64_t I = F / fusion;
+  if (fc2w->dims[1] != H) return QMOE_ERR_SHAPE;
+  if (fc1w->dims[2] * pack != H || fc2w->dims[2] * pack != I) return QMOE_ERR_SHAPE;
+  // quantBlockSizeOk, shape part
+  if (bs != 0 && (H % bs != 0 || I % bs != 0)) return QMOE_ERR_SHAPE;
+  // quantScalesOk
+  if (fc1s->rank < 2 || fc2s->rank < 2) return QMOE_ERR_SHAPE;
+  if (fc1s->dims[0] != E || fc2s->dims[0] != E || fc1s->dims[1] != F || fc2s->dims[1] != H)
+    return QMOE_ERR_SHAPE;
+  if (bs == 0) {
+    if (fc1s->rank != 2 || fc2s->rank != 2) return QMOE_ERR_SHAPE;
+  } else {
+    if (fc1s->rank != 3 || fc2s->rank != 3 || fc1s->dims[2] != H / bs || fc2s->dims[2] != I / bs)
+      return QMOE_ERR_SHAPE;
+  }
+  // quantContract: 1 <= k <= num_experts
+  if (a->k < 1 || a->k > E) return QMOE_ERR_ATTR;
+  // The routing kernels hold one row of logits per wavefront in registers.
+  if (E > kMaxExperts) return QMOE_ERR_UNSUPPORTED;
+
+  d->T = T; d->H = H; d->E = E; d->I = I; d->F = F; d->k = a->k;
+  d->bits = bits; d->pack = pack; d->mid = bits == 4 ? 8 : 128; d->fusion = fusion;
+  d->bs = bs; d->nb1 = bs ? H / bs : 1; d->nb2 = bs ? I / bs : 1;
+  d->act = swiglu ? QMOE_ACT_SWIGLU : QMOE_ACT_RELU;
+  d->routing = a->routing; d->normalize = a->normalize_routing_weights;
+  d->alpha = a->activation_alpha; d->beta = a->activation_beta;
+  return QMOE_OK;
+}
+
+void make_plan(const Dims& d, Plan* p) {
+  *p = Plan();
+  p->d = d;
+  p->S = d.T * d.k;
+  if (d.T == 0) return;  // nothing to enqueue
+  // Every expert receives at most T rows (a token selects distinct experts),
+  // so up to 64 tokens one M tile of ceil(T/16)*16 rows holds any expert's
+  // rows and the weights stream from HBM exactly once.
+  p->decode = d.T <= 64;
+  p->mt = p->decode ? int((d.T + 15) / 16) : 4;
+  p->bm = 16 * p->mt;
+  p->max_tiles = (p->S + p->bm - 1) / p->bm + d.E;
+  // With I == 0 only the routing stages run (output is a zero fill).
+  p->kp1 = d.I > 0 ? round_up(d.H, 128) : 0;
+  p->kp2 = round_up(d.I, 128);
+  p->aligned = (d.H % 8 == 0) && (d.I % 8 == 0);
+  p->nchunks = (p->S + p->chunk - 1) / p->chunk;
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  p->off_topk_idx = take(sizeof(int32_t) * p->S);
+  p->off_topk_w = take(sizeof(float) * p->S);
+  p->off_counts = take(sizeof(int32_t) * d.E);
+  p->off_offsets = take(sizeof(int32_t) * (d.E + 1));
+  p->off_perm = take(sizeof(int32_t) * p->S);
+  p->off_tiles = take(sizeof(int32_t) * 4 * p->max_tiles);
+  p->off_ntiles = take(sizeof(int32_t) * 4);
+  p->off_hist = take(sizeof(int32_t) * p->nchunks * d.E);
+  p->off_xa = take(size_t(4) * d.T * p->kp1);     // f16 hi + lo per element
+  p->off_act = take(size_t(4) * p->S * p->kp2);   // f16 hi + lo per element
+  p->off_slot = take(d.I > 0 ? sizeof(float) * p->S * d.H : 0); // FC2 rows by slot id
+  p->bytes = o;
+}
+
+}  // namespace qmoe

@@ -1,0 +1,59 @@
+// Host-side contract check and launch plan for the QMoE operator.
+// Pure C++ (no HIP types), so the contract logic runs and is tested on any CPU.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "qmoe.h"
+
+namespace qmoe {
+
+// Sizes derived from the tensors (QMoE WebGPU manifest, `derive`:
+// hiddenSize, numTokens, fusionSize, interSize, packSize, quantMidpoint,
+// colWiseScales, fc1ScaleBlocks, fc2ScaleBlocks).
+struct Dims {
+  int64_t T = 0;   // tokens = numel(input) / H
+  int64_t H = 0;   // hidden size
+  int64_t E = 0;   // experts
+  int64_t I = 0;   // inter size
+  int64_t F = 0;   // FC1 rows = fusion * I
+  int64_t k = 0;
+  int bits = 4, pack = 2, mid = 8, fusion = 1;
+  int64_t bs = 0;            // 0 = column-wise
+  int64_t nb1 = 1, nb2 = 1;  // scale blocks per FC1 / FC2 row
+  int act = QMOE_ACT_RELU;
+  int routing = QMOE_ROUTE_QMOE;
+  int normalize = 0;
+  float alpha = 1.f, beta = 0.f;
+};
+
+// Largest expert count the routing kernels hold in registers / LDS.
+constexpr int64_t kMaxExperts = 1024;
+
+qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const qmoe_tensor* fc1w,
+                     const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
+                     const qmoe_tensor* output, const qmoe_attrs* attrs, Dims* d);
+
+// Which kernels run, with what tiles, and where each intermediate lives in the
+// caller's workspace.  Offsets are bytes from the workspace base, 256-aligned.
+struct Plan {
+  Dims d;
+  int64_t S = 0;         // slots = T * k
+  bool decode = false;   // weight-streaming path (every expert's rows fit one M tile)
+  int mt = 1;            // 16-row M subtiles per tile
+  int64_t bm = 16;       // rows per M tile
+  int64_t max_tiles = 0; // ceil(S / bm) + E
+  int64_t kp1 = 0, kp2 = 0;  // padded reduction lengths of the A operands (codes)
+  bool aligned = true;   // packed rows allow vector loads
+  int64_t chunk = 1024;  // slots per permutation block
+  int64_t nchunks = 0;
+  // workspace layout
+  size_t off_topk_idx = 0, off_topk_w = 0, off_counts = 0, off_offsets = 0, off_perm = 0;
+  size_t off_tiles = 0, off_ntiles = 0, off_hist = 0, off_xa = 0, off_act = 0, off_slot = 0;
+  size_t bytes = 0;
+};
+
+// Fill *p from validated dims.  Never fails.
+void make_plan(const Dims& d, Plan* p);
+
+}  // namespace qmoe

@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+entry point include/qmoe.h declares, reports the manifest defaults, and its
+contract check agrees with the oracle's on every clause."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_mixture_experts_router_amd as qm
+from oracle import qmoe_oracle as Q
+from quantized_mixture_experts_router_amd import workloads as W
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qmoe.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmoe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qm.LIB_PATH):
+        pytest.skip("libqmoe.so not built (run __graft_entry__.build())")
+    return qm.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"qmoe_forward", "qmoe_validate", "qmoe_workspace_size", "qmoe_forward_debug",
+            "qmoe_status_string", "qmoe_attrs_default", "qmoe_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings(lib):
+    assert qm.qmoe_abi_version() == 1
+    for s in range(9):
+        assert qm.qmoe_status_string(s) != "unknown status"
+
+
+def test_attribute_defaults_match_manifest(lib):
+    a = qm.qmoe_attrs_default()
+    # QMoE WebGPU manifest, key "attributes"
+    assert a.k == 1 and a.expert_weight_bits == 4 and a.activation_type == 0
+    assert a.activation_alpha == 1.0 and a.activation_beta == 0.0
+    assert a.normalize_routing_weights == 0 and a.swiglu_fusion == 0
+    assert a.use_sparse_mixer == 0 and a.weights_prepacked == -1 and a.quant_type == 0
+    assert a.block_size == 0 and a.routing == 0
+
+
+KIND = {"shape": 2, "attr": 3, "unsupported": 4, "dtype": 7}
+
+
+def _case(rng, **kw):
+    base = dict(tokens_shape=(6,), hidden=32, experts=4, inter=32, k=1, bits=4, block_size=0,
+                activation="relu")
+    base.update(kw)
+    return W.random_case(rng, **base)
+
+
+def _mutate(a, attrs, mut):
+    if mut == "blocks64":
+        attrs["block_size"] = 64
+        a["fc1_scales"] = a["fc1_scales"][..., None]
+        a["fc2_scales"] = a["fc2_scales"][..., None]
+    elif mut == "router_rows":
+        a["router_probs"] = a["router_probs"][:-1]
+    elif mut == "fc2_rows":
+        a["fc2_experts_weights"] = a["fc2_experts_weights"][:, :-1]
+    elif mut == "packed_cols":
+        a["fc1_experts_weights"] = a["fc1_experts_weights"][:, :, :-1]
+    elif mut == "scale_rank":
+        a["fc1_scales"] = a["fc1_scales"][..., None]
+    elif mut == "dtype":
+        a["input"] = a["input"].astype(np.float64)
+    elif mut == "rank4":
+        a["input"] = a["input"][None, None]
+
+
+CASES = [
+    ("ok", {}, None), ("k0", dict(k=0), None), ("k_gt_e", dict(k=5), None),
+    ("bits2", dict(expert_weight_bits=2), None), ("normalize2", dict(normalize_routing_weights=2), None),
+    ("prepacked1", dict(weights_prepacked=1), None), ("prepacked2", dict(weights_prepacked=2), None),
+    ("sparse", dict(use_sparse_mixer=1), None), ("quant_fp", dict(quant_type="fp"), None),
+    ("relu_fused", dict(swiglu_fusion=1), None), ("fusion2", dict(swiglu_fusion=2), None),
+    ("bs8", dict(block_size=8), None), ("bs24", dict(block_size=24), None),
+    ("bs64_not_dividing", {}, "blocks64"), ("router_rows", {}, "router_rows"), ("fc2_rows", {}, "fc2_rows"),
+    ("packed_cols", {}, "packed_cols"), ("scale_rank", {}, "scale_rank"), ("dtype", {}, "dtype"),
+    ("rank4", {}, "rank4"), ("moe_norm", dict(routing="moe", normalize_routing_weights=1), None),
+    ("bs16", dict(block_size=16), "bs16"), ("swiglu", dict(activation_type="swiglu", swiglu_fusion=1), "swiglu"),
+]
+
+
+@pytest.mark.parametrize("name,over,mut", CASES, ids=[c[0] for c in CASES])
+def test_validate_agrees_with_oracle(lib, name, over, mut):
+    rng = np.random.default_rng(7)
+    if mut == "bs16":
+        w, a = _case(rng, block_size=16)
+    elif mut == "swiglu":
+        w, a = _case(rng, activation="swiglu")
+    else:
+        w, a = _case(rng)
+    attrs = dict(w.attrs(), **over)
+    if mut not in (None, "bs16", "swiglu"):
+        _mutate(a, attrs, mut)
+    try:
+        Q.validate(*a.values(), attrs=attrs)
+        expect = 0
+    except Q.ContractError as e:
+        expect = KIND[e.kind]
+    got = qm.qmoe_validate(*a.values(), attrs=attrs)
+    assert got == expect, (name, got, expect)
+
+
+def test_validate_output_shape_and_zero_sizes(lib):
+    rng = np.random.default_rng(8)
+    w, a = _case(rng)
+    out_bad = np.zeros((5, 32), dtype=np.float32)
+    assert qm.qmoe_validate(*a.values(), output=out_bad, attrs=w.attrs()) == 2
+    assert qm.qmoe_validate(*a.values(), output=a["input"], attrs=w.attrs()) == 0
+    # T == 0 and I == 0 are in contract
+    b = dict(a, input=a["input"][:0], router_probs=a["router_probs"][:0])
+    assert qm.qmoe_validate(*b.values(), attrs=w.attrs()) == 0
+    assert qm.qmoe_workspace_size(*b.values(), attrs=w.attrs()) == 0
+    w0, c = _case(rng, inter=0)
+    assert qm.qmoe_validate(*c.values(), attrs=w0.attrs()) == 0
+
+
+def test_workspace_size_covers_intermediates(lib):
+    for name in ("decode", "prefill", "fine", "large_e"):
+        w = W.WORKLOADS[name]
+        s = W.shapes(w)
+        fake = {k: np.lib.stride_tricks.as_strided(np.zeros(1, dtype=np.float32 if "weights" not in k else np.uint8),
+                                                    shape=v, strides=(0,) * len(v)) for k, v in s.items()}
+        n = qm.qmoe_workspace_size(fake["input"], fake["router_probs"], fake["fc1_experts_weights"],
+                                   fake["fc1_scales"], fake["fc2_experts_weights"], fake["fc2_scales"], w.attrs())
+        S = w.tokens * w.k
+        assert n >= 4 * S * w.hidden + 4 * S * w.inter + 4 * w.tokens * w.hidden
+        assert n < 3 * (4 * S * w.hidden + 4 * S * w.inter + 4 * w.tokens * w.hidden) + (1 << 20)
+
+
+def test_null_arguments(lib):
+    assert lib.qmoe_validate(None, None, None, None, None, None, None, None) == 1
+    a = qm.qmoe_attrs_default()
+    assert lib.qmoe_workspace_size(None, None, None, None, None, None, ctypes.byref(a), None) == 1

@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact routing indices, counts, offsets and permutation; routing weights
+within 1e-6; outputs within 2e-3 x RMS of the oracle's output.  Small cases
+compare every element; the full-size workloads compare the routing exactly
+and a sample of output rows that the oracle computes one by one.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import qmoe_oracle as Q
+from quantized_mixture_experts_router_amd import workloads as W
+
+from conftest import GOLDEN
+from gpu_util import check_output, check_routing, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    if not _t.cuda.is_available():
+        pytest.skip("no GPU")
+    return _t
+
+
+def _full_check(w, a, torch, label):
+    attrs = w.attrs()
+    say(f"[case] {label} T={w.tokens} H={w.hidden} E={w.experts} I={w.inter} k={w.k} bits={w.bits} "
+        f"bs={w.block_size} act={w.activation}")
+    res = run_gpu(a, attrs, torch)
+    ref, inter = oracle.qmoe(*a.values(), attrs=attrs, return_intermediates=True)
+    check_routing(res, inter["sel"], inter["w"], inter["counts"], inter["offsets"], inter["perm"])
+    return check_output(res["out"], ref, label)
+
+
+def test_tiny_workload_every_element(torch):
+    w = W.WORKLOADS["tiny"]
+    _full_check(w, W.generate(w), torch, "tiny")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_lifted_with_bias_example(torch):
+    g = _golden("qmoe_lifted_with_bias.json")
+    fc1 = np.array(g["fc1_codes"], dtype=np.uint8)
+    fc2 = np.array(g["fc2_codes"], dtype=np.uint8)
+    a = dict(input=np.array(g["input"], dtype=np.float32),
+             router_probs=np.array(g["router_probs"], dtype=np.float32),
+             fc1_experts_weights=fc1, fc1_scales=np.full(fc1.shape[:2], g["fc1_scale"], dtype=np.float32),
+             fc2_experts_weights=fc2, fc2_scales=np.full(fc2.shape[:2], g["fc2_scale"], dtype=np.float32))
+    res = run_gpu(a, dict(g["attrs"]), torch)
+    np.testing.assert_array_equal(res["topk_idx"].reshape(2, 2), np.array(g["expected_selection"]))
+    np.testing.assert_allclose(res["topk_w"].reshape(2, 2), g["expected_weights"], atol=1e-7)
+    np.testing.assert_allclose(res["out"], np.array(g["expected_output"]), atol=g["tolerance"], rtol=0)
+
+
+def test_swiglu_closed_form(torch):
+    g = _golden("swiglu_interleave.json")
+    fc1 = np.array(g["fc1_codes"], dtype=np.uint8)
+    fc2 = np.array(g["fc2_codes"], dtype=np.uint8)
+    a = dict(input=np.array(g["input"], dtype=np.float32),
+             router_probs=np.array(g["router_probs"], dtype=np.float32),
+             fc1_experts_weights=fc1, fc1_scales=np.full(fc1.shape[:2], g["fc1_scale"], dtype=np.float32),
+             fc2_experts_weights=fc2, fc2_scales=np.full(fc2.shape[:2], g["fc2_scale"], dtype=np.float32))
+    for c in g["cases"]:
+        attrs = dict(k=1, expert_weight_bits=8, activation_type="swiglu", swiglu_fusion=1,
+                     activation_alpha=c["alpha"], activation_beta=c["beta"])
+        res = run_gpu(a, attrs, torch)
+        assert abs(float(res["out"][0, 0]) - c["expected_out0"]) <= 2e-6 * abs(c["expected_out0"])
+        assert res["out"][0, 1] == 0.0
+
+
+def test_route_ties_through_gpu(torch):
+    g = _golden("route_ties.json")
+    for c in g["cases"]:
+        L = np.array(c["logits"], dtype=np.float32)
+        E = L.shape[1]
+        rng = np.random.default_rng(1)
+        w = W.Workload("ties", (1, 32), E, 32, c["k"], 8, 0, "relu", (0.01, 0.02))
+        a = W.generate(w, seed=3)
+        a["router_probs"] = L
+        res = run_gpu(a, w.attrs(), torch)
+        np.testing.assert_array_equal(res["topk_idx"].reshape(1, -1), np.array(c["expected"]))
+        np.testing.assert_allclose(res["topk_w"].reshape(1, -1), np.array(c["weights"]), rtol=2e-6, atol=0)
+        del rng
+
+
+# Small sweeps: every element.  (T, H, E, I, k) chosen to cover one and several
+# M subtiles on the weight-streaming path (T <= 64), the tiled path (T > 64),
+# ragged tails in every dimension, unused experts and k = E.
+SHAPES = [
+    (1, 64, 4, 32, 1), (5, 128, 3, 64, 2), (16, 256, 8, 96, 2), (17, 64, 4, 160, 3),
+    (33, 128, 6, 64, 6), (64, 192, 8, 128, 2), (70, 128, 5, 96, 2), (200, 64, 16, 64, 4),
+    (300, 256, 1, 32, 1),
+]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bs", [0, 16, 32, 64])
+@pytest.mark.parametrize("act", ["relu", "swiglu"])
+def test_small_sweep(torch, bits, bs, act):
+    rng = np.random.default_rng(1000 + bits * 10 + bs + (act == "swiglu"))
+    for (T, H, E, I, k) in SHAPES:
+        if bs and (H % bs or I % bs):
+            continue
+        shape = (T,) if T % 2 else (2, T // 2)
+        w, a = W.random_case(rng, tokens_shape=shape, hidden=H, experts=E, inter=I, k=k, bits=bits,
+                             block_size=bs, activation=act)
+        _full_check(w, a, torch, f"sweep T{T} H{H} E{E} I{I} k{k}")
+
+
+def test_unaligned_shapes(torch):
+    rng = np.random.default_rng(77)
+    # H or I not a multiple of 8 takes the byte-load path
+    for (T, H, E, I, k, bits) in [(3, 6, 2, 4, 1, 4), (9, 20, 3, 12, 2, 8), (70, 36, 4, 10, 2, 4), (5, 3, 2, 5, 2, 8)]:
+        for act in ("relu", "swiglu"):
+            w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=E, inter=I, k=k, bits=bits,
+                                 block_size=0, activation=act)
+            _full_check(w, a, torch, f"unaligned T{T} H{H} I{I} bits{bits} {act}")
+
+
+def test_moe_routing_modes(torch):
+    rng = np.random.default_rng(78)
+    for normalize in (0, 1):
+        for k in (1, 3, 8):
+            w, a = W.random_case(rng, tokens_shape=(40,), hidden=64, experts=8, inter=64, k=k, bits=4,
+                                 block_size=32, activation="swiglu", logit_sigma=2.0)
+            attrs = dict(w.attrs(), routing="moe", normalize_routing_weights=normalize)
+            res = run_gpu(a, attrs, torch)
+            ref, inter = oracle.qmoe(*a.values(), attrs=attrs, return_intermediates=True)
+            check_routing(res, inter["sel"], inter["w"], inter["counts"], inter["offsets"], inter["perm"],
+                          selected_softmax=bool(normalize))
+            check_output(res["out"], ref, f"moe normalize={normalize} k={k}")
+
+
+def test_alpha_beta(torch):
+    rng = np.random.default_rng(79)
+    w, a = W.random_case(rng, tokens_shape=(24,), hidden=128, experts=4, inter=64, k=2, bits=8,
+                         block_size=0, activation="swiglu")
+    attrs = dict(w.attrs(), activation_alpha=1.702, activation_beta=1.0)
+    res = run_gpu(a, attrs, torch)
+    check_output(res["out"], oracle.qmoe(*a.values(), attrs=attrs), "alpha=1.702 beta=1")
+
+
+# ------------------------------------------------------------------ exact invariants on the GPU
+def test_all_midpoint_codes_give_exact_zero(torch):
+    rng = np.random.default_rng(80)
+    for bits in (4, 8):
+        w, a = W.random_case(rng, tokens_shape=(20,), hidden=64, experts=4, inter=64, k=2, bits=bits,
+                             block_size=32, activation="swiglu")
+        a["fc1_experts_weights"][:] = 0x88 if bits == 4 else 128
+        res = run_gpu(a, w.attrs(), torch)
+        assert np.all(res["out"] == 0.0)
+
+
+def test_scale_doubling_doubles_output_bitwise(torch):
+    rng = np.random.default_rng(81)
+    for bs in (0, 32):
+        w, a = W.random_case(rng, tokens_shape=(40,), hidden=128, experts=4, inter=64, k=2, bits=4,
+                             block_size=bs, activation="relu")
+        r1 = run_gpu(a, w.attrs(), torch)["out"]
+        b = dict(a, fc2_scales=a["fc2_scales"] * 2)
+        r2 = run_gpu(b, w.attrs(), torch)["out"]
+        np.testing.assert_array_equal(r2, 2 * r1)
+
+
+def test_4bit_reencoded_as_8bit(torch):
+    rng = np.random.default_rng(82)
+    w, a = W.random_case(rng, tokens_shape=(30,), hidden=128, experts=4, inter=64, k=2, bits=4,
+                         block_size=0, activation="swiglu")
+    q1 = Q.unpack_codes(a["fc1_experts_weights"], 4)
+    q2 = Q.unpack_codes(a["fc2_experts_weights"], 4)
+    b = dict(a, fc1_experts_weights=(q1 + 120).astype(np.uint8), fc2_experts_weights=(q2 + 120).astype(np.uint8))
+    r4 = run_gpu(a, w.attrs(), torch)["out"]
+    r8 = run_gpu(b, dict(w.attrs(), expert_weight_bits=8), torch)["out"]
+    ref = oracle.qmoe(*a.values(), attrs=w.attrs())
+    check_output(r4, ref, "4-bit")
+    check_output(r8, ref, "same codes as 8-bit")
+
+
+def test_determinism_bitwise(torch):
+    w = W.WORKLOADS["tiny"]
+    a = W.generate(w)
+    r1 = run_gpu(a, w.attrs(), torch)
+    r2 = run_gpu(a, w.attrs(), torch)
+    for key in r1:
+        np.testing.assert_array_equal(r1[key], r2[key])
+
+
+# ------------------------------------------------------------------ edge cases and errors
+def test_zero_tokens_and_zero_inter(torch):
+    rng = np.random.default_rng(83)
+    w, a = W.random_case(rng, tokens_shape=(6,), hidden=64, experts=4, inter=0, k=2, bits=8, block_size=0,
+                         activation="relu")
+    res = run_gpu(a, w.attrs(), torch)
+    assert np.all(res["out"] == 0.0)
+    ref_sel, _ = oracle.route(a["router_probs"], 2)
+    np.testing.assert_array_equal(res["topk_idx"].reshape(6, 2), ref_sel)
+    w2, b = W.random_case(rng, tokens_shape=(6,), hidden=64, experts=4, inter=32, k=2, bits=8, block_size=0,
+                          activation="relu")
+    b["input"] = b["input"][:0]
+    b["router_probs"] = b["router_probs"][:0]
+    res = run_gpu(b, w2.attrs(), torch, debug=False)
+    assert res["out"].shape == (0, 64)
+
+
+def test_error_statuses(torch):
+    import quantized_mixture_experts_router_amd as qm
+    rng = np.random.default_rng(84)
+    w, a = W.random_case(rng, tokens_shape=(8,), hidden=64, experts=4, inter=32, k=2, bits=8, block_size=0,
+                         activation="relu")
+    d = {k: torch.from_numpy(v).cuda() for k, v in a.items()}
+    args = [d[k] for k in ("input", "router_probs", "fc1_experts_weights", "fc1_scales", "fc2_experts_weights",
+                           "fc2_scales")]
+    need = qm.qmoe_workspace_size(*args, w.attrs())
+    out = torch.full_like(d["input"], 5.0)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(qm.QmoeError) as ei:
+        qm.qmoe_forward(*args, w.attrs(), out, small)
+    assert ei.value.name == "WORKSPACE"
+    big = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    with pytest.raises(qm.QmoeError) as ei:
+        qm.qmoe_forward(*args, w.attrs(), out, big[4:])
+    assert ei.value.name == "ALIGN"
+    with pytest.raises(qm.QmoeError) as ei:
+        qm.qmoe_forward(*args, dict(w.attrs(), k=9), out, big)
+    assert ei.value.name == "ATTR"
+    torch.cuda.synchronize()
+    assert torch.all(out == 5.0)  # untouched on error
+
+
+# ------------------------------------------------------------------ full-size workloads
+def _sample_tokens(sel, counts, T):
+    ids = {0, T - 1, T // 2, T // 3}
+    nz = np.nonzero(counts)[0]
+    rare = nz[np.argmin(counts[nz])]
+    ids.add(int(np.nonzero((sel == rare).any(axis=1))[0][0]))
+    return sorted(ids)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "fine", "large_e"])
+def test_full_size_workload(torch, name):
+    w = W.WORKLOADS[name]
+    say(f"[case] full {name}: generating")
+    a = W.generate(w)
+    attrs = w.attrs()
+    res = run_gpu(a, attrs, torch)
+    sel, wts = oracle.route(a["router_probs"], w.k)
+    counts, offsets, perm = oracle.expert_permutation(sel, w.experts)
+    check_routing(res, sel, wts, counts, offsets, perm)
+    say(f"  routing bit-exact over {w.tokens} tokens; counts min/max {counts.min()}/{counts.max()}")
+    if name == "decode":
+        ids = list(range(w.tokens))
+    else:
+        ids = _sample_tokens(sel, counts, w.tokens)
+    ref = oracle.qmoe_tokens(ids, *a.values(), attrs=attrs)
+    out = res["out"].reshape(w.tokens, w.hidden)[ids]
+    check_output(out, ref, f"{name} rows {ids}")
+    # determinism at full size
+    res2 = run_gpu(a, attrs, torch, debug=False)
+    np.testing.assert_array_equal(res2["out"], res["out"])
