@@ -142,8 +142,8 @@ qmoe_status qmoe_workspace_size(const qmoe_tensor* input, const qmoe_tensor* rou
                                 const qmoe_attrs* attrs, size_t* bytes);
 
 /* Enqueue the whole operator on stream (a hipStream_t; NULL = the null
- * stream).  Device pointers: input, router_probs, scales 4-byte aligned;
- * input, weights and output 16-byte aligned (QMOE_ERR_ALIGN otherwise).
+ * stream).  Device pointers: router_probs 4-byte aligned; input, weights,
+ * scales and output 16-byte aligned (QMOE_ERR_ALIGN otherwise).
  * workspace: device memory of at least qmoe_workspace_size bytes, 256-byte
  * aligned, exclusively owned by this call until the stream reaches it.  The
  * output must not alias any input. */

@@ -21,6 +21,7 @@ SOURCES = [
     "qmoe_api.cpp",
     "kernels/route.hip",
     "kernels/gemm.hip",
+    "kernels/stream.hip",
 ]
 
 ARCH = os.environ.get("QMOE_OFFLOAD_ARCH", "gfx950")

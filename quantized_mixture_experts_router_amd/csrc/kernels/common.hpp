@@ -24,23 +24,37 @@ constexpr int kWave = 64;
 //
 // A row holds Kp codes (Kp a multiple of 128, zero padded).  Codes are stored
 // in groups of 8: 16 bytes of hi halves then 16 bytes of lo halves, so one
-// 32-byte group is what a lane feeds to one matrix instruction.  Inside a
-// group of 8 the storage order follows how the weight unpacker emits codes:
+// 32-byte group is what a lane feeds to one matrix instruction.  Each 32-code
+// block is one matrix-instruction step; lane group g (lanes 16g..16g+15) of
+// that step feeds storage group g, which holds the block's code group
+//   4-bit: g            8-bit: sigma(g) = (0, 2, 1, 3)[g]
+// (the order in which the weight loader's cross-lane exchange leaves packed
+// bytes).  Inside a group of 8 the order follows the weight unpacker:
 //   8-bit: natural order;
-//   4-bit: storage slot i holds logical code kPerm4[i] (pairs (0,4),(1,5),...)
+//   4-bit: storage slot i holds code perm4(i), i.e. pairs (0,4),(1,5),(2,6),(3,7).
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int perm4_of_slot(int i) { return (i >> 1) | ((i & 1) << 2); }
 __host__ __device__ constexpr int slot4_of_code(int c) { return ((c & 3) << 1) | (c >> 2); }
+__host__ __device__ constexpr int sigma8(int g) { return ((g & 1) << 1) | (g >> 1); }  // an involution
+
+// Code group (0..3 inside a 32-code block) fed by lane group g.
+template <int BITS>
+__device__ __forceinline__ int code_group_of_lane(int g) {
+  if constexpr (BITS == 4) return g;
+  else return sigma8(g);
+}
 
 template <int BITS>
 __device__ __forceinline__ int storage_of_code(int j) {
+  const int g = (j >> 3) & 3;
   if constexpr (BITS == 4) return (j & ~7) | slot4_of_code(j & 7);
-  else return j;
+  else return (j & ~31) | (sigma8(g) << 3) | (j & 7);
 }
 template <int BITS>
 __device__ __forceinline__ int code_of_storage(int q) {
+  const int g = (q >> 3) & 3;
   if constexpr (BITS == 4) return (q & ~7) | perm4_of_slot(q & 7);
-  else return q;
+  else return (q & ~31) | (sigma8(g) << 3) | (q & 7);
 }
 
 // Split fp32 into f16 hi + lo.
@@ -97,6 +111,41 @@ __device__ __forceinline__ f16x8 unpack8x2(uint32_t d0, uint32_t d1) {
 
 __device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Cross-lane exchanges between the four 16-lane row groups of a wavefront
+// (gfx950 v_permlane32_swap / v_permlane16_swap).
+//   swap32(x, y): lanes 32..63 of x trade places with lanes 0..31 of y.
+//   swap16(x, y): rows 1 and 3 of x trade places with rows 0 and 2 of y.
+__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+
+// 4x4 transpose of dwords across row groups: afterwards row group g holds in
+// register j what row group j held in register g.
+__device__ __forceinline__ void transpose4x4(u32x4& v) {
+  uint32_t d0 = v[0], d1 = v[1], d2 = v[2], d3 = v[3];
+  swap32(d0, d2);
+  swap32(d1, d3);
+  swap16(d0, d1);
+  swap16(d2, d3);
+  v = u32x4{d0, d1, d2, d3};
+}
+
+// Exchange of dword pairs between row groups {0,1} and {2,3}: row group g's
+// registers (2,3) trade places with row group (g+2)'s registers (0,1).
+__device__ __forceinline__ void swap_pairs(u32x4& v) {
+  uint32_t d0 = v[0], d1 = v[1], d2 = v[2], d3 = v[3];
+  swap32(d0, d2);
+  swap32(d1, d3);
+  v = u32x4{d0, d1, d2, d3};
 }
 
 // Wave-wide helpers.

@@ -25,13 +25,10 @@
 
 namespace qmoe {
 
-// Scale modes
-enum { SC_COL = 0, SC_BLOCK = 1, SC_BLOCK16 = 2 };
-
 constexpr int kNT = 4;     // 16-row weight subtiles per wavefront
 constexpr int kWaves = 4;  // wavefronts per workgroup
 
-// Eight codes of weight row `row` starting at code c0 = 32*s + 8*grp, as
+// Eight codes of weight row `row` starting at code c0 = 32*s + 8*group, as
 // exact f16 (q - mid) in A-row storage order.  Codes at or beyond K read as 0
 // (their activation partner is zero padding).
 template <int BITS, bool ALIGNED>
@@ -116,7 +113,7 @@ __global__ void __launch_bounds__(64 * kWaves) qmoe_gemm(GemmArgs g) {
       ahi[mt] = *(const f16x8*)ap;
       alo[mt] = *(const f16x8*)(ap + 16);
     }
-    const int c0 = s * 32 + grp * 8;
+    const int c0 = s * 32 + code_group_of_lane<BITS>(grp) * 8;
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       const f16x8 b = load_b<BITS, ALIGNED>(brow[nt], c0, g.K);
@@ -131,7 +128,7 @@ __global__ void __launch_bounds__(64 * kWaves) qmoe_gemm(GemmArgs g) {
         } else {
           // 16-code scale blocks: code groups 0,1 and 2,3 of a step belong to
           // different blocks; split the step by masking the activation side.
-          const bool first = grp < 2;
+          const bool first = code_group_of_lane<BITS>(grp) < 2;
           const f16x8 h0 = first ? ahi[mt] : zero8, l0 = first ? alo[mt] : zero8;
           const f16x8 h1 = first ? zero8 : ahi[mt], l1 = first ? zero8 : alo[mt];
           blk[mt][nt] = mfma16(h0, b, blk[mt][nt]);
@@ -262,11 +259,13 @@ hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& 
   return hipGetLastError();
 }
 
-// out[t, h] = sum_s w[t, s] * slot_out[t*k + s, h], s ascending, fp32.
+// out[t, h] = sum_s w[t, s] * (sum_z slot_out[z][t*k + s, h]); z then s
+// ascending, fp32.  One writer per output element, no atomics.
 __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ slot_out,
                                                     const float* __restrict__ topk_w, int T, int k, int H,
-                                                    float* __restrict__ out) {
+                                                    int splits, float* __restrict__ out) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long S = (long)T * k;
   if ((H & 3) == 0) {
     const long n4 = (long)T * H / 4;
     if (i >= n4) return;
@@ -275,7 +274,8 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < k; ++s) {
       const float w = topk_w[t * k + s];
-      const f32x4 y = *(const f32x4*)(slot_out + (t * k + s) * H + h);
+      f32x4 y = *(const f32x4*)(slot_out + (t * k + s) * H + h);
+      for (int z = 1; z < splits; ++z) y += *(const f32x4*)(slot_out + ((long)z * S + t * k + s) * H + h);
       acc += w * y;
     }
     *(f32x4*)(out + t * H + h) = acc;
@@ -284,15 +284,19 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
     const long t = i / H;
     const int h = (int)(i % H);
     float acc = 0.f;
-    for (int s = 0; s < k; ++s) acc += topk_w[t * k + s] * slot_out[(t * k + s) * H + h];
+    for (int s = 0; s < k; ++s) {
+      float y = slot_out[(t * k + s) * H + h];
+      for (int z = 1; z < splits; ++z) y += slot_out[((long)z * S + t * k + s) * H + h];
+      acc += topk_w[t * k + s] * y;
+    }
     out[t * H + h] = acc;
   }
 }
 
-hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, float* out,
+hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, int splits, float* out,
                           hipStream_t st) {
   const long n = (H & 3) == 0 ? (long)T * H / 4 : (long)T * H;
-  hipLaunchKernelGGL(qmoe_combine, dim3((n + 255) / 256), dim3(256), 0, st, slot_out, topk_w, T, k, H, out);
+  hipLaunchKernelGGL(qmoe_combine, dim3((n + 255) / 256), dim3(256), 0, st, slot_out, topk_w, T, k, H, splits, out);
   return hipGetLastError();
 }
 

@@ -27,19 +27,36 @@ struct GemmArgs {
   const int* tiles;     // [max_tiles][4] = expert, first position, rows, 0
   const int* ntiles;
   int N, K, kb, nblk, bs;
+  int chunks_per_split;  // stream kernel: 64-byte row chunks per K range (blockIdx.z)
+  int rb_per_group;      // stream kernel: row blocks per workgroup (blockIdx.y)
+  int store_by_slot;     // stream kernel: partial rows by slot id (1) or by sorted position (0)
+  int S;                 // slots (stride between split partials, in rows)
   // epilogue
   uint8_t* act;         // FC1 output rows, stride act_stride bytes
   long act_stride;
-  float* slot_out;      // FC2 output [S][N] by slot id
+  float* slot_out;      // FC2 output [splits][S][N] by slot id
   const int* perm;      // FC2: sorted position -> slot
   float alpha, beta;
 };
 
 enum { EPI_RELU = 0, EPI_SWIGLU = 1, EPI_STORE = 2 };
 
+// Scale modes: column-wise, blocks of >= 32 codes, blocks of 16 codes.
+enum { SC_COL = 0, SC_BLOCK = 1, SC_BLOCK16 = 2 };
+
 hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& g, int max_tiles, hipStream_t st);
 
-hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, float* out,
+// Weight-streaming variant for small token counts (see stream.hip): writes fp32
+// partial rows part[z][row][N] for K ranges z < splits.
+hipError_t launch_stream(int bits, int mt, int nt, int cpi, int splits, int rb_groups, const GemmArgs& g,
+                         int max_tiles, hipStream_t st);
+
+// Sum FC1 partials over K ranges, apply the activation, write FC2 operand rows.
+hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,
+                      float beta, uint8_t* act, hipStream_t st);
+
+// out[t, h] = sum_s w[t, s] * sum_z slot_out[z][t*k + s][h]  (fixed order)
+hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, int splits, float* out,
                           hipStream_t st);
 
 hipError_t launch_fill_zero(float* out, long n, hipStream_t st);

@@ -45,8 +45,8 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
   for (const qmoe_tensor* t : all)
     if (numel(t) > 0 && t->data == nullptr) return QMOE_ERR_NULL;
   if (!aligned_to(input->data, 16) || !aligned_to(output->data, 16) || !aligned_to(fc1w->data, 16) ||
-      !aligned_to(fc2w->data, 16) || !aligned_to(router->data, 4) || !aligned_to(fc1s->data, 4) ||
-      !aligned_to(fc2s->data, 4))
+      !aligned_to(fc2w->data, 16) || !aligned_to(router->data, 4) || !aligned_to(fc1s->data, 16) ||
+      !aligned_to(fc2s->data, 16))
     return QMOE_ERR_ALIGN;
   if (p.bytes > 0) {
     if (workspace == nullptr) return QMOE_ERR_NULL;
@@ -107,8 +107,19 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g1.act_stride = 4 * p.kp2;
     g1.alpha = d.alpha;
     g1.beta = d.beta;
-    QMOE_TRY_HIP(launch_gemm(d.bits, d.act == QMOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU, p.mt, p.aligned, g1,
-                             (int)p.max_tiles, s));
+    g1.S = S;
+    const int epi1 = d.act == QMOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
+    if (p.s1.on) {
+      float* part1 = reinterpret_cast<float*>(ws + p.off_part1);
+      g1.chunks_per_split = (int)p.s1.cps;
+      g1.rb_per_group = p.s1.rb_per_group;
+      g1.store_by_slot = 0;
+      g1.slot_out = part1;
+      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.nt, p.s1.cpi, p.s1.splits, p.s1.rb_groups, g1, (int)p.max_tiles, s));
+      QMOE_TRY_HIP(launch_act(d.bits, epi1, part1, p.s1.splits, S, (int)d.F, I, (int)p.kp2, d.alpha, d.beta, act, s));
+    } else {
+      QMOE_TRY_HIP(launch_gemm(d.bits, epi1, p.mt, p.aligned, g1, (int)p.max_tiles, s));
+    }
     QMOE_TRY_HIP(mark(2));
     GemmArgs g2{};
     g2.wq = static_cast<const uint8_t*>(fc2w->data);
@@ -126,9 +137,17 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g2.bs = (int)d.bs;
     g2.slot_out = slot;
     g2.perm = perm;
-    QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
+    g2.S = S;
+    if (p.s2.on) {
+      g2.chunks_per_split = (int)p.s2.cps;
+      g2.rb_per_group = p.s2.rb_per_group;
+      g2.store_by_slot = 1;
+      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.nt, p.s2.cpi, p.s2.splits, p.s2.rb_groups, g2, (int)p.max_tiles, s));
+    } else {
+      QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
+    }
     QMOE_TRY_HIP(mark(3));
-    QMOE_TRY_HIP(launch_combine(slot, topk_w, T, k, H, out, s));
+    QMOE_TRY_HIP(launch_combine(slot, topk_w, T, k, H, p.splits2, out, s));
     QMOE_TRY_HIP(mark(4));
   }
   if (dbg) {

@@ -15,6 +15,15 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// The streaming kernel needs whole 64-byte row chunks and scale blocks of at
+// least one 32-code matrix step.
+bool stream_ok(int bits, int64_t K, int64_t bs) {
+  const int64_t cc = bits == 4 ? 128 : 64;
+  return K > 0 && K % cc == 0 && (bs == 0 || bs >= 32);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 bool rank_ok(const qmoe_tensor* t, int r) { return t->rank == r; }
 
 }  // namespace
@@ -120,7 +129,37 @@ void make_plan(const Dims& d, Plan* p) {
   p->kp2 = round_up(d.I, 128);
   p->aligned = (d.H % 8 == 0) && (d.I % 8 == 0);
   p->nchunks = (p->S + p->chunk - 1) / p->chunk;
-
+  if (p->decode && d.I > 0) {
+    const int64_t cc = d.bits == 4 ? 128 : 64;
+    // K range: the tile's activation rows for it must fit 64 KB of LDS.
+    const int64_t cps_max = 65536 / (16 * p->mt * cc * 4);
+    const int64_t used = d.E < p->S ? d.E : p->S;  // experts that can receive rows
+    auto shape = [&](Plan::Stream& st, int64_t K, int64_t N) {
+      st.on = stream_ok(d.bits, K, d.bs) && cps_max >= 1;
+      if (!st.on) return;
+      const int64_t nch = K / cc;
+      // Items of two chunks cover whole 128-byte lines of every weight row.
+      st.cpi = (nch % 2 == 0 && cps_max >= 2) ? 2 : 1;
+      const int64_t nit = nch / st.cpi;
+      const int64_t ipr_max = cps_max / st.cpi;
+      st.splits = (int)ceil_div(nit, ipr_max);
+      const int64_t ipr = ceil_div(nit, st.splits);
+      st.cps = ipr * st.cpi;
+      st.splits = (int)ceil_div(nch, st.cps);
+      st.nt = 2;  // 32 rows per wavefront keeps the load ring within 128 VGPRs
+      const int64_t nrb = ceil_div(N, 8 * 16 * st.nt);  // 8 wavefronts per workgroup
+      // Row blocks per workgroup: about kWgTarget workgroups per launch.
+      constexpr int64_t kWgTarget = 1024;
+      int64_t rpg = ceil_div(used * nrb * st.splits, kWgTarget);
+      if (rpg < 1) rpg = 1;
+      if (rpg > nrb) rpg = nrb;
+      st.rb_per_group = (int)rpg;
+      st.rb_groups = (int)ceil_div(nrb, rpg);
+    };
+    shape(p->s1, d.H, d.F);
+    shape(p->s2, d.I, d.H);
+    if (p->s2.on) p->splits2 = p->s2.splits;
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   p->off_topk_idx = take(sizeof(int32_t) * p->S);
@@ -133,7 +172,8 @@ void make_plan(const Dims& d, Plan* p) {
   p->off_hist = take(sizeof(int32_t) * p->nchunks * d.E);
   p->off_xa = take(size_t(4) * d.T * p->kp1);     // f16 hi + lo per element
   p->off_act = take(size_t(4) * p->S * p->kp2);   // f16 hi + lo per element
-  p->off_slot = take(d.I > 0 ? sizeof(float) * p->S * d.H : 0); // FC2 rows by slot id
+  p->off_slot = take(d.I > 0 ? sizeof(float) * p->splits2 * p->S * d.H : 0); // FC2 rows by slot id
+  p->off_part1 = take(p->s1.on ? sizeof(float) * p->s1.splits * p->S * d.F : 0);
   p->bytes = o;
 }
 

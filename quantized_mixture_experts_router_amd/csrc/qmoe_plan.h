@@ -45,6 +45,18 @@ struct Plan {
   int64_t max_tiles = 0; // ceil(S / bm) + E
   int64_t kp1 = 0, kp2 = 0;  // padded reduction lengths of the A operands (codes)
   bool aligned = true;   // packed rows allow vector loads
+  // weight-streaming kernels (decode): used per GEMM when its shapes allow
+  struct Stream {
+    bool on = false;
+    int nt = 4;          // 16-row weight subtiles per wavefront
+    int cpi = 1;         // 64-byte chunks per streamed item (2 = whole 128-byte lines)
+    int splits = 1;      // K ranges (fp32 partials summed afterwards, in order)
+    int64_t cps = 0;     // 64-byte chunks per K range
+    int rb_per_group = 1;
+    int rb_groups = 1;
+  } s1, s2;
+  int splits2 = 1;       // FC2 partial sets the combine sums (1 off the stream path)
+  size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path)
   int64_t chunk = 1024;  // slots per permutation block
   int64_t nchunks = 0;
   // workspace layout

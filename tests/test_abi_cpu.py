@@ -143,7 +143,8 @@ def test_workspace_size_covers_intermediates(lib):
                                    fake["fc1_scales"], fake["fc2_experts_weights"], fake["fc2_scales"], w.attrs())
         S = w.tokens * w.k
         assert n >= 4 * S * w.hidden + 4 * S * w.inter + 4 * w.tokens * w.hidden
-        assert n < 3 * (4 * S * w.hidden + 4 * S * w.inter + 4 * w.tokens * w.hidden) + (1 << 20)
+        # plus split-K partials on the weight-streaming path (a few MB at decode sizes)
+        assert n < 3 * (4 * S * w.hidden + 4 * S * w.inter + 4 * w.tokens * w.hidden) + (64 << 20)
 
 
 def test_null_arguments(lib):
