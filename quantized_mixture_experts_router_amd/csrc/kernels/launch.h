@@ -27,8 +27,6 @@ struct GemmArgs {
   const int* tiles;     // [max_tiles][4] = expert, first position, rows, 0
   const int* ntiles;
   int N, K, kb, nblk, bs;
-  int chunks_per_split;  // stream kernel: 64-byte row chunks per K range (blockIdx.z)
-  int rb_per_group;      // stream kernel: row blocks per workgroup (blockIdx.y)
   int store_by_slot;     // stream kernel: partial rows by slot id (1) or by sorted position (0)
   int S;                 // slots (stride between split partials, in rows)
   // epilogue
@@ -47,9 +45,10 @@ enum { SC_COL = 0, SC_BLOCK = 1, SC_BLOCK16 = 2 };
 hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& g, int max_tiles, hipStream_t st);
 
 // Weight-streaming variant for small token counts (see stream.hip): writes fp32
-// partial rows part[z][row][N] for K ranges z < splits.
-hipError_t launch_stream(int bits, int mt, int nt, int cpi, int splits, int rb_groups, const GemmArgs& g,
-                         int max_tiles, hipStream_t st);
+// partial rows part[z][row][N] for K ranges z < splits of `items` 128-byte
+// row items each; workgroups stream rbw row blocks (mt == 1 only).
+hipError_t launch_stream(int bits, int mt, int items, int rbw, int splits, const GemmArgs& g, int max_tiles,
+                         hipStream_t st);
 
 // Sum FC1 partials over K ranges, apply the activation, write FC2 operand rows.
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,

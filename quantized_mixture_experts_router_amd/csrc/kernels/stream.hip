@@ -7,21 +7,26 @@
 // WebGPU manifest's description and derive.quantMidpoint state), organised so
 // that packed weights leave HBM exactly once, in long coalesced runs:
 //
-//  * a workgroup owns one expert tile, one K range (blockIdx.z) and a group of
-//    row blocks (blockIdx.y); it stages the tile's activation rows for its K
-//    range in LDS once;
-//  * each wavefront streams (row block, CPI 64-byte chunks) items: 16*NT
-//    weight rows, lane (n, g) loading 16 contiguous bytes of row n per chunk,
-//    so an item covers whole 128-byte lines; P items of loads are in flight in
-//    a register ring that runs across row blocks;
+//  * a workgroup owns one expert tile (blockIdx.x), RBW blocks of 32 weight
+//    rows per wavefront (blockIdx.y) and one K range (blockIdx.z); it stages
+//    the tile's activation rows for that K range in LDS once and streams its
+//    row blocks one after another;
+//  * each wavefront streams ITEMS items of 16*NT weight rows x 128 bytes
+//    (whole cache lines), lane (n, g) loading 16 bytes of row n from each
+//    64-byte half; the item loop is fully unrolled and the next kP items'
+//    loads are in flight while one item is consumed, so every wait is exact;
 //  * a cross-lane exchange (v_permlane32/16_swap) puts each lane's bytes in
 //    the matrix-core operand position; bytes are unpacked to exact f16
 //    (q - mid) in registers and multiplied by the f16 hi and lo parts of the
 //    activations on v_mfma_f32_16x16x32_f16 (fp32 accumulation);
-//  * scales travel in the same ring and are applied in fp32 at the end of each
-//    scale block;
-//  * fp32 partial rows go to part[z]; qmoe_act (FC1) and the combine (FC2)
-//    sum the K ranges in a fixed order, so nothing uses atomics.
+//  * block scales travel in the ring with the weights and are applied in fp32
+//    at the end of each scale block;
+//  * fp32 partial rows of all row blocks are stored once, after the stream
+//    (no stores interleave with the weight loads); qmoe_act (FC1) and the
+//    combine (FC2) sum the K ranges in a fixed order (no atomics).
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.h"
 
@@ -30,12 +35,18 @@ namespace qmoe {
 namespace {
 
 constexpr int kSWaves = 8;  // wavefronts per workgroup
+constexpr int kCPI = 2;     // 64-byte chunks per item (one 128-byte line per row)
+constexpr int kP = 2;       // items of loads in flight per wavefront while one is consumed
 
 template <int BITS>
 __device__ __forceinline__ f16x8 chunk_operand(const u32x4& v, int j) {
   if constexpr (BITS == 4) return unpack4(v[j]);
   else return unpack8x2(v[2 * j], v[2 * j + 1]);
 }
+
+// Keep a scale-block flush where it is written: without this the compiler may
+// sink every "acc += blk * scale" to the end and keep all block partials live.
+__device__ __forceinline__ void pin(f32x4& v) { asm volatile("" : "+v"(v)); }
 
 template <int BITS>
 __device__ __forceinline__ void exchange(u32x4& v) {
@@ -46,42 +57,56 @@ __device__ __forceinline__ void exchange(u32x4& v) {
 }  // namespace
 
 // SPB: MFMA steps per scale block when blocks end inside a chunk; 0 when the
-// scales are column-wise or a block spans whole chunks.
-// CPI: 64-byte chunks per streamed item (2 = whole 128-byte lines per row).
-template <int BITS, int MT, int NT, int P, int SCALE, int SPB, int CPI>
-__global__ void __launch_bounds__(64 * kSWaves, 2) qmoe_stream(GemmArgs g) {
-  constexpr int CC = BITS == 4 ? 128 : 64;     // codes per 64-byte chunk
-  constexpr int NS = CC / 32;                  // MFMA steps per chunk
-  constexpr int NSC = SPB > 0 ? NS / SPB : 1;  // scale blocks ending per chunk
-  constexpr int NSI = NSC * CPI;               // scales per item and row
+// scales are column-wise or a block spans whole chunks.  RBW: row blocks of
+// kSWaves*16*NT rows that the workgroup streams one after another (the staged
+// activations are reused for all of them).
+template <int BITS, int MT, int NT, int ITEMS, int SCALE, int SPB, int RBW>
+__global__ void __launch_bounds__(64 * kSWaves) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2, MT == 1 ? 4 : 2)))
+qmoe_stream(GemmArgs g) {
+  constexpr int CC = BITS == 4 ? 128 : 64;      // codes per 64-byte chunk
+  constexpr int NS = CC / 32;                   // MFMA steps per chunk
+  constexpr int NSC = SPB > 0 ? NS / SPB : 1;   // scale blocks ending per chunk
+  constexpr int NSI = NSC * kCPI;               // scales per item and row
   constexpr int ROWS = 16 * MT;
-  extern __shared__ __align__(16) uint8_t lds[];
+  constexpr int NCHR = ITEMS * kCPI;            // chunks in the K range
+  constexpr int LSTRIDE = NCHR * CC * 4;        // LDS bytes per activation row
+  constexpr int PIECES = LSTRIDE / 16;          // 16-byte pieces per row
+  constexpr int PPT = ROWS * PIECES / (64 * kSWaves);  // pieces per thread
+  static_assert(ROWS * PIECES % (64 * kSWaves) == 0, "staging must divide evenly");
+  constexpr int WROWS = kSWaves * 16 * NT;      // weight rows of one row block
+  constexpr int NITEMS = RBW * ITEMS;           // items streamed by each wavefront
+  extern __shared__ __align__(16) uint8_t lds[];  // [ROWS][LSTRIDE] activations
+  __shared__ long s_rowbase[ROWS];
 
   const int tile = blockIdx.x;
   if (tile >= g.ntiles[0]) return;
   const int e = g.tiles[4 * tile + 0];
   const int p0 = g.tiles[4 * tile + 1];
   const int rows = g.tiles[4 * tile + 2];
-  const int nch = g.K / CC;
-  const int c0 = blockIdx.z * g.chunks_per_split;
-  const int c1 = min(nch, c0 + g.chunks_per_split);
-  if (c0 >= c1) return;
-  const int nchr = c1 - c0;
-  // LDS row r holds the K range's 16-byte pieces with the piece index XOR-ed
-  // by (r & 15), so the 16 rows read by one instruction hit distinct banks.
-  const int lstride = nchr * CC * 4;
+  const int c0 = blockIdx.z * NCHR;
 
-  // Stage activation rows [p0, p0 + ROWS) (clamped to valid rows) for codes of
-  // chunks [c0, c1) into LDS, 16 bytes per thread per pass.
+  // Stage activation rows [p0, p0 + ROWS) (clamped to valid rows) for the K
+  // range into LDS.  Row r keeps its 16-byte pieces with the piece index XOR-ed
+  // by (r & 15), so the 16 rows read by one instruction hit distinct banks.
+  if (threadIdx.x < ROWS) {
+    const int p = p0 + min((int)threadIdx.x, rows - 1);
+    const long ar = g.a_map ? (long)(g.a_map[p] / g.a_div) : (long)p;
+    s_rowbase[threadIdx.x] = ar * g.a_stride + (long)c0 * CC * 4;
+  }
+  __syncthreads();
   {
-    const int pieces = nchr * CC * 4 / 16;  // 16-byte pieces per row
-    for (int i = threadIdx.x; i < ROWS * pieces; i += 64 * kSWaves) {
-      const int r = i / pieces;
-      const int q = i - r * pieces;
-      const int p = p0 + min(r, rows - 1);
-      const long ar = g.a_map ? (long)(g.a_map[p] / g.a_div) : (long)p;
-      const u32x4 v = *(const u32x4*)(g.a + ar * g.a_stride + (long)c0 * CC * 4 + q * 16);
-      *(u32x4*)(lds + r * lstride + ((q ^ (r & 15)) * 16)) = v;
+    u32x4 v[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int idx = threadIdx.x + i * 64 * kSWaves;
+      const int r = idx / PIECES, q = idx % PIECES;
+      v[i] = *(const u32x4*)(g.a + s_rowbase[r] + q * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int idx = threadIdx.x + i * 64 * kSWaves;
+      const int r = idx / PIECES, q = idx % PIECES;
+      *(u32x4*)(lds + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = v[i];
     }
   }
   __syncthreads();
@@ -90,21 +115,15 @@ __global__ void __launch_bounds__(64 * kSWaves, 2) qmoe_stream(GemmArgs g) {
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int rb_rows = kSWaves * 16 * NT;              // rows per row block
-  const int rg0 = blockIdx.y * g.rb_per_group;        // first row block of this group
-  // row blocks of this wave that start inside N form a prefix
-  int nrb = 0;
-  for (int rb = 0; rb < g.rb_per_group; ++rb)
-    if ((rg0 + rb) * rb_rows + wave * 16 * NT < g.N) nrb = rb + 1;
-  const int ipr = nchr / CPI;  // items per row block (K ranges are whole items)
-  const int items = nrb * ipr;
-  if (items == 0) return;
-
+  // This wavefront's rows in row block r: rb0 + r * WROWS + nt * 16 + col.
+  const int rb0 = blockIdx.y * RBW * WROWS + wave * 16 * NT;
+  if (rb0 >= g.N) return;
   const long ebase = (long)e * g.N;
-  auto row_of = [&](int rb, int nt) { return min((rg0 + rb) * rb_rows + wave * 16 * NT + nt * 16 + col, g.N - 1); };
+  const long kb_bytes = g.kb;
 
   f32x4 acc[MT][NT];
   f32x4 blk[MT][NT];
+  f32x4 res[RBW][MT][NT];  // finished row blocks, stored after the stream
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -114,22 +133,22 @@ __global__ void __launch_bounds__(64 * kSWaves, 2) qmoe_stream(GemmArgs g) {
       blk[mt][nt] = zero4;
     }
 
-  u32x4 bq[P][NT][CPI];
-  float sq[P][NT][NSI];
-  auto issue = [&](int slot, int it) {
-    const int rb = it / ipr;
-    const int c = c0 + (it - rb * ipr) * CPI;
+  // Ring of kP items in flight: packed weights and the scales they need.
+  u32x4 bq[kP][NT][kCPI];
+  float sq[kP][NT][NSI];
+  auto issue = [&](int slot, int it) {  // it is a compile-time constant after unrolling
+    const int r = it / ITEMS, il = it % ITEMS;
+    const int c = c0 + il * kCPI;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const long row = ebase + row_of(rb, nt);
-      const uint8_t* src = g.wq + row * g.kb + grp * 16 + (long)c * 64;
+      const long row = ebase + min(rb0 + r * WROWS + nt * 16 + col, g.N - 1);
+      const uint8_t* src = g.wq + row * kb_bytes + grp * 16 + (long)c * 64;
 #pragma unroll
-      for (int h = 0; h < CPI; ++h) bq[slot][nt][h] = *(const u32x4*)(src + h * 64);
+      for (int h = 0; h < kCPI; ++h) bq[slot][nt][h] = *(const u32x4*)(src + h * 64);
       if constexpr (SCALE != SC_COL) {
         const float* sr = g.ws + row * g.nblk;
         if constexpr (SPB > 0) {
-          // NSI consecutive block scales starting at this item's first block
-          const float* sp = sr + (c * CC) / g.bs;
+          const float* sp = sr + (c * CC) / (SPB * 32);  // NSI consecutive block scales
           if constexpr (NSI == 4) {
             const f32x4 v = *(const f32x4*)sp;
 #pragma unroll
@@ -143,112 +162,136 @@ __global__ void __launch_bounds__(64 * kSWaves, 2) qmoe_stream(GemmArgs g) {
             for (int i = 0; i < NSI; ++i) sq[slot][nt][i] = sp[i];
           }
         } else {
-          // blocks of whole chunks: the block scale of each chunk of the item
 #pragma unroll
-          for (int h = 0; h < CPI; ++h) sq[slot][nt][h] = sr[((c + h) * CC) / g.bs];
+          for (int h = 0; h < kCPI; ++h) sq[slot][nt][h] = sr[((c + h) * CC) / g.bs];
         }
       }
     }
   };
-#pragma unroll
-  for (int u = 0; u < P; ++u)
-    if (u < items) issue(u, u);
 
   const int cpb = (SCALE != SC_COL && SPB == 0) ? g.bs / CC : 1;  // chunks per scale block
   const uint8_t* lrow[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) lrow[mt] = lds + (mt * 16 + col) * lstride;
-  const int swz = col;  // (row & 15) of every row this lane reads
-
-  for (int i0 = 0; i0 < items; i0 += P) {
+  for (int mt = 0; mt < MT; ++mt) lrow[mt] = lds + (mt * 16 + col) * LSTRIDE;
+  // Swizzled piece q of row r sits at ((q & ~15) | ((q & 15) ^ r)) * 16.  The
+  // low four bits of q here are 8*(step parity) + 2*grp + (0 hi | 1 lo), so the
+  // runtime part of every activation address is one of four per-lane offsets.
+  int aoff[2][2];
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const int it = i0 + u;
-      if (it < items) {
-        const int rb = it / ipr;
-        const int il = it - rb * ipr;  // item index inside the K range
-        u32x4 cur[NT][CPI];
-        float scur[NT][NSI];
+  for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) aoff[jp][hl] = (((jp * 8 + grp * 2 + hl) ^ col) * 16);
+
+#pragma unroll
+  for (int u = 0; u < kP && u < NITEMS; ++u) issue(u, u);
+
+#pragma unroll
+  for (int it = 0; it < NITEMS; ++it) {
+    // keep each item's work in its own scheduling region (bounded live ranges)
+    __builtin_amdgcn_sched_barrier(0);
+    const int u = it % kP;
+    const int r = it / ITEMS, il = it % ITEMS;
+    u32x4 cur[NT][kCPI];
+    float scur[NT][NSI];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int h = 0; h < kCPI; ++h) cur[nt][h] = bq[u][nt][h];
+#pragma unroll
+      for (int i = 0; i < NSI; ++i) scur[nt][i] = sq[u][nt][i];
+    }
+    if (it + kP < NITEMS) issue(u, it + kP);
+#pragma unroll
+    for (int h = 0; h < kCPI; ++h) {
+      const int cl = il * kCPI + h;  // chunk index inside the K range
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) exchange<BITS>(cur[nt][h]);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        __builtin_amdgcn_sched_barrier(0);  // one step at a time: bounded live operands
+        f16x8 ahi[MT], alo[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int qhigh = ((cl * NS + j) * 8) & ~15;  // compile-time part of the piece index
+          ahi[mt] = *(const f16x8*)(lrow[mt] + qhigh * 16 + aoff[j & 1][0]);
+          alo[mt] = *(const f16x8*)(lrow[mt] + qhigh * 16 + aoff[j & 1][1]);
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
+          const f16x8 b = chunk_operand<BITS>(cur[nt][h], j);
 #pragma unroll
-          for (int h = 0; h < CPI; ++h) cur[nt][h] = bq[u][nt][h];
-#pragma unroll
-          for (int i = 0; i < NSI; ++i) scur[nt][i] = sq[u][nt][i];
-        }
-        if (it + P < items) issue(u, it + P);
-#pragma unroll
-        for (int h = 0; h < CPI; ++h) {
-          const int cl = il * CPI + h;  // chunk index inside the K range
-          const int c = c0 + cl;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) exchange<BITS>(cur[nt][h]);
-#pragma unroll
-          for (int j = 0; j < NS; ++j) {
-            f16x8 ahi[MT], alo[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const int q = (cl * NS + j) * 8 + grp * 2;  // 16-byte piece of the hi half
-              ahi[mt] = *(const f16x8*)(lrow[mt] + ((q ^ swz) * 16));
-              alo[mt] = *(const f16x8*)(lrow[mt] + (((q + 1) ^ swz) * 16));
-            }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              const f16x8 b = chunk_operand<BITS>(cur[nt][h], j);
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt) {
-                if constexpr (SCALE == SC_COL) {
-                  acc[mt][nt] = mfma16(ahi[mt], b, acc[mt][nt]);
-                  acc[mt][nt] = mfma16(alo[mt], b, acc[mt][nt]);
-                } else if constexpr (SPB > 0) {
-                  f32x4 t = mfma16(ahi[mt], b, (j % SPB == 0) ? zero4 : blk[mt][nt]);
-                  t = mfma16(alo[mt], b, t);
-                  if (j % SPB == SPB - 1) acc[mt][nt] += t * scur[nt][h * NSC + j / SPB];
-                  else blk[mt][nt] = t;
-                } else {
-                  blk[mt][nt] = mfma16(ahi[mt], b, blk[mt][nt]);
-                  blk[mt][nt] = mfma16(alo[mt], b, blk[mt][nt]);
-                }
+          for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (SCALE == SC_COL) {
+              acc[mt][nt] = mfma16(ahi[mt], b, acc[mt][nt]);
+              acc[mt][nt] = mfma16(alo[mt], b, acc[mt][nt]);
+            } else if constexpr (SPB > 0) {
+              if (j % SPB == 0) blk[mt][nt] = mfma16(ahi[mt], b, zero4);
+              else blk[mt][nt] = mfma16(ahi[mt], b, blk[mt][nt]);
+              blk[mt][nt] = mfma16(alo[mt], b, blk[mt][nt]);
+              if (j % SPB == SPB - 1) {
+                // block of SPB*32 codes ends inside the chunk: apply its scale
+                acc[mt][nt] += blk[mt][nt] * scur[nt][h * NSC + j / SPB];
+                pin(acc[mt][nt]);
               }
-            }
-          }
-          if constexpr (SCALE != SC_COL && SPB == 0) {
-            // end of a scale block, or end of this K range's share of one
-            if ((c + 1) % cpb == 0 || cl == nchr - 1) {
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                  acc[mt][nt] += blk[mt][nt] * scur[nt][h];
-                  blk[mt][nt] = zero4;
-                }
-            }
-          }
-        }
-        if (il == ipr - 1) {
-          // row block done: column scales, then fp32 partial rows
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const int n = (rg0 + rb) * rb_rows + wave * 16 * NT + nt * 16 + col;
-            float sc = 1.f;
-            if constexpr (SCALE == SC_COL) sc = g.ws[ebase + min(n, g.N - 1)];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-              for (int i2 = 0; i2 < 4; ++i2) {
-                const int r = mt * 16 + 4 * grp + i2;
-                if (r < rows && n < g.N) {
-                  const long prow = g.store_by_slot ? (long)g.perm[p0 + r] : (long)(p0 + r);
-                  g.slot_out[((long)blockIdx.z * g.S + prow) * g.N + n] = acc[mt][nt][i2] * sc;
-                }
-              }
-              acc[mt][nt] = zero4;
+            } else {
+              blk[mt][nt] = mfma16(ahi[mt], b, blk[mt][nt]);
+              blk[mt][nt] = mfma16(alo[mt], b, blk[mt][nt]);
             }
           }
         }
       }
+      if constexpr (SCALE != SC_COL && SPB == 0) {
+        // end of a scale block, or end of this K range's share of one
+        if ((c0 + cl + 1) % cpb == 0 || cl == NCHR - 1) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              acc[mt][nt] += blk[mt][nt] * scur[nt][h];
+              pin(acc[mt][nt]);
+              blk[mt][nt] = zero4;
+            }
+        }
+      }
+    }
+    if (il == ITEMS - 1) {
+      // row block r finished: keep it until the stream ends
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          res[r][mt][nt] = acc[mt][nt];
+          acc[mt][nt] = zero4;
+        }
     }
   }
+
+  // Output rows (slot ids or sorted positions), then column scales and the
+  // fp32 partial rows of every row block.
+  int orow[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = min(mt * 16 + 4 * grp + i, rows - 1);
+      orow[mt][i] = g.store_by_slot ? g.perm[p0 + rr] : p0 + rr;
+    }
+#pragma unroll
+  for (int r = 0; r < RBW; ++r)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = rb0 + r * WROWS + nt * 16 + col;
+      float sc = 1.f;
+      if constexpr (SCALE == SC_COL) sc = g.ws[ebase + min(n, g.N - 1)];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = mt * 16 + 4 * grp + i;
+          if (rr < rows && n < g.N)
+            g.slot_out[((long)blockIdx.z * g.S + orow[mt][i]) * g.N + n] = res[r][mt][nt][i] * sc;
+        }
+    }
 }
 
 // FC1 epilogue for the streamed path: sum the K-range partials of each
@@ -296,50 +339,73 @@ __global__ void __launch_bounds__(256) qmoe_act(const float* __restrict__ part, 
 
 namespace {
 
-template <int BITS, int MT, int NT, int SCALE, int SPB>
-void go(int cpi, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
-  if (cpi == 2)
-    hipLaunchKernelGGL((qmoe_stream<BITS, MT, NT, 2, SCALE, SPB, 2>), grid, dim3(64 * kSWaves), lds, st, g);
-  else
-    hipLaunchKernelGGL((qmoe_stream<BITS, MT, NT, 3, SCALE, SPB, 1>), grid, dim3(64 * kSWaves), lds, st, g);
-}
-
-template <int BITS, int MT, int NT>
-void pick_scale(int cpi, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
-  constexpr int CC = BITS == 4 ? 128 : 64;
-  if (g.bs == 0) return go<BITS, MT, NT, SC_COL, 0>(cpi, g, grid, lds, st);
-  if (g.bs >= CC) return go<BITS, MT, NT, SC_BLOCK, 0>(cpi, g, grid, lds, st);
-  if (g.bs == 32) return go<BITS, MT, NT, SC_BLOCK, 1>(cpi, g, grid, lds, st);
-  if constexpr (BITS == 4) {
-    if (g.bs == 64) return go<BITS, MT, NT, SC_BLOCK, 2>(cpi, g, grid, lds, st);
+template <int BITS, int MT, int NT, int ITEMS, int SCALE, int SPB, int RBW>
+hipError_t go(const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
+  auto kern = qmoe_stream<BITS, MT, NT, ITEMS, SCALE, SPB, RBW>;
+  // Dynamic LDS above the 64 KB default needs a per-kernel opt-in (host-side,
+  // no synchronisation); remember the largest size granted so far.
+  static std::atomic<size_t> granted{64 * 1024};
+  if (lds > granted.load()) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    granted.store(lds);
   }
+  hipLaunchKernelGGL(kern, grid, dim3(64 * kSWaves), lds, st, g);
+  return hipGetLastError();
 }
 
-template <int BITS, int NT>
-void pick_mt(int mt, int cpi, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
+template <int BITS, int MT, int NT, int ITEMS, int RBW>
+hipError_t pick_scale(const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr int CC = BITS == 4 ? 128 : 64;
+  if (g.bs == 0) return go<BITS, MT, NT, ITEMS, SC_COL, 0, RBW>(g, grid, lds, st);
+  if (g.bs >= CC) return go<BITS, MT, NT, ITEMS, SC_BLOCK, 0, RBW>(g, grid, lds, st);
+  if (g.bs == 32) return go<BITS, MT, NT, ITEMS, SC_BLOCK, 1, RBW>(g, grid, lds, st);
+  if constexpr (BITS == 4) {
+    if (g.bs == 64) return go<BITS, MT, NT, ITEMS, SC_BLOCK, 2, RBW>(g, grid, lds, st);
+  }
+  return hipErrorInvalidValue;  // scale layouts the planner never routes here
+}
+
+// Item counts per K range allowed by the 64 KB activation slice (16*MT rows,
+// 4 bytes a code, 256 or 128 codes an item).
+template <int BITS, int MT>
+constexpr int max_items() { return 65536 / (64 * MT * (BITS == 4 ? 256 : 128)); }
+
+template <int BITS, int MT, int RBW>
+hipError_t pick_items(int items, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr int MX = max_items<BITS, MT>();
+  if (items == 1) return pick_scale<BITS, MT, 2, 1, RBW>(g, grid, lds, st);
+  if constexpr (MX >= 2) if (items == 2) return pick_scale<BITS, MT, 2, 2, RBW>(g, grid, lds, st);
+  if constexpr (MX >= 4) if (items == 4) return pick_scale<BITS, MT, 2, 4, RBW>(g, grid, lds, st);
+  if constexpr (MX >= 8) if (items == 8) return pick_scale<BITS, MT, 2, 8, RBW>(g, grid, lds, st);
+  return hipErrorInvalidValue;
+}
+
+template <int BITS, int MT>
+hipError_t pick_rbw(int rbw, int items, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
+  if (rbw == 2) return pick_items<BITS, MT, 2>(items, g, grid, lds, st);
+  return pick_items<BITS, MT, 1>(items, g, grid, lds, st);
+}
+
+template <int BITS>
+hipError_t pick_mt(int mt, int rbw, int items, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
   switch (mt) {
-    case 1: return pick_scale<BITS, 1, NT>(cpi, g, grid, lds, st);
-    case 2: return pick_scale<BITS, 2, NT>(cpi, g, grid, lds, st);
-    case 3: return pick_scale<BITS, 3, NT>(cpi, g, grid, lds, st);
-    default: return pick_scale<BITS, 4, NT>(cpi, g, grid, lds, st);
+    case 1: return pick_rbw<BITS, 1>(rbw, items, g, grid, lds, st);
+    case 2: return pick_rbw<BITS, 2>(1, items, g, grid, lds, st);
+    case 3: return pick_rbw<BITS, 3>(1, items, g, grid, lds, st);
+    default: return pick_rbw<BITS, 4>(1, items, g, grid, lds, st);
   }
 }
 
 }  // namespace
 
-hipError_t launch_stream(int bits, int mt, int nt, int cpi, int splits, int rb_groups, const GemmArgs& g,
-                         int max_tiles, hipStream_t st) {
+hipError_t launch_stream(int bits, int mt, int items, int rbw, int splits, const GemmArgs& g, int max_tiles,
+                         hipStream_t st) {
   const int cc = bits == 4 ? 128 : 64;
-  const size_t lds = (size_t)16 * mt * g.chunks_per_split * cc * 4;
-  const dim3 grid(max_tiles, rb_groups, splits);
-  if (bits == 4) {
-    if (nt == 2) pick_mt<4, 2>(mt, cpi, g, grid, lds, st);
-    else pick_mt<4, 4>(mt, cpi, g, grid, lds, st);
-  } else {
-    if (nt == 2) pick_mt<8, 2>(mt, cpi, g, grid, lds, st);
-    else pick_mt<8, 4>(mt, cpi, g, grid, lds, st);
-  }
-  return hipGetLastError();
+  const int rows_per_wg = kSWaves * 16 * 2 * (mt == 1 ? rbw : 1);
+  const size_t lds = (size_t)16 * mt * items * kCPI * cc * 4;
+  const dim3 grid(max_tiles, (g.N + rows_per_wg - 1) / rows_per_wg, splits);
+  return bits == 4 ? pick_mt<4>(mt, rbw, items, g, grid, lds, st) : pick_mt<8>(mt, rbw, items, g, grid, lds, st);
 }
 
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,

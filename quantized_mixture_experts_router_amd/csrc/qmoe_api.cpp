@@ -111,11 +111,9 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     const int epi1 = d.act == QMOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
     if (p.s1.on) {
       float* part1 = reinterpret_cast<float*>(ws + p.off_part1);
-      g1.chunks_per_split = (int)p.s1.cps;
-      g1.rb_per_group = p.s1.rb_per_group;
       g1.store_by_slot = 0;
       g1.slot_out = part1;
-      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.nt, p.s1.cpi, p.s1.splits, p.s1.rb_groups, g1, (int)p.max_tiles, s));
+      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.items, p.s1.rbw, p.s1.splits, g1, (int)p.max_tiles, s));
       QMOE_TRY_HIP(launch_act(d.bits, epi1, part1, p.s1.splits, S, (int)d.F, I, (int)p.kp2, d.alpha, d.beta, act, s));
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, epi1, p.mt, p.aligned, g1, (int)p.max_tiles, s));
@@ -139,10 +137,8 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g2.perm = perm;
     g2.S = S;
     if (p.s2.on) {
-      g2.chunks_per_split = (int)p.s2.cps;
-      g2.rb_per_group = p.s2.rb_per_group;
       g2.store_by_slot = 1;
-      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.nt, p.s2.cpi, p.s2.splits, p.s2.rb_groups, g2, (int)p.max_tiles, s));
+      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.items, p.s2.rbw, p.s2.splits, g2, (int)p.max_tiles, s));
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
     }

@@ -6,6 +6,8 @@
 // quantBlockSizeOk, quantScalesOk, quantShapeOk and quantContract.
 #include "qmoe_plan.h"
 
+#include <algorithm>
+
 namespace qmoe {
 namespace {
 
@@ -15,11 +17,11 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// The streaming kernel needs whole 64-byte row chunks and scale blocks of at
+// The streaming kernel needs whole 128-byte row items and scale blocks of at
 // least one 32-code matrix step.
 bool stream_ok(int bits, int64_t K, int64_t bs) {
-  const int64_t cc = bits == 4 ? 128 : 64;
-  return K > 0 && K % cc == 0 && (bs == 0 || bs >= 32);
+  const int64_t item_codes = bits == 4 ? 256 : 128;
+  return K > 0 && K % item_codes == 0 && (bs == 0 || bs >= 32);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -130,34 +132,28 @@ void make_plan(const Dims& d, Plan* p) {
   p->aligned = (d.H % 8 == 0) && (d.I % 8 == 0);
   p->nchunks = (p->S + p->chunk - 1) / p->chunk;
   if (p->decode && d.I > 0) {
-    const int64_t cc = d.bits == 4 ? 128 : 64;
-    // K range: the tile's activation rows for it must fit 64 KB of LDS.
-    const int64_t cps_max = 65536 / (16 * p->mt * cc * 4);
-    const int64_t used = d.E < p->S ? d.E : p->S;  // experts that can receive rows
-    auto shape = [&](Plan::Stream& st, int64_t K, int64_t N) {
-      st.on = stream_ok(d.bits, K, d.bs) && cps_max >= 1;
+    const int64_t item_codes = d.bits == 4 ? 256 : 128;
+    // Items per K range: the tile's activation rows for the range (16*mt rows,
+    // 4 bytes a code) must fit 64 KB of LDS (two workgroups per compute unit),
+    // and the ranges must tile K exactly.
+    constexpr int64_t kLdsBudget = 64 * 1024;
+    auto lds_bytes = [&](int64_t items) { return 16 * p->mt * items * item_codes * 4; };
+    auto shape = [&](Plan::Stream& st, int64_t K) {
+      st.on = stream_ok(d.bits, K, d.bs);
       if (!st.on) return;
-      const int64_t nch = K / cc;
-      // Items of two chunks cover whole 128-byte lines of every weight row.
-      st.cpi = (nch % 2 == 0 && cps_max >= 2) ? 2 : 1;
-      const int64_t nit = nch / st.cpi;
-      const int64_t ipr_max = cps_max / st.cpi;
-      st.splits = (int)ceil_div(nit, ipr_max);
-      const int64_t ipr = ceil_div(nit, st.splits);
-      st.cps = ipr * st.cpi;
-      st.splits = (int)ceil_div(nch, st.cps);
-      st.nt = 2;  // 32 rows per wavefront keeps the load ring within 128 VGPRs
-      const int64_t nrb = ceil_div(N, 8 * 16 * st.nt);  // 8 wavefronts per workgroup
-      // Row blocks per workgroup: about kWgTarget workgroups per launch.
-      constexpr int64_t kWgTarget = 1024;
-      int64_t rpg = ceil_div(used * nrb * st.splits, kWgTarget);
-      if (rpg < 1) rpg = 1;
-      if (rpg > nrb) rpg = nrb;
-      st.rb_per_group = (int)rpg;
-      st.rb_groups = (int)ceil_div(nrb, rpg);
+      const int64_t nit = K / item_codes;
+      int ipr = 0;
+      for (int cand : {8, 4, 2, 1})
+        if (lds_bytes(cand) <= kLdsBudget && nit % cand == 0) { ipr = cand; break; }
+      st.on = ipr > 0;
+      st.items = ipr;
+      st.splits = (int)(nit / ipr);
+      // Two row blocks per workgroup amortise the activation staging; 32-code
+      // scale blocks need the registers for their scales instead.
+      st.rbw = (p->mt == 1 && d.bs != 32) ? 2 : 1;
     };
-    shape(p->s1, d.H, d.F);
-    shape(p->s2, d.I, d.H);
+    shape(p->s1, d.H);
+    shape(p->s2, d.I);
     if (p->s2.on) p->splits2 = p->s2.splits;
   }
   size_t o = 0;

@@ -48,12 +48,9 @@ struct Plan {
   // weight-streaming kernels (decode): used per GEMM when its shapes allow
   struct Stream {
     bool on = false;
-    int nt = 4;          // 16-row weight subtiles per wavefront
-    int cpi = 1;         // 64-byte chunks per streamed item (2 = whole 128-byte lines)
+    int items = 4;       // 128-byte row items per wavefront (one K range)
+    int rbw = 1;         // row blocks streamed per workgroup (register budget)
     int splits = 1;      // K ranges (fp32 partials summed afterwards, in order)
-    int64_t cps = 0;     // 64-byte chunks per K range
-    int rb_per_group = 1;
-    int rb_groups = 1;
   } s1, s2;
   int splits2 = 1;       // FC2 partial sets the combine sums (1 off the stream path)
   size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path)
