@@ -78,21 +78,21 @@ def stage_times(qm, call_debug, steps):
     """Average per-stage durations (ms) from HIP events recorded by the library."""
     hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
     evs = []
-    for _ in range(5):
+    for _ in range(6):
         e = ctypes.c_void_p()
         assert hip.hipEventCreate(ctypes.byref(e)) == 0
         evs.append(e)
-    sums = [0.0] * 4
+    sums = [0.0] * 5
     for _ in range(steps):
         call_debug([e.value for e in evs])
-        assert hip.hipEventSynchronize(evs[4]) == 0
-        for i in range(4):
+        assert hip.hipEventSynchronize(evs[5]) == 0
+        for i in range(5):
             ms = ctypes.c_float()
             assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[i], evs[i + 1]) == 0
             sums[i] += ms.value
     for e in evs:
         hip.hipEventDestroy(e)
-    return dict(zip(("routing", "fc1", "fc2", "combine"), [s / steps for s in sums]))
+    return dict(zip(("routing", "fc1", "fc1_act", "fc2", "combine"), [s / steps for s in sums]))
 
 
 def cpu_baseline(w, arrs):

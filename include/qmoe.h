@@ -97,7 +97,7 @@ typedef struct {
 } qmoe_attrs;
 
 /* Stage boundaries at which qmoe_forward_debug records events. */
-#define QMOE_STAGE_EVENTS 5
+#define QMOE_STAGE_EVENTS 6
 
 /* Optional outputs for parity checks and timing.  Any field may be NULL.
  * Device buffers: topk_idx, topk_w [T*k] (row t, slot s at t*k+s); counts
@@ -105,9 +105,10 @@ typedef struct {
  * position, stable within an expert).
  * events: caller-created hipEvent_t handles recorded on the stream at
  *   [0] before the router, [1] after the routing front end (router,
- *   permutation, operand preparation), [2] after FC1, [3] after FC2,
- *   [4] after the combine (before any debug copy).  Events are only recorded
- *   when T > 0 and I > 0. */
+ *   permutation, operand preparation), [2] after the FC1 GEMM, [3] after
+ *   the FC1 activation pass (where FC1 writes split partials; else equal to
+ *   [2]), [4] after the FC2 GEMM, [5] after the combine (before any debug
+ *   copy).  Events are only recorded when T > 0 and I > 0. */
 typedef struct {
   int32_t* topk_idx;
   float* topk_w;

@@ -41,7 +41,7 @@ class QmoeAttrs(ctypes.Structure):
                 ("quant_type", ctypes.c_int32)]
 
 
-QMOE_STAGE_EVENTS = 5
+QMOE_STAGE_EVENTS = 6
 
 
 class QmoeDebug(ctypes.Structure):

@@ -32,7 +32,7 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-]
+] + [f for f in os.environ.get("QMOE_EXTRA_CFLAGS", "").split() if f]
 
 
 def _hipcc() -> str:

@@ -74,22 +74,36 @@ __device__ __forceinline__ void split_f16(float v, _Float16& hi, _Float16& lo) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
+// Bit masks used by the unpackers, held in registers: gfx9 three-operand
+// instructions take no literal constants, so a mask in a VGPR lets
+// (d & mask) | exponent fuse into one v_and_or_b32.
+struct UnpackMasks {
+  uint32_t lo, hi, exp;
+};
+__device__ __forceinline__ UnpackMasks unpack_masks() {
+  UnpackMasks m{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+  asm volatile("" : "+v"(m.lo), "+v"(m.hi), "+v"(m.exp));
+  return m;
+}
+
 // 8 four-bit codes of one little-endian dword (code j in bits 4j..4j+3) ->
 // f16x8 in storage order (0,4,1,5,2,6,3,7), each value q - 8.
-__device__ __forceinline__ f16x8 unpack4(uint32_t d) {
+__device__ __forceinline__ f16x8 unpack4(uint32_t d, const UnpackMasks& m) {
   const f16x2 bias = {(_Float16)-1032.f, (_Float16)-1032.f};   // -(1024 + 8)
   const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const f16x2 bias16 = {(_Float16)-72.f, (_Float16)-72.f};     // -(64 + 8)
   const uint32_t d8 = d >> 8;
-  f16x2 p0 = as_h2((d & 0x000F000Fu) | 0x64006400u) + bias;                    // codes 0, 4
-  f16x2 p1 = as_h2((d & 0x00F000F0u) | 0x64006400u) * sixteenth + bias16;      // codes 1, 5
-  f16x2 p2 = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + bias;                   // codes 2, 6
-  f16x2 p3 = as_h2((d8 & 0x00F000F0u) | 0x64006400u) * sixteenth + bias16;     // codes 3, 7
+  f16x2 p0 = as_h2((d & m.lo) | m.exp) + bias;                    // codes 0, 4
+  f16x2 p1 = as_h2((d & m.hi) | m.exp) * sixteenth + bias16;      // codes 1, 5
+  f16x2 p2 = as_h2((d8 & m.lo) | m.exp) + bias;                   // codes 2, 6
+  f16x2 p3 = as_h2((d8 & m.hi) | m.exp) * sixteenth + bias16;     // codes 3, 7
   f16x8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
 }
+
+__device__ __forceinline__ f16x8 unpack4(uint32_t d) { return unpack4(d, UnpackMasks{0x000F000Fu, 0x00F000F0u, 0x64006400u}); }
 
 // 4 eight-bit codes (byte j = code j) -> two f16x2 in natural order, q - 128.
 __device__ __forceinline__ void unpack8(uint32_t d, f16x2& a, f16x2& b) {

@@ -7,8 +7,8 @@
 // WebGPU manifest's description and derive.quantMidpoint state), organised so
 // that packed weights leave HBM exactly once, in long coalesced runs:
 //
-//  * a workgroup owns one expert tile (blockIdx.x), RBW blocks of 32 weight
-//    rows per wavefront (blockIdx.y) and one K range (blockIdx.z); it stages
+//  * a workgroup owns one K range (blockIdx.x), one expert tile (blockIdx.y)
+//    and RBW blocks of 32 weight rows per wavefront (blockIdx.z); it stages
 //    the tile's activation rows for that K range in LDS once and streams its
 //    row blocks one after another;
 //  * each wavefront streams ITEMS items of 16*NT weight rows x 128 bytes
@@ -34,13 +34,29 @@ namespace qmoe {
 
 namespace {
 
+// Tunables (compile-time).
+#ifndef QMOE_STREAM_INFLIGHT
+#define QMOE_STREAM_INFLIGHT 2
+#endif
+#ifndef QMOE_STREAM_NT_LOADS
+#define QMOE_STREAM_NT_LOADS 0
+#endif
 constexpr int kSWaves = 8;  // wavefronts per workgroup
 constexpr int kCPI = 2;     // 64-byte chunks per item (one 128-byte line per row)
-constexpr int kP = 2;       // items of loads in flight per wavefront while one is consumed
+constexpr int kP = QMOE_STREAM_INFLIGHT;  // items of loads in flight per wavefront while one is consumed
+
+// Packed weights are read exactly once: optionally mark the loads streaming.
+__device__ __forceinline__ u32x4 load_weights(const uint8_t* p) {
+#if QMOE_STREAM_NT_LOADS
+  return __builtin_nontemporal_load((const u32x4*)p);
+#else
+  return *(const u32x4*)p;
+#endif
+}
 
 template <int BITS>
-__device__ __forceinline__ f16x8 chunk_operand(const u32x4& v, int j) {
-  if constexpr (BITS == 4) return unpack4(v[j]);
+__device__ __forceinline__ f16x8 chunk_operand(const u32x4& v, int j, const UnpackMasks& m) {
+  if constexpr (BITS == 4) return unpack4(v[j], m);
   else return unpack8x2(v[2 * j], v[2 * j + 1]);
 }
 
@@ -65,8 +81,6 @@ __global__ void __launch_bounds__(64 * kSWaves) __attribute__((amdgpu_waves_per_
 qmoe_stream(GemmArgs g) {
   constexpr int CC = BITS == 4 ? 128 : 64;      // codes per 64-byte chunk
   constexpr int NS = CC / 32;                   // MFMA steps per chunk
-  constexpr int NSC = SPB > 0 ? NS / SPB : 1;   // scale blocks ending per chunk
-  constexpr int NSI = NSC * kCPI;               // scales per item and row
   constexpr int ROWS = 16 * MT;
   constexpr int NCHR = ITEMS * kCPI;            // chunks in the K range
   constexpr int LSTRIDE = NCHR * CC * 4;        // LDS bytes per activation row
@@ -78,12 +92,110 @@ qmoe_stream(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];  // [ROWS][LSTRIDE] activations
   __shared__ long s_rowbase[ROWS];
 
-  const int tile = blockIdx.x;
+  // Block scales of the K range per weight row when blocks end inside a chunk
+  // (SPB > 0): NBR of them, Q per lane group.
+  constexpr int NBR = SPB > 0 ? NCHR * CC / (SPB * 32) : 4;
+  constexpr int Q = NBR / 4;
+  static_assert(SPB == 0 || (NBR % 4 == 0 && Q <= 8), "scale blocks per K range");
+
+  // Grid: x = K range (fastest, so the K ranges of the same weight rows are
+  // fetched by neighbouring workgroups at the same time), y = expert tile,
+  // z = group of RBW row blocks.
+  const int split = blockIdx.x;
+  const int tile = blockIdx.y;
+  const int rgroup = blockIdx.z;
   if (tile >= g.ntiles[0]) return;
   const int e = g.tiles[4 * tile + 0];
   const int p0 = g.tiles[4 * tile + 1];
   const int rows = g.tiles[4 * tile + 2];
-  const int c0 = blockIdx.z * NCHR;
+  const int c0 = split * NCHR;
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  // This wavefront's rows in row block r: rb0 + r * WROWS + nt * 16 + col.
+  const int rb0 = rgroup * RBW * WROWS + wave * 16 * NT;
+  const bool active = rb0 < g.N;  // all waves take part in the staging below
+  const long ebase = (long)e * g.N;
+  const long kb_bytes = g.kb;
+
+  // Per-subtile base pointers for row block 0; row block r adds r * WROWS rows
+  // (with RBW > 1 the rows of every block are in range: N is a multiple of
+  // RBW * WROWS).
+  const uint8_t* bbase[NT];
+  const float* sbase[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const long row = ebase + min(rb0 + nt * 16 + col, g.N - 1);
+    bbase[nt] = g.wq + row * kb_bytes + grp * 16 + (long)c0 * 64;
+    sbase[nt] = g.ws + row * g.nblk;
+    if constexpr (SPB > 0) sbase[nt] += (c0 * CC) / (SPB * 32) + grp * Q;  // this lane group's blocks
+  }
+  const long bstep = (long)WROWS * kb_bytes;  // bytes between row blocks
+  const long sstep = (long)WROWS * g.nblk;    // scales between row blocks
+
+  // Ring of kP items in flight: packed weights, plus the scales of blocks
+  // that span whole chunks.
+  u32x4 bq[kP][NT][kCPI];
+  float sq[kP][NT][kCPI];
+  auto issue = [&](int slot, int it) {  // it is a compile-time constant after unrolling
+    const int r = it / ITEMS, il = it % ITEMS;
+    const int c = c0 + il * kCPI;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint8_t* src = bbase[nt] + r * bstep + il * kCPI * 64;
+#pragma unroll
+      for (int h = 0; h < kCPI; ++h) bq[slot][nt][h] = load_weights(src + h * 64);
+      if constexpr (SCALE != SC_COL && SPB == 0) {
+        const float* sr = sbase[nt] + r * sstep;
+#pragma unroll
+        for (int h = 0; h < kCPI; ++h) sq[slot][nt][h] = sr[((c + h) * CC) / g.bs];
+      }
+    }
+  };
+  // Blocks that end inside chunks: each lane group loads Q consecutive block
+  // scales of its row once per row block (one coalesced 16-byte-class load);
+  // a block's scale is then fetched from the owning lane group by ds_bpermute.
+  float sreg[2][NT][Q];
+  auto issue_scales = [&](int r) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float* sp = sbase[nt] + r * sstep;
+#pragma unroll
+      for (int q4 = 0; q4 < Q; q4 += 4) {
+        if constexpr (Q >= 4) {
+          const f32x4 v = *(const f32x4*)(sp + q4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sreg[r & 1][nt][q4 + i] = v[i];
+        }
+      }
+      if constexpr (Q == 2) {
+        const float2 v = *(const float2*)sp;
+        sreg[r & 1][nt][0] = v.x;
+        sreg[r & 1][nt][1] = v.y;
+      } else if constexpr (Q == 1) {
+        sreg[r & 1][nt][0] = sp[0];
+      }
+    }
+  };
+
+  // Start the weight stream before the activation staging so that its latency
+  // overlaps the staging's dependent loads.
+  if (active) {
+    if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(0);
+#pragma unroll
+    for (int u = 0; u < kP && u < NITEMS; ++u) issue(u, u);
+  }
+  // Output rows (slot ids or sorted positions) for the epilogue.
+  int orow[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = min(mt * 16 + 4 * grp + i, rows - 1);
+      orow[mt][i] = g.store_by_slot ? g.perm[p0 + rr] : p0 + rr;
+    }
 
   // Stage activation rows [p0, p0 + ROWS) (clamped to valid rows) for the K
   // range into LDS.  Row r keeps its 16-byte pieces with the piece index XOR-ed
@@ -95,31 +207,24 @@ qmoe_stream(GemmArgs g) {
   }
   __syncthreads();
   {
+    // Only the tile's valid rows are staged; matrix rows beyond them read the
+    // last valid row (their results are discarded).
     u32x4 v[PPT];
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int idx = threadIdx.x + i * 64 * kSWaves;
       const int r = idx / PIECES, q = idx % PIECES;
-      v[i] = *(const u32x4*)(g.a + s_rowbase[r] + q * 16);
+      if (r < rows) v[i] = *(const u32x4*)(g.a + s_rowbase[r] + q * 16);
     }
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int idx = threadIdx.x + i * 64 * kSWaves;
       const int r = idx / PIECES, q = idx % PIECES;
-      *(u32x4*)(lds + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = v[i];
+      if (r < rows) *(u32x4*)(lds + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = v[i];
     }
   }
   __syncthreads();
-
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  // This wavefront's rows in row block r: rb0 + r * WROWS + nt * 16 + col.
-  const int rb0 = blockIdx.y * RBW * WROWS + wave * 16 * NT;
-  if (rb0 >= g.N) return;
-  const long ebase = (long)e * g.N;
-  const long kb_bytes = g.kb;
+  if (!active) return;
 
   f32x4 acc[MT][NT];
   f32x4 blk[MT][NT];
@@ -133,57 +238,24 @@ qmoe_stream(GemmArgs g) {
       blk[mt][nt] = zero4;
     }
 
-  // Ring of kP items in flight: packed weights and the scales they need.
-  u32x4 bq[kP][NT][kCPI];
-  float sq[kP][NT][NSI];
-  auto issue = [&](int slot, int it) {  // it is a compile-time constant after unrolling
-    const int r = it / ITEMS, il = it % ITEMS;
-    const int c = c0 + il * kCPI;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const long row = ebase + min(rb0 + r * WROWS + nt * 16 + col, g.N - 1);
-      const uint8_t* src = g.wq + row * kb_bytes + grp * 16 + (long)c * 64;
-#pragma unroll
-      for (int h = 0; h < kCPI; ++h) bq[slot][nt][h] = *(const u32x4*)(src + h * 64);
-      if constexpr (SCALE != SC_COL) {
-        const float* sr = g.ws + row * g.nblk;
-        if constexpr (SPB > 0) {
-          const float* sp = sr + (c * CC) / (SPB * 32);  // NSI consecutive block scales
-          if constexpr (NSI == 4) {
-            const f32x4 v = *(const f32x4*)sp;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sq[slot][nt][i] = v[i];
-          } else if constexpr (NSI == 2) {
-            const float2 v = *(const float2*)sp;
-            sq[slot][nt][0] = v.x;
-            sq[slot][nt][1] = v.y;
-          } else {
-#pragma unroll
-            for (int i = 0; i < NSI; ++i) sq[slot][nt][i] = sp[i];
-          }
-        } else {
-#pragma unroll
-          for (int h = 0; h < kCPI; ++h) sq[slot][nt][h] = sr[((c + h) * CC) / g.bs];
-        }
-      }
-    }
-  };
-
   const int cpb = (SCALE != SC_COL && SPB == 0) ? g.bs / CC : 1;  // chunks per scale block
+  // Swizzled piece q of row r sits at ((q & ~15) | ((q & 15) ^ (r & 15))) * 16.
+  // The low four bits of q here are 8*(step parity) + 2*grp + (0 hi | 1 lo),
+  // so the runtime part of every activation address is one of four per-lane
+  // offsets per row subtile.
   const uint8_t* lrow[MT];
+  int aoff[MT][2][2];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) lrow[mt] = lds + (mt * 16 + col) * LSTRIDE;
-  // Swizzled piece q of row r sits at ((q & ~15) | ((q & 15) ^ r)) * 16.  The
-  // low four bits of q here are 8*(step parity) + 2*grp + (0 hi | 1 lo), so the
-  // runtime part of every activation address is one of four per-lane offsets.
-  int aoff[2][2];
+  for (int mt = 0; mt < MT; ++mt) {
+    const int ar = min(mt * 16 + col, rows - 1);
+    lrow[mt] = lds + ar * LSTRIDE;
 #pragma unroll
-  for (int jp = 0; jp < 2; ++jp)
+    for (int jp = 0; jp < 2; ++jp)
 #pragma unroll
-    for (int hl = 0; hl < 2; ++hl) aoff[jp][hl] = (((jp * 8 + grp * 2 + hl) ^ col) * 16);
+      for (int hl = 0; hl < 2; ++hl) aoff[mt][jp][hl] = (((jp * 8 + grp * 2 + hl) ^ (ar & 15)) * 16);
+  }
 
-#pragma unroll
-  for (int u = 0; u < kP && u < NITEMS; ++u) issue(u, u);
+  const UnpackMasks um = unpack_masks();
 
 #pragma unroll
   for (int it = 0; it < NITEMS; ++it) {
@@ -192,14 +264,17 @@ qmoe_stream(GemmArgs g) {
     const int u = it % kP;
     const int r = it / ITEMS, il = it % ITEMS;
     u32x4 cur[NT][kCPI];
-    float scur[NT][NSI];
+    float scur[NT][kCPI];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int h = 0; h < kCPI; ++h) cur[nt][h] = bq[u][nt][h];
-#pragma unroll
-      for (int i = 0; i < NSI; ++i) scur[nt][i] = sq[u][nt][i];
+      for (int h = 0; h < kCPI; ++h) {
+        cur[nt][h] = bq[u][nt][h];
+        scur[nt][h] = sq[u][nt][h];
+      }
     }
+    if constexpr (SCALE == SC_BLOCK && SPB > 0)
+      if (il == 0 && r + 1 < RBW) issue_scales(r + 1);  // next row block's scales
     if (it + kP < NITEMS) issue(u, it + kP);
 #pragma unroll
     for (int h = 0; h < kCPI; ++h) {
@@ -213,12 +288,12 @@ qmoe_stream(GemmArgs g) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int qhigh = ((cl * NS + j) * 8) & ~15;  // compile-time part of the piece index
-          ahi[mt] = *(const f16x8*)(lrow[mt] + qhigh * 16 + aoff[j & 1][0]);
-          alo[mt] = *(const f16x8*)(lrow[mt] + qhigh * 16 + aoff[j & 1][1]);
+          ahi[mt] = *(const f16x8*)(lrow[mt] + qhigh * 16 + aoff[mt][j & 1][0]);
+          alo[mt] = *(const f16x8*)(lrow[mt] + qhigh * 16 + aoff[mt][j & 1][1]);
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const f16x8 b = chunk_operand<BITS>(cur[nt][h], j);
+          const f16x8 b = chunk_operand<BITS>(cur[nt][h], j, um);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             if constexpr (SCALE == SC_COL) {
@@ -230,7 +305,9 @@ qmoe_stream(GemmArgs g) {
               blk[mt][nt] = mfma16(alo[mt], b, blk[mt][nt]);
               if (j % SPB == SPB - 1) {
                 // block of SPB*32 codes ends inside the chunk: apply its scale
-                acc[mt][nt] += blk[mt][nt] * scur[nt][h * NSC + j / SPB];
+                const int b = (cl * CC + j * 32) / (SPB * 32);  // block inside the K range
+                const float sc = __shfl(sreg[r & 1][nt][b % Q], col + 16 * (b / Q));
+                acc[mt][nt] += blk[mt][nt] * sc;
                 pin(acc[mt][nt]);
               }
             } else {
@@ -266,16 +343,7 @@ qmoe_stream(GemmArgs g) {
     }
   }
 
-  // Output rows (slot ids or sorted positions), then column scales and the
-  // fp32 partial rows of every row block.
-  int orow[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = min(mt * 16 + 4 * grp + i, rows - 1);
-      orow[mt][i] = g.store_by_slot ? g.perm[p0 + rr] : p0 + rr;
-    }
+  // Column scales, then the fp32 partial rows of every row block.
 #pragma unroll
   for (int r = 0; r < RBW; ++r)
 #pragma unroll
@@ -289,7 +357,7 @@ qmoe_stream(GemmArgs g) {
         for (int i = 0; i < 4; ++i) {
           const int rr = mt * 16 + 4 * grp + i;
           if (rr < rows && n < g.N)
-            g.slot_out[((long)blockIdx.z * g.S + orow[mt][i]) * g.N + n] = res[r][mt][nt][i] * sc;
+            g.slot_out[((long)split * g.S + orow[mt][i]) * g.N + n] = res[r][mt][nt][i] * sc;
         }
     }
 }
@@ -404,7 +472,7 @@ hipError_t launch_stream(int bits, int mt, int items, int rbw, int splits, const
   const int cc = bits == 4 ? 128 : 64;
   const int rows_per_wg = kSWaves * 16 * 2 * (mt == 1 ? rbw : 1);
   const size_t lds = (size_t)16 * mt * items * kCPI * cc * 4;
-  const dim3 grid(max_tiles, (g.N + rows_per_wg - 1) / rows_per_wg, splits);
+  const dim3 grid(splits, max_tiles, (g.N + rows_per_wg - 1) / rows_per_wg);
   return bits == 4 ? pick_mt<4>(mt, rbw, items, g, grid, lds, st) : pick_mt<8>(mt, rbw, items, g, grid, lds, st);
 }
 

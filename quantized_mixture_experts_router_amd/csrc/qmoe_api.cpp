@@ -114,11 +114,13 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
       g1.store_by_slot = 0;
       g1.slot_out = part1;
       QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.items, p.s1.rbw, p.s1.splits, g1, (int)p.max_tiles, s));
+      QMOE_TRY_HIP(mark(2));
       QMOE_TRY_HIP(launch_act(d.bits, epi1, part1, p.s1.splits, S, (int)d.F, I, (int)p.kp2, d.alpha, d.beta, act, s));
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, epi1, p.mt, p.aligned, g1, (int)p.max_tiles, s));
+      QMOE_TRY_HIP(mark(2));
     }
-    QMOE_TRY_HIP(mark(2));
+    QMOE_TRY_HIP(mark(3));
     GemmArgs g2{};
     g2.wq = static_cast<const uint8_t*>(fc2w->data);
     g2.ws = static_cast<const float*>(fc2s->data);
@@ -142,9 +144,9 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
     }
-    QMOE_TRY_HIP(mark(3));
-    QMOE_TRY_HIP(launch_combine(slot, topk_w, T, k, H, p.splits2, out, s));
     QMOE_TRY_HIP(mark(4));
+    QMOE_TRY_HIP(launch_combine(slot, topk_w, T, k, H, p.splits2, out, s));
+    QMOE_TRY_HIP(mark(5));
   }
   if (dbg) {
     if (dbg->topk_idx) QMOE_TRY_HIP(launch_copy_i32(topk_idx, dbg->topk_idx, S, s));

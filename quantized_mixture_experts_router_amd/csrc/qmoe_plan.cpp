@@ -138,7 +138,7 @@ void make_plan(const Dims& d, Plan* p) {
     // and the ranges must tile K exactly.
     constexpr int64_t kLdsBudget = 64 * 1024;
     auto lds_bytes = [&](int64_t items) { return 16 * p->mt * items * item_codes * 4; };
-    auto shape = [&](Plan::Stream& st, int64_t K) {
+    auto shape = [&](Plan::Stream& st, int64_t K, int64_t N) {
       st.on = stream_ok(d.bits, K, d.bs);
       if (!st.on) return;
       const int64_t nit = K / item_codes;
@@ -148,12 +148,13 @@ void make_plan(const Dims& d, Plan* p) {
       st.on = ipr > 0;
       st.items = ipr;
       st.splits = (int)(nit / ipr);
-      // Two row blocks per workgroup amortise the activation staging; 32-code
-      // scale blocks need the registers for their scales instead.
-      st.rbw = (p->mt == 1 && d.bs != 32) ? 2 : 1;
+      // Two row blocks of 256 rows per workgroup amortise the activation
+      // staging (when they tile N exactly); 32-code scale blocks need the
+      // registers for their scales instead.
+      st.rbw = (p->mt == 1 && d.bs != 32 && N % 512 == 0) ? 2 : 1;
     };
-    shape(p->s1, d.H);
-    shape(p->s2, d.I);
+    shape(p->s1, d.H, d.F);
+    shape(p->s2, d.I, d.H);
     if (p->s2.on) p->splits2 = p->s2.splits;
   }
   size_t o = 0;
