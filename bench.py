@@ -43,6 +43,8 @@ def _args():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stage-timing", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     return ap.parse_args()
 
 
@@ -95,8 +97,10 @@ def stage_times(qm, call_debug, steps):
     return dict(zip(("routing", "fc1", "fc1_act", "fc2", "combine"), [s / steps for s in sums]))
 
 
-def cpu_baseline(w, arrs):
-    import numpy as np
+def cpu_baseline(w, arrs, budget_s=12.0, max_reps=8):
+    """Time the float64 oracle on the host cores over a bounded sample of the
+    workload: the whole batch, repeated until about budget_s seconds of work
+    (small batches), or its first tokens (large batches)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -104,34 +108,58 @@ def cpu_baseline(w, arrs):
     except Exception:  # threadpoolctl missing: numpy runs single threaded loops
         threads = 1
     attrs = w.attrs()
-    if w.tokens <= 16:
-        ids = list(range(w.tokens))
-        sample = f"all {w.tokens} tokens of the workload (every used expert dequantised once)"
-    else:
-        ids = list(range(4))
-        sample = "first 4 tokens of the workload (oracle.qmoe_tokens: their experts dequantised once)"
+    ids = list(range(w.tokens)) if w.tokens <= 16 else list(range(4))
+    done, reps = 0, 0
     t0 = time.perf_counter()
-    oracle.qmoe_tokens(ids, *arrs.values(), attrs=attrs)
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < budget_s):
+        oracle.qmoe_tokens(ids, *arrs.values(), attrs=attrs)
+        done += len(ids)
+        reps += 1
     dt = time.perf_counter() - t0
-    return dict(value=round(len(ids) / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
+    if w.tokens <= 16:
+        sample = (f"all {w.tokens} tokens of the workload x {reps} repetitions "
+                  "(every used expert dequantised once per repetition)")
+    else:
+        sample = f"first 4 tokens of the workload x {reps} repetitions (their experts dequantised once per repetition)"
+    return dict(value=round(done / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=sample, seconds=round(dt, 2))
 
 
-def traffic_for(kernel_key):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the kernel source now in the tree; otherwise None."""
+def _sha(path):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+KERNEL_SRC = {
+    "qmoe_stream": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "stream.hip"),
+    "qmoe_gemm": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gemm.hip"),
+}
+
+
+def traffic_for(key, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel source now in the tree; otherwise None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except OSError:
         return None
-    ent = rec.get(kernel_key)
-    if not ent:
+    ent = rec.get(key)
+    if not ent or ent.get("kernel") != kernel:
         return None
-    import hashlib
-    src = os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gemm.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return ent.get("bytes") if ent.get("gemm_sha") == h else None
+    return ent.get("bytes") if ent.get("source_sha") == _sha(KERNEL_SRC[kernel]) else None
+
+
+def copy_calibration(nbytes, reps=3):
+    """A plain device-to-device copy of nbytes (for scaling the HBM byte
+    counters: its FETCH_SIZE and WRITE_SIZE should each read nbytes)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def main():
@@ -140,6 +168,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(every run here uses a single MI355X); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import numpy as np
     import torch
 
@@ -189,12 +220,13 @@ def main():
         key = "fc1" if stages["fc1"] >= stages["fc2"] else "fc2"
         work = fc1_work if key == "fc1" else fc2_work
         roofline = roofline_for(work, stages[key])
-        roofline["kernel"] = f"qmoe_gemm ({key.upper()}, {'SwiGLU' if w.activation == 'swiglu' else 'ReLU'} "\
-                             f"epilogue)" if key == "fc1" else "qmoe_gemm (FC2, slot-row store)"
+        # every expert's rows fit one 64-row tile: the weight-streaming kernel
+        kernel = "qmoe_stream" if w.tokens <= 64 else "qmoe_gemm"
+        roofline["kernel"] = f"{kernel} ({key.upper()})"
         roofline["avg_ms"] = round(stages[key], 5)
         roofline["algorithmic_bytes"] = int(work["bytes"])
         roofline["algorithmic_flops"] = work["flops"]
-        roofline["traffic"] = traffic_for(f"{args.workload}:{key}")
+        roofline["traffic"] = traffic_for(f"{args.workload}:{key}", kernel)
 
     cpu = None
     if not args.no_cpu_baseline:
