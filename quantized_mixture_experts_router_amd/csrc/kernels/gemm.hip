@@ -274,8 +274,18 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < k; ++s) {
       const float w = topk_w[t * k + s];
-      f32x4 y = *(const f32x4*)(slot_out + (t * k + s) * H + h);
-      for (int z = 1; z < splits; ++z) y += *(const f32x4*)(slot_out + ((long)z * S + t * k + s) * H + h);
+      const float* src = slot_out + (t * k + s) * H + h;
+      f32x4 y;
+      // eight partial rows in flight at a time, summed in range order
+      for (int z0 = 0; z0 < splits; z0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (z0 + i < splits) v[i] = *(const f32x4*)(src + (long)(z0 + i) * S * H);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (z0 + i < splits) y = (z0 + i == 0) ? v[i] : y + v[i];
+      }
       acc += w * y;
     }
     *(f32x4*)(out + t * H + h) = acc;

@@ -8,6 +8,12 @@ namespace qmoe {
 hipError_t launch_router(const float* logits, int T, int E, int k, int routing, int normalize, int* topk_idx,
                          float* topk_w, hipStream_t st);
 
+// Router, counts, offsets, tile table and stable permutation in one launch
+// (T * k <= 1024 and E <= 1024).
+hipError_t launch_route_small(const float* logits, int T, int E, int k, int routing, int normalize, int bm,
+                              int* topk_idx, float* topk_w, int* counts, int* offsets, int* perm, int* tiles,
+                              int* ntiles, hipStream_t st);
+
 hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchunks, int bm, int* hist,
                           int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st);
 
@@ -21,6 +27,7 @@ struct GemmArgs {
   const uint8_t* wq;    // packed weights [E][N][kb]
   const float* ws;      // scales [E][N] or [E][N][nblk]
   const uint8_t* a;     // operand rows (f16 hi/lo groups), row stride a_stride bytes
+  int a_f32;            // stream kernel: a holds fp32 rows (4 bytes a code) to split while staging
   const int* a_map;     // FC1: perm (sorted position -> slot); FC2: nullptr (row = position)
   int a_div;            // FC1: k (slot -> token)
   long a_stride;

@@ -3,6 +3,7 @@
 //   qmoe_hist          per-chunk expert histogram of the selected slots
 //   qmoe_scan          per-expert counts, exclusive offsets, chunk bases, M-tile table
 //   qmoe_scatter       stable expert-sorted slot order (perm)
+//   qmoe_route_small   all of the above in one workgroup (<= 1024 slots)
 //   qmoe_prep_a        fp32 tokens -> f16 hi/lo operand rows (see common.hpp)
 //
 // Routing follows the QMoE WebGPU manifest (description: softmax over the
@@ -24,14 +25,14 @@ __device__ __forceinline__ bool key_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// One wavefront per token; each lane holds logits e = lane + 64 * j.
+// Routing of token t by one wavefront; each lane holds logits e = lane + 64 * j.
+// Lane 0 writes the selected experts (also to s_idx when given, for kernels
+// that keep working on them in LDS).
 template <int V>
-__global__ void __launch_bounds__(256) qmoe_router(const float* __restrict__ logits, int T, int E, int k,
-                                                   int routing, int normalize, int* __restrict__ topk_idx,
-                                                   float* __restrict__ topk_w) {
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k, int routing,
+                                            int normalize, int* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                            int* s_idx) {
   const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
   const float* row = logits + (size_t)t * E;
   float v[V];
 #pragma unroll
@@ -72,7 +73,10 @@ __global__ void __launch_bounds__(256) qmoe_router(const float* __restrict__ log
     if (r == 0) v0 = bv;
     const float ex = expf(bv - v0);  // identical in every lane
     sum_sel += ex;
-    if (lane == 0) topk_idx[(size_t)t * k + r] = bi;
+    if (lane == 0) {
+      topk_idx[(size_t)t * k + r] = bi;
+      if (s_idx) s_idx[t * k + r] = bi;
+    }
     if (lane == (r & 63)) {
       if (r < 64) my_val = ex;
       else topk_w[(size_t)t * k + r] = ex;  // picks beyond 64 wait in the output buffer
@@ -97,6 +101,16 @@ __global__ void __launch_bounds__(256) qmoe_router(const float* __restrict__ log
   }
 }
 
+// One wavefront per token.
+template <int V>
+__global__ void __launch_bounds__(256) qmoe_router(const float* __restrict__ logits, int T, int E, int k,
+                                                   int routing, int normalize, int* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token<V>(logits, t, E, k, routing, normalize, topk_idx, topk_w, nullptr);
+}
+
 // Histogram of selected experts over chunks of `chunk` consecutive slots.
 __global__ void __launch_bounds__(256) qmoe_hist(const int* __restrict__ topk_idx, int S, int E, int chunk,
                                                  int* __restrict__ hist) {
@@ -110,28 +124,19 @@ __global__ void __launch_bounds__(256) qmoe_hist(const int* __restrict__ topk_id
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Single block: counts, offsets, per-chunk bases and the M-tile table.
-// tiles[4*i .. 4*i+3] = (expert, first sorted position, rows, 0); ntiles[0] = count.
-__global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nchunks, int E, int S, int bm,
-                                                  int* __restrict__ counts, int* __restrict__ offsets,
-                                                  int* __restrict__ tiles, int* __restrict__ ntiles) {
-  __shared__ int s_cnt[1024];
-  __shared__ int s_tiles[1024];
+// Block-wide (1024 threads, thread e = expert e < E <= 1024): given each
+// expert's slot count c, write counts, exclusive offsets and the M-tile table
+//   tiles[4*i .. 4*i+3] = (expert, first sorted position, rows, 0), ntiles[0] = count;
+// returns the expert's first sorted position.
+__device__ __forceinline__ int scan_experts(int c, int E, int S, int bm, int* __restrict__ counts,
+                                            int* __restrict__ offsets, int* __restrict__ tiles,
+                                            int* __restrict__ ntiles) {
   __shared__ int s_warp[16];
   __shared__ int s_warp2[16];
   const int e = threadIdx.x;
-  int c = 0;
-  if (e < E) {
-    for (int ch = 0; ch < nchunks; ++ch) {
-      int* h = hist + (size_t)ch * E + e;
-      const int v = *h;
-      *h = c;  // exclusive prefix over chunks
-      c += v;
-    }
-    counts[e] = c;
-  }
+  if (e < E) counts[e] = c;
   const int nt = (c + bm - 1) / bm;
-  // Block-wide inclusive scans of counts and tile counts (wave scan, then wave totals).
+  // Inclusive scans of counts and tile counts (wave scan, then wave totals).
   int inc = c, inct = nt;
   const int lane = lane_id(), w = threadIdx.x >> 6;
 #pragma unroll
@@ -162,10 +167,7 @@ __global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nc
   const int off_e = inc - c + s_warp[w];
   const int tile0 = inct - nt + s_warp2[w];
   if (e < E) {
-    s_cnt[e] = off_e;
-    s_tiles[e] = tile0;
     offsets[e] = off_e;
-    for (int ch = 0; ch < nchunks; ++ch) hist[(size_t)ch * E + e] += off_e;
     for (int i = 0; i < nt; ++i) {
       int* tp = tiles + 4 * (tile0 + i);
       tp[0] = e;
@@ -178,6 +180,27 @@ __global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nc
     offsets[E] = S;
     ntiles[0] = tile0 + nt;
   }
+  return off_e;
+}
+
+// Single block: counts from the chunk histograms (which become per-chunk
+// bases for the scatter), offsets and the M-tile table.
+__global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nchunks, int E, int S, int bm,
+                                                  int* __restrict__ counts, int* __restrict__ offsets,
+                                                  int* __restrict__ tiles, int* __restrict__ ntiles) {
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E) {
+    for (int ch = 0; ch < nchunks; ++ch) {
+      int* h = hist + (size_t)ch * E + e;
+      const int v = *h;
+      *h = c;  // exclusive prefix over chunks
+      c += v;
+    }
+  }
+  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles);
+  if (e < E)
+    for (int ch = 0; ch < nchunks; ++ch) hist[(size_t)ch * E + e] += off_e;
 }
 
 // Stable scatter: slot s (expert e) goes to base[chunk][e] + (number of slots
@@ -221,6 +244,53 @@ __global__ void __launch_bounds__(256) qmoe_scatter(const int* __restrict__ topk
   }
 }
 
+// The whole front end in one workgroup of 1024 threads, for up to 1024 slots
+// and 1024 experts: routing (16 tokens at a time, one per wavefront), counts
+// in LDS, the scan and tile table, then the stable scatter.  The scatter runs
+// wavefront by wavefront in slot order: a wavefront ranks its 64 slots among
+// equal experts with ballots and advances each expert's cursor, so slot ids
+// stay ascending within every expert.
+template <int V>
+__global__ void __launch_bounds__(1024) qmoe_route_small(const float* __restrict__ logits, int T, int E, int k,
+                                                         int routing, int normalize, int bm,
+                                                         int* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                         int* __restrict__ counts, int* __restrict__ offsets,
+                                                         int* __restrict__ perm, int* __restrict__ tiles,
+                                                         int* __restrict__ ntiles) {
+  __shared__ int s_idx[1024];
+  __shared__ int s_cnt[1024];  // counts, then each expert's next sorted position
+  const int S = T * k;
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  if (threadIdx.x < E) s_cnt[threadIdx.x] = 0;
+  for (int t = w; t < T; t += 16) route_token<V>(logits, t, E, k, routing, normalize, topk_idx, topk_w, s_idx);
+  __syncthreads();
+  if (threadIdx.x < S) atomicAdd(&s_cnt[s_idx[threadIdx.x]], 1);
+  __syncthreads();
+  const int c = threadIdx.x < E ? s_cnt[threadIdx.x] : 0;
+  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles);  // synchronises
+  if (threadIdx.x < E) s_cnt[threadIdx.x] = off_e;
+  __syncthreads();
+  const int nw = (S + 63) / 64;
+  for (int ww = 0; ww < nw; ++ww) {
+    if (w == ww) {
+      const int s = threadIdx.x;
+      const bool valid = s < S;
+      const int e = valid ? s_idx[s] : -1;
+      unsigned long long todo = __ballot(valid);
+      while (todo) {
+        const int leader = __ffsll((long long)todo) - 1;
+        const int le = __shfl(e, leader);
+        const unsigned long long m = __ballot(valid && e == le);
+        const int base = s_cnt[le];
+        if (valid && e == le) perm[base + __popcll(m & ((1ull << lane) - 1ull))] = s;
+        if (lane == leader) s_cnt[le] = base + __popcll(m);
+        todo &= ~m;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // fp32 token rows -> f16 hi/lo operand rows (storage order of common.hpp),
 // zero padded to kp codes.  One thread per group of 8 codes.  When act_pad is
 // given, also zero the padding columns [I, kp2) of every act row.
@@ -248,17 +318,18 @@ __global__ void __launch_bounds__(256) qmoe_prep_a(const float* __restrict__ x, 
     *(f16x8*)(dst + 16) = lo;
   }
   if (act != nullptr) {
-    // padding groups of act rows: storage groups covering codes >= I
-    const int g0 = I / 8;  // first group that may hold codes >= I
+    // padding of act rows: every storage group of the 32-code blocks from the
+    // one holding code I onwards (inside a block, 8-bit storage groups hold
+    // permuted code groups, so a group's index does not bound its codes)
+    const int g0 = (I / 32) * 4;  // first group that may hold codes >= I
     const int pg = kp2 / 8 - g0;
     const long pid = gid - groups;
     if (pid >= 0 && pid < (long)S * pg) {
       const int p = pid / pg;
       const int g = g0 + pid % pg;
       uint8_t* dst = act + (size_t)p * kp2 * 4 + (size_t)g * 32;
-      // codes < I in a partial group are written later by FC1; zero the rest now
-      // (FC1 writes only valid codes, so a full clear of the group is safe
-      // because FC1 runs after this kernel on the same stream)
+      // codes < I in these groups are written later by FC1 (on the same
+      // stream), so clearing whole groups is safe
       *(f16x8*)dst = f16x8{};
       *(f16x8*)(dst + 16) = f16x8{};
     }
@@ -278,6 +349,23 @@ hipError_t launch_router(const float* logits, int T, int E, int k, int routing, 
   return hipGetLastError();
 }
 
+hipError_t launch_route_small(const float* logits, int T, int E, int k, int routing, int normalize, int bm,
+                              int* topk_idx, float* topk_w, int* counts, int* offsets, int* perm, int* tiles,
+                              int* ntiles, hipStream_t st) {
+  if (T * k > 1024 || E > 1024) return hipErrorInvalidValue;
+  const int V = (E + 63) / 64;
+#define QMOE_ROUTE_SMALL(VV)                                                                                       \
+  hipLaunchKernelGGL(qmoe_route_small<VV>, dim3(1), dim3(1024), 0, st, logits, T, E, k, routing, normalize, bm,  \
+                     topk_idx, topk_w, counts, offsets, perm, tiles, ntiles)
+  if (V <= 1) QMOE_ROUTE_SMALL(1);
+  else if (V <= 2) QMOE_ROUTE_SMALL(2);
+  else if (V <= 4) QMOE_ROUTE_SMALL(4);
+  else if (V <= 8) QMOE_ROUTE_SMALL(8);
+  else QMOE_ROUTE_SMALL(16);
+#undef QMOE_ROUTE_SMALL
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchunks, int bm, int* hist,
                           int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st) {
   hipLaunchKernelGGL(qmoe_hist, dim3(nchunks), dim3(256), E * sizeof(int), st, topk_idx, S, E, chunk, hist);
@@ -289,7 +377,7 @@ hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchu
 hipError_t launch_prep_a(int bits, const float* x, int T, int H, int kp, uint8_t* xa, uint8_t* act, int S, int I,
                          int kp2, hipStream_t st) {
   long work = (long)T * (kp / 8);
-  if (act) work += (long)S * (kp2 / 8 - I / 8);
+  if (act) work += (long)S * (kp2 / 8 - (I / 32) * 4);
   const dim3 grid((work + 255) / 256), block(256);
   if (bits == 4) hipLaunchKernelGGL(qmoe_prep_a<4>, grid, block, 0, st, x, T, H, kp, xa, act, S, I, kp2);
   else hipLaunchKernelGGL(qmoe_prep_a<8>, grid, block, 0, st, x, T, H, kp, xa, act, S, I, kp2);

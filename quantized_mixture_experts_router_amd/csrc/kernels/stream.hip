@@ -98,12 +98,19 @@ qmoe_stream(GemmArgs g) {
   constexpr int Q = NBR / 4;
   static_assert(SPB == 0 || (NBR % 4 == 0 && Q <= 8), "scale blocks per K range");
 
-  // Grid: x = K range (fastest, so the K ranges of the same weight rows are
-  // fetched by neighbouring workgroups at the same time), y = expert tile,
-  // z = group of RBW row blocks.
-  const int split = blockIdx.x;
-  const int tile = blockIdx.y;
-  const int rgroup = blockIdx.z;
+  // Work w = (K range, expert tile, group of RBW row blocks), K range fastest.
+  // Workgroups are dealt to the 8 XCDs round robin by linear id; each XCD is
+  // given a contiguous run of work ids, so the K ranges of the same weight
+  // rows run side by side on one XCD and share its L2 (scale rows and
+  // activation slices are fetched from HBM once).
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int total = gx * gy * gridDim.z;
+  const int lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int xcd = lin & 7, per = total >> 3, extra = total & 7;
+  const int w = xcd * per + min(xcd, extra) + (lin >> 3);
+  const int split = w % gx;
+  const int tile = (w / gx) % gy;
+  const int rgroup = w / (gx * gy);
   if (tile >= g.ntiles[0]) return;
   const int e = g.tiles[4 * tile + 0];
   const int p0 = g.tiles[4 * tile + 1];
@@ -206,9 +213,47 @@ qmoe_stream(GemmArgs g) {
     s_rowbase[threadIdx.x] = ar * g.a_stride + (long)c0 * CC * 4;
   }
   __syncthreads();
-  {
-    // Only the tile's valid rows are staged; matrix rows beyond them read the
-    // last valid row (their results are discarded).
+  // Only the tile's valid rows are staged; matrix rows beyond them read the
+  // last valid row (their results are discarded).
+  if (g.a_f32) {
+    // fp32 rows (the layer input): each thread converts groups of 8 codes,
+    // 32 bytes of floats, into their 16-byte hi and lo pieces.
+    constexpr int GR = PIECES / 2;                                // groups per row
+    constexpr int GPT = (ROWS * GR + 64 * kSWaves - 1) / (64 * kSWaves);
+    f32x4 v[GPT][2];
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int idx = threadIdx.x + i * 64 * kSWaves;
+      const int r = idx / GR, gq = idx % GR;
+      // first code of storage group gq (see common.hpp): 4-bit groups hold
+      // their own 8 codes, 8-bit groups those of code group sigma(gq % 4)
+      const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
+      if (idx < ROWS * GR && r < rows) {
+        const float* src = (const float*)(g.a + s_rowbase[r]) + j0;
+        v[i][0] = *(const f32x4*)src;
+        v[i][1] = *(const f32x4*)(src + 4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int idx = threadIdx.x + i * 64 * kSWaves;
+      const int r = idx / GR, gq = idx % GR;
+      if (idx < ROWS * GR && r < rows) {
+        f16x8 hi, lo;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code inside the group at storage slot sl
+          _Float16 h, l;
+          split_f16(v[i][c >> 2][c & 3], h, l);
+          hi[sl] = h;
+          lo[sl] = l;
+        }
+        uint8_t* row = lds + r * LSTRIDE;
+        *(f16x8*)(row + (((2 * gq) ^ (r & 15)) * 16)) = hi;
+        *(f16x8*)(row + (((2 * gq + 1) ^ (r & 15)) * 16)) = lo;
+      }
+    }
+  } else {
     u32x4 v[PPT];
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
@@ -365,42 +410,69 @@ qmoe_stream(GemmArgs g) {
 // FC1 epilogue for the streamed path: sum the K-range partials of each
 // expert-sorted row p in range order, apply ReLU or interleaved SwiGLU
 // (g * sigmoid(alpha * g) * (u + beta), g = h[2j], u = h[2j+1]) and write the
-// f16 hi/lo operand rows of FC2.  One thread per 8-code storage group; groups
-// beyond I are zero padding.
+// f16 hi/lo operand rows of FC2.  One thread per 8-code storage group: its 8
+// codes are consecutive (see common.hpp), so it reads 8 (ReLU) or 16 (SwiGLU)
+// consecutive fp32 values of every partial row with 16-byte loads, all
+// partials of a batch of four ranges in flight at once.  Groups beyond I are
+// zero padding.
 template <int BITS, int EPI>
 __global__ void __launch_bounds__(256) qmoe_act(const float* __restrict__ part, int splits, int S, int F, int I,
                                                 int kp2, float alpha, float beta, uint8_t* __restrict__ act) {
+  constexpr int W = EPI == EPI_SWIGLU ? 16 : 8;  // FC1 values per group
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const int groups = kp2 / 8;
   if (gid >= (long)S * groups) return;
   const int p = gid / groups;
-  const int q0 = (gid % groups) * 8;
+  const int gq = gid % groups;
+  const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);  // first code of the group
+  const long zstride = (long)S * F;
+  float h[W];
+  if (j0 + 8 <= I && (F & 3) == 0) {
+    const float* base = part + (long)p * F + (W / 8) * j0;
+    for (int z0 = 0; z0 < splits; z0 += 4) {
+      f32x4 v[4][W / 4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (z0 + i < splits)
+#pragma unroll
+          for (int m = 0; m < W / 4; ++m) v[i][m] = *(const f32x4*)(base + (z0 + i) * zstride + 4 * m);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (z0 + i < splits)
+#pragma unroll
+          for (int m = 0; m < W / 4; ++m)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) h[4 * m + c] = (z0 + i == 0) ? v[i][m][c] : h[4 * m + c] + v[i][m][c];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < W; ++c) {
+      const int f = (W / 8) * j0 + c;  // FC1 row of value c
+      float a = 0.f;
+      if (f < (W / 8) * I)
+        for (int z = 0; z < splits; ++z) a = (z == 0) ? part[(long)p * F + f] : a + part[z * zstride + (long)p * F + f];
+      h[c] = a;
+    }
+  }
   f16x8 hi, lo;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = code_of_storage<BITS>(q0 + i);
+  for (int sl = 0; sl < 8; ++sl) {
+    const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code j0 + c sits at storage slot sl
     float a = 0.f;
-    if (j < I) {
+    if (j0 + c < I) {
       if constexpr (EPI == EPI_SWIGLU) {
-        float gv = 0.f, uv = 0.f;
-        for (int z = 0; z < splits; ++z) {
-          const float* row = part + ((long)z * S + p) * F;
-          gv += row[2 * j];
-          uv += row[2 * j + 1];
-        }
+        const float gv = h[2 * c], uv = h[2 * c + 1];
         a = gv / (1.f + expf(-alpha * gv)) * (uv + beta);
       } else {
-        float hv = 0.f;
-        for (int z = 0; z < splits; ++z) hv += part[((long)z * S + p) * F + j];
-        a = fmaxf(hv, 0.f);
+        a = fmaxf(h[c], 0.f);
       }
     }
-    _Float16 h, l;
-    split_f16(a, h, l);
-    hi[i] = h;
-    lo[i] = l;
+    _Float16 hh, ll;
+    split_f16(a, hh, ll);
+    hi[sl] = hh;
+    lo[sl] = ll;
   }
-  uint8_t* dst = act + (long)p * kp2 * 4 + (long)q0 * 4;
+  uint8_t* dst = act + (long)p * kp2 * 4 + (long)gq * 32;
   *(f16x8*)dst = hi;
   *(f16x8*)(dst + 16) = lo;
 }

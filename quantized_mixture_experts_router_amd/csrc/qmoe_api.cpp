@@ -81,21 +81,33 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     return hipSuccess;
   };
   QMOE_TRY_HIP(mark(0));
-  QMOE_TRY_HIP(launch_router(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize, topk_idx,
-                             topk_w, s));
-  QMOE_TRY_HIP(launch_permute(topk_idx, S, E, (int)p.chunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets, perm,
-                              tiles, ntiles, s));
+  if (p.small_front) {
+    QMOE_TRY_HIP(launch_route_small(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize,
+                                    (int)p.bm, topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, s));
+  } else {
+    QMOE_TRY_HIP(launch_router(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize, topk_idx,
+                               topk_w, s));
+    QMOE_TRY_HIP(launch_permute(topk_idx, S, E, (int)p.chunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets,
+                                perm, tiles, ntiles, s));
+  }
   if (d.I > 0) {
-    QMOE_TRY_HIP(launch_prep_a(d.bits, static_cast<const float*>(input->data), T, H, (int)p.kp1, xa, act, S, I,
-                               (int)p.kp2, s));
+    // The streaming FC1 splits the fp32 input rows itself while staging them
+    // (and its activation pass writes whole FC2 operand rows, padding
+    // included); otherwise the operand rows and the padding codes [I, kp2)
+    // of FC2's operand rows are prepared here.
+    const bool a_f32 = p.s1.on;
+    if (!a_f32)
+      QMOE_TRY_HIP(launch_prep_a(d.bits, static_cast<const float*>(input->data), T, H, (int)p.kp1, xa, act, S, I,
+                                 (int)p.kp2, s));
     QMOE_TRY_HIP(mark(1));
     GemmArgs g1{};
     g1.wq = static_cast<const uint8_t*>(fc1w->data);
     g1.ws = static_cast<const float*>(fc1s->data);
-    g1.a = xa;
+    g1.a = a_f32 ? static_cast<const uint8_t*>(input->data) : xa;
+    g1.a_f32 = a_f32;
     g1.a_map = perm;
     g1.a_div = k;
-    g1.a_stride = 4 * p.kp1;
+    g1.a_stride = a_f32 ? 4 * H : 4 * p.kp1;
     g1.tiles = tiles;
     g1.ntiles = ntiles;
     g1.N = (int)d.F;

@@ -131,6 +131,7 @@ void make_plan(const Dims& d, Plan* p) {
   p->kp2 = round_up(d.I, 128);
   p->aligned = (d.H % 8 == 0) && (d.I % 8 == 0);
   p->nchunks = (p->S + p->chunk - 1) / p->chunk;
+  p->small_front = p->S <= 1024 && d.E <= 1024;
   if (p->decode && d.I > 0) {
     const int64_t item_codes = d.bits == 4 ? 256 : 128;
     // Items per K range: the tile's activation rows for the range (16*mt rows,
@@ -167,7 +168,7 @@ void make_plan(const Dims& d, Plan* p) {
   p->off_tiles = take(sizeof(int32_t) * 4 * p->max_tiles);
   p->off_ntiles = take(sizeof(int32_t) * 4);
   p->off_hist = take(sizeof(int32_t) * p->nchunks * d.E);
-  p->off_xa = take(size_t(4) * d.T * p->kp1);     // f16 hi + lo per element
+  p->off_xa = take(p->s1.on ? 0 : size_t(4) * d.T * p->kp1);  // f16 hi + lo per element (streaming FC1 reads fp32 rows)
   p->off_act = take(size_t(4) * p->S * p->kp2);   // f16 hi + lo per element
   p->off_slot = take(d.I > 0 ? sizeof(float) * p->splits2 * p->S * d.H : 0); // FC2 rows by slot id
   p->off_part1 = take(p->s1.on ? sizeof(float) * p->s1.splits * p->S * d.F : 0);

@@ -54,6 +54,7 @@ struct Plan {
   } s1, s2;
   int splits2 = 1;       // FC2 partial sets the combine sums (1 off the stream path)
   size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path)
+  bool small_front = false;  // router + permutation in one workgroup (S, E <= 1024)
   int64_t chunk = 1024;  // slots per permutation block
   int64_t nchunks = 0;
   // workspace layout

@@ -36,8 +36,13 @@ def run_gpu(arrs, attrs, torch, debug=True, stream=None):
                    offsets=torch.full((E + 1,), -7, dtype=torch.int32, device="cuda"),
                    perm=torch.full((T * k,), -7, dtype=torch.int32, device="cuda"))
     out = torch.full_like(d["input"], float("nan"))
-    qm.forward(d["input"], d["router_probs"], d["fc1_experts_weights"], d["fc1_scales"],
-               d["fc2_experts_weights"], d["fc2_scales"], attrs, output=out, debug=dbg, stream=stream)
+    # Workspace bytes 0xFF (every float a NaN): a read of anything the path
+    # did not write first shows up in the output.
+    args = [d[n] for n in ("input", "router_probs", "fc1_experts_weights", "fc1_scales", "fc2_experts_weights",
+                           "fc2_scales")]
+    need = qm.qmoe_workspace_size(*args, attrs)
+    ws = torch.full((max(need, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+    qm.forward(*args, attrs, output=out, debug=dbg, stream=stream, workspace=ws)
     torch.cuda.synchronize()
     res = {"out": out.cpu().numpy()}
     if dbg:

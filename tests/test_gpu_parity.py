@@ -100,7 +100,7 @@ def test_route_ties_through_gpu(torch):
 SHAPES = [
     (1, 64, 4, 32, 1), (5, 128, 3, 64, 2), (16, 256, 8, 96, 2), (17, 64, 4, 160, 3),
     (33, 128, 6, 64, 6), (64, 192, 8, 128, 2), (70, 128, 5, 96, 2), (200, 64, 16, 64, 4),
-    (300, 256, 1, 32, 1),
+    (300, 256, 1, 32, 1), (24, 512, 8, 256, 3), (40, 256, 4, 256, 2), (60, 256, 4, 128, 2),
 ]
 
 
@@ -116,6 +116,16 @@ def test_small_sweep(torch, bits, bs, act):
         w, a = W.random_case(rng, tokens_shape=shape, hidden=H, experts=E, inter=I, k=k, bits=bits,
                              block_size=bs, activation=act)
         _full_check(w, a, torch, f"sweep T{T} H{H} E{E} I{I} k{k}")
+
+
+def test_front_end_paths(torch):
+    """Routing and permutation on both front ends: one workgroup (up to 1024
+    slots and 1024 experts) and the chunked multi-kernel path beyond."""
+    rng = np.random.default_rng(76)
+    for (T, E, k) in [(512, 8, 2), (205, 16, 5), (4, 1024, 3), (300, 1000, 3), (64, 300, 16), (700, 1024, 2)]:
+        w, a = W.random_case(rng, tokens_shape=(T,), hidden=64, experts=E, inter=16, k=k, bits=8,
+                             block_size=0, activation="relu")
+        _full_check(w, a, torch, f"front end T{T} E{E} k{k} (slots {T * k})")
 
 
 def test_unaligned_shapes(torch):
