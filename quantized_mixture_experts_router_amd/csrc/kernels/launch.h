@@ -42,6 +42,9 @@ struct GemmArgs {
   float* slot_out;      // FC2 output [splits][S][N] by slot id
   const int* perm;      // FC2: sorted position -> slot
   float alpha, beta;
+  // stream kernel
+  int nst;              // stages per K range
+  int act_swiglu;       // FC1 over the whole of K: activation written by the kernel (act != nullptr)
 };
 
 enum { EPI_RELU = 0, EPI_SWIGLU = 1, EPI_STORE = 2 };
@@ -51,11 +54,14 @@ enum { SC_COL = 0, SC_BLOCK = 1, SC_BLOCK16 = 2 };
 
 hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& g, int max_tiles, hipStream_t st);
 
-// Weight-streaming variant for small token counts (see stream.hip): writes fp32
-// partial rows part[z][row][N] for K ranges z < splits of `items` 128-byte
-// row items each; workgroups stream rbw row blocks (mt == 1 only).
-hipError_t launch_stream(int bits, int mt, int items, int rbw, int splits, const GemmArgs& g, int max_tiles,
-                         hipStream_t st);
+// Weight-streaming variant for small token counts (see stream.hip).  FC1
+// (g.a_f32 set): A rows are the fp32 input; with g.act set (one K range) the
+// kernel writes FC2 operand rows after the activation, else fp32 partial rows
+// part[z][p][N].  FC2: partial rows by slot id, slot_out[z][slot][N].
+// z < splits K ranges of g.nst stages each.
+int stream_stage_items(int mt);
+size_t stream_lds_bytes(int bits, int mt);
+hipError_t launch_stream(int bits, int mt, int stg, int splits, const GemmArgs& g, int max_tiles, hipStream_t st);
 
 // Sum FC1 partials over K ranges, apply the activation, write FC2 operand rows.
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,

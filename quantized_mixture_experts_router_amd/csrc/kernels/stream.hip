@@ -1,31 +1,36 @@
 // Weight-streaming grouped GEMM for small token counts (every expert's rows fit
 // one M tile of at most 64 rows): the same product as gemm.hip,
 //
-//   part[z, p, n] = sum_{c in K-range z} a[p, c] * (q[e, n, c] - mid) * scale[e, n, c / bs]
+//   y[p, n] = sum_{c in K range z} a[p, c] * (q[e, n, c] - mid) * scale[e, n, c / bs]
 //
 // (ONNX GroupedMatMul-29, Summary, over weights dequantised as the QMoE
 // WebGPU manifest's description and derive.quantMidpoint state), organised so
 // that packed weights leave HBM exactly once, in long coalesced runs:
 //
-//  * a workgroup owns one K range (blockIdx.x), one expert tile (blockIdx.y)
-//    and RBW blocks of 32 weight rows per wavefront (blockIdx.z); it stages
-//    the tile's activation rows for that K range in LDS once and streams its
-//    row blocks one after another;
-//  * each wavefront streams ITEMS items of 16*NT weight rows x 128 bytes
-//    (whole cache lines), lane (n, g) loading 16 bytes of row n from each
-//    64-byte half; the item loop is fully unrolled and the next kP items'
-//    loads are in flight while one item is consumed, so every wait is exact;
+//  * a workgroup owns one expert tile (blockIdx.y), 256 weight rows
+//    (blockIdx.z, 32 per wavefront) and one K range (blockIdx.x; the whole of
+//    K unless there are too few workgroups to fill the chip).  It walks the
+//    range in stages; the tile's activation slice of the next stage is
+//    fetched while the current one is used (two LDS buffers, one barrier a
+//    stage), so each weight row is read front to back in one pass;
+//  * each wavefront streams items of 32 weight rows x 128 bytes (whole cache
+//    lines), lane (n, g) loading 16 bytes of row n from each 64-byte half; kP
+//    items are in flight while one is consumed, and only loads are in flight
+//    during the stream, so every wait is exact;
 //  * a cross-lane exchange (v_permlane32/16_swap) puts each lane's bytes in
 //    the matrix-core operand position; bytes are unpacked to exact f16
 //    (q - mid) in registers and multiplied by the f16 hi and lo parts of the
 //    activations on v_mfma_f32_16x16x32_f16 (fp32 accumulation);
-//  * block scales travel in the ring with the weights and are applied in fp32
-//    at the end of each scale block;
-//  * fp32 partial rows of all row blocks are stored once, after the stream
-//    (no stores interleave with the weight loads); qmoe_act (FC1) and the
-//    combine (FC2) sum the K ranges in a fixed order (no atomics).
+//  * block scales are loaded one stage ahead, shared across lanes with
+//    ds_bpermute, and applied in fp32 as each block closes;
+//  * results go through an LDS tile and leave as contiguous 16-byte stores:
+//    FC1 over the whole of K applies ReLU or interleaved SwiGLU there and
+//    writes FC2's operand rows directly; otherwise fp32 partial rows per K
+//    range are written, and qmoe_act (FC1) or the combine (FC2) sum the
+//    ranges in a fixed order (no atomics).
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.h"
@@ -38,12 +43,23 @@ namespace {
 #ifndef QMOE_STREAM_INFLIGHT
 #define QMOE_STREAM_INFLIGHT 2
 #endif
+#ifndef QMOE_STREAM_XCD_ORDER
+#define QMOE_STREAM_XCD_ORDER 0
+#endif
+#ifndef QMOE_STREAM_LATE_REFILL
+#define QMOE_STREAM_LATE_REFILL 1
+#endif
 #ifndef QMOE_STREAM_NT_LOADS
 #define QMOE_STREAM_NT_LOADS 0
 #endif
 constexpr int kSWaves = 8;  // wavefronts per workgroup
 constexpr int kCPI = 2;     // 64-byte chunks per item (one 128-byte line per row)
 constexpr int kP = QMOE_STREAM_INFLIGHT;  // items of loads in flight per wavefront while one is consumed
+#ifndef QMOE_STREAM_NT
+#define QMOE_STREAM_NT 2
+#endif
+constexpr int kNT = QMOE_STREAM_NT;  // 16-row weight subtiles per wavefront
+constexpr int kWGRows = kSWaves * 16 * kNT;  // weight rows per workgroup
 
 // Packed weights are read exactly once: optionally mark the loads streaming.
 __device__ __forceinline__ u32x4 load_weights(const uint8_t* p) {
@@ -72,37 +88,44 @@ __device__ __forceinline__ void exchange(u32x4& v) {
 
 }  // namespace
 
-// SPB: MFMA steps per scale block when blocks end inside a chunk; 0 when the
-// scales are column-wise or a block spans whole chunks.  RBW: row blocks of
-// kSWaves*16*NT rows that the workgroup streams one after another (the staged
-// activations are reused for all of them).
-template <int BITS, int MT, int NT, int ITEMS, int SCALE, int SPB, int RBW>
+// Template parameters: STG items per stage; SCALE mode; SPB = MFMA steps per
+// scale block when blocks end inside a chunk (0 when scales are column-wise or
+// a block spans whole chunks); FC1 = the A rows are the layer's fp32 input
+// (split into f16 hi/lo while staging) and the epilogue may apply the
+// activation; otherwise A rows are FC2 operand rows (f16 hi/lo groups).
+template <int BITS, int MT, int STG, int SCALE, int SPB, bool FC1>
 __global__ void __launch_bounds__(64 * kSWaves) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2, MT == 1 ? 4 : 2)))
 qmoe_stream(GemmArgs g) {
   constexpr int CC = BITS == 4 ? 128 : 64;      // codes per 64-byte chunk
   constexpr int NS = CC / 32;                   // MFMA steps per chunk
   constexpr int ROWS = 16 * MT;
-  constexpr int NCHR = ITEMS * kCPI;            // chunks in the K range
-  constexpr int LSTRIDE = NCHR * CC * 4;        // LDS bytes per activation row
+  constexpr int NT = kNT;
+  constexpr int SCH = STG * kCPI;               // chunks per stage
+  constexpr int SCODES = SCH * CC;              // codes per stage
+  constexpr int LSTRIDE = SCODES * 4;           // LDS bytes per activation row of a stage
+  constexpr int BUF = ROWS * LSTRIDE;           // bytes of one stage buffer
   constexpr int PIECES = LSTRIDE / 16;          // 16-byte pieces per row
-  constexpr int PPT = ROWS * PIECES / (64 * kSWaves);  // pieces per thread
-  static_assert(ROWS * PIECES % (64 * kSWaves) == 0, "staging must divide evenly");
-  constexpr int WROWS = kSWaves * 16 * NT;      // weight rows of one row block
-  constexpr int NITEMS = RBW * ITEMS;           // items streamed by each wavefront
-  extern __shared__ __align__(16) uint8_t lds[];  // [ROWS][LSTRIDE] activations
+  constexpr int GR = PIECES / 2;                // 8-code groups per row
+  constexpr int NTH = 64 * kSWaves;
+  constexpr int PPT = (ROWS * PIECES + NTH - 1) / NTH;  // staged pieces per thread (f16 rows)
+  constexpr int GPT = (ROWS * GR + NTH - 1) / NTH;      // staged groups per thread (fp32 rows)
+  // stages per loop trip: a whole number of ring turns, so ring slots are
+  // compile-time constants
+  constexpr int SPT = (STG % kP == 0) ? 1 : kP / STG;
+  static_assert(STG % kP == 0 || kP % STG == 0, "ring and stage sizes must nest");
+  extern __shared__ __align__(16) uint8_t lds[];  // 2 stage buffers, then the output tile
   __shared__ long s_rowbase[ROWS];
+  __shared__ int s_orow[ROWS];
 
-  // Block scales of the K range per weight row when blocks end inside a chunk
-  // (SPB > 0): NBR of them, Q per lane group.
-  constexpr int NBR = SPB > 0 ? NCHR * CC / (SPB * 32) : 4;
-  constexpr int Q = NBR / 4;
-  static_assert(SPB == 0 || (NBR % 4 == 0 && Q <= 8), "scale blocks per K range");
+  // Block scales of one stage per weight row when blocks end inside a chunk
+  // (SPB > 0): NBS of them, Q per lane group.
+  constexpr int NBS = SPB > 0 ? SCODES / (SPB * 32) : 4;
+  constexpr int Q = NBS / 4;
+  static_assert(SPB == 0 || (NBS % 4 == 0 && Q >= 1 && Q <= 4), "scale blocks per stage");
 
-  // Work w = (K range, expert tile, group of RBW row blocks), K range fastest.
-  // Workgroups are dealt to the 8 XCDs round robin by linear id; each XCD is
-  // given a contiguous run of work ids, so the K ranges of the same weight
-  // rows run side by side on one XCD and share its L2 (scale rows and
-  // activation slices are fetched from HBM once).
+#if QMOE_STREAM_XCD_ORDER
+  // Workgroups are dealt to the 8 XCDs round robin by linear id; give each
+  // XCD a contiguous run of work ids (K ranges of the same rows side by side).
   const int gx = gridDim.x, gy = gridDim.y;
   const int total = gx * gy * gridDim.z;
   const int lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
@@ -111,169 +134,171 @@ qmoe_stream(GemmArgs g) {
   const int split = w % gx;
   const int tile = (w / gx) % gy;
   const int rgroup = w / (gx * gy);
+#else
+  const int split = blockIdx.x;
+  const int tile = blockIdx.y;
+  const int rgroup = blockIdx.z;
+#endif
   if (tile >= g.ntiles[0]) return;
   const int e = g.tiles[4 * tile + 0];
   const int p0 = g.tiles[4 * tile + 1];
   const int rows = g.tiles[4 * tile + 2];
-  const int c0 = split * NCHR;
+  const int nst = g.nst;                 // stages in this K range
+  const int nit = nst * STG;             // items in this K range
+  const int c0 = split * nst * SCH;      // first chunk of the K range
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  // This wavefront's rows in row block r: rb0 + r * WROWS + nt * 16 + col.
-  const int rb0 = rgroup * RBW * WROWS + wave * 16 * NT;
-  const bool active = rb0 < g.N;  // all waves take part in the staging below
+  const int n0 = rgroup * kWGRows;       // first weight row of the workgroup
   const long ebase = (long)e * g.N;
   const long kb_bytes = g.kb;
 
-  // Per-subtile base pointers for row block 0; row block r adds r * WROWS rows
-  // (with RBW > 1 the rows of every block are in range: N is a multiple of
-  // RBW * WROWS).
+  // Rows past N (last row group) stream a clamped row; their results are dropped.
   const uint8_t* bbase[NT];
   const float* sbase[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const long row = ebase + min(rb0 + nt * 16 + col, g.N - 1);
+    const long row = ebase + min(n0 + wave * 16 * NT + nt * 16 + col, g.N - 1);
     bbase[nt] = g.wq + row * kb_bytes + grp * 16 + (long)c0 * 64;
     sbase[nt] = g.ws + row * g.nblk;
     if constexpr (SPB > 0) sbase[nt] += (c0 * CC) / (SPB * 32) + grp * Q;  // this lane group's blocks
   }
-  const long bstep = (long)WROWS * kb_bytes;  // bytes between row blocks
-  const long sstep = (long)WROWS * g.nblk;    // scales between row blocks
 
-  // Ring of kP items in flight: packed weights, plus the scales of blocks
-  // that span whole chunks.
+  // Ring of kP items: packed weights, plus the scales of blocks that span
+  // whole chunks.  Item indices past the range re-read its last item (kept
+  // unconditional so that the waits stay exact).
   u32x4 bq[kP][NT][kCPI];
   float sq[kP][NT][kCPI];
-  auto issue = [&](int slot, int it) {  // it is a compile-time constant after unrolling
-    const int r = it / ITEMS, il = it % ITEMS;
-    const int c = c0 + il * kCPI;
+  auto issue = [&](int slot, int it) {
+    const int itc = min(it, nit - 1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint8_t* src = bbase[nt] + r * bstep + il * kCPI * 64;
+      const uint8_t* src = bbase[nt] + (long)itc * (kCPI * 64);
 #pragma unroll
       for (int h = 0; h < kCPI; ++h) bq[slot][nt][h] = load_weights(src + h * 64);
       if constexpr (SCALE != SC_COL && SPB == 0) {
-        const float* sr = sbase[nt] + r * sstep;
 #pragma unroll
-        for (int h = 0; h < kCPI; ++h) sq[slot][nt][h] = sr[((c + h) * CC) / g.bs];
+        for (int h = 0; h < kCPI; ++h) sq[slot][nt][h] = sbase[nt][((c0 + itc * kCPI + h) * CC) / g.bs];
       }
     }
   };
-  // Blocks that end inside chunks: each lane group loads Q consecutive block
-  // scales of its row once per row block (one coalesced 16-byte-class load);
-  // a block's scale is then fetched from the owning lane group by ds_bpermute.
-  float sreg[2][NT][Q];
-  auto issue_scales = [&](int r) {
+  // Blocks that end inside chunks: each lane group loads its Q consecutive
+  // block scales of the stage (one 4- to 16-byte load), one stage ahead; a
+  // block's scale is then fetched from the owning lane group by ds_bpermute.
+  float snext[NT][Q], scur[NT][Q];
+  auto issue_scales = [&](int st) {
+    const int stc = min(st, nst - 1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float* sp = sbase[nt] + r * sstep;
+      const float* sp = sbase[nt] + stc * NBS;
+      if constexpr (Q == 4) {
+        const f32x4 v = *(const f32x4*)sp;
 #pragma unroll
-      for (int q4 = 0; q4 < Q; q4 += 4) {
-        if constexpr (Q >= 4) {
-          const f32x4 v = *(const f32x4*)(sp + q4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sreg[r & 1][nt][q4 + i] = v[i];
-        }
-      }
-      if constexpr (Q == 2) {
+        for (int i = 0; i < 4; ++i) snext[nt][i] = v[i];
+      } else if constexpr (Q == 2) {
         const float2 v = *(const float2*)sp;
-        sreg[r & 1][nt][0] = v.x;
-        sreg[r & 1][nt][1] = v.y;
-      } else if constexpr (Q == 1) {
-        sreg[r & 1][nt][0] = sp[0];
+        snext[nt][0] = v.x;
+        snext[nt][1] = v.y;
+      } else {
+        snext[nt][0] = sp[0];
       }
     }
   };
 
-  // Start the weight stream before the activation staging so that its latency
-  // overlaps the staging's dependent loads.
-  if (active) {
-    if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(0);
+  // Start the weight stream before anything else: its addresses depend only
+  // on the tile.
+  if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(0);
 #pragma unroll
-    for (int u = 0; u < kP && u < NITEMS; ++u) issue(u, u);
-  }
-  // Output rows (slot ids or sorted positions) for the epilogue.
-  int orow[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = min(mt * 16 + 4 * grp + i, rows - 1);
-      orow[mt][i] = g.store_by_slot ? g.perm[p0 + rr] : p0 + rr;
-    }
+  for (int u = 0; u < kP; ++u) issue(u, u);
 
-  // Stage activation rows [p0, p0 + ROWS) (clamped to valid rows) for the K
-  // range into LDS.  Row r keeps its 16-byte pieces with the piece index XOR-ed
-  // by (r & 15), so the 16 rows read by one instruction hit distinct banks.
+  // Activation row of every tile row (clamped to valid rows) and its output row.
   if (threadIdx.x < ROWS) {
     const int p = p0 + min((int)threadIdx.x, rows - 1);
-    const long ar = g.a_map ? (long)(g.a_map[p] / g.a_div) : (long)p;
+    const long ar = FC1 ? (long)(g.a_map[p] / g.a_div) : (long)p;
     s_rowbase[threadIdx.x] = ar * g.a_stride + (long)c0 * CC * 4;
+    s_orow[threadIdx.x] = g.store_by_slot ? g.perm[p] : p;
   }
   __syncthreads();
-  // Only the tile's valid rows are staged; matrix rows beyond them read the
-  // last valid row (their results are discarded).
-  if (g.a_f32) {
-    // fp32 rows (the layer input): each thread converts groups of 8 codes,
-    // 32 bytes of floats, into their 16-byte hi and lo pieces.
-    constexpr int GR = PIECES / 2;                                // groups per row
-    constexpr int GPT = (ROWS * GR + 64 * kSWaves - 1) / (64 * kSWaves);
-    f32x4 v[GPT][2];
+
+  // Activation staging of one stage: loads into registers, then LDS writes.
+  // Row r keeps its 16-byte pieces with the piece index XOR-ed by (r & 15), so
+  // the 16 rows read by one instruction hit distinct banks.  Invalid rows
+  // (>= rows) re-read the last valid row; loads are unconditional.
+  // The next stage's slice is fetched in NPART parts, one per item, each
+  // held in registers for one item only.
+  constexpr int NPART = FC1 ? (GPT % STG == 0 ? STG : 1) : (PPT % STG == 0 ? STG : 1);
+  constexpr int GPP = GPT / (FC1 ? NPART : 1);   // fp32 groups per thread per part
+  constexpr int PPP = PPT / (FC1 ? 1 : NPART);   // f16 pieces per thread per part
+  f32x4 areg32[FC1 ? GPP : 1][2];
+  u32x4 areg16[FC1 ? 1 : PPP];
+  auto stage_load = [&](int st, int part) {
+    const long off = (long)min(st, nst - 1) * SCODES * 4;
+    if constexpr (FC1) {
 #pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int idx = threadIdx.x + i * 64 * kSWaves;
-      const int r = idx / GR, gq = idx % GR;
-      // first code of storage group gq (see common.hpp): 4-bit groups hold
-      // their own 8 codes, 8-bit groups those of code group sigma(gq % 4)
-      const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
-      if (idx < ROWS * GR && r < rows) {
-        const float* src = (const float*)(g.a + s_rowbase[r]) + j0;
-        v[i][0] = *(const f32x4*)src;
-        v[i][1] = *(const f32x4*)(src + 4);
+      for (int ii = 0; ii < GPP; ++ii) {
+        const int i = part * GPP + ii;
+        const int idx = min((int)threadIdx.x + i * NTH, ROWS * GR - 1);
+        const int r = idx / GR, gq = idx % GR;
+        // first code of storage group gq (see common.hpp): 4-bit groups hold
+        // their own 8 codes, 8-bit groups those of code group sigma(gq % 4)
+        const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
+        const float* src = (const float*)(g.a + s_rowbase[min(r, rows - 1)] + off) + j0;
+        areg32[ii][0] = *(const f32x4*)src;
+        areg32[ii][1] = *(const f32x4*)(src + 4);
+      }
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < PPP; ++ii) {
+        const int i = part * PPP + ii;
+        const int idx = min((int)threadIdx.x + i * NTH, ROWS * PIECES - 1);
+        const int r = idx / PIECES, q = idx % PIECES;
+        areg16[ii] = *(const u32x4*)(g.a + s_rowbase[min(r, rows - 1)] + off + q * 16);
       }
     }
+  };
+  auto stage_store = [&](int buf, int part) {
+    uint8_t* base = lds + buf * BUF;
+    if constexpr (FC1) {
 #pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int idx = threadIdx.x + i * 64 * kSWaves;
-      const int r = idx / GR, gq = idx % GR;
-      if (idx < ROWS * GR && r < rows) {
-        f16x8 hi, lo;
+      for (int ii = 0; ii < GPP; ++ii) {
+        const int idx = threadIdx.x + (part * GPP + ii) * NTH;
+        const int r = idx / GR, gq = idx % GR;
+        if (idx < ROWS * GR) {
+          f16x8 hi, lo;
 #pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code inside the group at storage slot sl
-          _Float16 h, l;
-          split_f16(v[i][c >> 2][c & 3], h, l);
-          hi[sl] = h;
-          lo[sl] = l;
+          for (int sl = 0; sl < 8; ++sl) {
+            const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code inside the group at storage slot sl
+            _Float16 h, l;
+            split_f16(areg32[ii][c >> 2][c & 3], h, l);
+            hi[sl] = h;
+            lo[sl] = l;
+          }
+          uint8_t* row = base + r * LSTRIDE;
+          *(f16x8*)(row + (((2 * gq) ^ (r & 15)) * 16)) = hi;
+          *(f16x8*)(row + (((2 * gq + 1) ^ (r & 15)) * 16)) = lo;
         }
-        uint8_t* row = lds + r * LSTRIDE;
-        *(f16x8*)(row + (((2 * gq) ^ (r & 15)) * 16)) = hi;
-        *(f16x8*)(row + (((2 * gq + 1) ^ (r & 15)) * 16)) = lo;
+      }
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < PPP; ++ii) {
+        const int idx = threadIdx.x + (part * PPP + ii) * NTH;
+        const int r = idx / PIECES, q = idx % PIECES;
+        if (idx < ROWS * PIECES) *(u32x4*)(base + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = areg16[ii];
       }
     }
-  } else {
-    u32x4 v[PPT];
+  };
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int idx = threadIdx.x + i * 64 * kSWaves;
-      const int r = idx / PIECES, q = idx % PIECES;
-      if (r < rows) v[i] = *(const u32x4*)(g.a + s_rowbase[r] + q * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int idx = threadIdx.x + i * 64 * kSWaves;
-      const int r = idx / PIECES, q = idx % PIECES;
-      if (r < rows) *(u32x4*)(lds + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = v[i];
-    }
+  for (int part = 0; part < NPART; ++part) {
+    stage_load(0, part);
+    stage_store(0, part);
   }
+
   __syncthreads();
-  if (!active) return;
 
   f32x4 acc[MT][NT];
   f32x4 blk[MT][NT];
-  f32x4 res[RBW][MT][NT];  // finished row blocks, stored after the stream
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -288,12 +313,12 @@ qmoe_stream(GemmArgs g) {
   // The low four bits of q here are 8*(step parity) + 2*grp + (0 hi | 1 lo),
   // so the runtime part of every activation address is one of four per-lane
   // offsets per row subtile.
-  const uint8_t* lrow[MT];
+  int lrow[MT];
   int aoff[MT][2][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int ar = min(mt * 16 + col, rows - 1);
-    lrow[mt] = lds + ar * LSTRIDE;
+    lrow[mt] = ar * LSTRIDE;
 #pragma unroll
     for (int jp = 0; jp < 2; ++jp)
 #pragma unroll
@@ -302,109 +327,203 @@ qmoe_stream(GemmArgs g) {
 
   const UnpackMasks um = unpack_masks();
 
+  // One stage: its STG items from LDS buffer (st & 1), with the next stage's
+  // scales and activation slice fetched during the last item (issued before
+  // that item's ring refill, so waiting for them never waits for the refill).
+  // Q0 = position of the stage in the loop trip (compile-time), so ring slots
+  // are constants.
+  auto stage = [&](int st, auto q0c) {
+    constexpr int Q0 = decltype(q0c)::value;
+    const uint8_t* abuf = lds + (st & 1) * BUF;
+    if constexpr (SCALE == SC_BLOCK && SPB > 0) {
 #pragma unroll
-  for (int it = 0; it < NITEMS; ++it) {
-    // keep each item's work in its own scheduling region (bounded live ranges)
-    __builtin_amdgcn_sched_barrier(0);
-    const int u = it % kP;
-    const int r = it / ITEMS, il = it % ITEMS;
-    u32x4 cur[NT][kCPI];
-    float scur[NT][kCPI];
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+        for (int i = 0; i < Q; ++i) scur[nt][i] = snext[nt][i];
+    }
+#pragma unroll
+    for (int il = 0; il < STG; ++il) {
+      // keep each item's work in its own scheduling region (bounded live ranges)
+      __builtin_amdgcn_sched_barrier(0);
+      const int u = (Q0 * STG + il) % kP;
+      const int it = st * STG + il;
+#if QMOE_STREAM_LATE_REFILL
+      // consume the ring slot in place; it is refilled after the item
+      u32x4 (&cur)[NT][kCPI] = bq[u];
+      float (&sc1)[NT][kCPI] = sq[u];
+#else
+      u32x4 cur[NT][kCPI];
+      float sc1[NT][kCPI];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int h = 0; h < kCPI; ++h) {
+          cur[nt][h] = bq[u][nt][h];
+          sc1[nt][h] = sq[u][nt][h];
+        }
+#endif
+      if (il == STG - 1)
+        if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(st + 1);
+      if (NPART == STG || il == STG - 1) stage_load(st + 1, NPART == STG ? il : 0);
+#if !QMOE_STREAM_LATE_REFILL
+      issue(u, it + kP);
+#endif
 #pragma unroll
       for (int h = 0; h < kCPI; ++h) {
-        cur[nt][h] = bq[u][nt][h];
-        scur[nt][h] = sq[u][nt][h];
-      }
-    }
-    if constexpr (SCALE == SC_BLOCK && SPB > 0)
-      if (il == 0 && r + 1 < RBW) issue_scales(r + 1);  // next row block's scales
-    if (it + kP < NITEMS) issue(u, it + kP);
+        const int cl = il * kCPI + h;  // chunk index inside the stage
 #pragma unroll
-    for (int h = 0; h < kCPI; ++h) {
-      const int cl = il * kCPI + h;  // chunk index inside the K range
+        for (int nt = 0; nt < NT; ++nt) exchange<BITS>(cur[nt][h]);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) exchange<BITS>(cur[nt][h]);
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        __builtin_amdgcn_sched_barrier(0);  // one step at a time: bounded live operands
-        f16x8 ahi[MT], alo[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int qhigh = ((cl * NS + j) * 8) & ~15;  // compile-time part of the piece index
-          ahi[mt] = *(const f16x8*)(lrow[mt] + qhigh * 16 + aoff[mt][j & 1][0]);
-          alo[mt] = *(const f16x8*)(lrow[mt] + qhigh * 16 + aoff[mt][j & 1][1]);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const f16x8 b = chunk_operand<BITS>(cur[nt][h], j, um);
+        for (int j = 0; j < NS; ++j) {
+          __builtin_amdgcn_sched_barrier(0);  // one step at a time: bounded live operands
+          f16x8 ahi[MT], alo[MT];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            if constexpr (SCALE == SC_COL) {
-              acc[mt][nt] = mfma16(ahi[mt], b, acc[mt][nt]);
-              acc[mt][nt] = mfma16(alo[mt], b, acc[mt][nt]);
-            } else if constexpr (SPB > 0) {
-              if (j % SPB == 0) blk[mt][nt] = mfma16(ahi[mt], b, zero4);
-              else blk[mt][nt] = mfma16(ahi[mt], b, blk[mt][nt]);
-              blk[mt][nt] = mfma16(alo[mt], b, blk[mt][nt]);
-              if (j % SPB == SPB - 1) {
-                // block of SPB*32 codes ends inside the chunk: apply its scale
-                const int b = (cl * CC + j * 32) / (SPB * 32);  // block inside the K range
-                const float sc = __shfl(sreg[r & 1][nt][b % Q], col + 16 * (b / Q));
-                acc[mt][nt] += blk[mt][nt] * sc;
-                pin(acc[mt][nt]);
+            const int qhigh = ((cl * NS + j) * 8) & ~15;  // compile-time part of the piece index
+            ahi[mt] = *(const f16x8*)(abuf + lrow[mt] + qhigh * 16 + aoff[mt][j & 1][0]);
+            alo[mt] = *(const f16x8*)(abuf + lrow[mt] + qhigh * 16 + aoff[mt][j & 1][1]);
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const f16x8 b = chunk_operand<BITS>(cur[nt][h], j, um);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              if constexpr (SCALE == SC_COL) {
+                acc[mt][nt] = mfma16(ahi[mt], b, acc[mt][nt]);
+                acc[mt][nt] = mfma16(alo[mt], b, acc[mt][nt]);
+              } else if constexpr (SPB > 0) {
+                if (j % SPB == 0) blk[mt][nt] = mfma16(ahi[mt], b, zero4);
+                else blk[mt][nt] = mfma16(ahi[mt], b, blk[mt][nt]);
+                blk[mt][nt] = mfma16(alo[mt], b, blk[mt][nt]);
+                if (j % SPB == SPB - 1) {
+                  // block of SPB*32 codes ends inside the chunk: apply its scale
+                  const int bk = (cl * CC + j * 32) / (SPB * 32);  // block inside the stage
+                  const float sc = __shfl(scur[nt][bk % Q], col + 16 * (bk / Q));
+                  acc[mt][nt] += blk[mt][nt] * sc;
+                  pin(acc[mt][nt]);
+                }
+              } else {
+                blk[mt][nt] = mfma16(ahi[mt], b, blk[mt][nt]);
+                blk[mt][nt] = mfma16(alo[mt], b, blk[mt][nt]);
               }
-            } else {
-              blk[mt][nt] = mfma16(ahi[mt], b, blk[mt][nt]);
-              blk[mt][nt] = mfma16(alo[mt], b, blk[mt][nt]);
             }
           }
         }
-      }
-      if constexpr (SCALE != SC_COL && SPB == 0) {
-        // end of a scale block, or end of this K range's share of one
-        if ((c0 + cl + 1) % cpb == 0 || cl == NCHR - 1) {
+        if constexpr (SCALE != SC_COL && SPB == 0) {
+          // end of a scale block, or end of this K range's share of one
+          const int chunk = c0 + it * kCPI + h;
+          if ((chunk + 1) % cpb == 0 || (it == nit - 1 && h == kCPI - 1)) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              acc[mt][nt] += blk[mt][nt] * scur[nt][h];
-              pin(acc[mt][nt]);
-              blk[mt][nt] = zero4;
-            }
+              for (int mt = 0; mt < MT; ++mt) {
+                acc[mt][nt] += blk[mt][nt] * sc1[nt][h];
+                pin(acc[mt][nt]);
+                blk[mt][nt] = zero4;
+              }
+          }
         }
       }
+#if QMOE_STREAM_LATE_REFILL
+      issue(u, it + kP);
+#endif
+      // Publish this part of the next stage's activations: its buffer was last
+      // read in the previous stage, which every wavefront finished before the
+      // last barrier.
+      if (NPART == STG || il == STG - 1)
+        if (st + 1 < nst) stage_store((st + 1) & 1, NPART == STG ? il : 0);
     }
-    if (il == ITEMS - 1) {
-      // row block r finished: keep it until the stream ends
+    __syncthreads();
+  };
+
+  const int nmain = nst - nst % SPT;
+  for (int s0 = 0; s0 < nmain; s0 += SPT) {
+    stage(s0, std::integral_constant<int, 0>{});
+    if constexpr (SPT > 1) stage(s0 + 1, std::integral_constant<int, 1>{});
+  }
+  if constexpr (SPT > 1)
+    if (nmain < nst) stage(nmain, std::integral_constant<int, 0>{});
+
+  // Output: every wavefront puts its rows (column scales applied) into the
+  // LDS tile [ROWS][kWGRows] (the stage buffers are free after the last
+  // barrier); tile columns are XOR-swizzled by 16 * ((row / 4) % 4), so the
+  // four row groups of one write hit distinct banks.
+  float* otile = reinterpret_cast<float*>(lds);
+  auto tix = [](int rr, int c) { return rr * kWGRows + (c ^ (16 * ((rr >> 2) & 3))); };
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+  for (int nt = 0; nt < NT; ++nt) {
+    const int c = wave * 16 * NT + nt * 16 + col;  // tile column
+    float sc = 1.f;
+    if constexpr (SCALE == SC_COL) sc = g.ws[ebase + min(n0 + c, g.N - 1)];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          res[r][mt][nt] = acc[mt][nt];
-          acc[mt][nt] = zero4;
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = mt * 16 + 4 * grp + i;
+        if (rr < rows) otile[tix(rr, c)] = acc[mt][nt][i] * sc;
+      }
+  }
+  __syncthreads();
+
+  if (FC1 && g.act != nullptr) {
+    // Whole of K: apply the activation and write FC2 operand rows (f16 hi/lo
+    // groups, storage order of common.hpp) for this workgroup's codes.
+    // ReLU: code j = row n.  Interleaved SwiGLU: code j takes rows 2j (gate)
+    // and 2j + 1 (linear): g * sigmoid(alpha * g) * (u + beta).
+    const bool swiglu = g.act_swiglu != 0;
+    const int I = swiglu ? g.N / 2 : g.N;
+    const int jw = swiglu ? kWGRows / 2 : kWGRows;   // codes of this workgroup (whole 32-code blocks)
+    const int jbase = swiglu ? n0 / 2 : n0;
+    const int gtot = (int)(g.act_stride / 32);       // groups per operand row
+    for (int idx = threadIdx.x; idx < rows * (jw / 8); idx += NTH) {
+      const int rr = idx / (jw / 8);
+      const int gq = jbase / 8 + idx % (jw / 8);
+      if (gq >= gtot) continue;
+      const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
+      float a[8];
+      if (swiglu) {
+        const int t0 = 2 * (j0 - jbase);  // tile column of row 2*j0 (16 consecutive columns)
+        f32x4 v[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float gv = v[c >> 1][2 * (c & 1)], uv = v[c >> 1][2 * (c & 1) + 1];
+          a[c] = j0 + c < I ? gv / (1.f + expf(-g.alpha * gv)) * (uv + g.beta) : 0.f;
         }
+      } else {
+        const int t0 = j0 - jbase;
+        f32x4 v[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a[c] = j0 + c < I ? fmaxf(v[c >> 2][c & 3], 0.f) : 0.f;
+      }
+      f16x8 hi, lo;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code j0 + c sits at storage slot sl
+        _Float16 hh, ll;
+        split_f16(a[c], hh, ll);
+        hi[sl] = hh;
+        lo[sl] = ll;
+      }
+      uint8_t* dst = g.act + (long)(p0 + rr) * g.act_stride + (long)gq * 32;
+      *(f16x8*)dst = hi;
+      *(f16x8*)(dst + 16) = lo;
+    }
+  } else if ((g.N & 3) == 0) {
+    for (int idx = threadIdx.x; idx < rows * (kWGRows / 4); idx += NTH) {
+      const int rr = idx / (kWGRows / 4), c = 4 * (idx % (kWGRows / 4));
+      if (n0 + c < g.N)
+        *(f32x4*)(g.slot_out + ((long)split * g.S + s_orow[rr]) * g.N + n0 + c) = *(const f32x4*)(otile + tix(rr, c));
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < rows * kWGRows; idx += NTH) {
+      const int rr = idx / kWGRows, c = idx % kWGRows;
+      if (n0 + c < g.N) g.slot_out[((long)split * g.S + s_orow[rr]) * g.N + n0 + c] = otile[tix(rr, c)];
     }
   }
-
-  // Column scales, then the fp32 partial rows of every row block.
-#pragma unroll
-  for (int r = 0; r < RBW; ++r)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = rb0 + r * WROWS + nt * 16 + col;
-      float sc = 1.f;
-      if constexpr (SCALE == SC_COL) sc = g.ws[ebase + min(n, g.N - 1)];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = mt * 16 + 4 * grp + i;
-          if (rr < rows && n < g.N)
-            g.slot_out[((long)split * g.S + orow[mt][i]) * g.N + n] = res[r][mt][nt][i] * sc;
-        }
-    }
 }
 
 // FC1 epilogue for the streamed path: sum the K-range partials of each
@@ -479,9 +598,9 @@ __global__ void __launch_bounds__(256) qmoe_act(const float* __restrict__ part, 
 
 namespace {
 
-template <int BITS, int MT, int NT, int ITEMS, int SCALE, int SPB, int RBW>
+template <int BITS, int MT, int STG, int SCALE, int SPB, bool FC1>
 hipError_t go(const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
-  auto kern = qmoe_stream<BITS, MT, NT, ITEMS, SCALE, SPB, RBW>;
+  auto kern = qmoe_stream<BITS, MT, STG, SCALE, SPB, FC1>;
   // Dynamic LDS above the 64 KB default needs a per-kernel opt-in (host-side,
   // no synchronisation); remember the largest size granted so far.
   static std::atomic<size_t> granted{64 * 1024};
@@ -494,58 +613,45 @@ hipError_t go(const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BITS, int MT, int NT, int ITEMS, int RBW>
+template <int BITS, int MT, int STG, bool FC1>
 hipError_t pick_scale(const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
   constexpr int CC = BITS == 4 ? 128 : 64;
-  if (g.bs == 0) return go<BITS, MT, NT, ITEMS, SC_COL, 0, RBW>(g, grid, lds, st);
-  if (g.bs >= CC) return go<BITS, MT, NT, ITEMS, SC_BLOCK, 0, RBW>(g, grid, lds, st);
-  if (g.bs == 32) return go<BITS, MT, NT, ITEMS, SC_BLOCK, 1, RBW>(g, grid, lds, st);
+  if (g.bs == 0) return go<BITS, MT, STG, SC_COL, 0, FC1>(g, grid, lds, st);
+  if (g.bs >= CC) return go<BITS, MT, STG, SC_BLOCK, 0, FC1>(g, grid, lds, st);
+  if (g.bs == 32) return go<BITS, MT, STG, SC_BLOCK, 1, FC1>(g, grid, lds, st);
   if constexpr (BITS == 4) {
-    if (g.bs == 64) return go<BITS, MT, NT, ITEMS, SC_BLOCK, 2, RBW>(g, grid, lds, st);
+    if (g.bs == 64) return go<BITS, MT, STG, SC_BLOCK, 2, FC1>(g, grid, lds, st);
   }
   return hipErrorInvalidValue;  // scale layouts the planner never routes here
 }
 
-// Item counts per K range allowed by the 64 KB activation slice (16*MT rows,
-// 4 bytes a code, 256 or 128 codes an item).
-template <int BITS, int MT>
-constexpr int max_items() { return 65536 / (64 * MT * (BITS == 4 ? 256 : 128)); }
-
-template <int BITS, int MT, int RBW>
-hipError_t pick_items(int items, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
-  constexpr int MX = max_items<BITS, MT>();
-  if (items == 1) return pick_scale<BITS, MT, 2, 1, RBW>(g, grid, lds, st);
-  if constexpr (MX >= 2) if (items == 2) return pick_scale<BITS, MT, 2, 2, RBW>(g, grid, lds, st);
-  if constexpr (MX >= 4) if (items == 4) return pick_scale<BITS, MT, 2, 4, RBW>(g, grid, lds, st);
-  if constexpr (MX >= 8) if (items == 8) return pick_scale<BITS, MT, 2, 8, RBW>(g, grid, lds, st);
-  return hipErrorInvalidValue;
-}
-
-template <int BITS, int MT>
-hipError_t pick_rbw(int rbw, int items, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
-  if (rbw == 2) return pick_items<BITS, MT, 2>(items, g, grid, lds, st);
-  return pick_items<BITS, MT, 1>(items, g, grid, lds, st);
-}
-
-template <int BITS>
-hipError_t pick_mt(int mt, int rbw, int items, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
+template <int BITS, bool FC1>
+hipError_t pick_mt(int mt, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
   switch (mt) {
-    case 1: return pick_rbw<BITS, 1>(rbw, items, g, grid, lds, st);
-    case 2: return pick_rbw<BITS, 2>(1, items, g, grid, lds, st);
-    case 3: return pick_rbw<BITS, 3>(1, items, g, grid, lds, st);
-    default: return pick_rbw<BITS, 4>(1, items, g, grid, lds, st);
+    case 1: return pick_scale<BITS, 1, 2, FC1>(g, grid, lds, st);
+    case 2: return pick_scale<BITS, 2, 1, FC1>(g, grid, lds, st);
+    case 3: return pick_scale<BITS, 3, 1, FC1>(g, grid, lds, st);
+    default: return pick_scale<BITS, 4, 1, FC1>(g, grid, lds, st);
   }
 }
 
 }  // namespace
 
-hipError_t launch_stream(int bits, int mt, int items, int rbw, int splits, const GemmArgs& g, int max_tiles,
-                         hipStream_t st) {
-  const int cc = bits == 4 ? 128 : 64;
-  const int rows_per_wg = kSWaves * 16 * 2 * (mt == 1 ? rbw : 1);
-  const size_t lds = (size_t)16 * mt * items * kCPI * cc * 4;
-  const dim3 grid(splits, max_tiles, (g.N + rows_per_wg - 1) / rows_per_wg);
-  return bits == 4 ? pick_mt<4>(mt, rbw, items, g, grid, lds, st) : pick_mt<8>(mt, rbw, items, g, grid, lds, st);
+int stream_stage_items(int mt) { return mt == 1 ? 2 : 1; }
+
+size_t stream_lds_bytes(int bits, int mt) {
+  const int item_codes = bits == 4 ? 256 : 128;
+  const size_t stage = (size_t)16 * mt * stream_stage_items(mt) * item_codes * 4;
+  return std::max(2 * stage, (size_t)16 * mt * kWGRows * 4);
+}
+
+hipError_t launch_stream(int bits, int mt, int stg, int splits, const GemmArgs& g, int max_tiles, hipStream_t st) {
+  if (stg != stream_stage_items(mt) || mt < 1 || mt > 4) return hipErrorInvalidValue;
+  const size_t lds = stream_lds_bytes(bits, mt);
+  const dim3 grid(splits, max_tiles, (g.N + kWGRows - 1) / kWGRows);
+  const bool fc1 = g.a_f32 != 0;
+  if (bits == 4) return fc1 ? pick_mt<4, true>(mt, g, grid, lds, st) : pick_mt<4, false>(mt, g, grid, lds, st);
+  return fc1 ? pick_mt<8, true>(mt, g, grid, lds, st) : pick_mt<8, false>(mt, g, grid, lds, st);
 }
 
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,

@@ -122,12 +122,22 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g1.S = S;
     const int epi1 = d.act == QMOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
     if (p.s1.on) {
-      float* part1 = reinterpret_cast<float*>(ws + p.off_part1);
       g1.store_by_slot = 0;
-      g1.slot_out = part1;
-      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.items, p.s1.rbw, p.s1.splits, g1, (int)p.max_tiles, s));
-      QMOE_TRY_HIP(mark(2));
-      QMOE_TRY_HIP(launch_act(d.bits, epi1, part1, p.s1.splits, S, (int)d.F, I, (int)p.kp2, d.alpha, d.beta, act, s));
+      g1.nst = p.s1.nst;
+      g1.act_swiglu = d.act == QMOE_ACT_SWIGLU;
+      if (p.s1.splits == 1) {
+        // whole of K per workgroup: the kernel applies the activation itself
+        QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.stg, 1, g1, (int)p.max_tiles, s));
+        QMOE_TRY_HIP(mark(2));
+      } else {
+        float* part1 = reinterpret_cast<float*>(ws + p.off_part1);
+        g1.act = nullptr;
+        g1.slot_out = part1;
+        QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.stg, p.s1.splits, g1, (int)p.max_tiles, s));
+        QMOE_TRY_HIP(mark(2));
+        QMOE_TRY_HIP(launch_act(d.bits, epi1, part1, p.s1.splits, S, (int)d.F, I, (int)p.kp2, d.alpha, d.beta, act,
+                                s));
+      }
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, epi1, p.mt, p.aligned, g1, (int)p.max_tiles, s));
       QMOE_TRY_HIP(mark(2));
@@ -152,7 +162,8 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g2.S = S;
     if (p.s2.on) {
       g2.store_by_slot = 1;
-      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.items, p.s2.rbw, p.s2.splits, g2, (int)p.max_tiles, s));
+      g2.nst = p.s2.nst;
+      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.stg, p.s2.splits, g2, (int)p.max_tiles, s));
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
     }

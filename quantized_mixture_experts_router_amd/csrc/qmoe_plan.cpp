@@ -8,6 +8,15 @@
 
 #include <algorithm>
 
+// Workgroups the streaming kernels aim for before splitting K (two per
+// compute unit on 256 compute units).
+#ifndef QMOE_STREAM_NT
+#define QMOE_STREAM_NT 2
+#endif
+#ifndef QMOE_STREAM_MIN_WORKGROUPS
+#define QMOE_STREAM_MIN_WORKGROUPS 512
+#endif
+
 namespace qmoe {
 namespace {
 
@@ -19,11 +28,6 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // The streaming kernel needs whole 128-byte row items and scale blocks of at
 // least one 32-code matrix step.
-bool stream_ok(int bits, int64_t K, int64_t bs) {
-  const int64_t item_codes = bits == 4 ? 256 : 128;
-  return K > 0 && K % item_codes == 0 && (bs == 0 || bs >= 32);
-}
-
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool rank_ok(const qmoe_tensor* t, int r) { return t->rank == r; }
@@ -125,7 +129,9 @@ void make_plan(const Dims& d, Plan* p) {
   p->decode = d.T <= 64;
   p->mt = p->decode ? int((d.T + 15) / 16) : 4;
   p->bm = 16 * p->mt;
-  p->max_tiles = (p->S + p->bm - 1) / p->bm + d.E;
+  // Sum over experts of ceil(count / bm) <= ceil(S / bm) + E; when one tile
+  // holds any expert's rows it is at most E (one tile per used expert).
+  p->max_tiles = p->decode ? d.E : (p->S + p->bm - 1) / p->bm + d.E;
   // With I == 0 only the routing stages run (output is a zero fill).
   p->kp1 = d.I > 0 ? round_up(d.H, 128) : 0;
   p->kp2 = round_up(d.I, 128);
@@ -133,26 +139,33 @@ void make_plan(const Dims& d, Plan* p) {
   p->nchunks = (p->S + p->chunk - 1) / p->chunk;
   p->small_front = p->S <= 1024 && d.E <= 1024;
   if (p->decode && d.I > 0) {
+    // Weight-streaming kernels: stages of stg items (256 codes an item at 4
+    // bits, 128 at 8); the stages must tile K.  Scale blocks that end inside a
+    // 64-byte chunk (bs < codes per chunk) must come 4 to 16 to a stage.
     const int64_t item_codes = d.bits == 4 ? 256 : 128;
-    // Items per K range: the tile's activation rows for the range (16*mt rows,
-    // 4 bytes a code) must fit 64 KB of LDS (two workgroups per compute unit),
-    // and the ranges must tile K exactly.
-    constexpr int64_t kLdsBudget = 64 * 1024;
-    auto lds_bytes = [&](int64_t items) { return 16 * p->mt * items * item_codes * 4; };
+    const int64_t chunk_codes = item_codes / 2;
     auto shape = [&](Plan::Stream& st, int64_t K, int64_t N) {
-      st.on = stream_ok(d.bits, K, d.bs);
+      st.stg = p->mt == 1 ? 2 : 1;
+      const int64_t scodes = st.stg * item_codes;
+      st.on = K > 0 && K % scodes == 0 && (d.bs == 0 || d.bs >= 32);
+      if (st.on && d.bs > 0 && d.bs < chunk_codes) {
+        const int64_t nbs = scodes / d.bs;
+        st.on = nbs % 4 == 0 && nbs <= 16;
+      }
       if (!st.on) return;
-      const int64_t nit = K / item_codes;
-      int ipr = 0;
-      for (int cand : {8, 4, 2, 1})
-        if (lds_bytes(cand) <= kLdsBudget && nit % cand == 0) { ipr = cand; break; }
-      st.on = ipr > 0;
-      st.items = ipr;
-      st.splits = (int)(nit / ipr);
-      // Two row blocks of 256 rows per workgroup amortise the activation
-      // staging (when they tile N exactly); 32-code scale blocks need the
-      // registers for their scales instead.
-      st.rbw = (p->mt == 1 && d.bs != 32 && N % 512 == 0) ? 2 : 1;
+      // Whole of K per workgroup unless the row groups alone cannot fill the
+      // chip (two workgroups on each of 256 compute units): then the fewest K
+      // ranges that do.
+      const int64_t nst_total = K / scodes;
+      const int64_t units = d.E * ceil_div(N, 128 * QMOE_STREAM_NT);
+      int64_t splits = nst_total;
+      for (int64_t z = 1; z <= nst_total; ++z)
+        if (nst_total % z == 0 && units * z >= QMOE_STREAM_MIN_WORKGROUPS) {
+          splits = z;
+          break;
+        }
+      st.splits = (int)splits;
+      st.nst = (int)(nst_total / splits);
     };
     shape(p->s1, d.H, d.F);
     shape(p->s2, d.I, d.H);
@@ -171,7 +184,7 @@ void make_plan(const Dims& d, Plan* p) {
   p->off_xa = take(p->s1.on ? 0 : size_t(4) * d.T * p->kp1);  // f16 hi + lo per element (streaming FC1 reads fp32 rows)
   p->off_act = take(size_t(4) * p->S * p->kp2);   // f16 hi + lo per element
   p->off_slot = take(d.I > 0 ? sizeof(float) * p->splits2 * p->S * d.H : 0); // FC2 rows by slot id
-  p->off_part1 = take(p->s1.on ? sizeof(float) * p->s1.splits * p->S * d.F : 0);
+  p->off_part1 = take(p->s1.on && p->s1.splits > 1 ? sizeof(float) * p->s1.splits * p->S * d.F : 0);
   p->bytes = o;
 }
 

@@ -48,12 +48,12 @@ struct Plan {
   // weight-streaming kernels (decode): used per GEMM when its shapes allow
   struct Stream {
     bool on = false;
-    int items = 4;       // 128-byte row items per wavefront (one K range)
-    int rbw = 1;         // row blocks streamed per workgroup (register budget)
+    int stg = 2;         // 128-byte row items per stage (activation slice per LDS buffer)
+    int nst = 1;         // stages per K range
     int splits = 1;      // K ranges (fp32 partials summed afterwards, in order)
   } s1, s2;
   int splits2 = 1;       // FC2 partial sets the combine sums (1 off the stream path)
-  size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path)
+  size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path with K ranges)
   bool small_front = false;  // router + permutation in one workgroup (S, E <= 1024)
   int64_t chunk = 1024;  // slots per permutation block
   int64_t nchunks = 0;
