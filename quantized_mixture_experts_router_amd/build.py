@@ -22,6 +22,7 @@ SOURCES = [
     "kernels/route.hip",
     "kernels/gemm.hip",
     "kernels/stream.hip",
+    "kernels/tiled.hip",
 ]
 
 ARCH = os.environ.get("QMOE_OFFLOAD_ARCH", "gfx950")

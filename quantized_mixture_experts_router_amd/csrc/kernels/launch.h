@@ -54,6 +54,10 @@ enum { SC_COL = 0, SC_BLOCK = 1, SC_BLOCK16 = 2 };
 
 hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& g, int max_tiles, hipStream_t st);
 
+// LDS-tiled variant (see tiled.hip): 128-row tiles, K a multiple of 64,
+// column-wise or >= 32-code block scales, 8-code-aligned rows, N % 4 == 0.
+hipError_t launch_tiled(int bits, int epi, const GemmArgs& g, int max_tiles, hipStream_t st);
+
 // Weight-streaming variant for small token counts (see stream.hip).  FC1
 // (g.a_f32 set): A rows are the fp32 input; with g.act set (one K range) the
 // kernel writes FC2 operand rows after the activation, else fp32 partial rows

@@ -1,0 +1,351 @@
+// LDS-tiled grouped GEMM for the QMoE expert FFN at larger token counts, on
+// gfx950 matrix cores (v_mfma_f32_16x16x32_f16):
+//
+//   y[p, n] = sum_c a[p, c] * (q[e, n, c] - mid) * scale[e, n, c / bs]
+//
+// for the expert-sorted rows p of one 128-row tile of expert e (the
+// GroupedMatMul of the ONNX GroupedMatMul-29 page, Summary, over weights
+// dequantised as the QMoE WebGPU manifest's description and
+// derive.quantMidpoint state).  FC1 epilogue: ReLU, or interleaved SwiGLU
+// g*sigmoid(alpha*g)*(u+beta) on row pairs (2j, 2j+1) (manifest
+// attributeDescriptions.swiglu_fusion, activation_alpha, activation_beta),
+// written as FC2's f16 hi/lo operand rows.  FC2 epilogue: rows are written at
+// their slot id, so the combine gathers them without atomics.
+//
+// Work decomposition: a workgroup of 8 wavefronts computes a 128 x 256 tile
+// (2 x 4 wavefronts of 64 x 64).  Each 64-code K step stages the tile's
+// activation slice (f16 hi/lo, 32 KB) and packed weight slice (8 or 16 KB)
+// plus its block scales in LDS, double buffered: the next step's global loads
+// are in flight while the current step runs on the matrix cores.  Weights
+// are unpacked from LDS straight into matrix-core operands (exact f16 q - mid)
+// and each fragment feeds 8 instructions (4 row subtiles x hi/lo).
+// Workgroups are ordered so that the ones resident on an XCD at the same time
+// cover 8 row tiles x 4 column tiles: both operands are reused from that
+// XCD's L2.
+#include <algorithm>
+#include <atomic>
+
+#include "common.hpp"
+#include "launch.h"
+
+namespace qmoe {
+
+namespace {
+
+constexpr int kTM = 128;           // tile rows (expert-sorted activation rows)
+constexpr int kTN = 256;           // tile columns (weight rows)
+constexpr int kTK = 64;            // codes per K step
+constexpr int kTWaves = 8;         // 2 (rows) x 4 (columns) wavefronts of 64 x 64
+constexpr int kTThreads = 64 * kTWaves;
+constexpr int kGroupM = 8;         // row tiles per tile group (L2 reuse)
+constexpr int kABuf = kTM * kTK * 4;  // activation slice: 128 rows x 256 bytes
+
+template <int BITS>
+struct TiledLayout {
+  static constexpr int kBRow = kTK * BITS / 8;      // packed bytes per weight row per step
+  static constexpr int kBStride = kBRow + 16;       // LDS row stride (bank spread)
+  static constexpr int kBBuf = kTN * kBStride;
+  static constexpr int kSBuf = kTN * 2 * 4;         // up to two block scales per row per step
+  static constexpr int kStage = kABuf + kBBuf + kSBuf;
+  static constexpr int kLds = 2 * kStage;           // also holds the 64 x 256 fp32 epilogue tile
+  static_assert(kLds >= 64 * kTN * 4, "epilogue tile must fit");
+};
+
+// Eight codes [32*j + 8*cg, +8) of a staged weight row as exact f16 (q - mid)
+// in A-row storage order (see common.hpp).
+template <int BITS>
+__device__ __forceinline__ f16x8 tile_operand(const uint8_t* row, int j, int cg, const UnpackMasks& m) {
+  if constexpr (BITS == 4) {
+    return unpack4(*(const uint32_t*)(row + 16 * j + 4 * cg), m);
+  } else {
+    const u32x2 v = *(const u32x2*)(row + 32 * j + 8 * cg);
+    return unpack8x2(v[0], v[1]);
+  }
+}
+
+}  // namespace
+
+template <int BITS, int SCALE, int EPI>
+__global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
+  using L = TiledLayout<BITS>;
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ long s_arow[kTM];
+  __shared__ int s_orow[kTM];
+
+  // Tile order: each XCD (workgroups are dealt round robin by linear id)
+  // takes a contiguous run of work ids; work ids run over groups of kGroupM
+  // row tiles, column tile by column tile, row tile fastest.
+  const int total = gridDim.x;
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, per = total >> 3, extra = total & 7;
+  const int w = xcd * per + min(xcd, extra) + (lin >> 3);
+  const int mtiles = total / ntn;
+  const int grp0 = (w / (kGroupM * ntn)) * kGroupM;
+  const int gsize = min(kGroupM, mtiles - grp0);
+  const int wr = w % (kGroupM * ntn);
+  const int tile = grp0 + wr % gsize;
+  const int ntile = wr / gsize;
+  if (tile >= g.ntiles[0]) return;
+  const int e = g.tiles[4 * tile + 0];
+  const int p0 = g.tiles[4 * tile + 1];
+  const int rows = g.tiles[4 * tile + 2];
+  const int n0 = ntile * kTN;
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int col = lane & 15, grp = lane >> 4;
+  const long ebase = (long)e * g.N;
+
+  if (tid < kTM) {
+    const int p = p0 + min(tid, rows - 1);
+    const long ar = g.a_map ? (long)(g.a_map[p] / g.a_div) : (long)p;
+    s_arow[tid] = ar * g.a_stride;
+    s_orow[tid] = g.store_by_slot ? g.perm[p] : p;
+  }
+  __syncthreads();
+
+  // Global -> register staging of one K step (loads are unconditional:
+  // rows past the tile or past N re-read a valid row).
+  constexpr int BPT = L::kBRow * kTN / 16 / kTThreads;  // 16-byte weight pieces per thread
+  u32x4 ra[4], rb[BPT];
+  float rs[2];
+  const int nk = g.K / kTK;
+  const uint8_t* bsrc[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    const int idx = tid + i * kTThreads;
+    const int r = idx / (L::kBRow / 16), q = idx % (L::kBRow / 16);
+    bsrc[i] = g.wq + (ebase + min(n0 + r, g.N - 1)) * (long)g.kb + q * 16;
+  }
+  const float* ssrc = g.ws + (ebase + min(n0 + (tid & (kTN - 1)), g.N - 1)) * (long)g.nblk;
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + i * kTThreads;
+      const int r = idx >> 4, q = idx & 15;
+      ra[i] = *(const u32x4*)(g.a + s_arow[r] + (long)kt * (kTK * 4) + q * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) rb[i] = *(const u32x4*)(bsrc[i] + (long)kt * L::kBRow);
+    if constexpr (SCALE == SC_BLOCK) {
+      // scales of the blocks that end in this step (two when bs == 32)
+      if (g.bs == 32) {
+        const float2 v = *(const float2*)(ssrc + 2 * kt);
+        rs[0] = v.x;
+        rs[1] = v.y;
+      } else {
+        rs[0] = ssrc[(kt * kTK) / g.bs];
+        rs[1] = rs[0];
+      }
+    }
+  };
+  auto store = [&](int buf) {
+    uint8_t* base = lds + buf * L::kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + i * kTThreads;
+      const int r = idx >> 4, q = idx & 15;
+      *(u32x4*)(base + r * 256 + ((q ^ (r & 15)) * 16)) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int idx = tid + i * kTThreads;
+      const int r = idx / (L::kBRow / 16), q = idx % (L::kBRow / 16);
+      *(u32x4*)(base + kABuf + r * L::kBStride + q * 16) = rb[i];
+    }
+    if constexpr (SCALE == SC_BLOCK) {
+      if (tid < kTN) *(float2*)(base + kABuf + L::kBBuf + tid * 8) = float2{rs[0], rs[1]};
+    }
+  };
+
+  f32x4 acc[4][4];
+  f32x4 blk[4][4];
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      acc[ms][ns] = zero4;
+      blk[ms][ns] = zero4;
+    }
+  const UnpackMasks um = unpack_masks();
+  const int cg = code_group_of_lane<BITS>(grp);
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* base = lds + (kt & 1) * L::kStage;
+    load(min(kt + 1, nk - 1));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f16x8 ahi[4], alo[4], bf[4];
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        const int r = wm * 64 + ms * 16 + col;  // r & 15 == col
+        const uint8_t* arow = base + r * 256;
+        ahi[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp) ^ col) * 16));
+        alo[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
+      }
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns)
+        bf[ns] = tile_operand<BITS>(base + kABuf + (wn * 64 + ns * 16 + col) * L::kBStride, j, cg, um);
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+          if constexpr (SCALE == SC_COL) {
+            acc[ms][ns] = mfma16(ahi[ms], bf[ns], acc[ms][ns]);
+            acc[ms][ns] = mfma16(alo[ms], bf[ns], acc[ms][ns]);
+          } else {
+            blk[ms][ns] = mfma16(ahi[ms], bf[ns], blk[ms][ns]);
+            blk[ms][ns] = mfma16(alo[ms], bf[ns], blk[ms][ns]);
+          }
+        }
+      if constexpr (SCALE == SC_BLOCK) {
+        const int ks = 2 * kt + j;  // 32-code step
+        if (((ks + 1) * 32) % g.bs == 0) {
+          const float* srow = (const float*)(base + kABuf + L::kBBuf);
+#pragma unroll
+          for (int ns = 0; ns < 4; ++ns) {
+            const float sc = srow[(wn * 64 + ns * 16 + col) * 2 + (g.bs == 32 ? j : 0)];
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+              acc[ms][ns] += blk[ms][ns] * sc;
+              blk[ms][ns] = zero4;
+            }
+          }
+        }
+      }
+    }
+    // The other buffer was last read in the previous step, which every
+    // wavefront finished before the last barrier.
+    if (kt + 1 < nk) store((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  if constexpr (SCALE == SC_COL) {
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      const float sc = g.ws[ebase + min(n0 + wn * 64 + ns * 16 + col, g.N - 1)];
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) acc[ms][ns] *= sc;
+    }
+  }
+
+  // Epilogue in two rounds of 64 rows: the wavefronts of that row half put
+  // their results in an fp32 LDS tile [64][256] (columns XOR-swizzled by
+  // 16 * ((row / 4) % 4)), then the workgroup writes whole rows.
+  float* otile = reinterpret_cast<float*>(lds);
+  auto tix = [](int rr, int c) { return rr * kTN + (c ^ (16 * ((rr >> 2) & 3))); };
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) otile[tix(ms * 16 + 4 * grp + i, wn * 64 + ns * 16 + col)] = acc[ms][ns][i];
+    }
+    __syncthreads();
+    const int rlim = min(64, rows - half * 64);  // valid rows of this half
+    if constexpr (EPI == EPI_STORE) {
+      for (int idx = tid; idx < rlim * (kTN / 4); idx += kTThreads) {
+        const int rr = idx / (kTN / 4), c = 4 * (idx % (kTN / 4));
+        if (n0 + c < g.N)
+          *(f32x4*)(g.slot_out + (long)s_orow[half * 64 + rr] * g.N + n0 + c) = *(const f32x4*)(otile + tix(rr, c));
+      }
+    } else {
+      // FC2 operand rows for this tile's codes: ReLU code j = column n;
+      // SwiGLU code j = columns 2j (gate) and 2j + 1 (linear).
+      constexpr bool swiglu = EPI == EPI_SWIGLU;
+      const int I = swiglu ? g.N / 2 : g.N;
+      constexpr int jw = swiglu ? kTN / 2 : kTN;  // codes of this tile (whole 32-code blocks)
+      const int jbase = swiglu ? n0 / 2 : n0;
+      const int gtot = (int)(g.act_stride / 32);
+      for (int idx = tid; idx < rlim * (jw / 8); idx += kTThreads) {
+        const int rr = idx / (jw / 8);
+        const int gq = jbase / 8 + idx % (jw / 8);
+        if (gq >= gtot) continue;
+        const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
+        float a[8];
+        if constexpr (swiglu) {
+          const int t0 = 2 * (j0 - jbase);
+          f32x4 v[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float gv = v[c >> 1][2 * (c & 1)], uv = v[c >> 1][2 * (c & 1) + 1];
+            a[c] = j0 + c < I ? gv / (1.f + expf(-g.alpha * gv)) * (uv + g.beta) : 0.f;
+          }
+        } else {
+          const int t0 = j0 - jbase;
+          f32x4 v[2];
+#pragma unroll
+          for (int m = 0; m < 2; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
+#pragma unroll
+          for (int c = 0; c < 8; ++c) a[c] = j0 + c < I ? fmaxf(v[c >> 2][c & 3], 0.f) : 0.f;
+        }
+        f16x8 hi, lo;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code j0 + c sits at storage slot sl
+          _Float16 hh, ll;
+          split_f16(a[c], hh, ll);
+          hi[sl] = hh;
+          lo[sl] = ll;
+        }
+        uint8_t* dst = g.act + (long)(p0 + half * 64 + rr) * g.act_stride + (long)gq * 32;
+        *(f16x8*)dst = hi;
+        *(f16x8*)(dst + 16) = lo;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+namespace {
+
+template <int BITS, int SCALE, int EPI>
+hipError_t go_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
+  auto kern = qmoe_tiled<BITS, SCALE, EPI>;
+  constexpr size_t lds = TiledLayout<BITS>::kLds;
+  static std::atomic<bool> granted{false};
+  if (lds > 64 * 1024 && !granted.load()) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    granted.store(true);
+  }
+  hipLaunchKernelGGL(kern, dim3(max_tiles * ntn), dim3(kTThreads), lds, st, g, ntn);
+  return hipGetLastError();
+}
+
+template <int BITS, int EPI>
+hipError_t pick_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
+  if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI>(g, max_tiles, ntn, st);
+  return go_tiled<BITS, SC_BLOCK, EPI>(g, max_tiles, ntn, st);
+}
+
+}  // namespace
+
+int tiled_rows() { return kTM; }
+
+bool tiled_ok(int64_t K, int64_t bs, bool aligned) { return aligned && K > 0 && K % kTK == 0 && (bs == 0 || bs >= 32); }
+
+hipError_t launch_tiled(int bits, int epi, const GemmArgs& g, int max_tiles, hipStream_t st) {
+  if (!tiled_ok(g.K, g.bs, true) || (g.N & 3) != 0) return hipErrorInvalidValue;
+  const int ntn = (g.N + kTN - 1) / kTN;
+  if (bits == 4) {
+    if (epi == EPI_RELU) return pick_tiled<4, EPI_RELU>(g, max_tiles, ntn, st);
+    if (epi == EPI_SWIGLU) return pick_tiled<4, EPI_SWIGLU>(g, max_tiles, ntn, st);
+    return pick_tiled<4, EPI_STORE>(g, max_tiles, ntn, st);
+  }
+  if (epi == EPI_RELU) return pick_tiled<8, EPI_RELU>(g, max_tiles, ntn, st);
+  if (epi == EPI_SWIGLU) return pick_tiled<8, EPI_SWIGLU>(g, max_tiles, ntn, st);
+  return pick_tiled<8, EPI_STORE>(g, max_tiles, ntn, st);
+}
+
+}  // namespace qmoe

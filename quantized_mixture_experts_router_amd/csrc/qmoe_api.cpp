@@ -138,6 +138,9 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
         QMOE_TRY_HIP(launch_act(d.bits, epi1, part1, p.s1.splits, S, (int)d.F, I, (int)p.kp2, d.alpha, d.beta, act,
                                 s));
       }
+    } else if (p.tiled) {
+      QMOE_TRY_HIP(launch_tiled(d.bits, epi1, g1, (int)p.max_tiles, s));
+      QMOE_TRY_HIP(mark(2));
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, epi1, p.mt, p.aligned, g1, (int)p.max_tiles, s));
       QMOE_TRY_HIP(mark(2));
@@ -160,10 +163,12 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g2.slot_out = slot;
     g2.perm = perm;
     g2.S = S;
+    g2.store_by_slot = 1;  // FC2 rows go to their slot id
     if (p.s2.on) {
-      g2.store_by_slot = 1;
       g2.nst = p.s2.nst;
       QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.stg, p.s2.splits, g2, (int)p.max_tiles, s));
+    } else if (p.tiled) {
+      QMOE_TRY_HIP(launch_tiled(d.bits, EPI_STORE, g2, (int)p.max_tiles, s));
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
     }

@@ -129,6 +129,12 @@ void make_plan(const Dims& d, Plan* p) {
   p->decode = d.T <= 64;
   p->mt = p->decode ? int((d.T + 15) / 16) : 4;
   p->bm = 16 * p->mt;
+  // Larger token counts: the LDS-tiled GEMMs when both reductions are whole
+  // 64-code steps, rows are 8-code aligned and scale blocks are >= 32 codes
+  // (else the register-tiled GEMMs with 64-row tiles).
+  const bool aligned8 = (d.H % 8 == 0) && (d.I % 8 == 0);
+  p->tiled = !p->decode && d.I > 0 && aligned8 && d.H % 64 == 0 && d.I % 64 == 0 && (d.bs == 0 || d.bs >= 32);
+  if (p->tiled) p->bm = 128;
   // Sum over experts of ceil(count / bm) <= ceil(S / bm) + E; when one tile
   // holds any expert's rows it is at most E (one tile per used expert).
   p->max_tiles = p->decode ? d.E : (p->S + p->bm - 1) / p->bm + d.E;

@@ -40,6 +40,7 @@ struct Plan {
   Dims d;
   int64_t S = 0;         // slots = T * k
   bool decode = false;   // weight-streaming path (every expert's rows fit one M tile)
+  bool tiled = false;    // LDS-tiled GEMMs (128-row tiles) for both FC1 and FC2
   int mt = 1;            // 16-row M subtiles per tile
   int64_t bm = 16;       // rows per M tile
   int64_t max_tiles = 0; // ceil(S / bm) + E

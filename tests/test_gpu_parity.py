@@ -95,12 +95,14 @@ def test_route_ties_through_gpu(torch):
 
 
 # Small sweeps: every element.  (T, H, E, I, k) chosen to cover one and several
-# M subtiles on the weight-streaming path (T <= 64), the tiled path (T > 64),
-# ragged tails in every dimension, unused experts and k = E.
+# M subtiles on the weight-streaming path (T <= 64), the LDS-tiled path (T > 64,
+# H and I multiples of 64) and the register-tiled path (other shapes), ragged
+# tails in every dimension, unused experts and k = E.
 SHAPES = [
     (1, 64, 4, 32, 1), (5, 128, 3, 64, 2), (16, 256, 8, 96, 2), (17, 64, 4, 160, 3),
     (33, 128, 6, 64, 6), (64, 192, 8, 128, 2), (70, 128, 5, 96, 2), (200, 64, 16, 64, 4),
     (300, 256, 1, 32, 1), (24, 512, 8, 256, 3), (40, 256, 4, 256, 2), (60, 256, 4, 128, 2),
+    (130, 128, 3, 192, 2), (257, 320, 4, 128, 3),
 ]
 
 
