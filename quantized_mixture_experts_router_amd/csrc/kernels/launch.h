@@ -63,9 +63,8 @@ hipError_t launch_tiled(int bits, int epi, const GemmArgs& g, int max_tiles, hip
 // kernel writes FC2 operand rows after the activation, else fp32 partial rows
 // part[z][p][N].  FC2: partial rows by slot id, slot_out[z][slot][N].
 // z < splits K ranges of g.nst stages each.
-int stream_stage_items(int mt);
-size_t stream_lds_bytes(int bits, int mt);
-hipError_t launch_stream(int bits, int mt, int stg, int splits, const GemmArgs& g, int max_tiles, hipStream_t st);
+size_t stream_lds_bytes(int bits, int mt, bool one, int N);
+hipError_t launch_stream(int bits, int mt, bool one, int splits, const GemmArgs& g, int max_tiles, hipStream_t st);
 
 // Sum FC1 partials over K ranges, apply the activation, write FC2 operand rows.
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,

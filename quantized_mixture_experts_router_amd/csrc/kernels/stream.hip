@@ -34,6 +34,7 @@
 
 #include "common.hpp"
 #include "launch.h"
+#include "qmoe_plan.h"
 
 namespace qmoe {
 
@@ -45,9 +46,6 @@ namespace {
 #endif
 #ifndef QMOE_STREAM_XCD_ORDER
 #define QMOE_STREAM_XCD_ORDER 0
-#endif
-#ifndef QMOE_STREAM_LATE_REFILL
-#define QMOE_STREAM_LATE_REFILL 1
 #endif
 #ifndef QMOE_STREAM_NT_LOADS
 #define QMOE_STREAM_NT_LOADS 0
@@ -93,9 +91,19 @@ __device__ __forceinline__ void exchange(u32x4& v) {
 // a block spans whole chunks); FC1 = the A rows are the layer's fp32 input
 // (split into f16 hi/lo while staging) and the epilogue may apply the
 // activation; otherwise A rows are FC2 operand rows (f16 hi/lo groups).
-template <int BITS, int MT, int STG, int SCALE, int SPB, bool FC1>
+// ONE: the K range is a single stage, staged once (no barriers in the
+// stream); otherwise stages are double buffered.  RB: row blocks of
+// kWGRows weight rows streamed one after the other against the one stage
+// (ONE only), amortising the staging.
+template <int BITS, int MT, int SCALE, int SPB, bool FC1, bool ONE, int RB>
 __global__ void __launch_bounds__(64 * kSWaves) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2, MT == 1 ? 4 : 2)))
 qmoe_stream(GemmArgs g) {
+  constexpr int STG = stream_stage_items(MT, ONE);  // items per stage
+  static_assert(RB == 1 || ONE, "row blocks reuse a single stage");
+  constexpr int WGR = kWGRows * RB;                 // weight rows of the workgroup
+  // With one stage there is no next stage to stage, so registers allow the
+  // ring to be copied out and refilled before each item is consumed.
+  constexpr bool LATE = !ONE;
   constexpr int CC = BITS == 4 ? 128 : 64;      // codes per 64-byte chunk
   constexpr int NS = CC / 32;                   // MFMA steps per chunk
   constexpr int ROWS = 16 * MT;
@@ -151,11 +159,14 @@ qmoe_stream(GemmArgs g) {
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int n0 = rgroup * kWGRows;       // first weight row of the workgroup
+  const int n0 = rgroup * WGR;           // first weight row of the workgroup
   const long ebase = (long)e * g.N;
   const long kb_bytes = g.kb;
 
-  // Rows past N (last row group) stream a clamped row; their results are dropped.
+  // Rows past N (last row group) stream a clamped row; their results are
+  // dropped.  Row block rb adds rb * kWGRows rows (RB > 1: N is a multiple of WGR).
+  const long bstep = (long)kWGRows * kb_bytes;
+  const long sstep = (long)kWGRows * g.nblk;
   const uint8_t* bbase[NT];
   const float* sbase[NT];
 #pragma unroll
@@ -172,15 +183,17 @@ qmoe_stream(GemmArgs g) {
   u32x4 bq[kP][NT][kCPI];
   float sq[kP][NT][kCPI];
   auto issue = [&](int slot, int it) {
-    const int itc = min(it, nit - 1);
+    // ONE: item it is piece it % STG of row block it / STG (compile-time)
+    const int rb = ONE ? it / STG : 0;
+    const int itc = ONE ? it % STG : min(it, nit - 1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint8_t* src = bbase[nt] + (long)itc * (kCPI * 64);
+      const uint8_t* src = bbase[nt] + rb * bstep + (long)itc * (kCPI * 64);
 #pragma unroll
       for (int h = 0; h < kCPI; ++h) bq[slot][nt][h] = load_weights(src + h * 64);
       if constexpr (SCALE != SC_COL && SPB == 0) {
 #pragma unroll
-        for (int h = 0; h < kCPI; ++h) sq[slot][nt][h] = sbase[nt][((c0 + itc * kCPI + h) * CC) / g.bs];
+        for (int h = 0; h < kCPI; ++h) sq[slot][nt][h] = sbase[nt][rb * sstep + ((c0 + itc * kCPI + h) * CC) / g.bs];
       }
     }
   };
@@ -188,11 +201,11 @@ qmoe_stream(GemmArgs g) {
   // block scales of the stage (one 4- to 16-byte load), one stage ahead; a
   // block's scale is then fetched from the owning lane group by ds_bpermute.
   float snext[NT][Q], scur[NT][Q];
-  auto issue_scales = [&](int st) {
-    const int stc = min(st, nst - 1);
+  auto issue_scales = [&](int st) {  // ONE: st is the row block
+    const long off = ONE ? st * sstep : (long)min(st, nst - 1) * NBS;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float* sp = sbase[nt] + stc * NBS;
+      const float* sp = sbase[nt] + off;
       if constexpr (Q == 4) {
         const f32x4 v = *(const f32x4*)sp;
 #pragma unroll
@@ -211,7 +224,8 @@ qmoe_stream(GemmArgs g) {
   // on the tile.
   if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(0);
 #pragma unroll
-  for (int u = 0; u < kP; ++u) issue(u, u);
+  for (int u = 0; u < kP; ++u)
+    if (!ONE || u < RB * STG) issue(u, u);
 
   // Activation row of every tile row (clamped to valid rows) and its output row.
   if (threadIdx.x < ROWS) {
@@ -289,16 +303,48 @@ qmoe_stream(GemmArgs g) {
       }
     }
   };
+  if constexpr (ONE) {
+    // The only stage: stage just the tile's valid rows (the matrix rows past
+    // them read the last valid row).  Loads here may be conditional: only the
+    // ring's first items are in flight, and they are older.
+    if constexpr (FC1) {
+      for (int idx = threadIdx.x; idx < rows * GR; idx += NTH) {
+        const int r = idx / GR, gq = idx % GR;
+        const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
+        const float* src = (const float*)(g.a + s_rowbase[r]) + j0;
+        const f32x4 v0 = *(const f32x4*)src, v1 = *(const f32x4*)(src + 4);
+        f16x8 hi, lo;
 #pragma unroll
-  for (int part = 0; part < NPART; ++part) {
-    stage_load(0, part);
-    stage_store(0, part);
+        for (int sl = 0; sl < 8; ++sl) {
+          const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code inside the group at storage slot sl
+          _Float16 h, l;
+          split_f16(c < 4 ? v0[c] : v1[c - 4], h, l);
+          hi[sl] = h;
+          lo[sl] = l;
+        }
+        uint8_t* row = lds + r * LSTRIDE;
+        *(f16x8*)(row + (((2 * gq) ^ (r & 15)) * 16)) = hi;
+        *(f16x8*)(row + (((2 * gq + 1) ^ (r & 15)) * 16)) = lo;
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < rows * PIECES; idx += NTH) {
+        const int r = idx / PIECES, q = idx % PIECES;
+        *(u32x4*)(lds + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = *(const u32x4*)(g.a + s_rowbase[r] + q * 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int part = 0; part < NPART; ++part) {
+      stage_load(0, part);
+      stage_store(0, part);
+    }
   }
 
   __syncthreads();
 
   f32x4 acc[MT][NT];
   f32x4 blk[MT][NT];
+  f32x4 res[RB > 1 ? MT : 1][NT];  // first row block's results (RB == 2)
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -335,42 +381,50 @@ qmoe_stream(GemmArgs g) {
   auto stage = [&](int st, auto q0c) {
     constexpr int Q0 = decltype(q0c)::value;
     const uint8_t* abuf = lds + (st & 1) * BUF;
-    if constexpr (SCALE == SC_BLOCK && SPB > 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < Q; ++i) scur[nt][i] = snext[nt][i];
-    }
-#pragma unroll
-    for (int il = 0; il < STG; ++il) {
+    for (int il = 0; il < RB * STG; ++il) {
       // keep each item's work in its own scheduling region (bounded live ranges)
       __builtin_amdgcn_sched_barrier(0);
       const int u = (Q0 * STG + il) % kP;
-      const int it = st * STG + il;
-#if QMOE_STREAM_LATE_REFILL
-      // consume the ring slot in place; it is refilled after the item
-      u32x4 (&cur)[NT][kCPI] = bq[u];
-      float (&sc1)[NT][kCPI] = sq[u];
-#else
-      u32x4 cur[NT][kCPI];
-      float sc1[NT][kCPI];
+      const int it = st * STG + il;          // ONE: st == 0
+      const int ii = il % STG;               // item inside the stage
+      const int rb = il / STG;               // row block (ONE)
+      if constexpr (SCALE == SC_BLOCK && SPB > 0)
+        if (ii == 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int h = 0; h < kCPI; ++h) {
-          cur[nt][h] = bq[u][nt][h];
-          sc1[nt][h] = sq[u][nt][h];
+            for (int i = 0; i < Q; ++i) scur[nt][i] = snext[nt][i];
         }
-#endif
-      if (il == STG - 1)
-        if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(st + 1);
-      if (NPART == STG || il == STG - 1) stage_load(st + 1, NPART == STG ? il : 0);
-#if !QMOE_STREAM_LATE_REFILL
-      issue(u, it + kP);
-#endif
+      // LATE: consume the ring slot in place and refill it after the item;
+      // otherwise copy it out and refill it first.
+      u32x4 cur_copy[LATE ? 1 : NT][kCPI];
+      float sc1_copy[LATE ? 1 : NT][kCPI];
+      if constexpr (!LATE) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int h = 0; h < kCPI; ++h) {
+            cur_copy[nt][h] = bq[u][nt][h];
+            sc1_copy[nt][h] = sq[u][nt][h];
+          }
+      }
+      u32x4 (&cur)[NT][kCPI] = *(LATE ? &bq[u] : reinterpret_cast<u32x4(*)[NT][kCPI]>(&cur_copy));
+      float (&sc1)[NT][kCPI] = *(LATE ? &sq[u] : reinterpret_cast<float(*)[NT][kCPI]>(&sc1_copy));
+      if constexpr (!ONE) {
+        if (il == STG - 1)
+          if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(st + 1);
+        if (NPART == STG || il == STG - 1) stage_load(st + 1, NPART == STG ? il : 0);
+      } else if constexpr (SCALE == SC_BLOCK && SPB > 0) {
+        if (ii == STG - 1 && rb + 1 < RB) issue_scales(rb + 1);  // next row block's scales
+      }
+      // (with one stage the items past the range are known at compile time
+      // and are not fetched)
+      if constexpr (!LATE)
+        if (!ONE || il + kP < RB * STG) issue(u, it + kP);
 #pragma unroll
       for (int h = 0; h < kCPI; ++h) {
-        const int cl = il * kCPI + h;  // chunk index inside the stage
+        const int cl = ii * kCPI + h;  // chunk index inside the stage
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) exchange<BITS>(cur[nt][h]);
 #pragma unroll
@@ -411,8 +465,8 @@ qmoe_stream(GemmArgs g) {
         }
         if constexpr (SCALE != SC_COL && SPB == 0) {
           // end of a scale block, or end of this K range's share of one
-          const int chunk = c0 + it * kCPI + h;
-          if ((chunk + 1) % cpb == 0 || (it == nit - 1 && h == kCPI - 1)) {
+          const int chunk = c0 + (ONE ? ii : it) * kCPI + h;
+          if ((chunk + 1) % cpb == 0 || ((ONE ? ii == STG - 1 : it == nit - 1) && h == kCPI - 1)) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -424,14 +478,25 @@ qmoe_stream(GemmArgs g) {
           }
         }
       }
-#if QMOE_STREAM_LATE_REFILL
-      issue(u, it + kP);
-#endif
+      if constexpr (LATE)
+        if (!ONE || il + kP < RB * STG) issue(u, it + kP);
+      if constexpr (RB > 1)
+        if (ii == STG - 1 && rb + 1 < RB) {
+          // row block done: keep it until the stream ends
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              res[mt][nt] = acc[mt][nt];
+              acc[mt][nt] = zero4;
+            }
+        }
       // Publish this part of the next stage's activations: its buffer was last
       // read in the previous stage, which every wavefront finished before the
       // last barrier.
-      if (NPART == STG || il == STG - 1)
-        if (st + 1 < nst) stage_store((st + 1) & 1, NPART == STG ? il : 0);
+      if constexpr (!ONE)
+        if (NPART == STG || il == STG - 1)
+          if (st + 1 < nst) stage_store((st + 1) & 1, NPART == STG ? il : 0);
     }
     __syncthreads();
   };
@@ -445,24 +510,27 @@ qmoe_stream(GemmArgs g) {
     if (nmain < nst) stage(nmain, std::integral_constant<int, 0>{});
 
   // Output: every wavefront puts its rows (column scales applied) into the
-  // LDS tile [ROWS][kWGRows] (the stage buffers are free after the last
+  // LDS tile [ROWS][WGR] (the stage buffers are free after the last
   // barrier); tile columns are XOR-swizzled by 16 * ((row / 4) % 4), so the
   // four row groups of one write hit distinct banks.
   float* otile = reinterpret_cast<float*>(lds);
-  auto tix = [](int rr, int c) { return rr * kWGRows + (c ^ (16 * ((rr >> 2) & 3))); };
+  auto tix = [](int rr, int c) { return rr * WGR + (c ^ (16 * ((rr >> 2) & 3))); };
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int c = wave * 16 * NT + nt * 16 + col;  // tile column
-    float sc = 1.f;
-    if constexpr (SCALE == SC_COL) sc = g.ws[ebase + min(n0 + c, g.N - 1)];
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int nt = 0; nt < NT; ++nt) {
+      const int c = rb * kWGRows + wave * 16 * NT + nt * 16 + col;  // tile column
+      float sc = 1.f;
+      if constexpr (SCALE == SC_COL) sc = g.ws[ebase + min(n0 + c, g.N - 1)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = mt * 16 + 4 * grp + i;
-        if (rr < rows) otile[tix(rr, c)] = acc[mt][nt][i] * sc;
-      }
-  }
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = mt * 16 + 4 * grp + i;
+          const float v = (RB > 1 && rb == 0) ? res[RB > 1 ? mt : 0][nt][i] : acc[mt][nt][i];
+          if (rr < rows) otile[tix(rr, c)] = v * sc;
+        }
+    }
   __syncthreads();
 
   if (FC1 && g.act != nullptr) {
@@ -472,7 +540,7 @@ qmoe_stream(GemmArgs g) {
     // and 2j + 1 (linear): g * sigmoid(alpha * g) * (u + beta).
     const bool swiglu = g.act_swiglu != 0;
     const int I = swiglu ? g.N / 2 : g.N;
-    const int jw = swiglu ? kWGRows / 2 : kWGRows;   // codes of this workgroup (whole 32-code blocks)
+    const int jw = swiglu ? WGR / 2 : WGR;   // codes of this workgroup (whole 32-code blocks)
     const int jbase = swiglu ? n0 / 2 : n0;
     const int gtot = (int)(g.act_stride / 32);       // groups per operand row
     for (int idx = threadIdx.x; idx < rows * (jw / 8); idx += NTH) {
@@ -513,14 +581,14 @@ qmoe_stream(GemmArgs g) {
       *(f16x8*)(dst + 16) = lo;
     }
   } else if ((g.N & 3) == 0) {
-    for (int idx = threadIdx.x; idx < rows * (kWGRows / 4); idx += NTH) {
-      const int rr = idx / (kWGRows / 4), c = 4 * (idx % (kWGRows / 4));
+    for (int idx = threadIdx.x; idx < rows * (WGR / 4); idx += NTH) {
+      const int rr = idx / (WGR / 4), c = 4 * (idx % (WGR / 4));
       if (n0 + c < g.N)
         *(f32x4*)(g.slot_out + ((long)split * g.S + s_orow[rr]) * g.N + n0 + c) = *(const f32x4*)(otile + tix(rr, c));
     }
   } else {
-    for (int idx = threadIdx.x; idx < rows * kWGRows; idx += NTH) {
-      const int rr = idx / kWGRows, c = idx % kWGRows;
+    for (int idx = threadIdx.x; idx < rows * WGR; idx += NTH) {
+      const int rr = idx / WGR, c = idx % WGR;
       if (n0 + c < g.N) g.slot_out[((long)split * g.S + s_orow[rr]) * g.N + n0 + c] = otile[tix(rr, c)];
     }
   }
@@ -598,9 +666,9 @@ __global__ void __launch_bounds__(256) qmoe_act(const float* __restrict__ part, 
 
 namespace {
 
-template <int BITS, int MT, int STG, int SCALE, int SPB, bool FC1>
+template <int BITS, int MT, int SCALE, int SPB, bool FC1, bool ONE, int RB>
 hipError_t go(const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
-  auto kern = qmoe_stream<BITS, MT, STG, SCALE, SPB, FC1>;
+  auto kern = qmoe_stream<BITS, MT, SCALE, SPB, FC1, ONE, RB>;
   // Dynamic LDS above the 64 KB default needs a per-kernel opt-in (host-side,
   // no synchronisation); remember the largest size granted so far.
   static std::atomic<size_t> granted{64 * 1024};
@@ -613,45 +681,63 @@ hipError_t go(const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BITS, int MT, int STG, bool FC1>
+template <int BITS, int MT, bool FC1, bool ONE, int RB>
 hipError_t pick_scale(const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
   constexpr int CC = BITS == 4 ? 128 : 64;
-  if (g.bs == 0) return go<BITS, MT, STG, SC_COL, 0, FC1>(g, grid, lds, st);
-  if (g.bs >= CC) return go<BITS, MT, STG, SC_BLOCK, 0, FC1>(g, grid, lds, st);
-  if (g.bs == 32) return go<BITS, MT, STG, SC_BLOCK, 1, FC1>(g, grid, lds, st);
+  if (g.bs == 0) return go<BITS, MT, SC_COL, 0, FC1, ONE, RB>(g, grid, lds, st);
+  if (g.bs >= CC) return go<BITS, MT, SC_BLOCK, 0, FC1, ONE, RB>(g, grid, lds, st);
+  if (g.bs == 32) {
+    // 32-code blocks: at most 16 a stage
+    if constexpr (stream_stage_items(MT, ONE) * (BITS == 4 ? 256 : 128) / 32 <= 16)
+      return go<BITS, MT, SC_BLOCK, 1, FC1, ONE, RB>(g, grid, lds, st);
+    return hipErrorInvalidValue;
+  }
   if constexpr (BITS == 4) {
-    if (g.bs == 64) return go<BITS, MT, STG, SC_BLOCK, 2, FC1>(g, grid, lds, st);
+    if (g.bs == 64) return go<BITS, MT, SC_BLOCK, 2, FC1, ONE, RB>(g, grid, lds, st);
   }
   return hipErrorInvalidValue;  // scale layouts the planner never routes here
 }
 
-template <int BITS, bool FC1>
-hipError_t pick_mt(int mt, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
+template <int BITS, bool FC1, bool ONE>
+hipError_t pick_mt(int mt, int rb, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
   switch (mt) {
-    case 1: return pick_scale<BITS, 1, 2, FC1>(g, grid, lds, st);
-    case 2: return pick_scale<BITS, 2, 1, FC1>(g, grid, lds, st);
-    case 3: return pick_scale<BITS, 3, 1, FC1>(g, grid, lds, st);
-    default: return pick_scale<BITS, 4, 1, FC1>(g, grid, lds, st);
+    case 1:
+      if constexpr (ONE)
+        if (rb == 2) return pick_scale<BITS, 1, FC1, ONE, 2>(g, grid, lds, st);
+      return pick_scale<BITS, 1, FC1, ONE, 1>(g, grid, lds, st);
+    case 2: return pick_scale<BITS, 2, FC1, ONE, 1>(g, grid, lds, st);
+    case 3: return pick_scale<BITS, 3, FC1, ONE, 1>(g, grid, lds, st);
+    default: return pick_scale<BITS, 4, FC1, ONE, 1>(g, grid, lds, st);
   }
+}
+
+template <int BITS>
+hipError_t pick_mode(bool fc1, bool one, int mt, int rb, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
+  if (fc1)
+    return one ? pick_mt<BITS, true, true>(mt, rb, g, grid, lds, st) : pick_mt<BITS, true, false>(mt, rb, g, grid, lds, st);
+  return one ? pick_mt<BITS, false, true>(mt, rb, g, grid, lds, st) : pick_mt<BITS, false, false>(mt, rb, g, grid, lds, st);
 }
 
 }  // namespace
 
-int stream_stage_items(int mt) { return mt == 1 ? 2 : 1; }
+// Row blocks per workgroup: two for one-stage launches at mt == 1 when
+// they tile N exactly.
+static int stream_row_blocks(int mt, bool one, int N) { return one && mt == 1 && N % (2 * kWGRows) == 0 ? 2 : 1; }
 
-size_t stream_lds_bytes(int bits, int mt) {
+size_t stream_lds_bytes(int bits, int mt, bool one, int N) {
   const int item_codes = bits == 4 ? 256 : 128;
-  const size_t stage = (size_t)16 * mt * stream_stage_items(mt) * item_codes * 4;
-  return std::max(2 * stage, (size_t)16 * mt * kWGRows * 4);
+  const size_t stage = (size_t)16 * mt * stream_stage_items(mt, one) * item_codes * 4;
+  return std::max((one ? 1 : 2) * stage, (size_t)16 * mt * kWGRows * stream_row_blocks(mt, one, N) * 4);
 }
 
-hipError_t launch_stream(int bits, int mt, int stg, int splits, const GemmArgs& g, int max_tiles, hipStream_t st) {
-  if (stg != stream_stage_items(mt) || mt < 1 || mt > 4) return hipErrorInvalidValue;
-  const size_t lds = stream_lds_bytes(bits, mt);
-  const dim3 grid(splits, max_tiles, (g.N + kWGRows - 1) / kWGRows);
+hipError_t launch_stream(int bits, int mt, bool one, int splits, const GemmArgs& g, int max_tiles, hipStream_t st) {
+  if (mt < 1 || mt > 4 || (one && g.nst != 1)) return hipErrorInvalidValue;
+  const int rb = stream_row_blocks(mt, one, g.N);
+  const size_t lds = stream_lds_bytes(bits, mt, one, g.N);
+  const int wg_rows = kWGRows * rb;
+  const dim3 grid(splits, max_tiles, (g.N + wg_rows - 1) / wg_rows);
   const bool fc1 = g.a_f32 != 0;
-  if (bits == 4) return fc1 ? pick_mt<4, true>(mt, g, grid, lds, st) : pick_mt<4, false>(mt, g, grid, lds, st);
-  return fc1 ? pick_mt<8, true>(mt, g, grid, lds, st) : pick_mt<8, false>(mt, g, grid, lds, st);
+  return bits == 4 ? pick_mode<4>(fc1, one, mt, rb, g, grid, lds, st) : pick_mode<8>(fc1, one, mt, rb, g, grid, lds, st);
 }
 
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,

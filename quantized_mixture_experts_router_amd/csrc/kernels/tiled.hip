@@ -24,6 +24,7 @@
 // XCD's L2.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.h"
@@ -130,15 +131,10 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
 #pragma unroll
     for (int i = 0; i < BPT; ++i) rb[i] = *(const u32x4*)(bsrc[i] + (long)kt * L::kBRow);
     if constexpr (SCALE == SC_BLOCK) {
-      // scales of the blocks that end in this step (two when bs == 32)
-      if (g.bs == 32) {
-        const float2 v = *(const float2*)(ssrc + 2 * kt);
-        rs[0] = v.x;
-        rs[1] = v.y;
-      } else {
-        rs[0] = ssrc[(kt * kTK) / g.bs];
-        rs[1] = rs[0];
-      }
+      // scales of the blocks holding the step's two 32-code halves (the same
+      // block unless bs == 32); no branches, so every wait stays exact
+      rs[0] = ssrc[(kt * kTK) / g.bs];
+      rs[1] = ssrc[(kt * kTK + 32) / g.bs];
     }
   };
   auto store = [&](int buf) {
@@ -173,44 +169,67 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   const UnpackMasks um = unpack_masks();
   const int cg = code_group_of_lane<BITS>(grp);
 
+  // L2 prefetch three steps ahead: every thread touches one 128-byte line of
+  // a coming step (waves 0-3 the activation slice, 2 lines a row; waves 4-7
+  // the weight rows) with a dword load whose value is consumed two steps
+  // later.  Loads complete in issue order, so a step's own loads (issued
+  // before its prefetch) never wait for that prefetch.
+  const uint8_t* pfbase = tid < 256 ? g.a + s_arow[tid >> 1] + (tid & 1) * 128
+                                    : g.wq + (ebase + min(n0 + (tid - 256), g.N - 1)) * (long)g.kb;
+  const int pfstep = tid < 256 ? kTK * 4 : L::kBRow;
+  auto prefetch = [&](int kt) -> uint32_t {
+    return *(const uint32_t*)(pfbase + (long)min(kt, nk - 1) * pfstep);
+  };
+  uint32_t pf[2];
+  pf[0] = prefetch(1);
+  pf[1] = prefetch(2);
+
   load(0);
   store(0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* base = lds + (kt & 1) * L::kStage;
+  // One K step; P = kt & 1 at compile time (ring of prefetch values).
+  auto kstep = [&](int kt, auto pc) {
+    constexpr int P = decltype(pc)::value;
+    const uint8_t* base = lds + P * L::kStage;
+    asm volatile("" ::"v"(pf[P]));  // step kt + 1 is in L2
     load(min(kt + 1, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);  // the step's own loads are issued before its prefetch
+    pf[P] = prefetch(kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      f16x8 ahi[4], alo[4], bf[4];
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        const int r = wm * 64 + ms * 16 + col;  // r & 15 == col
-        const uint8_t* arow = base + r * 256;
-        ahi[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp) ^ col) * 16));
-        alo[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
-      }
+      // weight fragments of the step, then the four row subtiles with their
+      // activation fragments loaded one subtile ahead; hi parts then lo
+      // parts, so the two instructions on one accumulator are 4 apart
+      f16x8 bf[4], ah[2], al[2];
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns)
         bf[ns] = tile_operand<BITS>(base + kABuf + (wn * 64 + ns * 16 + col) * L::kBStride, j, cg, um);
+      auto aload = [&](int ms, f16x8& h, f16x8& l) {
+        const uint8_t* arow = base + (wm * 64 + ms * 16 + col) * 256;  // row & 15 == col
+        h = *(const f16x8*)(arow + (((8 * j + 2 * grp) ^ col) * 16));
+        l = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
+      };
+      aload(0, ah[0], al[0]);
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
+      for (int ms = 0; ms < 4; ++ms) {
+        if (ms < 3) aload(ms + 1, ah[(ms + 1) & 1], al[(ms + 1) & 1]);
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-          if constexpr (SCALE == SC_COL) {
-            acc[ms][ns] = mfma16(ahi[ms], bf[ns], acc[ms][ns]);
-            acc[ms][ns] = mfma16(alo[ms], bf[ns], acc[ms][ns]);
-          } else {
-            blk[ms][ns] = mfma16(ahi[ms], bf[ns], blk[ms][ns]);
-            blk[ms][ns] = mfma16(alo[ms], bf[ns], blk[ms][ns]);
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+          for (int ns = 0; ns < 4; ++ns) {
+            const f16x8& av = hl ? al[ms & 1] : ah[ms & 1];
+            if constexpr (SCALE == SC_COL) acc[ms][ns] = mfma16(av, bf[ns], acc[ms][ns]);
+            else blk[ms][ns] = mfma16(av, bf[ns], blk[ms][ns]);
           }
-        }
+      }
       if constexpr (SCALE == SC_BLOCK) {
         const int ks = 2 * kt + j;  // 32-code step
         if (((ks + 1) * 32) % g.bs == 0) {
           const float* srow = (const float*)(base + kABuf + L::kBBuf);
 #pragma unroll
           for (int ns = 0; ns < 4; ++ns) {
-            const float sc = srow[(wn * 64 + ns * 16 + col) * 2 + (g.bs == 32 ? j : 0)];
+            const float sc = srow[(wn * 64 + ns * 16 + col) * 2 + j];
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) {
               acc[ms][ns] += blk[ms][ns] * sc;
@@ -222,9 +241,16 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     }
     // The other buffer was last read in the previous step, which every
     // wavefront finished before the last barrier.
-    if (kt + 1 < nk) store((kt + 1) & 1);
+    if (kt + 1 < nk) store(P ^ 1);
     __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    kstep(kt, std::integral_constant<int, 0>{});
+    kstep(kt + 1, std::integral_constant<int, 1>{});
   }
+  if (kt < nk) kstep(kt, std::integral_constant<int, 0>{});
+  asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
 
   if constexpr (SCALE == SC_COL) {
 #pragma unroll

@@ -13,6 +13,9 @@
 #ifndef QMOE_STREAM_NT
 #define QMOE_STREAM_NT 2
 #endif
+#ifndef QMOE_STREAM_MAX_ONE_SPLITS
+#define QMOE_STREAM_MAX_ONE_SPLITS 8
+#endif
 #ifndef QMOE_STREAM_MIN_WORKGROUPS
 #define QMOE_STREAM_MIN_WORKGROUPS 512
 #endif
@@ -151,19 +154,33 @@ void make_plan(const Dims& d, Plan* p) {
     const int64_t item_codes = d.bits == 4 ? 256 : 128;
     const int64_t chunk_codes = item_codes / 2;
     auto shape = [&](Plan::Stream& st, int64_t K, int64_t N) {
-      st.stg = p->mt == 1 ? 2 : 1;
-      const int64_t scodes = st.stg * item_codes;
-      st.on = K > 0 && K % scodes == 0 && (d.bs == 0 || d.bs >= 32);
-      if (st.on && d.bs > 0 && d.bs < chunk_codes) {
-        const int64_t nbs = scodes / d.bs;
-        st.on = nbs % 4 == 0 && nbs <= 16;
-      }
-      if (!st.on) return;
-      // Whole of K per workgroup unless the row groups alone cannot fill the
-      // chip (two workgroups on each of 256 compute units): then the fewest K
-      // ranges that do.
-      const int64_t nst_total = K / scodes;
       const int64_t units = d.E * ceil_div(N, 128 * QMOE_STREAM_NT);
+      auto fits = [&](int64_t scodes) {
+        if (!(K > 0 && K % scodes == 0 && (d.bs == 0 || d.bs >= 32))) return false;
+        if (d.bs > 0 && d.bs < chunk_codes) {
+          const int64_t nbs = scodes / d.bs;  // blocks ending inside chunks, per stage
+          return nbs % 4 == 0 && nbs <= 16;
+        }
+        return true;
+      };
+      // One stage per K range (staged once) when that takes at most
+      // QMOE_STREAM_MAX_ONE_SPLITS ranges; else double-buffered stages over
+      // the whole of K, split only as far as needed to fill the chip.
+      const int64_t one_codes = stream_stage_items(p->mt, true) * item_codes;
+      if (fits(one_codes) && K / one_codes <= QMOE_STREAM_MAX_ONE_SPLITS) {
+        st.on = true;
+        st.one = true;
+        st.stg = stream_stage_items(p->mt, true);
+        st.splits = (int)(K / one_codes);
+        st.nst = 1;
+        return;
+      }
+      st.one = false;
+      st.stg = stream_stage_items(p->mt, false);
+      const int64_t scodes = st.stg * item_codes;
+      st.on = fits(scodes);
+      if (!st.on) return;
+      const int64_t nst_total = K / scodes;
       int64_t splits = nst_total;
       for (int64_t z = 1; z <= nst_total; ++z)
         if (nst_total % z == 0 && units * z >= QMOE_STREAM_MIN_WORKGROUPS) {

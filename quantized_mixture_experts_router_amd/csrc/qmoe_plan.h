@@ -34,6 +34,13 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
                      const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
                      const qmoe_tensor* output, const qmoe_attrs* attrs, Dims* d);
 
+// Items (128-byte weight-row pieces) per activation stage of the streaming
+// kernel: one stage holding the whole K range (one = true, a single 64 KB LDS
+// buffer of 16*mt rows), or double-buffered stages.
+constexpr int stream_stage_items(int mt, bool one) {
+  return one ? (mt == 1 ? 4 : mt == 2 ? 2 : 1) : (mt == 1 ? 2 : 1);
+}
+
 // Which kernels run, with what tiles, and where each intermediate lives in the
 // caller's workspace.  Offsets are bytes from the workspace base, 256-aligned.
 struct Plan {
@@ -49,6 +56,7 @@ struct Plan {
   // weight-streaming kernels (decode): used per GEMM when its shapes allow
   struct Stream {
     bool on = false;
+    bool one = false;    // the K range is one stage (staged once, no barriers)
     int stg = 2;         // 128-byte row items per stage (activation slice per LDS buffer)
     int nst = 1;         // stages per K range
     int splits = 1;      // K ranges (fp32 partials summed afterwards, in order)
