@@ -14,7 +14,7 @@
 #define QMOE_STREAM_NT 2
 #endif
 #ifndef QMOE_STREAM_MAX_ONE_SPLITS
-#define QMOE_STREAM_MAX_ONE_SPLITS 8
+#define QMOE_STREAM_MAX_ONE_SPLITS 16
 #endif
 #ifndef QMOE_STREAM_MIN_WORKGROUPS
 #define QMOE_STREAM_MIN_WORKGROUPS 512
