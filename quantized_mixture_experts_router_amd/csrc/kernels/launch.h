@@ -9,13 +9,19 @@ hipError_t launch_router(const float* logits, int T, int E, int k, int routing, 
                          float* topk_w, hipStream_t st);
 
 // Router, counts, offsets, tile table and stable permutation in one launch
-// (T * k <= 1024 and E <= 1024).
+// (T * k <= 1024 and E <= 1024); with trows given, also the tile-row table
+// (see launch_tile_rows).
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int routing, int normalize, int bm,
                               int* topk_idx, float* topk_w, int* counts, int* offsets, int* perm, int* tiles,
-                              int* ntiles, hipStream_t st);
+                              int* ntiles, int* trows, hipStream_t st);
 
 hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchunks, int bm, int* hist,
                           int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st);
+
+// Tile-row table of the streaming kernels: trows[t * bm + r] = slot id of row
+// r of tile t (rows past the tile's count repeat its last row), t < ntiles.
+hipError_t launch_tile_rows(const int* perm, const int* tiles, const int* ntiles, int max_tiles, int bm, int* trows,
+                            hipStream_t st);
 
 hipError_t launch_prep_a(int bits, const float* x, int T, int H, int kp, uint8_t* xa, uint8_t* act, int S, int I,
                          int kp2, hipStream_t st);
@@ -45,6 +51,7 @@ struct GemmArgs {
   // stream kernel
   int nst;              // stages per K range
   int act_swiglu;       // FC1 over the whole of K: activation written by the kernel (act != nullptr)
+  const int* trows;     // stream kernel: slot id of every tile row, [max_tiles][16 * mt] (see launch_tile_rows)
 };
 
 enum { EPI_RELU = 0, EPI_SWIGLU = 1, EPI_STORE = 2 };

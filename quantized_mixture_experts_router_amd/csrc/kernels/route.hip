@@ -127,10 +127,10 @@ __global__ void __launch_bounds__(256) qmoe_hist(const int* __restrict__ topk_id
 // Block-wide (1024 threads, thread e = expert e < E <= 1024): given each
 // expert's slot count c, write counts, exclusive offsets and the M-tile table
 //   tiles[4*i .. 4*i+3] = (expert, first sorted position, rows, 0), ntiles[0] = count;
-// returns the expert's first sorted position.
+// returns the expert's first sorted position (and in *first_tile its first tile).
 __device__ __forceinline__ int scan_experts(int c, int E, int S, int bm, int* __restrict__ counts,
                                             int* __restrict__ offsets, int* __restrict__ tiles,
-                                            int* __restrict__ ntiles) {
+                                            int* __restrict__ ntiles, int* first_tile = nullptr) {
   __shared__ int s_warp[16];
   __shared__ int s_warp2[16];
   const int e = threadIdx.x;
@@ -180,7 +180,20 @@ __device__ __forceinline__ int scan_experts(int c, int E, int S, int bm, int* __
     offsets[E] = S;
     ntiles[0] = tile0 + nt;
   }
+  if (first_tile) *first_tile = tile0;
   return off_e;
+}
+
+// Slot id of every row of tile t: trows[t * bm + r] = perm[first + min(r, rows - 1)]
+// (rows past the tile's count repeat its last row), for the tiles of expert e
+// (nt tiles from tile0, sorted positions from off_e).  perm may be LDS.
+__device__ __forceinline__ void write_tile_rows(const int* perm, int off_e, int c, int tile0, int bm,
+                                                int* __restrict__ trows) {
+  const int nt = (c + bm - 1) / bm;
+  for (int i = 0; i < nt; ++i) {
+    const int rows = min(bm, c - i * bm);
+    for (int r = 0; r < bm; ++r) trows[(tile0 + i) * bm + r] = perm[off_e + i * bm + min(r, rows - 1)];
+  }
 }
 
 // Single block: counts from the chunk histograms (which become per-chunk
@@ -256,9 +269,10 @@ __global__ void __launch_bounds__(1024) qmoe_route_small(const float* __restrict
                                                          int* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                          int* __restrict__ counts, int* __restrict__ offsets,
                                                          int* __restrict__ perm, int* __restrict__ tiles,
-                                                         int* __restrict__ ntiles) {
+                                                         int* __restrict__ ntiles, int* __restrict__ trows) {
   __shared__ int s_idx[1024];
   __shared__ int s_cnt[1024];  // counts, then each expert's next sorted position
+  __shared__ int s_perm[1024];
   const int S = T * k;
   const int lane = lane_id(), w = threadIdx.x >> 6;
   if (threadIdx.x < E) s_cnt[threadIdx.x] = 0;
@@ -267,7 +281,8 @@ __global__ void __launch_bounds__(1024) qmoe_route_small(const float* __restrict
   if (threadIdx.x < S) atomicAdd(&s_cnt[s_idx[threadIdx.x]], 1);
   __syncthreads();
   const int c = threadIdx.x < E ? s_cnt[threadIdx.x] : 0;
-  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles);  // synchronises
+  int tile0 = 0;
+  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles, &tile0);  // synchronises
   if (threadIdx.x < E) s_cnt[threadIdx.x] = off_e;
   __syncthreads();
   const int nw = (S + 63) / 64;
@@ -282,13 +297,31 @@ __global__ void __launch_bounds__(1024) qmoe_route_small(const float* __restrict
         const int le = __shfl(e, leader);
         const unsigned long long m = __ballot(valid && e == le);
         const int base = s_cnt[le];
-        if (valid && e == le) perm[base + __popcll(m & ((1ull << lane) - 1ull))] = s;
+        if (valid && e == le) {
+          const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+          perm[pos] = s;
+          s_perm[pos] = s;
+        }
         if (lane == leader) s_cnt[le] = base + __popcll(m);
         todo &= ~m;
       }
     }
     __syncthreads();
   }
+  if (trows && threadIdx.x < E) write_tile_rows(s_perm, off_e, c, tile0, bm, trows);
+}
+
+// Tile-row table after the multi-kernel permutation: one thread per
+// (tile, row) entry; entries of unused tiles are left alone.
+__global__ void __launch_bounds__(256) qmoe_tile_rows(const int* __restrict__ perm, const int* __restrict__ tiles,
+                                                      const int* __restrict__ ntiles, int max_tiles, int bm,
+                                                      int* __restrict__ trows) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= max_tiles * bm) return;
+  const int t = i / bm, r = i % bm;
+  if (t >= ntiles[0]) return;
+  const int p0 = tiles[4 * t + 1], rows = tiles[4 * t + 2];
+  trows[i] = perm[p0 + min(r, rows - 1)];
 }
 
 // fp32 token rows -> f16 hi/lo operand rows (storage order of common.hpp),
@@ -351,12 +384,12 @@ hipError_t launch_router(const float* logits, int T, int E, int k, int routing, 
 
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int routing, int normalize, int bm,
                               int* topk_idx, float* topk_w, int* counts, int* offsets, int* perm, int* tiles,
-                              int* ntiles, hipStream_t st) {
+                              int* ntiles, int* trows, hipStream_t st) {
   if (T * k > 1024 || E > 1024) return hipErrorInvalidValue;
   const int V = (E + 63) / 64;
 #define QMOE_ROUTE_SMALL(VV)                                                                                       \
   hipLaunchKernelGGL(qmoe_route_small<VV>, dim3(1), dim3(1024), 0, st, logits, T, E, k, routing, normalize, bm,  \
-                     topk_idx, topk_w, counts, offsets, perm, tiles, ntiles)
+                     topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows)
   if (V <= 1) QMOE_ROUTE_SMALL(1);
   else if (V <= 2) QMOE_ROUTE_SMALL(2);
   else if (V <= 4) QMOE_ROUTE_SMALL(4);
@@ -371,6 +404,13 @@ hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchu
   hipLaunchKernelGGL(qmoe_hist, dim3(nchunks), dim3(256), E * sizeof(int), st, topk_idx, S, E, chunk, hist);
   hipLaunchKernelGGL(qmoe_scan, dim3(1), dim3(1024), 0, st, hist, nchunks, E, S, bm, counts, offsets, tiles, ntiles);
   hipLaunchKernelGGL(qmoe_scatter, dim3(nchunks), dim3(256), 5 * E * sizeof(int), st, topk_idx, hist, S, E, chunk, perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_rows(const int* perm, const int* tiles, const int* ntiles, int max_tiles, int bm, int* trows,
+                            hipStream_t st) {
+  const int n = max_tiles * bm;
+  hipLaunchKernelGGL(qmoe_tile_rows, dim3((n + 255) / 256), dim3(256), 0, st, perm, tiles, ntiles, max_tiles, bm, trows);
   return hipGetLastError();
 }
 

@@ -52,7 +52,13 @@ namespace {
 #endif
 constexpr int kSWaves = 8;  // wavefronts per workgroup
 constexpr int kCPI = 2;     // 64-byte chunks per item (one 128-byte line per row)
-constexpr int kP = QMOE_STREAM_INFLIGHT;  // items of loads in flight per wavefront while one is consumed
+// Items of loads in flight per wavefront while one is consumed: double-buffered
+// stages / single stage.
+constexpr int kPStaged = QMOE_STREAM_INFLIGHT;
+#ifndef QMOE_STREAM_INFLIGHT_ONE
+#define QMOE_STREAM_INFLIGHT_ONE 2
+#endif
+constexpr int kPOne = QMOE_STREAM_INFLIGHT_ONE;
 #ifndef QMOE_STREAM_NT
 #define QMOE_STREAM_NT 2
 #endif
@@ -103,7 +109,10 @@ qmoe_stream(GemmArgs g) {
   constexpr int WGR = kWGRows * RB;                 // weight rows of the workgroup
   // With one stage there is no next stage to stage, so registers allow the
   // ring to be copied out and refilled before each item is consumed.
-  constexpr bool LATE = !ONE;
+#ifndef QMOE_STREAM_ONE_LATE
+#define QMOE_STREAM_ONE_LATE 0
+#endif
+  constexpr bool LATE = !ONE || QMOE_STREAM_ONE_LATE;
   constexpr int CC = BITS == 4 ? 128 : 64;      // codes per 64-byte chunk
   constexpr int NS = CC / 32;                   // MFMA steps per chunk
   constexpr int ROWS = 16 * MT;
@@ -119,8 +128,9 @@ qmoe_stream(GemmArgs g) {
   constexpr int GPT = (ROWS * GR + NTH - 1) / NTH;      // staged groups per thread (fp32 rows)
   // stages per loop trip: a whole number of ring turns, so ring slots are
   // compile-time constants
-  constexpr int SPT = (STG % kP == 0) ? 1 : kP / STG;
-  static_assert(STG % kP == 0 || kP % STG == 0, "ring and stage sizes must nest");
+  constexpr int KP = ONE ? kPOne : kPStaged;      // ring depth
+  constexpr int SPT = (ONE || STG % KP == 0) ? 1 : KP / STG;
+  static_assert(ONE || STG % KP == 0 || KP % STG == 0, "ring and stage sizes must nest");
   extern __shared__ __align__(16) uint8_t lds[];  // 2 stage buffers, then the output tile
   __shared__ long s_rowbase[ROWS];
   __shared__ int s_orow[ROWS];
@@ -147,10 +157,24 @@ qmoe_stream(GemmArgs g) {
   const int tile = blockIdx.y;
   const int rgroup = blockIdx.z;
 #endif
-  if (tile >= g.ntiles[0]) return;
+  // The tile record is read together with the tile count (the record of a
+  // tile past the count is never used): one round trip, not two.
+  const int ntl = g.ntiles[0];
   const int e = g.tiles[4 * tile + 0];
   const int p0 = g.tiles[4 * tile + 1];
   const int rows = g.tiles[4 * tile + 2];
+  const int* trow = g.trows + tile * ROWS;  // slot id of each tile row (rows past the count: the last row)
+  // Single stage, FC1: the fp32 input row of each tile row this wavefront
+  // stages (rows wv + 8i), from the same round trip.
+  constexpr int RPW = ROWS / kSWaves;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int rslot[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) rslot[i] = (ONE && FC1) ? trow[wv + kSWaves * i] : 0;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) asm volatile("" ::"s"(rslot[i]));
+  asm volatile("" ::"s"(ntl), "s"(e), "s"(p0), "s"(rows));
+  if (tile >= ntl) return;
   const int nst = g.nst;                 // stages in this K range
   const int nit = nst * STG;             // items in this K range
   const int c0 = split * nst * SCH;      // first chunk of the K range
@@ -177,11 +201,11 @@ qmoe_stream(GemmArgs g) {
     if constexpr (SPB > 0) sbase[nt] += (c0 * CC) / (SPB * 32) + grp * Q;  // this lane group's blocks
   }
 
-  // Ring of kP items: packed weights, plus the scales of blocks that span
+  // Ring of KP items: packed weights, plus the scales of blocks that span
   // whole chunks.  Item indices past the range re-read its last item (kept
   // unconditional so that the waits stay exact).
-  u32x4 bq[kP][NT][kCPI];
-  float sq[kP][NT][kCPI];
+  u32x4 bq[KP][NT][kCPI];
+  float sq[KP][NT][kCPI];
   auto issue = [&](int slot, int it) {
     // ONE: item it is piece it % STG of row block it / STG (compile-time)
     const int rb = ONE ? it / STG : 0;
@@ -220,33 +244,38 @@ qmoe_stream(GemmArgs g) {
     }
   };
 
-  // Start the weight stream before anything else: its addresses depend only
-  // on the tile.
-  if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(0);
+  // Start the weight stream: its addresses depend only on the tile.
+  auto start_stream = [&]() {
+    if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(0);
 #pragma unroll
-  for (int u = 0; u < kP; ++u)
-    if (!ONE || u < RB * STG) issue(u, u);
-
-  // Activation row of every tile row (clamped to valid rows) and its output row.
-  if (threadIdx.x < ROWS) {
-    const int p = p0 + min((int)threadIdx.x, rows - 1);
-    const long ar = FC1 ? (long)(g.a_map[p] / g.a_div) : (long)p;
-    s_rowbase[threadIdx.x] = ar * g.a_stride + (long)c0 * CC * 4;
-    s_orow[threadIdx.x] = g.store_by_slot ? g.perm[p] : p;
+    for (int u = 0; u < KP; ++u)
+      if (!ONE || u < RB * STG) issue(u, u);
+  };
+  if constexpr (!ONE) {
+    start_stream();
+    // Activation row of every tile row (clamped to valid rows) and its output row.
+    if (threadIdx.x < ROWS) {
+      const int p = p0 + min((int)threadIdx.x, rows - 1);
+      const int slot = trow[threadIdx.x];
+      const long ar = FC1 ? (long)(slot / g.a_div) : (long)p;
+      s_rowbase[threadIdx.x] = ar * g.a_stride + (long)c0 * CC * 4;
+      s_orow[threadIdx.x] = g.store_by_slot ? slot : p;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // Activation staging of one stage: loads into registers, then LDS writes.
   // Row r keeps its 16-byte pieces with the piece index XOR-ed by (r & 15), so
   // the 16 rows read by one instruction hit distinct banks.  Invalid rows
   // (>= rows) re-read the last valid row; loads are unconditional.
-  // The next stage's slice is fetched in NPART parts, one per item, each
-  // held in registers for one item only.
+  // The next stage's slice is fetched in NPART parts at the start of a stage
+  // (before that stage's ring refills, so that waiting for it never waits
+  // for them) and written to LDS one part after each item.
   constexpr int NPART = FC1 ? (GPT % STG == 0 ? STG : 1) : (PPT % STG == 0 ? STG : 1);
   constexpr int GPP = GPT / (FC1 ? NPART : 1);   // fp32 groups per thread per part
   constexpr int PPP = PPT / (FC1 ? 1 : NPART);   // f16 pieces per thread per part
-  f32x4 areg32[FC1 ? GPP : 1][2];
-  u32x4 areg16[FC1 ? 1 : PPP];
+  f32x4 areg32[FC1 ? NPART : 1][FC1 ? GPP : 1][2];
+  u32x4 areg16[FC1 ? 1 : NPART][FC1 ? 1 : PPP];
   auto stage_load = [&](int st, int part) {
     const long off = (long)min(st, nst - 1) * SCODES * 4;
     if constexpr (FC1) {
@@ -259,8 +288,8 @@ qmoe_stream(GemmArgs g) {
         // their own 8 codes, 8-bit groups those of code group sigma(gq % 4)
         const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
         const float* src = (const float*)(g.a + s_rowbase[min(r, rows - 1)] + off) + j0;
-        areg32[ii][0] = *(const f32x4*)src;
-        areg32[ii][1] = *(const f32x4*)(src + 4);
+        areg32[part][ii][0] = *(const f32x4*)src;
+        areg32[part][ii][1] = *(const f32x4*)(src + 4);
       }
     } else {
 #pragma unroll
@@ -268,7 +297,7 @@ qmoe_stream(GemmArgs g) {
         const int i = part * PPP + ii;
         const int idx = min((int)threadIdx.x + i * NTH, ROWS * PIECES - 1);
         const int r = idx / PIECES, q = idx % PIECES;
-        areg16[ii] = *(const u32x4*)(g.a + s_rowbase[min(r, rows - 1)] + off + q * 16);
+        areg16[part][ii] = *(const u32x4*)(g.a + s_rowbase[min(r, rows - 1)] + off + q * 16);
       }
     }
   };
@@ -285,7 +314,7 @@ qmoe_stream(GemmArgs g) {
           for (int sl = 0; sl < 8; ++sl) {
             const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code inside the group at storage slot sl
             _Float16 h, l;
-            split_f16(areg32[ii][c >> 2][c & 3], h, l);
+            split_f16(areg32[part][ii][c >> 2][c & 3], h, l);
             hi[sl] = h;
             lo[sl] = l;
           }
@@ -299,38 +328,91 @@ qmoe_stream(GemmArgs g) {
       for (int ii = 0; ii < PPP; ++ii) {
         const int idx = threadIdx.x + (part * PPP + ii) * NTH;
         const int r = idx / PIECES, q = idx % PIECES;
-        if (idx < ROWS * PIECES) *(u32x4*)(base + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = areg16[ii];
+        if (idx < ROWS * PIECES) *(u32x4*)(base + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = areg16[part][ii];
       }
     }
   };
   if constexpr (ONE) {
-    // The only stage: stage just the tile's valid rows (the matrix rows past
-    // them read the last valid row).  Loads here may be conditional: only the
-    // ring's first items are in flight, and they are older.
-    if constexpr (FC1) {
-      for (int idx = threadIdx.x; idx < rows * GR; idx += NTH) {
-        const int r = idx / GR, gq = idx % GR;
-        const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
-        const float* src = (const float*)(g.a + s_rowbase[r]) + j0;
-        const f32x4 v0 = *(const f32x4*)src, v1 = *(const f32x4*)(src + 4);
-        f16x8 hi, lo;
+    // The only stage, staged once: wavefront w stages tile rows w + 8i (valid
+    // rows only; the matrix rows past them read the last valid row), with
+    // loads issued before the weight stream, so that waiting for them never
+    // waits for it (loads complete in issue order).  FC1 holds the fp32 rows
+    // in registers until the stream is issued, then splits them into f16
+    // hi/lo in LDS; FC2 rows are already f16 hi/lo and load straight into LDS.
+    constexpr int UPR = FC1 ? GR : PIECES;           // load units per row: fp32 8-code groups / f16 pieces
+    constexpr int RPI = UPR >= 64 ? 1 : 64 / UPR;    // rows per load instruction
+    constexpr int MPW = RPI > 1 ? (RPW + RPI - 1) / RPI : RPW * UPR / 64;  // units per lane
+    static_assert(UPR % 64 == 0 || 64 % UPR == 0, "staging units");
+    long rbase[RPW];
 #pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code inside the group at storage slot sl
-          _Float16 h, l;
-          split_f16(c < 4 ? v0[c] : v1[c - 4], h, l);
-          hi[sl] = h;
-          lo[sl] = l;
+    for (int i = 0; i < RPW; ++i) {
+      const int r = wv + kSWaves * i;
+      const long ar = FC1 ? (long)(rslot[i] / g.a_div) : (long)(p0 + min(r, rows - 1));
+      rbase[i] = ar * g.a_stride + (long)c0 * CC * 4;
+    }
+    // unit m of this lane: tile row r (r >= ROWS: none), load unit q, row base
+    auto unit = [&](int m, int& r, int& q, long& base) {
+      const int i0 = RPI > 1 ? m * RPI : (64 * m) / UPR;
+      const int i = RPI > 1 ? i0 + lane / UPR : i0;
+      r = i < RPW ? wv + kSWaves * i : ROWS;
+      q = RPI > 1 ? lane % UPR : (64 * m + lane) % UPR;
+      base = rbase[min(i0, RPW - 1)];
+#pragma unroll
+      for (int k = 1; k < RPI; ++k) {
+        long v = rbase[min(i0 + k, RPW - 1)];
+        asm volatile("" : "+s"(v));  // a plain select, not an indexed private array
+        if (lane / UPR == k) base = v;
+      }
+    };
+    if constexpr (FC1) {
+      f32x4 sv[MPW][2];
+#pragma unroll
+      for (int m = 0; m < MPW; ++m) {
+        int r, q;
+        long base;
+        unit(m, r, q, base);
+        if (r < rows) {
+          const int j0 = BITS == 4 ? 8 * q : ((8 * q) & ~31) | (sigma8(q & 3) << 3);
+          const float* src = (const float*)(g.a + base) + j0;
+          sv[m][0] = *(const f32x4*)src;
+          sv[m][1] = *(const f32x4*)(src + 4);
         }
-        uint8_t* row = lds + r * LSTRIDE;
-        *(f16x8*)(row + (((2 * gq) ^ (r & 15)) * 16)) = hi;
-        *(f16x8*)(row + (((2 * gq + 1) ^ (r & 15)) * 16)) = lo;
+      }
+      start_stream();
+#pragma unroll
+      for (int m = 0; m < MPW; ++m) {
+        int r, q;
+        long base;
+        unit(m, r, q, base);
+        if (r < rows) {
+          f16x8 hi, lo;
+#pragma unroll
+          for (int sl = 0; sl < 8; ++sl) {
+            const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code inside the group at storage slot sl
+            _Float16 h, l;
+            split_f16(sv[m][c >> 2][c & 3], h, l);
+            hi[sl] = h;
+            lo[sl] = l;
+          }
+          uint8_t* row = lds + r * LSTRIDE;
+          *(f16x8*)(row + (((2 * q) ^ (r & 15)) * 16)) = hi;
+          *(f16x8*)(row + (((2 * q + 1) ^ (r & 15)) * 16)) = lo;
+        }
       }
     } else {
-      for (int idx = threadIdx.x; idx < rows * PIECES; idx += NTH) {
-        const int r = idx / PIECES, q = idx % PIECES;
-        *(u32x4*)(lds + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = *(const u32x4*)(g.a + s_rowbase[r] + q * 16);
+      // One instruction fills up to 64 consecutive swizzled piece slots of
+      // row r: lane l writes slot P0 + l, so it loads piece (P0 + l) ^ (r & 15).
+      constexpr int NI = UPR >= 64 ? RPW * UPR / 64 : RPW;  // instructions per wavefront
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const int i = UPR >= 64 ? (64 * m) / UPR : m, P0 = UPR >= 64 ? (64 * m) % UPR : 0;
+        const int r = wv + kSWaves * i;
+        if (r < rows && (UPR >= 64 || lane < UPR))
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(g.a + rbase[i] + ((P0 + lane) ^ (r & 15)) * 16),
+              (__attribute__((address_space(3))) void*)(lds + r * LSTRIDE + P0 * 16), 16, 0, 0);
       }
+      start_stream();
     }
   } else {
 #pragma unroll
@@ -385,7 +467,7 @@ qmoe_stream(GemmArgs g) {
     for (int il = 0; il < RB * STG; ++il) {
       // keep each item's work in its own scheduling region (bounded live ranges)
       __builtin_amdgcn_sched_barrier(0);
-      const int u = (Q0 * STG + il) % kP;
+      const int u = (Q0 * STG + il) % KP;
       const int it = st * STG + il;          // ONE: st == 0
       const int ii = il % STG;               // item inside the stage
       const int rb = il / STG;               // row block (ONE)
@@ -414,14 +496,16 @@ qmoe_stream(GemmArgs g) {
       if constexpr (!ONE) {
         if (il == STG - 1)
           if constexpr (SCALE == SC_BLOCK && SPB > 0) issue_scales(st + 1);
-        if (NPART == STG || il == STG - 1) stage_load(st + 1, NPART == STG ? il : 0);
+        if (il == 0)
+#pragma unroll
+          for (int part = 0; part < NPART; ++part) stage_load(st + 1, part);
       } else if constexpr (SCALE == SC_BLOCK && SPB > 0) {
         if (ii == STG - 1 && rb + 1 < RB) issue_scales(rb + 1);  // next row block's scales
       }
       // (with one stage the items past the range are known at compile time
       // and are not fetched)
       if constexpr (!LATE)
-        if (!ONE || il + kP < RB * STG) issue(u, it + kP);
+        if (!ONE || il + KP < RB * STG) issue(u, it + KP);
 #pragma unroll
       for (int h = 0; h < kCPI; ++h) {
         const int cl = ii * kCPI + h;  // chunk index inside the stage
@@ -479,7 +563,7 @@ qmoe_stream(GemmArgs g) {
         }
       }
       if constexpr (LATE)
-        if (!ONE || il + kP < RB * STG) issue(u, it + kP);
+        if (!ONE || il + KP < RB * STG) issue(u, it + KP);
       if constexpr (RB > 1)
         if (ii == STG - 1 && rb + 1 < RB) {
           // row block done: keep it until the stream ends
@@ -514,6 +598,10 @@ qmoe_stream(GemmArgs g) {
   // barrier); tile columns are XOR-swizzled by 16 * ((row / 4) % 4), so the
   // four row groups of one write hit distinct banks.
   float* otile = reinterpret_cast<float*>(lds);
+  // single stage: output row ids now (the stream is drained, so this load
+  // waits for nothing else)
+  int orow = 0;
+  if (ONE && threadIdx.x < ROWS) orow = g.store_by_slot ? trow[threadIdx.x] : p0 + min((int)threadIdx.x, rows - 1);
   auto tix = [](int rr, int c) { return rr * WGR + (c ^ (16 * ((rr >> 2) & 3))); };
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -531,6 +619,7 @@ qmoe_stream(GemmArgs g) {
           if (rr < rows) otile[tix(rr, c)] = v * sc;
         }
     }
+  if (ONE && threadIdx.x < ROWS) s_orow[threadIdx.x] = orow;
   __syncthreads();
 
   if (FC1 && g.act != nullptr) {
@@ -731,7 +820,7 @@ size_t stream_lds_bytes(int bits, int mt, bool one, int N) {
 }
 
 hipError_t launch_stream(int bits, int mt, bool one, int splits, const GemmArgs& g, int max_tiles, hipStream_t st) {
-  if (mt < 1 || mt > 4 || (one && g.nst != 1)) return hipErrorInvalidValue;
+  if (mt < 1 || mt > 4 || (one && g.nst != 1) || g.trows == nullptr) return hipErrorInvalidValue;
   const int rb = stream_row_blocks(mt, one, g.N);
   const size_t lds = stream_lds_bytes(bits, mt, one, g.N);
   const int wg_rows = kWGRows * rb;

@@ -75,6 +75,8 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
   uint8_t* xa = ws + p.off_xa;
   uint8_t* act = ws + p.off_act;
   float* slot = reinterpret_cast<float*>(ws + p.off_slot);
+  // slot ids of the tile rows, for the weight-streaming kernels
+  int* trows = p.s1.on || p.s2.on ? reinterpret_cast<int*>(ws + p.off_trows) : nullptr;
 
   auto mark = [&](int i) -> hipError_t {
     if (dbg && d.I > 0 && dbg->events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(dbg->events[i]), s);
@@ -83,12 +85,13 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
   QMOE_TRY_HIP(mark(0));
   if (p.small_front) {
     QMOE_TRY_HIP(launch_route_small(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize,
-                                    (int)p.bm, topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, s));
+                                    (int)p.bm, topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows, s));
   } else {
     QMOE_TRY_HIP(launch_router(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize, topk_idx,
                                topk_w, s));
     QMOE_TRY_HIP(launch_permute(topk_idx, S, E, (int)p.chunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets,
                                 perm, tiles, ntiles, s));
+    if (trows) QMOE_TRY_HIP(launch_tile_rows(perm, tiles, ntiles, (int)p.max_tiles, (int)p.bm, trows, s));
   }
   if (d.I > 0) {
     // The streaming FC1 splits the fp32 input rows itself while staging them
@@ -110,6 +113,7 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g1.a_stride = a_f32 ? 4 * H : 4 * p.kp1;
     g1.tiles = tiles;
     g1.ntiles = ntiles;
+    g1.trows = trows;
     g1.N = (int)d.F;
     g1.K = H;
     g1.kb = (int)(d.H / d.pack);
@@ -155,6 +159,7 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g2.a_stride = 4 * p.kp2;
     g2.tiles = tiles;
     g2.ntiles = ntiles;
+    g2.trows = trows;
     g2.N = H;
     g2.K = I;
     g2.kb = (int)(d.I / d.pack);

@@ -208,6 +208,7 @@ void make_plan(const Dims& d, Plan* p) {
   p->off_act = take(size_t(4) * p->S * p->kp2);   // f16 hi + lo per element
   p->off_slot = take(d.I > 0 ? sizeof(float) * p->splits2 * p->S * d.H : 0); // FC2 rows by slot id
   p->off_part1 = take(p->s1.on && p->s1.splits > 1 ? sizeof(float) * p->s1.splits * p->S * d.F : 0);
+  p->off_trows = take(p->s1.on || p->s2.on ? sizeof(int32_t) * p->max_tiles * p->bm : 0);
   p->bytes = o;
 }
 

@@ -63,6 +63,7 @@ struct Plan {
   } s1, s2;
   int splits2 = 1;       // FC2 partial sets the combine sums (1 off the stream path)
   size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path with K ranges)
+  size_t off_trows = 0;  // streaming kernels: slot id of every tile row [max_tiles][bm]
   bool small_front = false;  // router + permutation in one workgroup (S, E <= 1024)
   int64_t chunk = 1024;  // slots per permutation block
   int64_t nchunks = 0;
