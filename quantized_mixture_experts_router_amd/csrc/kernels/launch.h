@@ -52,6 +52,7 @@ struct GemmArgs {
   int nst;              // stages per K range
   int act_swiglu;       // FC1 over the whole of K: activation written by the kernel (act != nullptr)
   const int* trows;     // stream kernel: slot id of every tile row, [max_tiles][16 * mt] (see launch_tile_rows)
+  int wg_rows;          // stream kernel, double-buffered: weight rows per workgroup (set by launch_stream)
 };
 
 enum { EPI_RELU = 0, EPI_SWIGLU = 1, EPI_STORE = 2 };
@@ -70,8 +71,11 @@ hipError_t launch_tiled(int bits, int epi, const GemmArgs& g, int max_tiles, hip
 // kernel writes FC2 operand rows after the activation, else fp32 partial rows
 // part[z][p][N].  FC2: partial rows by slot id, slot_out[z][slot][N].
 // z < splits K ranges of g.nst stages each.
+// wg_rows: double-buffered mode, weight rows per workgroup (a multiple of 64
+// up to 512, above 256 only for mt == 1; 0 = 256).
 size_t stream_lds_bytes(int bits, int mt, bool one, int N);
-hipError_t launch_stream(int bits, int mt, bool one, int splits, const GemmArgs& g, int max_tiles, hipStream_t st);
+hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, const GemmArgs& g, int max_tiles,
+                         hipStream_t st);
 
 // Sum FC1 partials over K ranges, apply the activation, write FC2 operand rows.
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,

@@ -50,6 +50,9 @@ namespace {
 #ifndef QMOE_STREAM_NT_LOADS
 #define QMOE_STREAM_NT_LOADS 0
 #endif
+#ifndef QMOE_STREAM_ROTATE
+#define QMOE_STREAM_ROTATE 0
+#endif
 constexpr int kSWaves = 8;  // wavefronts per workgroup
 constexpr int kCPI = 2;     // 64-byte chunks per item (one 128-byte line per row)
 // Items of loads in flight per wavefront while one is consumed: double-buffered
@@ -105,8 +108,10 @@ template <int BITS, int MT, int SCALE, int SPB, bool FC1, bool ONE, int RB>
 __global__ void __launch_bounds__(64 * kSWaves) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2, MT == 1 ? 4 : 2)))
 qmoe_stream(GemmArgs g) {
   constexpr int STG = stream_stage_items(MT, ONE);  // items per stage
-  static_assert(RB == 1 || ONE, "row blocks reuse a single stage");
+  // Row blocks: ONE streams them one after the other against its one stage;
+  // double-buffered mode walks the whole K range once per row block.
   constexpr int WGR = kWGRows * RB;                 // weight rows of the workgroup
+  constexpr int RBI = ONE ? RB : 1;                 // row blocks inside one stage
   // With one stage there is no next stage to stage, so registers allow the
   // ring to be copied out and refilled before each item is consumed.
 #ifndef QMOE_STREAM_ONE_LATE
@@ -131,6 +136,7 @@ qmoe_stream(GemmArgs g) {
   constexpr int KP = ONE ? kPOne : kPStaged;      // ring depth
   constexpr int SPT = (ONE || STG % KP == 0) ? 1 : KP / STG;
   static_assert(ONE || STG % KP == 0 || KP % STG == 0, "ring and stage sizes must nest");
+  static_assert(ONE || RB == 1 || SPT == 1, "row blocks of a walk start on ring slot 0");
   extern __shared__ __align__(16) uint8_t lds[];  // 2 stage buffers, then the output tile
   __shared__ long s_rowbase[ROWS];
   __shared__ int s_orow[ROWS];
@@ -178,17 +184,30 @@ qmoe_stream(GemmArgs g) {
   const int nst = g.nst;                 // stages in this K range
   const int nit = nst * STG;             // items in this K range
   const int c0 = split * nst * SCH;      // first chunk of the K range
+  const int nstt = ONE ? 1 : RB * nst;   // stages of the whole walk
+  // Double-buffered mode starts its walk of the K range at stage rot (then
+  // wraps), so that concurrent workgroups read different columns of their rows.
+#if QMOE_STREAM_ROTATE
+  const int rot = ONE ? 0 : (int)((blockIdx.z * 5u + blockIdx.y * 3u + blockIdx.x) % (unsigned)nst);
+#else
+  const int rot = 0;
+#endif
+  auto kpos = [&](int kst) { return kst + rot < nst ? kst + rot : kst + rot - nst; };  // stage -> K stage
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int n0 = rgroup * WGR;           // first weight row of the workgroup
+  // Rows of the workgroup: WGR, or in double-buffered mode g.wg_rows (up to
+  // RB row blocks; waves whose rows of a row block lie past them re-read one
+  // cached line instead and their results are dropped).
+  const int R = ONE ? WGR : g.wg_rows;
+  const int n0 = rgroup * R;             // first weight row of the workgroup
   const long ebase = (long)e * g.N;
   const long kb_bytes = g.kb;
 
   // Rows past N (last row group) stream a clamped row; their results are
-  // dropped.  Row block rb adds rb * kWGRows rows (RB > 1: N is a multiple of WGR).
+  // dropped.  Row block rb adds rb * kWGRows rows.
   const long bstep = (long)kWGRows * kb_bytes;
   const long sstep = (long)kWGRows * g.nblk;
   const uint8_t* bbase[NT];
@@ -206,18 +225,36 @@ qmoe_stream(GemmArgs g) {
   // unconditional so that the waits stay exact).
   u32x4 bq[KP][NT][kCPI];
   float sq[KP][NT][kCPI];
+  // K item of walk item i of a row block
+  auto kitem = [&](int i) { return kpos(i / STG) * STG + i % STG; };
   auto issue = [&](int slot, int it) {
-    // ONE: item it is piece it % STG of row block it / STG (compile-time)
-    const int rb = ONE ? it / STG : 0;
-    const int itc = ONE ? it % STG : min(it, nit - 1);
+    // ONE: item it is piece it % STG of row block it / STG (compile-time);
+    // otherwise walk item it % nit of row block it / nit, past the end the
+    // last item again
+    int rb, itc;
+    bool live = true;  // this wave has rows in the row block
+    if constexpr (ONE) {
+      rb = it / STG;
+      itc = it % STG;
+    } else {
+      const int itw = min(it, RB * nit - 1);
+      rb = RB > 1 && itw >= nit ? itw / nit : 0;
+      itc = kitem(itw - rb * nit);
+      if constexpr (RB > 1) live = rb * kWGRows + wv * 16 * NT < R;
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint8_t* src = bbase[nt] + rb * bstep + (long)itc * (kCPI * 64);
+      // (a wave without rows here re-reads its first line: a cache hit)
+      const uint8_t* src;
+      if constexpr (!ONE && RB > 1) src = bbase[nt] + (live ? (int)(rb * bstep) + itc * (kCPI * 64) : 0);
+      else src = bbase[nt] + rb * bstep + (long)itc * (kCPI * 64);
 #pragma unroll
       for (int h = 0; h < kCPI; ++h) bq[slot][nt][h] = load_weights(src + h * 64);
       if constexpr (SCALE != SC_COL && SPB == 0) {
 #pragma unroll
-        for (int h = 0; h < kCPI; ++h) sq[slot][nt][h] = sbase[nt][rb * sstep + ((c0 + itc * kCPI + h) * CC) / g.bs];
+        for (int h = 0; h < kCPI; ++h)
+          sq[slot][nt][h] = sbase[nt][(!ONE && RB > 1) ? (live ? (int)(rb * sstep) + ((c0 + itc * kCPI + h) * CC) / g.bs : 0)
+                                                       : rb * sstep + ((c0 + itc * kCPI + h) * CC) / g.bs];
       }
     }
   };
@@ -226,7 +263,16 @@ qmoe_stream(GemmArgs g) {
   // block's scale is then fetched from the owning lane group by ds_bpermute.
   float snext[NT][Q], scur[NT][Q];
   auto issue_scales = [&](int st) {  // ONE: st is the row block
-    const long off = ONE ? st * sstep : (long)min(st, nst - 1) * NBS;
+    long off;
+    if constexpr (ONE) {
+      off = st * sstep;
+    } else {
+      const int stw = min(st, nstt - 1);
+      int rb = RB > 1 && stw >= nst ? stw / nst : 0;
+      const int kst = stw - rb * nst;
+      if (RB > 1 && rb * kWGRows + wv * 16 * NT >= R) rb = 0;  // no rows there: row block 0's scales
+      off = rb * sstep + (long)kpos(kst) * NBS;
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float* sp = sbase[nt] + off;
@@ -277,7 +323,8 @@ qmoe_stream(GemmArgs g) {
   f32x4 areg32[FC1 ? NPART : 1][FC1 ? GPP : 1][2];
   u32x4 areg16[FC1 ? 1 : NPART][FC1 ? 1 : PPP];
   auto stage_load = [&](int st, int part) {
-    const long off = (long)min(st, nst - 1) * SCODES * 4;
+    const int stw = min(st, nstt - 1);
+    const long off = (long)kpos(stw % nst) * SCODES * 4;
     if constexpr (FC1) {
 #pragma unroll
       for (int ii = 0; ii < GPP; ++ii) {
@@ -455,6 +502,99 @@ qmoe_stream(GemmArgs g) {
 
   const UnpackMasks um = unpack_masks();
 
+  // Output of TW weight rows from n0e: every wavefront puts its rows
+  // (column scales applied; val(row block, mt, nt, i) gives the results) into
+  // the LDS tile [ROWS][TW]; tile columns are XOR-swizzled by
+  // 16 * ((row / 4) % 4), so the four row groups of one write hit distinct
+  // banks.  Then FC1 with one K range applies the activation and writes FC2
+  // operand rows; otherwise fp32 partial rows of this K range are written.
+  auto emit = [&](float* otile, auto twc, const int n0e, const int ncols, auto val) {
+  constexpr int TW = decltype(twc)::value;
+  auto tix = [](int rr, int c) { return rr * TW + (c ^ (16 * ((rr >> 2) & 3))); };
+#pragma unroll
+  for (int cb = 0; cb < TW / kWGRows; ++cb)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int c = cb * kWGRows + wave * 16 * NT + nt * 16 + col;  // tile column
+      float sc = 1.f;
+      if constexpr (SCALE == SC_COL) sc = g.ws[ebase + min(n0e + c, g.N - 1)];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = mt * 16 + 4 * grp + i;
+          if (rr < rows) otile[tix(rr, c)] = val(cb, mt, nt, i) * sc;
+        }
+    }
+  __syncthreads();
+
+  if (FC1 && g.act != nullptr) {
+    // Whole of K: apply the activation and write FC2 operand rows (f16 hi/lo
+    // groups, storage order of common.hpp) for this workgroup's codes.
+    // ReLU: code j = row n.  Interleaved SwiGLU: code j takes rows 2j (gate)
+    // and 2j + 1 (linear): g * sigmoid(alpha * g) * (u + beta).
+    const bool swiglu = g.act_swiglu != 0;
+    const int I = swiglu ? g.N / 2 : g.N;
+    const int jbase = swiglu ? n0e / 2 : n0e;
+    const int gtot = (int)(g.act_stride / 32);       // groups per operand row
+    // codes of this tile (whole 32-code blocks); the tile holding row N - 1
+    // also writes the zero padding codes up to the end of the operand row
+    int jw = swiglu ? ncols / 2 : ncols;
+    if (n0e + ncols >= g.N) jw = max(jw, gtot * 8 - jbase);
+    for (int idx = threadIdx.x; idx < rows * (jw / 8); idx += NTH) {
+      const int rr = idx / (jw / 8);
+      const int gq = jbase / 8 + idx % (jw / 8);
+      if (gq >= gtot) continue;
+      const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
+      float a[8];
+      if (j0 >= I) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a[c] = 0.f;
+      } else if (swiglu) {
+        const int t0 = 2 * (j0 - jbase);  // tile column of row 2*j0 (16 consecutive columns)
+        f32x4 v[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float gv = v[c >> 1][2 * (c & 1)], uv = v[c >> 1][2 * (c & 1) + 1];
+          a[c] = j0 + c < I ? gv / (1.f + expf(-g.alpha * gv)) * (uv + g.beta) : 0.f;
+        }
+      } else {
+        const int t0 = j0 - jbase;
+        f32x4 v[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a[c] = j0 + c < I ? fmaxf(v[c >> 2][c & 3], 0.f) : 0.f;
+      }
+      f16x8 hi, lo;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code j0 + c sits at storage slot sl
+        _Float16 hh, ll;
+        split_f16(a[c], hh, ll);
+        hi[sl] = hh;
+        lo[sl] = ll;
+      }
+      uint8_t* dst = g.act + (long)(p0 + rr) * g.act_stride + (long)gq * 32;
+      *(f16x8*)dst = hi;
+      *(f16x8*)(dst + 16) = lo;
+    }
+  } else if ((g.N & 3) == 0) {
+    for (int idx = threadIdx.x; idx < rows * (TW / 4); idx += NTH) {
+      const int rr = idx / (TW / 4), c = 4 * (idx % (TW / 4));
+      if (c < ncols && n0e + c < g.N)
+        *(f32x4*)(g.slot_out + ((long)split * g.S + s_orow[rr]) * g.N + n0e + c) = *(const f32x4*)(otile + tix(rr, c));
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < rows * TW; idx += NTH) {
+      const int rr = idx / TW, c = idx % TW;
+      if (c < ncols && n0e + c < g.N) g.slot_out[((long)split * g.S + s_orow[rr]) * g.N + n0e + c] = otile[tix(rr, c)];
+    }
+  }
+  };
+
   // One stage: its STG items from LDS buffer (st & 1), with the next stage's
   // scales and activation slice fetched during the last item (issued before
   // that item's ring refill, so waiting for them never waits for the refill).
@@ -463,14 +603,16 @@ qmoe_stream(GemmArgs g) {
   auto stage = [&](int st, auto q0c) {
     constexpr int Q0 = decltype(q0c)::value;
     const uint8_t* abuf = lds + (st & 1) * BUF;
+    const int kst = ONE ? 0 : st % nst;    // walk stage inside the row block
 #pragma unroll
-    for (int il = 0; il < RB * STG; ++il) {
+    for (int il = 0; il < RBI * STG; ++il) {
       // keep each item's work in its own scheduling region (bounded live ranges)
       __builtin_amdgcn_sched_barrier(0);
       const int u = (Q0 * STG + il) % KP;
       const int it = st * STG + il;          // ONE: st == 0
       const int ii = il % STG;               // item inside the stage
       const int rb = il / STG;               // row block (ONE)
+      const int itc = kst * STG + ii;        // walk item inside the row block (double-buffered)
       if constexpr (SCALE == SC_BLOCK && SPB > 0)
         if (ii == 0) {
 #pragma unroll
@@ -505,7 +647,7 @@ qmoe_stream(GemmArgs g) {
       // (with one stage the items past the range are known at compile time
       // and are not fetched)
       if constexpr (!LATE)
-        if (!ONE || il + KP < RB * STG) issue(u, it + KP);
+        if (!ONE || il + KP < RBI * STG) issue(u, it + KP);
 #pragma unroll
       for (int h = 0; h < kCPI; ++h) {
         const int cl = ii * kCPI + h;  // chunk index inside the stage
@@ -549,8 +691,8 @@ qmoe_stream(GemmArgs g) {
         }
         if constexpr (SCALE != SC_COL && SPB == 0) {
           // end of a scale block, or end of this K range's share of one
-          const int chunk = c0 + (ONE ? ii : it) * kCPI + h;
-          if ((chunk + 1) % cpb == 0 || ((ONE ? ii == STG - 1 : it == nit - 1) && h == kCPI - 1)) {
+          const int chunk = c0 + (ONE ? ii : kitem(itc)) * kCPI + h;
+          if ((chunk + 1) % cpb == 0 || ((ONE ? ii == STG - 1 : itc == nit - 1) && h == kCPI - 1)) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -563,8 +705,8 @@ qmoe_stream(GemmArgs g) {
         }
       }
       if constexpr (LATE)
-        if (!ONE || il + KP < RB * STG) issue(u, it + KP);
-      if constexpr (RB > 1)
+        if (!ONE || il + KP < RBI * STG) issue(u, it + KP);
+      if constexpr (ONE && RB > 1)
         if (ii == STG - 1 && rb + 1 < RB) {
           // row block done: keep it until the stream ends
 #pragma unroll
@@ -580,106 +722,49 @@ qmoe_stream(GemmArgs g) {
       // last barrier.
       if constexpr (!ONE)
         if (NPART == STG || il == STG - 1)
-          if (st + 1 < nst) stage_store((st + 1) & 1, NPART == STG ? il : 0);
+          if (st + 1 < nstt) stage_store((st + 1) & 1, NPART == STG ? il : 0);
     }
     __syncthreads();
   };
 
-  const int nmain = nst - nst % SPT;
-  for (int s0 = 0; s0 < nmain; s0 += SPT) {
-    stage(s0, std::integral_constant<int, 0>{});
-    if constexpr (SPT > 1) stage(s0 + 1, std::integral_constant<int, 1>{});
-  }
-  if constexpr (SPT > 1)
-    if (nmain < nst) stage(nmain, std::integral_constant<int, 0>{});
-
-  // Output: every wavefront puts its rows (column scales applied) into the
-  // LDS tile [ROWS][WGR] (the stage buffers are free after the last
-  // barrier); tile columns are XOR-swizzled by 16 * ((row / 4) % 4), so the
-  // four row groups of one write hit distinct banks.
-  float* otile = reinterpret_cast<float*>(lds);
-  // single stage: output row ids now (the stream is drained, so this load
-  // waits for nothing else)
-  int orow = 0;
-  if (ONE && threadIdx.x < ROWS) orow = g.store_by_slot ? trow[threadIdx.x] : p0 + min((int)threadIdx.x, rows - 1);
-  auto tix = [](int rr, int c) { return rr * WGR + (c ^ (16 * ((rr >> 2) & 3))); };
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int c = rb * kWGRows + wave * 16 * NT + nt * 16 + col;  // tile column
-      float sc = 1.f;
-      if constexpr (SCALE == SC_COL) sc = g.ws[ebase + min(n0 + c, g.N - 1)];
+  // Row block rb is complete: its results leave through the stage buffer just
+  // read (free after the barrier; the next write to it follows the next
+  // stage) or, after the last stage, through the whole allocation; then the
+  // accumulators restart.
+  auto close_block = [&](int rb) {
+    const int st = (rb + 1) * nst - 1;  // its last stage
+    emit(reinterpret_cast<float*>(lds + (st + 1 < nstt ? (st & 1) * BUF : 0)), std::integral_constant<int, kWGRows>{},
+         n0 + rb * kWGRows, min(kWGRows, R - rb * kWGRows), [&](int, int mt, int nt, int i) { return acc[mt][nt][i]; });
+    if (rb + 1 < RB) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = mt * 16 + 4 * grp + i;
-          const float v = (RB > 1 && rb == 0) ? res[RB > 1 ? mt : 0][nt][i] : acc[mt][nt][i];
-          if (rr < rows) otile[tix(rr, c)] = v * sc;
-        }
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4;
+      __syncthreads();
     }
-  if (ONE && threadIdx.x < ROWS) s_orow[threadIdx.x] = orow;
-  __syncthreads();
+  };
 
-  if (FC1 && g.act != nullptr) {
-    // Whole of K: apply the activation and write FC2 operand rows (f16 hi/lo
-    // groups, storage order of common.hpp) for this workgroup's codes.
-    // ReLU: code j = row n.  Interleaved SwiGLU: code j takes rows 2j (gate)
-    // and 2j + 1 (linear): g * sigmoid(alpha * g) * (u + beta).
-    const bool swiglu = g.act_swiglu != 0;
-    const int I = swiglu ? g.N / 2 : g.N;
-    const int jw = swiglu ? WGR / 2 : WGR;   // codes of this workgroup (whole 32-code blocks)
-    const int jbase = swiglu ? n0 / 2 : n0;
-    const int gtot = (int)(g.act_stride / 32);       // groups per operand row
-    for (int idx = threadIdx.x; idx < rows * (jw / 8); idx += NTH) {
-      const int rr = idx / (jw / 8);
-      const int gq = jbase / 8 + idx % (jw / 8);
-      if (gq >= gtot) continue;
-      const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
-      float a[8];
-      if (swiglu) {
-        const int t0 = 2 * (j0 - jbase);  // tile column of row 2*j0 (16 consecutive columns)
-        f32x4 v[4];
+  const int nmain = nst - nst % SPT;  // stages of one row block's walk in whole loop trips
 #pragma unroll
-        for (int m = 0; m < 4; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const float gv = v[c >> 1][2 * (c & 1)], uv = v[c >> 1][2 * (c & 1) + 1];
-          a[c] = j0 + c < I ? gv / (1.f + expf(-g.alpha * gv)) * (uv + g.beta) : 0.f;
-        }
-      } else {
-        const int t0 = j0 - jbase;
-        f32x4 v[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) a[c] = j0 + c < I ? fmaxf(v[c >> 2][c & 3], 0.f) : 0.f;
-      }
-      f16x8 hi, lo;
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code j0 + c sits at storage slot sl
-        _Float16 hh, ll;
-        split_f16(a[c], hh, ll);
-        hi[sl] = hh;
-        lo[sl] = ll;
-      }
-      uint8_t* dst = g.act + (long)(p0 + rr) * g.act_stride + (long)gq * 32;
-      *(f16x8*)dst = hi;
-      *(f16x8*)(dst + 16) = lo;
+  for (int rb = 0; rb < (ONE ? 1 : RB); ++rb) {
+    const int sb = rb * nst;
+    for (int s0 = 0; s0 < nmain; s0 += SPT) {
+      stage(sb + s0, std::integral_constant<int, 0>{});
+      if constexpr (SPT > 1) stage(sb + s0 + 1, std::integral_constant<int, 1>{});
     }
-  } else if ((g.N & 3) == 0) {
-    for (int idx = threadIdx.x; idx < rows * (WGR / 4); idx += NTH) {
-      const int rr = idx / (WGR / 4), c = 4 * (idx % (WGR / 4));
-      if (n0 + c < g.N)
-        *(f32x4*)(g.slot_out + ((long)split * g.S + s_orow[rr]) * g.N + n0 + c) = *(const f32x4*)(otile + tix(rr, c));
-    }
-  } else {
-    for (int idx = threadIdx.x; idx < rows * WGR; idx += NTH) {
-      const int rr = idx / WGR, c = idx % WGR;
-      if (n0 + c < g.N) g.slot_out[((long)split * g.S + s_orow[rr]) * g.N + n0 + c] = otile[tix(rr, c)];
-    }
+    if constexpr (SPT > 1)
+      if (nmain < nst) stage(sb + nmain, std::integral_constant<int, 0>{});
+    if constexpr (!ONE) close_block(rb);
+  }
+
+  if constexpr (ONE) {
+    // Output: the stage buffer is free after the last barrier.  Output row
+    // ids are read now (the stream is drained, so this load waits for
+    // nothing else).
+    if (threadIdx.x < ROWS) s_orow[threadIdx.x] = g.store_by_slot ? trow[threadIdx.x] : p0 + min((int)threadIdx.x, rows - 1);
+    emit(reinterpret_cast<float*>(lds), std::integral_constant<int, WGR>{}, n0, WGR, [&](int cb, int mt, int nt, int i) {
+      return (RB > 1 && cb < RB - 1) ? res[RB > 1 ? mt : 0][nt][i] : acc[mt][nt][i];
+    });
   }
 }
 
@@ -791,8 +876,7 @@ template <int BITS, bool FC1, bool ONE>
 hipError_t pick_mt(int mt, int rb, const GemmArgs& g, dim3 grid, size_t lds, hipStream_t st) {
   switch (mt) {
     case 1:
-      if constexpr (ONE)
-        if (rb == 2) return pick_scale<BITS, 1, FC1, ONE, 2>(g, grid, lds, st);
+      if (rb == 2) return pick_scale<BITS, 1, FC1, ONE, 2>(g, grid, lds, st);
       return pick_scale<BITS, 1, FC1, ONE, 1>(g, grid, lds, st);
     case 2: return pick_scale<BITS, 2, FC1, ONE, 1>(g, grid, lds, st);
     case 3: return pick_scale<BITS, 3, FC1, ONE, 1>(g, grid, lds, st);
@@ -811,19 +895,32 @@ hipError_t pick_mode(bool fc1, bool one, int mt, int rb, const GemmArgs& g, dim3
 
 // Row blocks per workgroup: two for one-stage launches at mt == 1 when
 // they tile N exactly.
+// Row blocks per workgroup: two for one-stage launches at mt == 1 when they
+// tile N exactly.
 static int stream_row_blocks(int mt, bool one, int N) { return one && mt == 1 && N % (2 * kWGRows) == 0 ? 2 : 1; }
 
 size_t stream_lds_bytes(int bits, int mt, bool one, int N) {
   const int item_codes = bits == 4 ? 256 : 128;
   const size_t stage = (size_t)16 * mt * stream_stage_items(mt, one) * item_codes * 4;
-  return std::max((one ? 1 : 2) * stage, (size_t)16 * mt * kWGRows * stream_row_blocks(mt, one, N) * 4);
+  // output tile: the workgroup's rows (one stage) or one row block
+  const int tile_rb = one ? stream_row_blocks(mt, one, N) : 1;
+  return std::max((one ? 1 : 2) * stage, (size_t)16 * mt * kWGRows * tile_rb * 4);
 }
 
-hipError_t launch_stream(int bits, int mt, bool one, int splits, const GemmArgs& g, int max_tiles, hipStream_t st) {
-  if (mt < 1 || mt > 4 || (one && g.nst != 1) || g.trows == nullptr) return hipErrorInvalidValue;
-  const int rb = stream_row_blocks(mt, one, g.N);
+hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, const GemmArgs& g_in, int max_tiles,
+                         hipStream_t st) {
+  if (mt < 1 || mt > 4 || (one && g_in.nst != 1) || g_in.trows == nullptr) return hipErrorInvalidValue;
+  GemmArgs g = g_in;
+  int rb = stream_row_blocks(mt, one, g.N);
+  if (!one) {
+    if (wg_rows == 0) wg_rows = kWGRows;
+    if (wg_rows % 64 != 0 || wg_rows > 2 * kWGRows || (wg_rows > kWGRows && mt != 1)) return hipErrorInvalidValue;
+    rb = wg_rows > kWGRows ? 2 : 1;
+  } else {
+    wg_rows = kWGRows * rb;
+  }
+  g.wg_rows = wg_rows;
   const size_t lds = stream_lds_bytes(bits, mt, one, g.N);
-  const int wg_rows = kWGRows * rb;
   const dim3 grid(splits, max_tiles, (g.N + wg_rows - 1) / wg_rows);
   const bool fc1 = g.a_f32 != 0;
   return bits == 4 ? pick_mode<4>(fc1, one, mt, rb, g, grid, lds, st) : pick_mode<8>(fc1, one, mt, rb, g, grid, lds, st);

@@ -189,6 +189,16 @@ void make_plan(const Dims& d, Plan* p) {
         }
       st.splits = (int)splits;
       st.nst = (int)(nst_total / splits);
+      // With one K range and one tile row of 16, size the workgroups so that
+      // the grid is one round of QMOE_STREAM_MIN_WORKGROUPS equal workgroups
+      // when that takes 256 to 512 rows each (whole 64-row pieces): every
+      // compute unit then streams the same share to the end.
+      st.wg_rows = 0;
+      const int64_t rbrows = 128 * QMOE_STREAM_NT;
+      if (p->mt == 1 && splits == 1 && units > QMOE_STREAM_MIN_WORKGROUPS) {
+        const int64_t r = round_up(ceil_div(d.E * N, QMOE_STREAM_MIN_WORKGROUPS), 64);
+        st.wg_rows = (int)std::min(r, 2 * rbrows);
+      }
     };
     shape(p->s1, d.H, d.F);
     shape(p->s2, d.I, d.H);

@@ -60,6 +60,7 @@ struct Plan {
     int stg = 2;         // 128-byte row items per stage (activation slice per LDS buffer)
     int nst = 1;         // stages per K range
     int splits = 1;      // K ranges (fp32 partials summed afterwards, in order)
+    int wg_rows = 0;     // double-buffered mode: weight rows per workgroup (0 = one row block of 256)
   } s1, s2;
   int splits2 = 1;       // FC2 partial sets the combine sums (1 off the stream path)
   size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path with K ranges)
