@@ -44,32 +44,52 @@ constexpr int kABuf = kTM * kTK * 4;  // activation slice: 128 rows x 256 bytes
 template <int BITS>
 struct TiledLayout {
   static constexpr int kBRow = kTK * BITS / 8;      // packed bytes per weight row per step
-  static constexpr int kBStride = kBRow + 16;       // LDS row stride (bank spread)
-  static constexpr int kBBuf = kTN * kBStride;
-  static constexpr int kSBuf = kTN * 2 * 4;         // up to two block scales per row per step
+  static constexpr int kGPR = kBRow / 16;           // 16-byte granules per weight row per step
+  static constexpr int kBBuf = kTN * kBRow;
+  static constexpr int kSBuf = 2 * kTN * 4;         // block scales of the step's two 32-code halves
   static constexpr int kStage = kABuf + kBBuf + kSBuf;
-  static constexpr int kLds = 2 * kStage;           // also holds the 64 x 256 fp32 epilogue tile
-  static_assert(kLds >= 64 * kTN * 4, "epilogue tile must fit");
+  static_assert(kStage >= 32 * kTN * 4, "a 32-row epilogue tile must fit one stage");
 };
 
-// Eight codes [32*j + 8*cg, +8) of a staged weight row as exact f16 (q - mid)
+// Granule swizzle of a staged weight row (bank spread of the fragment reads):
+// granule g of row n sits at g ^ swz(n).
+template <int BITS>
+__device__ __forceinline__ int bswz(int n) { return BITS == 4 ? (n >> 3) & 1 : (n >> 2) & 3; }
+
+// Eight codes [32*j + 8*cg, +8) of staged weight row n as exact f16 (q - mid)
 // in A-row storage order (see common.hpp).
 template <int BITS>
-__device__ __forceinline__ f16x8 tile_operand(const uint8_t* row, int j, int cg, const UnpackMasks& m) {
+__device__ __forceinline__ f16x8 tile_operand(const uint8_t* bbuf, int n, int j, int cg, const UnpackMasks& m) {
   if constexpr (BITS == 4) {
-    return unpack4(*(const uint32_t*)(row + 16 * j + 4 * cg), m);
+    return unpack4(*(const uint32_t*)(bbuf + n * 32 + ((j ^ bswz<4>(n)) * 16) + 4 * cg), m);
   } else {
-    const u32x2 v = *(const u32x2*)(row + 32 * j + 8 * cg);
+    const u32x2 v = *(const u32x2*)(bbuf + n * 64 + (((2 * j + (cg >> 1)) ^ bswz<8>(n)) * 16) + (cg & 1) * 8);
     return unpack8x2(v[0], v[1]);
   }
 }
 
+// Wait until at most n vector-memory operations of this wavefront are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 }  // namespace
+
+// Direct-to-LDS loads of one step: lane l of a load instruction fills the
+// 16-byte LDS slot base + 16 * l (4 bytes for the scale loads).
+#define QMOE_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
+#define QMOE_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <int BITS, int SCALE, int EPI>
 __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   using L = TiledLayout<BITS>;
-  extern __shared__ __align__(16) uint8_t lds[];
+  // Three stage buffers: a step's operands arrive by direct-to-LDS loads two
+  // steps ahead of their use.
+  __shared__ __align__(16) uint8_t st0[L::kStage];
+  __shared__ __align__(16) uint8_t st1[L::kStage];
+  __shared__ __align__(16) uint8_t st2[L::kStage];
   __shared__ long s_arow[kTM];
   __shared__ int s_orow[kTM];
 
@@ -94,7 +114,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int col = lane & 15, grp = lane >> 4;
   const long ebase = (long)e * g.N;
@@ -107,53 +127,44 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   }
   __syncthreads();
 
-  // Global -> register staging of one K step (loads are unconditional:
-  // rows past the tile or past N re-read a valid row).
-  constexpr int BPT = L::kBRow * kTN / 16 / kTThreads;  // 16-byte weight pieces per thread
-  u32x4 ra[4], rb[BPT];
-  float rs[2];
-  const int nk = g.K / kTK;
-  const uint8_t* bsrc[BPT];
+  // Per-lane sources of the step's direct-to-LDS loads (rows past the tile
+  // or past N re-read a valid row; every wavefront issues the same count).
+  //  A: wavefront w fills rows 16w .. 16w + 15, four rows an instruction; the
+  //     slot of row r holding piece q is q ^ (r & 15);
+  //  B: the step's weight rows, GPR granules a row, granule g of row n in
+  //     slot g ^ swz(n);
+  //  S (block scales): wavefronts 0-3 the first 32-code half, 4-7 the second.
+  constexpr int BPW = L::kGPR * kTN / 64 / kTWaves;  // weight load instructions per wavefront
+  constexpr int NV = 4 + BPW + (SCALE == SC_BLOCK ? 1 : 0);
+  const uint8_t* asrc[4];
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    const int idx = tid + i * kTThreads;
-    const int r = idx / (L::kBRow / 16), q = idx % (L::kBRow / 16);
-    bsrc[i] = g.wq + (ebase + min(n0 + r, g.N - 1)) * (long)g.kb + q * 16;
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 4 + (lane >> 4);
+    asrc[i] = g.a + s_arow[r] + (((lane & 15) ^ (r & 15)) * 16);
   }
-  const float* ssrc = g.ws + (ebase + min(n0 + (tid & (kTN - 1)), g.N - 1)) * (long)g.nblk;
-  auto load = [&](int kt) {
+  const uint8_t* bsrc[BPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + i * kTThreads;
-      const int r = idx >> 4, q = idx & 15;
-      ra[i] = *(const u32x4*)(g.a + s_arow[r] + (long)kt * (kTK * 4) + q * 16);
-    }
+  for (int i = 0; i < BPW; ++i) {
+    const int G = (wave * BPW + i) * 64 + lane;
+    const int n = G / L::kGPR, gs = G % L::kGPR;
+    bsrc[i] = g.wq + (ebase + min(n0 + n, g.N - 1)) * (long)g.kb + ((gs ^ bswz<BITS>(n)) * 16);
+  }
+  const float* ssrc = g.ws + (ebase + min(n0 + (wave & 3) * 64 + lane, g.N - 1)) * (long)g.nblk;
+  const int shalf = (wave >> 2) * 32;
+  const int nk = g.K / kTK;
+  auto issue = [&](uint8_t* sb, int kt) {
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) rb[i] = *(const u32x4*)(bsrc[i] + (long)kt * L::kBRow);
-    if constexpr (SCALE == SC_BLOCK) {
-      // scales of the blocks holding the step's two 32-code halves (the same
-      // block unless bs == 32); no branches, so every wait stays exact
-      rs[0] = ssrc[(kt * kTK) / g.bs];
-      rs[1] = ssrc[(kt * kTK + 32) / g.bs];
-    }
-  };
-  auto store = [&](int buf) {
-    uint8_t* base = lds + buf * L::kStage;
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(asrc[i] + (long)kt * (kTK * 4)), QMOE_LOCAL(sb + (wave * 4 + i) * 1024),
+                                       16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + i * kTThreads;
-      const int r = idx >> 4, q = idx & 15;
-      *(u32x4*)(base + r * 256 + ((q ^ (r & 15)) * 16)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int idx = tid + i * kTThreads;
-      const int r = idx / (L::kBRow / 16), q = idx % (L::kBRow / 16);
-      *(u32x4*)(base + kABuf + r * L::kBStride + q * 16) = rb[i];
-    }
-    if constexpr (SCALE == SC_BLOCK) {
-      if (tid < kTN) *(float2*)(base + kABuf + L::kBBuf + tid * 8) = float2{rs[0], rs[1]};
-    }
+    for (int i = 0; i < BPW; ++i)
+      __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(bsrc[i] + (long)kt * L::kBRow),
+                                       QMOE_LOCAL(sb + kABuf + (wave * BPW + i) * 1024), 16, 0, 0);
+    if constexpr (SCALE == SC_BLOCK)
+      __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(ssrc + (kt * kTK + shalf) / g.bs),
+                                       QMOE_LOCAL(sb + kABuf + L::kBBuf + (wave >> 2) * (kTN * 4) + (wave & 3) * 256),
+                                       4, 0, 0);
   };
 
   f32x4 acc[4][4];
@@ -169,33 +180,19 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   const UnpackMasks um = unpack_masks();
   const int cg = code_group_of_lane<BITS>(grp);
 
-  // L2 prefetch three steps ahead: every thread touches one 128-byte line of
-  // a coming step (waves 0-3 the activation slice, 2 lines a row; waves 4-7
-  // the weight rows) with a dword load whose value is consumed two steps
-  // later.  Loads complete in issue order, so a step's own loads (issued
-  // before its prefetch) never wait for that prefetch.
-  const uint8_t* pfbase = tid < 256 ? g.a + s_arow[tid >> 1] + (tid & 1) * 128
-                                    : g.wq + (ebase + min(n0 + (tid - 256), g.N - 1)) * (long)g.kb;
-  const int pfstep = tid < 256 ? kTK * 4 : L::kBRow;
-  auto prefetch = [&](int kt) -> uint32_t {
-    return *(const uint32_t*)(pfbase + (long)min(kt, nk - 1) * pfstep);
-  };
-  uint32_t pf[2];
-  pf[0] = prefetch(1);
-  pf[1] = prefetch(2);
-
-  load(0);
-  store(0);
-  __syncthreads();
-  // One K step; P = kt & 1 at compile time (ring of prefetch values).
-  auto kstep = [&](int kt, auto pc) {
-    constexpr int P = decltype(pc)::value;
-    const uint8_t* base = lds + P * L::kStage;
-    asm volatile("" ::"v"(pf[P]));  // step kt + 1 is in L2
-    load(min(kt + 1, nk - 1));
-    __builtin_amdgcn_sched_barrier(0);  // the step's own loads are issued before its prefetch
-    pf[P] = prefetch(kt + 3);
+  // Step kt reads stage buffer kt % 3.  Its loads were issued two steps
+  // earlier: wait for them (the next step's may stay in flight), then the
+  // barrier makes every wavefront's loads visible and frees buffer
+  // (kt + 2) % 3 (last read in step kt - 1) for the loads of step kt + 2.
+  auto kstep = [&](int kt, uint8_t* base, uint8_t* next2) {
+    wait_vm<NV>();
+    __builtin_amdgcn_s_barrier();
+    // nothing moves across the barrier: reads of buffer kt % 3 stay after it,
+    // the refill of buffer (kt + 2) % 3 stays after every wavefront's reads
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    issue(next2, min(kt + 2, nk - 1));
+    const uint8_t* bbuf = base + kABuf;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       // weight fragments of the step, then the four row subtiles with their
@@ -203,8 +200,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
       // parts, so the two instructions on one accumulator are 4 apart
       f16x8 bf[4], ah[2], al[2];
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns)
-        bf[ns] = tile_operand<BITS>(base + kABuf + (wn * 64 + ns * 16 + col) * L::kBStride, j, cg, um);
+      for (int ns = 0; ns < 4; ++ns) bf[ns] = tile_operand<BITS>(bbuf, wn * 64 + ns * 16 + col, j, cg, um);
       auto aload = [&](int ms, f16x8& h, f16x8& l) {
         const uint8_t* arow = base + (wm * 64 + ms * 16 + col) * 256;  // row & 15 == col
         h = *(const f16x8*)(arow + (((8 * j + 2 * grp) ^ col) * 16));
@@ -226,10 +222,10 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
       if constexpr (SCALE == SC_BLOCK) {
         const int ks = 2 * kt + j;  // 32-code step
         if (((ks + 1) * 32) % g.bs == 0) {
-          const float* srow = (const float*)(base + kABuf + L::kBBuf);
+          const float* srow = (const float*)(base + kABuf + L::kBBuf) + j * kTN;
 #pragma unroll
           for (int ns = 0; ns < 4; ++ns) {
-            const float sc = srow[(wn * 64 + ns * 16 + col) * 2 + j];
+            const float sc = srow[wn * 64 + ns * 16 + col];
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) {
               acc[ms][ns] += blk[ms][ns] * sc;
@@ -239,18 +235,20 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
         }
       }
     }
-    // The other buffer was last read in the previous step, which every
-    // wavefront finished before the last barrier.
-    if (kt + 1 < nk) store(P ^ 1);
-    __syncthreads();
   };
+  issue(st0, 0);
+  issue(st1, min(1, nk - 1));
   int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    kstep(kt, std::integral_constant<int, 0>{});
-    kstep(kt + 1, std::integral_constant<int, 1>{});
+  for (; kt + 2 < nk; kt += 3) {
+    kstep(kt, st0, st2);
+    kstep(kt + 1, st1, st0);
+    kstep(kt + 2, st2, st1);
   }
-  if (kt < nk) kstep(kt, std::integral_constant<int, 0>{});
-  asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
+  if (kt < nk) kstep(kt, st0, st2);
+  if (kt + 1 < nk) kstep(kt + 1, st1, st0);
+  // every load has landed and every wavefront is done with the stages
+  wait_vm<0>();
+  __syncthreads();
 
   if constexpr (SCALE == SC_COL) {
 #pragma unroll
@@ -261,27 +259,31 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     }
   }
 
-  // Epilogue in two rounds of 64 rows: the wavefronts of that row half put
-  // their results in an fp32 LDS tile [64][256] (columns XOR-swizzled by
+  // Epilogue in four rounds of 32 rows: the wavefronts holding those rows put
+  // them in an fp32 LDS tile [32][256] (columns XOR-swizzled by
   // 16 * ((row / 4) % 4)), then the workgroup writes whole rows.
-  float* otile = reinterpret_cast<float*>(lds);
+  float* otile = reinterpret_cast<float*>(st0);
   auto tix = [](int rr, int c) { return rr * kTN + (c ^ (16 * ((rr >> 2) & 3))); };
-  for (int half = 0; half < 2; ++half) {
-    if (wm == half) {
+  for (int round = 0; round < 4; ++round) {
+    if (wm == round >> 1) {
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
+      for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) otile[tix(ms * 16 + 4 * grp + i, wn * 64 + ns * 16 + col)] = acc[ms][ns][i];
+          for (int i = 0; i < 4; ++i) {
+            const int ms = (round & 1) * 2 + m2;
+            otile[tix(m2 * 16 + 4 * grp + i, wn * 64 + ns * 16 + col)] = acc[ms][ns][i];
+          }
     }
     __syncthreads();
-    const int rlim = min(64, rows - half * 64);  // valid rows of this half
+    const int r0 = round * 32;
+    const int rlim = min(32, rows - r0);  // valid rows of this round
     if constexpr (EPI == EPI_STORE) {
       for (int idx = tid; idx < rlim * (kTN / 4); idx += kTThreads) {
         const int rr = idx / (kTN / 4), c = 4 * (idx % (kTN / 4));
         if (n0 + c < g.N)
-          *(f32x4*)(g.slot_out + (long)s_orow[half * 64 + rr] * g.N + n0 + c) = *(const f32x4*)(otile + tix(rr, c));
+          *(f32x4*)(g.slot_out + (long)s_orow[r0 + rr] * g.N + n0 + c) = *(const f32x4*)(otile + tix(rr, c));
       }
     } else {
       // FC2 operand rows for this tile's codes: ReLU code j = column n;
@@ -324,7 +326,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
           hi[sl] = hh;
           lo[sl] = ll;
         }
-        uint8_t* dst = g.act + (long)(p0 + half * 64 + rr) * g.act_stride + (long)gq * 32;
+        uint8_t* dst = g.act + (long)(p0 + r0 + rr) * g.act_stride + (long)gq * 32;
         *(f16x8*)dst = hi;
         *(f16x8*)(dst + 16) = lo;
       }
@@ -333,19 +335,15 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   }
 }
 
+#undef QMOE_GLOBAL
+#undef QMOE_LOCAL
+
 namespace {
 
 template <int BITS, int SCALE, int EPI>
 hipError_t go_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
   auto kern = qmoe_tiled<BITS, SCALE, EPI>;
-  constexpr size_t lds = TiledLayout<BITS>::kLds;
-  static std::atomic<bool> granted{false};
-  if (lds > 64 * 1024 && !granted.load()) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    granted.store(true);
-  }
-  hipLaunchKernelGGL(kern, dim3(max_tiles * ntn), dim3(kTThreads), lds, st, g, ntn);
+  hipLaunchKernelGGL(kern, dim3(max_tiles * ntn), dim3(kTThreads), 0, st, g, ntn);
   return hipGetLastError();
 }
 
