@@ -13,17 +13,17 @@
 // their slot id, so the combine gathers them without atomics.
 //
 // Work decomposition: a workgroup of 8 wavefronts computes a 128 x 256 tile
-// (2 x 4 wavefronts of 64 x 64).  Each 64-code K step stages the tile's
-// activation slice (f16 hi/lo, 32 KB) and packed weight slice (8 or 16 KB)
-// plus its block scales in LDS, double buffered: the next step's global loads
-// are in flight while the current step runs on the matrix cores.  Weights
-// are unpacked from LDS straight into matrix-core operands (exact f16 q - mid)
-// and each fragment feeds 8 instructions (4 row subtiles x hi/lo).
+// (2 x 4 wavefronts of 64 x 64).  Each 64-code K step's operands - the
+// tile's activation slice (f16 hi/lo, 32 KB), packed weight slice (8 or
+// 16 KB) and block scales - arrive in one of three LDS stage buffers by
+// direct-to-LDS loads issued two steps ahead, so two steps of loads are in
+// flight while a step runs on the matrix cores.  Weights are unpacked from
+// LDS straight into matrix-core operands (exact f16 q - mid) and each
+// fragment feeds 8 instructions (4 row subtiles x hi/lo).
 // Workgroups are ordered so that the ones resident on an XCD at the same time
 // cover 8 row tiles x 4 column tiles: both operands are reused from that
 // XCD's L2.
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
