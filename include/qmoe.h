@@ -136,7 +136,10 @@ qmoe_status qmoe_validate(const qmoe_tensor* input, const qmoe_tensor* router_pr
 
 /* Bytes of device workspace qmoe_forward needs for these shapes (validates
  * first).  *bytes receives the size; it is 0 when T == 0.  With I == 0 only
- * the (small) routing part is needed. */
+ * the (small) routing part is needed.  The size depends on the kernel plan,
+ * which the environment variable QMOE_STREAM_SINGLE_STAGE_MAX_SPLITS (most K
+ * ranges of a single-stage streaming GEMM, default 16) can change: query the
+ * size under the same environment as the forward call. */
 qmoe_status qmoe_workspace_size(const qmoe_tensor* input, const qmoe_tensor* router_probs,
                                 const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_scales,
                                 const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_scales,

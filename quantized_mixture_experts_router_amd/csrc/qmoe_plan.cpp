@@ -7,6 +7,7 @@
 #include "qmoe_plan.h"
 
 #include <algorithm>
+#include <cstdlib>
 
 // Workgroups the streaming kernels aim for before splitting K (two per
 // compute unit on 256 compute units).
@@ -32,6 +33,18 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // The streaming kernel needs whole 128-byte row items and scale blocks of at
 // least one 32-code matrix step.
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Most K ranges a single-stage streaming launch may take; the environment
+// variable QMOE_STREAM_SINGLE_STAGE_MAX_SPLITS (a non-negative integer)
+// overrides it, e.g. 0 to run every streaming GEMM double-buffered.
+int64_t max_one_splits() {
+  if (const char* v = std::getenv("QMOE_STREAM_SINGLE_STAGE_MAX_SPLITS")) {
+    char* end = nullptr;
+    const long x = std::strtol(v, &end, 10);
+    if (end != v && *end == 0 && x >= 0) return x;
+  }
+  return QMOE_STREAM_MAX_ONE_SPLITS;
+}
 
 bool rank_ok(const qmoe_tensor* t, int r) { return t->rank == r; }
 
@@ -167,7 +180,7 @@ void make_plan(const Dims& d, Plan* p) {
       // QMOE_STREAM_MAX_ONE_SPLITS ranges; else double-buffered stages over
       // the whole of K, split only as far as needed to fill the chip.
       const int64_t one_codes = stream_stage_items(p->mt, true) * item_codes;
-      if (fits(one_codes) && K / one_codes <= QMOE_STREAM_MAX_ONE_SPLITS) {
+      if (fits(one_codes) && K / one_codes <= max_one_splits()) {
         st.on = true;
         st.one = true;
         st.stg = stream_stage_items(p->mt, true);

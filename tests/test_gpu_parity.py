@@ -280,3 +280,30 @@ def test_full_size_workload(torch, name):
     # determinism at full size
     res2 = run_gpu(a, attrs, torch, debug=False)
     np.testing.assert_array_equal(res2["out"], res["out"])
+
+
+def test_double_buffered_streaming(torch):
+    """The streaming kernels' double-buffered mode (whole-K walks, several row
+    blocks per workgroup, sized workgroups, fused activation), forced for
+    every streaming GEMM: the decode workload in full and small shapes."""
+    key = "QMOE_STREAM_SINGLE_STAGE_MAX_SPLITS"
+    old = os.environ.get(key)
+    os.environ[key] = "0"
+    try:
+        w = W.WORKLOADS["decode"]
+        say("[case] decode, double-buffered streaming: generating")
+        _full_check(w, W.generate(w), torch, "decode double-buffered")
+        rng = np.random.default_rng(78)
+        for bits in (4, 8):
+            for bs, act in ((0, "relu"), (32, "swiglu"), (64, "swiglu")):
+                for (T, H, E, I, k) in [(5, 128, 3, 64, 2), (16, 512, 8, 256, 2), (33, 256, 6, 128, 6),
+                                        (64, 256, 4, 512, 2)]:
+                    shape = (T,) if T % 2 else (2, T // 2)
+                    wc, a = W.random_case(rng, tokens_shape=shape, hidden=H, experts=E, inter=I, k=k,
+                                          bits=bits, block_size=bs, activation=act)
+                    _full_check(wc, a, torch, f"double-buffered bits{bits} bs{bs} {act} T{T} H{H} E{E} I{I}")
+    finally:
+        if old is None:
+            del os.environ[key]
+        else:
+            os.environ[key] = old
