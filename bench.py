@@ -13,8 +13,10 @@ The roofline object describes the dominant kernel (FC1 or FC2, whichever is
 slower), timed with HIP events recorded on the launch stream around that
 kernel over K further steps; its algorithmic bytes and FLOPs are counted from
 the shapes (packed weights and scales of the experts that receive a slot,
-activations in and out).  The CPU baseline times the float64 oracle on the
-host cores over a bounded sample of the same workload.
+activations in and out).  latency_ms gives per-call median / p10 / p90 with
+warm caches and with L2 and the Infinity Cache flushed before every call.
+The CPU baseline times the float64 oracle on the host cores over a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -43,6 +45,7 @@ def _args():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stage-timing", action="store_true")
+    ap.add_argument("--no-latency", action="store_true", help="skip the per-call warm/cold latency percentiles")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -132,8 +135,41 @@ def _sha(path):
 
 KERNEL_SRC = {
     "qmoe_stream": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "stream.hip"),
+    "qmoe_tiled": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "tiled.hip"),
     "qmoe_gemm": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gemm.hip"),
 }
+
+
+def gemm_kernel(w):
+    """Which grouped-GEMM kernel the library runs for this workload (the
+    library's plan: weight streaming up to 64 tokens, the LDS-tiled GEMM for
+    64-multiple H and I with column-wise or >= 32-code scale blocks, else the
+    register-tiled one)."""
+    if w.tokens <= 64:
+        return "qmoe_stream"
+    tiled = w.hidden % 64 == 0 and w.inter % 64 == 0 and (w.block_size == 0 or w.block_size >= 32)
+    return "qmoe_tiled" if tiled else "qmoe_gemm"
+
+
+def call_latency(step, n, evict=None):
+    """Per-call latency (ms) of n calls timed with events on the launch stream:
+    median, p10, p90.  With evict (a large device buffer), it is rewritten
+    before every call so that no operand is left in L2 or the Infinity Cache."""
+    import numpy as np
+    import torch
+    ts = []
+    for _ in range(n):
+        if evict is not None:
+            evict.add_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    q = np.percentile(np.array(ts), [50, 10, 90])
+    return dict(median=round(float(q[0]), 5), p10=round(float(q[1]), 5), p90=round(float(q[2]), 5), calls=n)
 
 
 def traffic_for(key, kernel):
@@ -220,13 +256,22 @@ def main():
         key = "fc1" if stages["fc1"] >= stages["fc2"] else "fc2"
         work = fc1_work if key == "fc1" else fc2_work
         roofline = roofline_for(work, stages[key])
-        # every expert's rows fit one 64-row tile: the weight-streaming kernel
-        kernel = "qmoe_stream" if w.tokens <= 64 else "qmoe_gemm"
+        kernel = gemm_kernel(w)
         roofline["kernel"] = f"{kernel} ({key.upper()})"
         roofline["avg_ms"] = round(stages[key], 5)
         roofline["algorithmic_bytes"] = int(work["bytes"])
         roofline["algorithmic_flops"] = work["flops"]
         roofline["traffic"] = traffic_for(f"{args.workload}:{key}", kernel)
+
+    # Per-call latency outside the throughput loop: warm (operands may sit in
+    # L2 / the Infinity Cache from the previous call) and cold (a 1 GiB
+    # buffer rewritten before every call).
+    latency = None
+    if not args.no_latency:
+        n = max(10, min(args.steps, 50))
+        evict = torch.empty(1 << 28, dtype=torch.float32, device="cuda").zero_()
+        latency = dict(warm=call_latency(step, n), cold=call_latency(step, n, evict))
+        del evict
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -254,6 +299,7 @@ def main():
         "layer_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "stage_ms": {k: round(v, 5) for k, v in stages.items()} if stages else None,
         "roofline": roofline,
+        "latency_ms": latency,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
