@@ -61,7 +61,15 @@ typedef enum {
   QMOE_ERR_ALIGN = 8        /* a device pointer is not 16-byte aligned        */
 } qmoe_status;
 
-typedef enum { QMOE_F32 = 1, QMOE_U8 = 2 } qmoe_dtype;
+typedef enum {
+  QMOE_F32 = 1,
+  QMOE_U8 = 2,
+  QMOE_I32 = 3,
+  QMOE_I64 = 4,
+  QMOE_F16 = 5,  /* accepted by GroupedMatMul's type list; not implemented */
+  QMOE_BF16 = 6, /* accepted by GroupedMatMul's type list; not implemented */
+  QMOE_F64 = 7   /* accepted by GroupedMatMul's type list; not implemented */
+} qmoe_dtype;
 
 typedef enum { QMOE_ACT_RELU = 0, QMOE_ACT_SWIGLU = 1 } qmoe_activation;
 
@@ -165,6 +173,50 @@ qmoe_status qmoe_forward_debug(const qmoe_tensor* input, const qmoe_tensor* rout
                                const qmoe_attrs* attrs, const qmoe_tensor* output,
                                void* workspace, size_t workspace_bytes, void* stream,
                                const qmoe_debug* debug);
+
+/* ------------------------------------------------------------------------
+ * GroupedMatMul (ONNX operator page "GroupedMatMul - 29": Summary, Inputs,
+ * Outputs, Type Constraints), float32 weights:
+ *
+ *   output[m, i, :] = input[m, :] @ weights[g, :, :]  (+ bias[g, :])
+ *   g = group_indices[m, i]
+ *
+ * input [M, K], weights [G, K, N], group_indices [M, S] (int32 or int64),
+ * optional bias [G, N] (NULL = no bias), output [M, S, N].  input, weights,
+ * bias and output are QMOE_F32 (QMOE_F16 / QMOE_BF16 / QMOE_F64 are in the
+ * page's type list and return QMOE_ERR_UNSUPPORTED; any other code is
+ * QMOE_ERR_DTYPE); group_indices is QMOE_I32 or QMOE_I64 (else
+ * QMOE_ERR_DTYPE).  Ranks or extents that disagree: QMOE_ERR_SHAPE.
+ * Limits (QMOE_ERR_UNSUPPORTED beyond them): G <= 1023, M * S < 2^30,
+ * K < 2^30, N < 2^30, and (ceil(M * S / 64) + G + 1) * ceil(N / 128)
+ * < 2^31 (one workgroup per 64-row, 128-column output tile).
+ *
+ * Indices outside [0, G) are invalid input, for which the page defines no
+ * result; this library writes zeros to those output rows and reads no weight
+ * or bias for them (negative values do not count back from G).
+ *
+ * Products and sums are float32: the matrix cores (v_mfma_f32_16x16x4_f32)
+ * add four K terms per instruction into a float32 accumulator, in K order
+ * from 0; the bias is added last.
+ * Conventions (ownership, streams, status, no allocation) as above.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace qmoe_grouped_matmul needs (validates first;
+ * output may be NULL to skip its check).  0 when M * S * N == 0. */
+qmoe_status qmoe_grouped_matmul_workspace_size(const qmoe_tensor* input, const qmoe_tensor* weights,
+                                               const qmoe_tensor* group_indices, const qmoe_tensor* bias,
+                                               const qmoe_tensor* output, size_t* bytes);
+
+/* Enqueue GroupedMatMul on stream (a hipStream_t; NULL = the null stream).
+ * Device pointers: float tensors 4-byte aligned, group_indices aligned to its
+ * element size (QMOE_ERR_ALIGN otherwise); 16-byte aligned input and weights
+ * with K and N multiples of 4 take the vector-load path.  workspace: at least
+ * qmoe_grouped_matmul_workspace_size bytes, 256-byte aligned, owned by this
+ * call until the stream reaches it.  The output must not alias an input.
+ * With M * S * N == 0 nothing is enqueued. */
+qmoe_status qmoe_grouped_matmul(const qmoe_tensor* input, const qmoe_tensor* weights,
+                                const qmoe_tensor* group_indices, const qmoe_tensor* bias,
+                                const qmoe_tensor* output, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* qmoe_status_string(qmoe_status s);

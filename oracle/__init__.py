@@ -14,4 +14,4 @@ from .qmoe_oracle import (  # noqa: F401
     ContractError, validate, route, expert_permutation, dequantize, activation,
     qmoe, qmoe_dense, qmoe_tokens, expert_ffn,
 )
-from .grouped_matmul import grouped_matmul  # noqa: F401
+from .grouped_matmul import grouped_matmul, grouped_matmul_rows  # noqa: F401

@@ -5,11 +5,13 @@ kernels behind the C ABI of include/qmoe.h.  PyTorch supplies device memory
 and the current stream.  The functions keep the C names:
 
     qmoe_abi_version, qmoe_attrs_default, qmoe_validate, qmoe_workspace_size,
-    qmoe_forward, qmoe_forward_debug, qmoe_status_string
+    qmoe_forward, qmoe_forward_debug, qmoe_status_string,
+    qmoe_grouped_matmul_workspace_size, qmoe_grouped_matmul
 
-plus ``forward`` (allocates output and workspace with torch, then calls
-qmoe_forward) for convenience.  The library is loaded on first use; a missing
-build raises immediately, there is no fallback.
+plus ``forward`` and ``grouped_matmul`` (allocate output and workspace with
+torch, then call qmoe_forward / qmoe_grouped_matmul) for convenience.  The
+library is loaded on first use; a missing build raises immediately, there is
+no fallback.
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmoe.so")
 
-QMOE_F32, QMOE_U8 = 1, 2
+QMOE_F32, QMOE_U8, QMOE_I32, QMOE_I64, QMOE_F16, QMOE_BF16, QMOE_F64 = 1, 2, 3, 4, 5, 6, 7
 QMOE_ACT = {"relu": 0, "swiglu": 1}
 QMOE_ROUTING = {"qmoe": 0, "moe": 1}
 STATUS = {0: "OK", 1: "NULL", 2: "SHAPE", 3: "ATTR", 4: "UNSUPPORTED", 5: "WORKSPACE", 6: "HIP",
@@ -83,6 +85,10 @@ def _lib():
         lib.qmoe_forward_debug.argtypes = [T, T, T, T, T, T, A, T, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p, ctypes.POINTER(QmoeDebug)]
         lib.qmoe_forward_debug.restype = ctypes.c_int
+        lib.qmoe_grouped_matmul_workspace_size.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_size_t)]
+        lib.qmoe_grouped_matmul_workspace_size.restype = ctypes.c_int
+        lib.qmoe_grouped_matmul.argtypes = [T, T, T, T, T, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.qmoe_grouped_matmul.restype = ctypes.c_int
         lib.qmoe_status_string.argtypes = [ctypes.c_int]
         lib.qmoe_status_string.restype = ctypes.c_char_p
         _lib_handle = lib
@@ -99,7 +105,8 @@ def describe(t, data: bool = True) -> QmoeTensor:
     """qmoe_tensor for a torch tensor or numpy array (shape, dtype, pointer)."""
     shape = tuple(t.shape)  # ranks above 3 pass through so the library rejects them
     name = str(t.dtype).replace("torch.", "")
-    code = {"float32": QMOE_F32, "uint8": QMOE_U8}.get(name, 0)
+    code = {"float32": QMOE_F32, "uint8": QMOE_U8, "int32": QMOE_I32, "int64": QMOE_I64, "float16": QMOE_F16,
+            "bfloat16": QMOE_BF16, "float64": QMOE_F64}.get(name, 0)
     ptr = None
     if data and hasattr(t, "data_ptr"):
         if not t.is_contiguous():
@@ -219,4 +226,48 @@ def forward(input, router_probs, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None, stream=
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=input.device)
     qmoe_forward(input, router_probs, fc1_w, fc1_s, fc2_w, fc2_s, attrs, output, workspace, stream, debug)
+    return output
+
+
+def _ref(t, data):
+    return ctypes.byref(describe(t, data)) if t is not None else None
+
+
+def qmoe_grouped_matmul_workspace_size(input, weights, group_indices, bias=None, output=None) -> int:
+    """Workspace bytes of qmoe_grouped_matmul.  Arrays may live anywhere."""
+    n = ctypes.c_size_t(0)
+    st = _lib().qmoe_grouped_matmul_workspace_size(_ref(input, False), _ref(weights, False),
+                                                   _ref(group_indices, False), _ref(bias, False),
+                                                   _ref(output, False), ctypes.byref(n))
+    if st != 0:
+        raise QmoeError(st, "qmoe_grouped_matmul_workspace_size")
+    return int(n.value)
+
+
+def qmoe_grouped_matmul(input, weights, group_indices, bias, output, workspace, stream=None) -> None:
+    """Enqueue GroupedMatMul on ``stream`` (default: torch's current stream).
+
+    Contiguous device tensors; ``bias`` may be None; ``workspace`` a uint8
+    device tensor of at least qmoe_grouped_matmul_workspace_size bytes (or
+    None when that size is 0).
+    """
+    wptr = workspace.data_ptr() if workspace is not None and workspace.numel() > 0 else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib().qmoe_grouped_matmul(_ref(input, True), _ref(weights, True), _ref(group_indices, True),
+                                    _ref(bias, True), _ref(output, True), ctypes.c_void_p(wptr),
+                                    ctypes.c_size_t(wbytes), _stream_handle(stream))
+    if st != 0:
+        raise QmoeError(st, "qmoe_grouped_matmul")
+
+
+def grouped_matmul(input, weights, group_indices, bias=None, stream=None, workspace=None, output=None):
+    """Allocate output [M, S, N] (and workspace unless given) with torch, then qmoe_grouped_matmul."""
+    import torch
+    if output is None:
+        output = torch.empty((input.shape[0], group_indices.shape[1], weights.shape[2]), dtype=input.dtype,
+                             device=input.device)
+    need = qmoe_grouped_matmul_workspace_size(input, weights, group_indices, bias, output)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=input.device)
+    qmoe_grouped_matmul(input, weights, group_indices, bias, output, workspace, stream)
     return output

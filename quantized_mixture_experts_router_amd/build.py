@@ -19,10 +19,12 @@ LIB = os.path.join(PKG, "libqmoe.so")
 SOURCES = [
     "qmoe_plan.cpp",
     "qmoe_api.cpp",
+    "qmoe_gmm.cpp",
     "kernels/route.hip",
     "kernels/gemm.hip",
     "kernels/stream.hip",
     "kernels/tiled.hip",
+    "kernels/gmm.hip",
 ]
 
 ARCH = os.environ.get("QMOE_OFFLOAD_ARCH", "gfx950")

@@ -85,6 +85,16 @@ hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, i
 hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, int splits, float* out,
                           hipStream_t st);
 
+// GroupedMatMul (see gmm.hip).  Index conversion: out[j] = idx[j] when in
+// [0, G), else G.  Tile GEMM over the permutation of G + 1 groups with
+// gmm_tile_rows()-row tiles; tiles of group G write zero rows.  vec: K, N
+// multiples of 4 and x, w 16-byte aligned.
+int gmm_tile_rows();
+hipError_t launch_gmm_index(const void* idx, bool idx64, long n, int G, int* out, hipStream_t st);
+hipError_t launch_gmm_f32(const float* x, const float* w, const float* bias, const int* perm, const int* tiles,
+                          const int* ntiles, int max_tiles, int S, int K, int N, int G, float* out, bool vec,
+                          hipStream_t st);
+
 hipError_t launch_fill_zero(float* out, long n, hipStream_t st);
 
 hipError_t launch_copy_i32(const int* src, int* dst, long n, hipStream_t st);

@@ -1,0 +1,148 @@
+// C ABI of GroupedMatMul (ONNX operator page "GroupedMatMul - 29"; declared
+// in include/qmoe.h): contract check, workspace plan and enqueue.
+//
+// qmoe_grouped_matmul enqueues, on the caller's stream:
+//   index conversion (invalid indices -> group G) -> permutation (histogram,
+//   scan, stable scatter over G + 1 groups, 64-row tiles) -> tile GEMM
+// with every intermediate in the caller's workspace.
+#include <hip/hip_runtime.h>
+
+#include "kernels/launch.h"
+#include "qmoe.h"
+
+using namespace qmoe;
+
+namespace {
+
+bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+constexpr int64_t kChunk = 1024;       // slots per permutation block
+constexpr int64_t kMaxGroups = 1023;   // G + 1 buckets, one scan thread each
+
+struct GmmPlan {
+  int64_t M = 0, K = 0, G = 0, N = 0, S = 0, R = 0;  // R = M * S rows
+  int64_t bm = 0, max_tiles = 0, nchunks = 0, nblk = 0;
+  bool idx64 = false, has_bias = false;
+  size_t off_idx = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_tiles = 0, off_ntiles = 0, off_hist = 0;
+  size_t bytes = 0;
+};
+
+bool float_code(int32_t dt) { return dt == QMOE_F32 || dt == QMOE_F16 || dt == QMOE_BF16 || dt == QMOE_F64; }
+
+qmoe_status check(const qmoe_tensor* input, const qmoe_tensor* weights, const qmoe_tensor* idx,
+                  const qmoe_tensor* bias, const qmoe_tensor* output, GmmPlan* p) {
+  if (!input || !weights || !idx) return QMOE_ERR_NULL;
+  if (input->rank != 2 || weights->rank != 3 || idx->rank != 2) return QMOE_ERR_SHAPE;
+  if (bias && bias->rank != 2) return QMOE_ERR_SHAPE;
+  if (output && output->rank != 3) return QMOE_ERR_SHAPE;
+  // one floating type T for input, weights, bias and output (Type Constraints)
+  const int32_t T = input->dtype;
+  if (!float_code(T)) return QMOE_ERR_DTYPE;
+  if (weights->dtype != T || (bias && bias->dtype != T) || (output && output->dtype != T)) return QMOE_ERR_DTYPE;
+  if (idx->dtype != QMOE_I32 && idx->dtype != QMOE_I64) return QMOE_ERR_DTYPE;
+  const qmoe_tensor* ts[] = {input, weights, idx, bias, output};
+  for (const qmoe_tensor* t : ts)
+    if (t)
+      for (int i = 0; i < t->rank; ++i)
+        if (t->dims[i] < 0) return QMOE_ERR_SHAPE;
+  p->M = input->dims[0];
+  p->K = input->dims[1];
+  p->G = weights->dims[0];
+  p->N = weights->dims[2];
+  p->S = idx->dims[1];
+  if (weights->dims[1] != p->K || idx->dims[0] != p->M) return QMOE_ERR_SHAPE;
+  if (bias && (bias->dims[0] != p->G || bias->dims[1] != p->N)) return QMOE_ERR_SHAPE;
+  if (output && (output->dims[0] != p->M || output->dims[1] != p->S || output->dims[2] != p->N))
+    return QMOE_ERR_SHAPE;
+  if (T != QMOE_F32) return QMOE_ERR_UNSUPPORTED;
+  const int64_t lim30 = int64_t(1) << 30;
+  if (p->M > lim30 || p->S > lim30) return QMOE_ERR_UNSUPPORTED;
+  p->R = p->M * p->S;
+  if (p->G > kMaxGroups || p->R >= lim30 || p->K >= lim30 || p->N >= lim30) return QMOE_ERR_UNSUPPORTED;
+  p->bm = gmm_tile_rows();
+  p->idx64 = idx->dtype == QMOE_I64;
+  p->has_bias = bias != nullptr;
+  p->max_tiles = (p->R + p->bm - 1) / p->bm + p->G + 1;
+  p->nblk = (p->N + 127) / 128;
+  if (p->max_tiles * p->nblk >= (int64_t(1) << 31)) return QMOE_ERR_UNSUPPORTED;
+  p->nchunks = (p->R + kChunk - 1) / kChunk;
+  if (p->R == 0 || p->N == 0) return QMOE_OK;  // empty output: nothing to enqueue
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  const int64_t buckets = p->G + 1;
+  p->off_idx = take(sizeof(int32_t) * p->R);
+  p->off_counts = take(sizeof(int32_t) * buckets);
+  p->off_offsets = take(sizeof(int32_t) * (buckets + 1));
+  p->off_perm = take(sizeof(int32_t) * p->R);
+  p->off_tiles = take(sizeof(int32_t) * 4 * p->max_tiles);
+  p->off_ntiles = take(sizeof(int32_t) * 4);
+  p->off_hist = take(sizeof(int32_t) * p->nchunks * buckets);
+  p->bytes = o;
+  return QMOE_OK;
+}
+
+int64_t numel(const qmoe_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->rank; ++i) n *= t->dims[i];
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmoe_status qmoe_grouped_matmul_workspace_size(const qmoe_tensor* input, const qmoe_tensor* weights,
+                                               const qmoe_tensor* group_indices, const qmoe_tensor* bias,
+                                               const qmoe_tensor* output, size_t* bytes) {
+  if (!bytes) return QMOE_ERR_NULL;
+  GmmPlan p;
+  const qmoe_status st = check(input, weights, group_indices, bias, output, &p);
+  if (st != QMOE_OK) return st;
+  *bytes = p.bytes;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_grouped_matmul(const qmoe_tensor* input, const qmoe_tensor* weights,
+                                const qmoe_tensor* group_indices, const qmoe_tensor* bias,
+                                const qmoe_tensor* output, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!output) return QMOE_ERR_NULL;
+  GmmPlan p;
+  const qmoe_status st = check(input, weights, group_indices, bias, output, &p);
+  if (st != QMOE_OK) return st;
+  if (p.R == 0 || p.N == 0) return QMOE_OK;
+  const qmoe_tensor* all[] = {input, weights, group_indices, bias, output};
+  for (const qmoe_tensor* t : all)
+    if (t && numel(t) > 0 && t->data == nullptr) return QMOE_ERR_NULL;
+  for (const qmoe_tensor* t : {input, weights, bias, output})
+    if (t && !aligned_to(t->data, 4)) return QMOE_ERR_ALIGN;
+  if (!aligned_to(group_indices->data, p.idx64 ? 8 : 4)) return QMOE_ERR_ALIGN;
+  if (workspace == nullptr) return QMOE_ERR_NULL;
+  if (workspace_bytes < p.bytes) return QMOE_ERR_WORKSPACE;
+  if (!aligned_to(workspace, 256)) return QMOE_ERR_ALIGN;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int* idx = reinterpret_cast<int*>(ws + p.off_idx);
+  int* counts = reinterpret_cast<int*>(ws + p.off_counts);
+  int* offsets = reinterpret_cast<int*>(ws + p.off_offsets);
+  int* perm = reinterpret_cast<int*>(ws + p.off_perm);
+  int* tiles = reinterpret_cast<int*>(ws + p.off_tiles);
+  int* ntiles = reinterpret_cast<int*>(ws + p.off_ntiles);
+  int* hist = reinterpret_cast<int*>(ws + p.off_hist);
+  const int R = (int)p.R, G = (int)p.G;
+  if (launch_gmm_index(group_indices->data, p.idx64, R, G, idx, s) != hipSuccess) return QMOE_ERR_HIP;
+  if (launch_permute(idx, R, G + 1, (int)kChunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets, perm, tiles,
+                     ntiles, s) != hipSuccess)
+    return QMOE_ERR_HIP;
+  const bool vec = p.K % 4 == 0 && p.N % 4 == 0 && aligned_to(input->data, 16) && aligned_to(weights->data, 16);
+  if (launch_gmm_f32(static_cast<const float*>(input->data), static_cast<const float*>(weights->data),
+                     bias ? static_cast<const float*>(bias->data) : nullptr, perm, tiles, ntiles, (int)p.max_tiles,
+                     (int)p.S, (int)p.K, (int)p.N, G, static_cast<float*>(const_cast<void*>(output->data)), vec,
+                     s) != hipSuccess)
+    return QMOE_ERR_HIP;
+  return QMOE_OK;
+}
+
+}  // extern "C"

@@ -131,3 +131,53 @@ def random_case(rng: np.random.Generator, *, tokens_shape, hidden, experts, inte
     w = Workload("sweep", tuple(tokens_shape) + (hidden,), experts, inter, k, bits, block_size,
                  activation, scale_range, logit_sigma=logit_sigma)
     return w, generate(w, seed=int(rng.integers(0, 2**31 - 1)))
+
+
+# ---------------------------------------------------------------- GroupedMatMul
+# Float workloads of the standalone GroupedMatMul (ONNX "GroupedMatMul - 29"):
+# the FC1 products of the decode and fine-grained layers above with float32
+# weights, as a graph that dequantises before the operator would pass them.
+# Draw order (one default_rng(seed)): input ~ N(0, 1); weights ~ N(0, 1) *
+# wscale; bias ~ N(0, 1) * wscale (when used); group_indices: S distinct
+# groups per row, drawn without replacement with probability proportional to
+# 1 / rank**2 when zipf is set (the fine-grained layer's skew), else uniform.
+@dataclass(frozen=True)
+class GmmWorkload:
+    name: str
+    M: int
+    K: int
+    G: int
+    N: int
+    S: int
+    bias: bool = True
+    zipf: bool = False
+    wscale: float = 0.01
+    seed: int = 0
+
+    def describe(self) -> dict:
+        return asdict(self)
+
+
+GMM_WORKLOADS = {
+    "gmm_decode_fc1": GmmWorkload("gmm_decode_fc1", 16, 4096, 8, 28672, 2),
+    "gmm_fine_fc1": GmmWorkload("gmm_fine_fc1", 2048, 2048, 64, 2816, 6, zipf=True),
+}
+
+
+def gmm_generate(w: GmmWorkload, seed: Optional[int] = None, index_dtype=np.int64) -> dict:
+    """Draw input, weights, group_indices (and bias) of ``w`` in the order above."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    x = rng.standard_normal((w.M, w.K), dtype=np.float32)
+    wts = rng.standard_normal((w.G, w.K, w.N), dtype=np.float32)
+    wts *= np.float32(w.wscale)
+    b = None
+    if w.bias:
+        b = rng.standard_normal((w.G, w.N), dtype=np.float32) * np.float32(w.wscale)
+    p = None
+    if w.zipf:
+        p = 1.0 / np.arange(1, w.G + 1, dtype=np.float64) ** 2
+        p /= p.sum()
+    idx = np.empty((w.M, w.S), dtype=index_dtype)
+    for m in range(w.M):
+        idx[m] = rng.choice(w.G, size=w.S, replace=w.S > w.G, p=p)
+    return {"input": x, "weights": wts, "group_indices": idx, "bias": b}

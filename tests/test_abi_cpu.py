@@ -151,3 +151,66 @@ def test_null_arguments(lib):
     assert lib.qmoe_validate(None, None, None, None, None, None, None, None) == 1
     a = qm.qmoe_attrs_default()
     assert lib.qmoe_workspace_size(None, None, None, None, None, None, ctypes.byref(a), None) == 1
+
+
+# ---------------------------------------------------------------- GroupedMatMul
+def _gmm(M=4, K=3, G=2, N=5, S=2, dt=np.float32, it=np.int64, bias=True):
+    z = lambda shape, d: np.lib.stride_tricks.as_strided(np.zeros(1, dtype=d), shape=shape,
+                                                         strides=(0,) * len(shape))
+    return dict(input=z((M, K), dt), weights=z((G, K, N), dt), group_indices=z((M, S), it),
+                bias=z((G, N), dt) if bias else None, output=z((M, S, N), dt))
+
+
+def _gmm_status(**kw):
+    try:
+        qm.qmoe_grouped_matmul_workspace_size(**kw)
+        return 0
+    except qm.QmoeError as e:
+        return e.status
+
+
+def test_grouped_matmul_contract(lib):
+    # ONNX "GroupedMatMul - 29": Inputs, Outputs, Type Constraints
+    assert _gmm_status(**_gmm()) == 0
+    assert _gmm_status(**_gmm(it=np.int32, bias=False)) == 0
+    assert _gmm_status(**dict(_gmm(), output=None)) == 0
+    # shape clauses
+    a = _gmm()
+    assert _gmm_status(**dict(a, input=a["input"][:, :2])) == 2               # K mismatch
+    assert _gmm_status(**dict(a, group_indices=a["group_indices"][:3])) == 2  # M mismatch
+    assert _gmm_status(**dict(a, bias=a["bias"][:1])) == 2                    # bias [G, N]
+    assert _gmm_status(**dict(a, output=a["output"][:, :1])) == 2             # output [M, S, N]
+    assert _gmm_status(**dict(a, input=a["input"][None])) == 2                # rank 3 input
+    # dtype clauses: T is one float type for input, weights, bias, output
+    assert _gmm_status(**_gmm(it=np.int16)) == 7
+    assert _gmm_status(**_gmm(it=np.float32)) == 7
+    assert _gmm_status(**dict(a, weights=a["weights"].astype(np.float64))) == 7
+    assert _gmm_status(**_gmm(dt=np.uint8)) == 7
+    for dt in (np.float16, np.float64):  # in the type list, not implemented
+        assert _gmm_status(**_gmm(dt=dt)) == 4
+    # group count limit of the permutation (G + 1 buckets <= 1024)
+    assert _gmm_status(**_gmm(G=1023)) == 0
+    assert _gmm_status(**_gmm(G=1024)) == 4
+
+
+def test_grouped_matmul_workspace_and_empty(lib):
+    # empty outputs need no workspace; G == 0 and K == 0 are in contract
+    for kw in (dict(M=0), dict(S=0), dict(N=0)):
+        assert qm.qmoe_grouped_matmul_workspace_size(**_gmm(**kw)) == 0
+    for kw in (dict(G=0), dict(K=0)):
+        assert qm.qmoe_grouped_matmul_workspace_size(**_gmm(**kw)) > 0
+    # index copy, permutation and tile table grow with M * S
+    small = qm.qmoe_grouped_matmul_workspace_size(**_gmm(M=64, S=2))
+    big = qm.qmoe_grouped_matmul_workspace_size(**_gmm(M=4096, S=8))
+    assert big >= 2 * 4 * 4096 * 8 > small
+
+
+def test_grouped_matmul_null_arguments(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.qmoe_grouped_matmul_workspace_size(None, None, None, None, None, ctypes.byref(n)) == 1
+    a = {k: qm.describe(v, False) for k, v in _gmm().items()}
+    refs = [ctypes.byref(a[k]) for k in ("input", "weights", "group_indices", "bias", "output")]
+    assert lib.qmoe_grouped_matmul_workspace_size(*refs, None) == 1
+    # missing output descriptor, then a missing device pointer
+    assert lib.qmoe_grouped_matmul(*refs[:4], None, None, 0, None) == 1
+    assert lib.qmoe_grouped_matmul(*refs, None, 1 << 20, None) == 1

@@ -57,6 +57,59 @@ def test_grouped_matmul_rejects_bad_index():
         oracle.grouped_matmul(np.ones((1, 2)), np.ones((2, 2, 2)), np.array([[-1]]))
 
 
+@pytest.mark.parametrize("case", _load("grouped_matmul_examples.json")["cases"], ids=lambda c: c["name"])
+def test_grouped_matmul_rows_page_examples(case):
+    # the row-sampled form reproduces the page's examples too
+    if case["expected"] is None:
+        return
+    inp = np.array(case["input"], dtype=np.float64)
+    if "input_shape" in case:
+        inp = inp.reshape(case["input_shape"])
+    wts = np.array(case["weights"], dtype=np.float64)
+    idx = np.array(case["group_indices"], dtype=np.int64)
+    if "group_indices_shape" in case:
+        idx = idx.reshape(case["group_indices_shape"])
+    elif idx.size == 0:
+        idx = idx.reshape(inp.shape[0], 0)
+    bias = None if case["bias"] is None else np.array(case["bias"], dtype=np.float64)
+    out = oracle.grouped_matmul_rows(inp, wts, idx, bias)
+    np.testing.assert_allclose(out, np.array(case["expected"]).reshape(out.shape), atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_grouped_matmul_rows_agrees_with_loops(seed):
+    rng = np.random.default_rng(seed)
+    M, K, G, N, S = 5, 7, 3, 4, 2
+    inp = rng.standard_normal((M, K)).astype(np.float32)
+    wts = rng.standard_normal((G, K, N)).astype(np.float32)
+    bias = rng.standard_normal((G, N)).astype(np.float32)
+    idx = rng.integers(0, G, size=(M, S))
+    full = oracle.grouped_matmul(inp, wts, idx, bias, out_dtype=np.float64)
+    np.testing.assert_allclose(oracle.grouped_matmul_rows(inp, wts, idx, bias), full, rtol=1e-13, atol=1e-13)
+    rows = np.array([4, 1])
+    np.testing.assert_allclose(oracle.grouped_matmul_rows(inp, wts, idx, None, rows),
+                               oracle.grouped_matmul(inp, wts, idx, None, out_dtype=np.float64)[rows],
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_grouped_matmul_closed_forms():
+    # identity weights give the input back; a one-hot column picks one input
+    # element; bias alone (K == 0) is the result
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 4))
+    eye = np.stack([np.eye(4), 2 * np.eye(4)])
+    idx = np.array([[0, 1], [1, 1], [0, 0]])
+    for f in (oracle.grouped_matmul, oracle.grouped_matmul_rows):
+        out = f(x, eye, idx)
+        np.testing.assert_array_equal(out[:, 0], x * np.array([1, 2, 1])[:, None])
+        np.testing.assert_array_equal(out[:, 1], x * np.array([2, 2, 1])[:, None])
+        b = rng.standard_normal((2, 5))
+        out0 = f(np.zeros((3, 0)), np.zeros((2, 0, 5)), idx, b)
+        np.testing.assert_array_equal(out0, b[idx])
+    with pytest.raises(ValueError):
+        oracle.grouped_matmul_rows(np.ones((1, 2)), np.ones((2, 2, 2)), np.array([[-1]]))
+
+
 # ---------------------------------------------------------------- P2: lifted with_bias example
 def _lifted_arrays():
     g = _load("qmoe_lifted_with_bias.json")
