@@ -9,6 +9,10 @@ block size 64).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 
+Workloads named gmm_* measure the standalone float32 GroupedMatMul instead
+(one step = one qmoe_grouped_matmul call; roofline of its tile GEMM against
+the fp32 matrix peak or HBM).
+
 The roofline object describes the dominant kernel (FC1 or FC2, whichever is
 slower), timed with HIP events recorded on the launch stream around that
 kernel over K further steps; its algorithmic bytes and FLOPs are counted from
@@ -33,6 +37,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 F16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense f16 matrix peak, TFLOP/s
+F32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X fp32 matrix (and vector) peak, TFLOP/s
 METRIC = "QMoE layer tokens/s + achieved HBM GB/s vs peak (int4 decode & prefill)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -67,16 +72,16 @@ def kernel_work(w, counts):
     return fc1, fc2
 
 
-def roofline_for(work, ms):
+def roofline_for(work, ms, mfma_peak=F16_DENSE_PEAK_TFLOPS):
     intensity = work["flops"] / work["bytes"]
-    ridge = F16_DENSE_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     if intensity < ridge:
         ach = work["bytes"] / (ms * 1e-3) / 1e9
         return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4))
     ach = work["flops"] / (ms * 1e-3) / 1e12
-    return dict(bound="mfma", achieved=round(ach, 1), peak=F16_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=round(ach / F16_DENSE_PEAK_TFLOPS, 4))
+    return dict(bound="mfma", achieved=round(ach, 1), peak=mfma_peak, unit="TFLOP/s",
+                frac=round(ach / mfma_peak, 4))
 
 
 def stage_times(qm, call_debug, steps):
@@ -137,7 +142,19 @@ KERNEL_SRC = {
     "qmoe_stream": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "stream.hip"),
     "qmoe_tiled": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "tiled.hip"),
     "qmoe_gemm": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gemm.hip"),
+    "qmoe_gmm_f32": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm.hip"),
+    "qmoe_gmm_f32_rows16": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm.hip"),
 }
+
+
+def gmm_kernel(w):
+    """The library's GroupedMatMul kernel for this shape: the weight-streaming
+    one over 16-row tiles when the rows average at most 16 per group (and K, N
+    are multiples of 4; bench tensors are 16-byte aligned), else the LDS-tiled
+    one over 64-row tiles."""
+    R = w.M * w.S
+    rows16 = w.K % 4 == 0 and w.N % 4 == 0 and R <= 16 * max(1, min(w.G, R))
+    return "qmoe_gmm_f32_rows16" if rows16 else "qmoe_gmm_f32"
 
 
 def gemm_kernel(w):
@@ -198,6 +215,124 @@ def copy_calibration(nbytes, reps=3):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def gmm_work(w, idx):
+    """Algorithmic bytes and FLOPs of one GroupedMatMul call: weights (and
+    bias rows) of the groups that receive a row, input rows, output rows."""
+    import numpy as np
+    used = int(np.unique(idx).size)
+    wb = used * w.K * w.N * 4 + (used * w.N * 4 if w.bias else 0)
+    return dict(bytes=wb + w.M * w.K * 4 + w.M * w.S * w.N * 4, flops=2.0 * w.M * w.S * w.K * w.N,
+                weight_bytes=wb, used_groups=used)
+
+
+def gmm_cpu_baseline(w, a, budget_s=12.0, max_reps=64):
+    """The float64 oracle (row-sampled form) on the host cores over the first
+    rows of the workload, repeated up to about budget_s seconds."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    rows = list(range(min(4, w.M)))
+    done, reps = 0, 0
+    t0 = time.perf_counter()
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < budget_s):
+        oracle.grouped_matmul_rows(a["input"], a["weights"], a["group_indices"], a["bias"], rows)
+        done += len(rows)
+        reps += 1
+    dt = time.perf_counter() - t0
+    return dict(value=round(done / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"first {len(rows)} token rows (all {w.S} selections each) x {reps} repetitions",
+                seconds=round(dt, 2))
+
+
+def main_gmm(args):
+    """GroupedMatMul (float32) on one of its workloads: one step = one
+    qmoe_grouped_matmul call (index conversion, group permutation, tile GEMM)."""
+    import numpy as np
+    import torch
+
+    import quantized_mixture_experts_router_amd as qm
+    from quantized_mixture_experts_router_amd import workloads as W
+
+    w = W.GMM_WORKLOADS[args.workload]
+    a = W.gmm_generate(w)
+    torch.cuda.set_device(0)
+    d = {k: (torch.from_numpy(v).cuda() if v is not None else None) for k, v in a.items()}
+    out = torch.empty((w.M, w.S, w.N), dtype=torch.float32, device="cuda")
+    need = qm.qmoe_grouped_matmul_workspace_size(d["input"], d["weights"], d["group_indices"], d["bias"], out)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        qm.qmoe_grouped_matmul(d["input"], d["weights"], d["group_indices"], d["bias"], out, ws, stream, events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    work = gmm_work(w, a["group_indices"])
+
+    roofline = None
+    stages = None
+    if not args.no_stage_timing:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        evs = []
+        for _ in range(3):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e)
+        sums = [0.0, 0.0]
+        for _ in range(args.steps):
+            step([e.value for e in evs])
+            assert hip.hipEventSynchronize(evs[2]) == 0
+            for i in range(2):
+                ms = ctypes.c_float()
+                assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[i], evs[i + 1]) == 0
+                sums[i] += ms.value
+        for e in evs:
+            hip.hipEventDestroy(e)
+        stages = dict(permutation=sums[0] / args.steps, gemm=sums[1] / args.steps)
+        roofline = roofline_for(work, stages["gemm"], F32_MATRIX_PEAK_TFLOPS)
+        kernel = gmm_kernel(w)
+        roofline["kernel"] = kernel
+        roofline["avg_ms"] = round(stages["gemm"], 5)
+        roofline["algorithmic_bytes"] = int(work["bytes"])
+        roofline["algorithmic_flops"] = work["flops"]
+        roofline["traffic"] = traffic_for(f"{args.workload}:gemm", kernel)
+
+    cpu = None if args.no_cpu_baseline else gmm_cpu_baseline(w, a)
+    line = {
+        "metric": "GroupedMatMul float32 tokens/s + achieved GB/s or TFLOP/s vs peak",
+        "value": round(w.M * args.steps / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy draws: input N(0,1), weights and bias N(0,1)*wscale, "
+                "Zipf or uniform distinct group indices)",
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "G": w.G, "N": w.N, "S": w.S, "bias": w.bias,
+                   "zipf": w.zipf},
+        "gbs": round(work["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "tflops": round(work["flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+        "stage_ms": {k: round(v, 5) for k, v in stages.items()} if stages else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -206,6 +341,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.workload.startswith("gmm_"):
+        main_gmm(args)
         return
     import numpy as np
     import torch

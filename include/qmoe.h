@@ -188,8 +188,10 @@ qmoe_status qmoe_forward_debug(const qmoe_tensor* input, const qmoe_tensor* rout
  * QMOE_ERR_DTYPE); group_indices is QMOE_I32 or QMOE_I64 (else
  * QMOE_ERR_DTYPE).  Ranks or extents that disagree: QMOE_ERR_SHAPE.
  * Limits (QMOE_ERR_UNSUPPORTED beyond them): G <= 1023, M * S < 2^30,
- * K < 2^30, N < 2^30, and (ceil(M * S / 64) + G + 1) * ceil(N / 128)
- * < 2^31 (one workgroup per 64-row, 128-column output tile).
+ * K < 2^30, N < 2^30, and (ceil(M * S / B) + G + 1) * ceil(N / 128)
+ * < 2^31, B = 16 when M * S <= 16 min(G, M * S) and K, N are multiples of
+ * 4 (weight-streaming kernel over 16-row tiles), else 64 (LDS-tiled kernel
+ * over 64-row, 128-column tiles); one workgroup per tile and column block.
  *
  * Indices outside [0, G) are invalid input, for which the page defines no
  * result; this library writes zeros to those output rows and reads no weight
@@ -210,13 +212,26 @@ qmoe_status qmoe_grouped_matmul_workspace_size(const qmoe_tensor* input, const q
 /* Enqueue GroupedMatMul on stream (a hipStream_t; NULL = the null stream).
  * Device pointers: float tensors 4-byte aligned, group_indices aligned to its
  * element size (QMOE_ERR_ALIGN otherwise); 16-byte aligned input and weights
- * with K and N multiples of 4 take the vector-load path.  workspace: at least
+ * with K and N multiples of 4 take the vector-load path, and the
+ * weight-streaming kernel also needs 16-byte aligned bias and output.  workspace: at least
  * qmoe_grouped_matmul_workspace_size bytes, 256-byte aligned, owned by this
  * call until the stream reaches it.  The output must not alias an input.
  * With M * S * N == 0 nothing is enqueued. */
 qmoe_status qmoe_grouped_matmul(const qmoe_tensor* input, const qmoe_tensor* weights,
                                 const qmoe_tensor* group_indices, const qmoe_tensor* bias,
                                 const qmoe_tensor* output, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage boundaries at which qmoe_grouped_matmul_debug records events. */
+#define QMOE_GMM_EVENTS 3
+
+/* As qmoe_grouped_matmul, and also records the caller-created hipEvent_t
+ * handles of events (each may be NULL) on the stream: [0] before the index
+ * conversion, [1] after the group permutation, [2] after the tile GEMM.
+ * Nothing is recorded when M * S * N == 0. */
+qmoe_status qmoe_grouped_matmul_debug(const qmoe_tensor* input, const qmoe_tensor* weights,
+                                      const qmoe_tensor* group_indices, const qmoe_tensor* bias,
+                                      const qmoe_tensor* output, void* workspace, size_t workspace_bytes,
+                                      void* stream, void* const events[QMOE_GMM_EVENTS]);
 
 /* Static, human-readable name of a status code. */
 const char* qmoe_status_string(qmoe_status s);

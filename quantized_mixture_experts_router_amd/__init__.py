@@ -6,7 +6,8 @@ and the current stream.  The functions keep the C names:
 
     qmoe_abi_version, qmoe_attrs_default, qmoe_validate, qmoe_workspace_size,
     qmoe_forward, qmoe_forward_debug, qmoe_status_string,
-    qmoe_grouped_matmul_workspace_size, qmoe_grouped_matmul
+    qmoe_grouped_matmul_workspace_size, qmoe_grouped_matmul,
+    qmoe_grouped_matmul_debug
 
 plus ``forward`` and ``grouped_matmul`` (allocate output and workspace with
 torch, then call qmoe_forward / qmoe_grouped_matmul) for convenience.  The
@@ -44,6 +45,7 @@ class QmoeAttrs(ctypes.Structure):
 
 
 QMOE_STAGE_EVENTS = 6
+QMOE_GMM_EVENTS = 3
 
 
 class QmoeDebug(ctypes.Structure):
@@ -89,6 +91,9 @@ def _lib():
         lib.qmoe_grouped_matmul_workspace_size.restype = ctypes.c_int
         lib.qmoe_grouped_matmul.argtypes = [T, T, T, T, T, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         lib.qmoe_grouped_matmul.restype = ctypes.c_int
+        lib.qmoe_grouped_matmul_debug.argtypes = [T, T, T, T, T, ctypes.c_void_p, ctypes.c_size_t,
+                                                  ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+        lib.qmoe_grouped_matmul_debug.restype = ctypes.c_int
         lib.qmoe_status_string.argtypes = [ctypes.c_int]
         lib.qmoe_status_string.restype = ctypes.c_char_p
         _lib_handle = lib
@@ -244,20 +249,29 @@ def qmoe_grouped_matmul_workspace_size(input, weights, group_indices, bias=None,
     return int(n.value)
 
 
-def qmoe_grouped_matmul(input, weights, group_indices, bias, output, workspace, stream=None) -> None:
+def qmoe_grouped_matmul(input, weights, group_indices, bias, output, workspace, stream=None, events=None) -> None:
     """Enqueue GroupedMatMul on ``stream`` (default: torch's current stream).
 
     Contiguous device tensors; ``bias`` may be None; ``workspace`` a uint8
     device tensor of at least qmoe_grouped_matmul_workspace_size bytes (or
-    None when that size is 0).
+    None when that size is 0).  ``events``: up to QMOE_GMM_EVENTS raw
+    hipEvent_t handles (calls qmoe_grouped_matmul_debug).
     """
     wptr = workspace.data_ptr() if workspace is not None and workspace.numel() > 0 else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib().qmoe_grouped_matmul(_ref(input, True), _ref(weights, True), _ref(group_indices, True),
-                                    _ref(bias, True), _ref(output, True), ctypes.c_void_p(wptr),
-                                    ctypes.c_size_t(wbytes), _stream_handle(stream))
+    args = [_ref(input, True), _ref(weights, True), _ref(group_indices, True), _ref(bias, True),
+            _ref(output, True), ctypes.c_void_p(wptr), ctypes.c_size_t(wbytes), _stream_handle(stream)]
+    if events is None:
+        st = _lib().qmoe_grouped_matmul(*args)
+        where = "qmoe_grouped_matmul"
+    else:
+        ev = (ctypes.c_void_p * QMOE_GMM_EVENTS)()
+        for i, e in enumerate(events):
+            ev[i] = e
+        st = _lib().qmoe_grouped_matmul_debug(*args, ev)
+        where = "qmoe_grouped_matmul_debug"
     if st != 0:
-        raise QmoeError(st, "qmoe_grouped_matmul")
+        raise QmoeError(st, where)
 
 
 def grouped_matmul(input, weights, group_indices, bias=None, stream=None, workspace=None, output=None):
@@ -271,3 +285,6 @@ def grouped_matmul(input, weights, group_indices, bias=None, stream=None, worksp
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=input.device)
     qmoe_grouped_matmul(input, weights, group_indices, bias, output, workspace, stream)
     return output
+
+
+qmoe_grouped_matmul_debug = qmoe_grouped_matmul

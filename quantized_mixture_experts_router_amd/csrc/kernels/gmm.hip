@@ -170,7 +170,121 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const float* __restric
   }
 }
 
+// Weight-streaming variant for groups of at most 16 rows (16-row tiles):
+// each wavefront owns a 64-column strip of one tile and streams that strip of
+// the group's [K, N] weights from HBM straight into matrix-core operands, with
+// no LDS and no barriers.  The 16 columns of MFMA block i are the columns
+// n0 + 4c + i (c = 0..15), so one 16-byte load per lane fetches a 256-byte
+// row segment serving all four blocks, and the four MFMAs of one 16-deep K
+// group take k = 16 kg + 4 kq + j (j = 0..3) in lane group kq: one 16-byte
+// load of the input row covers them.  kD K groups of loads stay in flight
+// ahead of the matrix instructions.  Requires K % 4 == 0, N % 4 == 0 and
+// 16-byte aligned x, w, bias and out.
+constexpr int kSD = 4;  // K groups (16 deep) of loads in flight per wavefront
+
+__global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const float* __restrict__ x, const float* __restrict__ w,
+                                                           const float* __restrict__ bias, const int* __restrict__ perm,
+                                                           const int* __restrict__ tiles,
+                                                           const int* __restrict__ ntiles, int nblk, int S, int K,
+                                                           int N, int G, float* __restrict__ out) {
+  const int tile = blockIdx.x / nblk;
+  if (tile >= ntiles[0]) return;
+  const int g = tiles[4 * tile + 0];
+  const int p0 = tiles[4 * tile + 1];
+  const int rows = tiles[4 * tile + 2];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x % nblk) * 256 + wave * 64;
+  if (n0 >= N) return;  // whole wavefront: no barriers below
+  const int c = lane & 15, kq = lane >> 4;
+  const int n = n0 + 4 * c;
+  const bool col_ok = n < N;  // N % 4 == 0: all four columns or none
+  const int row = lane & 15;  // A operand row of this lane
+  const int slot_a = perm[p0 + min(row, rows - 1)];
+  if (g >= G) {
+    // invalid group index: zero rows
+    if (col_ok) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 4 * kq + t;
+        if (r < rows) *(f32x4*)(out + (long)perm[p0 + r] * N + n) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  }
+  const float* arow = x + (long)(slot_a / S) * K + 4 * kq;
+  // lanes past N re-read column 0 (results discarded)
+  const float* wcol = w + (long)g * K * N + (col_ok ? n : 0) + (long)(4 * kq) * N;
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nfull = K / 16;  // K groups without a tail
+  f32x4 ra[kSD], rb[kSD][4];
+  auto load = [&](int slot, int kg) {
+    const long k = (long)kg * 16;
+    ra[slot] = *(const f32x4*)(arow + k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rb[slot][j] = *(const f32x4*)(wcol + (k + j) * N);
+  };
+  auto mma = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[slot][j], rb[slot][j][i], acc[i], 0, 0, 0);
+  };
+  // Branch-free pipeline (exact load counts for the waits): past the last
+  // full group the loads repeat it, and those values are never used.
+  int kg = 0;
+  if (nfull > 0) {
+#pragma unroll
+    for (int d = 0; d < kSD; ++d) load(d, min(d, nfull - 1));
+    for (; kg + kSD <= nfull; kg += kSD) {
+#pragma unroll
+      for (int d = 0; d < kSD; ++d) {
+        mma(d);
+        load(d, min(kg + kSD + d, nfull - 1));
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < kSD; ++d)
+      if (kg + d < nfull) mma(d);
+  }
+  if (nfull * 16 < K) {
+    // tail group: k past K reads as zero on both operands
+    const int k0 = nfull * 16 + 4 * kq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = k0 + j < K;
+      ra[0][j] = ok ? arow[nfull * 16 + j] : 0.f;
+      rb[0][j] = ok ? *(const f32x4*)(wcol + ((long)nfull * 16 + j) * N) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    mma(0);
+  }
+  if (!col_ok) return;
+  const f32x4 bv = bias ? *(const f32x4*)(bias + (long)g * N + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = 4 * kq + t;
+    if (r < rows) {
+      const f32x4 v = {acc[0][t] + bv[0], acc[1][t] + bv[1], acc[2][t] + bv[2], acc[3][t] + bv[3]};
+      *(f32x4*)(out + (long)perm[p0 + r] * N + n) = v;
+    }
+  }
+}
+
 int gmm_tile_rows() { return kGM; }
+int gmm_rows16_tile_rows() { return 16; }
+
+hipError_t launch_gmm_rows16(const float* x, const float* w, const float* bias, const int* perm, const int* tiles,
+                             const int* ntiles, int max_tiles, int S, int K, int N, int G, float* out,
+                             hipStream_t st) {
+  if (max_tiles <= 0 || N <= 0) return hipSuccess;
+  if (K % 4 != 0 || N % 4 != 0) return hipErrorInvalidValue;
+  const int nblk = (N + 255) / 256;
+  const dim3 grid((unsigned)((long)max_tiles * nblk)), block(256);
+  hipLaunchKernelGGL(qmoe_gmm_f32_rows16, grid, block, 0, st, x, w, bias, perm, tiles, ntiles, nblk, S, K, N, G, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_gmm_index(const void* idx, bool idx64, long n, int G, int* out, hipStream_t st) {
   if (n <= 0) return hipSuccess;

@@ -94,6 +94,12 @@ hipError_t launch_gmm_index(const void* idx, bool idx64, long n, int G, int* out
 hipError_t launch_gmm_f32(const float* x, const float* w, const float* bias, const int* perm, const int* tiles,
                           const int* ntiles, int max_tiles, int S, int K, int N, int G, float* out, bool vec,
                           hipStream_t st);
+// Weight-streaming variant for tiles of at most gmm_rows16_tile_rows() rows:
+// K, N multiples of 4; x, w, bias, out 16-byte aligned.
+int gmm_rows16_tile_rows();
+hipError_t launch_gmm_rows16(const float* x, const float* w, const float* bias, const int* perm, const int* tiles,
+                             const int* ntiles, int max_tiles, int S, int K, int N, int G, float* out,
+                             hipStream_t st);
 
 hipError_t launch_fill_zero(float* out, long n, hipStream_t st);
 

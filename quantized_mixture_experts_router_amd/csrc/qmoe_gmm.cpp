@@ -7,6 +7,8 @@
 // with every intermediate in the caller's workspace.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kernels/launch.h"
 #include "qmoe.h"
 
@@ -25,6 +27,7 @@ struct GmmPlan {
   int64_t M = 0, K = 0, G = 0, N = 0, S = 0, R = 0;  // R = M * S rows
   int64_t bm = 0, max_tiles = 0, nchunks = 0, nblk = 0;
   bool idx64 = false, has_bias = false;
+  bool rows16 = false;  // groups average at most 16 rows: 16-row tiles, weight-streaming kernel
   size_t off_idx = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_tiles = 0, off_ntiles = 0, off_hist = 0;
   size_t bytes = 0;
 };
@@ -61,8 +64,14 @@ qmoe_status check(const qmoe_tensor* input, const qmoe_tensor* weights, const qm
   if (p->M > lim30 || p->S > lim30) return QMOE_ERR_UNSUPPORTED;
   p->R = p->M * p->S;
   if (p->G > kMaxGroups || p->R >= lim30 || p->K >= lim30 || p->N >= lim30) return QMOE_ERR_UNSUPPORTED;
-  p->bm = gmm_tile_rows();
   p->idx64 = idx->dtype == QMOE_I64;
+  // Rows per group if the rows spread over min(G, R) groups: at most one
+  // 16-row tile each, the weights are streamed once (16-row tiles); else
+  // LDS-tiled 64-row tiles.  With misaligned pointers the tiled kernel also
+  // runs the 16-row tiles.
+  const int64_t spread = std::max<int64_t>(1, std::min(p->G, p->R));
+  p->rows16 = p->K % 4 == 0 && p->N % 4 == 0 && p->R <= 16 * spread;
+  p->bm = p->rows16 ? gmm_rows16_tile_rows() : gmm_tile_rows();
   p->has_bias = bias != nullptr;
   p->max_tiles = (p->R + p->bm - 1) / p->bm + p->G + 1;
   p->nblk = (p->N + 127) / 128;
@@ -104,9 +113,13 @@ qmoe_status qmoe_grouped_matmul_workspace_size(const qmoe_tensor* input, const q
   return QMOE_OK;
 }
 
-qmoe_status qmoe_grouped_matmul(const qmoe_tensor* input, const qmoe_tensor* weights,
-                                const qmoe_tensor* group_indices, const qmoe_tensor* bias,
-                                const qmoe_tensor* output, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const qmoe_tensor* group_indices,
+                     const qmoe_tensor* bias, const qmoe_tensor* output, void* workspace, size_t workspace_bytes,
+                     void* stream, void* const* events) {
   if (!output) return QMOE_ERR_NULL;
   GmmPlan p;
   const qmoe_status st = check(input, weights, group_indices, bias, output, &p);
@@ -132,17 +145,48 @@ qmoe_status qmoe_grouped_matmul(const qmoe_tensor* input, const qmoe_tensor* wei
   int* ntiles = reinterpret_cast<int*>(ws + p.off_ntiles);
   int* hist = reinterpret_cast<int*>(ws + p.off_hist);
   const int R = (int)p.R, G = (int)p.G;
+  auto mark = [&](int i) -> hipError_t {
+    if (events && events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s);
+    return hipSuccess;
+  };
+  if (mark(0) != hipSuccess) return QMOE_ERR_HIP;
   if (launch_gmm_index(group_indices->data, p.idx64, R, G, idx, s) != hipSuccess) return QMOE_ERR_HIP;
   if (launch_permute(idx, R, G + 1, (int)kChunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets, perm, tiles,
                      ntiles, s) != hipSuccess)
     return QMOE_ERR_HIP;
+  if (mark(1) != hipSuccess) return QMOE_ERR_HIP;
   const bool vec = p.K % 4 == 0 && p.N % 4 == 0 && aligned_to(input->data, 16) && aligned_to(weights->data, 16);
-  if (launch_gmm_f32(static_cast<const float*>(input->data), static_cast<const float*>(weights->data),
+  const bool stream16 = p.rows16 && vec && aligned_to(output->data, 16) && (!bias || aligned_to(bias->data, 16));
+  if (stream16) {
+    if (launch_gmm_rows16(static_cast<const float*>(input->data), static_cast<const float*>(weights->data),
+                          bias ? static_cast<const float*>(bias->data) : nullptr, perm, tiles, ntiles,
+                          (int)p.max_tiles, (int)p.S, (int)p.K, (int)p.N, G,
+                          static_cast<float*>(const_cast<void*>(output->data)), s) != hipSuccess)
+      return QMOE_ERR_HIP;
+  } else if (launch_gmm_f32(static_cast<const float*>(input->data), static_cast<const float*>(weights->data),
                      bias ? static_cast<const float*>(bias->data) : nullptr, perm, tiles, ntiles, (int)p.max_tiles,
                      (int)p.S, (int)p.K, (int)p.N, G, static_cast<float*>(const_cast<void*>(output->data)), vec,
                      s) != hipSuccess)
     return QMOE_ERR_HIP;
+  if (mark(2) != hipSuccess) return QMOE_ERR_HIP;
   return QMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmoe_status qmoe_grouped_matmul(const qmoe_tensor* input, const qmoe_tensor* weights,
+                                const qmoe_tensor* group_indices, const qmoe_tensor* bias,
+                                const qmoe_tensor* output, void* workspace, size_t workspace_bytes, void* stream) {
+  return gmm_impl(input, weights, group_indices, bias, output, workspace, workspace_bytes, stream, nullptr);
+}
+
+qmoe_status qmoe_grouped_matmul_debug(const qmoe_tensor* input, const qmoe_tensor* weights,
+                                      const qmoe_tensor* group_indices, const qmoe_tensor* bias,
+                                      const qmoe_tensor* output, void* workspace, size_t workspace_bytes,
+                                      void* stream, void* const events[QMOE_GMM_EVENTS]) {
+  return gmm_impl(input, weights, group_indices, bias, output, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

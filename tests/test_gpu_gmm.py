@@ -117,6 +117,13 @@ def test_page_examples(torch, case):
 
 
 SHAPES = [  # M, K, G, N, S: one tile, several tiles, ragged K / N / M tails
+    # at most 16 rows per group on average, K and N multiples of 4: 16-row
+    # tiles, weight-streaming kernel
+    (16, 256, 8, 512, 2),
+    (20, 100, 16, 260, 3),
+    (8, 8, 4, 64, 2),
+    (8, 4, 4, 68, 2),
+    # 64-row tiles, LDS-tiled kernel
     (1, 1, 1, 1, 1),
     (5, 3, 2, 7, 2),
     (64, 16, 1, 128, 1),
@@ -154,9 +161,12 @@ def test_skewed_and_unused_groups(torch):
     _check(got, x, w, idx, b, label="skewed")
 
 
-def test_misaligned_pointers_take_scalar_path(torch):
+@pytest.mark.parametrize("shape", [(70, 64, 3, 136, 2), (16, 64, 8, 136, 2)], ids=["tiles64", "tiles16"])
+def test_misaligned_pointers_take_scalar_path(torch, shape):
+    # input and weights 4 bytes past a 16-byte boundary: scalar loads, and
+    # 16-row tiles run on the LDS-tiled kernel
     rng = np.random.default_rng(8)
-    M, K, G, N, S = 70, 64, 3, 136, 2
+    M, K, G, N, S = shape
     x = rng.standard_normal((M, K), dtype=np.float32)
     w = rng.standard_normal((G, K, N), dtype=np.float32)
     b = rng.standard_normal((G, N), dtype=np.float32)
@@ -165,9 +175,22 @@ def test_misaligned_pointers_take_scalar_path(torch):
     _check(got, x, w, idx, b, label="misaligned")
 
 
-def test_invalid_indices_give_zero_rows(torch):
+def test_small_groups_spanning_several_16_row_tiles(torch):
+    # 16-row tiles with one group of 40 rows (three tiles) and a few empty groups
+    rng = np.random.default_rng(12)
+    M, K, G, N, S = 64, 64, 8, 128, 1
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    w = rng.standard_normal((G, K, N), dtype=np.float32)
+    b = rng.standard_normal((G, N), dtype=np.float32)
+    idx = np.concatenate([np.zeros(40, np.int64), rng.choice([2, 5, 7], size=M - 40)])[:, None]
+    got = _run(torch, x, w, idx, b, label="rows16-multi")
+    _check(got, x, w, idx, b, label="rows16-multi")
+
+
+@pytest.mark.parametrize("shape", [(150, 48, 4, 160, 3), (16, 64, 4, 128, 2)], ids=["tiles64", "tiles16"])
+def test_invalid_indices_give_zero_rows(torch, shape):
     rng = np.random.default_rng(9)
-    M, K, G, N, S = 150, 48, 4, 160, 3
+    M, K, G, N, S = shape
     x = rng.standard_normal((M, K), dtype=np.float32)
     w = rng.standard_normal((G, K, N), dtype=np.float32)
     b = rng.standard_normal((G, N), dtype=np.float32)
