@@ -15,3 +15,4 @@ from .qmoe_oracle import (  # noqa: F401
     qmoe, qmoe_dense, qmoe_tokens, expert_ffn,
 )
 from .grouped_matmul import grouped_matmul, grouped_matmul_rows  # noqa: F401
+from .moe_oracle import moe, moe_tokens, moe_validate, moe_activation, gelu  # noqa: F401
