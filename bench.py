@@ -11,7 +11,8 @@ block size 64).  Prints one JSON line.
 
 Workloads named gmm_* measure the standalone float32 GroupedMatMul instead
 (one step = one qmoe_grouped_matmul call; roofline of its tile GEMM against
-the fp32 matrix peak or HBM).
+the fp32 matrix peak or HBM), and moe_* the float MoE operator (one step =
+one qmoe_moe_forward; roofline of its slower projection).
 
 The roofline object describes the dominant kernel (FC1 or FC2, whichever is
 slower), timed with HIP events recorded on the launch stream around that
@@ -333,6 +334,124 @@ def main_gmm(args):
     print(json.dumps(line), flush=True)
 
 
+def moe_work(w, counts):
+    """Algorithmic bytes and FLOPs of the float MoE projections for one call:
+    FC1 (with FC3 when read) and FC2 over the experts that receive a slot."""
+    import numpy as np
+    used = int(np.count_nonzero(counts))
+    T, H, E, I, k, F = w.tokens, w.hidden, w.experts, w.inter, w.k, w.fc1_rows
+    S = T * k
+    n1 = F + (I if w.fc3 and w.activation in ("silu", "swiglu") else 0)
+    b1 = used * n1 * (H + (1 if w.bias else 0)) * 4
+    b2 = used * H * (I + (1 if w.bias else 0)) * 4
+    fc1 = dict(bytes=b1 + T * H * 4 + S * n1 * 4, flops=2.0 * S * n1 * H, weight_bytes=b1, used_experts=used)
+    fc2 = dict(bytes=b2 + S * I * 4 + S * H * 4, flops=2.0 * S * H * I, weight_bytes=b2, used_experts=used)
+    return fc1, fc2
+
+
+def main_moe(args):
+    """Float MoE on one of its workloads: one step = one qmoe_moe_forward
+    (router, permutation, FC1 (+FC3), activation, FC2, combine)."""
+    import numpy as np
+    import torch
+
+    import quantized_mixture_experts_router_amd as qm
+    from quantized_mixture_experts_router_amd import workloads as W
+
+    w = W.MOE_WORKLOADS[args.workload]
+    a = W.moe_generate(w)
+    torch.cuda.set_device(0)
+    d = {k: torch.from_numpy(v).cuda() for k, v in a.items() if v is not None}
+    attrs = qm.make_moe_attrs(w.attrs())
+    out = torch.empty_like(d["input"])
+    need = qm.qmoe_moe_workspace_size(d, attrs)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(debug=None):
+        qm.qmoe_moe_forward(d, attrs, out, ws, stream, debug)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    counts_t = torch.empty(w.experts, dtype=torch.int32, device="cuda")
+    step({"counts": counts_t})
+    torch.cuda.synchronize()
+    fc1_work, fc2_work = moe_work(w, counts_t.cpu().numpy())
+
+    roofline = None
+    stages = None
+    if not args.no_stage_timing:
+        stages = stage_times(qm, lambda events: step({"events": events}), args.steps)
+        stages = dict(zip(("routing", "fc1", "activation", "fc2", "combine"), stages.values()))
+        key = "fc1" if stages["fc1"] >= stages["fc2"] else "fc2"
+        work = fc1_work if key == "fc1" else fc2_work
+        roofline = roofline_for(work, stages[key], F32_MATRIX_PEAK_TFLOPS)
+        S = w.tokens * w.k
+        rows16 = S <= 16 * max(1, min(w.experts, S)) and (w.hidden if key == "fc1" else w.inter) % 4 == 0
+        kernel = "qmoe_gmm_f32_rows16" if rows16 else "qmoe_gmm_f32"
+        roofline["kernel"] = f"{kernel} ({key.upper()})"
+        roofline["avg_ms"] = round(stages[key], 5)
+        roofline["algorithmic_bytes"] = int(work["bytes"])
+        roofline["algorithmic_flops"] = work["flops"]
+        roofline["traffic"] = traffic_for(f"{args.workload}:{key}", kernel)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        except Exception:
+            threads = 1
+        ids = list(range(min(2, w.tokens)))
+        done, reps = 0, 0
+        t0 = time.perf_counter()
+        args_o = dict(x=a["input"], logits=a["router_probs"], fc1_w=a["fc1_experts_weights"],
+                      fc2_w=a["fc2_experts_weights"], fc3_w=a["fc3_experts_weights"], fc1_b=a["fc1_experts_bias"],
+                      fc2_b=a["fc2_experts_bias"], fc3_b=a["fc3_experts_bias"])
+        while reps < 16 and (reps == 0 or time.perf_counter() - t0 < 12.0):
+            oracle.moe_tokens(ids, **args_o, attrs=w.attrs())
+            done += len(ids)
+            reps += 1
+        dt = time.perf_counter() - t0
+        cpu = dict(value=round(done / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
+                   sample=f"first {len(ids)} tokens x {reps} repetitions (their experts' weights read in float64 "
+                          "per token)", seconds=round(dt, 2))
+
+    line = {
+        "metric": "float MoE layer tokens/s + achieved GB/s or TFLOP/s vs peak",
+        "value": round(w.tokens * args.steps / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy draws: input and logits N(0,1), weights N(0,1)/sqrt(fan-in), "
+                "biases N(0,1)*0.1)",
+        "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden, "experts": w.experts,
+                   "inter": w.inter, "k": w.k, "activation": w.activation, "swiglu_fusion": w.fusion,
+                   "bias": w.bias, "fc3": w.fc3, "input_shape": list(w.input_shape)},
+        "layer_gbs": round((fc1_work["bytes"] + fc2_work["bytes"]) / (ms_per_step * 1e-3) / 1e9, 1),
+        "layer_tflops": round((fc1_work["flops"] + fc2_work["flops"]) / (ms_per_step * 1e-3) / 1e12, 2),
+        "stage_ms": {k: round(v, 5) for k, v in stages.items()} if stages else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -344,6 +463,9 @@ def main():
         return
     if args.workload.startswith("gmm_"):
         main_gmm(args)
+        return
+    if args.workload.startswith("moe_"):
+        main_moe(args)
         return
     import numpy as np
     import torch

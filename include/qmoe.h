@@ -71,7 +71,13 @@ typedef enum {
   QMOE_F64 = 7   /* accepted by GroupedMatMul's type list; not implemented */
 } qmoe_dtype;
 
-typedef enum { QMOE_ACT_RELU = 0, QMOE_ACT_SWIGLU = 1 } qmoe_activation;
+typedef enum {
+  QMOE_ACT_RELU = 0,
+  QMOE_ACT_SWIGLU = 1,
+  QMOE_ACT_GELU = 2,     /* float MoE only */
+  QMOE_ACT_SILU = 3,     /* float MoE only */
+  QMOE_ACT_IDENTITY = 4  /* float MoE only */
+} qmoe_activation;
 
 typedef enum {
   QMOE_ROUTE_QMOE = 0, /* softmax over the k selected logits (QMoE manifest)      */
@@ -232,6 +238,88 @@ qmoe_status qmoe_grouped_matmul_debug(const qmoe_tensor* input, const qmoe_tenso
                                       const qmoe_tensor* group_indices, const qmoe_tensor* bias,
                                       const qmoe_tensor* output, void* workspace, size_t workspace_bytes,
                                       void* stream, void* const events[QMOE_GMM_EVENTS]);
+
+/* ------------------------------------------------------------------------
+ * Float MoE (com.microsoft.MoE README: Description, Inputs, Outputs,
+ * Attributes), float32 throughout:
+ *
+ *   p         = softmax over all E logits of token t
+ *   sel[t]    = the k largest logits, largest first, ties to the lower index
+ *   w[t, s]   = p[sel[t, s]], renormalised over the k when
+ *               normalize_routing_weights = 1
+ *   h         = W1[e] x[t] + b1[e]        fc1 [E, F, H], bias [E, F]
+ *   u3        = W3[e] x[t] + b3[e]        fc3 [E, I, H], bias [E, I]
+ *   a         = relu(h) | h Phi(h) (exact GELU) | h sigmoid(h) [* u3] |
+ *               g sigmoid(alpha g) (u + beta) | h
+ *   y         = W2[e] a + b2[e]            fc2 [E, H, I], bias [E, H]
+ *   out[t]    = sum_s w[t, s] y(sel[t, s])
+ *
+ * SwiGLU operands: swiglu_fusion 0: g = h, u = u3 (fc3 required);
+ * 1: g = h[2j], u = h[2j+1]; 2: g = h[j], u = h[I + j].  F = 2 I for
+ * swiglu with fusion 1 or 2, else F = I.  FC3 is read by swiglu with
+ * fusion 0 and (optionally) by silu, where it multiplies the result; other
+ * activations ignore it.  alpha and beta are read by swiglu only.
+ *
+ * Tensors: input [T, H] or [B, S, H]; router_probs [T, E]; output of
+ * input's shape; every tensor QMOE_F32 (else QMOE_ERR_DTYPE).  Biases and
+ * fc3 may be NULL; fc3_b needs fc3.  Limits (QMOE_ERR_UNSUPPORTED): E <=
+ * 1024, T * k < 2^30, F, H < 2^30.  Products and sums are float32 on the
+ * matrix cores (v_mfma_f32_16x16x4_f32); activations use float32 libm.
+ * Conventions as above; the output must not alias an input.
+ * ------------------------------------------------------------------------ */
+
+/* Attributes of the MoE README (Attributes table), defaults in brackets. */
+typedef struct {
+  int32_t k;                         /* [1]  1 <= k <= E                      */
+  int32_t activation_type;           /* [RELU] any qmoe_activation            */
+  int32_t swiglu_fusion;             /* [0]  0, 1 or 2                        */
+  float activation_alpha;            /* [1]  swiglu gate sigmoid slope         */
+  float activation_beta;             /* [0]  added to the swiglu linear branch */
+  int32_t normalize_routing_weights; /* [0]  0 or 1                           */
+  int32_t use_sparse_mixer;          /* [0]  1 is QMOE_ERR_UNSUPPORTED        */
+} qmoe_moe_attrs;
+
+/* Fill *a with the defaults listed above.  a must not be NULL. */
+void qmoe_moe_attrs_default(qmoe_moe_attrs* a);
+
+/* Contract check of the tables above (shapes, dtypes, attributes: ranks or
+ * extents QMOE_ERR_SHAPE, attribute values QMOE_ERR_ATTR).  Pure host code.
+ * output may be NULL to skip its check. */
+qmoe_status qmoe_moe_validate(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                              const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_experts_bias,
+                              const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_experts_bias,
+                              const qmoe_tensor* fc3_experts_weights, const qmoe_tensor* fc3_experts_bias,
+                              const qmoe_tensor* output, const qmoe_moe_attrs* attrs);
+
+/* Device workspace bytes of qmoe_moe_forward (validates first; 0 when
+ * T * H == 0). */
+qmoe_status qmoe_moe_workspace_size(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                                    const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_experts_bias,
+                                    const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_experts_bias,
+                                    const qmoe_tensor* fc3_experts_weights, const qmoe_tensor* fc3_experts_bias,
+                                    const qmoe_moe_attrs* attrs, size_t* bytes);
+
+/* Enqueue the float MoE on stream.  Device pointers: input, output and the
+ * weights 16-byte aligned, router_probs and biases 4-byte aligned
+ * (QMOE_ERR_ALIGN otherwise).  workspace as for qmoe_forward. */
+qmoe_status qmoe_moe_forward(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                             const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_experts_bias,
+                             const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_experts_bias,
+                             const qmoe_tensor* fc3_experts_weights, const qmoe_tensor* fc3_experts_bias,
+                             const qmoe_moe_attrs* attrs, const qmoe_tensor* output,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* As qmoe_moe_forward, also copying the routing results to the non-NULL
+ * buffers of *debug and recording its events at [0] before the router,
+ * [1] after the routing front end, [2] after FC1 (and FC3), [3] after the
+ * activation, [4] after FC2, [5] after the combine (when T * H > 0). */
+qmoe_status qmoe_moe_forward_debug(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                                   const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_experts_bias,
+                                   const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_experts_bias,
+                                   const qmoe_tensor* fc3_experts_weights, const qmoe_tensor* fc3_experts_bias,
+                                   const qmoe_moe_attrs* attrs, const qmoe_tensor* output,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   const qmoe_debug* debug);
 
 /* Static, human-readable name of a status code. */
 const char* qmoe_status_string(qmoe_status s);

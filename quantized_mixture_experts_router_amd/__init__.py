@@ -7,10 +7,11 @@ and the current stream.  The functions keep the C names:
     qmoe_abi_version, qmoe_attrs_default, qmoe_validate, qmoe_workspace_size,
     qmoe_forward, qmoe_forward_debug, qmoe_status_string,
     qmoe_grouped_matmul_workspace_size, qmoe_grouped_matmul,
-    qmoe_grouped_matmul_debug
+    qmoe_grouped_matmul_debug, qmoe_moe_attrs_default, qmoe_moe_validate,
+    qmoe_moe_workspace_size, qmoe_moe_forward, qmoe_moe_forward_debug
 
-plus ``forward`` and ``grouped_matmul`` (allocate output and workspace with
-torch, then call qmoe_forward / qmoe_grouped_matmul) for convenience.  The
+plus ``forward``, ``grouped_matmul`` and ``moe_forward`` (allocate output and
+workspace with torch, then call the entry point) for convenience.  The
 library is loaded on first use; a missing build raises immediately, there is
 no fallback.
 """
@@ -24,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmoe.so")
 
 QMOE_F32, QMOE_U8, QMOE_I32, QMOE_I64, QMOE_F16, QMOE_BF16, QMOE_F64 = 1, 2, 3, 4, 5, 6, 7
-QMOE_ACT = {"relu": 0, "swiglu": 1}
+QMOE_ACT = {"relu": 0, "swiglu": 1, "gelu": 2, "silu": 3, "identity": 4}
 QMOE_ROUTING = {"qmoe": 0, "moe": 1}
 STATUS = {0: "OK", 1: "NULL", 2: "SHAPE", 3: "ATTR", 4: "UNSUPPORTED", 5: "WORKSPACE", 6: "HIP",
           7: "DTYPE", 8: "ALIGN"}
@@ -42,6 +43,12 @@ class QmoeAttrs(ctypes.Structure):
                 ("normalize_routing_weights", ctypes.c_int32), ("routing", ctypes.c_int32),
                 ("use_sparse_mixer", ctypes.c_int32), ("weights_prepacked", ctypes.c_int32),
                 ("quant_type", ctypes.c_int32)]
+
+
+class QmoeMoeAttrs(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_int32), ("activation_type", ctypes.c_int32), ("swiglu_fusion", ctypes.c_int32),
+                ("activation_alpha", ctypes.c_float), ("activation_beta", ctypes.c_float),
+                ("normalize_routing_weights", ctypes.c_int32), ("use_sparse_mixer", ctypes.c_int32)]
 
 
 QMOE_STAGE_EVENTS = 6
@@ -94,6 +101,18 @@ def _lib():
         lib.qmoe_grouped_matmul_debug.argtypes = [T, T, T, T, T, ctypes.c_void_p, ctypes.c_size_t,
                                                   ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
         lib.qmoe_grouped_matmul_debug.restype = ctypes.c_int
+        MA = ctypes.POINTER(QmoeMoeAttrs)
+        lib.qmoe_moe_attrs_default.argtypes = [MA]
+        lib.qmoe_moe_attrs_default.restype = None
+        lib.qmoe_moe_validate.argtypes = [T] * 9 + [MA]
+        lib.qmoe_moe_validate.restype = ctypes.c_int
+        lib.qmoe_moe_workspace_size.argtypes = [T] * 8 + [MA, ctypes.POINTER(ctypes.c_size_t)]
+        lib.qmoe_moe_workspace_size.restype = ctypes.c_int
+        lib.qmoe_moe_forward.argtypes = [T] * 8 + [MA, T, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.qmoe_moe_forward.restype = ctypes.c_int
+        lib.qmoe_moe_forward_debug.argtypes = [T] * 8 + [MA, T, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                                         ctypes.POINTER(QmoeDebug)]
+        lib.qmoe_moe_forward_debug.restype = ctypes.c_int
         lib.qmoe_status_string.argtypes = [ctypes.c_int]
         lib.qmoe_status_string.restype = ctypes.c_char_p
         _lib_handle = lib
@@ -288,3 +307,89 @@ def grouped_matmul(input, weights, group_indices, bias=None, stream=None, worksp
 
 
 qmoe_grouped_matmul_debug = qmoe_grouped_matmul
+
+
+# ------------------------------------------------------------------ float MoE
+MOE_TENSORS = ("input", "router_probs", "fc1_experts_weights", "fc1_experts_bias", "fc2_experts_weights",
+               "fc2_experts_bias", "fc3_experts_weights", "fc3_experts_bias")
+
+
+def qmoe_moe_attrs_default() -> QmoeMoeAttrs:
+    a = QmoeMoeAttrs()
+    _lib().qmoe_moe_attrs_default(ctypes.byref(a))
+    return a
+
+
+def make_moe_attrs(attrs: Optional[dict] = None) -> QmoeMoeAttrs:
+    """qmoe_moe_attrs from a dict of the README's attribute names."""
+    a = qmoe_moe_attrs_default()
+    for key, val in (attrs or {}).items():
+        if key == "activation_type" and isinstance(val, str):
+            val = QMOE_ACT.get(val, 99)
+        setattr(a, key, val)
+    return a
+
+
+def _moe_refs(ts, data):
+    """Eight tensor arguments in C order from a dict (missing = NULL)."""
+    return [_ref(ts.get(n), data) for n in MOE_TENSORS]
+
+
+def _moe_a(attrs):
+    return attrs if isinstance(attrs, QmoeMoeAttrs) else make_moe_attrs(attrs)
+
+
+def qmoe_moe_validate(tensors: dict, attrs=None, output=None) -> int:
+    """Status code of the float MoE contract check.  Arrays may live anywhere."""
+    a = _moe_a(attrs)
+    return int(_lib().qmoe_moe_validate(*_moe_refs(tensors, False), _ref(output, False), ctypes.byref(a)))
+
+
+def qmoe_moe_workspace_size(tensors: dict, attrs=None) -> int:
+    a = _moe_a(attrs)
+    n = ctypes.c_size_t(0)
+    st = _lib().qmoe_moe_workspace_size(*_moe_refs(tensors, False), ctypes.byref(a), ctypes.byref(n))
+    if st != 0:
+        raise QmoeError(st, "qmoe_moe_workspace_size")
+    return int(n.value)
+
+
+def qmoe_moe_forward(tensors: dict, attrs, output, workspace, stream=None, debug: Optional[dict] = None) -> None:
+    """Enqueue the float MoE on ``stream``.  ``tensors`` maps the names of
+    MOE_TENSORS to contiguous device tensors (optional ones may be absent);
+    ``debug`` as for qmoe_forward."""
+    a = _moe_a(attrs)
+    wptr = workspace.data_ptr() if workspace is not None and workspace.numel() > 0 else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = [*_moe_refs(tensors, True), ctypes.byref(a), _ref(output, True), ctypes.c_void_p(wptr),
+            ctypes.c_size_t(wbytes), _stream_handle(stream)]
+    if debug is None:
+        st = _lib().qmoe_moe_forward(*args)
+        where = "qmoe_moe_forward"
+    else:
+        dbg = QmoeDebug()
+        for f in ("topk_idx", "topk_w", "counts", "offsets", "perm"):
+            t = debug.get(f)
+            setattr(dbg, f, t.data_ptr() if t is not None and t.numel() > 0 else None)
+        for i, ev in enumerate(debug.get("events") or ()):
+            dbg.events[i] = ev
+        st = _lib().qmoe_moe_forward_debug(*args, ctypes.byref(dbg))
+        where = "qmoe_moe_forward_debug"
+    if st != 0:
+        raise QmoeError(st, where)
+
+
+qmoe_moe_forward_debug = qmoe_moe_forward
+
+
+def moe_forward(tensors: dict, attrs=None, stream=None, workspace=None, output=None, debug=None):
+    """Allocate output (and workspace unless given) with torch, then qmoe_moe_forward."""
+    import torch
+    x = tensors["input"]
+    if output is None:
+        output = torch.empty_like(x)
+    need = qmoe_moe_workspace_size(tensors, attrs)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    qmoe_moe_forward(tensors, attrs, output, workspace, stream, debug)
+    return output

@@ -20,11 +20,13 @@ SOURCES = [
     "qmoe_plan.cpp",
     "qmoe_api.cpp",
     "qmoe_gmm.cpp",
+    "qmoe_moe.cpp",
     "kernels/route.hip",
     "kernels/gemm.hip",
     "kernels/stream.hip",
     "kernels/tiled.hip",
     "kernels/gmm.hip",
+    "kernels/moe.hip",
 ]
 
 ARCH = os.environ.get("QMOE_OFFLOAD_ARCH", "gfx950")

@@ -1,22 +1,30 @@
-// GroupedMatMul over float32 weights (ONNX GroupedMatMul-29, Summary):
+// Float32 grouped GEMM over group-sorted rows, shared by GroupedMatMul
+// (ONNX operator page "GroupedMatMul - 29", Summary) and the float MoE
+// operator's FC1, FC3 and FC2 (com.microsoft.MoE README, Inputs):
 //
-//   output[m, i, :] = input[m, :] @ weights[g, :, :] (+ bias[g, :]),
-//   g = group_indices[m, i]
+//   out[orow(p), n] = sum_k a[arow(p), k] * W[g](k, n)  (+ bias[g, n])
 //
-// The (m, i) pairs are the "slots" of the routing front end: their group
-// indices are sorted into group-major order by the same histogram / scan /
-// stable scatter kernels (route.hip), so that every 64-row tile multiplies
-// rows of one group by that group's [K, N] matrix, read once per tile.
-// Indices outside [0, G) are invalid input (the page leaves the result
-// undefined); they are gathered into an extra group G whose rows are written
-// as zeros, and no weight or bias outside the tensors is ever read.
+// for every sorted position p of a tile whose rows all belong to group g.
+// The rows come from the routing front end (route.hip): its stable
+// permutation perm maps sorted position -> slot id, and its tile table cuts
+// each group's positions into tiles.  Operand row arow(p) is
+// a_perm[p] / a_div (rows gathered from tokens) or p (rows already in sorted
+// order); output row orow(p) is perm[p] (by slot id) or p (sorted order).
+// W[g](k, n) is w[g][k][n] (KN layout, GroupedMatMul's weights [G, K, N]) or
+// w[g][n][k] (NK layout, the MoE weights whose rows are output features).
+// Tiles of group g >= G write zero rows (GroupedMatMul's invalid indices).
 //
-// The tile GEMM runs on v_mfma_f32_16x16x4_f32 (fp32 operands, fp32
-// accumulation): products are exact in fp32, like the definition's
-// float32 arithmetic.  A workgroup of 4 wavefronts computes a 64 x 128 tile
-// (2 x 2 wavefronts of 32 x 64); each 16-deep K step of both operands is
-// staged in LDS (double buffered, the next step's loads in flight during the
-// current step's matrix instructions).
+// All products and sums are float32 on v_mfma_f32_16x16x4_f32 (fp32 operands,
+// fp32 accumulation); the bias is added last.
+//
+// Two kernels:
+//  * qmoe_gmm_f32: LDS-tiled, 64-row x 128-column tiles, 4 wavefronts of
+//    32 x 64, both operands of each 16-deep K step staged in LDS (double
+//    buffered, the next step's loads in flight during the matrix
+//    instructions).  Any K, N, alignment (scalar loads off the vector path).
+//  * qmoe_gmm_f32_rows16: weight streaming for tiles of at most 16 rows: each
+//    wavefront owns 64 columns of one tile and streams that strip of W[g]
+//    from HBM straight into matrix-core operands (no LDS, no barriers).
 #include "common.hpp"
 #include "launch.h"
 
@@ -24,12 +32,13 @@ namespace qmoe {
 
 namespace {
 
-constexpr int kGM = 64;            // tile rows (group-sorted (m, i) pairs)
+constexpr int kGM = 64;            // tile rows
 constexpr int kGN = 128;           // tile columns
 constexpr int kGK = 16;            // K per step
 constexpr int kGThreads = 256;
-constexpr int kAStride = kGK + 1;  // LDS floats per A row (bank spread)
-constexpr int kBStride = kGN + 16; // LDS floats per B row (bank spread)
+constexpr int kAStride = kGK + 1;  // LDS floats per A row, and per B column in NK layout (bank spread)
+constexpr int kBStride = kGN + 16; // LDS floats per B row in KN layout (bank spread)
+constexpr int kBBuf = kGK * kBStride > kGN * kAStride ? kGK * kBStride : kGN * kAStride;
 
 }  // namespace
 
@@ -43,48 +52,54 @@ __global__ void __launch_bounds__(256) qmoe_gmm_index(const IT* __restrict__ idx
   out[j] = (v >= 0 && v < (IT)G) ? (int)v : G;
 }
 
-// VEC: K and N are multiples of 4 and x, w 16-byte aligned (16-byte loads).
-template <bool VEC>
-__global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const float* __restrict__ x, const float* __restrict__ w,
-                                                          const float* __restrict__ bias, const int* __restrict__ perm,
-                                                          const int* __restrict__ tiles, const int* __restrict__ ntiles,
-                                                          int nblk, int S, int K, int N, int G,
-                                                          float* __restrict__ out) {
+__device__ __forceinline__ int gmm_arow(const F32Gemm& g, int p) { return g.a_perm ? g.a_perm[p] / g.a_div : p; }
+__device__ __forceinline__ int gmm_orow(const F32Gemm& g, int p) { return g.out_by_slot ? g.perm[p] : p; }
+
+// VEC: 16-byte loads (K % 4 == 0, a and w 16-byte aligned; KN also N % 4 == 0).
+template <bool NK, bool VEC>
+__global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const F32Gemm g, int nblk) {
   __shared__ __attribute__((aligned(16))) float sa[2][kGM * kAStride];
-  __shared__ __attribute__((aligned(16))) float sb[2][kGK * kBStride];
-  __shared__ int s_slot[kGM];
+  __shared__ __attribute__((aligned(16))) float sb[2][kBBuf];
+  __shared__ int s_arow[kGM];
+  __shared__ int s_orow[kGM];
   // one workgroup per (tile, 128-column block); column blocks of a tile are
-  // adjacent, so they run together and share its input rows in L2
+  // adjacent, so they run together and share its operand rows in L2
   const int tile = blockIdx.x / nblk;
-  if (tile >= ntiles[0]) return;
-  const int g = tiles[4 * tile + 0];
-  const int p0 = tiles[4 * tile + 1];
-  const int rows = tiles[4 * tile + 2];
+  if (tile >= g.ntiles[0]) return;
+  const int grp = g.tiles[4 * tile + 0];
+  const int p0 = g.tiles[4 * tile + 1];
+  const int rows = g.tiles[4 * tile + 2];
   const int n0 = (blockIdx.x % nblk) * kGN;
+  const int K = g.K, N = g.N;
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int col = lane & 15, kq = lane >> 4;
 
-  if (tid < kGM) s_slot[tid] = perm[p0 + min(tid, rows - 1)];
+  if (tid < kGM) {
+    const int p = p0 + min(tid, rows - 1);
+    s_arow[tid] = gmm_arow(g, p);
+    s_orow[tid] = gmm_orow(g, p);
+  }
   __syncthreads();
 
-  if (g >= G) {
-    // invalid group index: zero rows
+  if (grp >= g.G) {
     for (int idx = tid; idx < rows * kGN; idx += kGThreads) {
       const int rr = idx / kGN, c = idx % kGN;
-      if (n0 + c < N) out[(long)s_slot[rr] * N + n0 + c] = 0.f;
+      if (n0 + c < N) g.out[(long)s_orow[rr] * N + n0 + c] = 0.f;
     }
     return;
   }
 
   // Global -> register staging of one K step.  A: row tid / 4, four k from
-  // 4 * (tid % 4); B: k row tid / 16, eight columns from 8 * (tid % 16).
-  // Elements past K or N are zero; rows past the tile re-read a valid row.
-  const float* arow = x + (long)(s_slot[tid >> 2] / S) * K;
-  const float* wg = w + (long)g * K * N;
+  // 4 * (tid % 4).  B, KN: k row tid / 16, eight columns from 8 * (tid % 16);
+  // NK: column tid / 2, eight k from 8 * (tid % 2).  Elements past K or N
+  // are zero; rows past the tile re-read a valid row.
+  const float* arow = g.a + (long)s_arow[tid >> 2] * K;
+  const float* wg = g.w + (long)grp * K * N;
   const int ak = (tid & 3) * 4;
-  const int bk = tid >> 4, bn = (tid & 15) * 8;
+  const int bk = NK ? (tid & 1) * 8 : tid >> 4;
+  const int bn = NK ? tid >> 1 : (tid & 15) * 8;
   f32x4 ra;
   f32x4 rb[2];
   auto load = [&](int kt) {
@@ -95,16 +110,31 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const float* __restric
 #pragma unroll
       for (int i = 0; i < 4; ++i) ra[i] = k0 + ak + i < K ? arow[k0 + ak + i] : 0.f;
     }
-    const int kk = k0 + bk;
-    const float* brow = wg + (long)min(kk, K - 1) * N;
+    if (NK) {
+      const int n = n0 + bn;
+      const float* brow = wg + (long)min(n, N - 1) * K;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n = n0 + bn + 4 * h;
-      if (VEC && kk < K && n + 4 <= N) {
-        rb[h] = *(const f32x4*)(brow + n);
-      } else {
+      for (int h = 0; h < 2; ++h) {
+        const int kk = k0 + bk + 4 * h;
+        if (VEC && n < N && kk + 4 <= K) {
+          rb[h] = *(const f32x4*)(brow + kk);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rb[h][i] = (kk < K && n + i < N) ? brow[n + i] : 0.f;
+          for (int i = 0; i < 4; ++i) rb[h][i] = (n < N && kk + i < K) ? brow[kk + i] : 0.f;
+        }
+      }
+    } else {
+      const int kk = k0 + bk;
+      const float* brow = wg + (long)min(kk, K - 1) * N;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = n0 + bn + 4 * h;
+        if (VEC && kk < K && n + 4 <= N) {
+          rb[h] = *(const f32x4*)(brow + n);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rb[h][i] = (kk < K && n + i < N) ? brow[n + i] : 0.f;
+        }
       }
     }
   };
@@ -112,9 +142,18 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const float* __restric
     float* a = sa[buf] + (tid >> 2) * kAStride + ak;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = ra[i];
-    float* b = sb[buf] + bk * kBStride + bn;
-    *(f32x4*)b = rb[0];
-    *(f32x4*)(b + 4) = rb[1];
+    if (NK) {
+      // B column bn, k from bk: the same row layout as A
+      float* b = sb[buf] + bn * kAStride + bk;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[4 * h + i] = rb[h][i];
+    } else {
+      float* b = sb[buf] + bk * kBStride + bn;
+      *(f32x4*)b = rb[0];
+      *(f32x4*)(b + 4) = rb[1];
+    }
   };
 
   f32x4 acc[2][4];
@@ -142,7 +181,10 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const float* __restric
 #pragma unroll
       for (int ms = 0; ms < 2; ++ms) av[ms] = a[(wm * 32 + ms * 16 + col) * kAStride + k4 * 4 + kq];
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns) bv[ns] = b[(k4 * 4 + kq) * kBStride + wn * 64 + ns * 16 + col];
+      for (int ns = 0; ns < 4; ++ns) {
+        const int c = wn * 64 + ns * 16 + col;
+        bv[ns] = NK ? b[c * kAStride + k4 * 4 + kq] : b[(k4 * 4 + kq) * kBStride + c];
+      }
 #pragma unroll
       for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
@@ -159,78 +201,99 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const float* __restric
   for (int ns = 0; ns < 4; ++ns) {
     const int c = n0 + wn * 64 + ns * 16 + col;
     if (c >= N) continue;
-    const float bv = bias ? bias[(long)g * N + c] : 0.f;
+    const float bv = g.bias ? g.bias[(long)grp * N + c] : 0.f;
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = wm * 32 + ms * 16 + 4 * kq + i;
-        if (rr < rows) out[(long)s_slot[rr] * N + c] = acc[ms][ns][i] + bv;
+        if (rr < rows) g.out[(long)s_orow[rr] * N + c] = acc[ms][ns][i] + bv;
       }
   }
 }
 
-// Weight-streaming variant for groups of at most 16 rows (16-row tiles):
-// each wavefront owns a 64-column strip of one tile and streams that strip of
-// the group's [K, N] weights from HBM straight into matrix-core operands, with
-// no LDS and no barriers.  The 16 columns of MFMA block i are the columns
-// n0 + 4c + i (c = 0..15), so one 16-byte load per lane fetches a 256-byte
-// row segment serving all four blocks, and the four MFMAs of one 16-deep K
-// group take k = 16 kg + 4 kq + j (j = 0..3) in lane group kq: one 16-byte
-// load of the input row covers them.  kD K groups of loads stay in flight
-// ahead of the matrix instructions.  Requires K % 4 == 0, N % 4 == 0 and
-// 16-byte aligned x, w, bias and out.
-constexpr int kSD = 4;  // K groups (16 deep) of loads in flight per wavefront
+// Weight-streaming variant for tiles of at most 16 rows.  The four MFMAs of
+// one 16-deep K group take k = 16 kg + 4 kq + j (j = 0..3) in lane group kq,
+// so one 16-byte load of the operand row covers them.  Columns of MFMA block
+// i (c = 0..15):
+//   KN: n0 + 4c + i: one 16-byte load per lane and k row fetches a 256-byte
+//       row segment serving all four blocks, and the results leave as
+//       16-byte stores;
+//   NK: n0 + 16i + c: one 16-byte load per lane and block fetches the four
+//       k of its weight row.
+// kSD K groups of loads stay in flight ahead of the matrix instructions.
+// Requires K % 4 == 0 and 16-byte aligned a, w (KN: also N % 4 == 0 and
+// 16-byte aligned bias and out).
+constexpr int kSD = 4;
 
-__global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const float* __restrict__ x, const float* __restrict__ w,
-                                                           const float* __restrict__ bias, const int* __restrict__ perm,
-                                                           const int* __restrict__ tiles,
-                                                           const int* __restrict__ ntiles, int nblk, int S, int K,
-                                                           int N, int G, float* __restrict__ out) {
+template <bool NK>
+__global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const F32Gemm g, int nblk) {
   const int tile = blockIdx.x / nblk;
-  if (tile >= ntiles[0]) return;
-  const int g = tiles[4 * tile + 0];
-  const int p0 = tiles[4 * tile + 1];
-  const int rows = tiles[4 * tile + 2];
+  if (tile >= g.ntiles[0]) return;
+  const int grp = g.tiles[4 * tile + 0];
+  const int p0 = g.tiles[4 * tile + 1];
+  const int rows = g.tiles[4 * tile + 2];
+  const int K = g.K, N = g.N;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int n0 = (blockIdx.x % nblk) * 256 + wave * 64;
   if (n0 >= N) return;  // whole wavefront: no barriers below
   const int c = lane & 15, kq = lane >> 4;
-  const int n = n0 + 4 * c;
-  const bool col_ok = n < N;  // N % 4 == 0: all four columns or none
-  const int row = lane & 15;  // A operand row of this lane
-  const int slot_a = perm[p0 + min(row, rows - 1)];
-  if (g >= G) {
-    // invalid group index: zero rows
-    if (col_ok) {
+  // output rows of this lane: 4 kq + t
+  int orow[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 4 * kq + t;
-        if (r < rows) *(f32x4*)(out + (long)perm[p0 + r] * N + n) = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 4; ++t) orow[t] = 4 * kq + t < rows ? gmm_orow(g, p0 + 4 * kq + t) : -1;
+  // columns of this lane: KN n0 + 4c + i (all or none valid, N % 4 == 0);
+  // NK n0 + 16i + c (each checked)
+  bool cok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cok[i] = (NK ? n0 + 16 * i + c : n0 + 4 * c) < N;
+  if (grp >= g.G) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (orow[t] < 0) continue;
+      float* o = g.out + (long)orow[t] * N;
+      if (NK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (cok[i]) o[n0 + 16 * i + c] = 0.f;
+      } else if (cok[0]) {
+        *(f32x4*)(o + n0 + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
     return;
   }
-  const float* arow = x + (long)(slot_a / S) * K + 4 * kq;
-  // lanes past N re-read column 0 (results discarded)
-  const float* wcol = w + (long)g * K * N + (col_ok ? n : 0) + (long)(4 * kq) * N;
+  const float* arow = g.a + (long)gmm_arow(g, p0 + min(c, rows - 1)) * K + 4 * kq;
+  const float* wg = g.w + (long)grp * K * N;
+  // weight pointers of this lane at k = 4 kq (NK: one per block; KN: k row
+  // 4 kq, the rows below it N apart); lanes past N re-read a valid column
+  const float* wp[NK ? 4 : 1];
+  if (NK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wp[i] = wg + (long)min(n0 + 16 * i + c, N - 1) * K + 4 * kq;
+  } else {
+    wp[0] = wg + (cok[0] ? n0 + 4 * c : 0) + (long)(4 * kq) * N;
+  }
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nfull = K / 16;  // K groups without a tail
+  // KN: rb[d][j] = columns n0 + 4c .. + 3 at k row 16 kg + 4 kq + j
+  // NK: rb[d][i] = k 16 kg + 4 kq .. + 3 of column n0 + 16 i + c
   f32x4 ra[kSD], rb[kSD][4];
   auto load = [&](int slot, int kg) {
     const long k = (long)kg * 16;
     ra[slot] = *(const f32x4*)(arow + k);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rb[slot][j] = *(const f32x4*)(wcol + (k + j) * N);
+    for (int i = 0; i < 4; ++i) rb[slot][i] = NK ? *(const f32x4*)(wp[i] + k) : *(const f32x4*)(wp[0] + (k + i) * N);
   };
   auto mma = [&](int slot) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[slot][j], rb[slot][j][i], acc[i], 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[slot][j], NK ? rb[slot][i][j] : rb[slot][j][i], acc[i], 0,
+                                                      0, 0);
   };
   // Branch-free pipeline (exact load counts for the waits): past the last
   // full group the loads repeat it, and those values are never used.
@@ -251,23 +314,35 @@ __global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const float* __restri
   }
   if (nfull * 16 < K) {
     // tail group: k past K reads as zero on both operands
-    const int k0 = nfull * 16 + 4 * kq;
+    const int kb = nfull * 16;
+    const int k0 = kb + 4 * kq;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = k0 + j < K;
-      ra[0][j] = ok ? arow[nfull * 16 + j] : 0.f;
-      rb[0][j] = ok ? *(const f32x4*)(wcol + ((long)nfull * 16 + j) * N) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < 4; ++j) ra[0][j] = k0 + j < K ? arow[kb + j] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = k0 + j < K;
+        // NK: element j of column i; KN: element i of k row j (pointer of row j)
+        if (NK) rb[0][i][j] = ok ? wp[i][kb + j] : 0.f;
+        else rb[0][j][i] = ok ? wp[0][(long)(kb + j) * N + i] : 0.f;
+      }
     mma(0);
   }
-  if (!col_ok) return;
-  const f32x4 bv = bias ? *(const f32x4*)(bias + (long)g * N + n) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int r = 4 * kq + t;
-    if (r < rows) {
-      const f32x4 v = {acc[0][t] + bv[0], acc[1][t] + bv[1], acc[2][t] + bv[2], acc[3][t] + bv[3]};
-      *(f32x4*)(out + (long)perm[p0 + r] * N + n) = v;
+    if (orow[t] < 0) continue;
+    float* o = g.out + (long)orow[t] * N;
+    if (NK) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + 16 * i + c;
+        if (cok[i]) o[n] = acc[i][t] + (g.bias ? g.bias[(long)grp * N + n] : 0.f);
+      }
+    } else if (cok[0]) {
+      const int n = n0 + 4 * c;
+      const f32x4 bv = g.bias ? *(const f32x4*)(g.bias + (long)grp * N + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)(o + n) = f32x4{acc[0][t] + bv[0], acc[1][t] + bv[1], acc[2][t] + bv[2], acc[3][t] + bv[3]};
     }
   }
 }
@@ -275,14 +350,13 @@ __global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const float* __restri
 int gmm_tile_rows() { return kGM; }
 int gmm_rows16_tile_rows() { return 16; }
 
-hipError_t launch_gmm_rows16(const float* x, const float* w, const float* bias, const int* perm, const int* tiles,
-                             const int* ntiles, int max_tiles, int S, int K, int N, int G, float* out,
-                             hipStream_t st) {
-  if (max_tiles <= 0 || N <= 0) return hipSuccess;
-  if (K % 4 != 0 || N % 4 != 0) return hipErrorInvalidValue;
-  const int nblk = (N + 255) / 256;
+hipError_t launch_gmm_rows16(const F32Gemm& g, bool nk, int max_tiles, hipStream_t st) {
+  if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  if (g.K % 4 != 0 || (!nk && g.N % 4 != 0)) return hipErrorInvalidValue;
+  const int nblk = (g.N + 255) / 256;
   const dim3 grid((unsigned)((long)max_tiles * nblk)), block(256);
-  hipLaunchKernelGGL(qmoe_gmm_f32_rows16, grid, block, 0, st, x, w, bias, perm, tiles, ntiles, nblk, S, K, N, G, out);
+  if (nk) hipLaunchKernelGGL(qmoe_gmm_f32_rows16<true>, grid, block, 0, st, g, nblk);
+  else hipLaunchKernelGGL(qmoe_gmm_f32_rows16<false>, grid, block, 0, st, g, nblk);
   return hipGetLastError();
 }
 
@@ -294,17 +368,18 @@ hipError_t launch_gmm_index(const void* idx, bool idx64, long n, int G, int* out
   return hipGetLastError();
 }
 
-hipError_t launch_gmm_f32(const float* x, const float* w, const float* bias, const int* perm, const int* tiles,
-                          const int* ntiles, int max_tiles, int S, int K, int N, int G, float* out, bool vec,
-                          hipStream_t st) {
-  if (max_tiles <= 0 || N <= 0) return hipSuccess;
-  const int nblk = (N + kGN - 1) / kGN;
+hipError_t launch_gmm_f32(const F32Gemm& g, bool nk, bool vec, int max_tiles, hipStream_t st) {
+  if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  if (vec && (g.K % 4 != 0 || (!nk && g.N % 4 != 0))) return hipErrorInvalidValue;
+  const int nblk = (g.N + kGN - 1) / kGN;
   const dim3 grid((unsigned)((long)max_tiles * nblk)), block(kGThreads);
-  if (vec && (K % 4 != 0 || N % 4 != 0)) return hipErrorInvalidValue;
-  if (vec)
-    hipLaunchKernelGGL(qmoe_gmm_f32<true>, grid, block, 0, st, x, w, bias, perm, tiles, ntiles, nblk, S, K, N, G, out);
-  else
-    hipLaunchKernelGGL(qmoe_gmm_f32<false>, grid, block, 0, st, x, w, bias, perm, tiles, ntiles, nblk, S, K, N, G, out);
+  if (nk) {
+    if (vec) hipLaunchKernelGGL((qmoe_gmm_f32<true, true>), grid, block, 0, st, g, nblk);
+    else hipLaunchKernelGGL((qmoe_gmm_f32<true, false>), grid, block, 0, st, g, nblk);
+  } else {
+    if (vec) hipLaunchKernelGGL((qmoe_gmm_f32<false, true>), grid, block, 0, st, g, nblk);
+    else hipLaunchKernelGGL((qmoe_gmm_f32<false, false>), grid, block, 0, st, g, nblk);
+  }
   return hipGetLastError();
 }
 

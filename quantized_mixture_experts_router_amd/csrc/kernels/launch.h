@@ -85,21 +85,40 @@ hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, i
 hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, int splits, float* out,
                           hipStream_t st);
 
-// GroupedMatMul (see gmm.hip).  Index conversion: out[j] = idx[j] when in
-// [0, G), else G.  Tile GEMM over the permutation of G + 1 groups with
-// gmm_tile_rows()-row tiles; tiles of group G write zero rows.  vec: K, N
-// multiples of 4 and x, w 16-byte aligned.
-int gmm_tile_rows();
+// Float32 grouped GEMM over group-sorted rows (see gmm.hip), shared by
+// GroupedMatMul and the float MoE projections.
+struct F32Gemm {
+  const float* a;       // operand rows, K floats each
+  const int* a_perm;    // operand row of sorted position p: a_perm[p] / a_div; nullptr: row p
+  int a_div;
+  const float* w;       // KN layout [G][K][N] or NK layout [G][N][K]
+  const float* bias;    // [G][N] or nullptr
+  const int* perm;      // sorted position -> slot id
+  int out_by_slot;      // output row perm[p] (1) or p (0)
+  const int* tiles;     // [max_tiles][4] = group, first position, rows, 0
+  const int* ntiles;
+  int K, N, G;          // tiles of group >= G write zero rows
+  float* out;           // N floats per row
+};
+
+// Index conversion: out[j] = idx[j] when in [0, G), else G.
 hipError_t launch_gmm_index(const void* idx, bool idx64, long n, int G, int* out, hipStream_t st);
-hipError_t launch_gmm_f32(const float* x, const float* w, const float* bias, const int* perm, const int* tiles,
-                          const int* ntiles, int max_tiles, int S, int K, int N, int G, float* out, bool vec,
-                          hipStream_t st);
-// Weight-streaming variant for tiles of at most gmm_rows16_tile_rows() rows:
-// K, N multiples of 4; x, w, bias, out 16-byte aligned.
+// LDS-tiled kernel: tiles of at most gmm_tile_rows() rows, any K / N; vec:
+// K % 4 == 0, a and w 16-byte aligned (KN: also N % 4 == 0).
+int gmm_tile_rows();
+hipError_t launch_gmm_f32(const F32Gemm& g, bool nk, bool vec, int max_tiles, hipStream_t st);
+// Weight-streaming kernel: tiles of at most gmm_rows16_tile_rows() rows;
+// K % 4 == 0, a and w 16-byte aligned (KN: also N % 4 == 0 and 16-byte
+// aligned bias and out).
 int gmm_rows16_tile_rows();
-hipError_t launch_gmm_rows16(const float* x, const float* w, const float* bias, const int* perm, const int* tiles,
-                             const int* ntiles, int max_tiles, int S, int K, int N, int G, float* out,
-                             hipStream_t st);
+hipError_t launch_gmm_rows16(const F32Gemm& g, bool nk, int max_tiles, hipStream_t st);
+
+// Float MoE activation pass (see moe.hip): act[p][j], p < S, j < I, from
+// FC1 rows h (F floats) and FC3 rows u3 (I floats, or nullptr).  Codes
+// match qmoe_activation.
+enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1, MOE_ACT_GELU = 2, MOE_ACT_SILU = 3, MOE_ACT_IDENTITY = 4 };
+hipError_t launch_moe_act(int act_type, const float* h, const float* u3, long S, int I, int F, int fusion,
+                          float alpha, float beta, float* act, hipStream_t st);
 
 hipError_t launch_fill_zero(float* out, long n, hipStream_t st);
 

@@ -157,17 +157,23 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
   if (mark(1) != hipSuccess) return QMOE_ERR_HIP;
   const bool vec = p.K % 4 == 0 && p.N % 4 == 0 && aligned_to(input->data, 16) && aligned_to(weights->data, 16);
   const bool stream16 = p.rows16 && vec && aligned_to(output->data, 16) && (!bias || aligned_to(bias->data, 16));
-  if (stream16) {
-    if (launch_gmm_rows16(static_cast<const float*>(input->data), static_cast<const float*>(weights->data),
-                          bias ? static_cast<const float*>(bias->data) : nullptr, perm, tiles, ntiles,
-                          (int)p.max_tiles, (int)p.S, (int)p.K, (int)p.N, G,
-                          static_cast<float*>(const_cast<void*>(output->data)), s) != hipSuccess)
-      return QMOE_ERR_HIP;
-  } else if (launch_gmm_f32(static_cast<const float*>(input->data), static_cast<const float*>(weights->data),
-                     bias ? static_cast<const float*>(bias->data) : nullptr, perm, tiles, ntiles, (int)p.max_tiles,
-                     (int)p.S, (int)p.K, (int)p.N, G, static_cast<float*>(const_cast<void*>(output->data)), vec,
-                     s) != hipSuccess)
-    return QMOE_ERR_HIP;
+  F32Gemm g{};
+  g.a = static_cast<const float*>(input->data);
+  g.a_perm = perm;  // slot id m * S + i -> token row m
+  g.a_div = (int)p.S;
+  g.w = static_cast<const float*>(weights->data);
+  g.bias = bias ? static_cast<const float*>(bias->data) : nullptr;
+  g.perm = perm;
+  g.out_by_slot = 1;  // output row m * S + i of [M, S, N]
+  g.tiles = tiles;
+  g.ntiles = ntiles;
+  g.K = (int)p.K;
+  g.N = (int)p.N;
+  g.G = G;
+  g.out = static_cast<float*>(const_cast<void*>(output->data));
+  const hipError_t e = stream16 ? launch_gmm_rows16(g, false, (int)p.max_tiles, s)
+                                : launch_gmm_f32(g, false, vec, (int)p.max_tiles, s);
+  if (e != hipSuccess) return QMOE_ERR_HIP;
   if (mark(2) != hipSuccess) return QMOE_ERR_HIP;
   return QMOE_OK;
 }

@@ -181,3 +181,97 @@ def gmm_generate(w: GmmWorkload, seed: Optional[int] = None, index_dtype=np.int6
     for m in range(w.M):
         idx[m] = rng.choice(w.G, size=w.S, replace=w.S > w.G, p=p)
     return {"input": x, "weights": wts, "group_indices": idx, "bias": b}
+
+
+# ---------------------------------------------------------------- float MoE
+# Float workloads of the MoE operator (com.microsoft.MoE README): the decode
+# and fine-grained layers above with float32 weights and biases.
+# Draw order (one default_rng(seed)): input ~ N(0, 1); router logits ~
+# N(0, sigma) (plus -2 ln(rank) with rank = e + 1 when zipf is set); fc1
+# weights ~ N(0, 1) / sqrt(H); fc1 bias ~ N(0, 1) * 0.1; fc2 weights ~
+# N(0, 1) / sqrt(I); fc2 bias ~ N(0, 1) * 0.1; fc3 weights ~ N(0, 1) / sqrt(H);
+# fc3 bias ~ N(0, 1) * 0.1 (biases and fc3 only when used).
+@dataclass(frozen=True)
+class MoeWorkload:
+    name: str
+    input_shape: Tuple[int, ...]
+    experts: int
+    inter: int
+    k: int
+    activation: str = "swiglu"
+    fusion: int = 1
+    bias: bool = True
+    fc3: bool = False
+    zipf: bool = False
+    logit_sigma: float = 1.0
+    normalize: int = 0
+    alpha: float = 1.0
+    beta: float = 0.0
+    seed: int = 0
+
+    @property
+    def hidden(self) -> int:
+        return self.input_shape[-1]
+
+    @property
+    def tokens(self) -> int:
+        t = 1
+        for d in self.input_shape[:-1]:
+            t *= d
+        return t
+
+    @property
+    def fc1_rows(self) -> int:
+        fused = self.activation == "swiglu" and self.fusion in (1, 2)
+        return (2 if fused else 1) * self.inter
+
+    def attrs(self) -> dict:
+        return dict(k=self.k, activation_type=self.activation, swiglu_fusion=self.fusion,
+                    activation_alpha=self.alpha, activation_beta=self.beta,
+                    normalize_routing_weights=self.normalize)
+
+    def describe(self) -> dict:
+        d = asdict(self)
+        d["tokens"] = self.tokens
+        return d
+
+
+MOE_WORKLOADS = {
+    "moe_decode": MoeWorkload("moe_decode", (16, 4096), 8, 14336, 2),
+    "moe_fine": MoeWorkload("moe_fine", (2048, 2048), 64, 1408, 6, zipf=True),
+}
+
+
+def moe_generate(w: MoeWorkload, seed: Optional[int] = None) -> dict:
+    """Draw the inputs of ``w`` in the order above; keys are the operator's
+    input names (absent optional inputs are None)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    T, H, E, I, F = w.tokens, w.hidden, w.experts, w.inter, w.fc1_rows
+
+    def normal(shape, scale):
+        a = rng.standard_normal(shape, dtype=np.float32)
+        a *= np.float32(scale)
+        return a
+
+    x = rng.standard_normal(tuple(w.input_shape), dtype=np.float32)
+    logits = rng.standard_normal((T, E), dtype=np.float64) * w.logit_sigma
+    if w.zipf:
+        logits = logits + (-2.0 * np.log(np.arange(1, E + 1, dtype=np.float64)))[None, :]
+    logits = logits.astype(np.float32)
+    fc1 = normal((E, F, H), 1.0 / np.sqrt(max(H, 1)))
+    fc1_b = normal((E, F), 0.1) if w.bias else None
+    fc2 = normal((E, H, I), 1.0 / np.sqrt(max(I, 1)))
+    fc2_b = normal((E, H), 0.1) if w.bias else None
+    fc3 = normal((E, I, H), 1.0 / np.sqrt(max(H, 1))) if w.fc3 else None
+    fc3_b = normal((E, I), 0.1) if w.fc3 and w.bias else None
+    return {"input": x, "router_probs": logits, "fc1_experts_weights": fc1, "fc1_experts_bias": fc1_b,
+            "fc2_experts_weights": fc2, "fc2_experts_bias": fc2_b, "fc3_experts_weights": fc3,
+            "fc3_experts_bias": fc3_b}
+
+
+def moe_random_case(rng: np.random.Generator, *, tokens_shape, hidden, experts, inter, k, activation="relu",
+                    fusion=0, bias=True, fc3=False, normalize=0, alpha=1.0, beta=0.0, logit_sigma=1.0) -> tuple:
+    """A small random float MoE case for sweeps; returns (MoeWorkload, arrays)."""
+    w = MoeWorkload("sweep", tuple(tokens_shape) + (hidden,), experts, inter, k, activation, fusion, bias, fc3,
+                    logit_sigma=logit_sigma, normalize=normalize, alpha=alpha, beta=beta)
+    return w, moe_generate(w, seed=int(rng.integers(0, 2**31 - 1)))

@@ -214,3 +214,64 @@ def test_grouped_matmul_null_arguments(lib):
     # missing output descriptor, then a missing device pointer
     assert lib.qmoe_grouped_matmul(*refs[:4], None, None, 0, None) == 1
     assert lib.qmoe_grouped_matmul(*refs, None, 1 << 20, None) == 1
+
+
+# ---------------------------------------------------------------- float MoE
+def test_moe_attribute_defaults_match_readme(lib):
+    a = qm.qmoe_moe_attrs_default()
+    # MoE README, Attributes table
+    assert a.k == 1 and a.activation_type == 0 and a.swiglu_fusion == 0
+    assert a.activation_alpha == 1.0 and a.activation_beta == 0.0
+    assert a.normalize_routing_weights == 0 and a.use_sparse_mixer == 0
+
+
+def _moe_tensors(a):
+    return {"input": a["x"], "router_probs": a["logits"], "fc1_experts_weights": a["fc1_w"],
+            "fc1_experts_bias": a["fc1_b"], "fc2_experts_weights": a["fc2_w"], "fc2_experts_bias": a["fc2_b"],
+            "fc3_experts_weights": a["fc3_w"], "fc3_experts_bias": a["fc3_b"]}
+
+
+def test_moe_validate_agrees_with_oracle(lib):
+    from test_oracle_moe import CONTRACT, _case
+    from oracle import moe_oracle as MO
+    for name, mut, over, kind in CONTRACT:
+        rng = np.random.default_rng(9)
+        a, attrs = _case(rng)
+        mut(a)
+        attrs = dict(attrs, **over)
+        with pytest.raises(Q.ContractError) as ei:
+            MO.moe_validate(**a, attrs=attrs)
+        assert ei.value.kind == kind
+        assert qm.qmoe_moe_validate(_moe_tensors(a), attrs) == KIND[kind], name
+    # accepted combinations, including unused FC3 and both fused layouts
+    rng = np.random.default_rng(10)
+    for act, fusion, fc3 in [("relu", 2, True), ("gelu", 0, True), ("swiglu", 1, False), ("swiglu", 2, False),
+                             ("swiglu", 0, True), ("silu", 0, False), ("identity", 1, False)]:
+        a, attrs = _case(rng, act=act, fusion=fusion, fc3=fc3)
+        MO.moe_validate(**a, attrs=attrs)
+        assert qm.qmoe_moe_validate(_moe_tensors(a), attrs, output=a["x"]) == 0, (act, fusion, fc3)
+
+
+def test_moe_dtype_output_and_empty(lib):
+    from test_oracle_moe import _case
+    rng = np.random.default_rng(11)
+    a, attrs = _case(rng)
+    t = _moe_tensors(a)
+    assert qm.qmoe_moe_validate(dict(t, fc2_experts_bias=t["fc2_experts_bias"].astype(np.float64)), attrs) == 7
+    assert qm.qmoe_moe_validate(t, attrs, output=np.zeros((5, 7), np.float32)) == 2
+    # T == 0 and H == 0 need no workspace; I == 0 is in contract
+    a0, attrs0 = _case(rng, T=0)
+    assert qm.qmoe_moe_workspace_size(_moe_tensors(a0), attrs0) == 0
+    aI, attrsI = _case(rng, I=0)
+    assert qm.qmoe_moe_validate(_moe_tensors(aI), attrsI) == 0
+    assert qm.qmoe_moe_workspace_size(_moe_tensors(aI), attrsI) > 0
+    # E above the routing kernels' limit
+    aE, attrsE = _case(rng, E=1025, T=2, H=4, I=4)
+    assert qm.qmoe_moe_validate(_moe_tensors(aE), attrsE) == 4
+
+
+def test_moe_null_arguments(lib):
+    a = qm.qmoe_moe_attrs_default()
+    assert lib.qmoe_moe_validate(*([None] * 9), ctypes.byref(a)) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.qmoe_moe_workspace_size(*([None] * 8), ctypes.byref(a), ctypes.byref(n)) == 1
