@@ -212,22 +212,34 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const F32Gemm g, int n
   }
 }
 
-// Weight-streaming variant for tiles of at most 16 rows.  The four MFMAs of
-// one 16-deep K group take k = 16 kg + 4 kq + j (j = 0..3) in lane group kq,
-// so one 16-byte load of the operand row covers them.  Columns of MFMA block
-// i (c = 0..15):
+// Weight-streaming variant for tiles of at most 16 rows.  K is walked in
+// groups of KG = 16 V: the 4 V MFMAs of a group take k = KG kg + 4 V kq + j
+// (j < 4 V) in lane group kq, so V 16-byte loads of the operand row cover
+// them.  Columns of MFMA block i (c = 0..15):
 //   KN: n0 + 4c + i: one 16-byte load per lane and k row fetches a 256-byte
 //       row segment serving all four blocks, and the results leave as
 //       16-byte stores;
-//   NK: n0 + 16i + c: one 16-byte load per lane and block fetches the four
-//       k of its weight row.
-// kSD K groups of loads stay in flight ahead of the matrix instructions.
-// Requires K % 4 == 0 and 16-byte aligned a, w (KN: also N % 4 == 0 and
-// 16-byte aligned bias and out).
-constexpr int kSD = 4;
-
+//   NK: n0 + 16i + c: V 16-byte loads per lane and block fetch 16 V
+//       consecutive bytes of its weight row (V = 2: whole 128-byte lines per
+//       four lanes).
+// KSPLIT = 1: the four wavefronts of a workgroup take four 64-column strips;
+// KSPLIT = 4: they take four K ranges of one strip and add their partial
+// sums through LDS in wavefront order (for narrow N, to keep enough
+// wavefronts streaming).  kSD groups of loads stay in flight ahead of the
+// matrix instructions.  Requires K % 4 == 0 and 16-byte aligned a, w (KN:
+// also N % 4 == 0 and 16-byte aligned bias and out).
 template <bool NK>
+struct StreamShape {
+  static constexpr int V = NK ? 2 : 1;  // 16-byte vectors per lane and row per K group
+  static constexpr int KG = 16 * V;     // K per group
+  static constexpr int SD = NK ? 2 : 4; // groups in flight
+};
+
+template <bool NK, int KSPLIT>
 __global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const F32Gemm g, int nblk) {
+  using SS = StreamShape<NK>;
+  constexpr int V = SS::V, KG = SS::KG, SD = SS::SD;
+  constexpr int NB = 4 * V;  // 16-byte B loads per lane and group (NK: V per block; KN: one per k row)
   const int tile = blockIdx.x / nblk;
   if (tile >= g.ntiles[0]) return;
   const int grp = g.tiles[4 * tile + 0];
@@ -235,8 +247,8 @@ __global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const F32Gemm g, int 
   const int rows = g.tiles[4 * tile + 2];
   const int K = g.K, N = g.N;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x % nblk) * 256 + wave * 64;
-  if (n0 >= N) return;  // whole wavefront: no barriers below
+  const int n0 = KSPLIT == 1 ? (blockIdx.x % nblk) * 256 + wave * 64 : (blockIdx.x % nblk) * 64;
+  if (n0 >= N) return;  // whole wavefront (whole workgroup when KSPLIT > 1): before any barrier
   const int c = lane & 15, kq = lane >> 4;
   // output rows of this lane: 4 kq + t
   int orow[4];
@@ -248,6 +260,7 @@ __global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const F32Gemm g, int 
 #pragma unroll
   for (int i = 0; i < 4; ++i) cok[i] = (NK ? n0 + 16 * i + c : n0 + 4 * c) < N;
   if (grp >= g.G) {
+    if (KSPLIT > 1 && wave > 0) return;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (orow[t] < 0) continue;
@@ -262,72 +275,102 @@ __global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const F32Gemm g, int 
     }
     return;
   }
-  const float* arow = g.a + (long)gmm_arow(g, p0 + min(c, rows - 1)) * K + 4 * kq;
+  // K groups of this wavefront: [g0, g1) of the nfull full groups; the last
+  // K range also takes the tail
+  const int nfull = K / KG;
+  const int g0 = KSPLIT == 1 ? 0 : (int)((long)nfull * wave / KSPLIT);
+  const int g1 = KSPLIT == 1 ? nfull : (int)((long)nfull * (wave + 1) / KSPLIT);
+  const bool tail = nfull * KG < K && (KSPLIT == 1 || wave == KSPLIT - 1);
+  const float* arow = g.a + (long)gmm_arow(g, p0 + min(c, rows - 1)) * K + 4 * V * kq;
   const float* wg = g.w + (long)grp * K * N;
-  // weight pointers of this lane at k = 4 kq (NK: one per block; KN: k row
-  // 4 kq, the rows below it N apart); lanes past N re-read a valid column
+  // weight pointers of this lane at k = 4 V kq (NK: one per block; KN: that k
+  // row, the rows below it N apart); lanes past N re-read a valid column
   const float* wp[NK ? 4 : 1];
   if (NK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wp[i] = wg + (long)min(n0 + 16 * i + c, N - 1) * K + 4 * kq;
+    for (int i = 0; i < 4; ++i) wp[i] = wg + (long)min(n0 + 16 * i + c, N - 1) * K + 4 * V * kq;
   } else {
-    wp[0] = wg + (cok[0] ? n0 + 4 * c : 0) + (long)(4 * kq) * N;
+    wp[0] = wg + (cok[0] ? n0 + 4 * c : 0) + (long)(4 * V * kq) * N;
   }
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nfull = K / 16;  // K groups without a tail
-  // KN: rb[d][j] = columns n0 + 4c .. + 3 at k row 16 kg + 4 kq + j
-  // NK: rb[d][i] = k 16 kg + 4 kq .. + 3 of column n0 + 16 i + c
-  f32x4 ra[kSD], rb[kSD][4];
+  // ra[d][v] = operand k KG kg + 4 V kq + 4 v .. + 3
+  // KN: rb[d][j] = columns n0 + 4c .. + 3 at k row KG kg + 4 V kq + j
+  // NK: rb[d][V i + v] = k KG kg + 4 V kq + 4 v .. + 3 of column n0 + 16 i + c
+  f32x4 ra[SD][V], rb[SD][NB];
   auto load = [&](int slot, int kg) {
-    const long k = (long)kg * 16;
-    ra[slot] = *(const f32x4*)(arow + k);
+    const long k = (long)kg * KG;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rb[slot][i] = NK ? *(const f32x4*)(wp[i] + k) : *(const f32x4*)(wp[0] + (k + i) * N);
+    for (int v = 0; v < V; ++v) ra[slot][v] = *(const f32x4*)(arow + k + 4 * v);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (NK) rb[slot][b] = *(const f32x4*)(wp[b / V] + k + 4 * (b % V));
+      else rb[slot][b] = *(const f32x4*)(wp[0] + (k + b) * N);
+    }
   };
   auto mma = [&](int slot) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4 * V; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[slot][j], NK ? rb[slot][i][j] : rb[slot][j][i], acc[i], 0,
-                                                      0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const float av = ra[slot][j / 4][j % 4];
+        const float bv = NK ? rb[slot][V * i + j / 4][j % 4] : rb[slot][j][i];
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[i], 0, 0, 0);
+      }
   };
   // Branch-free pipeline (exact load counts for the waits): past the last
-  // full group the loads repeat it, and those values are never used.
-  int kg = 0;
-  if (nfull > 0) {
+  // group of the range the loads repeat it, and those values are never used.
+  if (g1 > g0) {
+    int kg = g0;
 #pragma unroll
-    for (int d = 0; d < kSD; ++d) load(d, min(d, nfull - 1));
-    for (; kg + kSD <= nfull; kg += kSD) {
+    for (int d = 0; d < SD; ++d) load(d, min(g0 + d, g1 - 1));
+    for (; kg + SD <= g1; kg += SD) {
 #pragma unroll
-      for (int d = 0; d < kSD; ++d) {
+      for (int d = 0; d < SD; ++d) {
         mma(d);
-        load(d, min(kg + kSD + d, nfull - 1));
+        load(d, min(kg + SD + d, g1 - 1));
+        // keep each refill right behind the matrix instructions that free
+        // its registers, ahead of the next group's waits
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int d = 0; d < kSD; ++d)
-      if (kg + d < nfull) mma(d);
+    for (int d = 0; d < SD; ++d)
+      if (kg + d < g1) mma(d);
   }
-  if (nfull * 16 < K) {
+  if (tail) {
     // tail group: k past K reads as zero on both operands
-    const int kb = nfull * 16;
-    const int k0 = kb + 4 * kq;
+    const int kb = nfull * KG;
+    const int k0 = kb + 4 * V * kq;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ra[0][j] = k0 + j < K ? arow[kb + j] : 0.f;
+    for (int j = 0; j < 4 * V; ++j) ra[0][j / 4][j % 4] = k0 + j < K ? arow[kb + j] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int e = 0; e < 4; ++e) {
+        // NK: element e of vector b % V of column b / V; KN: column e of k row b
+        const int j = NK ? 4 * (b % V) + e : b;
         const bool ok = k0 + j < K;
-        // NK: element j of column i; KN: element i of k row j (pointer of row j)
-        if (NK) rb[0][i][j] = ok ? wp[i][kb + j] : 0.f;
-        else rb[0][j][i] = ok ? wp[0][(long)(kb + j) * N + i] : 0.f;
+        if (NK) rb[0][b][e] = ok ? wp[b / V][kb + j] : 0.f;
+        else rb[0][b][e] = ok ? wp[0][(long)(kb + j) * N + e] : 0.f;
       }
     mma(0);
+  }
+  if (KSPLIT > 1) {
+    // partial sums of waves 1.. through LDS, added in wavefront order
+    __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT - 1 : 1][4][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave - 1][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KSPLIT - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += red[w][i][lane];
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -350,14 +393,28 @@ __global__ void __launch_bounds__(256) qmoe_gmm_f32_rows16(const F32Gemm g, int 
 int gmm_tile_rows() { return kGM; }
 int gmm_rows16_tile_rows() { return 16; }
 
-hipError_t launch_gmm_rows16(const F32Gemm& g, bool nk, int max_tiles, hipStream_t st) {
+hipError_t launch_gmm_rows16(const F32Gemm& g, bool nk, int ksplit, int max_tiles, hipStream_t st) {
   if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
   if (g.K % 4 != 0 || (!nk && g.N % 4 != 0)) return hipErrorInvalidValue;
-  const int nblk = (g.N + 255) / 256;
+  if (ksplit != 1 && ksplit != 4) return hipErrorInvalidValue;
+  const int cols = ksplit == 1 ? 256 : 64;  // columns per workgroup
+  const int nblk = (g.N + cols - 1) / cols;
   const dim3 grid((unsigned)((long)max_tiles * nblk)), block(256);
-  if (nk) hipLaunchKernelGGL(qmoe_gmm_f32_rows16<true>, grid, block, 0, st, g, nblk);
-  else hipLaunchKernelGGL(qmoe_gmm_f32_rows16<false>, grid, block, 0, st, g, nblk);
+  if (nk) {
+    if (ksplit == 1) hipLaunchKernelGGL((qmoe_gmm_f32_rows16<true, 1>), grid, block, 0, st, g, nblk);
+    else hipLaunchKernelGGL((qmoe_gmm_f32_rows16<true, 4>), grid, block, 0, st, g, nblk);
+  } else {
+    if (ksplit == 1) hipLaunchKernelGGL((qmoe_gmm_f32_rows16<false, 1>), grid, block, 0, st, g, nblk);
+    else hipLaunchKernelGGL((qmoe_gmm_f32_rows16<false, 4>), grid, block, 0, st, g, nblk);
+  }
   return hipGetLastError();
+}
+
+int gmm_rows16_ksplit(long est_tiles, int N) {
+  // wavefronts streaming with one strip per wavefront; below about two
+  // thousand (eight per compute unit) the K ranges are split four ways
+  const long waves = est_tiles * ((N + 255) / 256) * 4;
+  return waves < 2048 ? 4 : 1;
 }
 
 hipError_t launch_gmm_index(const void* idx, bool idx64, long n, int G, int* out, hipStream_t st) {

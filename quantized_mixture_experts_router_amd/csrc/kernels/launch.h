@@ -110,8 +110,12 @@ hipError_t launch_gmm_f32(const F32Gemm& g, bool nk, bool vec, int max_tiles, hi
 // Weight-streaming kernel: tiles of at most gmm_rows16_tile_rows() rows;
 // K % 4 == 0, a and w 16-byte aligned (KN: also N % 4 == 0 and 16-byte
 // aligned bias and out).
+// ksplit 1 or 4: wavefronts of a workgroup on four column strips or on four
+// K ranges of one strip; gmm_rows16_ksplit picks it from an estimate of the
+// tiles in use.
 int gmm_rows16_tile_rows();
-hipError_t launch_gmm_rows16(const F32Gemm& g, bool nk, int max_tiles, hipStream_t st);
+int gmm_rows16_ksplit(long est_tiles, int N);
+hipError_t launch_gmm_rows16(const F32Gemm& g, bool nk, int ksplit, int max_tiles, hipStream_t st);
 
 // Float MoE activation pass (see moe.hip): act[p][j], p < S, j < I, from
 // FC1 rows h (F floats) and FC3 rows u3 (I floats, or nullptr).  Codes

@@ -171,7 +171,8 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
   g.N = (int)p.N;
   g.G = G;
   g.out = static_cast<float*>(const_cast<void*>(output->data));
-  const hipError_t e = stream16 ? launch_gmm_rows16(g, false, (int)p.max_tiles, s)
+  const long est_tiles = std::max<int64_t>(1, std::min<int64_t>(p.G, p.R));  // groups in use, at most
+  const hipError_t e = stream16 ? launch_gmm_rows16(g, false, gmm_rows16_ksplit(est_tiles, g.N), (int)p.max_tiles, s)
                                 : launch_gmm_f32(g, false, vec, (int)p.max_tiles, s);
   if (e != hipSuccess) return QMOE_ERR_HIP;
   if (mark(2) != hipSuccess) return QMOE_ERR_HIP;

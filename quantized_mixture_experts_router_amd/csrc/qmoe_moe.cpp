@@ -146,7 +146,10 @@ const float* fptr(const qmoe_tensor* t) { return t ? static_cast<const float*>(t
 // LDS-tiled kernel.
 hipError_t projection(const MoePlan& p, const F32Gemm& g, hipStream_t s) {
   const bool vec = g.K % 4 == 0 && aligned_to(g.a, 16) && aligned_to(g.w, 16);
-  if (p.rows16 && vec) return launch_gmm_rows16(g, true, (int)p.max_tiles, s);
+  if (p.rows16 && vec) {
+    const long est_tiles = std::max<int64_t>(1, std::min(p.E, p.S));  // experts in use, at most
+    return launch_gmm_rows16(g, true, gmm_rows16_ksplit(est_tiles, g.N), (int)p.max_tiles, s);
+  }
   return launch_gmm_f32(g, true, vec, (int)p.max_tiles, s);
 }
 

@@ -175,6 +175,19 @@ def test_misaligned_pointers_take_scalar_path(torch, shape):
     _check(got, x, w, idx, b, label="misaligned")
 
 
+def test_streaming_one_strip_per_wavefront_with_tails(torch):
+    # enough 256-column blocks that the streaming kernel gives each
+    # wavefront its own column strip (no K split); N % 256 != 0, K % 16 != 0
+    rng = np.random.default_rng(13)
+    M, K, G, N, S = 16, 100, 8, 20004, 1
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    w = rng.standard_normal((G, K, N), dtype=np.float32)
+    b = rng.standard_normal((G, N), dtype=np.float32)
+    idx = rng.permutation(np.repeat(np.arange(G), 2))[:, None]
+    got = _run(torch, x, w, idx, b, label="rows16-strips")
+    _check(got, x, w, idx, b, label="rows16-strips")
+
+
 def test_small_groups_spanning_several_16_row_tiles(torch):
     # 16-row tiles with one group of 40 rows (three tiles) and a few empty groups
     rng = np.random.default_rng(12)

@@ -136,6 +136,14 @@ def test_shapes_and_front_ends(torch, case):
     _full(torch, w, a, f"{case}")
 
 
+def test_streaming_fc1_one_strip_per_wavefront(torch):
+    # FC1 wide enough for one column strip per wavefront (no K split), with
+    # a K tail (H % 32 != 0); FC2 narrow (K split)
+    rng = np.random.default_rng(26)
+    w, a = W.moe_random_case(rng, tokens_shape=(8,), hidden=68, experts=8, inter=16400, k=2, activation="relu")
+    _full(torch, w, a, "fc1-strips")
+
+
 def test_zero_inter_gives_weighted_fc2_bias(torch):
     rng = np.random.default_rng(23)
     w, a = W.moe_random_case(rng, tokens_shape=(10,), hidden=32, experts=4, inter=0, k=2, activation="relu")
