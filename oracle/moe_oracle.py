@@ -29,7 +29,10 @@ the design notes; parity beyond these readings is unpinned by the pages):
   * fusion_size is 2 only for swiglu with fusion 1 or 2; the swiglu_fusion
     attribute is not read by other activations;
   * FC3 is read only by swiglu with fusion 0 (required there) and by silu
-    (optional); other activations ignore it.
+    (optional); other activations ignore it;
+  * the optional swiglu_limit L (README Attributes: a SwiGLU clamp, none when
+    omitted) bounds the gate above by L and the linear branch to [-L, L]
+    before the formula; it must be > 0 and only swiglu reads it.
 """
 from __future__ import annotations
 
@@ -37,12 +40,12 @@ import math
 
 import numpy as np
 
-from .qmoe_oracle import ContractError, ROUTING_MOE, expert_permutation, route
+from .qmoe_oracle import ContractError, ROUTING_MOE, clamp_swiglu, expert_permutation, route, swiglu_limit_of
 
 ACTIVATIONS = ("relu", "gelu", "silu", "swiglu", "identity")
 
 DEFAULTS = dict(k=1, activation_type="relu", swiglu_fusion=0, activation_alpha=1.0, activation_beta=0.0,
-                normalize_routing_weights=0, use_sparse_mixer=0)
+                normalize_routing_weights=0, use_sparse_mixer=0, swiglu_limit=None)
 
 
 def moe_attrs(attrs: dict | None) -> dict:
@@ -103,9 +106,10 @@ def moe_validate(x, logits, fc1_w, fc2_w, fc3_w=None, fc1_b=None, fc2_b=None, fc
     if fc3_b is not None and (fc3_w is None or _shape(fc3_b) != (E, I)):
         raise ContractError("shape", "fc3_experts_bias must be (E, I) and come with fc3 weights")
     uses_fc3 = fc3_w is not None and (act == "silu" or (act == "swiglu" and fusion == 0))
+    limit = swiglu_limit_of(a)
     return dict(T=T, H=H, E=E, I=I, F=F, k=k, act=act, fusion=fusion, fused=fused, uses_fc3=uses_fc3,
                 alpha=float(a["activation_alpha"]), beta=float(a["activation_beta"]),
-                normalize=int(a["normalize_routing_weights"]))
+                normalize=int(a["normalize_routing_weights"]), limit=limit)
 
 
 def gelu(h):
@@ -121,7 +125,7 @@ def sigmoid(v):
     return 1.0 / (1.0 + np.exp(-np.asarray(v, dtype=np.float64)))
 
 
-def moe_activation(h, act, fusion=0, alpha=1.0, beta=0.0, u3=None):
+def moe_activation(h, act, fusion=0, alpha=1.0, beta=0.0, u3=None, limit=float("inf")):
     """Activation of one FC1 output vector h (and the FC3 output u3 when read)."""
     h = np.asarray(h, dtype=np.float64)
     if act == "relu":
@@ -141,6 +145,7 @@ def moe_activation(h, act, fusion=0, alpha=1.0, beta=0.0, u3=None):
     else:
         half = h.shape[-1] // 2
         g, u = h[..., :half], h[..., half:]
+    g, u = clamp_swiglu(g, u, limit)
     return g * sigmoid(alpha * g) * (u + beta)
 
 
@@ -155,7 +160,7 @@ def moe_expert(xrow, e, d, fc1_w, fc2_w, fc3_w=None, fc1_b=None, fc2_b=None, fc3
         u3 = np.asarray(fc3_w[e], dtype=np.float64) @ x
         if fc3_b is not None:
             u3 = u3 + np.asarray(fc3_b[e], dtype=np.float64)
-    a = moe_activation(h, d["act"], d["fusion"], d["alpha"], d["beta"], u3)
+    a = moe_activation(h, d["act"], d["fusion"], d["alpha"], d["beta"], u3, d["limit"])
     y = np.asarray(fc2_w[e], dtype=np.float64) @ a
     if fc2_b is not None:
         y = y + np.asarray(fc2_b[e], dtype=np.float64)

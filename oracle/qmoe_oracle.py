@@ -28,6 +28,10 @@ Readings taken where the pages are silent:
   unpinned by the pages, pinned only as this convention);
 * interleaved SwiGLU: FC1 row 2j is the gate, row 2j+1 the linear branch,
   act = g * sigmoid(alpha * g) * (u + beta);
+* the optional swiglu_limit L (``attributeDescriptions.swiglu_limit``; the
+  pages give no formula) clamps before that formula: g <- min(g, L),
+  u <- clamp(u, -L, L); L must be > 0 (parity unpinned by the pages: pinned
+  only by invariants of this reading);
 * top-k order is descending logit, equal logits go to the lower expert index,
   and -0.0 equals +0.0;
 * the selected-logit softmax subtracts the largest selected logit;
@@ -57,7 +61,7 @@ class ContractError(ValueError):
 DEFAULT_ATTRS = dict(activation_alpha=1.0, activation_beta=0.0, activation_type="relu",
                      expert_weight_bits=4, k=1, normalize_routing_weights=0, quant_type="int",
                      swiglu_fusion=0, use_sparse_mixer=0, weights_prepacked=-1, block_size=0,
-                     routing=ROUTING_QMOE)
+                     routing=ROUTING_QMOE, swiglu_limit=None)
 
 
 def _attrs(attrs: dict | None) -> dict:
@@ -152,10 +156,11 @@ def validate(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None, out_shape=None) 
     k = a["k"]
     if not (1 <= k <= E):
         raise ContractError("attr", "k must lie in [1, num_experts]")
+    limit = swiglu_limit_of(a)
     return dict(T=T, H=H, E=E, I=I, F=F, k=k, bits=bits, pack=pack, fusion=fusion, bs=bs,
                 mid=8 if bits == 4 else 128, activation=act, alpha=float(a["activation_alpha"]),
                 beta=float(a["activation_beta"]), routing=a["routing"],
-                normalize=int(a["normalize_routing_weights"]))
+                normalize=int(a["normalize_routing_weights"]), limit=limit)
 
 
 def route(logits, k: int, routing: str = ROUTING_QMOE, normalize: int = 0):
@@ -230,20 +235,39 @@ def dequantize(packed, scales, bits: int, block_size: int):
     return (q - mid).astype(np.float64) * S
 
 
-def activation(h, act: str, alpha: float = 1.0, beta: float = 0.0):
-    """ReLU, or interleaved SwiGLU over FC1 row pairs (gate 2j, linear 2j+1)."""
+def swiglu_limit_of(a: dict) -> float:
+    """The optional SwiGLU clamp limit (QMoE manifest
+    ``attributeDescriptions.swiglu_limit``, ``constants.hasSwigluLimit``):
+    +inf when absent; a present limit must be a number > 0."""
+    v = a.get("swiglu_limit")
+    if v is None:
+        return float("inf")
+    v = float(v)
+    if not v > 0:
+        raise ContractError("attr", "swiglu_limit must be > 0")
+    return v
+
+
+def clamp_swiglu(g, u, limit: float):
+    """Reading of the clamp (the pages give no formula): the gate is bounded
+    above by the limit, the linear branch on both sides."""
+    return np.minimum(g, limit), np.clip(u, -limit, limit)
+
+
+def activation(h, act: str, alpha: float = 1.0, beta: float = 0.0, limit: float = float("inf")):
+    """ReLU, or interleaved SwiGLU over FC1 row pairs (gate 2j, linear 2j+1),
+    with the optional clamp limit."""
     h = np.asarray(h, dtype=np.float64)
     if act == "relu":
         return np.maximum(h, 0.0)
-    g = h[..., 0::2]
-    u = h[..., 1::2]
+    g, u = clamp_swiglu(h[..., 0::2], h[..., 1::2], limit)
     return g / (1.0 + np.exp(-alpha * g)) * (u + beta)
 
 
-def expert_ffn(xrows, w1, w2, act, alpha, beta):
+def expert_ffn(xrows, w1, w2, act, alpha, beta, limit=float("inf")):
     """FC1 -> activation -> FC2 for the rows routed to one expert (float64)."""
     h = np.asarray(xrows, dtype=np.float64) @ w1.T
-    a = activation(h, act, alpha, beta)
+    a = activation(h, act, alpha, beta, limit)
     return a @ w2.T
 
 
@@ -267,7 +291,7 @@ def qmoe(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None, return_intermediates
             rows = perm[offsets[e]:offsets[e + 1]]
             w1 = dequantize(fc1_w[e], fc1_s[e], d["bits"], d["bs"])
             w2 = dequantize(fc2_w[e], fc2_s[e], d["bits"], d["bs"])
-            slot_out[rows] = expert_ffn(xs[rows // k], w1, w2, d["activation"], d["alpha"], d["beta"])
+            slot_out[rows] = expert_ffn(xs[rows // k], w1, w2, d["activation"], d["alpha"], d["beta"], d["limit"])
     out = (w.reshape(T, k, 1) * slot_out.reshape(T, k, H)).sum(axis=1)
     out = out.reshape(np.asarray(x).shape)
     if return_intermediates:
@@ -294,7 +318,7 @@ def qmoe_tokens(token_ids, x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None):
         rows = hit[0]
         w1 = dequantize(fc1_w[e], fc1_s[e], d["bits"], d["bs"])
         w2 = dequantize(fc2_w[e], fc2_s[e], d["bits"], d["bs"])
-        y = expert_ffn(xs[rows], w1, w2, d["activation"], d["alpha"], d["beta"])
+        y = expert_ffn(xs[rows], w1, w2, d["activation"], d["alpha"], d["beta"], d["limit"])
         for r, (t, s) in enumerate(zip(*hit)):
             out[t] += w[t, s] * y[r]
     return out
@@ -322,7 +346,7 @@ def qmoe_dense(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None):
             h = np.zeros(d["F"])
             for n in range(d["F"]):
                 h[n] = float(np.dot(W1[e, n], xs[t]))
-            a = activation(h, d["activation"], d["alpha"], d["beta"])
+            a = activation(h, d["activation"], d["alpha"], d["beta"], d["limit"])
             y = np.array([float(np.dot(W2[e, c], a)) for c in range(H)])
             out[t] += w[t, s] * y
     return out.reshape(np.asarray(x).shape)

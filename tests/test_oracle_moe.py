@@ -246,11 +246,11 @@ def test_planted_mistakes_fail_a_pin(monkeypatch):
             test_gelu_textbook_values_and_library_cdf()
     real = M.moe_activation
 
-    def swapped(h, act, fusion=0, alpha=1.0, beta=0.0, u3=None):
+    def swapped(h, act, fusion=0, alpha=1.0, beta=0.0, u3=None, limit=float("inf")):
         if act == "swiglu" and fusion == 2:
             half = h.shape[-1] // 2
             h = np.concatenate([h[..., half:], h[..., :half]], axis=-1)
-        return real(h, act, fusion, alpha, beta, u3)
+        return real(h, act, fusion, alpha, beta, u3, limit)
     with monkeypatch.context() as m:
         m.setattr(M, "moe_activation", swapped)
         with pytest.raises(AssertionError):
