@@ -15,7 +15,8 @@
  *               4-bit bytes hold the even code in the low nibble
  *   h         = x[t] . W1[e]^T                (FC1, rows = fusion * I)
  *   a         = relu(h)  |  g * sigmoid(alpha * g) * (u + beta),
- *               g = h[2j], u = h[2j+1]        (interleaved SwiGLU)
+ *               g = h[2j], u = h[2j+1]        (interleaved SwiGLU; with
+ *               swiglu_limit L: g <- min(g, L), u <- clamp(u, -L, L))
  *   out[t]    = sum_s w[t, s] * (a . W2[sel[t, s]]^T)
  *
  * FC1 and FC2 are each a GroupedMatMul (ONNX GroupedMatMul-29, Summary) over
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 1
+#define QMOE_ABI_VERSION 2
 
 typedef enum {
   QMOE_OK = 0,
@@ -108,6 +109,14 @@ typedef struct {
   int32_t use_sparse_mixer;          /* [0]  1 is QMOE_ERR_UNSUPPORTED            */
   int32_t weights_prepacked;         /* [-1] -1 or 0; 1 is QMOE_ERR_UNSUPPORTED   */
   int32_t quant_type;                /* [0]  0 = "int"; others UNSUPPORTED        */
+  int32_t has_swiglu_limit;          /* [0]  1: swiglu_limit is given              */
+  float swiglu_limit;                /* [-]  SwiGLU clamp L > 0 (manifest
+                                             attributeDescriptions.swiglu_limit,
+                                             constants.hasSwigluLimit): the gate is
+                                             bounded above by L and the linear
+                                             branch to [-L, L] before the formula
+                                             (a reading: no formula on the pages);
+                                             read by SwiGLU only                  */
 } qmoe_attrs;
 
 /* Stage boundaries at which qmoe_forward_debug records events. */
@@ -277,6 +286,9 @@ typedef struct {
   float activation_beta;             /* [0]  added to the swiglu linear branch */
   int32_t normalize_routing_weights; /* [0]  0 or 1                           */
   int32_t use_sparse_mixer;          /* [0]  1 is QMOE_ERR_UNSUPPORTED        */
+  int32_t has_swiglu_limit;          /* [0]  1: swiglu_limit is given          */
+  float swiglu_limit;                /* [-]  SwiGLU clamp L > 0 (README
+                                             Attributes), as for QMoE          */
 } qmoe_moe_attrs;
 
 /* Fill *a with the defaults listed above.  a must not be NULL. */

@@ -42,13 +42,15 @@ class QmoeAttrs(ctypes.Structure):
                 ("activation_alpha", ctypes.c_float), ("activation_beta", ctypes.c_float),
                 ("normalize_routing_weights", ctypes.c_int32), ("routing", ctypes.c_int32),
                 ("use_sparse_mixer", ctypes.c_int32), ("weights_prepacked", ctypes.c_int32),
-                ("quant_type", ctypes.c_int32)]
+                ("quant_type", ctypes.c_int32), ("has_swiglu_limit", ctypes.c_int32),
+                ("swiglu_limit", ctypes.c_float)]
 
 
 class QmoeMoeAttrs(ctypes.Structure):
     _fields_ = [("k", ctypes.c_int32), ("activation_type", ctypes.c_int32), ("swiglu_fusion", ctypes.c_int32),
                 ("activation_alpha", ctypes.c_float), ("activation_beta", ctypes.c_float),
-                ("normalize_routing_weights", ctypes.c_int32), ("use_sparse_mixer", ctypes.c_int32)]
+                ("normalize_routing_weights", ctypes.c_int32), ("use_sparse_mixer", ctypes.c_int32),
+                ("has_swiglu_limit", ctypes.c_int32), ("swiglu_limit", ctypes.c_float)]
 
 
 QMOE_STAGE_EVENTS = 6
@@ -156,6 +158,11 @@ def make_attrs(attrs: Optional[dict] = None) -> QmoeAttrs:
             val = 0 if val in ("int", 0) else 1
         elif key == "block_size" and val is None:
             val = 0
+        elif key == "swiglu_limit":
+            # absent (None) or a value; a given value is passed as is and
+            # the library checks it
+            a.has_swiglu_limit = 0 if val is None else 1
+            val = 0.0 if val is None else val
         setattr(a, key, val)
     return a
 
@@ -326,6 +333,9 @@ def make_moe_attrs(attrs: Optional[dict] = None) -> QmoeMoeAttrs:
     for key, val in (attrs or {}).items():
         if key == "activation_type" and isinstance(val, str):
             val = QMOE_ACT.get(val, 99)
+        elif key == "swiglu_limit":
+            a.has_swiglu_limit = 0 if val is None else 1
+            val = 0.0 if val is None else val
         setattr(a, key, val)
     return a
 

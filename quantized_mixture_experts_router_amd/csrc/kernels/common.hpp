@@ -123,6 +123,16 @@ __device__ __forceinline__ f16x8 unpack8x2(uint32_t d0, uint32_t d1) {
   return r;
 }
 
+// SwiGLU g * sigmoid(alpha g) * (u + beta) after the optional clamp limit
+// (+inf: none): the gate is bounded above by limit, the linear branch to
+// [-limit, limit] (the reading taken of the QMoE manifest's and the MoE
+// README's swiglu_limit, which give no formula).
+__device__ __forceinline__ float swiglu_act(float g, float u, float alpha, float beta, float limit) {
+  g = fminf(g, limit);
+  u = fminf(fmaxf(u, -limit), limit);
+  return g / (1.f + expf(-alpha * g)) * (u + beta);
+}
+
 __device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(64 * kWaves) qmoe_gemm(GemmArgs g) {
           bool writer;
           if constexpr (EPI == EPI_SWIGLU) {
             const float u = __shfl_xor(v, 1);
-            a = v / (1.f + expf(-g.alpha * v)) * (u + g.beta);
+            a = swiglu_act(v, u, g.alpha, g.beta, g.limit);
             j = n >> 1;
             writer = (col & 1) == 0;
           } else {

@@ -48,6 +48,7 @@ struct GemmArgs {
   float* slot_out;      // FC2 output [splits][S][N] by slot id
   const int* perm;      // FC2: sorted position -> slot
   float alpha, beta;
+  float limit;          // SwiGLU clamp limit (+inf: none); set it, zero clamps everything
   // stream kernel
   int nst;              // stages per K range
   int act_swiglu;       // FC1 over the whole of K: activation written by the kernel (act != nullptr)
@@ -79,7 +80,7 @@ hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, co
 
 // Sum FC1 partials over K ranges, apply the activation, write FC2 operand rows.
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,
-                      float beta, uint8_t* act, hipStream_t st);
+                      float beta, float limit, uint8_t* act, hipStream_t st);
 
 // out[t, h] = sum_s w[t, s] * sum_z slot_out[z][t*k + s][h]  (fixed order)
 hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, int splits, float* out,
@@ -122,7 +123,7 @@ hipError_t launch_gmm_rows16(const F32Gemm& g, bool nk, int ksplit, int max_tile
 // match qmoe_activation.
 enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1, MOE_ACT_GELU = 2, MOE_ACT_SILU = 3, MOE_ACT_IDENTITY = 4 };
 hipError_t launch_moe_act(int act_type, const float* h, const float* u3, long S, int I, int F, int fusion,
-                          float alpha, float beta, float* act, hipStream_t st);
+                          float alpha, float beta, float limit, float* act, hipStream_t st);
 
 hipError_t launch_fill_zero(float* out, long n, hipStream_t st);
 

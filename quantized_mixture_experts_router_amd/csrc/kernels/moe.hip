@@ -7,7 +7,8 @@
 //   gelu      h Phi(h) = h erfc(-h / sqrt 2) / 2      (exact GELU)
 //   silu      h sigmoid(h)  [* u3 when FC3 is given]
 //   swiglu    g sigmoid(alpha g) (u + beta), (g, u) = (h[j], u3[j]) for
-//             fusion 0, (h[2j], h[2j+1]) for 1, (h[j], h[I + j]) for 2
+//             fusion 0, (h[2j], h[2j+1]) for 1, (h[j], h[I + j]) for 2,
+//             after the optional clamp limit (see swiglu_act in common.hpp)
 //   identity  h
 // float32 libm (erfcf, expf) throughout.
 #include "common.hpp"
@@ -20,7 +21,7 @@ __device__ __forceinline__ float moe_sigmoid(float v) { return 1.f / (1.f + expf
 template <int ACT>
 __global__ void __launch_bounds__(256) qmoe_moe_act(const float* __restrict__ h, const float* __restrict__ u3,
                                                     long S, int I, int F, int fusion, float alpha, float beta,
-                                                    float* __restrict__ act) {
+                                                    float limit, float* __restrict__ act) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= S * I) return;
   const long p = i / I;
@@ -39,7 +40,7 @@ __global__ void __launch_bounds__(256) qmoe_moe_act(const float* __restrict__ h,
       g = hp[j];
       u = hp[I + j];
     }
-    a = g * moe_sigmoid(alpha * g) * (u + beta);
+    a = swiglu_act(g, u, alpha, beta, limit);
   } else {
     const float v = hp[j];
     if (ACT == MOE_ACT_RELU) a = fmaxf(v, 0.f);
@@ -51,11 +52,11 @@ __global__ void __launch_bounds__(256) qmoe_moe_act(const float* __restrict__ h,
 }
 
 hipError_t launch_moe_act(int act_type, const float* h, const float* u3, long S, int I, int F, int fusion,
-                          float alpha, float beta, float* act, hipStream_t st) {
+                          float alpha, float beta, float limit, float* act, hipStream_t st) {
   const long n = S * I;
   if (n <= 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
-#define QMOE_MOE_ACT(A) hipLaunchKernelGGL(qmoe_moe_act<A>, grid, block, 0, st, h, u3, S, I, F, fusion, alpha, beta, act)
+#define QMOE_MOE_ACT(A) hipLaunchKernelGGL(qmoe_moe_act<A>, grid, block, 0, st, h, u3, S, I, F, fusion, alpha, beta, limit, act)
   switch (act_type) {
     case MOE_ACT_RELU: QMOE_MOE_ACT(MOE_ACT_RELU); break;
     case MOE_ACT_SWIGLU: QMOE_MOE_ACT(MOE_ACT_SWIGLU); break;

@@ -558,7 +558,7 @@ qmoe_stream(GemmArgs g) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const float gv = v[c >> 1][2 * (c & 1)], uv = v[c >> 1][2 * (c & 1) + 1];
-          a[c] = j0 + c < I ? gv / (1.f + expf(-g.alpha * gv)) * (uv + g.beta) : 0.f;
+          a[c] = j0 + c < I ? swiglu_act(gv, uv, g.alpha, g.beta, g.limit) : 0.f;
         }
       } else {
         const int t0 = j0 - jbase;
@@ -778,7 +778,8 @@ qmoe_stream(GemmArgs g) {
 // zero padding.
 template <int BITS, int EPI>
 __global__ void __launch_bounds__(256) qmoe_act(const float* __restrict__ part, int splits, int S, int F, int I,
-                                                int kp2, float alpha, float beta, uint8_t* __restrict__ act) {
+                                                int kp2, float alpha, float beta, float limit,
+                                                uint8_t* __restrict__ act) {
   constexpr int W = EPI == EPI_SWIGLU ? 16 : 8;  // FC1 values per group
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const int groups = kp2 / 8;
@@ -823,7 +824,7 @@ __global__ void __launch_bounds__(256) qmoe_act(const float* __restrict__ part, 
     if (j0 + c < I) {
       if constexpr (EPI == EPI_SWIGLU) {
         const float gv = h[2 * c], uv = h[2 * c + 1];
-        a = gv / (1.f + expf(-alpha * gv)) * (uv + beta);
+        a = swiglu_act(gv, uv, alpha, beta, limit);
       } else {
         a = fmaxf(h[c], 0.f);
       }
@@ -927,15 +928,15 @@ hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, co
 }
 
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,
-                      float beta, uint8_t* act, hipStream_t st) {
+                      float beta, float limit, uint8_t* act, hipStream_t st) {
   const long n = (long)S * (kp2 / 8);
   const dim3 grid((n + 255) / 256), block(256);
   if (bits == 4) {
-    if (epi == EPI_SWIGLU) hipLaunchKernelGGL((qmoe_act<4, EPI_SWIGLU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, act);
-    else hipLaunchKernelGGL((qmoe_act<4, EPI_RELU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, act);
+    if (epi == EPI_SWIGLU) hipLaunchKernelGGL((qmoe_act<4, EPI_SWIGLU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
+    else hipLaunchKernelGGL((qmoe_act<4, EPI_RELU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
   } else {
-    if (epi == EPI_SWIGLU) hipLaunchKernelGGL((qmoe_act<8, EPI_SWIGLU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, act);
-    else hipLaunchKernelGGL((qmoe_act<8, EPI_RELU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, act);
+    if (epi == EPI_SWIGLU) hipLaunchKernelGGL((qmoe_act<8, EPI_SWIGLU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
+    else hipLaunchKernelGGL((qmoe_act<8, EPI_RELU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
   }
   return hipGetLastError();
 }

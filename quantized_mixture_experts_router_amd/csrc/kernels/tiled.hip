@@ -307,7 +307,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             const float gv = v[c >> 1][2 * (c & 1)], uv = v[c >> 1][2 * (c & 1) + 1];
-            a[c] = j0 + c < I ? gv / (1.f + expf(-g.alpha * gv)) * (uv + g.beta) : 0.f;
+            a[c] = j0 + c < I ? swiglu_act(gv, uv, g.alpha, g.beta, g.limit) : 0.f;
           }
         } else {
           const int t0 = j0 - jbase;

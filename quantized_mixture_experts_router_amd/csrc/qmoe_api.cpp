@@ -123,6 +123,7 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g1.act_stride = 4 * p.kp2;
     g1.alpha = d.alpha;
     g1.beta = d.beta;
+    g1.limit = d.limit;
     g1.S = S;
     const int epi1 = d.act == QMOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
     if (p.s1.on) {
@@ -139,7 +140,7 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
         g1.slot_out = part1;
         QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.one, p.s1.splits, p.s1.wg_rows, g1, (int)p.max_tiles, s));
         QMOE_TRY_HIP(mark(2));
-        QMOE_TRY_HIP(launch_act(d.bits, epi1, part1, p.s1.splits, S, (int)d.F, I, (int)p.kp2, d.alpha, d.beta, act,
+        QMOE_TRY_HIP(launch_act(d.bits, epi1, part1, p.s1.splits, S, (int)d.F, I, (int)p.kp2, d.alpha, d.beta, d.limit, act,
                                 s));
       }
     } else if (p.tiled) {
@@ -166,6 +167,7 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g2.nblk = (int)d.nb2;
     g2.bs = (int)d.bs;
     g2.slot_out = slot;
+    g2.limit = __builtin_inff();  // no activation in FC2
     g2.perm = perm;
     g2.S = S;
     g2.store_by_slot = 1;  // FC2 rows go to their slot id
@@ -211,6 +213,8 @@ void qmoe_attrs_default(qmoe_attrs* a) {
   a->use_sparse_mixer = 0;
   a->weights_prepacked = -1;
   a->quant_type = 0;
+  a->has_swiglu_limit = 0;
+  a->swiglu_limit = 0.f;
 }
 
 qmoe_status qmoe_validate(const qmoe_tensor* input, const qmoe_tensor* router_probs, const qmoe_tensor* fc1w,

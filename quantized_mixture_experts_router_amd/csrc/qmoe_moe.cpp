@@ -34,6 +34,7 @@ struct MoePlan {
   int64_t T = 0, H = 0, E = 0, I = 0, F = 0, k = 0, S = 0;
   int act = QMOE_ACT_RELU, fusion = 0, normalize = 0;
   float alpha = 1.f, beta = 0.f;
+  float limit = __builtin_inff();  // SwiGLU clamp (+inf: none)
   bool uses_fc3 = false;
   bool small_front = false;
   bool rows16 = false;   // at most 16 rows per used expert on average: 16-row tiles, weight streaming
@@ -82,6 +83,9 @@ qmoe_status check(const qmoe_tensor* input, const qmoe_tensor* router, const qmo
   if (a->use_sparse_mixer != 0) return QMOE_ERR_ATTR;
   if (a->normalize_routing_weights != 0 && a->normalize_routing_weights != 1) return QMOE_ERR_ATTR;
   if (a->k < 1 || a->k > p->E) return QMOE_ERR_ATTR;
+  if (a->has_swiglu_limit != 0 && a->has_swiglu_limit != 1) return QMOE_ERR_ATTR;
+  if (a->has_swiglu_limit == 1 && !(a->swiglu_limit > 0.f)) return QMOE_ERR_ATTR;
+  p->limit = a->has_swiglu_limit ? a->swiglu_limit : __builtin_inff();
   p->k = a->k;
   p->act = a->activation_type;
   p->fusion = a->swiglu_fusion;
@@ -234,7 +238,7 @@ qmoe_status moe_impl(const qmoe_tensor* input, const qmoe_tensor* router, const 
   }
   QMOE_TRY_HIP(mark(2));
   QMOE_TRY_HIP(launch_moe_act(p.act, h1, p.uses_fc3 ? h3 : nullptr, S, (int)p.I, (int)p.F, p.fusion, p.alpha,
-                              p.beta, act, s));
+                              p.beta, p.limit, act, s));
   QMOE_TRY_HIP(mark(3));
   // FC2: operand rows in sorted order, results (bias included) by slot id.
   // With I == 0 the rows are the bias alone.
@@ -279,6 +283,8 @@ void qmoe_moe_attrs_default(qmoe_moe_attrs* a) {
   a->activation_beta = 0.f;
   a->normalize_routing_weights = 0;
   a->use_sparse_mixer = 0;
+  a->has_swiglu_limit = 0;
+  a->swiglu_limit = 0.f;
 }
 
 qmoe_status qmoe_moe_validate(const qmoe_tensor* input, const qmoe_tensor* router_probs,

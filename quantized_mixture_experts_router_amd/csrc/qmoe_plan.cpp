@@ -70,6 +70,9 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
   const bool relu = a->activation_type == QMOE_ACT_RELU && a->swiglu_fusion == 0;
   const bool swiglu = a->activation_type == QMOE_ACT_SWIGLU && a->swiglu_fusion == 1;
   if (!relu && !swiglu) return QMOE_ERR_ATTR;
+  // swiglu_limit: optional, > 0 when given
+  if (a->has_swiglu_limit != 0 && a->has_swiglu_limit != 1) return QMOE_ERR_ATTR;
+  if (a->has_swiglu_limit == 1 && !(a->swiglu_limit > 0.f)) return QMOE_ERR_ATTR;
   // quantBlockSizeOk, attribute part
   const int64_t bs = a->block_size;
   if (bs < 0 || (bs != 0 && (bs < 16 || !is_pow2(bs)))) return QMOE_ERR_ATTR;
@@ -131,6 +134,7 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
   d->act = swiglu ? QMOE_ACT_SWIGLU : QMOE_ACT_RELU;
   d->routing = a->routing; d->normalize = a->normalize_routing_weights;
   d->alpha = a->activation_alpha; d->beta = a->activation_beta;
+  d->limit = a->has_swiglu_limit ? a->swiglu_limit : __builtin_inff();
   return QMOE_OK;
 }
 

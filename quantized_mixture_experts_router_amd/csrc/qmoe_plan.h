@@ -25,6 +25,7 @@ struct Dims {
   int routing = QMOE_ROUTE_QMOE;
   int normalize = 0;
   float alpha = 1.f, beta = 0.f;
+  float limit = __builtin_inff();  // SwiGLU clamp (+inf: none)
 };
 
 // Largest expert count the routing kernels hold in registers / LDS.

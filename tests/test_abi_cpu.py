@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert qm.qmoe_abi_version() == 1
+    assert qm.qmoe_abi_version() == 2
     for s in range(9):
         assert qm.qmoe_status_string(s) != "unknown status"
 
@@ -53,6 +53,7 @@ def test_attribute_defaults_match_manifest(lib):
     assert a.normalize_routing_weights == 0 and a.swiglu_fusion == 0
     assert a.use_sparse_mixer == 0 and a.weights_prepacked == -1 and a.quant_type == 0
     assert a.block_size == 0 and a.routing == 0
+    assert a.has_swiglu_limit == 0  # swiglu_limit is optional: omitted means no clamp
 
 
 KIND = {"shape": 2, "attr": 3, "unsupported": 4, "dtype": 7}
@@ -275,3 +276,25 @@ def test_moe_null_arguments(lib):
     assert lib.qmoe_moe_validate(*([None] * 9), ctypes.byref(a)) == 1
     n = ctypes.c_size_t(0)
     assert lib.qmoe_moe_workspace_size(*([None] * 8), ctypes.byref(a), ctypes.byref(n)) == 1
+
+
+def test_swiglu_limit_contract_agrees_with_oracle(lib):
+    rng = np.random.default_rng(12)
+    w, a = W.random_case(rng, tokens_shape=(3,), hidden=32, experts=4, inter=32, k=2, bits=4, block_size=0,
+                         activation="swiglu")
+    for lim, kind in ((0.0, "attr"), (-2.0, "attr"), (float("nan"), "attr"), (3.5, None), (None, None)):
+        attrs = dict(w.attrs(), swiglu_limit=lim)
+        if kind:
+            with pytest.raises(Q.ContractError):
+                Q.validate(*a.values(), attrs=attrs)
+        else:
+            Q.validate(*a.values(), attrs=attrs)
+        assert qm.qmoe_validate(*a.values(), attrs=attrs) == (KIND[kind] if kind else 0), lim
+    from test_oracle_moe import _case
+    from oracle import moe_oracle as MO
+    am, attrs_m = _case(rng, act="swiglu", fusion=1)
+    for lim, code in ((0.0, 3), (float("nan"), 3), (1.5, 0)):
+        assert qm.qmoe_moe_validate(_moe_tensors(am), dict(attrs_m, swiglu_limit=lim)) == code
+    a2 = qm.make_attrs(dict(swiglu_limit=2.5))
+    assert a2.has_swiglu_limit == 1 and a2.swiglu_limit == 2.5
+    assert qm.make_attrs(dict(swiglu_limit=None)).has_swiglu_limit == 0

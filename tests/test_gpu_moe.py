@@ -121,6 +121,20 @@ def test_swiglu_alpha_beta_and_normalised_routing(torch, alpha, beta, normalize)
         _full(torch, w, a, f"swiglu{fusion} a={alpha} b={beta} n={normalize}")
 
 
+@pytest.mark.parametrize("fusion,fc3", [(0, True), (1, False), (2, False)])
+def test_swiglu_limit(torch, fusion, fc3):
+    rng = np.random.default_rng(30 + fusion)
+    for shape in ((6,), (3, 70)):  # 16-row and 64-row tiles
+        w, a = W.moe_random_case(rng, tokens_shape=shape, hidden=96, experts=4, inter=64, k=2,
+                                 activation="swiglu", fusion=fusion, fc3=fc3, alpha=1.702, beta=1.0)
+        for lim in (0.1, 0.5):
+            attrs = dict(w.attrs(), swiglu_limit=lim)
+            res = _run(torch, a, attrs, f"limit={lim}")
+            ref, inter = oracle.moe(**_args(a), attrs=attrs, return_intermediates=True)
+            _check_routing(res, inter, w.tokens, w.k)
+            _check_out(res["out"], ref, f"swiglu{fusion} limit={lim} {shape}")
+
+
 @pytest.mark.parametrize("case", [
     dict(tokens_shape=(7,), hidden=30, experts=3, inter=18, k=2, activation="gelu"),     # H, I not multiples of 4
     dict(tokens_shape=(9,), hidden=64, experts=5, inter=20, k=1, activation="silu", fc3=True),

@@ -307,3 +307,22 @@ def test_double_buffered_streaming(torch):
             del os.environ[key]
         else:
             os.environ[key] = old
+
+
+@pytest.mark.parametrize("tokens,bits,bs", [(16, 4, 64), (16, 8, 0), (200, 4, 32), (130, 8, 16)],
+                         ids=["stream-int4", "stream-int8", "tiled-int4", "gemm-int8"])
+def test_swiglu_limit(torch, tokens, bits, bs):
+    # the clamp reading on every FC1 path: weight streaming (<= 64 tokens),
+    # LDS-tiled, register-tiled (16-code blocks); limits that clamp a large
+    # share of the FC1 values, and one above all of them
+    rng = np.random.default_rng(40 + tokens + bits)
+    w, a = W.random_case(rng, tokens_shape=(tokens,), hidden=256, experts=6, inter=128, k=2, bits=bits,
+                         block_size=bs, activation="swiglu", scale_range=(0.01, 0.02))
+    for lim, alpha, beta in ((0.05, 1.702, 1.0), (0.3, 1.0, 0.0), (1e30, 1.0, 0.0)):
+        attrs = dict(w.attrs(), swiglu_limit=lim, activation_alpha=alpha, activation_beta=beta)
+        label = f"limit={lim} T={tokens} bits={bits} bs={bs}"
+        say(f"[case] {label}")
+        res = run_gpu(a, attrs, torch)
+        ref, inter = oracle.qmoe(*a.values(), attrs=attrs, return_intermediates=True)
+        check_routing(res, inter["sel"], inter["w"], inter["counts"], inter["offsets"], inter["perm"])
+        check_output(res["out"], ref, label)
