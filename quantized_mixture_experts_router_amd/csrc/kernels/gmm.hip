@@ -25,6 +25,8 @@
 //  * qmoe_gmm_f32_rows16: weight streaming for tiles of at most 16 rows: each
 //    wavefront owns 64 columns of one tile and streams that strip of W[g]
 //    from HBM straight into matrix-core operands (no LDS, no barriers).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.h"
 
@@ -163,38 +165,58 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const F32Gemm g, int n
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = zero4;
 
+  // Main loop, instantiated for the number of this wavefront's 16-row
+  // subtiles that hold a row of the tile (chosen once: subtiles wholly past
+  // the tile's rows run no matrix instructions, only their share of the
+  // staging and the barriers).
   const int nk = (K + kGK - 1) / kGK;
-  if (nk > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-    const float* a = sa[buf];
-    const float* b = sb[buf];
-#pragma unroll
-    for (int k4 = 0; k4 < kGK / 4; ++k4) {
-      // A operand: lane holds A[row col][k kq]; B operand: B[k kq][column col]
-      float av[2], bv[4];
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms) av[ms] = a[(wm * 32 + ms * 16 + col) * kAStride + k4 * 4 + kq];
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
-        const int c = wn * 64 + ns * 16 + col;
-        bv[ns] = NK ? b[c * kAStride + k4 * 4 + kq] : b[(k4 * 4 + kq) * kBStride + c];
-      }
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ms], bv[ns], acc[ms][ns], 0, 0, 0);
+  //   MSN = 0..2: that many subtiles, fixed for the loop ([K,N] weights);
+  //   MSN = -1: both subtiles with the test per instruction group ([N,K]
+  //   weights: the schedule the compiler makes of this form measured faster
+  //   there, the fixed form faster for [K,N]).
+  const bool live_rt[2] = {wm * 32 < rows, wm * 32 + 16 < rows};
+  auto mainloop = [&](auto msn_tag) {
+    constexpr int MSR = decltype(msn_tag)::value;
+    constexpr int MSN = MSR < 0 ? 2 : MSR;
+    if (nk > 0) {
+      load(0);
+      store(0);
     }
-    // the other buffer was last read in the previous step, finished by every
-    // wavefront before the last barrier
-    if (kt + 1 < nk) store(buf ^ 1);
     __syncthreads();
-  }
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) load(kt + 1);
+      const float* a = sa[buf];
+      const float* b = sb[buf];
+#pragma unroll
+      for (int k4 = 0; k4 < kGK / 4; ++k4) {
+        // A operand: lane holds A[row col][k kq]; B operand: B[k kq][column col]
+        float av[2], bv[4];
+#pragma unroll
+        for (int ms = 0; ms < MSN; ++ms) av[ms] = a[(wm * 32 + ms * 16 + col) * kAStride + k4 * 4 + kq];
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+          const int c = wn * 64 + ns * 16 + col;
+          if (MSN > 0) bv[ns] = NK ? b[c * kAStride + k4 * 4 + kq] : b[(k4 * 4 + kq) * kBStride + c];
+        }
+#pragma unroll
+        for (int ms = 0; ms < MSN; ++ms)
+          if (MSR >= 0 || live_rt[ms])
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns)
+              acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ms], bv[ns], acc[ms][ns], 0, 0, 0);
+      }
+      // the other buffer was last read in the previous step, finished by every
+      // wavefront before the last barrier
+      if (kt + 1 < nk) store(buf ^ 1);
+      __syncthreads();
+    }
+  };
+  const int live = min(max(rows - wm * 32, 0), 32);  // rows of this wavefront's 32
+  if constexpr (NK) mainloop(std::integral_constant<int, -1>{});
+  else if (live > 16) mainloop(std::integral_constant<int, 2>{});
+  else if (live > 0) mainloop(std::integral_constant<int, 1>{});
+  else mainloop(std::integral_constant<int, 0>{});
 
   // Output: lane holds rows 4 * kq + i of column col of each 16 x 16 subtile.
 #pragma unroll
