@@ -82,7 +82,8 @@ __device__ __forceinline__ void wait_vm() {
 #define QMOE_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
 #define QMOE_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int BITS, int SCALE, int EPI>
+// STEPFOLD (32-code scale blocks): every 32-code step is scaled on its own.
+template <int BITS, int SCALE, int EPI, bool STEPFOLD>
 __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   using L = TiledLayout<BITS>;
   // Three stage buffers: a step's operands arrive by direct-to-LDS loads two
@@ -206,30 +207,59 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
         h = *(const f16x8*)(arow + (((8 * j + 2 * grp) ^ col) * 16));
         l = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
       };
-      aload(0, ah[0], al[0]);
+      if constexpr (SCALE == SC_BLOCK && STEPFOLD) {
+        // 32-code scale blocks: every step's partial is scaled into acc.
+        // The step's hi-part instruction starts from zero (no zeroing
+        // moves), and each row subtile is folded right after the next
+        // subtile's instructions are issued, so no fold waits on the matrix
+        // pipeline.
+        const float* srow = (const float*)(base + kABuf + L::kBBuf) + j * kTN + wn * 64 + col;
+        float sc[4];
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        if (ms < 3) aload(ms + 1, ah[(ms + 1) & 1], al[(ms + 1) & 1]);
+        for (int ns = 0; ns < 4; ++ns) sc[ns] = srow[ns * 16];
+        auto fold = [&](int ms) {
 #pragma unroll
-        for (int hl = 0; hl < 2; ++hl)
+          for (int ns = 0; ns < 4; ++ns) acc[ms][ns] += blk[ms][ns] * sc[ns];
+        };
+        aload(0, ah[0], al[0]);
 #pragma unroll
-          for (int ns = 0; ns < 4; ++ns) {
-            const f16x8& av = hl ? al[ms & 1] : ah[ms & 1];
-            if constexpr (SCALE == SC_COL) acc[ms][ns] = mfma16(av, bf[ns], acc[ms][ns]);
-            else blk[ms][ns] = mfma16(av, bf[ns], blk[ms][ns]);
-          }
-      }
-      if constexpr (SCALE == SC_BLOCK) {
-        const int ks = 2 * kt + j;  // 32-code step
-        if (((ks + 1) * 32) % g.bs == 0) {
-          const float* srow = (const float*)(base + kABuf + L::kBBuf) + j * kTN;
+        for (int ms = 0; ms < 4; ++ms) {
+          if (ms < 3) aload(ms + 1, ah[(ms + 1) & 1], al[(ms + 1) & 1]);
 #pragma unroll
-          for (int ns = 0; ns < 4; ++ns) {
-            const float sc = srow[wn * 64 + ns * 16 + col];
+          for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
-              acc[ms][ns] += blk[ms][ns] * sc;
-              blk[ms][ns] = zero4;
+            for (int ns = 0; ns < 4; ++ns)
+              blk[ms][ns] = mfma16(hl ? al[ms & 1] : ah[ms & 1], bf[ns], hl ? blk[ms][ns] : zero4);
+          if (ms > 0) fold(ms - 1);
+        }
+        fold(3);
+      } else {
+        aload(0, ah[0], al[0]);
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+          if (ms < 3) aload(ms + 1, ah[(ms + 1) & 1], al[(ms + 1) & 1]);
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns) {
+              const f16x8& av = hl ? al[ms & 1] : ah[ms & 1];
+              if constexpr (SCALE == SC_COL) acc[ms][ns] = mfma16(av, bf[ns], acc[ms][ns]);
+              else blk[ms][ns] = mfma16(av, bf[ns], blk[ms][ns]);
+            }
+        }
+        if constexpr (SCALE == SC_BLOCK) {
+          // blocks of 64 codes and more: scale the block's sum when it closes
+          const int ks = 2 * kt + j;  // 32-code step
+          if (((ks + 1) * 32) % g.bs == 0) {
+            const float* srow = (const float*)(base + kABuf + L::kBBuf) + j * kTN;
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns) {
+              const float sc = srow[wn * 64 + ns * 16 + col];
+#pragma unroll
+              for (int ms = 0; ms < 4; ++ms) {
+                acc[ms][ns] += blk[ms][ns] * sc;
+                blk[ms][ns] = zero4;
+              }
             }
           }
         }
@@ -340,17 +370,21 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
 
 namespace {
 
-template <int BITS, int SCALE, int EPI>
+template <int BITS, int SCALE, int EPI, bool STEPFOLD>
 hipError_t go_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
-  auto kern = qmoe_tiled<BITS, SCALE, EPI>;
+  auto kern = qmoe_tiled<BITS, SCALE, EPI, STEPFOLD>;
   hipLaunchKernelGGL(kern, dim3(max_tiles * ntn), dim3(kTThreads), 0, st, g, ntn);
   return hipGetLastError();
 }
 
+// 32-code scale blocks fold every step (measured faster there); longer
+// blocks fold once per block (the step fold's extra multiply-adds cost more
+// than the pipeline drain it avoids at 128-code blocks).
 template <int BITS, int EPI>
 hipError_t pick_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
-  if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI>(g, max_tiles, ntn, st);
-  return go_tiled<BITS, SC_BLOCK, EPI>(g, max_tiles, ntn, st);
+  if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI, false>(g, max_tiles, ntn, st);
+  if (g.bs == 32) return go_tiled<BITS, SC_BLOCK, EPI, true>(g, max_tiles, ntn, st);
+  return go_tiled<BITS, SC_BLOCK, EPI, false>(g, max_tiles, ntn, st);
 }
 
 }  // namespace
