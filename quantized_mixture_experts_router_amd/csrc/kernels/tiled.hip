@@ -82,8 +82,9 @@ __device__ __forceinline__ void wait_vm() {
 #define QMOE_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
 #define QMOE_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
 
-// STEPFOLD (32-code scale blocks): every 32-code step is scaled on its own.
-template <int BITS, int SCALE, int EPI, bool STEPFOLD>
+// STEPFOLD: block sums are scaled every 32-code step (32-code blocks) or,
+// with STEPFOLD_KT, every 64-code K step (blocks of 64 codes and more).
+template <int BITS, int SCALE, int EPI, bool STEPFOLD, bool STEPFOLD_KT>
 __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   using L = TiledLayout<BITS>;
   // Three stage buffers: a step's operands arrive by direct-to-LDS loads two
@@ -208,15 +209,21 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
         l = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
       };
       if constexpr (SCALE == SC_BLOCK && STEPFOLD) {
-        // 32-code scale blocks: every step's partial is scaled into acc.
-        // The step's hi-part instruction starts from zero (no zeroing
-        // moves), and each row subtile is folded right after the next
-        // subtile's instructions are issued, so no fold waits on the matrix
-        // pipeline.
+        // Scale blocks folded per 32-code step (32-code blocks) or per K
+        // step (FOLDJ = 1: blocks of 64 codes and more, one scale for both
+        // halves of the step): the first instruction of a folded span starts
+        // from zero (no zeroing moves), and each row subtile is folded right
+        // after the next subtile's instructions are issued, so no fold waits
+        // on the matrix pipeline.
+        constexpr int FOLDJ = STEPFOLD_KT ? 1 : 0;  // fold after step half j == FOLDJ (and every half when 0)
+        const bool start = STEPFOLD_KT ? j == 0 : true;
+        const bool close = STEPFOLD_KT ? j == FOLDJ : true;
         const float* srow = (const float*)(base + kABuf + L::kBBuf) + j * kTN + wn * 64 + col;
         float sc[4];
+        if (close) {
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) sc[ns] = srow[ns * 16];
+          for (int ns = 0; ns < 4; ++ns) sc[ns] = srow[ns * 16];
+        }
         auto fold = [&](int ms) {
 #pragma unroll
           for (int ns = 0; ns < 4; ++ns) acc[ms][ns] += blk[ms][ns] * sc[ns];
@@ -229,10 +236,10 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
           for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns)
-              blk[ms][ns] = mfma16(hl ? al[ms & 1] : ah[ms & 1], bf[ns], hl ? blk[ms][ns] : zero4);
-          if (ms > 0) fold(ms - 1);
+              blk[ms][ns] = mfma16(hl ? al[ms & 1] : ah[ms & 1], bf[ns], (hl == 0 && start) ? zero4 : blk[ms][ns]);
+          if (close && ms > 0) fold(ms - 1);
         }
-        fold(3);
+        if (close) fold(3);
       } else {
         aload(0, ah[0], al[0]);
 #pragma unroll
@@ -370,9 +377,9 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
 
 namespace {
 
-template <int BITS, int SCALE, int EPI, bool STEPFOLD>
+template <int BITS, int SCALE, int EPI, bool STEPFOLD, bool STEPFOLD_KT>
 hipError_t go_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
-  auto kern = qmoe_tiled<BITS, SCALE, EPI, STEPFOLD>;
+  auto kern = qmoe_tiled<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT>;
   hipLaunchKernelGGL(kern, dim3(max_tiles * ntn), dim3(kTThreads), 0, st, g, ntn);
   return hipGetLastError();
 }
@@ -382,9 +389,9 @@ hipError_t go_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
 // than the pipeline drain it avoids at 128-code blocks).
 template <int BITS, int EPI>
 hipError_t pick_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
-  if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI, false>(g, max_tiles, ntn, st);
-  if (g.bs == 32) return go_tiled<BITS, SC_BLOCK, EPI, true>(g, max_tiles, ntn, st);
-  return go_tiled<BITS, SC_BLOCK, EPI, false>(g, max_tiles, ntn, st);
+  if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI, false, false>(g, max_tiles, ntn, st);
+  if (g.bs == 32) return go_tiled<BITS, SC_BLOCK, EPI, true, false>(g, max_tiles, ntn, st);
+  return go_tiled<BITS, SC_BLOCK, EPI, true, true>(g, max_tiles, ntn, st);
 }
 
 }  // namespace
