@@ -82,9 +82,10 @@ __device__ __forceinline__ void wait_vm() {
 #define QMOE_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
 #define QMOE_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
 
-// STEPFOLD: block sums are scaled every 32-code step (32-code blocks) or,
-// with STEPFOLD_KT, every 64-code K step (blocks of 64 codes and more).
-template <int BITS, int SCALE, int EPI, bool STEPFOLD, bool STEPFOLD_KT>
+// STEPFOLD: block sums are scaled every 32-code step (STEPFOLD_KT 0, 32-code
+// blocks), every 64-code K step (1, 64-code blocks) or every two K steps (2,
+// blocks of 128 codes and more).
+template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT>
 __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   using L = TiledLayout<BITS>;
   // Three stage buffers: a step's operands arrive by direct-to-LDS loads two
@@ -186,7 +187,8 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   // earlier: wait for them (the next step's may stay in flight), then the
   // barrier makes every wavefront's loads visible and frees buffer
   // (kt + 2) % 3 (last read in step kt - 1) for the loads of step kt + 2.
-  auto kstep = [&](int kt, uint8_t* base, uint8_t* next2) {
+  auto kstep = [&](int kt, uint8_t* base, uint8_t* next2, auto odd_tag) {
+    constexpr bool ODD = decltype(odd_tag)::value;  // second K step of a 128-code span
     wait_vm<NV>();
     __builtin_amdgcn_s_barrier();
     // nothing moves across the barrier: reads of buffer kt % 3 stay after it,
@@ -209,15 +211,16 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
         l = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
       };
       if constexpr (SCALE == SC_BLOCK && STEPFOLD) {
-        // Scale blocks folded per 32-code step (32-code blocks) or per K
-        // step (FOLDJ = 1: blocks of 64 codes and more, one scale for both
-        // halves of the step): the first instruction of a folded span starts
+        // Scale blocks folded per 32-code step (32-code blocks), per K step
+        // (64-code blocks) or per two K steps (blocks of 128 codes and more;
+        // a span never straddles blocks): the first instruction of a span starts
         // from zero (no zeroing moves), and each row subtile is folded right
         // after the next subtile's instructions are issued, so no fold waits
         // on the matrix pipeline.
-        constexpr int FOLDJ = STEPFOLD_KT ? 1 : 0;  // fold after step half j == FOLDJ (and every half when 0)
-        const bool start = STEPFOLD_KT ? j == 0 : true;
-        const bool close = STEPFOLD_KT ? j == FOLDJ : true;
+        // STEPFOLD_KT 0: every 32-code half starts and closes a span; 1: the
+        // K step is the span; 2: two K steps (128 codes) are the span
+        const bool start = STEPFOLD_KT == 0 ? true : STEPFOLD_KT == 1 ? j == 0 : (j == 0 && !ODD);
+        const bool close = STEPFOLD_KT == 0 ? true : STEPFOLD_KT == 1 ? j == 1 : (j == 1 && ODD);
         const float* srow = (const float*)(base + kABuf + L::kBBuf) + j * kTN + wn * 64 + col;
         float sc[4];
         if (close) {
@@ -275,14 +278,32 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   };
   issue(st0, 0);
   issue(st1, min(1, nk - 1));
+  // Step kt uses buffer kt % 3 and refills (kt + 2) % 3; with two-step
+  // folds the parity of kt must be static too, so that mode unrolls six.
+  uint8_t* const sts[3] = {st0, st1, st2};
+  auto step_d = [&](int kt, auto d_tag) {
+    constexpr int D = decltype(d_tag)::value;
+    kstep(kt, sts[D % 3], sts[(D + 2) % 3], std::integral_constant<bool, (D & 1) == 1>{});
+  };
+  constexpr int U = STEPFOLD_KT == 2 ? 6 : 3;
   int kt = 0;
-  for (; kt + 2 < nk; kt += 3) {
-    kstep(kt, st0, st2);
-    kstep(kt + 1, st1, st0);
-    kstep(kt + 2, st2, st1);
+  for (; kt + U - 1 < nk; kt += U) {
+    step_d(kt, std::integral_constant<int, 0>{});
+    step_d(kt + 1, std::integral_constant<int, 1>{});
+    step_d(kt + 2, std::integral_constant<int, 2>{});
+    if constexpr (U == 6) {
+      step_d(kt + 3, std::integral_constant<int, 3>{});
+      step_d(kt + 4, std::integral_constant<int, 4>{});
+      step_d(kt + 5, std::integral_constant<int, 5>{});
+    }
   }
-  if (kt < nk) kstep(kt, st0, st2);
-  if (kt + 1 < nk) kstep(kt + 1, st1, st0);
+  if (kt < nk) step_d(kt, std::integral_constant<int, 0>{});
+  if (kt + 1 < nk) step_d(kt + 1, std::integral_constant<int, 1>{});
+  if constexpr (U == 6) {
+    if (kt + 2 < nk) step_d(kt + 2, std::integral_constant<int, 2>{});
+    if (kt + 3 < nk) step_d(kt + 3, std::integral_constant<int, 3>{});
+    if (kt + 4 < nk) step_d(kt + 4, std::integral_constant<int, 4>{});
+  }
   // every load has landed and every wavefront is done with the stages
   wait_vm<0>();
   __syncthreads();
@@ -377,21 +398,22 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
 
 namespace {
 
-template <int BITS, int SCALE, int EPI, bool STEPFOLD, bool STEPFOLD_KT>
+template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT>
 hipError_t go_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
   auto kern = qmoe_tiled<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT>;
   hipLaunchKernelGGL(kern, dim3(max_tiles * ntn), dim3(kTThreads), 0, st, g, ntn);
   return hipGetLastError();
 }
 
-// 32-code scale blocks fold every step (measured faster there); longer
-// blocks fold once per block (the step fold's extra multiply-adds cost more
-// than the pipeline drain it avoids at 128-code blocks).
+// Block sums are folded once per span of one 32-code step (32-code
+// blocks), one K step (64) or two K steps (128 and more): fewer multiply-adds
+// than folding every step, and no pipeline drain of a fold at block ends.
 template <int BITS, int EPI>
 hipError_t pick_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
-  if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI, false, false>(g, max_tiles, ntn, st);
-  if (g.bs == 32) return go_tiled<BITS, SC_BLOCK, EPI, true, false>(g, max_tiles, ntn, st);
-  return go_tiled<BITS, SC_BLOCK, EPI, true, true>(g, max_tiles, ntn, st);
+  if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI, false, 0>(g, max_tiles, ntn, st);
+  if (g.bs == 32) return go_tiled<BITS, SC_BLOCK, EPI, true, 0>(g, max_tiles, ntn, st);
+  if (g.bs == 64) return go_tiled<BITS, SC_BLOCK, EPI, true, 1>(g, max_tiles, ntn, st);
+  return go_tiled<BITS, SC_BLOCK, EPI, true, 2>(g, max_tiles, ntn, st);
 }
 
 }  // namespace
