@@ -326,3 +326,19 @@ def test_swiglu_limit(torch, tokens, bits, bs):
         ref, inter = oracle.qmoe(*a.values(), attrs=attrs, return_intermediates=True)
         check_routing(res, inter["sel"], inter["w"], inter["counts"], inter["offsets"], inter["perm"])
         check_output(res["out"], ref, label)
+
+
+@pytest.mark.parametrize("bs", [64, 128, 256])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_tiled_scale_block_spans(torch, bs, bits):
+    # the tiled kernels fold block sums once per span of one K step (64-code
+    # blocks) or two K steps (128 codes and more); ragged expert tiles, both
+    # activations, K of 6 or 10 K steps so that the six-step unroll leaves
+    # a remainder
+    rng = np.random.default_rng(500 + bs + bits)
+    for act, (T, H, I) in (("swiglu", (200, 768, 256)), ("relu", (150, 512, 640))):
+        if H % bs or I % bs:
+            continue
+        w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=5, inter=I, k=2, bits=bits, block_size=bs,
+                             activation=act)
+        _full_check(w, a, torch, f"tiled bs{bs} bits{bits} {act} T{T} H{H} I{I}")
