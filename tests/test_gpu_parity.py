@@ -342,3 +342,23 @@ def test_tiled_scale_block_spans(torch, bs, bits):
         w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=5, inter=I, k=2, bits=bits, block_size=bs,
                              activation=act)
         _full_check(w, a, torch, f"tiled bs{bs} bits{bits} {act} T{T} H{H} I{I}")
+
+
+@pytest.mark.parametrize("case", [
+    # (T, H, E, I, k, bits, bs, act): one 16-row tile per expert with K-range
+    # partials on the streaming path, many experts with tokens (dozens of
+    # tiles, grids of several rounds), every scale layout the single-stage
+    # kernel takes, and I = 1152 leaving a partial row block
+    (16, 2048, 64, 1024, 8, 4, 64, "swiglu"),
+    (16, 2048, 64, 1024, 8, 4, 0, "relu"),
+    (10, 2048, 48, 1536, 6, 8, 32, "swiglu"),
+    (7, 2048, 16, 2048, 2, 4, 256, "relu"),
+    (12, 2048, 24, 1536, 5, 8, 128, "swiglu"),
+    (16, 2048, 32, 1152, 4, 4, 128, "relu"),
+])
+def test_stream_many_experts(torch, case):
+    T, H, E, I, k, bits, bs, act = case
+    rng = np.random.default_rng(900 + T + E + bits)
+    w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=E, inter=I, k=k, bits=bits, block_size=bs,
+                         activation=act)
+    _full_check(w, a, torch, f"many experts T{T} H{H} E{E} I{I} k{k} bits{bits} bs{bs} {act}")
