@@ -894,6 +894,8 @@ hipError_t pick_mode(bool fc1, bool one, int mt, int rb, const GemmArgs& g, dim3
 
 }  // namespace
 
+// Row blocks per workgroup: two for one-stage launches at mt == 1 when
+// they tile N exactly.
 // Row blocks per workgroup: two for one-stage launches at mt == 1 when they
 // tile N exactly.
 static int stream_row_blocks(int mt, bool one, int N) { return one && mt == 1 && N % (2 * kWGRows) == 0 ? 2 : 1; }
