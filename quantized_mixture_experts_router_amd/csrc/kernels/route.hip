@@ -4,6 +4,7 @@
 //   qmoe_scan          per-expert counts, exclusive offsets, chunk bases, M-tile table
 //   qmoe_scatter       stable expert-sorted slot order (perm)
 //   qmoe_route_small   all of the above in one workgroup (<= 1024 slots)
+//   qmoe_route_wave    all of the above in one wavefront (<= 64 tokens, E * k <= 64)
 //   qmoe_prep_a        fp32 tokens -> f16 hi/lo operand rows (see common.hpp)
 //
 // Routing follows the QMoE WebGPU manifest (description: softmax over the
@@ -311,6 +312,140 @@ __global__ void __launch_bounds__(1024) qmoe_route_small(const float* __restrict
   if (trows && threadIdx.x < E) write_tile_rows(s_perm, off_e, c, tile0, bm, trows);
 }
 
+// The whole front end in one wavefront when every token fits a lane and the
+// selection is short (T <= 64, E <= EV <= 64, E * k <= 64, tiles of at least
+// 16 rows): lane t routes
+// token t from its logits in registers (the key order of route_token, k
+// passes over the E keys), experts are counted with LDS atomics, lane e
+// scans expert e's count and tile count, and the stable scatter places the
+// slots of each expert in token order with one ballot per expert (a
+// token's k experts are distinct, so its slots of one expert are at most
+// one).  No barrier spans more than one wavefront.
+template <int EV>
+__global__ void __launch_bounds__(64) qmoe_route_wave(const float* __restrict__ logits, int T, int E, int k,
+                                                      int routing, int normalize, int bm,
+                                                      int* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                      int* __restrict__ counts, int* __restrict__ offsets,
+                                                      int* __restrict__ perm, int* __restrict__ tiles,
+                                                      int* __restrict__ ntiles, int* __restrict__ trows) {
+  // S <= 1024 slots and tile rows of at least 16: at most 64 + 64 tiles
+  __shared__ int s_cnt[64];
+  __shared__ int s_perm[1024];
+  __shared__ int s_tile[2 * 128];  // (first sorted position, rows) of each tile
+  const int lane = threadIdx.x;
+  const int S = T * k;
+  const bool tok = lane < T;
+  s_cnt[lane] = 0;
+  float v[EV];
+#pragma unroll
+  for (int e = 0; e < EV; ++e) {
+    const float x = (tok && e < E) ? logits[(size_t)lane * E + e] : -INFINITY;
+    v[e] = (x != x) ? -INFINITY : x;
+  }
+  __syncthreads();
+  // Selection: pass r takes the best key strictly after pass r - 1's.
+  int sel[EV];
+  float pv = INFINITY, v0 = 0.f, sum_sel = 0.f;
+  int pi = -1;
+  float ex[EV];
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int e = 0; e < EV; ++e)
+      if (e < E && key_before(pv, pi, v[e], e) && key_before(v[e], e, bv, bi)) {
+        bv = v[e];
+        bi = e;
+      }
+    bi = min(max(bi, 0), E - 1);
+    pv = bv;
+    pi = bi;
+    if (r == 0) v0 = bv;
+    const float x = expf(bv - v0);
+    sum_sel += x;
+#pragma unroll
+    for (int q = 0; q < EV; ++q)
+      if (q == r) {
+        sel[q] = bi;
+        ex[q] = x;
+      }
+  }
+  float denom = sum_sel;
+  if (routing == 1 && !normalize) {
+    // Full softmax over all experts, taken at the selection.
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < EV; ++e)
+      if (e < E) part += expf(v[e] - v0);
+    denom = part;
+  }
+  if (tok) {
+#pragma unroll
+    for (int q = 0; q < EV; ++q)
+      if (q < k) {
+        topk_idx[lane * k + q] = sel[q];
+        topk_w[lane * k + q] = ex[q] / denom;
+        atomicAdd(&s_cnt[sel[q]], 1);
+      }
+  }
+  __syncthreads();
+  // Counts, exclusive offsets and tile counts of expert e in lane e.
+  const int c = lane < E ? s_cnt[lane] : 0;
+  const int nt = (c + bm - 1) / bm;
+  int inc = c, inct = nt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int a = __shfl_up(inc, off);
+    const int b = __shfl_up(inct, off);
+    if (lane >= off) {
+      inc += a;
+      inct += b;
+    }
+  }
+  const int off_e = inc - c, tile0 = inct - nt;
+  const int ntot = __shfl(inct, 63);
+  if (lane < E) {
+    counts[lane] = c;
+    offsets[lane] = off_e;
+    for (int i = 0; i < nt; ++i) {
+      int* tp = tiles + 4 * (tile0 + i);
+      tp[0] = lane;
+      tp[1] = off_e + i * bm;
+      tp[2] = min(bm, c - i * bm);
+      tp[3] = 0;
+      s_tile[2 * (tile0 + i)] = off_e + i * bm;
+      s_tile[2 * (tile0 + i) + 1] = min(bm, c - i * bm);
+    }
+  }
+  if (lane == 0) {
+    offsets[E] = S;
+    ntiles[0] = ntot;
+  }
+  // Stable scatter: slots of expert e in token order.
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int e = 0; e < E; ++e) {
+    int slot = -1;
+#pragma unroll
+    for (int q = 0; q < EV; ++q)
+      if (q < k && sel[q] == e) slot = lane * k + q;
+    const bool has = tok && slot >= 0;
+    const unsigned long long m = __ballot(has);
+    const int base = __shfl(off_e, e);
+    if (has) {
+      const int pos = base + __popcll(m & below);
+      perm[pos] = slot;
+      s_perm[pos] = slot;
+    }
+  }
+  __syncthreads();
+  // Tile rows: rows past a tile's count repeat its last row.
+  if (trows)
+    for (int j = lane; j < ntot * bm; j += 64) {
+      const int t = j / bm, r = j - t * bm;
+      trows[j] = s_perm[s_tile[2 * t] + min(r, s_tile[2 * t + 1] - 1)];
+    }
+}
+
 // Tile-row table after the multi-kernel permutation: one thread per
 // (tile, row) entry; entries of unused tiles are left alone.
 __global__ void __launch_bounds__(256) qmoe_tile_rows(const int* __restrict__ perm, const int* __restrict__ tiles,
@@ -386,6 +521,17 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int rout
                               int* topk_idx, float* topk_w, int* counts, int* offsets, int* perm, int* tiles,
                               int* ntiles, int* trows, hipStream_t st) {
   if (T * k > 1024 || E > 1024) return hipErrorInvalidValue;
+  if (T <= 64 && E <= 64 && E * k <= 64 && bm >= 16) {
+#define QMOE_ROUTE_WAVE(EVV)                                                                                      \
+  hipLaunchKernelGGL(qmoe_route_wave<EVV>, dim3(1), dim3(64), 0, st, logits, T, E, k, routing, normalize, bm,     \
+                     topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows)
+    if (E <= 8) QMOE_ROUTE_WAVE(8);
+    else if (E <= 16) QMOE_ROUTE_WAVE(16);
+    else if (E <= 32) QMOE_ROUTE_WAVE(32);
+    else QMOE_ROUTE_WAVE(64);
+#undef QMOE_ROUTE_WAVE
+    return hipGetLastError();
+  }
   const int V = (E + 63) / 64;
 #define QMOE_ROUTE_SMALL(VV)                                                                                       \
   hipLaunchKernelGGL(qmoe_route_small<VV>, dim3(1), dim3(1024), 0, st, logits, T, E, k, routing, normalize, bm,  \

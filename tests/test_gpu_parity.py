@@ -362,3 +362,26 @@ def test_stream_many_experts(torch, case):
     w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=E, inter=I, k=k, bits=bits, block_size=bs,
                          activation=act)
     _full_check(w, a, torch, f"many experts T{T} H{H} E{E} I{I} k{k} bits{bits} bs{bs} {act}")
+
+
+@pytest.mark.parametrize("case", [
+    # (T, E, k, routing, normalize): the single-wavefront front end (T <= 64,
+    # E * k <= 64) and the workgroup one beside it, with signed zeros and
+    # repeated logits in every row
+    (16, 8, 2, "qmoe", 0), (64, 64, 1, "qmoe", 0), (37, 16, 4, "moe", 0), (50, 32, 2, "moe", 1),
+    (64, 8, 8, "qmoe", 0), (65, 8, 2, "qmoe", 0), (20, 40, 2, "moe", 0), (9, 64, 2, "qmoe", 0),
+])
+def test_front_end_ties_and_zeros(torch, case):
+    T, E, k, routing, normalize = case
+    rng = np.random.default_rng(77 + T + E + k)
+    w = W.Workload("front", (T, 64), E, 32, k, 8, 0, "relu", (0.01, 0.02))
+    a = W.generate(w, seed=int(rng.integers(0, 2**31 - 1)))
+    # logits drawn from a few values (ties everywhere), with -0.0 and +0.0
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 0.25, 1.0, 2.0], dtype=np.float32)
+    a["router_probs"] = vals[rng.integers(0, len(vals), size=(T, E))]
+    attrs = dict(w.attrs(), routing=routing, normalize_routing_weights=normalize)
+    res = run_gpu(a, attrs, torch)
+    ref, inter = oracle.qmoe(*a.values(), attrs=attrs, return_intermediates=True)
+    check_routing(res, inter["sel"], inter["w"], inter["counts"], inter["offsets"], inter["perm"],
+                  selected_softmax=(routing == "qmoe" or normalize == 1))
+    check_output(res["out"], ref, f"front end T{T} E{E} k{k} {routing}")
