@@ -74,7 +74,7 @@ hipError_t launch_tiled(int bits, int epi, const GemmArgs& g, int max_tiles, hip
 // z < splits K ranges of g.nst stages each.
 // wg_rows: double-buffered mode, weight rows per workgroup (a multiple of 64
 // up to 512, above 256 only for mt == 1; 0 = 256).
-size_t stream_lds_bytes(int bits, int mt, bool one, int N);
+size_t stream_lds_bytes(int bits, int mt, bool one, int rb);  // rb: row blocks per one-stage workgroup
 hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, const GemmArgs& g, int max_tiles,
                          hipStream_t st);
 

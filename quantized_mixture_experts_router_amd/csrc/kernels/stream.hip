@@ -894,17 +894,23 @@ hipError_t pick_mode(bool fc1, bool one, int mt, int rb, const GemmArgs& g, dim3
 
 }  // namespace
 
-// Row blocks per workgroup: two for one-stage launches at mt == 1 when
-// they tile N exactly.
 // Row blocks per workgroup: two for one-stage launches at mt == 1 when they
-// tile N exactly.
-static int stream_row_blocks(int mt, bool one, int N) { return one && mt == 1 && N % (2 * kWGRows) == 0 ? 2 : 1; }
+// tile N exactly and the grid still holds at least three rounds of
+// workgroups (two resident on each of 256 compute units); with fewer rounds
+// the idle share of the last round costs more than the shared staging saves
+// (the decode FC2: 896 workgroups of two row blocks, 62 us, against 1792 of
+// one, 60 us; its FC1: 1792 of two, 110 us, against 3584 of one, 112 us).
+static int stream_row_blocks(int mt, bool one, int N, int splits, int max_tiles) {
+  if (!(one && mt == 1 && N % (2 * kWGRows) == 0)) return 1;
+  const long wgs = (long)splits * max_tiles * (N / (2 * kWGRows));
+  return wgs >= 3 * 512 ? 2 : 1;
+}
 
-size_t stream_lds_bytes(int bits, int mt, bool one, int N) {
+size_t stream_lds_bytes(int bits, int mt, bool one, int rb) {
   const int item_codes = bits == 4 ? 256 : 128;
   const size_t stage = (size_t)16 * mt * stream_stage_items(mt, one) * item_codes * 4;
   // output tile: the workgroup's rows (one stage) or one row block
-  const int tile_rb = one ? stream_row_blocks(mt, one, N) : 1;
+  const int tile_rb = one ? rb : 1;
   return std::max((one ? 1 : 2) * stage, (size_t)16 * mt * kWGRows * tile_rb * 4);
 }
 
@@ -912,7 +918,7 @@ hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, co
                          hipStream_t st) {
   if (mt < 1 || mt > 4 || (one && g_in.nst != 1) || g_in.trows == nullptr) return hipErrorInvalidValue;
   GemmArgs g = g_in;
-  int rb = stream_row_blocks(mt, one, g.N);
+  int rb = stream_row_blocks(mt, one, g.N, splits, max_tiles);
   if (!one) {
     if (wg_rows == 0) wg_rows = kWGRows;
     if (wg_rows % 64 != 0 || wg_rows > 2 * kWGRows || (wg_rows > kWGRows && mt != 1)) return hipErrorInvalidValue;
@@ -921,7 +927,7 @@ hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, co
     wg_rows = kWGRows * rb;
   }
   g.wg_rows = wg_rows;
-  const size_t lds = stream_lds_bytes(bits, mt, one, g.N);
+  const size_t lds = stream_lds_bytes(bits, mt, one, one ? rb : 1);
   const dim3 grid(splits, max_tiles, (g.N + wg_rows - 1) / wg_rows);
   const bool fc1 = g.a_f32 != 0;
   return bits == 4 ? pick_mode<4>(fc1, one, mt, rb, g, grid, lds, st) : pick_mode<8>(fc1, one, mt, rb, g, grid, lds, st);
