@@ -1,0 +1,89 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the algorithmic
+byte and FLOP counts behind the roofline, the roofline classification, the
+kernel the plan picks per workload, and the rule that counter-derived HBM
+traffic is reported only for the kernel source it was measured on."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from quantized_mixture_experts_router_amd import workloads as W  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_decode_algorithmic_bytes():
+    # int4 codes two to a byte, one fp32 scale per 64 codes of a row; FC1 rows
+    # are the interleaved gate/linear pairs (2 * inter), FC2 rows the hidden size
+    w = W.WORKLOADS["decode"]
+    counts = np.full(w.experts, 4)
+    fc1, fc2 = bench.kernel_work(w, counts)
+    E, H, I, T, k = 8, 4096, 14336, 16, 2
+    fc1_weights = E * (2 * I) * (H // 2 + (H // 64) * 4)
+    fc2_weights = E * H * (I // 2 + (I // 64) * 4)
+    assert fc1["weight_bytes"] == fc1_weights
+    assert fc1["bytes"] == fc1_weights + T * H * 4 + T * k * I * 4 == 530579456
+    assert fc2["bytes"] == fc2_weights + T * k * I * 4 + T * k * H * 4
+    assert fc1["flops"] == 2.0 * T * k * 2 * I * H
+
+
+def test_unused_experts_are_not_counted():
+    w = W.WORKLOADS["decode"]
+    counts = np.array([3, 0, 5, 0, 0, 8, 16, 0])
+    fc1, _ = bench.kernel_work(w, counts)
+    full, _ = bench.kernel_work(w, np.ones(8))
+    assert fc1["used_experts"] == 4
+    assert fc1["weight_bytes"] * 2 == full["weight_bytes"]
+
+
+def test_roofline_bound_follows_intensity():
+    # decode FC1: about 14 FLOP/B, far below the f16 ridge (2500 TFLOP/s over
+    # 8 TB/s = 312.5 FLOP/B)
+    w = W.WORKLOADS["decode"]
+    fc1, _ = bench.kernel_work(w, np.ones(8))
+    r = bench.roofline_for(fc1, 0.1)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["achieved"] - fc1["bytes"] / 1e-4 / 1e9) < 0.1
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
+    # prefill FC1: thousands of FLOP/B, matrix-core bound
+    w = W.WORKLOADS["prefill"]
+    fc1, _ = bench.kernel_work(w, np.ones(8))
+    r = bench.roofline_for(fc1, 4.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert abs(r["achieved"] - fc1["flops"] / 4e-3 / 1e12) < 0.1
+
+
+def test_kernel_choice_per_workload():
+    assert bench.gemm_kernel(W.WORKLOADS["tiny"]) == "qmoe_stream"
+    assert bench.gemm_kernel(W.WORKLOADS["decode"]) == "qmoe_stream"
+    for name in ("prefill", "fine", "large_e"):
+        assert bench.gemm_kernel(W.WORKLOADS[name]) == "qmoe_tiled"
+    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1"]) == "qmoe_gmm_f32_rows16"
+    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_fine_fc1"]) == "qmoe_gmm_f32"
+
+
+def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel source\n")
+    rec = {"decode:fc1": {"kernel": "qmoe_stream", "source_sha": bench._sha(str(src)), "bytes": 123}}
+    tf = tmp_path / "traffic.json"
+    tf.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
+    monkeypatch.setitem(bench.KERNEL_SRC, "qmoe_stream", str(src))
+    assert bench.traffic_for("decode:fc1", "qmoe_stream") == 123
+    assert bench.traffic_for("decode:fc2", "qmoe_stream") is None      # never measured
+    assert bench.traffic_for("decode:fc1", "qmoe_tiled") is None       # another kernel
+    src.write_text("// kernel source, changed\n")
+    assert bench.traffic_for("decode:fc1", "qmoe_stream") is None      # source changed since
