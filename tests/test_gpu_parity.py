@@ -385,3 +385,30 @@ def test_front_end_ties_and_zeros(torch, case):
     check_routing(res, inter["sel"], inter["w"], inter["counts"], inter["offsets"], inter["perm"],
                   selected_softmax=(routing == "qmoe" or normalize == 1))
     check_output(res["out"], ref, f"front end T{T} E{E} k{k} {routing}")
+
+
+def test_two_streams_at_once(torch):
+    # two calls in flight together on two streams, each with its own
+    # workspace (the library keeps no per-call state of its own)
+    import quantized_mixture_experts_router_amd as qm
+    rng = np.random.default_rng(7100)
+    cases = [W.random_case(rng, tokens_shape=(16,), hidden=2048, experts=8, inter=1024, k=2, bits=4, block_size=64,
+                           activation="swiglu"),
+             W.random_case(rng, tokens_shape=(180,), hidden=256, experts=6, inter=192, k=3, bits=8, block_size=0,
+                           activation="relu")]
+    names = ("input", "router_probs", "fc1_experts_weights", "fc1_scales", "fc2_experts_weights", "fc2_scales")
+    runs = []
+    for w, a in cases:
+        args = [torch.from_numpy(np.ascontiguousarray(a[n])).cuda() for n in names]
+        attrs = w.attrs()
+        ws = torch.full((max(qm.qmoe_workspace_size(*args, attrs), 1),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = torch.full_like(args[0], float("nan"))
+        runs.append((w, a, args, attrs, ws, out, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for w, a, args, attrs, ws, out, st in runs:
+            qm.qmoe_forward(*args, attrs, out, ws, st)
+    torch.cuda.synchronize()
+    for w, a, args, attrs, ws, out, st in runs:
+        check_output(out.cpu().numpy(), oracle.qmoe(*[a[n] for n in names], attrs=attrs),
+                     f"two streams T{w.tokens}")
