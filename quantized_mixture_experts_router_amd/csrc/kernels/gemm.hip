@@ -276,14 +276,14 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
       const float w = topk_w[t * k + s];
       const float* src = slot_out + (t * k + s) * H + h;
       f32x4 y;
-      // eight partial rows in flight at a time, summed in range order
-      for (int z0 = 0; z0 < splits; z0 += 8) {
-        f32x4 v[8];
+      // sixteen partial rows in flight at a time, summed in range order
+      for (int z0 = 0; z0 < splits; z0 += 16) {
+        f32x4 v[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 16; ++i)
           if (z0 + i < splits) v[i] = *(const f32x4*)(src + (long)(z0 + i) * S * H);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 16; ++i)
           if (z0 + i < splits) y = (z0 + i == 0) ? v[i] : y + v[i];
       }
       acc += w * y;
