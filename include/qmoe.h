@@ -35,8 +35,11 @@
  *    |x| or |activation| at or above 65504 (the f16 range used by the matrix
  *    cores), are out of contract and produce unspecified (but bounded-time)
  *    results.
- *  - Entry points hold no global mutable state; calls on different streams
- *    with different workspaces may overlap.
+ *  - Entry points keep no state between calls (the only process-wide
+ *    record is which kernels were already granted more than 64 KB of LDS, set
+ *    once and thread-safely); calls on different streams with different
+ *    workspaces may overlap, and a call may be captured in a HIP graph (it
+ *    enqueues kernels only: no memset or copy nodes).
  */
 #ifndef QMOE_H_
 #define QMOE_H_
