@@ -272,6 +272,25 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
     const long t = (i * 4) / H;
     const int h = (int)((i * 4) % H);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (splits == 1) {
+      // one partial row per slot: eight slots' rows in flight at a time,
+      // weighted and summed in slot order
+      for (int s0 = 0; s0 < k; s0 += 8) {
+        f32x4 v[8];
+        float wv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (s0 + i < k) {
+            wv[i] = topk_w[t * k + s0 + i];
+            v[i] = *(const f32x4*)(slot_out + (t * k + s0 + i) * H + h);
+          }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (s0 + i < k) acc += wv[i] * v[i];
+      }
+      *(f32x4*)(out + t * H + h) = acc;
+      return;
+    }
     for (int s = 0; s < k; ++s) {
       const float w = topk_w[t * k + s];
       const float* src = slot_out + (t * k + s) * H + h;

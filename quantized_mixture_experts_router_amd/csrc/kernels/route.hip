@@ -204,17 +204,30 @@ __global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nc
                                                   int* __restrict__ tiles, int* __restrict__ ntiles) {
   const int e = threadIdx.x;
   int c = 0;
+  // eight chunks' counts in flight at a time (one round trip per eight)
   if (e < E) {
-    for (int ch = 0; ch < nchunks; ++ch) {
-      int* h = hist + (size_t)ch * E + e;
-      const int v = *h;
-      *h = c;  // exclusive prefix over chunks
-      c += v;
+    for (int ch0 = 0; ch0 < nchunks; ch0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ch0 + i < nchunks ? hist[(size_t)(ch0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (ch0 + i < nchunks) {
+          hist[(size_t)(ch0 + i) * E + e] = c;  // exclusive prefix over chunks
+          c += v[i];
+        }
     }
   }
   const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles);
   if (e < E)
-    for (int ch = 0; ch < nchunks; ++ch) hist[(size_t)ch * E + e] += off_e;
+    for (int ch0 = 0; ch0 < nchunks; ch0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ch0 + i < nchunks ? hist[(size_t)(ch0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (ch0 + i < nchunks) hist[(size_t)(ch0 + i) * E + e] = v[i] + off_e;
+    }
 }
 
 // Stable scatter: slot s (expert e) goes to base[chunk][e] + (number of slots
