@@ -231,18 +231,22 @@ __global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nc
 }
 
 // Stable scatter: slot s (expert e) goes to base[chunk][e] + (number of slots
-// of the same chunk with expert e and a smaller slot id).
-__global__ void __launch_bounds__(256) qmoe_scatter(const int* __restrict__ topk_idx, const int* __restrict__ hist,
-                                                    int S, int E, int chunk, int* __restrict__ perm) {
+// of the same chunk with expert e and a smaller slot id).  A workgroup of
+// kScatterWaves wavefronts takes 64 * kScatterWaves slots a round.
+constexpr int kScatterWaves = 8;
+__global__ void __launch_bounds__(64 * kScatterWaves) qmoe_scatter(const int* __restrict__ topk_idx,
+                                                                   const int* __restrict__ hist, int S, int E,
+                                                                   int chunk, int* __restrict__ perm) {
+  constexpr int NT = 64 * kScatterWaves;
   extern __shared__ int sm[];
   int* base = sm;          // [E]
-  int* wcnt = sm + E;      // [4][E]
+  int* wcnt = sm + E;      // [kScatterWaves][E]
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += 256) base[e] = hist[(size_t)blockIdx.x * E + e];
+  for (int e = threadIdx.x; e < E; e += NT) base[e] = hist[(size_t)blockIdx.x * E + e];
   const int s0 = blockIdx.x * chunk;
   const int s1 = min(S, s0 + chunk);
-  for (int r0 = s0; r0 < s1; r0 += 256) {
-    for (int i = threadIdx.x; i < 4 * E; i += 256) wcnt[i] = 0;
+  for (int r0 = s0; r0 < s1; r0 += NT) {
+    for (int i = threadIdx.x; i < kScatterWaves * E; i += NT) wcnt[i] = 0;
     __syncthreads();
     const int s = r0 + threadIdx.x;
     const bool valid = s < s1;
@@ -265,8 +269,12 @@ __global__ void __launch_bounds__(256) qmoe_scatter(const int* __restrict__ topk
       perm[pos] = s;
     }
     __syncthreads();
-    for (int ee = threadIdx.x; ee < E; ee += 256)
-      base[ee] += wcnt[ee] + wcnt[E + ee] + wcnt[2 * E + ee] + wcnt[3 * E + ee];
+    for (int ee = threadIdx.x; ee < E; ee += NT) {
+      int add = 0;
+#pragma unroll
+      for (int ww = 0; ww < kScatterWaves; ++ww) add += wcnt[ww * E + ee];
+      base[ee] += add;
+    }
     __syncthreads();
   }
 }
@@ -562,7 +570,8 @@ hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchu
                           int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st) {
   hipLaunchKernelGGL(qmoe_hist, dim3(nchunks), dim3(256), E * sizeof(int), st, topk_idx, S, E, chunk, hist);
   hipLaunchKernelGGL(qmoe_scan, dim3(1), dim3(1024), 0, st, hist, nchunks, E, S, bm, counts, offsets, tiles, ntiles);
-  hipLaunchKernelGGL(qmoe_scatter, dim3(nchunks), dim3(256), 5 * E * sizeof(int), st, topk_idx, hist, S, E, chunk, perm);
+  hipLaunchKernelGGL(qmoe_scatter, dim3(nchunks), dim3(64 * kScatterWaves), (1 + kScatterWaves) * E * sizeof(int), st,
+                     topk_idx, hist, S, E, chunk, perm);
   return hipGetLastError();
 }
 
