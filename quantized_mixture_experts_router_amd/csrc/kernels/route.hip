@@ -492,13 +492,28 @@ __global__ void __launch_bounds__(256) qmoe_prep_a(const float* __restrict__ x, 
   if (gid < groups) {
     const int t = gid / (kp / 8);
     const int g = gid % (kp / 8);
+    // a storage group holds 8 consecutive codes from j0 (permuted inside the
+    // group): two 16-byte loads when they are all in the row and H keeps
+    // rows 16-byte aligned (the input itself is), else one load a code
+    const int j0 = code_of_storage<BITS>(g * 8);
+    const float* row = x + (size_t)t * H;
+    float v[8];
+    if ((H & 3) == 0 && j0 + 8 <= H) {
+      const f32x4 a0 = *(const f32x4*)(row + j0), a1 = *(const f32x4*)(row + j0 + 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[c] = a0[c];
+        v[c + 4] = a1[c];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = j0 + c < H ? row[j0 + c] : 0.f;
+    }
     f16x8 hi, lo;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int c = code_of_storage<BITS>(g * 8 + i);
-      const float v = c < H ? x[(size_t)t * H + c] : 0.f;
       _Float16 h, l;
-      split_f16(v, h, l);
+      split_f16(v[code_of_storage<BITS>(g * 8 + i) - j0], h, l);
       hi[i] = h;
       lo[i] = l;
     }
