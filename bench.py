@@ -3,9 +3,13 @@
 
 One step = one full qmoe_forward (router, permutation, operand prep, FC1 +
 activation, FC2, combine) over one batch of seeded synthetic input already
-resident in HBM; by default 200 warm-up steps, then 500 timed steps.  Default workload: the Mixtral-like int4 decode layer
-(16 tokens x hidden 4096, 8 experts, inter 14336, k = 2, interleaved SwiGLU,
-block size 64).  Prints one JSON line.
+resident in HBM.  Before the W warm-up steps, steps run back to back for
+--settle-ms of wall time (untimed) so that the GPU is at its steady clocks;
+then exactly K steps are timed.  Default workload: the Mixtral-like int4
+decode layer (16 tokens x hidden 4096, 8 experts, inter 14336, k = 2,
+interleaved SwiGLU, block size 64); the same JSON line also carries the
+prefill layer (2 x 2048 tokens, same experts, block size 128) under
+"prefill", timed the same way.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 
@@ -51,9 +55,18 @@ def _args():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="decode")
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
+                    help="untimed back-to-back steps for this long before the warm-up (steady GPU clocks)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode workload only: skip the prefill entry of the JSON line")
+    ap.add_argument("--prefill-steps", type=int, default=0,
+                    help="timed steps of the prefill entry (default: the decode steps, clamped to 10..40)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stage-timing", action="store_true")
     ap.add_argument("--no-latency", action="store_true", help="skip the per-call warm/cold latency percentiles")
+    ap.add_argument("--crossover", default="", metavar="T1,T2,...",
+                    help="time the weight-streaming and the tiled GEMM paths (QMOE_PATH) on the decode layer's "
+                         "experts at these token counts; one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -64,7 +77,7 @@ def kernel_work(w, counts):
     import numpy as np
     used = int(np.count_nonzero(counts))
     T, H, E, I, k = w.tokens, w.hidden, w.experts, w.inter, w.k
-    S = T * k
+    S = int(np.sum(counts))  # slots on the experts the weights hold (all T * k slots unless a share)
     F = w.fusion * I
     nb1 = H // w.block_size if w.block_size else 1
     nb2 = I // w.block_size if w.block_size else 1
@@ -108,32 +121,49 @@ def stage_times(qm, call_debug, steps):
     return dict(zip(("routing", "fc1", "fc1_act", "fc2", "combine"), [s / steps for s in sums]))
 
 
-def cpu_baseline(w, arrs, budget_s=12.0, max_reps=8):
-    """Time the float64 oracle on the host cores over a bounded sample of the
-    workload: the whole batch, repeated until about budget_s seconds of work
-    (small batches), or its first tokens (large batches)."""
-    import oracle
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # threadpoolctl missing: numpy runs single threaded loops
-        threads = 1
+        return 1
+
+
+def timed_runs(run, budget_s, max_reps):
+    """One untimed warm-up run, then timed runs until about budget_s seconds
+    (at least one, at most max_reps): per-run seconds."""
+    run()
+    ts = []
+    t0 = time.perf_counter()
+    while len(ts) < max_reps and (not ts or time.perf_counter() - t0 < budget_s):
+        t = time.perf_counter()
+        run()
+        ts.append(time.perf_counter() - t)
+    return ts
+
+
+def cpu_baseline(w, arrs, budget_s=12.0, max_reps=8):
+    """Time the float64 oracle on the host cores over a bounded sample of the
+    workload (the whole batch for small batches, its first 4 tokens for large
+    ones): one warm-up run, then timed runs up to about budget_s seconds;
+    tokens/s from the median run."""
+    import numpy as np
+
+    import oracle
     attrs = w.attrs()
     ids = list(range(w.tokens)) if w.tokens <= 16 else list(range(4))
-    done, reps = 0, 0
-    t0 = time.perf_counter()
-    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < budget_s):
-        oracle.qmoe_tokens(ids, *arrs.values(), attrs=attrs)
-        done += len(ids)
-        reps += 1
-    dt = time.perf_counter() - t0
+    ts = timed_runs(lambda: oracle.qmoe_tokens(ids, *arrs.values(), attrs=attrs), budget_s, max_reps)
+    med = float(np.median(ts))
+    model, cores = cpu_info()
     if w.tokens <= 16:
-        sample = (f"all {w.tokens} tokens of the workload x {reps} repetitions "
-                  "(every used expert dequantised once per repetition)")
+        sample = (f"all {w.tokens} tokens of the workload; 1 warm-up run, median of {len(ts)} timed runs "
+                  "(every used expert dequantised in float64 once per run)")
     else:
-        sample = f"first 4 tokens of the workload x {reps} repetitions (their experts dequantised once per repetition)"
-    return dict(value=round(done / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=sample, seconds=round(dt, 2))
+        sample = (f"first 4 tokens of the workload; 1 warm-up run, median of {len(ts)} timed runs "
+                  "(their experts dequantised in float64 once per run)")
+    return dict(value=round(len(ids) / med, 4), unit="tokens/s", cores=int(_blas_threads()), kind="oracle",
+                sample=sample, seconds_per_run=round(med, 3), runs=len(ts), cpu_model=model,
+                cores_available=int(cores))
 
 
 def _sha(path):
@@ -160,13 +190,36 @@ def gmm_kernel(w):
     return "qmoe_gmm_f32_rows16" if rows16 else "qmoe_gmm_f32"
 
 
-def gemm_kernel(w):
-    """Which grouped-GEMM kernel the library runs for this workload (the
-    library's plan: weight streaming up to 64 tokens, the LDS-tiled GEMM for
+def stream_fits(w, K):
+    """Whether the planner streams a GEMM of reduction length K at this
+    workload's token count: whole stages of 128-byte row items (one stage of
+    4, 2 or 1 items at 16, 32 or 48-64 rows per tile, at most 16 K ranges;
+    else stages of 2 items at 16 rows, 1 above), and 32-code scale blocks
+    4 to 16 to a stage."""
+    mt = min((w.tokens + 15) // 16, 4)
+    item = 256 if w.bits == 4 else 128
+    bs = w.block_size
+
+    def fits(codes):
+        if not (K > 0 and K % codes == 0 and (bs == 0 or bs >= 32)):
+            return False
+        if 0 < bs < item // 2:
+            return (codes // bs) % 4 == 0 and codes // bs <= 16
+        return True
+    one = {1: 4, 2: 2}.get(mt, 1) * item
+    if fits(one) and K // one <= 16:
+        return True
+    return fits((2 if mt == 1 else 1) * item)
+
+
+def gemm_kernel(w, which="fc1"):
+    """Which grouped-GEMM kernel the library runs for one GEMM of this
+    workload (the library's plan: weight streaming up to 64 tokens when the
+    reduction length fits its stages, the LDS-tiled GEMM above 64 tokens for
     64-multiple H and I with column-wise or >= 32-code scale blocks, else the
     register-tiled one)."""
     if w.tokens <= 64:
-        return "qmoe_stream"
+        return "qmoe_stream" if stream_fits(w, w.hidden if which == "fc1" else w.inter) else "qmoe_gemm"
     tiled = w.hidden % 64 == 0 and w.inter % 64 == 0 and (w.block_size == 0 or w.block_size >= 32)
     return "qmoe_tiled" if tiled else "qmoe_gemm"
 
@@ -245,9 +298,10 @@ def gmm_cpu_baseline(w, a, budget_s=12.0, max_reps=64):
         done += len(rows)
         reps += 1
     dt = time.perf_counter() - t0
+    model, cores = cpu_info()
     return dict(value=round(done / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"first {len(rows)} token rows (all {w.S} selections each) x {reps} repetitions",
-                seconds=round(dt, 2))
+                seconds=round(dt, 2), cpu_model=model, cores_available=int(cores))
 
 
 def main_gmm(args):
@@ -271,6 +325,7 @@ def main_gmm(args):
     def step(events=None):
         qm.qmoe_grouped_matmul(d["input"], d["weights"], d["group_indices"], d["bias"], out, ws, stream, events)
 
+    settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -373,6 +428,7 @@ def main_moe(args):
     def step(debug=None):
         qm.qmoe_moe_forward(d, attrs, out, ws, stream, debug)
 
+    settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -424,9 +480,10 @@ def main_moe(args):
             done += len(ids)
             reps += 1
         dt = time.perf_counter() - t0
+        model, cores = cpu_info()
         cpu = dict(value=round(done / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
                    sample=f"first {len(ids)} tokens x {reps} repetitions (their experts' weights read in float64 "
-                          "per token)", seconds=round(dt, 2))
+                          "per token)", seconds=round(dt, 2), cpu_model=model, cores_available=int(cores))
 
     line = {
         "metric": "float MoE layer tokens/s + achieved GB/s or TFLOP/s vs peak",
@@ -454,29 +511,53 @@ def main_moe(args):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    args = _args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every run here uses a single MI355X); use --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.workload.startswith("gmm_"):
-        main_gmm(args)
-        return
-    if args.workload.startswith("moe_"):
-        main_moe(args)
-        return
+def cpu_info():
+    """Host CPU model (from /proc/cpuinfo) and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores
+
+
+def settle(step, settle_ms):
+    """Run the step back to back for about settle_ms of wall time (untimed),
+    so that the GPU reaches its steady clocks before the warm-up steps."""
+    import torch
+    if settle_ms <= 0:
+        return 0
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
+def measure_qmoe(w, steps, warmup, settle_ms, args, arrs=None):
+    """Time one QMoE workload: settle, warm-up, K timed steps (one step = one
+    qmoe_forward), then per-stage event timing, the roofline of the slower
+    GEMM, per-call latency and the oracle's CPU baseline.  Returns a dict of
+    the JSON fields."""
     import numpy as np
     import torch
 
     import quantized_mixture_experts_router_amd as qm
     from quantized_mixture_experts_router_amd import workloads as W
 
-    w = W.WORKLOADS[args.workload]
-    arrs = W.generate(w)
+    if arrs is None:
+        arrs = W.generate(w)
     torch.cuda.set_device(0)
     d = {k: torch.from_numpy(v).cuda() for k, v in arrs.items()}
     ins = [d[k] for k in ("input", "router_probs", "fc1_experts_weights", "fc1_scales", "fc2_experts_weights",
@@ -490,20 +571,21 @@ def main():
     def step():
         qm.qmoe_forward(*ins, attrs, out, ws, stream)
 
-    for _ in range(args.warmup):
+    settled = settle(step, settle_ms)
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = w.tokens * args.steps / elapsed
+    ms_per_step = elapsed * 1e3 / steps
+    value = w.tokens * steps / elapsed
 
     # routing counts (for the algorithmic work of the used experts)
-    counts_t = torch.empty(w.experts, dtype=torch.int32, device="cuda")
+    counts_t = torch.empty(w.held, dtype=torch.int32, device="cuda")  # over the experts the weights hold
     qm.qmoe_forward(*ins, attrs, out, ws, stream, debug={"counts": counts_t})
     torch.cuda.synchronize()
     counts = counts_t.cpu().numpy()
@@ -514,56 +596,155 @@ def main():
     if not args.no_stage_timing:
         def call_debug(events):
             qm.qmoe_forward(*ins, attrs, out, ws, stream, debug={"events": events})
-        stages = stage_times(qm, call_debug, args.steps)
+        stages = stage_times(qm, call_debug, steps)
         key = "fc1" if stages["fc1"] >= stages["fc2"] else "fc2"
         work = fc1_work if key == "fc1" else fc2_work
         roofline = roofline_for(work, stages[key])
-        kernel = gemm_kernel(w)
+        kernel = gemm_kernel(w, key)
         roofline["kernel"] = f"{kernel} ({key.upper()})"
         roofline["avg_ms"] = round(stages[key], 5)
         roofline["algorithmic_bytes"] = int(work["bytes"])
         roofline["algorithmic_flops"] = work["flops"]
-        roofline["traffic"] = traffic_for(f"{args.workload}:{key}", kernel)
+        roofline["traffic"] = traffic_for(f"{w.name}:{key}", kernel)
 
     # Per-call latency outside the throughput loop: warm (operands may sit in
     # L2 / the Infinity Cache from the previous call) and cold (a 1 GiB
     # buffer rewritten before every call).
     latency = None
     if not args.no_latency:
-        n = max(10, min(args.steps, 50))
+        n = max(10, min(steps, 50))
         evict = torch.empty(1 << 28, dtype=torch.float32, device="cuda").zero_()
         latency = dict(warm=call_latency(step, n), cold=call_latency(step, n, evict))
         del evict
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, arrs)
+    del ws, d, ins, out
+    torch.cuda.empty_cache()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, arrs)
 
     total_bytes = fc1_work["bytes"] + fc2_work["bytes"]
     total_flops = fc1_work["flops"] + fc2_work["flops"]
-    line = {
-        "metric": METRIC,
+    return {
         "value": round(value, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16 operands (fp32 activations as hi+lo f16), fp32 accumulate",
-        "data": "synthetic (seeded numpy draws per workload recipe; weights random uint8)",
-        "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden, "experts": w.experts,
-                   "inter": w.inter, "k": w.k, "bits": w.bits, "block_size": w.block_size,
-                   "activation": w.activation, "input_shape": list(w.input_shape)},
+        "steps": steps,
+        "warmup": warmup,
+        "settle_steps": settled,
+        "config": dict({"workload": w.name, "tokens": w.tokens, "hidden": w.hidden, "experts": w.experts,
+                        "inter": w.inter, "k": w.k, "bits": w.bits, "block_size": w.block_size,
+                        "activation": w.activation, "input_shape": list(w.input_shape)},
+                       **({"held_experts": w.held, "first_expert": w.first_expert} if w.local_experts else {})),
         "layer_hbm_gbs": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "layer_hbm_frac": round(total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "layer_mfma_frac": round(total_flops / (ms_per_step * 1e-3) / 1e12 / F16_DENSE_PEAK_TFLOPS, 4),
         "stage_ms": {k: round(v, 5) for k, v in stages.items()} if stages else None,
         "roofline": roofline,
         "latency_ms": latency,
         "cpu_baseline": cpu,
     }
+
+
+def main_crossover(args):
+    """Per-step time of the decode layer's experts (8 x int4, hidden 4096,
+    inter 14336, k = 2, block size 64) at several token counts, with the
+    GEMMs forced onto each path (QMOE_PATH = stream | tiled) and with the
+    plan's own choice."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import quantized_mixture_experts_router_amd as qm
+    from quantized_mixture_experts_router_amd import workloads as W
+
+    toks = [int(t) for t in args.crossover.split(",") if t]
+    base = W.WORKLOADS["decode"]
+    w = dataclasses.replace(base, name="crossover", input_shape=(max(toks), base.hidden))
+    a = W.generate(w)
+    torch.cuda.set_device(0)
+    d = {k: torch.from_numpy(v).cuda() for k, v in a.items()}
+    attrs = qm.make_attrs(w.attrs())
+    stream = torch.cuda.current_stream()
+    rows = []
+    for T in toks:
+        ins = [d["input"][:T], d["router_probs"][:T], d["fc1_experts_weights"], d["fc1_scales"],
+               d["fc2_experts_weights"], d["fc2_scales"]]
+        out = torch.empty_like(ins[0])
+        row = {"tokens": T}
+        for path in ("stream", "tiled", "auto"):
+            if path == "auto":
+                os.environ.pop("QMOE_PATH", None)
+            else:
+                os.environ["QMOE_PATH"] = path
+            ws = torch.empty(max(qm.qmoe_workspace_size(*ins, attrs), 1), dtype=torch.uint8, device="cuda")
+
+            def step():
+                qm.qmoe_forward(*ins, attrs, out, ws, stream)
+
+            settle(step, min(args.settle_ms, 300))
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                step()
+            torch.cuda.synchronize()
+            row[f"{path}_ms"] = round((time.perf_counter() - t0) * 1e3 / args.steps, 5)
+            del ws
+        os.environ.pop("QMOE_PATH", None)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        rows.append(row)
+    print(json.dumps({"crossover": rows, "layer": "decode experts (E 8, H 4096, I 14336, k 2, int4, bs 64)",
+                      "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every run here uses a single MI355X); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.crossover:
+        main_crossover(args)
+        return
+    if args.workload.startswith("gmm_"):
+        main_gmm(args)
+        return
+    if args.workload.startswith("moe_"):
+        main_moe(args)
+        return
+    from quantized_mixture_experts_router_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    head = measure_qmoe(w, args.steps, args.warmup, args.settle_ms, args)
+    line = {
+        "metric": METRIC,
+        "value": head.pop("value"),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 operands (fp32 activations as hi+lo f16 of a power-of-two scaled row), fp32 accumulate",
+        "data": "synthetic (seeded numpy draws per workload recipe; weights random uint8)",
+        "config": head.pop("config"),
+    }
+    head.pop("steps")
+    head.pop("warmup")
+    line.update(head)
+    # The metric names int4 decode and prefill: the decode line also carries
+    # the prefill layer (same experts, 4096 tokens), timed the same way.
+    if args.workload == "decode" and not args.no_prefill:
+        pw = W.WORKLOADS["prefill"]
+        psteps = args.prefill_steps or max(10, min(args.steps, 40))
+        pwarm = max(2, min(args.warmup, 10))
+        line["prefill"] = measure_qmoe(pw, psteps, pwarm, args.settle_ms, args)
     print(json.dumps(line), flush=True)
 
 

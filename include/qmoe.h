@@ -31,10 +31,16 @@
  *    synchronises, and enqueues all work on the caller's stream.
  *  - A non-OK status means nothing was enqueued and the output is untouched.
  *    On QMOE_OK every output element is written by work enqueued on stream.
- *  - Inputs that are finite are in contract; NaN/inf in x or logits, and
- *    |x| or |activation| at or above 65504 (the f16 range used by the matrix
- *    cores), are out of contract and produce unspecified (but bounded-time)
- *    results.
+ *  - Every finite input is in contract.  The matrix cores take f16 operands:
+ *    each fp32 operand row (a row of x for FC1, of the activation for FC2) is
+ *    multiplied by a power of two of its own, chosen so that its largest
+ *    magnitude lands in [2^13, 2^14), and split into f16 hi + lo; each row's
+ *    fp32 result is scaled back exactly.  An element is so carried to 2^-22
+ *    of itself plus 2^-39 of its row's largest magnitude, for rows of any
+ *    magnitude (GPU parity is tested on inputs scaled from 1e-7 to 1e5 and on
+ *    rows twelve orders of magnitude apart).  NaN/inf in x or logits are out
+ *    of contract and produce unspecified (but bounded-time) results; results
+ *    beyond the float32 range are infinite.
  *  - Entry points keep no state between calls (the only process-wide
  *    record is which kernels were already granted more than 64 KB of LDS, set
  *    once and thread-safely); calls on different streams with different
@@ -51,7 +57,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 2
+#define QMOE_ABI_VERSION 3
 
 typedef enum {
   QMOE_OK = 0,
@@ -120,21 +126,40 @@ typedef struct {
                                              branch to [-L, L] before the formula
                                              (a reading: no formula on the pages);
                                              read by SwiGLU only                  */
+  int32_t first_expert;              /* [0]  the weights' expert 0 is global
+                                             expert first_expert of the router's
+                                             E: the weights (and scales) hold
+                                             E_local = fc1 dims[0] consecutive
+                                             experts, 0 <= first_expert and
+                                             first_expert + E_local <= E
+                                             (QMOE_ERR_ATTR otherwise).  Routing
+                                             still ranks all E logits; slots
+                                             whose expert is not held contribute
+                                             nothing, so the output is this
+                                             share's part of the sum over slots
+                                             (one GPU's share when the experts
+                                             are spread over GPUs; the pages
+                                             define no such split).  E_local ==
+                                             E with first_expert 0 is the whole
+                                             operator; E_local == 0 gives zeros. */
 } qmoe_attrs;
 
 /* Stage boundaries at which qmoe_forward_debug records events. */
 #define QMOE_STAGE_EVENTS 6
 
 /* Optional outputs for parity checks and timing.  Any field may be NULL.
- * Device buffers: topk_idx, topk_w [T*k] (row t, slot s at t*k+s); counts
- * [E]; offsets [E+1]; perm [T*k] (slot id t*k+s at each expert-sorted
- * position, stable within an expert).
+ * Device buffers: topk_idx, topk_w [T*k] (row t, slot s at t*k+s; global
+ * expert indices); counts [E_local]; offsets [E_local+1]; perm [T*k] (slot id
+ * t*k+s at each expert-sorted position, stable within an expert; with
+ * E_local < E the slots of experts not held follow those of the held ones,
+ * in slot order, from offsets[E_local] on).
  * events: caller-created hipEvent_t handles recorded on the stream at
  *   [0] before the router, [1] after the routing front end (router,
- *   permutation, operand preparation), [2] after the FC1 GEMM, [3] after
- *   the FC1 activation pass (where FC1 writes split partials; else equal to
- *   [2]), [4] after the FC2 GEMM, [5] after the combine (before any debug
- *   copy).  Events are only recorded when T > 0 and I > 0. */
+ *   permutation, FC1 operand rows), [2] after the FC1 GEMM, [3] after the
+ *   FC2 operand rows (the FC1 activation pass where FC1 writes split
+ *   partials, the operand split where FC2 takes hi/lo rows), [4] after the
+ *   FC2 GEMM, [5] after the combine (before any debug copy).  Events are
+ *   only recorded when T > 0, I > 0 and E_local > 0. */
 typedef struct {
   int32_t* topk_idx;
   float* topk_w;

@@ -12,7 +12,7 @@ as a stated convention.
 """
 from .qmoe_oracle import (  # noqa: F401
     ContractError, validate, route, expert_permutation, dequantize, activation,
-    qmoe, qmoe_dense, qmoe_tokens, expert_ffn,
+    qmoe, qmoe_dense, qmoe_tokens, expert_ffn, local_experts,
 )
 from .grouped_matmul import grouped_matmul, grouped_matmul_rows  # noqa: F401
 from .moe_oracle import moe, moe_tokens, moe_validate, moe_activation, gelu  # noqa: F401

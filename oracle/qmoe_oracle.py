@@ -35,7 +35,12 @@ Readings taken where the pages are silent:
 * top-k order is descending logit, equal logits go to the lower expert index,
   and -0.0 equals +0.0;
 * the selected-logit softmax subtracts the largest selected logit;
-* the expert-sorted slot order is stable (ascending slot id t*k+s).
+* the expert-sorted slot order is stable (ascending slot id t*k+s);
+* a share of the experts (attribute ``first_expert``; the pages define no
+  split of the experts): the weights hold E_local consecutive experts from
+  global expert ``first_expert``; routing ranks all E logits as always, and
+  only slots whose expert is held contribute, so the shares of a partition of
+  the experts sum to the whole operator's output.
 
 Everything is float64; inputs are read exactly as stored.
 """
@@ -61,7 +66,7 @@ class ContractError(ValueError):
 DEFAULT_ATTRS = dict(activation_alpha=1.0, activation_beta=0.0, activation_type="relu",
                      expert_weight_bits=4, k=1, normalize_routing_weights=0, quant_type="int",
                      swiglu_fusion=0, use_sparse_mixer=0, weights_prepacked=-1, block_size=0,
-                     routing=ROUTING_QMOE, swiglu_limit=None)
+                     routing=ROUTING_QMOE, swiglu_limit=None, first_expert=0)
 
 
 def _attrs(attrs: dict | None) -> dict:
@@ -131,8 +136,12 @@ def validate(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None, out_shape=None) 
     E = logits.shape[1]
     if logits.shape[0] != T:
         raise ContractError("shape", "router rows must equal the token count")
-    if fc1_w.shape[0] != E or fc2_w.shape[0] != E:
+    El = fc1_w.shape[0]  # experts the weights hold (a share: fewer than E)
+    if El > E or fc2_w.shape[0] != El:
         raise ContractError("shape", "expert count mismatch")
+    first = int(a["first_expert"])
+    if first < 0 or first + El > E:
+        raise ContractError("attr", "first_expert + held experts must lie in [0, num_experts]")
     F = fc1_w.shape[1]
     if F % fusion != 0:
         raise ContractError("shape", "fc1 rows not divisible by the fusion size")
@@ -144,7 +153,7 @@ def validate(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None, out_shape=None) 
     if bs and (H % bs != 0 or I % bs != 0):
         raise ContractError("shape", "block_size must divide hidden and inter size")
     # quantScalesOk
-    if fc1_s.shape[:2] != (E, F) or fc2_s.shape[:2] != (E, H):
+    if fc1_s.shape[:2] != (El, F) or fc2_s.shape[:2] != (El, H):
         raise ContractError("shape", "scale leading dims")
     if bs == 0:
         if fc1_s.ndim != 2 or fc2_s.ndim != 2:
@@ -157,7 +166,7 @@ def validate(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None, out_shape=None) 
     if not (1 <= k <= E):
         raise ContractError("attr", "k must lie in [1, num_experts]")
     limit = swiglu_limit_of(a)
-    return dict(T=T, H=H, E=E, I=I, F=F, k=k, bits=bits, pack=pack, fusion=fusion, bs=bs,
+    return dict(T=T, H=H, E=E, El=El, first=first, I=I, F=F, k=k, bits=bits, pack=pack, fusion=fusion, bs=bs,
                 mid=8 if bits == 4 else 128, activation=act, alpha=float(a["activation_alpha"]),
                 beta=float(a["activation_beta"]), routing=a["routing"],
                 normalize=int(a["normalize_routing_weights"]), limit=limit)
@@ -203,6 +212,14 @@ def expert_permutation(sel, num_experts: int):
     offsets[1:] = np.cumsum(counts)
     perm = np.argsort(flat, kind="stable").astype(np.int64)
     return counts, offsets, perm
+
+
+def local_experts(sel, first: int, held: int):
+    """Index of each selected expert among the held ones [first, first +
+    held), or ``held`` for an expert not held."""
+    sel = np.asarray(sel)
+    inside = (sel >= first) & (sel < first + held)
+    return np.where(inside, sel - first, held)
 
 
 def unpack_codes(packed, bits: int):
@@ -279,13 +296,16 @@ def qmoe(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None, return_intermediates
     where they need the operator's output type).
     """
     d = validate(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs)
-    T, H, E, I, k = d["T"], d["H"], d["E"], d["I"], d["k"]
+    T, H, El, I, k = d["T"], d["H"], d["El"], d["I"], d["k"]
     xs = np.asarray(x, dtype=np.float32).reshape(T, H).astype(np.float64)
     sel, w = route(logits, k, d["routing"], d["normalize"])
-    counts, offsets, perm = expert_permutation(sel, E)
+    # slots grouped by held expert; the slots of experts not held form one
+    # more group after them (they contribute nothing)
+    local = local_experts(sel, d["first"], El)
+    counts, offsets, perm = expert_permutation(local, El + 1)
     slot_out = np.zeros((T * k, H), dtype=np.float64)
     if I > 0:
-        for e in range(E):
+        for e in range(El):
             if counts[e] == 0:
                 continue
             rows = perm[offsets[e]:offsets[e + 1]]
@@ -295,7 +315,7 @@ def qmoe(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None, return_intermediates
     out = (w.reshape(T, k, 1) * slot_out.reshape(T, k, H)).sum(axis=1)
     out = out.reshape(np.asarray(x).shape)
     if return_intermediates:
-        return out, dict(sel=sel, w=w, counts=counts, offsets=offsets, perm=perm, slot_out=slot_out)
+        return out, dict(sel=sel, w=w, counts=counts[:El], offsets=offsets[:El + 1], perm=perm, slot_out=slot_out)
     return out
 
 
@@ -313,8 +333,11 @@ def qmoe_tokens(token_ids, x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None):
     out = np.zeros((len(ids), H), dtype=np.float64)
     if d["I"] == 0:
         return out
-    for e in np.unique(sel):
-        hit = np.nonzero(sel == e)
+    local = local_experts(sel, d["first"], d["El"])
+    for e in np.unique(local):
+        if e == d["El"]:
+            continue  # expert not held
+        hit = np.nonzero(local == e)
         rows = hit[0]
         w1 = dequantize(fc1_w[e], fc1_s[e], d["bits"], d["bs"])
         w2 = dequantize(fc2_w[e], fc2_s[e], d["bits"], d["bs"])
@@ -340,8 +363,8 @@ def qmoe_dense(x, logits, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None):
     out = np.zeros((T, H), dtype=np.float64)
     for t in range(T):
         for s in range(k):
-            e = int(sel[t, s])
-            if d["I"] == 0:
+            e = int(sel[t, s]) - d["first"]
+            if d["I"] == 0 or not 0 <= e < d["El"]:
                 continue
             h = np.zeros(d["F"])
             for n in range(d["F"]):

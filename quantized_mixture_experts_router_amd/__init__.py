@@ -43,7 +43,7 @@ class QmoeAttrs(ctypes.Structure):
                 ("normalize_routing_weights", ctypes.c_int32), ("routing", ctypes.c_int32),
                 ("use_sparse_mixer", ctypes.c_int32), ("weights_prepacked", ctypes.c_int32),
                 ("quant_type", ctypes.c_int32), ("has_swiglu_limit", ctypes.c_int32),
-                ("swiglu_limit", ctypes.c_float)]
+                ("swiglu_limit", ctypes.c_float), ("first_expert", ctypes.c_int32)]
 
 
 class QmoeMoeAttrs(ctypes.Structure):

@@ -22,6 +22,7 @@ SOURCES = [
     "qmoe_gmm.cpp",
     "qmoe_moe.cpp",
     "kernels/route.hip",
+    "kernels/operand.hip",
     "kernels/gemm.hip",
     "kernels/stream.hip",
     "kernels/tiled.hip",

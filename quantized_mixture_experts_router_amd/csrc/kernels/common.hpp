@@ -16,11 +16,12 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------------------
 // Activation operand layout ("A rows").
 //
-// The matrix cores take f16 operands.  An fp32 activation v is carried as two
-// f16 values, hi = f16(v) and lo = f16(v - hi), so hi + lo keeps about 22
-// significant bits; each product runs twice (hi, then lo) into one fp32
-// accumulator.  Weights are exact small integers in f16, so the only rounding
-// is fp32 accumulation and the lo residual.
+// The matrix cores take f16 operands.  An fp32 activation v (scaled by a
+// power of two per row, see below) is carried as two f16 values,
+// hi = f16(v) and lo = f16(v - hi), so hi + lo keeps about 22 significant
+// bits; each product runs twice (hi, then lo) into one fp32 accumulator.
+// Weights are exact small integers in f16, so the only rounding is fp32
+// accumulation and the lo residual.
 //
 // A row holds Kp codes (Kp a multiple of 128, zero padded).  Codes are stored
 // in groups of 8: 16 bytes of hi halves then 16 bytes of lo halves, so one
@@ -44,23 +45,53 @@ __device__ __forceinline__ int code_group_of_lane(int g) {
   else return sigma8(g);
 }
 
-template <int BITS>
-__device__ __forceinline__ int storage_of_code(int j) {
-  const int g = (j >> 3) & 3;
-  if constexpr (BITS == 4) return (j & ~7) | slot4_of_code(j & 7);
-  else return (j & ~31) | (sigma8(g) << 3) | (j & 7);
-}
-template <int BITS>
-__device__ __forceinline__ int code_of_storage(int q) {
-  const int g = (q >> 3) & 3;
-  if constexpr (BITS == 4) return (q & ~7) | perm4_of_slot(q & 7);
-  else return (q & ~31) | (sigma8(g) << 3) | (q & 7);
+// ---------------------------------------------------------------------------
+// Operand row scaling.  f16 covers magnitudes from 2^-24 (subnormal spacing)
+// to 65504, so the split is taken of v * 2^e, where e depends on the row (or
+// on the K slice of a row that one launch reduces over): with m the row's
+// largest magnitude, m * 2^e lies in [2^(kRowTop - 1), 2^kRowTop).  Then
+// hi + lo carries every element to 2^-22 of itself plus 2^-(25 + kRowTop)
+// of m, whatever the row's magnitude, and hi never overflows.  Scaling by a
+// power of two is exact; the GEMM that consumes the row multiplies its fp32
+// result for that row by 2^-e.  Rows that are all zero (or hold a NaN or an
+// infinity, out of contract) take e = 0.
+// ---------------------------------------------------------------------------
+constexpr int kRowTop = 14;
+
+__device__ __forceinline__ int row_exp(float m) {
+  if (!(m > 0.f) || !(m <= 3.4028235e38f)) return 0;
+  return kRowTop - __builtin_amdgcn_frexp_expf(m);  // m = f * 2^x, f in [0.5, 1)
 }
 
-// Split fp32 into f16 hi + lo.
-__device__ __forceinline__ void split_f16(float v, _Float16& hi, _Float16& lo) {
-  hi = (_Float16)v;
-  lo = (_Float16)(v - (float)hi);
+// Split v * 2^e into f16 hi + lo (hi = f16(v * 2^e), lo = f16 of the rest).
+__device__ __forceinline__ void split_f16(float v, int e, _Float16& hi, _Float16& lo) {
+  const float s = __builtin_ldexpf(v, e);
+  hi = (_Float16)s;
+  lo = (_Float16)(s - (float)hi);
+}
+
+// Largest magnitude across the lanes of one wavefront whose lane index
+// differs only in the bits below SEG (SEG a power of two up to 64).
+template <int SEG>
+__device__ __forceinline__ float seg_max(float v) {
+#pragma unroll
+  for (int o = 1; o < SEG; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Eight fp32 values of one storage group (codes in natural order
+// c0 .. c0 + 7, see above) -> f16 hi and lo parts of v * 2^e in storage slot
+// order.
+template <int BITS>
+__device__ __forceinline__ void split_group(const float (&v)[8], int e, f16x8& hi, f16x8& lo) {
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) {
+    const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code at storage slot sl
+    _Float16 h, l;
+    split_f16(v[c], e, h, l);
+    hi[sl] = h;
+    lo[sl] = l;
+  }
 }
 
 // ---------------------------------------------------------------------------

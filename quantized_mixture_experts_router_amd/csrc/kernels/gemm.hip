@@ -8,7 +8,7 @@
 // dequantised as the QMoE WebGPU manifest's description and derive.quantMidpoint
 // state).  FC1 epilogue: ReLU, or interleaved SwiGLU g*sigmoid(alpha*g)*(u+beta)
 // on row pairs (2j, 2j+1) (manifest attributeDescriptions.swiglu_fusion,
-// activation_alpha, activation_beta), written as the next GEMM's f16 hi/lo
+// activation_alpha, activation_beta), written as the next GEMM's fp32
 // operand rows.  FC2 epilogue: rows are written back to their slot id, so the
 // combine can gather them without atomics.
 //
@@ -17,9 +17,11 @@
 // from HBM once, unpacks them in registers straight into the matrix-core B
 // operand, and reuses each unpacked fragment for all MT row subtiles.
 //
-// Operand precision: weights are exact integers in f16; activations are split
-// into f16 hi + lo and multiplied twice into fp32 accumulators.  Blockwise
-// scales are applied in fp32 when a scale block ends.
+// Operand precision: weights are exact integers in f16; activation rows are
+// scaled by 2^e (one e per row, see common.hpp), split into f16 hi + lo and
+// multiplied twice into fp32 accumulators; each row's result is multiplied
+// by 2^-e in the epilogue.  Blockwise scales are applied in fp32 when a scale
+// block ends.
 #include "common.hpp"
 #include "launch.h"
 
@@ -180,6 +182,15 @@ __global__ void __launch_bounds__(64 * kWaves) qmoe_gemm(GemmArgs g) {
   }
 
   // Epilogue.  acc[mt][nt][i] is row mt*16 + 4*grp + i, column nb + nt*16 + col.
+  int nexp[MT][4];  // -e of each row this lane holds
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + min(mt * 16 + 4 * grp + i, rows - 1);
+      const long ar = g.a_map ? (long)(g.a_map[p] / g.a_div) : (long)p;
+      nexp[mt][i] = -g.a_exp[ar];
+    }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -188,7 +199,7 @@ __global__ void __launch_bounds__(64 * kWaves) qmoe_gemm(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = mt * 16 + 4 * grp + i;
-        const float v = acc[mt][nt][i];
+        const float v = __builtin_ldexpf(acc[mt][nt][i], nexp[mt][i]);
         if constexpr (EPI == EPI_STORE) {
           if (r < rows && n < g.N) g.slot_out[(long)g.perm[p0 + r] * g.N + n] = v;
         } else {
@@ -205,14 +216,7 @@ __global__ void __launch_bounds__(64 * kWaves) qmoe_gemm(GemmArgs g) {
             j = n;
             writer = true;
           }
-          if (writer && r < rows && n < g.N) {
-            _Float16 h, l;
-            split_f16(a, h, l);
-            const int q = storage_of_code<BITS>(j);
-            uint8_t* dst = g.act + (long)(p0 + r) * g.act_stride + (q >> 3) * 32 + (q & 7) * 2;
-            *(_Float16*)dst = h;
-            *(_Float16*)(dst + 16) = l;
-          }
+          if (writer && r < rows && n < g.N) *(float*)(g.act + (long)(p0 + r) * g.act_stride + (long)j * 4) = a;
         }
       }
     }
@@ -260,10 +264,13 @@ hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& 
 }
 
 // out[t, h] = sum_s w[t, s] * (sum_z slot_out[z][t*k + s, h]); z then s
-// ascending, fp32.  One writer per output element, no atomics.
+// ascending, fp32.  One writer per output element, no atomics.  With local
+// given (a share of the experts), slots with local[t*k + s] >= El have no row
+// and are skipped.
 __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ slot_out,
                                                     const float* __restrict__ topk_w, int T, int k, int H,
-                                                    int splits, float* __restrict__ out) {
+                                                    int splits, float* __restrict__ out,
+                                                    const int* __restrict__ local, int El) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   const long S = (long)T * k;
   if ((H & 3) == 0) {
@@ -278,20 +285,24 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
       for (int s0 = 0; s0 < k; s0 += 8) {
         f32x4 v[8];
         float wv[8];
+        bool live[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (s0 + i < k) {
+        for (int i = 0; i < 8; ++i) {
+          live[i] = s0 + i < k && (local == nullptr || local[t * k + s0 + i] < El);
+          if (live[i]) {
             wv[i] = topk_w[t * k + s0 + i];
             v[i] = *(const f32x4*)(slot_out + (t * k + s0 + i) * H + h);
           }
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (s0 + i < k) acc += wv[i] * v[i];
+          if (live[i]) acc += wv[i] * v[i];
       }
       *(f32x4*)(out + t * H + h) = acc;
       return;
     }
     for (int s = 0; s < k; ++s) {
+      if (local != nullptr && local[t * k + s] >= El) continue;
       const float w = topk_w[t * k + s];
       const float* src = slot_out + (t * k + s) * H + h;
       f32x4 y;
@@ -314,6 +325,7 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
     const int h = (int)(i % H);
     float acc = 0.f;
     for (int s = 0; s < k; ++s) {
+      if (local != nullptr && local[t * k + s] >= El) continue;
       float y = slot_out[(t * k + s) * H + h];
       for (int z = 1; z < splits; ++z) y += slot_out[((long)z * S + t * k + s) * H + h];
       acc += topk_w[t * k + s] * y;
@@ -323,9 +335,10 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
 }
 
 hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, int splits, float* out,
-                          hipStream_t st) {
+                          hipStream_t st, const int* local, int El) {
   const long n = (H & 3) == 0 ? (long)T * H / 4 : (long)T * H;
-  hipLaunchKernelGGL(qmoe_combine, dim3((n + 255) / 256), dim3(256), 0, st, slot_out, topk_w, T, k, H, splits, out);
+  hipLaunchKernelGGL(qmoe_combine, dim3((n + 255) / 256), dim3(256), 0, st, slot_out, topk_w, T, k, H, splits, out,
+                     local, El);
   return hipGetLastError();
 }
 

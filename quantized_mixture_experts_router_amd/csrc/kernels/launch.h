@@ -15,16 +15,28 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int rout
                               int* topk_idx, float* topk_w, int* counts, int* offsets, int* perm, int* tiles,
                               int* ntiles, int* trows, hipStream_t st);
 
+// Counts, offsets, stable permutation and M-tile table over E groups; only
+// the first tile_groups groups (all when negative) get tiles.
 hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchunks, int bm, int* hist,
-                          int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st);
+                          int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st,
+                          int tile_groups = -1);
+
+// A share of the experts: local[s] = topk_idx[s] - first for the experts
+// [first, first + El) the weights hold, else El.
+hipError_t launch_local_index(const int* topk_idx, int S, int first, int El, int* local, hipStream_t st);
 
 // Tile-row table of the streaming kernels: trows[t * bm + r] = slot id of row
 // r of tile t (rows past the tile's count repeat its last row), t < ntiles.
 hipError_t launch_tile_rows(const int* perm, const int* tiles, const int* ntiles, int max_tiles, int bm, int* trows,
                             hipStream_t st);
 
-hipError_t launch_prep_a(int bits, const float* x, int T, int H, int kp, uint8_t* xa, uint8_t* act, int S, int I,
-                         int kp2, hipStream_t st);
+// Operand rows of the f16 GEMMs (see operand.hip): rows of n fp32 codes at
+// src + r * sstride (floats) -> kp hi/lo codes of v * 2^e at dst + r * dstride
+// (bytes), exps[r] = e; src and dst may be the same rows of 4-byte codes.
+hipError_t launch_split_rows(int bits, const float* src, long sstride, int n, uint8_t* dst, long dstride, int kp,
+                             long rows, int* exps, hipStream_t st);
+// exps[r] = e of the n fp32 codes at src + r * stride, r < rows.
+hipError_t launch_row_exp(const float* src, long stride, long rows, int n, int* exps, hipStream_t st);
 
 // Grouped quantised GEMM over expert-sorted rows.
 //   FC1: rows are tokens (via perm / k), weights fc1 [E][F][K/pack], output act rows.
@@ -34,6 +46,8 @@ struct GemmArgs {
   const float* ws;      // scales [E][N] or [E][N][nblk]
   const uint8_t* a;     // operand rows (f16 hi/lo groups), row stride a_stride bytes
   int a_f32;            // stream kernel: a holds fp32 rows (4 bytes a code) to split while staging
+  const int* a_exp;     // row scale exponent of every operand row (indexed like a), or nullptr: the
+                        // single-stage streaming kernel takes one per K range of its own
   const int* a_map;     // FC1: perm (sorted position -> slot); FC2: nullptr (row = position)
   int a_div;            // FC1: k (slot -> token)
   long a_stride;
@@ -43,7 +57,7 @@ struct GemmArgs {
   int store_by_slot;     // stream kernel: partial rows by slot id (1) or by sorted position (0)
   int S;                 // slots (stride between split partials, in rows)
   // epilogue
-  uint8_t* act;         // FC1 output rows, stride act_stride bytes
+  uint8_t* act;         // FC1 output rows (fp32 after the activation), stride act_stride bytes
   long act_stride;
   float* slot_out;      // FC2 output [splits][S][N] by slot id
   const int* perm;      // FC2: sorted position -> slot
@@ -67,10 +81,12 @@ hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& 
 // column-wise or >= 32-code block scales, 8-code-aligned rows, N % 4 == 0.
 hipError_t launch_tiled(int bits, int epi, const GemmArgs& g, int max_tiles, hipStream_t st);
 
-// Weight-streaming variant for small token counts (see stream.hip).  FC1
-// (g.a_f32 set): A rows are the fp32 input; with g.act set (one K range) the
-// kernel writes FC2 operand rows after the activation, else fp32 partial rows
-// part[z][p][N].  FC2: partial rows by slot id, slot_out[z][slot][N].
+// Weight-streaming variant for small token counts (see stream.hip).  A rows
+// are fp32 (g.a_f32 must be set).  FC1 (g.a_map set): A rows are the input's
+// token rows; with g.act set (one K range) the kernel writes fp32 FC2 operand
+// rows after the activation, else fp32 partial rows part[z][p][N].  FC2: A
+// rows are the fp32 operand rows in sorted order; partial rows by slot id,
+// slot_out[z][slot][N].
 // z < splits K ranges of g.nst stages each.
 // wg_rows: double-buffered mode, weight rows per workgroup (a multiple of 64
 // up to 512, above 256 only for mt == 1; 0 = 256).
@@ -78,13 +94,14 @@ size_t stream_lds_bytes(int bits, int mt, bool one, int rb);  // rb: row blocks 
 hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, const GemmArgs& g, int max_tiles,
                          hipStream_t st);
 
-// Sum FC1 partials over K ranges, apply the activation, write FC2 operand rows.
+// Sum FC1 partials over K ranges, apply the activation, write fp32 FC2 operand rows.
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,
                       float beta, float limit, uint8_t* act, hipStream_t st);
 
-// out[t, h] = sum_s w[t, s] * sum_z slot_out[z][t*k + s][h]  (fixed order)
+// out[t, h] = sum_s w[t, s] * sum_z slot_out[z][t*k + s][h]  (fixed order);
+// with local given, slots with local[t*k + s] >= El are skipped (no row).
 hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, int splits, float* out,
-                          hipStream_t st);
+                          hipStream_t st, const int* local = nullptr, int El = 0);
 
 // Float32 grouped GEMM over group-sorted rows (see gmm.hip), shared by
 // GroupedMatMul and the float MoE projections.

@@ -5,7 +5,6 @@
 //   qmoe_scatter       stable expert-sorted slot order (perm)
 //   qmoe_route_small   all of the above in one workgroup (<= 1024 slots)
 //   qmoe_route_wave    all of the above in one wavefront (<= 64 tokens, E * k <= 64)
-//   qmoe_prep_a        fp32 tokens -> f16 hi/lo operand rows (see common.hpp)
 //
 // Routing follows the QMoE WebGPU manifest (description: softmax over the
 // selected top-k logits; attributeDescriptions.normalize_routing_weights) and
@@ -129,14 +128,17 @@ __global__ void __launch_bounds__(256) qmoe_hist(const int* __restrict__ topk_id
 // expert's slot count c, write counts, exclusive offsets and the M-tile table
 //   tiles[4*i .. 4*i+3] = (expert, first sorted position, rows, 0), ntiles[0] = count;
 // returns the expert's first sorted position (and in *first_tile its first tile).
+// Only the first tile_groups groups get tiles (a share of the experts: the
+// last group holds the slots of experts the weights do not hold).
 __device__ __forceinline__ int scan_experts(int c, int E, int S, int bm, int* __restrict__ counts,
                                             int* __restrict__ offsets, int* __restrict__ tiles,
-                                            int* __restrict__ ntiles, int* first_tile = nullptr) {
+                                            int* __restrict__ ntiles, int* first_tile = nullptr,
+                                            int tile_groups = 1 << 30) {
   __shared__ int s_warp[16];
   __shared__ int s_warp2[16];
   const int e = threadIdx.x;
   if (e < E) counts[e] = c;
-  const int nt = (c + bm - 1) / bm;
+  const int nt = threadIdx.x < tile_groups ? (c + bm - 1) / bm : 0;
   // Inclusive scans of counts and tile counts (wave scan, then wave totals).
   int inc = c, inct = nt;
   const int lane = lane_id(), w = threadIdx.x >> 6;
@@ -201,7 +203,8 @@ __device__ __forceinline__ void write_tile_rows(const int* perm, int off_e, int 
 // bases for the scatter), offsets and the M-tile table.
 __global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nchunks, int E, int S, int bm,
                                                   int* __restrict__ counts, int* __restrict__ offsets,
-                                                  int* __restrict__ tiles, int* __restrict__ ntiles) {
+                                                  int* __restrict__ tiles, int* __restrict__ ntiles,
+                                                  int tile_groups) {
   const int e = threadIdx.x;
   int c = 0;
   // eight chunks' counts in flight at a time (one round trip per eight)
@@ -218,7 +221,7 @@ __global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nc
         }
     }
   }
-  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles);
+  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles, nullptr, tile_groups);
   if (e < E)
     for (int ch0 = 0; ch0 < nchunks; ch0 += 8) {
       int v[8];
@@ -480,64 +483,15 @@ __global__ void __launch_bounds__(256) qmoe_tile_rows(const int* __restrict__ pe
   trows[i] = perm[p0 + min(r, rows - 1)];
 }
 
-// fp32 token rows -> f16 hi/lo operand rows (storage order of common.hpp),
-// zero padded to kp codes.  One thread per group of 8 codes.  When act_pad is
-// given, also zero the padding columns [I, kp2) of every act row.
-template <int BITS>
-__global__ void __launch_bounds__(256) qmoe_prep_a(const float* __restrict__ x, int T, int H, int kp,
-                                                   uint8_t* __restrict__ xa, uint8_t* __restrict__ act,
-                                                   int S, int I, int kp2) {
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long groups = (long)T * (kp / 8);
-  if (gid < groups) {
-    const int t = gid / (kp / 8);
-    const int g = gid % (kp / 8);
-    // a storage group holds 8 consecutive codes from j0 (permuted inside the
-    // group): two 16-byte loads when they are all in the row and H keeps
-    // rows 16-byte aligned (the input itself is), else one load a code
-    const int j0 = code_of_storage<BITS>(g * 8);
-    const float* row = x + (size_t)t * H;
-    float v[8];
-    if ((H & 3) == 0 && j0 + 8 <= H) {
-      const f32x4 a0 = *(const f32x4*)(row + j0), a1 = *(const f32x4*)(row + j0 + 4);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        v[c] = a0[c];
-        v[c + 4] = a1[c];
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) v[c] = j0 + c < H ? row[j0 + c] : 0.f;
-    }
-    f16x8 hi, lo;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      _Float16 h, l;
-      split_f16(v[code_of_storage<BITS>(g * 8 + i) - j0], h, l);
-      hi[i] = h;
-      lo[i] = l;
-    }
-    uint8_t* dst = xa + (size_t)t * kp * 4 + (size_t)g * 32;
-    *(f16x8*)dst = hi;
-    *(f16x8*)(dst + 16) = lo;
-  }
-  if (act != nullptr) {
-    // padding of act rows: every storage group of the 32-code blocks from the
-    // one holding code I onwards (inside a block, 8-bit storage groups hold
-    // permuted code groups, so a group's index does not bound its codes)
-    const int g0 = (I / 32) * 4;  // first group that may hold codes >= I
-    const int pg = kp2 / 8 - g0;
-    const long pid = gid - groups;
-    if (pid >= 0 && pid < (long)S * pg) {
-      const int p = pid / pg;
-      const int g = g0 + pid % pg;
-      uint8_t* dst = act + (size_t)p * kp2 * 4 + (size_t)g * 32;
-      // codes < I in these groups are written later by FC1 (on the same
-      // stream), so clearing whole groups is safe
-      *(f16x8*)dst = f16x8{};
-      *(f16x8*)(dst + 16) = f16x8{};
-    }
-  }
+// A share of the experts: local[s] = topk_idx[s] - first when the weights
+// hold that expert (first <= e < first + El), else El (one more group, given
+// no tiles, whose slots the combine skips).
+__global__ void __launch_bounds__(256) qmoe_local_index(const int* __restrict__ topk_idx, int S, int first, int El,
+                                                        int* __restrict__ local) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= S) return;
+  const int e = topk_idx[s] - first;
+  local[s] = (e >= 0 && e < El) ? e : El;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -582,11 +536,18 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int rout
 }
 
 hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchunks, int bm, int* hist,
-                          int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st) {
+                          int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st,
+                          int tile_groups) {
   hipLaunchKernelGGL(qmoe_hist, dim3(nchunks), dim3(256), E * sizeof(int), st, topk_idx, S, E, chunk, hist);
-  hipLaunchKernelGGL(qmoe_scan, dim3(1), dim3(1024), 0, st, hist, nchunks, E, S, bm, counts, offsets, tiles, ntiles);
+  hipLaunchKernelGGL(qmoe_scan, dim3(1), dim3(1024), 0, st, hist, nchunks, E, S, bm, counts, offsets, tiles, ntiles,
+                     tile_groups < 0 ? E : tile_groups);
   hipLaunchKernelGGL(qmoe_scatter, dim3(nchunks), dim3(64 * kScatterWaves), (1 + kScatterWaves) * E * sizeof(int), st,
                      topk_idx, hist, S, E, chunk, perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_local_index(const int* topk_idx, int S, int first, int El, int* local, hipStream_t st) {
+  if (S > 0) hipLaunchKernelGGL(qmoe_local_index, dim3((S + 255) / 256), dim3(256), 0, st, topk_idx, S, first, El, local);
   return hipGetLastError();
 }
 
@@ -594,16 +555,6 @@ hipError_t launch_tile_rows(const int* perm, const int* tiles, const int* ntiles
                             hipStream_t st) {
   const int n = max_tiles * bm;
   hipLaunchKernelGGL(qmoe_tile_rows, dim3((n + 255) / 256), dim3(256), 0, st, perm, tiles, ntiles, max_tiles, bm, trows);
-  return hipGetLastError();
-}
-
-hipError_t launch_prep_a(int bits, const float* x, int T, int H, int kp, uint8_t* xa, uint8_t* act, int S, int I,
-                         int kp2, hipStream_t st) {
-  long work = (long)T * (kp / 8);
-  if (act) work += (long)S * (kp2 / 8 - (I / 32) * 4);
-  const dim3 grid((work + 255) / 256), block(256);
-  if (bits == 4) hipLaunchKernelGGL(qmoe_prep_a<4>, grid, block, 0, st, x, T, H, kp, xa, act, S, I, kp2);
-  else hipLaunchKernelGGL(qmoe_prep_a<8>, grid, block, 0, st, x, T, H, kp, xa, act, S, I, kp2);
   return hipGetLastError();
 }
 

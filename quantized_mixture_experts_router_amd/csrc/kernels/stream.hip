@@ -20,13 +20,17 @@
 //  * a cross-lane exchange (v_permlane32/16_swap) puts each lane's bytes in
 //    the matrix-core operand position; bytes are unpacked to exact f16
 //    (q - mid) in registers and multiplied by the f16 hi and lo parts of the
-//    activations on v_mfma_f32_16x16x32_f16 (fp32 accumulation);
+//    activations on v_mfma_f32_16x16x32_f16 (fp32 accumulation).  Operand
+//    rows are fp32 (the layer input for FC1, the activation rows for FC2) and
+//    are split into hi/lo while staged, after scaling by a power of two per
+//    row: a single-stage workgroup takes its own per K range, a
+//    double-buffered one the whole row's (see common.hpp);
 //  * block scales are loaded one stage ahead, shared across lanes with
 //    ds_bpermute, and applied in fp32 as each block closes;
 //  * results go through an LDS tile and leave as contiguous 16-byte stores:
 //    FC1 over the whole of K applies ReLU or interleaved SwiGLU there and
-//    writes FC2's operand rows directly; otherwise fp32 partial rows per K
-//    range are written, and qmoe_act (FC1) or the combine (FC2) sum the
+//    writes FC2's fp32 operand rows directly; otherwise fp32 partial rows per
+//    K range are written, and qmoe_act (FC1) or the combine (FC2) sum the
 //    ranges in a fixed order (no atomics).
 #include <algorithm>
 #include <atomic>
@@ -98,8 +102,9 @@ __device__ __forceinline__ void exchange(u32x4& v) {
 // Template parameters: STG items per stage; SCALE mode; SPB = MFMA steps per
 // scale block when blocks end inside a chunk (0 when scales are column-wise or
 // a block spans whole chunks); FC1 = the A rows are the layer's fp32 input
-// (split into f16 hi/lo while staging) and the epilogue may apply the
-// activation; otherwise A rows are FC2 operand rows (f16 hi/lo groups).
+// rows (token of each slot) and the epilogue may apply the activation;
+// otherwise A rows are the fp32 FC2 operand rows in sorted order.  Either way
+// rows are split into f16 hi/lo while staging.
 // ONE: the K range is a single stage, staged once (no barriers in the
 // stream); otherwise stages are double buffered.  RB: row blocks of
 // kWGRows weight rows streamed one after the other against the one stage
@@ -129,7 +134,6 @@ qmoe_stream(GemmArgs g) {
   constexpr int PIECES = LSTRIDE / 16;          // 16-byte pieces per row
   constexpr int GR = PIECES / 2;                // 8-code groups per row
   constexpr int NTH = 64 * kSWaves;
-  constexpr int PPT = (ROWS * PIECES + NTH - 1) / NTH;  // staged pieces per thread (f16 rows)
   constexpr int GPT = (ROWS * GR + NTH - 1) / NTH;      // staged groups per thread (fp32 rows)
   // stages per loop trip: a whole number of ring turns, so ring slots are
   // compile-time constants
@@ -140,6 +144,7 @@ qmoe_stream(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];  // 2 stage buffers, then the output tile
   __shared__ long s_rowbase[ROWS];
   __shared__ int s_orow[ROWS];
+  __shared__ int s_rexp[ROWS];  // row scale exponent of each tile row (results are multiplied by 2^-e)
 
   // Block scales of one stage per weight row when blocks end inside a chunk
   // (SPB > 0): NBS of them, Q per lane group.
@@ -306,6 +311,7 @@ qmoe_stream(GemmArgs g) {
       const long ar = FC1 ? (long)(slot / g.a_div) : (long)p;
       s_rowbase[threadIdx.x] = ar * g.a_stride + (long)c0 * CC * 4;
       s_orow[threadIdx.x] = g.store_by_slot ? slot : p;
+      s_rexp[threadIdx.x] = g.a_exp ? g.a_exp[ar] : 0;  // the whole row's: the walk spans the K range
     }
     __syncthreads();
   }
@@ -317,65 +323,40 @@ qmoe_stream(GemmArgs g) {
   // The next stage's slice is fetched in NPART parts at the start of a stage
   // (before that stage's ring refills, so that waiting for it never waits
   // for them) and written to LDS one part after each item.
-  constexpr int NPART = FC1 ? (GPT % STG == 0 ? STG : 1) : (PPT % STG == 0 ? STG : 1);
-  constexpr int GPP = GPT / (FC1 ? NPART : 1);   // fp32 groups per thread per part
-  constexpr int PPP = PPT / (FC1 ? 1 : NPART);   // f16 pieces per thread per part
-  f32x4 areg32[FC1 ? NPART : 1][FC1 ? GPP : 1][2];
-  u32x4 areg16[FC1 ? 1 : NPART][FC1 ? 1 : PPP];
+  constexpr int NPART = GPT % STG == 0 ? STG : 1;
+  constexpr int GPP = GPT / NPART;   // fp32 groups per thread per part
+  f32x4 areg32[NPART][GPP][2];
   auto stage_load = [&](int st, int part) {
     const int stw = min(st, nstt - 1);
     const long off = (long)kpos(stw % nst) * SCODES * 4;
-    if constexpr (FC1) {
 #pragma unroll
-      for (int ii = 0; ii < GPP; ++ii) {
-        const int i = part * GPP + ii;
-        const int idx = min((int)threadIdx.x + i * NTH, ROWS * GR - 1);
-        const int r = idx / GR, gq = idx % GR;
-        // first code of storage group gq (see common.hpp): 4-bit groups hold
-        // their own 8 codes, 8-bit groups those of code group sigma(gq % 4)
-        const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
-        const float* src = (const float*)(g.a + s_rowbase[min(r, rows - 1)] + off) + j0;
-        areg32[part][ii][0] = *(const f32x4*)src;
-        areg32[part][ii][1] = *(const f32x4*)(src + 4);
-      }
-    } else {
-#pragma unroll
-      for (int ii = 0; ii < PPP; ++ii) {
-        const int i = part * PPP + ii;
-        const int idx = min((int)threadIdx.x + i * NTH, ROWS * PIECES - 1);
-        const int r = idx / PIECES, q = idx % PIECES;
-        areg16[part][ii] = *(const u32x4*)(g.a + s_rowbase[min(r, rows - 1)] + off + q * 16);
-      }
+    for (int ii = 0; ii < GPP; ++ii) {
+      const int i = part * GPP + ii;
+      const int idx = min((int)threadIdx.x + i * NTH, ROWS * GR - 1);
+      const int r = idx / GR, gq = idx % GR;
+      // first code of storage group gq (see common.hpp): 4-bit groups hold
+      // their own 8 codes, 8-bit groups those of code group sigma(gq % 4)
+      const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
+      const float* src = (const float*)(g.a + s_rowbase[min(r, rows - 1)] + off) + j0;
+      areg32[part][ii][0] = *(const f32x4*)src;
+      areg32[part][ii][1] = *(const f32x4*)(src + 4);
     }
   };
   auto stage_store = [&](int buf, int part) {
     uint8_t* base = lds + buf * BUF;
-    if constexpr (FC1) {
 #pragma unroll
-      for (int ii = 0; ii < GPP; ++ii) {
-        const int idx = threadIdx.x + (part * GPP + ii) * NTH;
-        const int r = idx / GR, gq = idx % GR;
-        if (idx < ROWS * GR) {
-          f16x8 hi, lo;
+    for (int ii = 0; ii < GPP; ++ii) {
+      const int idx = threadIdx.x + (part * GPP + ii) * NTH;
+      const int r = idx / GR, gq = idx % GR;
+      if (idx < ROWS * GR) {
+        float v[8];
 #pragma unroll
-          for (int sl = 0; sl < 8; ++sl) {
-            const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code inside the group at storage slot sl
-            _Float16 h, l;
-            split_f16(areg32[part][ii][c >> 2][c & 3], h, l);
-            hi[sl] = h;
-            lo[sl] = l;
-          }
-          uint8_t* row = base + r * LSTRIDE;
-          *(f16x8*)(row + (((2 * gq) ^ (r & 15)) * 16)) = hi;
-          *(f16x8*)(row + (((2 * gq + 1) ^ (r & 15)) * 16)) = lo;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int ii = 0; ii < PPP; ++ii) {
-        const int idx = threadIdx.x + (part * PPP + ii) * NTH;
-        const int r = idx / PIECES, q = idx % PIECES;
-        if (idx < ROWS * PIECES) *(u32x4*)(base + r * LSTRIDE + ((q ^ (r & 15)) * 16)) = areg16[part][ii];
+        for (int c = 0; c < 8; ++c) v[c] = areg32[part][ii][c >> 2][c & 3];
+        f16x8 hi, lo;
+        split_group<BITS>(v, s_rexp[r], hi, lo);
+        uint8_t* row = base + r * LSTRIDE;
+        *(f16x8*)(row + (((2 * gq) ^ (r & 15)) * 16)) = hi;
+        *(f16x8*)(row + (((2 * gq + 1) ^ (r & 15)) * 16)) = lo;
       }
     }
   };
@@ -383,12 +364,14 @@ qmoe_stream(GemmArgs g) {
     // The only stage, staged once: wavefront w stages tile rows w + 8i (valid
     // rows only; the matrix rows past them read the last valid row), with
     // loads issued before the weight stream, so that waiting for them never
-    // waits for it (loads complete in issue order).  FC1 holds the fp32 rows
-    // in registers until the stream is issued, then splits them into f16
-    // hi/lo in LDS; FC2 rows are already f16 hi/lo and load straight into LDS.
-    constexpr int UPR = FC1 ? GR : PIECES;           // load units per row: fp32 8-code groups / f16 pieces
+    // waits for it (loads complete in issue order).  The fp32 rows are held
+    // in registers until the stream is issued; then each row's largest
+    // magnitude over this K range gives its scale exponent, and the rows go
+    // into LDS as f16 hi/lo of the scaled values.
+    constexpr int UPR = GR;                          // load units (fp32 8-code groups) per row
     constexpr int RPI = UPR >= 64 ? 1 : 64 / UPR;    // rows per load instruction
     constexpr int MPW = RPI > 1 ? (RPW + RPI - 1) / RPI : RPW * UPR / 64;  // units per lane
+    constexpr int SEG = UPR >= 64 ? 64 : UPR;        // lanes holding one row of one instruction
     static_assert(UPR % 64 == 0 || 64 % UPR == 0, "staging units");
     long rbase[RPW];
 #pragma unroll
@@ -411,55 +394,64 @@ qmoe_stream(GemmArgs g) {
         if (lane / UPR == k) base = v;
       }
     };
-    if constexpr (FC1) {
-      f32x4 sv[MPW][2];
+    f32x4 sv[MPW][2];
 #pragma unroll
-      for (int m = 0; m < MPW; ++m) {
-        int r, q;
-        long base;
-        unit(m, r, q, base);
-        if (r < rows) {
-          const int j0 = BITS == 4 ? 8 * q : ((8 * q) & ~31) | (sigma8(q & 3) << 3);
-          const float* src = (const float*)(g.a + base) + j0;
-          sv[m][0] = *(const f32x4*)src;
-          sv[m][1] = *(const f32x4*)(src + 4);
-        }
+    for (int m = 0; m < MPW; ++m) {
+      int r, q;
+      long base;
+      unit(m, r, q, base);
+      sv[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sv[m][1] = sv[m][0];
+      if (r < rows) {
+        const int j0 = BITS == 4 ? 8 * q : ((8 * q) & ~31) | (sigma8(q & 3) << 3);
+        const float* src = (const float*)(g.a + base) + j0;
+        sv[m][0] = *(const f32x4*)src;
+        sv[m][1] = *(const f32x4*)(src + 4);
       }
-      start_stream();
+    }
+    start_stream();
+    // Largest magnitude of each row over this K range: a row of one unit is
+    // held by SEG lanes; with whole-wavefront units a row spans UPR / 64
+    // consecutive units.
+    float um[MPW];
 #pragma unroll
-      for (int m = 0; m < MPW; ++m) {
-        int r, q;
-        long base;
-        unit(m, r, q, base);
-        if (r < rows) {
-          f16x8 hi, lo;
+    for (int m = 0; m < MPW; ++m) {
+      float v = 0.f;
 #pragma unroll
-          for (int sl = 0; sl < 8; ++sl) {
-            const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code inside the group at storage slot sl
-            _Float16 h, l;
-            split_f16(sv[m][c >> 2][c & 3], h, l);
-            hi[sl] = h;
-            lo[sl] = l;
-          }
-          uint8_t* row = lds + r * LSTRIDE;
-          *(f16x8*)(row + (((2 * q) ^ (r & 15)) * 16)) = hi;
-          *(f16x8*)(row + (((2 * q + 1) ^ (r & 15)) * 16)) = lo;
-        }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v = fmaxf(v, fabsf(sv[m][h][c]));
+      um[m] = seg_max<SEG>(v);
+    }
+    if constexpr (RPI == 1) {
+      constexpr int UW = UPR / 64;  // units per row
+#pragma unroll
+      for (int i = 0; i < MPW / UW; ++i) {
+        float rm = 0.f;
+#pragma unroll
+        for (int u = 0; u < UW; ++u) rm = fmaxf(rm, um[i * UW + u]);
+#pragma unroll
+        for (int u = 0; u < UW; ++u) um[i * UW + u] = rm;
       }
-    } else {
-      // One instruction fills up to 64 consecutive swizzled piece slots of
-      // row r: lane l writes slot P0 + l, so it loads piece (P0 + l) ^ (r & 15).
-      constexpr int NI = UPR >= 64 ? RPW * UPR / 64 : RPW;  // instructions per wavefront
+    }
 #pragma unroll
-      for (int m = 0; m < NI; ++m) {
-        const int i = UPR >= 64 ? (64 * m) / UPR : m, P0 = UPR >= 64 ? (64 * m) % UPR : 0;
-        const int r = wv + kSWaves * i;
-        if (r < rows && (UPR >= 64 || lane < UPR))
-          __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)(g.a + rbase[i] + ((P0 + lane) ^ (r & 15)) * 16),
-              (__attribute__((address_space(3))) void*)(lds + r * LSTRIDE + P0 * 16), 16, 0, 0);
+    for (int m = 0; m < MPW; ++m) {
+      int r, q;
+      long base;
+      unit(m, r, q, base);
+      const int e = row_exp(um[m]);
+      const bool first = RPI > 1 ? lane % UPR == 0 : (lane == 0 && m % (UPR / 64) == 0);
+      if (first && r < ROWS) s_rexp[r] = e;
+      if (r < rows) {
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = sv[m][c >> 2][c & 3];
+        f16x8 hi, lo;
+        split_group<BITS>(v, e, hi, lo);
+        uint8_t* row = lds + r * LSTRIDE;
+        *(f16x8*)(row + (((2 * q) ^ (r & 15)) * 16)) = hi;
+        *(f16x8*)(row + (((2 * q + 1) ^ (r & 15)) * 16)) = lo;
       }
-      start_stream();
     }
   } else {
 #pragma unroll
@@ -503,11 +495,12 @@ qmoe_stream(GemmArgs g) {
   const UnpackMasks um = unpack_masks();
 
   // Output of TW weight rows from n0e: every wavefront puts its rows
-  // (column scales applied; val(row block, mt, nt, i) gives the results) into
-  // the LDS tile [ROWS][TW]; tile columns are XOR-swizzled by
-  // 16 * ((row / 4) % 4), so the four row groups of one write hit distinct
-  // banks.  Then FC1 with one K range applies the activation and writes FC2
-  // operand rows; otherwise fp32 partial rows of this K range are written.
+  // (column scales applied, row scales undone; val(row block, mt, nt, i)
+  // gives the results) into the LDS tile [ROWS][TW]; tile columns are
+  // XOR-swizzled by 16 * ((row / 4) % 4), so the four row groups of one
+  // write hit distinct banks.  Then FC1 with one K range applies the
+  // activation and writes fp32 FC2 operand rows; otherwise fp32 partial rows
+  // of this K range are written.
   auto emit = [&](float* otile, auto twc, const int n0e, const int ncols, auto val) {
   constexpr int TW = decltype(twc)::value;
   auto tix = [](int rr, int c) { return rr * TW + (c ^ (16 * ((rr >> 2) & 3))); };
@@ -523,63 +516,42 @@ qmoe_stream(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = mt * 16 + 4 * grp + i;
-          if (rr < rows) otile[tix(rr, c)] = val(cb, mt, nt, i) * sc;
+          if (rr < rows) otile[tix(rr, c)] = __builtin_ldexpf(val(cb, mt, nt, i) * sc, -s_rexp[rr]);
         }
     }
   __syncthreads();
 
   if (FC1 && g.act != nullptr) {
-    // Whole of K: apply the activation and write FC2 operand rows (f16 hi/lo
-    // groups, storage order of common.hpp) for this workgroup's codes.
+    // Whole of K: apply the activation and write fp32 FC2 operand rows
+    // (natural code order) for this workgroup's codes, four a thread.
     // ReLU: code j = row n.  Interleaved SwiGLU: code j takes rows 2j (gate)
     // and 2j + 1 (linear): g * sigmoid(alpha * g) * (u + beta).
     const bool swiglu = g.act_swiglu != 0;
     const int I = swiglu ? g.N / 2 : g.N;
     const int jbase = swiglu ? n0e / 2 : n0e;
-    const int gtot = (int)(g.act_stride / 32);       // groups per operand row
-    // codes of this tile (whole 32-code blocks); the tile holding row N - 1
-    // also writes the zero padding codes up to the end of the operand row
-    int jw = swiglu ? ncols / 2 : ncols;
-    if (n0e + ncols >= g.N) jw = max(jw, gtot * 8 - jbase);
-    for (int idx = threadIdx.x; idx < rows * (jw / 8); idx += NTH) {
-      const int rr = idx / (jw / 8);
-      const int gq = jbase / 8 + idx % (jw / 8);
-      if (gq >= gtot) continue;
-      const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
-      float a[8];
-      if (j0 >= I) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) a[c] = 0.f;
-      } else if (swiglu) {
-        const int t0 = 2 * (j0 - jbase);  // tile column of row 2*j0 (16 consecutive columns)
-        f32x4 v[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const float gv = v[c >> 1][2 * (c & 1)], uv = v[c >> 1][2 * (c & 1) + 1];
-          a[c] = j0 + c < I ? swiglu_act(gv, uv, g.alpha, g.beta, g.limit) : 0.f;
-        }
+    const int jw = swiglu ? ncols / 2 : ncols;  // codes of this tile
+    for (int idx = threadIdx.x; idx < rows * (jw / 4); idx += NTH) {
+      const int rr = idx / (jw / 4);
+      const int j0 = jbase + 4 * (idx % (jw / 4));
+      if (j0 >= I) continue;
+      f32x4 a;
+      if (swiglu) {
+        const int t0 = 2 * (j0 - jbase);  // tile column of row 2*j0 (8 consecutive columns)
+        const f32x4 v0 = *(const f32x4*)(otile + tix(rr, t0)), v1 = *(const f32x4*)(otile + tix(rr, t0 + 4));
+        a[0] = swiglu_act(v0[0], v0[1], g.alpha, g.beta, g.limit);
+        a[1] = swiglu_act(v0[2], v0[3], g.alpha, g.beta, g.limit);
+        a[2] = swiglu_act(v1[0], v1[1], g.alpha, g.beta, g.limit);
+        a[3] = swiglu_act(v1[2], v1[3], g.alpha, g.beta, g.limit);
       } else {
-        const int t0 = j0 - jbase;
-        f32x4 v[2];
+        const f32x4 v = *(const f32x4*)(otile + tix(rr, j0 - jbase));
 #pragma unroll
-        for (int m = 0; m < 2; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) a[c] = j0 + c < I ? fmaxf(v[c >> 2][c & 3], 0.f) : 0.f;
+        for (int c = 0; c < 4; ++c) a[c] = fmaxf(v[c], 0.f);
       }
-      f16x8 hi, lo;
+      // the row is padded to a multiple of 128 codes: lanes past I write zeros there
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code j0 + c sits at storage slot sl
-        _Float16 hh, ll;
-        split_f16(a[c], hh, ll);
-        hi[sl] = hh;
-        lo[sl] = ll;
-      }
-      uint8_t* dst = g.act + (long)(p0 + rr) * g.act_stride + (long)gq * 32;
-      *(f16x8*)dst = hi;
-      *(f16x8*)(dst + 16) = lo;
+      for (int c = 0; c < 4; ++c)
+        if (j0 + c >= I) a[c] = 0.f;
+      *(f32x4*)(g.act + (long)(p0 + rr) * g.act_stride + (long)j0 * 4) = a;
     }
   } else if ((g.N & 3) == 0) {
     for (int idx = threadIdx.x; idx < rows * (TW / 4); idx += NTH) {
@@ -771,22 +743,20 @@ qmoe_stream(GemmArgs g) {
 // FC1 epilogue for the streamed path: sum the K-range partials of each
 // expert-sorted row p in range order, apply ReLU or interleaved SwiGLU
 // (g * sigmoid(alpha * g) * (u + beta), g = h[2j], u = h[2j+1]) and write the
-// f16 hi/lo operand rows of FC2.  One thread per 8-code storage group: its 8
-// codes are consecutive (see common.hpp), so it reads 8 (ReLU) or 16 (SwiGLU)
+// fp32 operand rows of FC2 (natural code order, row stride kp2 codes).  One
+// thread per 8 consecutive codes: it reads 8 (ReLU) or 16 (SwiGLU)
 // consecutive fp32 values of every partial row with 16-byte loads, all
-// partials of a batch of four ranges in flight at once.  Groups beyond I are
-// zero padding.
-template <int BITS, int EPI>
+// partials of a batch of four ranges in flight at once.
+template <int EPI>
 __global__ void __launch_bounds__(256) qmoe_act(const float* __restrict__ part, int splits, int S, int F, int I,
                                                 int kp2, float alpha, float beta, float limit,
                                                 uint8_t* __restrict__ act) {
-  constexpr int W = EPI == EPI_SWIGLU ? 16 : 8;  // FC1 values per group
+  constexpr int W = EPI == EPI_SWIGLU ? 16 : 8;  // FC1 values per thread
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const int groups = kp2 / 8;
+  const int groups = (I + 7) / 8;
   if (gid >= (long)S * groups) return;
   const int p = gid / groups;
-  const int gq = gid % groups;
-  const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);  // first code of the group
+  const int j0 = 8 * (int)(gid % groups);  // first code of the thread
   const long zstride = (long)S * F;
   float h[W];
   if (j0 + 8 <= I && (F & 3) == 0) {
@@ -816,27 +786,19 @@ __global__ void __launch_bounds__(256) qmoe_act(const float* __restrict__ part, 
       h[c] = a;
     }
   }
-  f16x8 hi, lo;
+  float a[8];
 #pragma unroll
-  for (int sl = 0; sl < 8; ++sl) {
-    const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code j0 + c sits at storage slot sl
-    float a = 0.f;
+  for (int c = 0; c < 8; ++c) {
+    a[c] = 0.f;
     if (j0 + c < I) {
-      if constexpr (EPI == EPI_SWIGLU) {
-        const float gv = h[2 * c], uv = h[2 * c + 1];
-        a = swiglu_act(gv, uv, alpha, beta, limit);
-      } else {
-        a = fmaxf(h[c], 0.f);
-      }
+      if constexpr (EPI == EPI_SWIGLU) a[c] = swiglu_act(h[2 * c], h[2 * c + 1], alpha, beta, limit);
+      else a[c] = fmaxf(h[c], 0.f);
     }
-    _Float16 hh, ll;
-    split_f16(a, hh, ll);
-    hi[sl] = hh;
-    lo[sl] = ll;
   }
-  uint8_t* dst = act + (long)p * kp2 * 4 + (long)gq * 32;
-  *(f16x8*)dst = hi;
-  *(f16x8*)(dst + 16) = lo;
+  // rows are padded to kp2 >= roundup(I, 8) codes: the tail group writes zeros there
+  float* dst = (float*)(act + (long)p * kp2 * 4) + j0;
+  *(f32x4*)dst = f32x4{a[0], a[1], a[2], a[3]};
+  *(f32x4*)(dst + 4) = f32x4{a[4], a[5], a[6], a[7]};
 }
 
 namespace {
@@ -929,21 +891,20 @@ hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, co
   g.wg_rows = wg_rows;
   const size_t lds = stream_lds_bytes(bits, mt, one, one ? rb : 1);
   const dim3 grid(splits, max_tiles, (g.N + wg_rows - 1) / wg_rows);
-  const bool fc1 = g.a_f32 != 0;
+  // operand rows are fp32 in both GEMMs; FC1 gathers them through the slot map
+  if (!g.a_f32) return hipErrorInvalidValue;
+  const bool fc1 = g.a_map != nullptr;
   return bits == 4 ? pick_mode<4>(fc1, one, mt, rb, g, grid, lds, st) : pick_mode<8>(fc1, one, mt, rb, g, grid, lds, st);
 }
 
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,
                       float beta, float limit, uint8_t* act, hipStream_t st) {
-  const long n = (long)S * (kp2 / 8);
+  (void)bits;
+  if (kp2 < (I + 7) / 8 * 8 || kp2 % 4 != 0) return hipErrorInvalidValue;
+  const long n = (long)S * ((I + 7) / 8);
   const dim3 grid((n + 255) / 256), block(256);
-  if (bits == 4) {
-    if (epi == EPI_SWIGLU) hipLaunchKernelGGL((qmoe_act<4, EPI_SWIGLU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
-    else hipLaunchKernelGGL((qmoe_act<4, EPI_RELU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
-  } else {
-    if (epi == EPI_SWIGLU) hipLaunchKernelGGL((qmoe_act<8, EPI_SWIGLU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
-    else hipLaunchKernelGGL((qmoe_act<8, EPI_RELU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
-  }
+  if (epi == EPI_SWIGLU) hipLaunchKernelGGL((qmoe_act<EPI_SWIGLU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
+  else hipLaunchKernelGGL((qmoe_act<EPI_RELU>), grid, block, 0, st, part, splits, S, F, I, kp2, alpha, beta, limit, act);
   return hipGetLastError();
 }
 

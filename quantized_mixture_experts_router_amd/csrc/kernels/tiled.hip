@@ -6,11 +6,13 @@
 // for the expert-sorted rows p of one 128-row tile of expert e (the
 // GroupedMatMul of the ONNX GroupedMatMul-29 page, Summary, over weights
 // dequantised as the QMoE WebGPU manifest's description and
-// derive.quantMidpoint state).  FC1 epilogue: ReLU, or interleaved SwiGLU
-// g*sigmoid(alpha*g)*(u+beta) on row pairs (2j, 2j+1) (manifest
-// attributeDescriptions.swiglu_fusion, activation_alpha, activation_beta),
-// written as FC2's f16 hi/lo operand rows.  FC2 epilogue: rows are written at
-// their slot id, so the combine gathers them without atomics.
+// derive.quantMidpoint state).  Operand rows are f16 hi/lo of the row scaled
+// by 2^e (see common.hpp); the epilogue multiplies each row's result by 2^-e.
+// FC1 epilogue: ReLU, or interleaved SwiGLU g*sigmoid(alpha*g)*(u+beta) on
+// row pairs (2j, 2j+1) (manifest attributeDescriptions.swiglu_fusion,
+// activation_alpha, activation_beta), written as FC2's fp32 operand rows.
+// FC2 epilogue: rows are written at their slot id, so the combine gathers
+// them without atomics.
 //
 // Work decomposition: a workgroup of 8 wavefronts computes a 128 x 256 tile
 // (2 x 4 wavefronts of 64 x 64).  Each 64-code K step's operands - the
@@ -95,21 +97,25 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   __shared__ __align__(16) uint8_t st2[L::kStage];
   __shared__ long s_arow[kTM];
   __shared__ int s_orow[kTM];
+  __shared__ int s_rexp[kTM];  // row scale exponent of each tile row
 
   // Tile order: each XCD (workgroups are dealt round robin by linear id)
   // takes a contiguous run of work ids; work ids run over groups of kGroupM
-  // row tiles, column tile by column tile, row tile fastest.
-  const int total = gridDim.x;
+  // row tiles, column tile by column tile, row tile fastest.  The grid is
+  // sized for the most tiles routing can produce; only the first
+  // ntiles * ntn linear ids carry work, and they are the ones dealt out, so
+  // every XCD gets its share of the real tiles.
+  const int mtiles = g.ntiles[0];
+  const int total = mtiles * ntn;
   const int lin = blockIdx.x;
+  if (lin >= total) return;
   const int xcd = lin & 7, per = total >> 3, extra = total & 7;
   const int w = xcd * per + min(xcd, extra) + (lin >> 3);
-  const int mtiles = total / ntn;
   const int grp0 = (w / (kGroupM * ntn)) * kGroupM;
   const int gsize = min(kGroupM, mtiles - grp0);
   const int wr = w % (kGroupM * ntn);
   const int tile = grp0 + wr % gsize;
   const int ntile = wr / gsize;
-  if (tile >= g.ntiles[0]) return;
   const int e = g.tiles[4 * tile + 0];
   const int p0 = g.tiles[4 * tile + 1];
   const int rows = g.tiles[4 * tile + 2];
@@ -127,6 +133,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     const long ar = g.a_map ? (long)(g.a_map[p] / g.a_div) : (long)p;
     s_arow[tid] = ar * g.a_stride;
     s_orow[tid] = g.store_by_slot ? g.perm[p] : p;
+    s_rexp[tid] = g.a_exp[ar];
   }
   __syncthreads();
 
@@ -318,8 +325,9 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   }
 
   // Epilogue in four rounds of 32 rows: the wavefronts holding those rows put
-  // them in an fp32 LDS tile [32][256] (columns XOR-swizzled by
-  // 16 * ((row / 4) % 4)), then the workgroup writes whole rows.
+  // them (row scales undone) in an fp32 LDS tile [32][256] (columns
+  // XOR-swizzled by 16 * ((row / 4) % 4)), then the workgroup writes whole
+  // rows.
   float* otile = reinterpret_cast<float*>(st0);
   auto tix = [](int rr, int c) { return rr * kTN + (c ^ (16 * ((rr >> 2) & 3))); };
   for (int round = 0; round < 4; ++round) {
@@ -331,7 +339,8 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int ms = (round & 1) * 2 + m2;
-            otile[tix(m2 * 16 + 4 * grp + i, wn * 64 + ns * 16 + col)] = acc[ms][ns][i];
+            const int rr = m2 * 16 + 4 * grp + i;
+            otile[tix(rr, wn * 64 + ns * 16 + col)] = __builtin_ldexpf(acc[ms][ns][i], -s_rexp[round * 32 + rr]);
           }
     }
     __syncthreads();
@@ -344,49 +353,31 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
           *(f32x4*)(g.slot_out + (long)s_orow[r0 + rr] * g.N + n0 + c) = *(const f32x4*)(otile + tix(rr, c));
       }
     } else {
-      // FC2 operand rows for this tile's codes: ReLU code j = column n;
-      // SwiGLU code j = columns 2j (gate) and 2j + 1 (linear).
+      // fp32 FC2 operand rows (natural code order) for this tile's codes,
+      // four a thread: ReLU code j = column n; SwiGLU code j = columns 2j
+      // (gate) and 2j + 1 (linear).
       constexpr bool swiglu = EPI == EPI_SWIGLU;
       const int I = swiglu ? g.N / 2 : g.N;
-      constexpr int jw = swiglu ? kTN / 2 : kTN;  // codes of this tile (whole 32-code blocks)
+      constexpr int jw = swiglu ? kTN / 2 : kTN;  // codes of this tile
       const int jbase = swiglu ? n0 / 2 : n0;
-      const int gtot = (int)(g.act_stride / 32);
-      for (int idx = tid; idx < rlim * (jw / 8); idx += kTThreads) {
-        const int rr = idx / (jw / 8);
-        const int gq = jbase / 8 + idx % (jw / 8);
-        if (gq >= gtot) continue;
-        const int j0 = BITS == 4 ? 8 * gq : ((8 * gq) & ~31) | (sigma8(gq & 3) << 3);
-        float a[8];
+      for (int idx = tid; idx < rlim * (jw / 4); idx += kTThreads) {
+        const int rr = idx / (jw / 4);
+        const int j0 = jbase + 4 * (idx % (jw / 4));
+        if (j0 >= I) continue;
+        f32x4 a;
         if constexpr (swiglu) {
           const int t0 = 2 * (j0 - jbase);
-          f32x4 v[4];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float gv = v[c >> 1][2 * (c & 1)], uv = v[c >> 1][2 * (c & 1) + 1];
-            a[c] = j0 + c < I ? swiglu_act(gv, uv, g.alpha, g.beta, g.limit) : 0.f;
-          }
+          const f32x4 v0 = *(const f32x4*)(otile + tix(rr, t0)), v1 = *(const f32x4*)(otile + tix(rr, t0 + 4));
+          a[0] = swiglu_act(v0[0], v0[1], g.alpha, g.beta, g.limit);
+          a[1] = swiglu_act(v0[2], v0[3], g.alpha, g.beta, g.limit);
+          a[2] = swiglu_act(v1[0], v1[1], g.alpha, g.beta, g.limit);
+          a[3] = swiglu_act(v1[2], v1[3], g.alpha, g.beta, g.limit);
         } else {
-          const int t0 = j0 - jbase;
-          f32x4 v[2];
+          const f32x4 v = *(const f32x4*)(otile + tix(rr, j0 - jbase));
 #pragma unroll
-          for (int m = 0; m < 2; ++m) v[m] = *(const f32x4*)(otile + tix(rr, t0 + 4 * m));
-#pragma unroll
-          for (int c = 0; c < 8; ++c) a[c] = j0 + c < I ? fmaxf(v[c >> 2][c & 3], 0.f) : 0.f;
+          for (int c = 0; c < 4; ++c) a[c] = fmaxf(v[c], 0.f);
         }
-        f16x8 hi, lo;
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          const int c = BITS == 4 ? perm4_of_slot(sl) : sl;  // code j0 + c sits at storage slot sl
-          _Float16 hh, ll;
-          split_f16(a[c], hh, ll);
-          hi[sl] = hh;
-          lo[sl] = ll;
-        }
-        uint8_t* dst = g.act + (long)(p0 + r0 + rr) * g.act_stride + (long)gq * 32;
-        *(f16x8*)dst = hi;
-        *(f16x8*)(dst + 16) = lo;
+        *(f32x4*)(g.act + (long)(p0 + r0 + rr) * g.act_stride + (long)j0 * 4) = a;
       }
     }
     __syncthreads();

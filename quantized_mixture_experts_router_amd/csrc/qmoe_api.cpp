@@ -1,8 +1,8 @@
 // C ABI entry points of the QMoE library (declared in include/qmoe.h).
 //
 // qmoe_forward enqueues, on the caller's stream:
-//   router -> permutation (histogram, scan, stable scatter) -> operand prep ->
-//   FC1 + activation -> FC2 -> combine
+//   router -> permutation (histogram, scan, stable scatter) -> FC1 operand
+//   rows -> FC1 + activation -> FC2 operand rows -> FC2 -> combine
 // with every intermediate in the caller's workspace.  It allocates nothing and
 // never synchronises.
 #include <hip/hip_runtime.h>
@@ -58,9 +58,12 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* out = static_cast<float*>(const_cast<void*>(output->data));
   const int T = (int)d.T, H = (int)d.H, E = (int)d.E, I = (int)d.I, k = (int)d.k, S = (int)p.S;
+  const int El = (int)d.El;
+  // no FFN work: I == 0 (variant quant_zero_inter of the manifest) or a
+  // share that holds no expert; every output element is zero
+  const bool ffn = d.I > 0 && d.El > 0;
 
-  if (d.I == 0) {
-    // Variant quant_zero_inter of the manifest: every output element is zero.
+  if (!ffn) {
     QMOE_TRY_HIP(launch_fill_zero(out, (long)d.T * d.H, s));
     if (!dbg) return QMOE_OK;
   }
@@ -77,15 +80,26 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
   float* slot = reinterpret_cast<float*>(ws + p.off_slot);
   // slot ids of the tile rows, for the weight-streaming kernels
   int* trows = p.s1.on || p.s2.on ? reinterpret_cast<int*>(ws + p.off_trows) : nullptr;
+  // a share of the experts: local expert of every slot (El = not held)
+  int* local = p.share ? reinterpret_cast<int*>(ws + p.off_local) : nullptr;
 
   auto mark = [&](int i) -> hipError_t {
-    if (dbg && d.I > 0 && dbg->events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(dbg->events[i]), s);
+    if (dbg && ffn && dbg->events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(dbg->events[i]), s);
     return hipSuccess;
   };
   QMOE_TRY_HIP(mark(0));
   if (p.small_front) {
     QMOE_TRY_HIP(launch_route_small(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize,
                                     (int)p.bm, topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows, s));
+  } else if (p.share) {
+    // routing over all E logits; the permutation groups the slots by the
+    // held experts, with one more group (no tiles) for the others
+    QMOE_TRY_HIP(launch_router(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize, topk_idx,
+                               topk_w, s));
+    QMOE_TRY_HIP(launch_local_index(topk_idx, S, (int)d.first, El, local, s));
+    QMOE_TRY_HIP(launch_permute(local, S, El + 1, (int)p.chunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets,
+                                perm, tiles, ntiles, s, El));
+    if (trows) QMOE_TRY_HIP(launch_tile_rows(perm, tiles, ntiles, (int)p.max_tiles, (int)p.bm, trows, s));
   } else {
     QMOE_TRY_HIP(launch_router(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize, topk_idx,
                                topk_w, s));
@@ -93,21 +107,26 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
                                 perm, tiles, ntiles, s));
     if (trows) QMOE_TRY_HIP(launch_tile_rows(perm, tiles, ntiles, (int)p.max_tiles, (int)p.bm, trows, s));
   }
-  if (d.I > 0) {
-    // The streaming FC1 splits the fp32 input rows itself while staging them
-    // (and its activation pass writes whole FC2 operand rows, padding
-    // included); otherwise the operand rows and the padding codes [I, kp2)
-    // of FC2's operand rows are prepared here.
+  if (ffn) {
+    // Operand rows of FC1.  The streaming FC1 splits the fp32 input rows
+    // itself while staging them (a single-stage launch scales each row per K
+    // range on its own; a double-buffered one takes each row's exponent from
+    // here); the tiled and register-tiled GEMMs read hi/lo rows prepared here.
+    int* exp1 = reinterpret_cast<int*>(ws + p.off_exp1);
+    int* exp2 = reinterpret_cast<int*>(ws + p.off_exp2);
+    const float* x = static_cast<const float*>(input->data);
     const bool a_f32 = p.s1.on;
     if (!a_f32)
-      QMOE_TRY_HIP(launch_prep_a(d.bits, static_cast<const float*>(input->data), T, H, (int)p.kp1, xa, act, S, I,
-                                 (int)p.kp2, s));
+      QMOE_TRY_HIP(launch_split_rows(d.bits, x, H, H, xa, 4 * (long)p.kp1, (int)p.kp1, T, exp1, s));
+    else if (!p.s1.one)
+      QMOE_TRY_HIP(launch_row_exp(x, H, T, H, exp1, s));
     QMOE_TRY_HIP(mark(1));
     GemmArgs g1{};
     g1.wq = static_cast<const uint8_t*>(fc1w->data);
     g1.ws = static_cast<const float*>(fc1s->data);
     g1.a = a_f32 ? static_cast<const uint8_t*>(input->data) : xa;
     g1.a_f32 = a_f32;
+    g1.a_exp = (a_f32 && p.s1.one) ? nullptr : exp1;
     g1.a_map = perm;
     g1.a_div = k;
     g1.a_stride = a_f32 ? 4 * H : 4 * p.kp1;
@@ -150,11 +169,21 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
       QMOE_TRY_HIP(launch_gemm(d.bits, epi1, p.mt, p.aligned, g1, (int)p.max_tiles, s));
       QMOE_TRY_HIP(mark(2));
     }
+    // Operand rows of FC2: FC1 left fp32 rows (stride kp2 codes).  The
+    // streaming FC2 splits them while staging; the other GEMMs take them as
+    // hi/lo rows, converted here in place.
+    float* act32 = reinterpret_cast<float*>(act);
+    if (!p.s2.on)
+      QMOE_TRY_HIP(launch_split_rows(d.bits, act32, p.kp2, I, act, 4 * (long)p.kp2, (int)p.kp2, S, exp2, s));
+    else if (!p.s2.one)
+      QMOE_TRY_HIP(launch_row_exp(act32, p.kp2, S, I, exp2, s));
     QMOE_TRY_HIP(mark(3));
     GemmArgs g2{};
     g2.wq = static_cast<const uint8_t*>(fc2w->data);
     g2.ws = static_cast<const float*>(fc2s->data);
     g2.a = act;
+    g2.a_f32 = p.s2.on;
+    g2.a_exp = (p.s2.on && p.s2.one) ? nullptr : exp2;
     g2.a_map = nullptr;
     g2.a_div = 1;
     g2.a_stride = 4 * p.kp2;
@@ -180,14 +209,14 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
       QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
     }
     QMOE_TRY_HIP(mark(4));
-    QMOE_TRY_HIP(launch_combine(slot, topk_w, T, k, H, p.splits2, out, s));
+    QMOE_TRY_HIP(launch_combine(slot, topk_w, T, k, H, p.splits2, out, s, local, El));
     QMOE_TRY_HIP(mark(5));
   }
   if (dbg) {
     if (dbg->topk_idx) QMOE_TRY_HIP(launch_copy_i32(topk_idx, dbg->topk_idx, S, s));
     if (dbg->topk_w) QMOE_TRY_HIP(launch_copy_f32(topk_w, dbg->topk_w, S, s));
-    if (dbg->counts) QMOE_TRY_HIP(launch_copy_i32(counts, dbg->counts, E, s));
-    if (dbg->offsets) QMOE_TRY_HIP(launch_copy_i32(offsets, dbg->offsets, E + 1, s));
+    if (dbg->counts) QMOE_TRY_HIP(launch_copy_i32(counts, dbg->counts, El, s));
+    if (dbg->offsets) QMOE_TRY_HIP(launch_copy_i32(offsets, dbg->offsets, El + 1, s));
     if (dbg->perm) QMOE_TRY_HIP(launch_copy_i32(perm, dbg->perm, S, s));
   }
   return QMOE_OK;
@@ -215,6 +244,7 @@ void qmoe_attrs_default(qmoe_attrs* a) {
   a->quant_type = 0;
   a->has_swiglu_limit = 0;
   a->swiglu_limit = 0.f;
+  a->first_expert = 0;
 }
 
 qmoe_status qmoe_validate(const qmoe_tensor* input, const qmoe_tensor* router_probs, const qmoe_tensor* fc1w,

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <string>
 
 // Workgroups the streaming kernels aim for before splitting K (two per
 // compute unit on 256 compute units).
@@ -47,6 +48,22 @@ int64_t max_one_splits() {
 }
 
 bool rank_ok(const qmoe_tensor* t, int r) { return t->rank == r; }
+
+// GEMM path override, for measuring the paths against each other: the
+// environment variable QMOE_PATH = "stream" (weight streaming, 64-row tiles
+// past 64 tokens), "tiled" (LDS-tiled where the shapes allow, else
+// register-tiled) or "gemm" (register-tiled); unset or anything else: the
+// plan's own choice.
+enum { PATH_AUTO = 0, PATH_STREAM = 1, PATH_TILED = 2, PATH_GEMM = 3 };
+int path_override() {
+  const char* v = std::getenv("QMOE_PATH");
+  if (!v) return PATH_AUTO;
+  const std::string s(v);
+  if (s == "stream") return PATH_STREAM;
+  if (s == "tiled") return PATH_TILED;
+  if (s == "gemm") return PATH_GEMM;
+  return PATH_AUTO;
+}
 
 }  // namespace
 
@@ -105,7 +122,10 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
   if (!rank_ok(router, 2) || !rank_ok(fc1w, 3) || !rank_ok(fc2w, 3)) return QMOE_ERR_SHAPE;
   const int64_t E = router->dims[1];
   if (router->dims[0] != T || E < 0) return QMOE_ERR_SHAPE;
-  if (fc1w->dims[0] != E || fc2w->dims[0] != E) return QMOE_ERR_SHAPE;
+  // The weights hold El consecutive experts from first_expert (all E by default).
+  const int64_t El = fc1w->dims[0];
+  if (El < 0 || El > E || fc2w->dims[0] != El) return QMOE_ERR_SHAPE;
+  if (a->first_expert < 0 || a->first_expert + El > E) return QMOE_ERR_ATTR;
   const int64_t F = fc1w->dims[1];
   if (F < 0 || F % fusion != 0) return QMOE_ERR_SHAPE;
   const int64_t I = F / fusion;
@@ -115,7 +135,7 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
   if (bs != 0 && (H % bs != 0 || I % bs != 0)) return QMOE_ERR_SHAPE;
   // quantScalesOk
   if (fc1s->rank < 2 || fc2s->rank < 2) return QMOE_ERR_SHAPE;
-  if (fc1s->dims[0] != E || fc2s->dims[0] != E || fc1s->dims[1] != F || fc2s->dims[1] != H)
+  if (fc1s->dims[0] != El || fc2s->dims[0] != El || fc1s->dims[1] != F || fc2s->dims[1] != H)
     return QMOE_ERR_SHAPE;
   if (bs == 0) {
     if (fc1s->rank != 2 || fc2s->rank != 2) return QMOE_ERR_SHAPE;
@@ -129,6 +149,7 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
   if (E > kMaxExperts) return QMOE_ERR_UNSUPPORTED;
 
   d->T = T; d->H = H; d->E = E; d->I = I; d->F = F; d->k = a->k;
+  d->El = El; d->first = a->first_expert;
   d->bits = bits; d->pack = pack; d->mid = bits == 4 ? 8 : 128; d->fusion = fusion;
   d->bs = bs; d->nb1 = bs ? H / bs : 1; d->nb2 = bs ? I / bs : 1;
   d->act = swiglu ? QMOE_ACT_SWIGLU : QMOE_ACT_RELU;
@@ -143,35 +164,41 @@ void make_plan(const Dims& d, Plan* p) {
   p->d = d;
   p->S = d.T * d.k;
   if (d.T == 0) return;  // nothing to enqueue
+  p->share = d.El < d.E;
   // Every expert receives at most T rows (a token selects distinct experts),
   // so up to 64 tokens one M tile of ceil(T/16)*16 rows holds any expert's
-  // rows and the weights stream from HBM exactly once.
-  p->decode = d.T <= 64;
-  p->mt = p->decode ? int((d.T + 15) / 16) : 4;
+  // rows and the weights stream from HBM exactly once.  Past that (forced by
+  // QMOE_PATH) an expert's rows take several 64-row tiles, each streaming the
+  // weights again.
+  const int force = path_override();
+  p->decode = force == PATH_STREAM || (force == PATH_AUTO && d.T <= kStreamMaxTokens);
+  p->mt = p->decode ? int(std::min<int64_t>((d.T + 15) / 16, 4)) : 4;
   p->bm = 16 * p->mt;
   // Larger token counts: the LDS-tiled GEMMs when both reductions are whole
   // 64-code steps, rows are 8-code aligned and scale blocks are >= 32 codes
   // (else the register-tiled GEMMs with 64-row tiles).
   const bool aligned8 = (d.H % 8 == 0) && (d.I % 8 == 0);
-  p->tiled = !p->decode && d.I > 0 && aligned8 && d.H % 64 == 0 && d.I % 64 == 0 && (d.bs == 0 || d.bs >= 32);
+  p->tiled = !p->decode && force != PATH_GEMM && d.I > 0 && aligned8 && d.H % 64 == 0 && d.I % 64 == 0 &&
+             (d.bs == 0 || d.bs >= 32);
   if (p->tiled) p->bm = 128;
   // Sum over experts of ceil(count / bm) <= ceil(S / bm) + E; when one tile
   // holds any expert's rows it is at most E (one tile per used expert).
-  p->max_tiles = p->decode ? d.E : (p->S + p->bm - 1) / p->bm + d.E;
+  p->max_tiles = (p->decode && d.T <= p->bm) ? d.El : (p->S + p->bm - 1) / p->bm + d.El;
   // With I == 0 only the routing stages run (output is a zero fill).
   p->kp1 = d.I > 0 ? round_up(d.H, 128) : 0;
   p->kp2 = round_up(d.I, 128);
   p->aligned = (d.H % 8 == 0) && (d.I % 8 == 0);
   p->nchunks = (p->S + p->chunk - 1) / p->chunk;
-  p->small_front = p->S <= 1024 && d.E <= 1024;
-  if (p->decode && d.I > 0) {
+  // a share permutes over El + 1 groups (the last: slots of experts not held)
+  p->small_front = !p->share && p->S <= 1024 && d.E <= 1024;
+  if (p->decode && d.I > 0 && d.El > 0) {
     // Weight-streaming kernels: stages of stg items (256 codes an item at 4
     // bits, 128 at 8); the stages must tile K.  Scale blocks that end inside a
     // 64-byte chunk (bs < codes per chunk) must come 4 to 16 to a stage.
     const int64_t item_codes = d.bits == 4 ? 256 : 128;
     const int64_t chunk_codes = item_codes / 2;
     auto shape = [&](Plan::Stream& st, int64_t K, int64_t N) {
-      const int64_t units = d.E * ceil_div(N, 128 * QMOE_STREAM_NT);
+      const int64_t units = d.El * ceil_div(N, 128 * QMOE_STREAM_NT);
       auto fits = [&](int64_t scodes) {
         if (!(K > 0 && K % scodes == 0 && (d.bs == 0 || d.bs >= 32))) return false;
         if (d.bs > 0 && d.bs < chunk_codes) {
@@ -213,7 +240,7 @@ void make_plan(const Dims& d, Plan* p) {
       st.wg_rows = 0;
       const int64_t rbrows = 128 * QMOE_STREAM_NT;
       if (p->mt == 1 && splits == 1 && units > QMOE_STREAM_MIN_WORKGROUPS) {
-        const int64_t r = round_up(ceil_div(d.E * N, QMOE_STREAM_MIN_WORKGROUPS), 64);
+        const int64_t r = round_up(ceil_div(d.El * N, QMOE_STREAM_MIN_WORKGROUPS), 64);
         st.wg_rows = (int)std::min(r, 2 * rbrows);
       }
     };
@@ -225,14 +252,18 @@ void make_plan(const Dims& d, Plan* p) {
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   p->off_topk_idx = take(sizeof(int32_t) * p->S);
   p->off_topk_w = take(sizeof(float) * p->S);
-  p->off_counts = take(sizeof(int32_t) * d.E);
-  p->off_offsets = take(sizeof(int32_t) * (d.E + 1));
+  const int64_t groups = p->share ? d.El + 1 : d.E;  // permutation groups
+  p->off_counts = take(sizeof(int32_t) * groups);
+  p->off_offsets = take(sizeof(int32_t) * (groups + 1));
   p->off_perm = take(sizeof(int32_t) * p->S);
   p->off_tiles = take(sizeof(int32_t) * 4 * p->max_tiles);
   p->off_ntiles = take(sizeof(int32_t) * 4);
-  p->off_hist = take(sizeof(int32_t) * p->nchunks * d.E);
+  p->off_hist = take(sizeof(int32_t) * p->nchunks * groups);
   p->off_xa = take(p->s1.on ? 0 : size_t(4) * d.T * p->kp1);  // f16 hi + lo per element (streaming FC1 reads fp32 rows)
-  p->off_act = take(size_t(4) * p->S * p->kp2);   // f16 hi + lo per element
+  p->off_act = take(size_t(4) * p->S * p->kp2);   // fp32 per element, or f16 hi + lo after the split pass
+  p->off_exp1 = take(sizeof(int32_t) * d.T);
+  p->off_exp2 = take(sizeof(int32_t) * p->S);
+  p->off_local = take(p->share ? sizeof(int32_t) * p->S : 0);
   p->off_slot = take(d.I > 0 ? sizeof(float) * p->splits2 * p->S * d.H : 0); // FC2 rows by slot id
   p->off_part1 = take(p->s1.on && p->s1.splits > 1 ? sizeof(float) * p->s1.splits * p->S * d.F : 0);
   p->off_trows = take(p->s1.on || p->s2.on ? sizeof(int32_t) * p->max_tiles * p->bm : 0);

@@ -14,7 +14,9 @@ namespace qmoe {
 struct Dims {
   int64_t T = 0;   // tokens = numel(input) / H
   int64_t H = 0;   // hidden size
-  int64_t E = 0;   // experts
+  int64_t E = 0;   // experts (router logits per token)
+  int64_t El = 0;  // experts held by the weights: global experts [first, first + El)
+  int64_t first = 0;
   int64_t I = 0;   // inter size
   int64_t F = 0;   // FC1 rows = fusion * I
   int64_t k = 0;
@@ -30,6 +32,10 @@ struct Dims {
 
 // Largest expert count the routing kernels hold in registers / LDS.
 constexpr int64_t kMaxExperts = 1024;
+
+// Token counts up to which the weight-streaming GEMMs run (every expert's
+// rows then fit one tile of at most 64 rows, and the weights leave HBM once).
+constexpr int64_t kStreamMaxTokens = 64;
 
 qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const qmoe_tensor* fc1w,
                      const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
@@ -67,11 +73,14 @@ struct Plan {
   size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path with K ranges)
   size_t off_trows = 0;  // streaming kernels: slot id of every tile row [max_tiles][bm]
   bool small_front = false;  // router + permutation in one workgroup (S, E <= 1024)
+  bool share = false;    // the weights hold only some of the experts (El < E)
   int64_t chunk = 1024;  // slots per permutation block
   int64_t nchunks = 0;
   // workspace layout
   size_t off_topk_idx = 0, off_topk_w = 0, off_counts = 0, off_offsets = 0, off_perm = 0;
   size_t off_tiles = 0, off_ntiles = 0, off_hist = 0, off_xa = 0, off_act = 0, off_slot = 0;
+  size_t off_exp1 = 0, off_exp2 = 0;  // row scale exponents of the FC1 [T] and FC2 [S] operand rows
+  size_t off_local = 0;  // share: local expert of every slot [S] (El = not held)
   size_t bytes = 0;
 };
 

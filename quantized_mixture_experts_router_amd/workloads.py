@@ -41,6 +41,8 @@ class Workload:
     seed: int = 0
     alpha: float = 1.0
     beta: float = 0.0
+    local_experts: int = 0         # > 0: the weights hold this many experts (a share)
+    first_expert: int = 0          # global index of the share's first expert
 
     @property
     def hidden(self) -> int:
@@ -54,6 +56,11 @@ class Workload:
         return t
 
     @property
+    def held(self) -> int:
+        """Experts the weights hold (all of them unless this is a share)."""
+        return self.local_experts or self.experts
+
+    @property
     def fusion(self) -> int:
         return 2 if self.activation == "swiglu" else 1
 
@@ -62,11 +69,14 @@ class Workload:
         return 2 if self.bits == 4 else 1
 
     def attrs(self) -> dict:
-        return dict(k=self.k, expert_weight_bits=self.bits, block_size=self.block_size,
-                    activation_type=self.activation,
-                    swiglu_fusion=1 if self.activation == "swiglu" else 0,
-                    activation_alpha=self.alpha, activation_beta=self.beta,
-                    normalize_routing_weights=0, routing="qmoe")
+        a = dict(k=self.k, expert_weight_bits=self.bits, block_size=self.block_size,
+                 activation_type=self.activation,
+                 swiglu_fusion=1 if self.activation == "swiglu" else 0,
+                 activation_alpha=self.alpha, activation_beta=self.beta,
+                 normalize_routing_weights=0, routing="qmoe")
+        if self.local_experts:
+            a["first_expert"] = self.first_expert
+        return a
 
     def describe(self) -> dict:
         d = asdict(self)
@@ -87,22 +97,38 @@ WORKLOADS = {
                         (0.001, 0.005), logit_sigma=1.5),
 }
 
+# One GPU's share of two layers when they are spread over 8 GPUs (the pages
+# define no such split; these are the shares measured on one GPU):
+#  * large_e_ep8: the 128-expert layer with its experts spread 16 to a GPU;
+#    the input and router logits are those of large_e (drawn first, with the
+#    same seed, so the routing is large_e's), the weights those of the 16
+#    experts from expert 0;
+#  * decode_tp8: the decode layer with its inter size split 8 ways (FC1 rows
+#    in gate/linear pairs, FC2 columns): inter 14336 / 8 = 1792.
+SHARE_WORKLOADS = {
+    "large_e_ep8": Workload("large_e_ep8", (4, 2048, 4096), 128, 1536, 8, 8, 0, "swiglu",
+                            (0.001, 0.005), logit_sigma=1.5, local_experts=16, first_expert=0),
+    "decode_tp8": Workload("decode_tp8", (16, 4096), 8, 1792, 2, 4, 64, "swiglu", (0.002, 0.01)),
+}
+WORKLOADS.update(SHARE_WORKLOADS)
+
 
 def shapes(w: Workload) -> dict:
     T, H, E, I = w.tokens, w.hidden, w.experts, w.inter
     F = w.fusion * I
+    El = w.held
     d = {
         "input": tuple(w.input_shape),
         "router_probs": (T, E),
-        "fc1_experts_weights": (E, F, H // w.pack),
-        "fc2_experts_weights": (E, H, I // w.pack),
+        "fc1_experts_weights": (El, F, H // w.pack),
+        "fc2_experts_weights": (El, H, I // w.pack),
     }
     if w.block_size:
-        d["fc1_scales"] = (E, F, H // w.block_size)
-        d["fc2_scales"] = (E, H, I // w.block_size)
+        d["fc1_scales"] = (El, F, H // w.block_size)
+        d["fc2_scales"] = (El, H, I // w.block_size)
     else:
-        d["fc1_scales"] = (E, F)
-        d["fc2_scales"] = (E, H)
+        d["fc1_scales"] = (El, F)
+        d["fc2_scales"] = (El, H)
     return d
 
 

@@ -26,7 +26,7 @@ def to_dev(arrs, torch):
 def run_gpu(arrs, attrs, torch, debug=True, stream=None):
     d = to_dev(arrs, torch)
     T = int(np.prod(arrs["input"].shape[:-1]))
-    E = arrs["router_probs"].shape[1]
+    E = arrs["fc1_experts_weights"].shape[0]  # experts the weights hold (counts/offsets are over them)
     k = attrs["k"]
     dbg = None
     if debug:

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert qm.qmoe_abi_version() == 2
+    assert qm.qmoe_abi_version() == 3
     for s in range(9):
         assert qm.qmoe_status_string(s) != "unknown status"
 
@@ -54,6 +54,7 @@ def test_attribute_defaults_match_manifest(lib):
     assert a.use_sparse_mixer == 0 and a.weights_prepacked == -1 and a.quant_type == 0
     assert a.block_size == 0 and a.routing == 0
     assert a.has_swiglu_limit == 0  # swiglu_limit is optional: omitted means no clamp
+    assert a.first_expert == 0  # the weights hold every expert from expert 0
 
 
 KIND = {"shape": 2, "attr": 3, "unsupported": 4, "dtype": 7}
@@ -83,6 +84,15 @@ def _mutate(a, attrs, mut):
         a["input"] = a["input"].astype(np.float64)
     elif mut == "rank4":
         a["input"] = a["input"][None, None]
+    elif mut == "share_more":
+        a["router_probs"] = a["router_probs"][:, :3]   # weights hold 4 experts, router only 3
+    elif mut.startswith("share"):
+        # weights for experts [first, first + held) of the router's 4
+        first, held = {"share": (1, 2), "share_top": (2, 2), "share_none": (4, 0), "share_past": (3, 2),
+                       "share_neg": (-1, 2)}[mut]
+        attrs["first_expert"] = first
+        for n in ("fc1_experts_weights", "fc1_scales", "fc2_experts_weights", "fc2_scales"):
+            a[n] = a[n][max(first, 0):max(first, 0) + held]
 
 
 CASES = [
@@ -96,6 +106,8 @@ CASES = [
     ("packed_cols", {}, "packed_cols"), ("scale_rank", {}, "scale_rank"), ("dtype", {}, "dtype"),
     ("rank4", {}, "rank4"), ("moe_norm", dict(routing="moe", normalize_routing_weights=1), None),
     ("bs16", dict(block_size=16), "bs16"), ("swiglu", dict(activation_type="swiglu", swiglu_fusion=1), "swiglu"),
+    ("share", {}, "share"), ("share_top", {}, "share_top"), ("share_none", {}, "share_none"),
+    ("share_past", {}, "share_past"), ("share_neg", {}, "share_neg"), ("share_more", {}, "share_more"),
 ]
 
 

@@ -43,31 +43,43 @@ def test_unused_experts_are_not_counted():
     w = W.WORKLOADS["decode"]
     counts = np.array([3, 0, 5, 0, 0, 8, 16, 0])
     fc1, _ = bench.kernel_work(w, counts)
-    full, _ = bench.kernel_work(w, np.ones(8))
+    full, _ = bench.kernel_work(w, np.full(8, 4))
     assert fc1["used_experts"] == 4
     assert fc1["weight_bytes"] * 2 == full["weight_bytes"]
+
+
+def test_share_work_counts_held_slots():
+    # an expert share counts only the slots routed to the experts it holds
+    w = W.WORKLOADS["large_e_ep8"]
+    counts = np.full(w.held, 512)
+    fc1, fc2 = bench.kernel_work(w, counts)
+    S = 16 * 512
+    assert fc1["flops"] == 2.0 * S * 2 * w.inter * w.hidden
+    assert fc2["flops"] == 2.0 * S * w.hidden * w.inter
 
 
 def test_roofline_bound_follows_intensity():
     # decode FC1: about 14 FLOP/B, far below the f16 ridge (2500 TFLOP/s over
     # 8 TB/s = 312.5 FLOP/B)
     w = W.WORKLOADS["decode"]
-    fc1, _ = bench.kernel_work(w, np.ones(8))
+    fc1, _ = bench.kernel_work(w, np.full(8, 4))
     r = bench.roofline_for(fc1, 0.1)
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert abs(r["achieved"] - fc1["bytes"] / 1e-4 / 1e9) < 0.1
     assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
     # prefill FC1: thousands of FLOP/B, matrix-core bound
     w = W.WORKLOADS["prefill"]
-    fc1, _ = bench.kernel_work(w, np.ones(8))
+    fc1, _ = bench.kernel_work(w, np.full(8, 1024))
     r = bench.roofline_for(fc1, 4.0)
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
     assert abs(r["achieved"] - fc1["flops"] / 4e-3 / 1e12) < 0.1
 
 
 def test_kernel_choice_per_workload():
-    assert bench.gemm_kernel(W.WORKLOADS["tiny"]) == "qmoe_stream"
+    assert bench.gemm_kernel(W.WORKLOADS["tiny"]) == "qmoe_gemm"          # K = 64: no whole 128-byte items
     assert bench.gemm_kernel(W.WORKLOADS["decode"]) == "qmoe_stream"
+    assert bench.gemm_kernel(W.WORKLOADS["decode"], "fc2") == "qmoe_stream"
+    assert bench.gemm_kernel(W.WORKLOADS["large_e_ep8"]) == "qmoe_tiled"
     for name in ("prefill", "fine", "large_e"):
         assert bench.gemm_kernel(W.WORKLOADS[name]) == "qmoe_tiled"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1"]) == "qmoe_gmm_f32_rows16"

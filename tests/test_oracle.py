@@ -132,6 +132,23 @@ def test_lifted_with_bias_example():
     np.testing.assert_allclose(dense, np.array(g["expected_output"]), atol=g["tolerance"], rtol=0)
 
 
+def test_relu_negative_branch_example():
+    # ReLU's negative branch: one FC1 output of every selected expert is
+    # negative and must be zeroed (hand-worked values in the fixture)
+    g = _load("qmoe_relu_negative.json")
+    x = np.array(g["input"], dtype=np.float32)
+    logits = np.array(g["router_probs"], dtype=np.float32)
+    fc1 = np.array(g["fc1_codes"], dtype=np.uint8)
+    fc2 = np.array(g["fc2_codes"], dtype=np.uint8)
+    arrs = (x, logits, fc1, np.full(fc1.shape[:2], g["fc1_scale"], dtype=np.float32), fc2,
+            np.full(fc2.shape[:2], g["fc2_scale"], dtype=np.float32))
+    out, inter = oracle.qmoe(*arrs, attrs=g["attrs"], return_intermediates=True)
+    np.testing.assert_array_equal(inter["sel"], np.array(g["expected_selection"]))
+    np.testing.assert_allclose(out, np.array(g["expected_output"]), atol=g["tolerance"], rtol=0)
+    dense = oracle.qmoe_dense(*arrs, attrs=g["attrs"])
+    np.testing.assert_allclose(dense, np.array(g["expected_output"]), atol=g["tolerance"], rtol=0)
+
+
 # ---------------------------------------------------------------- SwiGLU closed forms
 @pytest.mark.parametrize("ci", [0, 1])
 def test_swiglu_interleave_closed_form(ci):
@@ -446,6 +463,7 @@ def _pins_pass():
     """Run the value pins; return False if any of them fails."""
     try:
         test_lifted_with_bias_example()
+        test_relu_negative_branch_example()
         test_swiglu_interleave_closed_form(0)
         test_nibble_order_convention()
         for c in _load("route_ties.json")["cases"]:
@@ -455,7 +473,18 @@ def _pins_pass():
     return True
 
 
-@pytest.mark.parametrize("mutation", ["nibbles", "gate_odd", "fc1_transposed", "full_softmax", "no_midpoint"])
+def _relu_leaky(h, act, alpha=1.0, beta=0.0, limit=float("inf")):
+    # ReLU without its clamp (identity on negative values)
+    if act == "relu":
+        return np.asarray(h, dtype=np.float64)
+    return _orig_activation(h, act, alpha, beta, limit)
+
+
+_orig_activation = Q.activation
+
+
+@pytest.mark.parametrize("mutation", ["nibbles", "gate_odd", "fc1_transposed", "full_softmax", "no_midpoint",
+                                      "relu_no_clamp"])
 def test_planted_mistakes_fail_a_pin(monkeypatch, mutation):
     assert _pins_pass()
     if mutation == "nibbles":
@@ -469,6 +498,8 @@ def test_planted_mistakes_fail_a_pin(monkeypatch, mutation):
         wrong = _full_softmax_route(Q.route)
         monkeypatch.setattr(Q, "route", wrong)
         monkeypatch.setattr(oracle, "route", wrong)
+    elif mutation == "relu_no_clamp":
+        monkeypatch.setattr(Q, "activation", _relu_leaky)
     elif mutation == "no_midpoint":
         def no_mid(packed, scales, bits, bs):
             q = Q.unpack_codes(packed, bits).astype(np.float64)
