@@ -177,6 +177,7 @@ KERNEL_SRC = {
     "qmoe_gemm": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gemm.hip"),
     "qmoe_gmm_f32": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm.hip"),
     "qmoe_gmm_f32_rows16": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm.hip"),
+    "qmoe_gmm_typed": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
 }
 
 
@@ -214,11 +215,11 @@ def stream_fits(w, K):
 
 def gemm_kernel(w, which="fc1"):
     """Which grouped-GEMM kernel the library runs for one GEMM of this
-    workload (the library's plan: weight streaming up to 64 tokens when the
-    reduction length fits its stages, the LDS-tiled GEMM above 64 tokens for
+    workload (the library's plan: weight streaming up to 96 tokens when the
+    reduction length fits its stages, the LDS-tiled GEMM above 96 tokens for
     64-multiple H and I with column-wise or >= 32-code scale blocks, else the
     register-tiled one)."""
-    if w.tokens <= 64:
+    if w.tokens <= 96:
         return "qmoe_stream" if stream_fits(w, w.hidden if which == "fc1" else w.inter) else "qmoe_gemm"
     tiled = w.hidden % 64 == 0 and w.inter % 64 == 0 and (w.block_size == 0 or w.block_size >= 32)
     return "qmoe_tiled" if tiled else "qmoe_gemm"
@@ -245,9 +246,13 @@ def call_latency(step, n, evict=None):
     return dict(median=round(float(q[0]), 5), p10=round(float(q[1]), 5), p90=round(float(q[2]), 5), calls=n)
 
 
+PLAN_SRC = os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "qmoe_plan.cpp")
+
+
 def traffic_for(key, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the kernel source now in the tree; otherwise None."""
+    was taken on the kernel source and the launch planner (which sets the
+    K-range splits and tile shapes) now in the tree; otherwise None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -256,7 +261,9 @@ def traffic_for(key, kernel):
     ent = rec.get(key)
     if not ent or ent.get("kernel") != kernel:
         return None
-    return ent.get("bytes") if ent.get("source_sha") == _sha(KERNEL_SRC[kernel]) else None
+    if ent.get("source_sha") != _sha(KERNEL_SRC[kernel]) or ent.get("plan_sha") != _sha(PLAN_SRC):
+        return None
+    return ent.get("bytes")
 
 
 def copy_calibration(nbytes, reps=3):

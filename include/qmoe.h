@@ -29,8 +29,14 @@
  *    they are DEVICE pointers on the current HIP device.
  *  - The caller owns every buffer.  The library allocates nothing, never
  *    synchronises, and enqueues all work on the caller's stream.
- *  - A non-OK status means nothing was enqueued and the output is untouched.
- *    On QMOE_OK every output element is written by work enqueued on stream.
+ *  - A status from the contract checks (QMOE_ERR_NULL, _SHAPE, _ATTR,
+ *    _UNSUPPORTED, _WORKSPACE, _DTYPE, _ALIGN) means nothing was enqueued and
+ *    the output is untouched: every check runs before the first launch.
+ *    QMOE_ERR_HIP reports a HIP call that failed while enqueueing (a launch,
+ *    or a kernel's one-time opt-in to more than 64 KB of LDS): kernels
+ *    enqueued before it stay enqueued, and the output and workspace contents
+ *    are then unspecified.  On QMOE_OK every output element is written by
+ *    work enqueued on stream.
  *  - Every finite input is in contract.  The matrix cores take f16 operands:
  *    each fp32 operand row (a row of x for FC1, of the activation for FC2) is
  *    multiplied by a power of two of its own, chosen so that its largest
@@ -76,9 +82,9 @@ typedef enum {
   QMOE_U8 = 2,
   QMOE_I32 = 3,
   QMOE_I64 = 4,
-  QMOE_F16 = 5,  /* accepted by GroupedMatMul's type list; not implemented */
-  QMOE_BF16 = 6, /* accepted by GroupedMatMul's type list; not implemented */
-  QMOE_F64 = 7   /* accepted by GroupedMatMul's type list; not implemented */
+  QMOE_F16 = 5,  /* GroupedMatMul only */
+  QMOE_BF16 = 6, /* GroupedMatMul only */
+  QMOE_F64 = 7   /* GroupedMatMul only */
 } qmoe_dtype;
 
 typedef enum {
@@ -219,30 +225,37 @@ qmoe_status qmoe_forward_debug(const qmoe_tensor* input, const qmoe_tensor* rout
 
 /* ------------------------------------------------------------------------
  * GroupedMatMul (ONNX operator page "GroupedMatMul - 29": Summary, Inputs,
- * Outputs, Type Constraints), float32 weights:
+ * Outputs, Type Constraints), in each floating type T of the page's list:
  *
  *   output[m, i, :] = input[m, :] @ weights[g, :, :]  (+ bias[g, :])
  *   g = group_indices[m, i]
  *
  * input [M, K], weights [G, K, N], group_indices [M, S] (int32 or int64),
  * optional bias [G, N] (NULL = no bias), output [M, S, N].  input, weights,
- * bias and output are QMOE_F32 (QMOE_F16 / QMOE_BF16 / QMOE_F64 are in the
- * page's type list and return QMOE_ERR_UNSUPPORTED; any other code is
- * QMOE_ERR_DTYPE); group_indices is QMOE_I32 or QMOE_I64 (else
- * QMOE_ERR_DTYPE).  Ranks or extents that disagree: QMOE_ERR_SHAPE.
+ * bias and output share one type T: QMOE_F32, QMOE_F16, QMOE_BF16 or
+ * QMOE_F64 (any other code, or a mix, is QMOE_ERR_DTYPE); group_indices is
+ * QMOE_I32 or QMOE_I64 (else QMOE_ERR_DTYPE).  Ranks or extents that
+ * disagree: QMOE_ERR_SHAPE.
  * Limits (QMOE_ERR_UNSUPPORTED beyond them): G <= 1023, M * S < 2^30,
  * K < 2^30, N < 2^30, and (ceil(M * S / B) + G + 1) * ceil(N / 128)
- * < 2^31, B = 16 when M * S <= 16 min(G, M * S) and K, N are multiples of
- * 4 (weight-streaming kernel over 16-row tiles), else 64 (LDS-tiled kernel
- * over 64-row, 128-column tiles); one workgroup per tile and column block.
+ * < 2^31, B = 16 for float32 when M * S <= 16 min(G, M * S) and K, N are
+ * multiples of 4 (weight-streaming kernel over 16-row tiles), else 64
+ * (LDS-tiled kernels over 64-row, 128-column tiles); one workgroup per tile
+ * and column block.
  *
  * Indices outside [0, G) are invalid input, for which the page defines no
  * result; this library writes zeros to those output rows and reads no weight
  * or bias for them (negative values do not count back from G).
  *
- * Products and sums are float32: the matrix cores (v_mfma_f32_16x16x4_f32)
- * add four K terms per instruction into a float32 accumulator, in K order
- * from 0; the bias is added last.
+ * Arithmetic per type:
+ *  - float32: products and sums float32; the matrix cores
+ *    (v_mfma_f32_16x16x4_f32) add four K terms per instruction into a
+ *    float32 accumulator, in K order from 0; the bias is added last;
+ *  - float16, bfloat16: exact products of the 16-bit operands summed in a
+ *    float32 accumulator (v_mfma_f32_16x16x32_f16 / _bf16, 32 K terms an
+ *    instruction, in K order), the bias added in float32, the result
+ *    rounded once to T (to nearest, ties to even);
+ *  - double: float64 products and sums (v_mfma_f64_16x16x4_f64), bias last.
  * Conventions (ownership, streams, status, no allocation) as above.
  * ------------------------------------------------------------------------ */
 
@@ -253,9 +266,10 @@ qmoe_status qmoe_grouped_matmul_workspace_size(const qmoe_tensor* input, const q
                                                const qmoe_tensor* output, size_t* bytes);
 
 /* Enqueue GroupedMatMul on stream (a hipStream_t; NULL = the null stream).
- * Device pointers: float tensors 4-byte aligned, group_indices aligned to its
- * element size (QMOE_ERR_ALIGN otherwise); 16-byte aligned input and weights
- * with K and N multiples of 4 take the vector-load path, and the
+ * Device pointers: float tensors aligned to their element size,
+ * group_indices to its element size (QMOE_ERR_ALIGN otherwise); 16-byte
+ * aligned input and weights whose rows are whole 16-byte runs (K and N
+ * multiples of 16 / sizeof(T)) take the vector-load path, and the float32
  * weight-streaming kernel also needs 16-byte aligned bias and output.  workspace: at least
  * qmoe_grouped_matmul_workspace_size bytes, 256-byte aligned, owned by this
  * call until the stream reaches it.  The output must not alias an input.

@@ -27,6 +27,7 @@ SOURCES = [
     "kernels/stream.hip",
     "kernels/tiled.hip",
     "kernels/gmm.hip",
+    "kernels/gmm_typed.hip",
     "kernels/moe.hip",
 ]
 

@@ -264,9 +264,10 @@ hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& 
 }
 
 // out[t, h] = sum_s w[t, s] * (sum_z slot_out[z][t*k + s, h]); z then s
-// ascending, fp32.  One writer per output element, no atomics.  With local
-// given (a share of the experts), slots with local[t*k + s] >= El have no row
-// and are skipped.
+// ascending, fp32.  One writer per output element, no atomics.  SHARE (a
+// share of the experts): slots with local[t*k + s] >= El have no row and are
+// skipped.
+template <bool SHARE>
 __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ slot_out,
                                                     const float* __restrict__ topk_w, int T, int k, int H,
                                                     int splits, float* __restrict__ out,
@@ -279,30 +280,35 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
     const long t = (i * 4) / H;
     const int h = (int)((i * 4) % H);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (splits == 1 && SHARE) {
+      // one partial row per slot, held slots only (a share holds a few of
+      // each token's slots), in slot order
+      for (int s = 0; s < k; ++s)
+        if (local[t * k + s] < El) acc += topk_w[t * k + s] * *(const f32x4*)(slot_out + (t * k + s) * H + h);
+      *(f32x4*)(out + t * H + h) = acc;
+      return;
+    }
     if (splits == 1) {
       // one partial row per slot: eight slots' rows in flight at a time,
       // weighted and summed in slot order
       for (int s0 = 0; s0 < k; s0 += 8) {
         f32x4 v[8];
         float wv[8];
-        bool live[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          live[i] = s0 + i < k && (local == nullptr || local[t * k + s0 + i] < El);
-          if (live[i]) {
+        for (int i = 0; i < 8; ++i)
+          if (s0 + i < k) {
             wv[i] = topk_w[t * k + s0 + i];
             v[i] = *(const f32x4*)(slot_out + (t * k + s0 + i) * H + h);
           }
-        }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (live[i]) acc += wv[i] * v[i];
+          if (s0 + i < k) acc += wv[i] * v[i];
       }
       *(f32x4*)(out + t * H + h) = acc;
       return;
     }
     for (int s = 0; s < k; ++s) {
-      if (local != nullptr && local[t * k + s] >= El) continue;
+      if (SHARE && local[t * k + s] >= El) continue;
       const float w = topk_w[t * k + s];
       const float* src = slot_out + (t * k + s) * H + h;
       f32x4 y;
@@ -325,7 +331,7 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
     const int h = (int)(i % H);
     float acc = 0.f;
     for (int s = 0; s < k; ++s) {
-      if (local != nullptr && local[t * k + s] >= El) continue;
+      if (SHARE && local[t * k + s] >= El) continue;
       float y = slot_out[(t * k + s) * H + h];
       for (int z = 1; z < splits; ++z) y += slot_out[((long)z * S + t * k + s) * H + h];
       acc += topk_w[t * k + s] * y;
@@ -337,8 +343,12 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
 hipError_t launch_combine(const float* slot_out, const float* topk_w, int T, int k, int H, int splits, float* out,
                           hipStream_t st, const int* local, int El) {
   const long n = (H & 3) == 0 ? (long)T * H / 4 : (long)T * H;
-  hipLaunchKernelGGL(qmoe_combine, dim3((n + 255) / 256), dim3(256), 0, st, slot_out, topk_w, T, k, H, splits, out,
-                     local, El);
+  if (local)
+    hipLaunchKernelGGL(qmoe_combine<true>, dim3((n + 255) / 256), dim3(256), 0, st, slot_out, topk_w, T, k, H, splits,
+                       out, local, El);
+  else
+    hipLaunchKernelGGL(qmoe_combine<false>, dim3((n + 255) / 256), dim3(256), 0, st, slot_out, topk_w, T, k, H, splits,
+                       out, local, El);
   return hipGetLastError();
 }
 

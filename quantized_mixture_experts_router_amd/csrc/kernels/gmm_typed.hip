@@ -1,0 +1,270 @@
+// GroupedMatMul (ONNX operator page "GroupedMatMul - 29", Summary) in the
+// page's other floating types, float16, bfloat16 and double (Type
+// Constraints):
+//
+//   out[perm(p), n] = sum_k x[a_perm(p) / S, k] * W[g](k, n)  (+ bias[g, n])
+//
+// over group-sorted rows, with W[g](k, n) = w[g][k][n] (weights [G, K, N]);
+// tiles of group g >= G write zero rows (indices outside [0, G)).  The rows,
+// permutation and tile table come from the routing front end (route.hip),
+// exactly as for float32 (gmm.hip).
+//
+// Arithmetic, per type:
+//  * float16 / bfloat16: products on v_mfma_f32_16x16x32_f16 / _bf16 (exact
+//    products of the 16-bit operands, fp32 accumulation); the bias is added
+//    in fp32 and the sum rounded once to the output type (round to nearest
+//    even);
+//  * double: v_mfma_f64_16x16x4_f64 (fp64 products and accumulation), bias
+//    added in fp64.
+//
+// Work decomposition: a workgroup of 4 wavefronts computes a 64-row x
+// 128-column tile (2 x 2 wavefronts of 32 x 64); each K step's operand slice
+// of both operands is staged in LDS, double buffered, the next step's loads
+// in flight during the matrix instructions.  The 16-bit types keep the
+// weight slice transposed in LDS (column-major, K contiguous), so each lane
+// reads its 8 consecutive K values of a column as one 16-byte load; the
+// double kernel's 16x16x4 instruction takes one K value a lane and reads the
+// slice as stored.
+#include "common.hpp"
+#include "launch.h"
+
+namespace qmoe {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kYM = 64;     // tile rows
+constexpr int kYN = 128;    // tile columns
+constexpr int kYThreads = 256;
+
+template <typename ET>
+struct Ty;
+template <>
+struct Ty<_Float16> {
+  static constexpr int KS = 32;  // K per step: one 16x16x32 instruction
+  using Frag = f16x8;
+  using Acc = f32x4;
+  using AccT = float;
+  static __device__ __forceinline__ Acc mma(const Frag& a, const Frag& b, const Acc& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Ty<__bf16> {
+  static constexpr int KS = 32;
+  using Frag = bf16x8;
+  using Acc = f32x4;
+  using AccT = float;
+  static __device__ __forceinline__ Acc mma(const Frag& a, const Frag& b, const Acc& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Ty<double> {
+  static constexpr int KS = 16;  // K per step: four 16x16x4 instructions
+  using Frag = double;
+  using Acc = f64x4;
+  using AccT = double;
+  static __device__ __forceinline__ Acc mma(double a, double b, const Acc& c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+};
+
+}  // namespace
+
+// VEC: 16-byte loads (x and w 16-byte aligned, K and N whole 16-byte runs).
+template <typename ET, bool VEC>
+__global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, int nblk) {
+  using T = Ty<ET>;
+  constexpr bool WIDE = sizeof(ET) == 8;      // double: 16x16x4, one K value a lane
+  constexpr int KS = T::KS;
+  constexpr int EV = 16 / sizeof(ET);         // elements per 16-byte load
+  // LDS: A [row][k] (+ padding); B 16-bit: [column][k] (transposed), double: [k][column]
+  constexpr int AST = WIDE ? KS + 1 : KS + 8;
+  constexpr int BST = WIDE ? kYN + 2 : KS + 8;
+  constexpr int BLEN = WIDE ? KS * BST : kYN * BST;
+  __shared__ __attribute__((aligned(16))) ET sa[2][kYM * AST];
+  __shared__ __attribute__((aligned(16))) ET sb[2][BLEN];
+  __shared__ int s_arow[kYM];
+  __shared__ int s_orow[kYM];
+
+  const int tile = blockIdx.x / nblk;
+  if (tile >= g.ntiles[0]) return;
+  const int grp = g.tiles[4 * tile + 0];
+  const int p0 = g.tiles[4 * tile + 1];
+  const int rows = g.tiles[4 * tile + 2];
+  const int n0 = (blockIdx.x % nblk) * kYN;
+  const int K = g.K, N = g.N;
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int col = lane & 15, kq = lane >> 4;
+  ET* out = static_cast<ET*>(g.out);
+
+  if (tid < kYM) {
+    const int p = p0 + min(tid, rows - 1);
+    s_arow[tid] = g.a_perm[p] / g.a_div;
+    s_orow[tid] = g.perm[p];
+  }
+  __syncthreads();
+
+  if (grp >= g.G) {  // index outside [0, G): zero rows
+    for (int idx = tid; idx < rows * kYN; idx += kYThreads) {
+      const int rr = idx / kYN, c = idx % kYN;
+      if (n0 + c < N) out[(long)s_orow[rr] * N + n0 + c] = (ET)0.f;
+    }
+    return;
+  }
+
+  const ET* x = static_cast<const ET*>(g.a);
+  const ET* wg = static_cast<const ET*>(g.w) + (long)grp * K * N;
+  // Staging of one K step, global -> registers -> LDS.  Elements past K or
+  // N read as zero; rows past the tile re-read a valid row.
+  //  A: KS x 64 elements, row tid / 4, AQ = KS / 4 consecutive k from
+  //     AQ * (tid % 4);
+  //  B: KS x 128 elements, BQ = KS * 128 / 256 a thread, in runs of EV
+  //     consecutive columns of one k row.
+  constexpr int AQ = KS / 4;                 // 8 (16-bit) or 4 (double)
+  constexpr int BQ = KS * kYN / kYThreads;   // 16 or 8
+  constexpr int BR = BQ / EV;                // 16-byte runs a thread: 2 or 4
+  const ET* arow = x + (long)s_arow[tid >> 2] * K;
+  const int ak = (tid & 3) * AQ;
+  ET ra[AQ];
+  ET rb[BR][EV];
+  auto load = [&](int kt) {
+    const int k0 = kt * KS;
+#pragma unroll
+    for (int h = 0; h < AQ / EV; ++h) {
+      const int kk = k0 + ak + h * EV;
+      if (VEC && kk + EV <= K) {
+        const u32x4 v = *(const u32x4*)(arow + kk);
+        const ET* e = reinterpret_cast<const ET*>(&v);
+#pragma unroll
+        for (int i = 0; i < EV; ++i) ra[h * EV + i] = e[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < EV; ++i) ra[h * EV + i] = kk + i < K ? arow[kk + i] : (ET)0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < BR; ++r) {
+      const int idx = tid + r * kYThreads;
+      const int k = idx / (kYN / EV), n = (idx % (kYN / EV)) * EV;
+      const int kk = k0 + k, nn = n0 + n;
+      const ET* src = wg + (long)min(kk, K - 1) * N + nn;
+      if (VEC && kk < K && nn + EV <= N) {
+        const u32x4 v = *(const u32x4*)src;
+        const ET* e = reinterpret_cast<const ET*>(&v);
+#pragma unroll
+        for (int i = 0; i < EV; ++i) rb[r][i] = e[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < EV; ++i) rb[r][i] = (kk < K && nn + i < N) ? src[i] : (ET)0.f;
+      }
+    }
+  };
+  auto store = [&](int buf) {
+    ET* a = sa[buf] + (tid >> 2) * AST + ak;
+#pragma unroll
+    for (int i = 0; i < AQ; ++i) a[i] = ra[i];
+#pragma unroll
+    for (int r = 0; r < BR; ++r) {
+      const int idx = tid + r * kYThreads;
+      const int k = idx / (kYN / EV), n = (idx % (kYN / EV)) * EV;
+#pragma unroll
+      for (int i = 0; i < EV; ++i) {
+        if constexpr (WIDE) sb[buf][k * BST + n + i] = rb[r][i];
+        else sb[buf][(n + i) * BST + k] = rb[r][i];
+      }
+    }
+  };
+
+  typename T::Acc acc[2][4];
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = typename T::Acc{};
+
+  const int nk = (K + KS - 1) / KS;
+  if (nk > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+    const ET* a = sa[buf];
+    const ET* b = sb[buf];
+    if constexpr (WIDE) {
+#pragma unroll
+      for (int k4 = 0; k4 < KS / 4; ++k4) {
+        // lane holds A[row col][k kq] and B[k kq][column col]
+        double av[2], bv[4];
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) av[ms] = a[(wm * 32 + ms * 16 + col) * AST + k4 * 4 + kq];
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) bv[ns] = b[(k4 * 4 + kq) * BST + wn * 64 + ns * 16 + col];
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+          for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = T::mma(av[ms], bv[ns], acc[ms][ns]);
+      }
+    } else {
+      // lane holds A[row col][k 8kq .. 8kq + 7] and B[k 8kq .. 8kq + 7][column col]
+      typename T::Frag af[2], bf[4];
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) af[ms] = *(const typename T::Frag*)(a + (wm * 32 + ms * 16 + col) * AST + 8 * kq);
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) bf[ns] = *(const typename T::Frag*)(b + (wn * 64 + ns * 16 + col) * BST + 8 * kq);
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = T::mma(af[ms], bf[ns], acc[ms][ns]);
+    }
+    if (kt + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // acc[ms][ns][i]: column wn*64 + ns*16 + col of row wm*32 + ms*16 +
+  // 4*kq + i (16-bit types, f32 accumulators) or of row wm*32 + ms*16 + kq +
+  // 4*i (double: the fp64 instruction leaves row kq + 4i of its 16 x 16 block
+  // in register i of lane 16*kq + col)
+  const ET* bias = static_cast<const ET*>(g.bias);
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    const int n = n0 + wn * 64 + ns * 16 + col;
+    if (n >= N) continue;
+    const typename T::AccT bv = bias ? (typename T::AccT)bias[(long)grp * N + n] : (typename T::AccT)0;
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 32 + ms * 16 + (WIDE ? kq + 4 * i : 4 * kq + i);
+        if (r < rows) out[(long)s_orow[r] * N + n] = (ET)(acc[ms][ns][i] + bv);
+      }
+  }
+}
+
+hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tiles, hipStream_t st) {
+  if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  const int nblk = (g.N + kYN - 1) / kYN;
+  const dim3 grid((unsigned)((long)max_tiles * nblk)), block(kYThreads);
+#define QMOE_TYPED(ET)                                                                       \
+  do {                                                                                       \
+    if (vec) hipLaunchKernelGGL((qmoe_gmm_typed<ET, true>), grid, block, 0, st, g, nblk);   \
+    else hipLaunchKernelGGL((qmoe_gmm_typed<ET, false>), grid, block, 0, st, g, nblk);      \
+  } while (0)
+  switch (type) {
+    case GMM_F16: QMOE_TYPED(_Float16); break;
+    case GMM_BF16: QMOE_TYPED(__bf16); break;
+    case GMM_F64: QMOE_TYPED(double); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef QMOE_TYPED
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -135,6 +135,26 @@ int gmm_rows16_tile_rows();
 int gmm_rows16_ksplit(long est_tiles, int N);
 hipError_t launch_gmm_rows16(const F32Gemm& g, bool nk, int ksplit, int max_tiles, hipStream_t st);
 
+// GroupedMatMul in float16, bfloat16 and double (see gmm_typed.hip): the
+// rows of F32Gemm's GroupedMatMul use (a_perm / a_div gathers token rows,
+// output rows by slot id through perm), weights [G][K][N] of the element
+// type, optional bias [G][N]; 64-row tiles (gmm_tile_rows()).  vec: x and w
+// 16-byte aligned and rows of K and N elements whole 16-byte runs.
+enum { GMM_F16 = 0, GMM_BF16 = 1, GMM_F64 = 2 };
+struct TypedGemm {
+  const void* a;
+  const int* a_perm;
+  int a_div;
+  const void* w;
+  const void* bias;     // or nullptr
+  const int* perm;
+  const int* tiles;
+  const int* ntiles;
+  int K, N, G;          // tiles of group >= G write zero rows
+  void* out;
+};
+hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tiles, hipStream_t st);
+
 // Float MoE activation pass (see moe.hip): act[p][j], p < S, j < I, from
 // FC1 rows h (F floats) and FC3 rows u3 (I floats, or nullptr).  Codes
 // match qmoe_activation.

@@ -27,6 +27,7 @@ struct GmmPlan {
   int64_t M = 0, K = 0, G = 0, N = 0, S = 0, R = 0;  // R = M * S rows
   int64_t bm = 0, max_tiles = 0, nchunks = 0, nblk = 0;
   bool idx64 = false, has_bias = false;
+  int32_t dtype = QMOE_F32;  // T of the Type Constraints
   bool rows16 = false;  // groups average at most 16 rows: 16-row tiles, weight-streaming kernel
   size_t off_idx = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_tiles = 0, off_ntiles = 0, off_hist = 0;
   size_t bytes = 0;
@@ -59,7 +60,7 @@ qmoe_status check(const qmoe_tensor* input, const qmoe_tensor* weights, const qm
   if (bias && (bias->dims[0] != p->G || bias->dims[1] != p->N)) return QMOE_ERR_SHAPE;
   if (output && (output->dims[0] != p->M || output->dims[1] != p->S || output->dims[2] != p->N))
     return QMOE_ERR_SHAPE;
-  if (T != QMOE_F32) return QMOE_ERR_UNSUPPORTED;
+  p->dtype = T;
   const int64_t lim30 = int64_t(1) << 30;
   if (p->M > lim30 || p->S > lim30) return QMOE_ERR_UNSUPPORTED;
   p->R = p->M * p->S;
@@ -70,7 +71,8 @@ qmoe_status check(const qmoe_tensor* input, const qmoe_tensor* weights, const qm
   // LDS-tiled 64-row tiles.  With misaligned pointers the tiled kernel also
   // runs the 16-row tiles.
   const int64_t spread = std::max<int64_t>(1, std::min(p->G, p->R));
-  p->rows16 = p->K % 4 == 0 && p->N % 4 == 0 && p->R <= 16 * spread;
+  // (float32 only; the other types take the 64-row tiles of gmm_typed.hip)
+  p->rows16 = T == QMOE_F32 && p->K % 4 == 0 && p->N % 4 == 0 && p->R <= 16 * spread;
   p->bm = p->rows16 ? gmm_rows16_tile_rows() : gmm_tile_rows();
   p->has_bias = bias != nullptr;
   p->max_tiles = (p->R + p->bm - 1) / p->bm + p->G + 1;
@@ -128,8 +130,9 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
   const qmoe_tensor* all[] = {input, weights, group_indices, bias, output};
   for (const qmoe_tensor* t : all)
     if (t && numel(t) > 0 && t->data == nullptr) return QMOE_ERR_NULL;
+  const uintptr_t es = p.dtype == QMOE_F64 ? 8 : p.dtype == QMOE_F32 ? 4 : 2;  // element size
   for (const qmoe_tensor* t : {input, weights, bias, output})
-    if (t && !aligned_to(t->data, 4)) return QMOE_ERR_ALIGN;
+    if (t && !aligned_to(t->data, es)) return QMOE_ERR_ALIGN;
   if (!aligned_to(group_indices->data, p.idx64 ? 8 : 4)) return QMOE_ERR_ALIGN;
   if (workspace == nullptr) return QMOE_ERR_NULL;
   if (workspace_bytes < p.bytes) return QMOE_ERR_WORKSPACE;
@@ -155,6 +158,27 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
                      ntiles, s) != hipSuccess)
     return QMOE_ERR_HIP;
   if (mark(1) != hipSuccess) return QMOE_ERR_HIP;
+  if (p.dtype != QMOE_F32) {
+    TypedGemm tg{};
+    tg.a = input->data;
+    tg.a_perm = perm;  // slot id m * S + i -> token row m
+    tg.a_div = (int)p.S;
+    tg.w = weights->data;
+    tg.bias = bias ? bias->data : nullptr;
+    tg.perm = perm;    // output row m * S + i of [M, S, N]
+    tg.tiles = tiles;
+    tg.ntiles = ntiles;
+    tg.K = (int)p.K;
+    tg.N = (int)p.N;
+    tg.G = G;
+    tg.out = const_cast<void*>(output->data);
+    const bool tvec = (p.K * (int64_t)es) % 16 == 0 && (p.N * (int64_t)es) % 16 == 0 &&
+                      aligned_to(input->data, 16) && aligned_to(weights->data, 16);
+    const int ty = p.dtype == QMOE_F16 ? GMM_F16 : p.dtype == QMOE_BF16 ? GMM_BF16 : GMM_F64;
+    if (launch_gmm_typed(ty, tg, tvec, (int)p.max_tiles, s) != hipSuccess) return QMOE_ERR_HIP;
+    if (mark(2) != hipSuccess) return QMOE_ERR_HIP;
+    return QMOE_OK;
+  }
   const bool vec = p.K % 4 == 0 && p.N % 4 == 0 && aligned_to(input->data, 16) && aligned_to(weights->data, 16);
   const bool stream16 = p.rows16 && vec && aligned_to(output->data, 16) && (!bias || aligned_to(bias->data, 16));
   F32Gemm g{};

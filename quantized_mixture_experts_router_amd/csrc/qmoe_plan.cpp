@@ -49,6 +49,24 @@ int64_t max_one_splits() {
 
 bool rank_ok(const qmoe_tensor* t, int r) { return t->rank == r; }
 
+// Extents the kernels index with 32-bit integers, and the largest element
+// count of any intermediate (2^40 four-byte elements, beyond any GPU's
+// memory): past these a call is UNSUPPORTED, never computed with wrapped
+// sizes.
+constexpr int64_t kMaxExtent = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxElements = int64_t(1) << 40;
+
+// Rank 1..3 with every used extent in [0, kMaxExtent]: QMOE_OK, or SHAPE
+// (bad rank, negative extent) or UNSUPPORTED (an extent past kMaxExtent).
+qmoe_status extents_ok(const qmoe_tensor* t) {
+  if (t->rank < 1 || t->rank > 3) return QMOE_ERR_SHAPE;
+  for (int i = 0; i < t->rank; ++i) {
+    if (t->dims[i] < 0) return QMOE_ERR_SHAPE;
+    if (t->dims[i] > kMaxExtent) return QMOE_ERR_UNSUPPORTED;
+  }
+  return QMOE_OK;
+}
+
 // GEMM path override, for measuring the paths against each other: the
 // environment variable QMOE_PATH = "stream" (weight streaming, 64-row tiles
 // past 64 tokens), "tiled" (LDS-tiled where the shapes allow, else
@@ -102,12 +120,16 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
 
   // inputOutputShapeOk
   if (input->rank != 2 && input->rank != 3) return QMOE_ERR_SHAPE;
-  for (int i = 0; i < input->rank; ++i)
-    if (input->dims[i] < 0) return QMOE_ERR_SHAPE;
+  for (const qmoe_tensor* t : {input, router, fc1w, fc1s, fc2w, fc2s, output}) {
+    if (!t) continue;
+    const qmoe_status st = extents_ok(t);
+    if (st != QMOE_OK) return st;
+  }
   const int64_t H = input->dims[input->rank - 1];
   if (H <= 0) return QMOE_ERR_SHAPE;
-  int64_t T = 1;
+  int64_t T = 1;  // each factor < 2^31: the product of two fits int64
   for (int i = 0; i < input->rank - 1; ++i) T *= input->dims[i];
+  if (T > kMaxExtent) return QMOE_ERR_UNSUPPORTED;
   if (output) {
     if (output->rank != input->rank) return QMOE_ERR_SHAPE;
     for (int i = 0; i < input->rank; ++i)
@@ -130,7 +152,8 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
   if (F < 0 || F % fusion != 0) return QMOE_ERR_SHAPE;
   const int64_t I = F / fusion;
   if (fc2w->dims[1] != H) return QMOE_ERR_SHAPE;
-  if (fc1w->dims[2] * pack != H || fc2w->dims[2] * pack != I) return QMOE_ERR_SHAPE;
+  if (H % pack != 0 || I % pack != 0 || fc1w->dims[2] != H / pack || fc2w->dims[2] != I / pack)
+    return QMOE_ERR_SHAPE;
   // quantBlockSizeOk, shape part
   if (bs != 0 && (H % bs != 0 || I % bs != 0)) return QMOE_ERR_SHAPE;
   // quantScalesOk
@@ -145,6 +168,10 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
   }
   // quantContract: 1 <= k <= num_experts
   if (a->k < 1 || a->k > E) return QMOE_ERR_ATTR;
+  // slot count and intermediates within the kernels' index ranges
+  if (T * a->k > kMaxExtent) return QMOE_ERR_UNSUPPORTED;
+  if (T * H > kMaxElements || T * a->k * (F + 128) > kMaxElements || T * a->k * H > kMaxElements)
+    return QMOE_ERR_UNSUPPORTED;
   // The routing kernels hold one row of logits per wavefront in registers.
   if (E > kMaxExperts) return QMOE_ERR_UNSUPPORTED;
 
@@ -167,9 +194,9 @@ void make_plan(const Dims& d, Plan* p) {
   p->share = d.El < d.E;
   // Every expert receives at most T rows (a token selects distinct experts),
   // so up to 64 tokens one M tile of ceil(T/16)*16 rows holds any expert's
-  // rows and the weights stream from HBM exactly once.  Past that (forced by
-  // QMOE_PATH) an expert's rows take several 64-row tiles, each streaming the
-  // weights again.
+  // rows and the weights stream from HBM exactly once.  Past that (up to
+  // kStreamMaxTokens, or any count forced by QMOE_PATH) an expert's rows may
+  // take several 64-row tiles, each streaming the weights again.
   const int force = path_override();
   p->decode = force == PATH_STREAM || (force == PATH_AUTO && d.T <= kStreamMaxTokens);
   p->mt = p->decode ? int(std::min<int64_t>((d.T + 15) / 16, 4)) : 4;

@@ -199,8 +199,10 @@ def test_grouped_matmul_contract(lib):
     assert _gmm_status(**_gmm(it=np.float32)) == 7
     assert _gmm_status(**dict(a, weights=a["weights"].astype(np.float64))) == 7
     assert _gmm_status(**_gmm(dt=np.uint8)) == 7
-    for dt in (np.float16, np.float64):  # in the type list, not implemented
-        assert _gmm_status(**_gmm(dt=dt)) == 4
+    for dt in (np.float16, np.float64):  # the page's other types: accepted
+        assert _gmm_status(**_gmm(dt=dt)) == 0
+        b = _gmm(dt=dt)
+        assert _gmm_status(**dict(b, bias=b["bias"].astype(np.float32))) == 7   # one T for all four
     # group count limit of the permutation (G + 1 buckets <= 1024)
     assert _gmm_status(**_gmm(G=1023)) == 0
     assert _gmm_status(**_gmm(G=1024)) == 4

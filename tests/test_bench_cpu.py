@@ -89,7 +89,11 @@ def test_kernel_choice_per_workload():
 def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
     src = tmp_path / "kernel.hip"
     src.write_text("// kernel source\n")
-    rec = {"decode:fc1": {"kernel": "qmoe_stream", "source_sha": bench._sha(str(src)), "bytes": 123}}
+    plan = tmp_path / "plan.cpp"
+    plan.write_text("// planner\n")
+    monkeypatch.setattr(bench, "PLAN_SRC", str(plan))
+    rec = {"decode:fc1": {"kernel": "qmoe_stream", "source_sha": bench._sha(str(src)),
+                          "plan_sha": bench._sha(str(plan)), "bytes": 123}}
     tf = tmp_path / "traffic.json"
     tf.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
@@ -97,5 +101,8 @@ def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
     assert bench.traffic_for("decode:fc1", "qmoe_stream") == 123
     assert bench.traffic_for("decode:fc2", "qmoe_stream") is None      # never measured
     assert bench.traffic_for("decode:fc1", "qmoe_tiled") is None       # another kernel
+    plan.write_text("// planner, changed split rule\n")
+    assert bench.traffic_for("decode:fc1", "qmoe_stream") is None      # planner changed since
+    plan.write_text("// planner\n")
     src.write_text("// kernel source, changed\n")
     assert bench.traffic_for("decode:fc1", "qmoe_stream") is None      # source changed since

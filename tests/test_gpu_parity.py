@@ -108,7 +108,7 @@ def test_route_ties_through_gpu(torch):
 
 
 # Small sweeps: every element.  (T, H, E, I, k) chosen to cover one and several
-# M subtiles on the weight-streaming path (T <= 64), the LDS-tiled path (T > 64,
+# M subtiles on the weight-streaming path (T <= 96), the LDS-tiled path (T > 96,
 # H and I multiples of 64) and the register-tiled path (other shapes), ragged
 # tails in every dimension, unused experts and k = E.
 SHAPES = [
@@ -116,6 +116,10 @@ SHAPES = [
     (33, 128, 6, 64, 6), (64, 192, 8, 128, 2), (70, 128, 5, 96, 2), (200, 64, 16, 64, 4),
     (300, 256, 1, 32, 1), (24, 512, 8, 256, 3), (40, 256, 4, 256, 2), (60, 256, 4, 128, 2),
     (130, 128, 3, 192, 2), (257, 320, 4, 128, 3),
+    # either side of the streaming / tiled switch (96 tokens): 64-row
+    # streaming tiles with experts holding more than one tile, then 128-row
+    # LDS tiles
+    (96, 256, 2, 128, 2), (97, 256, 2, 128, 2), (90, 512, 8, 256, 3),
 ]
 
 
@@ -339,7 +343,7 @@ def test_double_buffered_streaming(torch):
 @pytest.mark.parametrize("tokens,bits,bs", [(16, 4, 64), (16, 8, 0), (200, 4, 32), (130, 8, 16)],
                          ids=["stream-int4", "stream-int8", "tiled-int4", "gemm-int8"])
 def test_swiglu_limit(torch, tokens, bits, bs):
-    # the clamp reading on every FC1 path: weight streaming (<= 64 tokens),
+    # the clamp reading on every FC1 path: weight streaming (<= 96 tokens),
     # LDS-tiled, register-tiled (16-code blocks); limits that clamp a large
     # share of the FC1 values, and one above all of them
     rng = np.random.default_rng(40 + tokens + bits)
