@@ -223,6 +223,28 @@ qmoe_status qmoe_forward_debug(const qmoe_tensor* input, const qmoe_tensor* rout
                                void* workspace, size_t workspace_bytes, void* stream,
                                const qmoe_debug* debug);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): qmoe_forward without a
+ * workspace argument.  Its intermediates live in a scratch array inside the
+ * library, one per GPU (qmoe_noalloc_scratch_bytes() bytes, 32 MiB: enough
+ * for up to about 16 decode tokens of an 8-expert hidden-4096 /
+ * inter-14336 layer), held from the first call on a GPU until the process
+ * ends.  Calls whose qmoe_workspace_size exceeds it return
+ * QMOE_ERR_WORKSPACE before anything is enqueued; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ * The stream must belong to the current HIP device (whose array is used);
+ * the first call on a device looks the array's address up (a host-side
+ * query, QMOE_ERR_HIP if it fails), so make one call outside graph capture
+ * first.  Every call on a GPU shares that GPU's array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that
+ * overlap on one GPU (other streams, or host threads) race and must be
+ * ordered by the caller.  Otherwise as qmoe_forward. */
+size_t qmoe_noalloc_scratch_bytes(void);
+qmoe_status qmoe_forward_noalloc(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                                 const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_scales,
+                                 const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_scales,
+                                 const qmoe_attrs* attrs, const qmoe_tensor* output, void* stream);
+
 /* ------------------------------------------------------------------------
  * GroupedMatMul (ONNX operator page "GroupedMatMul - 29": Summary, Inputs,
  * Outputs, Type Constraints), in each floating type T of the page's list:

@@ -5,7 +5,8 @@ kernels behind the C ABI of include/qmoe.h.  PyTorch supplies device memory
 and the current stream.  The functions keep the C names:
 
     qmoe_abi_version, qmoe_attrs_default, qmoe_validate, qmoe_workspace_size,
-    qmoe_forward, qmoe_forward_debug, qmoe_status_string,
+    qmoe_forward, qmoe_forward_debug, qmoe_forward_noalloc,
+    qmoe_noalloc_scratch_bytes, qmoe_status_string,
     qmoe_grouped_matmul_workspace_size, qmoe_grouped_matmul,
     qmoe_grouped_matmul_debug, qmoe_moe_attrs_default, qmoe_moe_validate,
     qmoe_moe_workspace_size, qmoe_moe_forward, qmoe_moe_forward_debug
@@ -96,6 +97,10 @@ def _lib():
         lib.qmoe_forward_debug.argtypes = [T, T, T, T, T, T, A, T, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p, ctypes.POINTER(QmoeDebug)]
         lib.qmoe_forward_debug.restype = ctypes.c_int
+        lib.qmoe_noalloc_scratch_bytes.argtypes = []
+        lib.qmoe_noalloc_scratch_bytes.restype = ctypes.c_size_t
+        lib.qmoe_forward_noalloc.argtypes = [T, T, T, T, T, T, A, T, ctypes.c_void_p]
+        lib.qmoe_forward_noalloc.restype = ctypes.c_int
         lib.qmoe_grouped_matmul_workspace_size.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_size_t)]
         lib.qmoe_grouped_matmul_workspace_size.restype = ctypes.c_int
         lib.qmoe_grouped_matmul.argtypes = [T, T, T, T, T, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -245,6 +250,23 @@ def qmoe_forward(input, router_probs, fc1_w, fc1_s, fc2_w, fc2_s, attrs, output,
 
 
 qmoe_forward_debug = qmoe_forward
+
+
+def qmoe_noalloc_scratch_bytes() -> int:
+    """Size of the library's per-GPU scratch array used by qmoe_forward_noalloc."""
+    return int(_lib().qmoe_noalloc_scratch_bytes())
+
+
+def qmoe_forward_noalloc(input, router_probs, fc1_w, fc1_s, fc2_w, fc2_s, attrs, output, stream=None) -> None:
+    """qmoe_forward without a workspace: the library's per-GPU scratch array
+    holds the intermediates (calls on one GPU must not overlap)."""
+    ts = _six(input, router_probs, fc1_w, fc1_s, fc2_w, fc2_s)
+    o = describe(output)
+    a = attrs if isinstance(attrs, QmoeAttrs) else make_attrs(attrs)
+    st = _lib().qmoe_forward_noalloc(*[ctypes.byref(t) for t in ts], ctypes.byref(a), ctypes.byref(o),
+                                     _stream_handle(stream))
+    if st != 0:
+        raise QmoeError(st, "qmoe_forward_noalloc")
 
 
 def forward(input, router_probs, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None, stream=None, workspace=None,

@@ -7,6 +7,8 @@
 // never synchronises.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels/launch.h"
 #include "qmoe.h"
 #include "qmoe_plan.h"
@@ -222,11 +224,58 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
   return QMOE_OK;
 }
 
+// Scratch of qmoe_forward_noalloc: one array per GPU, held until the process
+// ends.  In host code its name is a host-side stand-in; the device address
+// of each GPU's copy comes from hipGetSymbolAddress (kept per device).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up once per
+// device, with that device current), or nullptr if the lookup fails.
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t qmoe_abi_version(void) { return QMOE_ABI_VERSION; }
+
+size_t qmoe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+qmoe_status qmoe_forward_noalloc(const qmoe_tensor* input, const qmoe_tensor* router_probs, const qmoe_tensor* fc1w,
+                                 const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
+                                 const qmoe_attrs* attrs, const qmoe_tensor* output, void* stream) {
+  if (!output) return QMOE_ERR_NULL;
+  // the same contract and plan as qmoe_forward; sizes whose workspace
+  // exceeds the scratch array are refused before anything is enqueued
+  Dims d;
+  const qmoe_status st = validate(input, router_probs, fc1w, fc1s, fc2w, fc2s, output, attrs, &d);
+  if (st != QMOE_OK) return st;
+  Plan p;
+  make_plan(d, &p);
+  if (p.bytes > kScratchBytes) return QMOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (p.bytes > 0) {
+    ws = scratch_of_current_device();
+    if (!ws) return QMOE_ERR_HIP;
+  }
+  return forward_impl(input, router_probs, fc1w, fc1s, fc2w, fc2s, attrs, output, ws, kScratchBytes, stream,
+                      nullptr);
+}
 
 void qmoe_attrs_default(qmoe_attrs* a) {
   if (!a) return;
