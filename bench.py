@@ -67,6 +67,10 @@ def _args():
     ap.add_argument("--crossover", default="", metavar="T1,T2,...",
                     help="time the weight-streaming and the tiled GEMM paths (QMOE_PATH) on the decode layer's "
                          "experts at these token counts; one JSON line")
+    ap.add_argument("--layer", default="decode", choices=["decode", "fine", "large_e", "decode_tp8"],
+                    help="with --crossover: whose experts and routing recipe (the first T tokens of it)")
+    ap.add_argument("--tile-rows", action="store_true",
+                    help="with --crossover: also the streaming path with 32-, 48- and 64-row tiles")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -191,38 +195,28 @@ def gmm_kernel(w):
     return "qmoe_gmm_f32_rows16" if rows16 else "qmoe_gmm_f32"
 
 
-def stream_fits(w, K):
-    """Whether the planner streams a GEMM of reduction length K at this
-    workload's token count: whole stages of 128-byte row items (one stage of
-    4, 2 or 1 items at 16, 32 or 48-64 rows per tile, at most 16 K ranges;
-    else stages of 2 items at 16 rows, 1 above), and 32-code scale blocks
-    4 to 16 to a stage."""
-    mt = min((w.tokens + 15) // 16, 4)
-    item = 256 if w.bits == 4 else 128
-    bs = w.block_size
+def plan_of(w):
+    """The library's launch plan for a workload (qmoe_plan_describe: host
+    code, only the shapes are read)."""
+    import numpy as np
 
-    def fits(codes):
-        if not (K > 0 and K % codes == 0 and (bs == 0 or bs >= 32)):
-            return False
-        if 0 < bs < item // 2:
-            return (codes // bs) % 4 == 0 and codes // bs <= 16
-        return True
-    one = {1: 4, 2: 2}.get(mt, 1) * item
-    if fits(one) and K // one <= 16:
-        return True
-    return fits((2 if mt == 1 else 1) * item)
+    import quantized_mixture_experts_router_amd as qm
+    from quantized_mixture_experts_router_amd import workloads as W
+
+    s = W.shapes(w)
+    names = ("input", "router_probs", "fc1_experts_weights", "fc1_scales", "fc2_experts_weights", "fc2_scales")
+    arrs = []
+    for n in names:
+        dt = np.uint8 if n.endswith("weights") else np.float32
+        arrs.append(np.lib.stride_tricks.as_strided(np.zeros(1, dtype=dt), shape=s[n], strides=(0,) * len(s[n])))
+    return qm.qmoe_plan_describe(*arrs, w.attrs())
 
 
-def gemm_kernel(w, which="fc1"):
-    """Which grouped-GEMM kernel the library runs for one GEMM of this
-    workload (the library's plan: weight streaming up to 96 tokens when the
-    reduction length fits its stages, the LDS-tiled GEMM above 96 tokens for
-    64-multiple H and I with column-wise or >= 32-code scale blocks, else the
-    register-tiled one)."""
-    if w.tokens <= 96:
-        return "qmoe_stream" if stream_fits(w, w.hidden if which == "fc1" else w.inter) else "qmoe_gemm"
-    tiled = w.hidden % 64 == 0 and w.inter % 64 == 0 and (w.block_size == 0 or w.block_size >= 32)
-    return "qmoe_tiled" if tiled else "qmoe_gemm"
+def gemm_kernel(w, which="fc1", plan=None):
+    """Kernel the library runs for one GEMM of this workload, read from its
+    launch plan (fc1= / fc2= stream, tiled or gemm)."""
+    fields = dict(kv.split("=", 1) for kv in (plan or plan_of(w)).split())
+    return "qmoe_" + fields[which]
 
 
 def call_latency(step, n, evict=None):
@@ -246,13 +240,11 @@ def call_latency(step, n, evict=None):
     return dict(median=round(float(q[0]), 5), p10=round(float(q[1]), 5), p90=round(float(q[2]), 5), calls=n)
 
 
-PLAN_SRC = os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "qmoe_plan.cpp")
-
-
-def traffic_for(key, kernel):
+def traffic_for(key, kernel, plan=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the kernel source and the launch planner (which sets the
-    K-range splits and tile shapes) now in the tree; otherwise None."""
+    was taken on the kernel source now in the tree and (for the QMoE GEMMs)
+    under the launch plan the library now takes for the workload (K-range
+    splits, tile shapes); otherwise None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -261,7 +253,7 @@ def traffic_for(key, kernel):
     ent = rec.get(key)
     if not ent or ent.get("kernel") != kernel:
         return None
-    if ent.get("source_sha") != _sha(KERNEL_SRC[kernel]) or ent.get("plan_sha") != _sha(PLAN_SRC):
+    if ent.get("source_sha") != _sha(KERNEL_SRC[kernel]) or ent.get("plan") != plan:
         return None
     return ent.get("bytes")
 
@@ -607,12 +599,14 @@ def measure_qmoe(w, steps, warmup, settle_ms, args, arrs=None):
         key = "fc1" if stages["fc1"] >= stages["fc2"] else "fc2"
         work = fc1_work if key == "fc1" else fc2_work
         roofline = roofline_for(work, stages[key])
-        kernel = gemm_kernel(w, key)
+        plan = qm.qmoe_plan_describe(*ins, attrs)
+        kernel = gemm_kernel(w, key, plan)
         roofline["kernel"] = f"{kernel} ({key.upper()})"
         roofline["avg_ms"] = round(stages[key], 5)
         roofline["algorithmic_bytes"] = int(work["bytes"])
         roofline["algorithmic_flops"] = work["flops"]
-        roofline["traffic"] = traffic_for(f"{w.name}:{key}", kernel)
+        roofline["traffic"] = traffic_for(f"{w.name}:{key}", kernel, plan)
+        roofline["plan"] = plan
 
     # Per-call latency outside the throughput loop: warm (operands may sit in
     # L2 / the Infinity Cache from the previous call) and cold (a 1 GiB
@@ -652,10 +646,10 @@ def measure_qmoe(w, steps, warmup, settle_ms, args, arrs=None):
 
 
 def main_crossover(args):
-    """Per-step time of the decode layer's experts (8 x int4, hidden 4096,
-    inter 14336, k = 2, block size 64) at several token counts, with the
-    GEMMs forced onto each path (QMOE_PATH = stream | tiled) and with the
-    plan's own choice."""
+    """Per-step time of one layer's experts (--layer: the decode layer's by
+    default) at several token counts (the first T rows of that layer's
+    recipe), with the GEMMs forced onto each path (QMOE_PATH = stream |
+    tiled) and with the plan's own choice."""
     import dataclasses
 
     import numpy as np
@@ -665,7 +659,7 @@ def main_crossover(args):
     from quantized_mixture_experts_router_amd import workloads as W
 
     toks = [int(t) for t in args.crossover.split(",") if t]
-    base = W.WORKLOADS["decode"]
+    base = W.WORKLOADS[args.layer]
     w = dataclasses.replace(base, name="crossover", input_shape=(max(toks), base.hidden))
     a = W.generate(w)
     torch.cuda.set_device(0)
@@ -673,16 +667,19 @@ def main_crossover(args):
     attrs = qm.make_attrs(w.attrs())
     stream = torch.cuda.current_stream()
     rows = []
+    variants = [("stream", {"QMOE_PATH": "stream"}), ("tiled", {"QMOE_PATH": "tiled"}), ("auto", {})]
+    if args.tile_rows:
+        variants += [(f"stream{r}", {"QMOE_PATH": "stream", "QMOE_STREAM_TILE_ROWS": str(r)})
+                     for r in (32, 48, 64)]
     for T in toks:
         ins = [d["input"][:T], d["router_probs"][:T], d["fc1_experts_weights"], d["fc1_scales"],
                d["fc2_experts_weights"], d["fc2_scales"]]
         out = torch.empty_like(ins[0])
         row = {"tokens": T}
-        for path in ("stream", "tiled", "auto"):
-            if path == "auto":
-                os.environ.pop("QMOE_PATH", None)
-            else:
-                os.environ["QMOE_PATH"] = path
+        for path, env in variants:
+            for key in ("QMOE_PATH", "QMOE_STREAM_TILE_ROWS"):
+                os.environ.pop(key, None)
+            os.environ.update(env)
             ws = torch.empty(max(qm.qmoe_workspace_size(*ins, attrs), 1), dtype=torch.uint8, device="cuda")
 
             def step():
@@ -698,10 +695,13 @@ def main_crossover(args):
             torch.cuda.synchronize()
             row[f"{path}_ms"] = round((time.perf_counter() - t0) * 1e3 / args.steps, 5)
             del ws
-        os.environ.pop("QMOE_PATH", None)
+        for key in ("QMOE_PATH", "QMOE_STREAM_TILE_ROWS"):
+            os.environ.pop(key, None)
         print(json.dumps(row), file=sys.stderr, flush=True)
         rows.append(row)
-    print(json.dumps({"crossover": rows, "layer": "decode experts (E 8, H 4096, I 14336, k 2, int4, bs 64)",
+    print(json.dumps({"crossover": rows, "layer": f"{base.name} experts (E {base.experts}, H {base.hidden}, "
+                      f"I {base.inter}, k {base.k}, int{base.bits}, bs {base.block_size}, "
+                      f"{'Zipf' if base.zipf_bias else 'N(0,1)'} logits)",
                       "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 

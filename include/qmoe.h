@@ -202,6 +202,20 @@ qmoe_status qmoe_workspace_size(const qmoe_tensor* input, const qmoe_tensor* rou
                                 const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_scales,
                                 const qmoe_attrs* attrs, size_t* bytes);
 
+/* The launch plan qmoe_forward takes for these shapes and attributes, as one
+ * line of text (validates first; pure host code): the kernel of each GEMM
+ * (fc1=, fc2= stream | tiled | gemm | none), the routing front end, the
+ * M-tile height and count, whether the weights hold a share of the experts,
+ * the streaming split of each GEMM (single-stage:items per stage:stages per
+ * K range:K ranges:rows per workgroup) and the workspace bytes.  The plan
+ * depends on the environment as qmoe_workspace_size says.  At most len
+ * bytes are written to buf, NUL-terminated; NULL buf or len 0 is
+ * QMOE_ERR_NULL. */
+qmoe_status qmoe_plan_describe(const qmoe_tensor* input, const qmoe_tensor* router_probs,
+                               const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_scales,
+                               const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_scales,
+                               const qmoe_attrs* attrs, char* buf, size_t len);
+
 /* Enqueue the whole operator on stream (a hipStream_t; NULL = the null
  * stream).  Device pointers: router_probs 4-byte aligned; input, weights,
  * scales and output 16-byte aligned (QMOE_ERR_ALIGN otherwise).

@@ -5,7 +5,7 @@ kernels behind the C ABI of include/qmoe.h.  PyTorch supplies device memory
 and the current stream.  The functions keep the C names:
 
     qmoe_abi_version, qmoe_attrs_default, qmoe_validate, qmoe_workspace_size,
-    qmoe_forward, qmoe_forward_debug, qmoe_forward_noalloc,
+    qmoe_plan_describe, qmoe_forward, qmoe_forward_debug, qmoe_forward_noalloc,
     qmoe_noalloc_scratch_bytes, qmoe_status_string,
     qmoe_grouped_matmul_workspace_size, qmoe_grouped_matmul,
     qmoe_grouped_matmul_debug, qmoe_moe_attrs_default, qmoe_moe_validate,
@@ -97,6 +97,8 @@ def _lib():
         lib.qmoe_forward_debug.argtypes = [T, T, T, T, T, T, A, T, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p, ctypes.POINTER(QmoeDebug)]
         lib.qmoe_forward_debug.restype = ctypes.c_int
+        lib.qmoe_plan_describe.argtypes = [T, T, T, T, T, T, A, ctypes.c_char_p, ctypes.c_size_t]
+        lib.qmoe_plan_describe.restype = ctypes.c_int
         lib.qmoe_noalloc_scratch_bytes.argtypes = []
         lib.qmoe_noalloc_scratch_bytes.restype = ctypes.c_size_t
         lib.qmoe_forward_noalloc.argtypes = [T, T, T, T, T, T, A, T, ctypes.c_void_p]
@@ -207,6 +209,18 @@ def qmoe_workspace_size(input, router_probs, fc1_w, fc1_s, fc2_w, fc2_s, attrs=N
     if st != 0:
         raise QmoeError(st, "qmoe_workspace_size")
     return int(n.value)
+
+
+def qmoe_plan_describe(input, router_probs, fc1_w, fc1_s, fc2_w, fc2_s, attrs=None) -> str:
+    """The launch plan of qmoe_forward for these shapes, as one line of text.
+    Arrays may live anywhere (only shapes and dtypes are read)."""
+    ts = _six(input, router_probs, fc1_w, fc1_s, fc2_w, fc2_s, data=False)
+    a = attrs if isinstance(attrs, QmoeAttrs) else make_attrs(attrs)
+    buf = ctypes.create_string_buffer(512)
+    st = _lib().qmoe_plan_describe(*[ctypes.byref(t) for t in ts], ctypes.byref(a), buf, 512)
+    if st != 0:
+        raise QmoeError(st, "qmoe_plan_describe")
+    return buf.value.decode()
 
 
 def _stream_handle(stream):

@@ -33,8 +33,9 @@ hipError_t launch_tile_rows(const int* perm, const int* tiles, const int* ntiles
 // Operand rows of the f16 GEMMs (see operand.hip): rows of n fp32 codes at
 // src + r * sstride (floats) -> kp hi/lo codes of v * 2^e at dst + r * dstride
 // (bytes), exps[r] = e; src and dst may be the same rows of 4-byte codes.
+// live (device, optional): only rows below live[0] are in use.
 hipError_t launch_split_rows(int bits, const float* src, long sstride, int n, uint8_t* dst, long dstride, int kp,
-                             long rows, int* exps, hipStream_t st);
+                             long rows, int* exps, hipStream_t st, const int* live = nullptr);
 // exps[r] = e of the n fp32 codes at src + r * stride, r < rows.
 hipError_t launch_row_exp(const float* src, long stride, long rows, int n, int* exps, hipStream_t st);
 

@@ -68,12 +68,15 @@ __device__ __forceinline__ void store_block(uint8_t* __restrict__ d, int b, int 
 // dstride (bytes); exps[r] = e.  src and dst may be the same row of 4-byte
 // codes (every thread reads a block before it writes that block's bytes, and
 // no other thread touches them).  The first RB blocks of a thread stay in
-// registers between the two passes; longer rows read the rest again.
+// registers between the two passes; longer rows read the rest again.  With
+// live given, rows from *live on are not in use and are skipped.
 template <int BITS, int NT>
 __global__ void __launch_bounds__(NT) qmoe_split_rows(const float* src, long sstride, int n, int vec, uint8_t* dst,
-                                                      long dstride, int kp, int* __restrict__ exps) {
+                                                      long dstride, int kp, int* __restrict__ exps,
+                                                      const int* __restrict__ live) {
   constexpr int RB = 2;
   const long row = blockIdx.x;
+  if (live != nullptr && row >= live[0]) return;
   const float* s = src + row * sstride;
   uint8_t* d = dst + row * dstride;
   const int nb = kp / 32;
@@ -136,7 +139,7 @@ __global__ void __launch_bounds__(256) qmoe_row_exp(const float* __restrict__ sr
 }
 
 hipError_t launch_split_rows(int bits, const float* src, long sstride, int n, uint8_t* dst, long dstride, int kp,
-                             long rows, int* exps, hipStream_t st) {
+                             long rows, int* exps, hipStream_t st, const int* live) {
   if (rows <= 0) return hipSuccess;
   if (kp % 32 != 0 || n > kp) return hipErrorInvalidValue;
   // 16-byte loads need 16-byte aligned rows
@@ -144,11 +147,11 @@ hipError_t launch_split_rows(int bits, const float* src, long sstride, int n, ui
   const int nb = kp / 32;
   const dim3 grid((unsigned)rows);
   if (nb <= 128) {
-    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps);
-    else hipLaunchKernelGGL((qmoe_split_rows<8, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps);
+    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live);
+    else hipLaunchKernelGGL((qmoe_split_rows<8, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live);
   } else {
-    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps);
-    else hipLaunchKernelGGL((qmoe_split_rows<8, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps);
+    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live);
+    else hipLaunchKernelGGL((qmoe_split_rows<8, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live);
   }
   return hipGetLastError();
 }

@@ -7,6 +7,7 @@
 // never synchronises.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
 #include <mutex>
 
 #include "kernels/launch.h"
@@ -175,8 +176,11 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     // streaming FC2 splits them while staging; the other GEMMs take them as
     // hi/lo rows, converted here in place.
     float* act32 = reinterpret_cast<float*>(act);
+    // (a share: only the sorted positions of held experts' slots, the first
+    // offsets[El], have rows)
     if (!p.s2.on)
-      QMOE_TRY_HIP(launch_split_rows(d.bits, act32, p.kp2, I, act, 4 * (long)p.kp2, (int)p.kp2, S, exp2, s));
+      QMOE_TRY_HIP(launch_split_rows(d.bits, act32, p.kp2, I, act, 4 * (long)p.kp2, (int)p.kp2, S, exp2, s,
+                                     p.share ? offsets + El : nullptr));
     else if (!p.s2.one)
       QMOE_TRY_HIP(launch_row_exp(act32, p.kp2, S, I, exp2, s));
     QMOE_TRY_HIP(mark(3));
@@ -330,6 +334,27 @@ qmoe_status qmoe_forward_debug(const qmoe_tensor* input, const qmoe_tensor* rout
                                size_t workspace_bytes, void* stream, const qmoe_debug* debug) {
   return forward_impl(input, router_probs, fc1w, fc1s, fc2w, fc2s, attrs, output, workspace, workspace_bytes,
                       stream, debug);
+}
+
+qmoe_status qmoe_plan_describe(const qmoe_tensor* input, const qmoe_tensor* router_probs, const qmoe_tensor* fc1w,
+                               const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,
+                               const qmoe_attrs* attrs, char* buf, size_t len) {
+  if (!buf || len == 0) return QMOE_ERR_NULL;
+  Dims d;
+  const qmoe_status st = validate(input, router_probs, fc1w, fc1s, fc2w, fc2s, nullptr, attrs, &d);
+  if (st != QMOE_OK) return st;
+  Plan p;
+  make_plan(d, &p);
+  auto gemm = [&](const Plan::Stream& sp) { return sp.on ? "stream" : p.tiled ? "tiled" : "gemm"; };
+  const bool ffn = d.T > 0 && d.I > 0 && d.El > 0;
+  std::snprintf(buf, len,
+                "fc1=%s fc2=%s front=%s tile_rows=%lld max_tiles=%lld share=%d "
+                "s1=%d:%d:%d:%d:%d s2=%d:%d:%d:%d:%d workspace=%zu",
+                ffn ? gemm(p.s1) : "none", ffn ? gemm(p.s2) : "none",
+                p.small_front ? "one-workgroup" : "kernels", (long long)p.bm, (long long)p.max_tiles, p.share ? 1 : 0,
+                p.s1.one, p.s1.stg, p.s1.nst, p.s1.splits, p.s1.wg_rows, p.s2.one, p.s2.stg, p.s2.nst,
+                p.s2.splits, p.s2.wg_rows, p.bytes);
+  return QMOE_OK;
 }
 
 const char* qmoe_status_string(qmoe_status s) {

@@ -73,6 +73,16 @@ qmoe_status extents_ok(const qmoe_tensor* t) {
 // register-tiled) or "gemm" (register-tiled); unset or anything else: the
 // plan's own choice.
 enum { PATH_AUTO = 0, PATH_STREAM = 1, PATH_TILED = 2, PATH_GEMM = 3 };
+// Rows per streaming tile, for measurement: QMOE_STREAM_TILE_ROWS = 16, 32,
+// 48 or 64 (at most the token count rounded up to 16); anything else: the
+// plan's own (16).
+int stream_rows_override() {
+  const char* v = std::getenv("QMOE_STREAM_TILE_ROWS");
+  if (!v) return 0;
+  const std::string s(v);
+  return (s == "16" || s == "32" || s == "48" || s == "64") ? std::stoi(s) : 0;
+}
+
 int path_override() {
   const char* v = std::getenv("QMOE_PATH");
   if (!v) return PATH_AUTO;
@@ -186,24 +196,103 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
   return QMOE_OK;
 }
 
+namespace {
+
+// Split of one streaming GEMM (reduction length K, N weight rows) into K
+// ranges of stages of 128-byte row items, for tiles of 16 * mt rows; st->on
+// is false when the stages cannot tile K.
+void stream_shape(const Dims& d, int mt, int64_t K, int64_t N, Plan::Stream* st) {
+  *st = Plan::Stream();
+  // Stages of stg items (256 codes an item at 4 bits, 128 at 8) must tile
+  // K.  Scale blocks that end inside a 64-byte chunk (bs < codes per chunk)
+  // must come 4 to 16 to a stage.
+  const int64_t item_codes = d.bits == 4 ? 256 : 128;
+  const int64_t chunk_codes = item_codes / 2;
+  const int64_t units = d.El * ceil_div(N, 128 * QMOE_STREAM_NT);
+  auto fits = [&](int64_t scodes) {
+    if (!(K > 0 && K % scodes == 0 && (d.bs == 0 || d.bs >= 32))) return false;
+    if (d.bs > 0 && d.bs < chunk_codes) {
+      const int64_t nbs = scodes / d.bs;  // blocks ending inside chunks, per stage
+      return nbs % 4 == 0 && nbs <= 16;
+    }
+    return true;
+  };
+  // One stage per K range (staged once) when that takes at most
+  // QMOE_STREAM_MAX_ONE_SPLITS ranges; else double-buffered stages over the
+  // whole of K, split only as far as needed to fill the chip.
+  const int64_t one_codes = stream_stage_items(mt, true) * item_codes;
+  if (fits(one_codes) && K / one_codes <= max_one_splits()) {
+    st->on = true;
+    st->one = true;
+    st->stg = stream_stage_items(mt, true);
+    st->splits = (int)(K / one_codes);
+    st->nst = 1;
+    return;
+  }
+  st->one = false;
+  st->stg = stream_stage_items(mt, false);
+  const int64_t scodes = st->stg * item_codes;
+  st->on = fits(scodes);
+  if (!st->on) return;
+  const int64_t nst_total = K / scodes;
+  int64_t splits = nst_total;
+  for (int64_t z = 1; z <= nst_total; ++z)
+    if (nst_total % z == 0 && units * z >= QMOE_STREAM_MIN_WORKGROUPS) {
+      splits = z;
+      break;
+    }
+  st->splits = (int)splits;
+  st->nst = (int)(nst_total / splits);
+  // With one K range and one tile row of 16, size the workgroups so that the
+  // grid is one round of QMOE_STREAM_MIN_WORKGROUPS equal workgroups when
+  // that takes 256 to 512 rows each (whole 64-row pieces): every compute
+  // unit then streams the same share to the end.
+  st->wg_rows = 0;
+  const int64_t rbrows = 128 * QMOE_STREAM_NT;
+  if (mt == 1 && splits == 1 && units > QMOE_STREAM_MIN_WORKGROUPS) {
+    const int64_t r = round_up(ceil_div(d.El * N, QMOE_STREAM_MIN_WORKGROUPS), 64);
+    st->wg_rows = (int)std::min(r, 2 * rbrows);
+  }
+}
+
+}  // namespace
+
 void make_plan(const Dims& d, Plan* p) {
   *p = Plan();
   p->d = d;
   p->S = d.T * d.k;
   if (d.T == 0) return;  // nothing to enqueue
   p->share = d.El < d.E;
-  // Every expert receives at most T rows (a token selects distinct experts),
-  // so up to 64 tokens one M tile of ceil(T/16)*16 rows holds any expert's
-  // rows and the weights stream from HBM exactly once.  Past that (up to
-  // kStreamMaxTokens, or any count forced by QMOE_PATH) an expert's rows may
-  // take several 64-row tiles, each streaming the weights again.
+  // GEMM path.  The weight-streaming kernels read every weight row once per
+  // M tile of 16 rows (an expert with more rows takes several tiles); the
+  // LDS-tiled kernels use 128-row tiles.  Measured on the decode (8 large
+  // experts), large-E (128 int8 experts), fine-grained (64 small experts) and
+  // decode inter-share layers (bench.py --crossover): streaming is faster up
+  // to 256 tokens where both GEMMs stream (up to about 280 and 450 tokens on
+  // the first two); where only FC1 streams (FC2's reduction is not a whole
+  // number of stages) it is faster up to 64 tokens with 8 experts and slower
+  // at every size with 64.  Taller streaming tiles (each weight fragment
+  // feeding 2 to 4 row subtiles) made the kernel bound by matrix-core and LDS
+  // work instead of HBM: 0.36 / 0.63 / 0.72 ms at 32 / 64 / 96 decode tokens
+  // against 0.20 / 0.30 / 0.35 ms with 16-row tiles.
   const int force = path_override();
-  p->decode = force == PATH_STREAM || (force == PATH_AUTO && d.T <= kStreamMaxTokens);
-  p->mt = p->decode ? int(std::min<int64_t>((d.T + 15) / 16, 4)) : 4;
+  bool stream = force == PATH_STREAM;
+  if (force == PATH_AUTO && d.I > 0 && d.El > 0 && d.T <= kStreamMaxTokens) {
+    Plan::Stream a, b;
+    stream_shape(d, 1, d.H, d.F, &a);
+    stream_shape(d, 1, d.I, d.H, &b);
+    stream = (a.on && b.on) || (a.on && d.T <= kStreamMixedMaxTokens && d.El <= kStreamMixedMaxExperts);
+  }
+  p->decode = stream;
+  p->mt = 4;
+  if (p->decode) {
+    const int rows = stream_rows_override();
+    p->mt = rows > 0 ? int(std::min<int64_t>(rows / 16, (d.T + 15) / 16)) : 1;
+  }
   p->bm = 16 * p->mt;
-  // Larger token counts: the LDS-tiled GEMMs when both reductions are whole
-  // 64-code steps, rows are 8-code aligned and scale blocks are >= 32 codes
-  // (else the register-tiled GEMMs with 64-row tiles).
+  // Otherwise the LDS-tiled GEMMs when both reductions are whole 64-code
+  // steps, rows are 8-code aligned and scale blocks are >= 32 codes (else
+  // the register-tiled GEMMs with 64-row tiles).
   const bool aligned8 = (d.H % 8 == 0) && (d.I % 8 == 0);
   p->tiled = !p->decode && force != PATH_GEMM && d.I > 0 && aligned8 && d.H % 64 == 0 && d.I % 64 == 0 &&
              (d.bs == 0 || d.bs >= 32);
@@ -219,60 +308,8 @@ void make_plan(const Dims& d, Plan* p) {
   // a share permutes over El + 1 groups (the last: slots of experts not held)
   p->small_front = !p->share && p->S <= 1024 && d.E <= 1024;
   if (p->decode && d.I > 0 && d.El > 0) {
-    // Weight-streaming kernels: stages of stg items (256 codes an item at 4
-    // bits, 128 at 8); the stages must tile K.  Scale blocks that end inside a
-    // 64-byte chunk (bs < codes per chunk) must come 4 to 16 to a stage.
-    const int64_t item_codes = d.bits == 4 ? 256 : 128;
-    const int64_t chunk_codes = item_codes / 2;
-    auto shape = [&](Plan::Stream& st, int64_t K, int64_t N) {
-      const int64_t units = d.El * ceil_div(N, 128 * QMOE_STREAM_NT);
-      auto fits = [&](int64_t scodes) {
-        if (!(K > 0 && K % scodes == 0 && (d.bs == 0 || d.bs >= 32))) return false;
-        if (d.bs > 0 && d.bs < chunk_codes) {
-          const int64_t nbs = scodes / d.bs;  // blocks ending inside chunks, per stage
-          return nbs % 4 == 0 && nbs <= 16;
-        }
-        return true;
-      };
-      // One stage per K range (staged once) when that takes at most
-      // QMOE_STREAM_MAX_ONE_SPLITS ranges; else double-buffered stages over
-      // the whole of K, split only as far as needed to fill the chip.
-      const int64_t one_codes = stream_stage_items(p->mt, true) * item_codes;
-      if (fits(one_codes) && K / one_codes <= max_one_splits()) {
-        st.on = true;
-        st.one = true;
-        st.stg = stream_stage_items(p->mt, true);
-        st.splits = (int)(K / one_codes);
-        st.nst = 1;
-        return;
-      }
-      st.one = false;
-      st.stg = stream_stage_items(p->mt, false);
-      const int64_t scodes = st.stg * item_codes;
-      st.on = fits(scodes);
-      if (!st.on) return;
-      const int64_t nst_total = K / scodes;
-      int64_t splits = nst_total;
-      for (int64_t z = 1; z <= nst_total; ++z)
-        if (nst_total % z == 0 && units * z >= QMOE_STREAM_MIN_WORKGROUPS) {
-          splits = z;
-          break;
-        }
-      st.splits = (int)splits;
-      st.nst = (int)(nst_total / splits);
-      // With one K range and one tile row of 16, size the workgroups so that
-      // the grid is one round of QMOE_STREAM_MIN_WORKGROUPS equal workgroups
-      // when that takes 256 to 512 rows each (whole 64-row pieces): every
-      // compute unit then streams the same share to the end.
-      st.wg_rows = 0;
-      const int64_t rbrows = 128 * QMOE_STREAM_NT;
-      if (p->mt == 1 && splits == 1 && units > QMOE_STREAM_MIN_WORKGROUPS) {
-        const int64_t r = round_up(ceil_div(d.El * N, QMOE_STREAM_MIN_WORKGROUPS), 64);
-        st.wg_rows = (int)std::min(r, 2 * rbrows);
-      }
-    };
-    shape(p->s1, d.H, d.F);
-    shape(p->s2, d.I, d.H);
+    stream_shape(d, p->mt, d.H, d.F, &p->s1);
+    stream_shape(d, p->mt, d.I, d.H, &p->s2);
     if (p->s2.on) p->splits2 = p->s2.splits;
   }
   size_t o = 0;

@@ -33,13 +33,12 @@ struct Dims {
 // Largest expert count the routing kernels hold in registers / LDS.
 constexpr int64_t kMaxExperts = 1024;
 
-// Token counts up to which the weight-streaming GEMMs run.  Up to 64 tokens
-// every expert's rows fit one tile of at most 64 rows and the weights leave
-// HBM once; measured on the Mixtral-like decode experts (8 x int4, hidden
-// 4096, inter 14336, k = 2) the streaming path stays faster than the tiled
-// one up to 96 tokens (0.721 against 0.745 ms at 96; 0.794 against 0.759
-// ms at 128).
-constexpr int64_t kStreamMaxTokens = 96;
+// Token counts up to which the weight-streaming GEMMs run (measured
+// crossovers; see make_plan): when both GEMMs stream, and when only FC1
+// streams (then also at most kStreamMixedMaxExperts experts held).
+constexpr int64_t kStreamMaxTokens = 256;
+constexpr int64_t kStreamMixedMaxTokens = 64;
+constexpr int64_t kStreamMixedMaxExperts = 16;
 
 qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const qmoe_tensor* fc1w,
                      const qmoe_tensor* fc1s, const qmoe_tensor* fc2w, const qmoe_tensor* fc2s,

@@ -76,10 +76,14 @@ def test_roofline_bound_follows_intensity():
 
 
 def test_kernel_choice_per_workload():
-    assert bench.gemm_kernel(W.WORKLOADS["tiny"]) == "qmoe_gemm"          # K = 64: no whole 128-byte items
+    # read from the library's own launch plan (host code)
+    assert bench.gemm_kernel(W.WORKLOADS["tiny"]) == "qmoe_tiled"         # K = 64: no whole 128-byte items
+    assert bench.gemm_kernel(W.WORKLOADS["decode_tp8"], "fc2") == "qmoe_gemm"  # K = 1792: no whole 512-code stages
     assert bench.gemm_kernel(W.WORKLOADS["decode"]) == "qmoe_stream"
     assert bench.gemm_kernel(W.WORKLOADS["decode"], "fc2") == "qmoe_stream"
     assert bench.gemm_kernel(W.WORKLOADS["large_e_ep8"]) == "qmoe_tiled"
+    plan = bench.plan_of(W.WORKLOADS["decode"])
+    assert "tile_rows=16" in plan and "s1=1:4:1:4:0" in plan and "s2=1:4:1:14:0" in plan
     for name in ("prefill", "fine", "large_e"):
         assert bench.gemm_kernel(W.WORKLOADS[name]) == "qmoe_tiled"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1"]) == "qmoe_gmm_f32_rows16"
@@ -89,20 +93,15 @@ def test_kernel_choice_per_workload():
 def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
     src = tmp_path / "kernel.hip"
     src.write_text("// kernel source\n")
-    plan = tmp_path / "plan.cpp"
-    plan.write_text("// planner\n")
-    monkeypatch.setattr(bench, "PLAN_SRC", str(plan))
-    rec = {"decode:fc1": {"kernel": "qmoe_stream", "source_sha": bench._sha(str(src)),
-                          "plan_sha": bench._sha(str(plan)), "bytes": 123}}
+    plan = "fc1=stream fc2=stream s1=1:4:1:4:0"
+    rec = {"decode:fc1": {"kernel": "qmoe_stream", "source_sha": bench._sha(str(src)), "plan": plan, "bytes": 123}}
     tf = tmp_path / "traffic.json"
     tf.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
     monkeypatch.setitem(bench.KERNEL_SRC, "qmoe_stream", str(src))
-    assert bench.traffic_for("decode:fc1", "qmoe_stream") == 123
-    assert bench.traffic_for("decode:fc2", "qmoe_stream") is None      # never measured
-    assert bench.traffic_for("decode:fc1", "qmoe_tiled") is None       # another kernel
-    plan.write_text("// planner, changed split rule\n")
-    assert bench.traffic_for("decode:fc1", "qmoe_stream") is None      # planner changed since
-    plan.write_text("// planner\n")
+    assert bench.traffic_for("decode:fc1", "qmoe_stream", plan) == 123
+    assert bench.traffic_for("decode:fc2", "qmoe_stream", plan) is None      # never measured
+    assert bench.traffic_for("decode:fc1", "qmoe_tiled", plan) is None       # another kernel
+    assert bench.traffic_for("decode:fc1", "qmoe_stream", "fc1=stream s1=1:4:1:8:0") is None  # another plan
     src.write_text("// kernel source, changed\n")
-    assert bench.traffic_for("decode:fc1", "qmoe_stream") is None      # source changed since
+    assert bench.traffic_for("decode:fc1", "qmoe_stream", plan) is None      # source changed since

@@ -108,7 +108,8 @@ def test_route_ties_through_gpu(torch):
 
 
 # Small sweeps: every element.  (T, H, E, I, k) chosen to cover one and several
-# M subtiles on the weight-streaming path (T <= 96), the LDS-tiled path (T > 96,
+# M tiles on the weight-streaming path (up to 256 tokens where its stages
+# tile both reductions), the LDS-tiled path (larger T,
 # H and I multiples of 64) and the register-tiled path (other shapes), ragged
 # tails in every dimension, unused experts and k = E.
 SHAPES = [
@@ -116,10 +117,11 @@ SHAPES = [
     (33, 128, 6, 64, 6), (64, 192, 8, 128, 2), (70, 128, 5, 96, 2), (200, 64, 16, 64, 4),
     (300, 256, 1, 32, 1), (24, 512, 8, 256, 3), (40, 256, 4, 256, 2), (60, 256, 4, 128, 2),
     (130, 128, 3, 192, 2), (257, 320, 4, 128, 3),
-    # either side of the streaming / tiled switch (96 tokens): 64-row
-    # streaming tiles with experts holding more than one tile, then 128-row
-    # LDS tiles
-    (96, 256, 2, 128, 2), (97, 256, 2, 128, 2), (90, 512, 8, 256, 3),
+    # either side of the streaming / tiled switches: 256 tokens where both
+    # GEMMs stream (16-row streaming tiles, experts spread over many tiles),
+    # 64 where only FC1 does (int4: FC2's 256-code reduction is not a whole
+    # 512-code stage), then 128-row LDS tiles
+    (256, 512, 4, 512, 2), (257, 512, 4, 512, 2), (64, 512, 8, 256, 2), (65, 512, 8, 256, 2),
 ]
 
 
