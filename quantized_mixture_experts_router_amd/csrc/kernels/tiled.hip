@@ -18,10 +18,12 @@
 // (2 x 4 wavefronts of 64 x 64).  Each 64-code K step's operands - the
 // tile's activation slice (f16 hi/lo, 32 KB), packed weight slice (8 or
 // 16 KB) and block scales - arrive in one of three LDS stage buffers by
-// direct-to-LDS loads issued two steps ahead, so two steps of loads are in
-// flight while a step runs on the matrix cores.  Weights are unpacked from
-// LDS straight into matrix-core operands (exact f16 q - mid) and each
-// fragment feeds 8 instructions (4 row subtiles x hi/lo).
+// direct-to-LDS loads issued about two steps ahead.  The two rows of
+// wavefronts alternate per half-step between reading fragments from LDS and
+// running matrix instructions (a ping-pong on each SIMD, kept in step by
+// workgroup barriers).  Packed weights are unpacked in registers to exact
+// f16 (q - mid) between matrix instructions, and each fragment feeds 8
+// instructions (4 row subtiles x hi/lo).
 // Workgroups are ordered so that the ones resident on an XCD at the same time
 // cover 8 row tiles x 4 column tiles: both operands are reused from that
 // XCD's L2.
@@ -58,16 +60,22 @@ struct TiledLayout {
 template <int BITS>
 __device__ __forceinline__ int bswz(int n) { return BITS == 4 ? (n >> 3) & 1 : (n >> 2) & 3; }
 
-// Eight codes [32*j + 8*cg, +8) of staged weight row n as exact f16 (q - mid)
-// in A-row storage order (see common.hpp).
+// Eight codes [32*j + 8*cg, +8) of staged weight row n: the packed word(s)
+// (tile_raw), then exact f16 (q - mid) in A-row storage order (tile_unpack,
+// see common.hpp).
 template <int BITS>
-__device__ __forceinline__ f16x8 tile_operand(const uint8_t* bbuf, int n, int j, int cg, const UnpackMasks& m) {
-  if constexpr (BITS == 4) {
-    return unpack4(*(const uint32_t*)(bbuf + n * 32 + ((j ^ bswz<4>(n)) * 16) + 4 * cg), m);
-  } else {
-    const u32x2 v = *(const u32x2*)(bbuf + n * 64 + (((2 * j + (cg >> 1)) ^ bswz<8>(n)) * 16) + (cg & 1) * 8);
-    return unpack8x2(v[0], v[1]);
-  }
+struct BRaw {
+  using type = typename std::conditional<BITS == 4, uint32_t, u32x2>::type;
+};
+template <int BITS>
+__device__ __forceinline__ typename BRaw<BITS>::type tile_raw(const uint8_t* bbuf, int n, int j, int cg) {
+  if constexpr (BITS == 4) return *(const uint32_t*)(bbuf + n * 32 + ((j ^ bswz<4>(n)) * 16) + 4 * cg);
+  else return *(const u32x2*)(bbuf + n * 64 + (((2 * j + (cg >> 1)) ^ bswz<8>(n)) * 16) + (cg & 1) * 8);
+}
+template <int BITS>
+__device__ __forceinline__ f16x8 tile_unpack(typename BRaw<BITS>::type v, const UnpackMasks& m) {
+  if constexpr (BITS == 4) return unpack4(v, m);
+  else return unpack8x2(v[0], v[1]);
 }
 
 // Wait until at most n vector-memory operations of this wavefront are in flight.
@@ -178,7 +186,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   };
 
   f32x4 acc[4][4];
-  f32x4 blk[4][4];
+  f32x4 blk[4][4];  // block-scale spans: the span's sum, folded into acc when it closes
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms)
@@ -190,107 +198,148 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   const UnpackMasks um = unpack_masks();
   const int cg = code_group_of_lane<BITS>(grp);
 
-  // Step kt reads stage buffer kt % 3.  Its loads were issued two steps
-  // earlier: wait for them (the next step's may stay in flight), then the
-  // barrier makes every wavefront's loads visible and frees buffer
-  // (kt + 2) % 3 (last read in step kt - 1) for the loads of step kt + 2.
-  auto kstep = [&](int kt, uint8_t* base, uint8_t* next2, auto odd_tag) {
-    constexpr bool ODD = decltype(odd_tag)::value;  // second K step of a 128-code span
-    wait_vm<NV>();
+  // Schedule: the K loop runs in ticks separated by workgroup barriers.  Per
+  // 32-code half-step a wavefront has a fragment tick (read the half's
+  // operands from LDS into registers: the packed weight words of its four
+  // column subtiles, A hi/lo of its four row subtiles, the closing span's
+  // block scales; fold the span that closed before) and a matrix tick
+  // (unpack the weights and run its 32 matrix instructions, no LDS access).
+  // The second wavefront group (rows 64..127; one wavefront of each group on
+  // every SIMD) meets one extra barrier before the loop, so it runs one tick
+  // behind the first and on each SIMD one wavefront's matrix instructions
+  // overlap the other's fragment work.  Both groups run the same code and
+  // meet the same number of barriers (the first group's extra one comes
+  // after the loop).  (One barrier per half-step, met by the two groups at
+  // different points so that they alternate without a barrier between the
+  // phases, measured 20 % slower: the groups drift into the same phase.)
+  //
+  // A K step (two halves) is four ticks, its barriers p0..p3.  Before p3 of
+  // step kt a wavefront waits for its own loads of step kt + 1 (those of
+  // kt + 2 stay in flight): the first group's fragment tick of step kt + 1
+  // follows its p0 of kt + 1, which for the second group is p3 of step kt,
+  // so every wavefront's loads of a step have landed before any wavefront
+  // reads its buffer.  After p0 of step kt the loads of step kt + 2 go to the
+  // buffer of step kt - 1, whose last reader (the second group's fragment
+  // tick of half 1) ended at that barrier.
+  f16x8 ah[4], al[4];
+  typename BRaw<BITS>::type raw[4];
+  float sc[4] = {0.f, 0.f, 0.f, 0.f};  // block scales of the span that closed last
+  // nothing moves across a tick's barrier (LDS reads stay in their tick)
+  auto bar = []() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
-    // nothing moves across the barrier: reads of buffer kt % 3 stay after it,
-    // the refill of buffer (kt + 2) % 3 stays after every wavefront's reads
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    issue(next2, min(kt + 2, nk - 1));
+  };
+  auto fold = [&]() {
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) acc[ms][ns] += blk[ms][ns] * sc[ns];
+  };
+  // Fragment tick of half j of the step in buffer base: the packed weight
+  // words of the wavefront's four column subtiles, the activation hi/lo
+  // fragments of its four row subtiles and the closing span's scales come
+  // into registers; the fold of the span that closed before runs while they
+  // are in flight.  (The weights are unpacked in the matrix tick.)
+  auto frag = [&](const uint8_t* base, int j, bool fold_first, bool close) {
     const uint8_t* bbuf = base + kABuf;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // weight fragments of the step, then the four row subtiles with their
-      // activation fragments loaded one subtile ahead; hi parts then lo
-      // parts, so the two instructions on one accumulator are 4 apart
-      f16x8 bf[4], ah[2], al[2];
+    for (int ns = 0; ns < 4; ++ns) raw[ns] = tile_raw<BITS>(bbuf, wn * 64 + ns * 16 + col, j, cg);
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns) bf[ns] = tile_operand<BITS>(bbuf, wn * 64 + ns * 16 + col, j, cg, um);
-      auto aload = [&](int ms, f16x8& h, f16x8& l) {
-        const uint8_t* arow = base + (wm * 64 + ms * 16 + col) * 256;  // row & 15 == col
-        h = *(const f16x8*)(arow + (((8 * j + 2 * grp) ^ col) * 16));
-        l = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
-      };
-      if constexpr (SCALE == SC_BLOCK && STEPFOLD) {
-        // Scale blocks folded per 32-code step (32-code blocks), per K step
-        // (64-code blocks) or per two K steps (blocks of 128 codes and more;
-        // a span never straddles blocks): the first instruction of a span starts
-        // from zero (no zeroing moves), and each row subtile is folded right
-        // after the next subtile's instructions are issued, so no fold waits
-        // on the matrix pipeline.
-        // STEPFOLD_KT 0: every 32-code half starts and closes a span; 1: the
-        // K step is the span; 2: two K steps (128 codes) are the span
-        const bool start = STEPFOLD_KT == 0 ? true : STEPFOLD_KT == 1 ? j == 0 : (j == 0 && !ODD);
-        const bool close = STEPFOLD_KT == 0 ? true : STEPFOLD_KT == 1 ? j == 1 : (j == 1 && ODD);
-        const float* srow = (const float*)(base + kABuf + L::kBBuf) + j * kTN + wn * 64 + col;
-        float sc[4];
-        if (close) {
+    for (int ms = 0; ms < 4; ++ms) {
+      const uint8_t* arow = base + (wm * 64 + ms * 16 + col) * 256;  // row & 15 == col
+      ah[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp) ^ col) * 16));
+      al[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
+    }
+    float nsc[4];
+    if constexpr (SCALE == SC_BLOCK) {
+      if (close) {
+        const float* srow = (const float*)(bbuf + L::kBBuf) + j * kTN + wn * 64 + col;
 #pragma unroll
-          for (int ns = 0; ns < 4; ++ns) sc[ns] = srow[ns * 16];
-        }
-        auto fold = [&](int ms) {
+        for (int ns = 0; ns < 4; ++ns) nsc[ns] = srow[ns * 16];
+      }
+      if (fold_first) fold();
+      if (close) {
 #pragma unroll
-          for (int ns = 0; ns < 4; ++ns) acc[ms][ns] += blk[ms][ns] * sc[ns];
-        };
-        aload(0, ah[0], al[0]);
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-          if (ms < 3) aload(ms + 1, ah[(ms + 1) & 1], al[(ms + 1) & 1]);
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-            for (int ns = 0; ns < 4; ++ns)
-              blk[ms][ns] = mfma16(hl ? al[ms & 1] : ah[ms & 1], bf[ns], (hl == 0 && start) ? zero4 : blk[ms][ns]);
-          if (close && ms > 0) fold(ms - 1);
-        }
-        if (close) fold(3);
-      } else {
-        aload(0, ah[0], al[0]);
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-          if (ms < 3) aload(ms + 1, ah[(ms + 1) & 1], al[(ms + 1) & 1]);
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-            for (int ns = 0; ns < 4; ++ns) {
-              const f16x8& av = hl ? al[ms & 1] : ah[ms & 1];
-              if constexpr (SCALE == SC_COL) acc[ms][ns] = mfma16(av, bf[ns], acc[ms][ns]);
-              else blk[ms][ns] = mfma16(av, bf[ns], blk[ms][ns]);
-            }
-        }
-        if constexpr (SCALE == SC_BLOCK) {
-          // blocks of 64 codes and more: scale the block's sum when it closes
-          const int ks = 2 * kt + j;  // 32-code step
-          if (((ks + 1) * 32) % g.bs == 0) {
-            const float* srow = (const float*)(base + kABuf + L::kBBuf) + j * kTN;
-#pragma unroll
-            for (int ns = 0; ns < 4; ++ns) {
-              const float sc = srow[wn * 64 + ns * 16 + col];
-#pragma unroll
-              for (int ms = 0; ms < 4; ++ms) {
-                acc[ms][ns] += blk[ms][ns] * sc;
-                blk[ms][ns] = zero4;
-              }
-            }
-          }
-        }
+        for (int ns = 0; ns < 4; ++ns) sc[ns] = nsc[ns];
       }
     }
+    // every fragment is in registers before the barrier that ends the tick
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   };
+  // Matrix tick: column subtile by column subtile, hi parts then lo parts
+  // of the four row subtiles (the two instructions on one accumulator are 4
+  // apart; a span's first instruction starts from zero).  Each weight
+  // fragment is unpacked to exact f16 (q - mid) while the previous
+  // subtile's instructions run: the unpack instructions are interleaved
+  // one or two per matrix instruction.
+  auto mma = [&](bool start) {
+    __builtin_amdgcn_s_setprio(1);
+    f16x8 bcur = tile_unpack<BITS>(raw[0], um);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      f16x8 bnext = bcur;
+      if (ns < 3) bnext = tile_unpack<BITS>(raw[ns + 1], um);
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+          const f16x8& av = hl ? al[ms] : ah[ms];
+          if constexpr (SCALE == SC_COL) acc[ms][ns] = mfma16(av, bcur, acc[ms][ns]);
+          else blk[ms][ns] = mfma16(av, bcur, (hl == 0 && start) ? zero4 : blk[ms][ns]);
+        }
+      bcur = bnext;
+    }
+    // order: the first fragment's unpack, then per subtile 8 matrix
+    // instructions each followed by unpack instructions of the next one
+    constexpr int kU0 = BITS == 4 ? 2 : 1;  // int4 unpack: 9 instructions, int8: 8
+    __builtin_amdgcn_sched_group_barrier(0x002, kU0 + 7, 0);
+#define QMOE_MFMA_VALU(n)                                \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    \
+  __builtin_amdgcn_sched_group_barrier(0x002, n, 0);
+#define QMOE_SUBTILE() \
+  QMOE_MFMA_VALU(kU0) QMOE_MFMA_VALU(1) QMOE_MFMA_VALU(1) QMOE_MFMA_VALU(1) \
+  QMOE_MFMA_VALU(1) QMOE_MFMA_VALU(1) QMOE_MFMA_VALU(1) QMOE_MFMA_VALU(1)
+    QMOE_SUBTILE() QMOE_SUBTILE() QMOE_SUBTILE()
+#undef QMOE_SUBTILE
+#undef QMOE_MFMA_VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Spans of the block-scale sums: one half (STEPFOLD_KT 0, 32-code blocks),
+  // one K step (1, 64-code blocks) or two K steps (2, blocks of 128 codes and
+  // more; a span never straddles blocks).  Whether half j of a K step of
+  // parity odd starts (closing false) or closes (closing true) a span:
+  auto span = [](bool odd, int j, bool closing) {
+    if (STEPFOLD_KT == 0) return true;
+    if (STEPFOLD_KT == 1) return closing ? j == 1 : j == 0;
+    return closing ? (j == 1 && odd) : (j == 0 && !odd);
+  };
+  const bool trail = wm == 1;  // wave-uniform
+  uint8_t* const sts[3] = {st0, st1, st2};
   issue(st0, 0);
   issue(st1, min(1, nk - 1));
-  // Step kt uses buffer kt % 3 and refills (kt + 2) % 3; with two-step
-  // folds the parity of kt must be static too, so that mode unrolls six.
-  uint8_t* const sts[3] = {st0, st1, st2};
+  wait_vm<NV>();
+  if (trail) bar();
+  // one K step; D = kt modulo the unroll, so buffers and span parity are static
   auto step_d = [&](int kt, auto d_tag) {
     constexpr int D = decltype(d_tag)::value;
-    kstep(kt, sts[D % 3], sts[(D + 2) % 3], std::integral_constant<bool, (D & 1) == 1>{});
+    constexpr bool ODD = (D & 1) == 1;
+    const uint8_t* base = sts[D % 3];
+    bar();  // p0
+    issue(sts[(D + 2) % 3], min(kt + 2, nk - 1));
+    // fold the span that closed at half 1 of the previous step (before kt 0
+    // blk and sc are zero and the fold adds nothing)
+    frag(base, 0, span(!ODD, 1, true), span(ODD, 0, true));
+    bar();  // p1
+    mma(span(ODD, 0, false));
+    bar();  // p2
+    frag(base, 1, span(ODD, 0, true), span(ODD, 1, true));
+    wait_vm<NV>();
+    bar();  // p3
+    mma(span(ODD, 1, false));
   };
   constexpr int U = STEPFOLD_KT == 2 ? 6 : 3;
   int kt = 0;
@@ -311,6 +360,9 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     if (kt + 3 < nk) step_d(kt + 3, std::integral_constant<int, 3>{});
     if (kt + 4 < nk) step_d(kt + 4, std::integral_constant<int, 4>{});
   }
+  if (!trail) bar();
+  // the last span's fold: K is a whole number of spans
+  if constexpr (SCALE == SC_BLOCK) fold();
   // every load has landed and every wavefront is done with the stages
   wait_vm<0>();
   __syncthreads();
