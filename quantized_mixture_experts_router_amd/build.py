@@ -25,6 +25,7 @@ SOURCES = [
     "kernels/operand.hip",
     "kernels/gemm.hip",
     "kernels/stream.hip",
+    "kernels/stream_half.hip",
     "kernels/tiled.hip",
     "kernels/gmm.hip",
     "kernels/gmm_typed.hip",

@@ -91,9 +91,11 @@ hipError_t launch_tiled(int bits, int epi, const GemmArgs& g, int max_tiles, hip
 // z < splits K ranges of g.nst stages each.
 // wg_rows: double-buffered mode, weight rows per workgroup (a multiple of 64
 // up to 512, above 256 only for mt == 1; 0 = 256).
-size_t stream_lds_bytes(int bits, int mt, bool one, int rb);  // rb: row blocks per one-stage workgroup
-hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, const GemmArgs& g, int max_tiles,
-                         hipStream_t st);
+// half_stg: 0, or 1, 4 or 8 for tiles of 8 rows (g.trows holds 8 rows a
+// tile) whose single stage (one, mt == 1) holds that many items.
+size_t stream_lds_bytes(int bits, int mt, bool one, int rb, int half_stg);  // rb: row blocks per one-stage workgroup
+hipError_t launch_stream(int bits, int mt, bool one, int splits, int wg_rows, int half_stg, const GemmArgs& g,
+                         int max_tiles, hipStream_t st);
 
 // Sum FC1 partials over K ranges, apply the activation, write fp32 FC2 operand rows.
 hipError_t launch_act(int bits, int epi, const float* part, int splits, int S, int F, int I, int kp2, float alpha,

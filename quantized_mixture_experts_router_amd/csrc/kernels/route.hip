@@ -338,7 +338,7 @@ __global__ void __launch_bounds__(1024) qmoe_route_small(const float* __restrict
 
 // The whole front end in one wavefront when every token fits a lane and the
 // selection is short (T <= 64, E <= EV <= 64, E * k <= 64, tiles of at least
-// 16 rows): lane t routes
+// 8 rows): lane t routes
 // token t from its logits in registers (the key order of route_token, k
 // passes over the E keys), experts are counted with LDS atomics, lane e
 // scans expert e's count and tile count, and the stable scatter places the
@@ -352,7 +352,8 @@ __global__ void __launch_bounds__(64) qmoe_route_wave(const float* __restrict__ 
                                                       int* __restrict__ counts, int* __restrict__ offsets,
                                                       int* __restrict__ perm, int* __restrict__ tiles,
                                                       int* __restrict__ ntiles, int* __restrict__ trows) {
-  // S <= 1024 slots and tile rows of at least 16: at most 64 + 64 tiles
+  // k <= min(E, 64 / E) <= 8, so S <= 512 slots; with tiles of at least 8
+  // rows at most S / 8 + E <= 64 + 64 tiles
   __shared__ int s_cnt[64];
   __shared__ int s_perm[1024];
   __shared__ int s_tile[2 * 128];  // (first sorted position, rows) of each tile
@@ -511,7 +512,7 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int rout
                               int* topk_idx, float* topk_w, int* counts, int* offsets, int* perm, int* tiles,
                               int* ntiles, int* trows, hipStream_t st) {
   if (T * k > 1024 || E > 1024) return hipErrorInvalidValue;
-  if (T <= 64 && E <= 64 && E * k <= 64 && bm >= 16) {
+  if (T <= 64 && E <= 64 && E * k <= 64 && bm >= 8) {
 #define QMOE_ROUTE_WAVE(EVV)                                                                                      \
   hipLaunchKernelGGL(qmoe_route_wave<EVV>, dim3(1), dim3(64), 0, st, logits, T, E, k, routing, normalize, bm,     \
                      topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows)

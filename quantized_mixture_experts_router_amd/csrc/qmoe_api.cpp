@@ -154,13 +154,13 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
       g1.act_swiglu = d.act == QMOE_ACT_SWIGLU;
       if (p.s1.splits == 1) {
         // whole of K per workgroup: the kernel applies the activation itself
-        QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.one, 1, p.s1.wg_rows, g1, (int)p.max_tiles, s));
+        QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.one, 1, p.s1.wg_rows, p.half ? p.s1.stg : 0, g1, (int)p.max_tiles, s));
         QMOE_TRY_HIP(mark(2));
       } else {
         float* part1 = reinterpret_cast<float*>(ws + p.off_part1);
         g1.act = nullptr;
         g1.slot_out = part1;
-        QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.one, p.s1.splits, p.s1.wg_rows, g1, (int)p.max_tiles, s));
+        QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s1.one, p.s1.splits, p.s1.wg_rows, p.half ? p.s1.stg : 0, g1, (int)p.max_tiles, s));
         QMOE_TRY_HIP(mark(2));
         QMOE_TRY_HIP(launch_act(d.bits, epi1, part1, p.s1.splits, S, (int)d.F, I, (int)p.kp2, d.alpha, d.beta, d.limit, act,
                                 s));
@@ -208,7 +208,7 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g2.store_by_slot = 1;  // FC2 rows go to their slot id
     if (p.s2.on) {
       g2.nst = p.s2.nst;
-      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.one, p.s2.splits, p.s2.wg_rows, g2, (int)p.max_tiles, s));
+      QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.one, p.s2.splits, p.s2.wg_rows, p.half ? p.s2.stg : 0, g2, (int)p.max_tiles, s));
     } else if (p.tiled) {
       QMOE_TRY_HIP(launch_tiled(d.bits, EPI_STORE, g2, (int)p.max_tiles, s));
     } else {

@@ -54,6 +54,8 @@ bool rank_ok(const qmoe_tensor* t, int r) { return t->rank == r; }
 // memory): past these a call is UNSUPPORTED, never computed with wrapped
 // sizes.
 constexpr int64_t kMaxExtent = (int64_t(1) << 31) - 1;
+// Largest second and third grid dimension of a launch.
+constexpr int64_t kMaxGridYZ = 65535;
 constexpr int64_t kMaxElements = int64_t(1) << 40;
 
 // Rank 1..3 with every used extent in [0, kMaxExtent]: QMOE_OK, or SHAPE
@@ -73,14 +75,26 @@ qmoe_status extents_ok(const qmoe_tensor* t) {
 // register-tiled) or "gemm" (register-tiled); unset or anything else: the
 // plan's own choice.
 enum { PATH_AUTO = 0, PATH_STREAM = 1, PATH_TILED = 2, PATH_GEMM = 3 };
-// Rows per streaming tile, for measurement: QMOE_STREAM_TILE_ROWS = 16, 32,
-// 48 or 64 (at most the token count rounded up to 16); anything else: the
-// plan's own (16).
+// Rows per streaming tile, for measurement: QMOE_STREAM_TILE_ROWS = 8 (when
+// both GEMMs allow it), 16, 32, 48 or 64 (at most the token count rounded up
+// to 16); anything else: the plan's own.
 int stream_rows_override() {
   const char* v = std::getenv("QMOE_STREAM_TILE_ROWS");
   if (!v) return 0;
   const std::string s(v);
-  return (s == "16" || s == "32" || s == "48" || s == "64") ? std::stoi(s) : 0;
+  return (s == "8" || s == "16" || s == "32" || s == "48" || s == "64") ? std::stoi(s) : 0;
+}
+
+// Items per single stage of 8-row streaming tiles, for measurement and
+// tests: QMOE_STREAM_STAGE_ITEMS = n (both GEMMs) or "n1,n2" (FC1, FC2) with
+// n in {1, 4, 8}, where the shapes allow it; anything else: the plan's own.
+int stream_items_override(int gemm) {
+  const char* v = std::getenv("QMOE_STREAM_STAGE_ITEMS");
+  if (!v) return 0;
+  std::string s(v);
+  const size_t comma = s.find(',');
+  if (comma != std::string::npos) s = gemm == 0 ? s.substr(0, comma) : s.substr(comma + 1);
+  return s == "1" ? 1 : s == "4" ? 4 : s == "8" ? 8 : 0;
 }
 
 int path_override() {
@@ -198,6 +212,42 @@ qmoe_status validate(const qmoe_tensor* input, const qmoe_tensor* router, const 
 
 namespace {
 
+// Tiles of 8 rows: each K range is one stage, staged once, of 8, 4 or 1
+// items (2048, 1024 or 256 codes at 4 bits; half that at 8; 8 items take the
+// LDS of a 16-row tile's 4-item stage).  Preference, measured on the decode
+// layer at 8 and 16 tokens, the large-E layer at 8 and 16 tokens and the
+// decode inter share: FC1 (gemm 0) 8, 4, then 1 items (8 items faster by
+// 2-5 % even in as few as 224 workgroups); FC2 (gemm 1) 4, 8, then 1 (4
+// items faster by 0-5 %; single items 20-25 % slower where 4 fit, but they
+// stream the inter share's 1792-code FC2 in 17 us against 70 us on the
+// register-tiled GEMM).  st->on is false when no stage tiles K.
+void stream_shape_half(const Dims& d, int64_t K, int64_t N, int gemm, Plan::Stream* st) {
+  *st = Plan::Stream();
+  const int64_t item_codes = d.bits == 4 ? 256 : 128;
+  if (ceil_div(N, 128 * QMOE_STREAM_NT) > kMaxGridYZ) return;
+  const int force = stream_items_override(gemm);
+  int best = 0;
+  const int order[2][3] = {{8, 4, 1}, {4, 8, 1}};
+  for (int items : order[gemm]) {
+    const int64_t scodes = items * item_codes;
+    if (!(K > 0 && K % scodes == 0 && (d.bs == 0 || d.bs >= 32))) continue;
+    if (d.bs > 0 && d.bs < item_codes / 2) {
+      const int64_t nbs = scodes / d.bs;  // blocks ending inside 64-byte chunks, per stage
+      if (nbs % 4 != 0 || nbs > 32) continue;
+    }
+    if (K / scodes > max_one_splits()) continue;
+    if (force != 0 && items != force) continue;
+    best = items;
+    break;
+  }
+  if (best == 0) return;
+  st->on = true;
+  st->one = true;
+  st->stg = best;
+  st->splits = (int)(K / (best * item_codes));
+  st->nst = 1;
+}
+
 // Split of one streaming GEMM (reduction length K, N weight rows) into K
 // ranges of stages of 128-byte row items, for tiles of 16 * mt rows; st->on
 // is false when the stages cannot tile K.
@@ -209,6 +259,7 @@ void stream_shape(const Dims& d, int mt, int64_t K, int64_t N, Plan::Stream* st)
   const int64_t item_codes = d.bits == 4 ? 256 : 128;
   const int64_t chunk_codes = item_codes / 2;
   const int64_t units = d.El * ceil_div(N, 128 * QMOE_STREAM_NT);
+  if (ceil_div(N, 128 * QMOE_STREAM_NT) > kMaxGridYZ) return;  // row groups are a grid dimension
   auto fits = [&](int64_t scodes) {
     if (!(K > 0 && K % scodes == 0 && (d.bs == 0 || d.bs >= 32))) return false;
     if (d.bs > 0 && d.bs < chunk_codes) {
@@ -276,7 +327,9 @@ void make_plan(const Dims& d, Plan* p) {
   // work instead of HBM: 0.36 / 0.63 / 0.72 ms at 32 / 64 / 96 decode tokens
   // against 0.20 / 0.30 / 0.35 ms with 16-row tiles.
   const int force = path_override();
-  bool stream = force == PATH_STREAM;
+  // (the streaming grid's third dimension is the tile count: a forced
+  // streaming plan needs it within the grid limit)
+  bool stream = force == PATH_STREAM && (p->S + 15) / 16 + d.El <= kMaxGridYZ;
   if (force == PATH_AUTO && d.I > 0 && d.El > 0 && d.T <= kStreamMaxTokens) {
     Plan::Stream a, b;
     stream_shape(d, 1, d.H, d.F, &a);
@@ -287,9 +340,21 @@ void make_plan(const Dims& d, Plan* p) {
   p->mt = 4;
   if (p->decode) {
     const int rows = stream_rows_override();
-    p->mt = rows > 0 ? int(std::min<int64_t>(rows / 16, (d.T + 15) / 16)) : 1;
+    p->mt = rows >= 16 ? int(std::min<int64_t>(rows / 16, (d.T + 15) / 16)) : 1;
+    // Tiles of 8 rows when routing gives an expert 4 rows on average (most
+    // experts then fit one tile): a K range then spans twice the codes in
+    // the same LDS, which halves the fp32 K-range partials both GEMMs write
+    // and doubles each workgroup's contiguous run of every weight row.  An
+    // expert with more than 8 rows takes several tiles and streams its
+    // weights once per tile.
+    if (d.I > 0 && d.El > 0 && (rows == 8 || (rows == 0 && p->S <= 4 * d.El))) {
+      Plan::Stream a, b;
+      stream_shape_half(d, d.H, d.F, 0, &a);
+      stream_shape_half(d, d.I, d.H, 1, &b);
+      p->half = a.on && b.on;
+    }
   }
-  p->bm = 16 * p->mt;
+  p->bm = p->half ? 8 : 16 * p->mt;
   // Otherwise the LDS-tiled GEMMs when both reductions are whole 64-code
   // steps, rows are 8-code aligned and scale blocks are >= 32 codes (else
   // the register-tiled GEMMs with 64-row tiles).
@@ -308,8 +373,13 @@ void make_plan(const Dims& d, Plan* p) {
   // a share permutes over El + 1 groups (the last: slots of experts not held)
   p->small_front = !p->share && p->S <= 1024 && d.E <= 1024;
   if (p->decode && d.I > 0 && d.El > 0) {
-    stream_shape(d, p->mt, d.H, d.F, &p->s1);
-    stream_shape(d, p->mt, d.I, d.H, &p->s2);
+    if (p->half) {
+      stream_shape_half(d, d.H, d.F, 0, &p->s1);
+      stream_shape_half(d, d.I, d.H, 1, &p->s2);
+    } else {
+      stream_shape(d, p->mt, d.H, d.F, &p->s1);
+      stream_shape(d, p->mt, d.I, d.H, &p->s2);
+    }
     if (p->s2.on) p->splits2 = p->s2.splits;
   }
   size_t o = 0;

@@ -72,6 +72,7 @@ struct Plan {
     int splits = 1;      // K ranges (fp32 partials summed afterwards, in order)
     int wg_rows = 0;     // double-buffered mode: weight rows per workgroup (0 = one row block of 256)
   } s1, s2;
+  bool half = false;     // streaming tiles of 8 rows (each K range one stage of s.stg items), else 16 * mt rows
   int splits2 = 1;       // FC2 partial sets the combine sums (1 off the stream path)
   size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path with K ranges)
   size_t off_trows = 0;  // streaming kernels: slot id of every tile row [max_tiles][bm]

@@ -183,7 +183,7 @@ void check_plan(const qmoe::Dims& d, const qmoe::Plan& p) {
   // when bm covers every expert's rows)
   const int64_t worst = d.T <= p.bm ? d.El : (S + p.bm - 1) / p.bm + d.El;
   EXPECT(p.max_tiles >= worst, "max_tiles %" PRId64 " < %" PRId64, p.max_tiles, worst);
-  EXPECT(p.bm >= 16 && p.bm <= 128, "bm %" PRId64, p.bm);
+  EXPECT(p.bm >= 8 && p.bm <= 128 && (p.bm >= 16 || p.half), "bm %" PRId64, p.bm);
   EXPECT(p.kp1 % 128 == 0 && p.kp2 % 128 == 0 && p.kp2 >= d.I && (d.I == 0 || p.kp1 >= d.H), "kp");
   const int64_t item = d.bits == 4 ? 256 : 128;
   auto split_ok = [&](const Plan::Stream& st, int64_t K, const char* name) {

@@ -78,12 +78,16 @@ def test_roofline_bound_follows_intensity():
 def test_kernel_choice_per_workload():
     # read from the library's own launch plan (host code)
     assert bench.gemm_kernel(W.WORKLOADS["tiny"]) == "qmoe_tiled"         # K = 64: no whole 128-byte items
-    assert bench.gemm_kernel(W.WORKLOADS["decode_tp8"], "fc2") == "qmoe_gemm"  # K = 1792: no whole 512-code stages
+    # K = 1792: no whole 1024-code stage; 8-row tiles stream it in 256-code K ranges
+    assert bench.gemm_kernel(W.WORKLOADS["decode_tp8"], "fc2") == "qmoe_stream"
+    assert "tile_rows=8 " in bench.plan_of(W.WORKLOADS["decode_tp8"])
+    # the register-tiled GEMM: past the streaming range, I not a multiple of 64
+    assert bench.gemm_kernel(W.Workload("odd", (300, 192), 4, 96, 2, 4, 32, "swiglu", (0.005, 0.02))) == "qmoe_gemm"
     assert bench.gemm_kernel(W.WORKLOADS["decode"]) == "qmoe_stream"
     assert bench.gemm_kernel(W.WORKLOADS["decode"], "fc2") == "qmoe_stream"
     assert bench.gemm_kernel(W.WORKLOADS["large_e_ep8"]) == "qmoe_tiled"
     plan = bench.plan_of(W.WORKLOADS["decode"])
-    assert "tile_rows=16" in plan and "s1=1:4:1:4:0" in plan and "s2=1:4:1:14:0" in plan
+    assert "tile_rows=8 " in plan and "s1=1:8:1:2:0" in plan and "s2=1:4:1:14:0" in plan
     for name in ("prefill", "fine", "large_e"):
         assert bench.gemm_kernel(W.WORKLOADS[name]) == "qmoe_tiled"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1"]) == "qmoe_gmm_f32_rows16"

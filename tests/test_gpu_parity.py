@@ -139,6 +139,45 @@ def test_small_sweep(torch, bits, bs, act):
         _full_check(w, a, torch, f"sweep T{T} H{H} E{E} I{I} k{k}")
 
 
+# Weight streaming in tiles of 8 rows (single stages of 8 items: 2048 codes
+# at 4 bits, 1024 at 8), taken when routing gives an expert at most 4 rows on
+# average: (T, H, E, I, k, bits, bs, act, logit bias of expert 0, forced tile
+# rows).  A bias makes expert 0 draw most tokens, so it spans several tiles;
+# forcing 8-row tiles at larger batches gives every expert several.
+EIGHT_ROW = [
+    (16, 2048, 8, 2048, 2, 4, 64, "swiglu", 0.0, None),
+    (16, 2048, 8, 2048, 2, 4, 64, "swiglu", 4.0, None),
+    (13, 2048, 8, 4096, 2, 4, 128, "relu", 0.0, None),
+    (16, 2048, 8, 2048, 2, 4, 0, "swiglu", 2.0, None),
+    (12, 1024, 8, 2048, 2, 8, 0, "swiglu", 0.0, None),
+    (12, 1024, 8, 1024, 2, 8, 32, "relu", 3.0, None),
+    (10, 2048, 6, 2048, 2, 8, 64, "swiglu", 0.0, None),
+    (1, 2048, 4, 2048, 1, 4, 64, "swiglu", 0.0, None),
+    (40, 2048, 4, 2048, 2, 4, 64, "swiglu", 0.0, "8"),
+    (30, 1024, 3, 1024, 3, 8, 32, "relu", 0.0, "8"),
+]
+
+
+@pytest.mark.parametrize("items", ["1", "4", "8"])
+@pytest.mark.parametrize("case", EIGHT_ROW)
+def test_stream_eight_row_tiles(torch, monkeypatch, case, items):
+    """Every stage length of 8-row tiles (QMOE_STREAM_STAGE_ITEMS; the plan
+    itself takes the longest stage that still fills the chip)."""
+    import quantized_mixture_experts_router_amd as qm
+    T, H, E, I, k, bits, bs, act, bias, force = case
+    if force:
+        monkeypatch.setenv("QMOE_STREAM_TILE_ROWS", force)
+    monkeypatch.setenv("QMOE_STREAM_STAGE_ITEMS", items)
+    rng = np.random.default_rng(1300 + T + E + bits + bs)
+    w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=E, inter=I, k=k, bits=bits, block_size=bs,
+                         activation=act)
+    a["router_probs"] = a["router_probs"].copy()
+    a["router_probs"][:, 0] += bias
+    plan = qm.qmoe_plan_describe(*a.values(), attrs=w.attrs())
+    assert "fc1=stream fc2=stream" in plan and "tile_rows=8 " in plan and f"s1=1:{items}:" in plan, plan
+    _full_check(w, a, torch, f"8-row tiles T{T} H{H} E{E} I{I} k{k} bits{bits} bs{bs} {act} bias{bias} ({plan})")
+
+
 def test_front_end_paths(torch):
     """Routing and permutation on both front ends: one workgroup (up to 1024
     slots and 1024 experts) and the chunked multi-kernel path beyond."""
