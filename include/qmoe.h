@@ -44,7 +44,13 @@
  *    fp32 result is scaled back exactly.  An element is so carried to 2^-22
  *    of itself plus 2^-39 of its row's largest magnitude, for rows of any
  *    magnitude (GPU parity is tested on inputs scaled from 1e-7 to 1e5 and on
- *    rows twelve orders of magnitude apart).  NaN/inf in x or logits are out
+ *    rows twelve orders of magnitude apart).  Between the LDS-tiled GEMMs the
+ *    activation rows are scaled instead by one power of two per 128-row tile
+ *    and FC1 column tile (a 128- or 256-code segment of FC2's reduction):
+ *    an element is then carried to 2^-22 of itself plus 2^-26 of its row's
+ *    largest magnitude in the segment; a row more than 2^12 below its tile
+ *    (or any row of values from 2^113 on) falls back to the per-row scaling
+ *    above for the whole call.  NaN/inf in x or logits are out
  *    of contract and produce unspecified (but bounded-time) results; results
  *    beyond the float32 range are infinite.
  *  - Entry points keep no state between calls (the only process-wide

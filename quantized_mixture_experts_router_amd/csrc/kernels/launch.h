@@ -34,10 +34,19 @@ hipError_t launch_tile_rows(const int* perm, const int* tiles, const int* ntiles
 // src + r * sstride (floats) -> kp hi/lo codes of v * 2^e at dst + r * dstride
 // (bytes), exps[r] = e; src and dst may be the same rows of 4-byte codes.
 // live (device, optional): only rows below live[0] are in use.
+// zero_flag (device, optional): set to 0 by the launch.
 hipError_t launch_split_rows(int bits, const float* src, long sstride, int n, uint8_t* dst, long dstride, int kp,
-                             long rows, int* exps, hipStream_t st, const int* live = nullptr);
+                             long rows, int* exps, hipStream_t st, const int* live = nullptr,
+                             int* zero_flag = nullptr);
 // exps[r] = e of the n fp32 codes at src + r * stride, r < rows.
 hipError_t launch_row_exp(const float* src, long stride, long rows, int n, int* exps, hipStream_t st);
+// FC2 operand rows that the tiled FC1 wrote with segment exponents, back to
+// one exponent per row, in place, when flag[0] != 0 (else every workgroup
+// exits at once): row r < rows holds n hi/lo codes at d + r * stride
+// (bytes), code c written with exponent seg_rows[(c >> seg_shift) * rows +
+// r]; exps[r] = the row's new exponent.  live as above.
+hipError_t launch_resplit_rows(int bits, uint8_t* d, long stride, int n, long rows, const int* seg_rows, int seg_shift,
+                               int* exps, const int* flag, hipStream_t st, const int* live = nullptr);
 
 // Grouped quantised GEMM over expert-sorted rows.
 //   FC1: rows are tokens (via perm / k), weights fc1 [E][F][K/pack], output act rows.
@@ -59,6 +68,23 @@ struct GemmArgs {
   int S;                 // slots (stride between split partials, in rows)
   // epilogue
   uint8_t* act;         // FC1 output rows (fp32 after the activation), stride act_stride bytes
+  // Segment scales between the tiled GEMMs [max_tiles][seg_n]: when set, the
+  // FC1 epilogue writes FC2's operand rows as f16 hi/lo groups of v * 2^e
+  // with one e per row tile and FC1 column tile (2^seg_shift codes, a
+  // segment of FC2's reduction) and stores 2^-e in seg_scale; FC2 multiplies
+  // the sums of each segment by it (a_exp unused).  nullptr: FC1 writes fp32
+  // rows, split per row afterwards.
+  float* seg_scale;
+  int seg_shift, seg_n;
+  // FC1 with segment scales: a row whose largest magnitude in the segment is
+  // more than 2^12 below the tile's bound keeps its own exponent instead
+  // (and sets *seg_flag); seg_rows [seg_n][S] gets the exponent each row
+  // segment was written with
+  int* seg_rows;
+  int* seg_flag;
+  // the kernel runs only when (gate[0] != 0) == (gate_on != 0); nullptr: always
+  const int* gate;
+  int gate_on;
   long act_stride;
   float* slot_out;      // FC2 output [splits][S][N] by slot id
   const int* perm;      // FC2: sorted position -> slot

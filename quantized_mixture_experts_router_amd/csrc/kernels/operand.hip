@@ -8,10 +8,15 @@
 //                    as fp32 into hi/lo groups in place.
 //   qmoe_row_exp     e per fp32 row only (the weight-streaming kernels split
 //                    while staging; this serves their walks over a whole row).
+//   qmoe_resplit_rows hi/lo rows written with one exponent per segment (the
+//                    tiled FC1 epilogue's) -> one exponent per row, in place;
+//                    runs only when the epilogue flagged a row.
 //
 // The products these rows feed are the FC1 and FC2 sums of the QMoE WebGPU
 // manifest (description; inputs[0] is float32): the scaling only changes how
 // the fp32 values are carried to the matrix cores, never the sums.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.h"
 
@@ -73,9 +78,10 @@ __device__ __forceinline__ void store_block(uint8_t* __restrict__ d, int b, int 
 template <int BITS, int NT>
 __global__ void __launch_bounds__(NT) qmoe_split_rows(const float* src, long sstride, int n, int vec, uint8_t* dst,
                                                       long dstride, int kp, int* __restrict__ exps,
-                                                      const int* __restrict__ live) {
+                                                      const int* __restrict__ live, int* __restrict__ zero_flag) {
   constexpr int RB = 2;
   const long row = blockIdx.x;
+  if (zero_flag != nullptr && row == 0 && threadIdx.x == 0) *zero_flag = 0;
   if (live != nullptr && row >= live[0]) return;
   const float* s = src + row * sstride;
   uint8_t* d = dst + row * dstride;
@@ -138,8 +144,71 @@ __global__ void __launch_bounds__(256) qmoe_row_exp(const float* __restrict__ sr
   if (lane == 0) exps[row] = row_exp(m);
 }
 
+// A workgroup of NT threads a row (grid-stride over the rows, so that the
+// launch is short when the flag is down), a storage group (8 codes) a
+// thread at a time.  The elementwise rescaling keeps each group's slot
+// order, and the group's segment is that of its 32-code block (segments are
+// whole blocks).  Pass 1 finds the row's largest magnitude, pass 2 rewrites
+// each group in place (a group is read and written by one thread only).
+template <int NT>
+__global__ void __launch_bounds__(NT) qmoe_resplit_rows(uint8_t* d, long stride, int n, long rows,
+                                                        const int* __restrict__ seg_rows, int seg_shift,
+                                                        int* __restrict__ exps, const int* __restrict__ flag,
+                                                        const int* __restrict__ live) {
+  if (flag[0] == 0) return;
+  const long nrows = live != nullptr ? min((long)live[0], rows) : rows;
+  const int ng = n / 8;
+  const int tid = threadIdx.x;
+  __shared__ float red[NT / 64];
+  for (long row = blockIdx.x; row < nrows; row += gridDim.x) {
+    uint8_t* r = d + row * stride;
+    auto value = [&](int q, int sl, const f16x8& hi, const f16x8& lo) {
+      return __builtin_ldexpf((float)hi[sl] + (float)lo[sl], -seg_rows[(long)((8 * q) >> seg_shift) * rows + row]);
+    };
+    float m = 0.f;
+    for (int q = tid; q < ng; q += NT) {
+      const f16x8 hi = *(const f16x8*)(r + (long)q * 32), lo = *(const f16x8*)(r + (long)q * 32 + 16);
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) m = fmaxf(m, fabsf(value(q, sl, hi, lo)));
+    }
+    m = seg_max<64>(m);
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+    __syncthreads();  // red is rewritten by the next row
+    const int e = row_exp(m);
+    if (tid == 0) exps[row] = e;
+    for (int q = tid; q < ng; q += NT) {
+      uint8_t* g = r + (long)q * 32;
+      const f16x8 hi = *(const f16x8*)g, lo = *(const f16x8*)(g + 16);
+      f16x8 h2, l2;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        _Float16 a, b;
+        split_f16(value(q, sl, hi, lo), e, a, b);
+        h2[sl] = a;
+        l2[sl] = b;
+      }
+      *(f16x8*)g = h2;
+      *(f16x8*)(g + 16) = l2;
+    }
+  }
+}
+
+hipError_t launch_resplit_rows(int bits, uint8_t* d, long stride, int n, long rows, const int* seg_rows, int seg_shift,
+                               int* exps, const int* flag, hipStream_t st, const int* live) {
+  (void)bits;  // the rescaling is elementwise: the storage order of either width is kept
+  if (rows <= 0) return hipSuccess;
+  if (n % 32 != 0 || seg_shift < 5) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)std::min<long>(rows, 1024);
+  hipLaunchKernelGGL((qmoe_resplit_rows<256>), dim3(grid), dim3(256), 0, st, d, stride, n, rows, seg_rows, seg_shift,
+                     exps, flag, live);
+  return hipGetLastError();
+}
+
 hipError_t launch_split_rows(int bits, const float* src, long sstride, int n, uint8_t* dst, long dstride, int kp,
-                             long rows, int* exps, hipStream_t st, const int* live) {
+                             long rows, int* exps, hipStream_t st, const int* live, int* zero_flag) {
   if (rows <= 0) return hipSuccess;
   if (kp % 32 != 0 || n > kp) return hipErrorInvalidValue;
   // 16-byte loads need 16-byte aligned rows
@@ -147,11 +216,11 @@ hipError_t launch_split_rows(int bits, const float* src, long sstride, int n, ui
   const int nb = kp / 32;
   const dim3 grid((unsigned)rows);
   if (nb <= 128) {
-    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live);
-    else hipLaunchKernelGGL((qmoe_split_rows<8, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live);
+    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live, zero_flag);
+    else hipLaunchKernelGGL((qmoe_split_rows<8, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live, zero_flag);
   } else {
-    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live);
-    else hipLaunchKernelGGL((qmoe_split_rows<8, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live);
+    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live, zero_flag);
+    else hipLaunchKernelGGL((qmoe_split_rows<8, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live, zero_flag);
   }
   return hipGetLastError();
 }

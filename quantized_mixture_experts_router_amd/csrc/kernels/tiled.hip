@@ -91,12 +91,22 @@ __device__ __forceinline__ void wait_vm() {
 // 16-byte LDS slot base + 16 * l (4 bytes for the scale loads).
 #define QMOE_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
 #define QMOE_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
+// the kernel's helper lambdas are always inlined (arrays they capture stay in registers)
+#define QMOE_INLINE __attribute__((always_inline))
 
 // STEPFOLD: block sums are scaled every 32-code step (STEPFOLD_KT 0, 32-code
 // blocks), every 64-code K step (1, 64-code blocks) or every two K steps (2,
 // blocks of 128 codes and more).
-template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT>
+// SEG (FC2): the operand rows carry one power-of-two scale per row tile and
+// segment of 2^g.seg_shift codes (the FC1 epilogue's, see below) instead of
+// one per row.  A span never straddles a segment, so the segment's factor
+// g.seg_scale joins the span's block scales when the span closes (with
+// column-wise scales the spans are two K steps, folded with that factor
+// alone).
+template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT, bool SEG = false>
 __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
+  static_assert(!SEG || (EPI == EPI_STORE && STEPFOLD && (SCALE == SC_BLOCK || STEPFOLD_KT == 2)),
+                "segment scales: FC2, folded spans");
   using L = TiledLayout<BITS>;
   // Three stage buffers: a step's operands arrive by direct-to-LDS loads two
   // steps ahead of their use.
@@ -113,6 +123,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   // sized for the most tiles routing can produce; only the first
   // ntiles * ntn linear ids carry work, and they are the ones dealt out, so
   // every XCD gets its share of the real tiles.
+  if (g.gate != nullptr && (g.gate[0] != 0) != (g.gate_on != 0)) return;
   const int mtiles = g.ntiles[0];
   const int total = mtiles * ntn;
   const int lin = blockIdx.x;
@@ -141,7 +152,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     const long ar = g.a_map ? (long)(g.a_map[p] / g.a_div) : (long)p;
     s_arow[tid] = ar * g.a_stride;
     s_orow[tid] = g.store_by_slot ? g.perm[p] : p;
-    s_rexp[tid] = g.a_exp[ar];
+    s_rexp[tid] = SEG ? 0 : g.a_exp[ar];
   }
   __syncthreads();
 
@@ -170,7 +181,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   const float* ssrc = g.ws + (ebase + min(n0 + (wave & 3) * 64 + lane, g.N - 1)) * (long)g.nblk;
   const int shalf = (wave >> 2) * 32;
   const int nk = g.K / kTK;
-  auto issue = [&](uint8_t* sb, int kt) {
+  auto issue = [&](uint8_t* sb, int kt) QMOE_INLINE {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(asrc[i] + (long)kt * (kTK * 4)), QMOE_LOCAL(sb + (wave * 4 + i) * 1024),
@@ -225,25 +236,30 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   typename BRaw<BITS>::type raw[4];
   float sc[4] = {0.f, 0.f, 0.f, 0.f};  // block scales of the span that closed last
   // nothing moves across a tick's barrier (LDS reads stay in their tick)
-  auto bar = []() {
+  auto bar = []() QMOE_INLINE {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
   };
-  auto fold = [&]() {
+  // fold the span that closed: acc += blk * its scales
+  auto fold = [&]() QMOE_INLINE {
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) acc[ms][ns] += blk[ms][ns] * sc[ns];
   };
+  // SEG: the factor of the segment holding K step kt (a uniform load, read
+  // through the scalar cache)
+  const __attribute__((address_space(4))) float* segs =
+      SEG ? (const __attribute__((address_space(4))) float*)(g.seg_scale + (long)tile * g.seg_n) : nullptr;
   // Fragment tick of half j of the step in buffer base: the packed weight
   // words of the wavefront's four column subtiles, the activation hi/lo
   // fragments of its four row subtiles and the closing span's scales come
   // into registers; the fold of the span that closed before runs while they
   // are in flight.  (The weights are unpacked in the matrix tick.)
-  auto frag = [&](const uint8_t* base, int j, bool fold_first, bool close) {
+  auto frag = [&](const uint8_t* base, int j, bool fold_first, bool close, int kt) QMOE_INLINE {
     const uint8_t* bbuf = base + kABuf;
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) raw[ns] = tile_raw<BITS>(bbuf, wn * 64 + ns * 16 + col, j, cg);
@@ -253,17 +269,23 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
       ah[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp) ^ col) * 16));
       al[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
     }
-    float nsc[4];
+    float nsc[4] = {1.f, 1.f, 1.f, 1.f};
+    float fseg = 1.f;
+    if constexpr (SEG) {
+      if (close) fseg = segs[(kt * kTK) >> g.seg_shift];
+    }
     if constexpr (SCALE == SC_BLOCK) {
       if (close) {
         const float* srow = (const float*)(bbuf + L::kBBuf) + j * kTN + wn * 64 + col;
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) nsc[ns] = srow[ns * 16];
       }
+    }
+    if constexpr (SCALE == SC_BLOCK || SEG) {
       if (fold_first) fold();
       if (close) {
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) sc[ns] = nsc[ns];
+        for (int ns = 0; ns < 4; ++ns) sc[ns] = SEG ? nsc[ns] * fseg : nsc[ns];
       }
     }
     // every fragment is in registers before the barrier that ends the tick
@@ -275,7 +297,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   // fragment is unpacked to exact f16 (q - mid) while the previous
   // subtile's instructions run: the unpack instructions are interleaved
   // one or two per matrix instruction.
-  auto mma = [&](bool start) {
+  auto mma = [&](bool start) QMOE_INLINE {
     __builtin_amdgcn_s_setprio(1);
     f16x8 bcur = tile_unpack<BITS>(raw[0], um);
 #pragma unroll
@@ -287,7 +309,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
           const f16x8& av = hl ? al[ms] : ah[ms];
-          if constexpr (SCALE == SC_COL) acc[ms][ns] = mfma16(av, bcur, acc[ms][ns]);
+          if constexpr (SCALE == SC_COL && !SEG) acc[ms][ns] = mfma16(av, bcur, acc[ms][ns]);
           else blk[ms][ns] = mfma16(av, bcur, (hl == 0 && start) ? zero4 : blk[ms][ns]);
         }
       bcur = bnext;
@@ -312,7 +334,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   // one K step (1, 64-code blocks) or two K steps (2, blocks of 128 codes and
   // more; a span never straddles blocks).  Whether half j of a K step of
   // parity odd starts (closing false) or closes (closing true) a span:
-  auto span = [](bool odd, int j, bool closing) {
+  auto span = [](bool odd, int j, bool closing) QMOE_INLINE {
     if (STEPFOLD_KT == 0) return true;
     if (STEPFOLD_KT == 1) return closing ? j == 1 : j == 0;
     return closing ? (j == 1 && odd) : (j == 0 && !odd);
@@ -324,7 +346,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   wait_vm<NV>();
   if (trail) bar();
   // one K step; D = kt modulo the unroll, so buffers and span parity are static
-  auto step_d = [&](int kt, auto d_tag) {
+  auto step_d = [&](int kt, auto d_tag) QMOE_INLINE {
     constexpr int D = decltype(d_tag)::value;
     constexpr bool ODD = (D & 1) == 1;
     const uint8_t* base = sts[D % 3];
@@ -332,11 +354,11 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     issue(sts[(D + 2) % 3], min(kt + 2, nk - 1));
     // fold the span that closed at half 1 of the previous step (before kt 0
     // blk and sc are zero and the fold adds nothing)
-    frag(base, 0, span(!ODD, 1, true), span(ODD, 0, true));
+    frag(base, 0, span(!ODD, 1, true), span(ODD, 0, true), kt);
     bar();  // p1
     mma(span(ODD, 0, false));
     bar();  // p2
-    frag(base, 1, span(ODD, 0, true), span(ODD, 1, true));
+    frag(base, 1, span(ODD, 0, true), span(ODD, 1, true), kt);
     wait_vm<NV>();
     bar();  // p3
     mma(span(ODD, 1, false));
@@ -362,11 +384,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   }
   if (!trail) bar();
   // the last span's fold: K is a whole number of spans
-  if constexpr (SCALE == SC_BLOCK) fold();
-  // every load has landed and every wavefront is done with the stages
-  wait_vm<0>();
-  __syncthreads();
-
+  if constexpr (SCALE == SC_BLOCK || SEG) fold();
   if constexpr (SCALE == SC_COL) {
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
@@ -376,13 +394,77 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     }
   }
 
+  // FC1 with segment scales: one exponent e for the whole tile (a segment of
+  // FC2's reduction), from a bound B of its activated values' magnitudes so
+  // that B * 2^e < 2^kRowTop: with ReLU B is their largest value; with SwiGLU
+  // (|gate * sigmoid(alpha * gate)| <= |gate|) the largest gate magnitude
+  // times the largest linear magnitude plus |beta|, each rounded up to a
+  // power of two (a negative limit clamps to -limit).  The factor 2^-e goes
+  // to seg_scale, with e clamped to [-100, 64] so that it is a normal float
+  // (below -100, for magnitudes from 2^113 on, every row takes its own
+  // exponent; above 64 the rows that need more do, see the epilogue).
+  // Each wavefront's maxima cross the barrier below (the one that ends the
+  // K loop) in s_red.
+  constexpr bool seg1 = EPI != EPI_STORE;
+  __shared__ float s_red[seg1 ? 2 * kTWaves : 1];
+  if constexpr (seg1) {
+    if (g.seg_scale != nullptr) {
+      // per lane: its rows' largest magnitude (row scales undone); the lanes
+      // of even columns hold gates, of odd columns linear parts (SwiGLU)
+      float m = 0.f;
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float r = 0.f;
+#pragma unroll
+          for (int ns = 0; ns < 4; ++ns) r = fmaxf(r, EPI == EPI_RELU ? acc[ms][ns][i] : fabsf(acc[ms][ns][i]));
+          m = fmaxf(m, __builtin_ldexpf(r, -s_rexp[wm * 64 + ms * 16 + 4 * grp + i]));
+        }
+#pragma unroll
+      for (int o = EPI == EPI_SWIGLU ? 2 : 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+      if (lane < 2) s_red[wave * 2 + lane] = m;
+    }
+  }
+  // every load has landed and every wavefront is done with the stages
+  wait_vm<0>();
+  __syncthreads();
+  int tile_e = 0;
+  bool tile_own = false;  // every nonzero row takes its own exponent
+  if constexpr (seg1) {
+    if (g.seg_scale != nullptr) {
+      float G = 0.f, Lm = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kTWaves; ++w2) {
+        G = fmaxf(G, s_red[2 * w2]);
+        Lm = fmaxf(Lm, s_red[2 * w2 + 1]);
+      }
+      int e = 0;
+      if constexpr (EPI == EPI_SWIGLU) {
+        if (g.limit < 0.f) {
+          G = fmaxf(G, -g.limit);
+          Lm = fmaxf(Lm, -g.limit);
+        }
+        const float Lb = Lm + fabsf(g.beta);
+        if (G > 0.f && Lb > 0.f && G <= 3.4028235e38f && Lb <= 3.4028235e38f)
+          e = kRowTop - (__builtin_amdgcn_frexp_expf(G) + __builtin_amdgcn_frexp_expf(Lb));
+      } else {
+        e = row_exp(G);
+      }
+      tile_own = e < -100;
+      tile_e = max(min(e, 64), -100);
+      if (tid == 0) g.seg_scale[(long)tile * g.seg_n + ntile] = __builtin_ldexpf(1.f, -tile_e);
+    }
+  }
+
   // Epilogue in four rounds of 32 rows: the wavefronts holding those rows put
   // them (row scales undone) in an fp32 LDS tile [32][256] (columns
   // XOR-swizzled by 16 * ((row / 4) % 4)), then the workgroup writes whole
   // rows.
   float* otile = reinterpret_cast<float*>(st0);
   auto tix = [](int rr, int c) { return rr * kTN + (c ^ (16 * ((rr >> 2) & 3))); };
-  for (int round = 0; round < 4; ++round) {
+#pragma unroll
+  for (int round = 0; round < 4; ++round) {  // unrolled: acc is indexed by round
     if (wm == round >> 1) {
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2)
@@ -403,6 +485,77 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
         const int rr = idx / (kTN / 4), c = 4 * (idx % (kTN / 4));
         if (n0 + c < g.N)
           *(f32x4*)(g.slot_out + (long)s_orow[r0 + rr] * g.N + n0 + c) = *(const f32x4*)(otile + tix(rr, c));
+      }
+    } else if (g.seg_scale != nullptr) {
+      // FC2 operand rows as f16 hi/lo groups of v * 2^e (the layout of the
+      // operand split): this tile's codes are one segment of FC2's
+      // reduction.  A thread takes one 8-code group; the groups of a row are
+      // consecutive lanes.  e = tile_e unless the row's largest magnitude m
+      // in the segment is nonzero and more than 2^12 below the tile's bound
+      // (row_exp(m) - tile_e > 12, i.e. 0 < m < 2^(1 - tile_e)), or nonzero
+      // in a tile of magnitudes from 2^113 on: then e = row_exp(m), the
+      // row's own, and the flag goes up, so that FC2 takes the rows back to
+      // one exponent each.  Lane masks decide it; only a wavefront holding
+      // such a row reduces m across lanes.
+      constexpr bool swiglu = EPI == EPI_SWIGLU;
+      const int I = swiglu ? g.N / 2 : g.N;
+      constexpr int jw = swiglu ? kTN / 2 : kTN;  // codes of this tile
+      constexpr int GR = jw / 8;                  // 8-code groups a row
+      static_assert(GR <= 64 && (64 % GR) == 0, "a row's groups lie in one wavefront");
+      const int jbase = swiglu ? n0 / 2 : n0;
+      const float thr = __builtin_ldexpf(1.f, 1 - tile_e);
+#pragma unroll
+      for (int b = 0; b < 32 * GR; b += kTThreads) {
+        const int idx = b + tid;
+        const int rr = idx / GR, gq = idx % GR;
+        const int j0 = jbase + 8 * gq;
+        float v[8];
+        if constexpr (swiglu) {
+          const int t0 = 2 * (j0 - jbase);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const f32x4 u = *(const f32x4*)(otile + tix(rr, t0 + 4 * h));
+            v[2 * h] = swiglu_act(u[0], u[1], g.alpha, g.beta, g.limit);
+            v[2 * h + 1] = swiglu_act(u[2], u[3], g.alpha, g.beta, g.limit);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x4 u = *(const f32x4*)(otile + tix(rr, j0 - jbase + 4 * h));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[4 * h + c] = fmaxf(u[c], 0.f);
+          }
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (j0 + c >= I) v[c] = 0.f;
+          m = fmaxf(m, fabsf(v[c]));
+        }
+        const unsigned long long rowm = (GR == 64 ? ~0ull : ((1ull << GR) - 1)) << (lane & (64 - GR));
+        const unsigned long long big = __ballot(m >= thr), nz = __ballot(m > 0.f);
+        const bool own = (nz & rowm) != 0 && (tile_own || (big & rowm) == 0);
+        int e = tile_e;
+        if (__ballot(own) != 0) {
+          const float mr = seg_max<GR>(m);
+          if (own) e = row_exp(mr);
+        }
+        if (rr < rlim) {
+          const long prow = (long)(p0 + r0 + rr);
+          if (j0 < I) {
+            f16x8 hi, lo;
+            split_group<BITS>(v, e, hi, lo);
+            const int q = j0 / 8;  // code group; 8-bit rows keep group sigma(q % 4) of a 32-code block
+            const int sgrp = BITS == 4 ? q : ((q & ~3) | sigma8(q & 3));
+            uint8_t* dst = g.act + prow * g.act_stride + (long)sgrp * 32;
+            *(f16x8*)dst = hi;
+            *(f16x8*)(dst + 16) = lo;
+          }
+          if (gq == 0) {
+            g.seg_rows[(long)ntile * g.S + prow] = e;
+            if (own) *g.seg_flag = 1;
+          }
+        }
       }
     } else {
       // fp32 FC2 operand rows (natural code order) for this tile's codes,
@@ -438,12 +591,13 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
 
 #undef QMOE_GLOBAL
 #undef QMOE_LOCAL
+#undef QMOE_INLINE
 
 namespace {
 
-template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT>
+template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT, bool SEG = false>
 hipError_t go_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
-  auto kern = qmoe_tiled<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT>;
+  auto kern = qmoe_tiled<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT, SEG>;
   hipLaunchKernelGGL(kern, dim3(max_tiles * ntn), dim3(kTThreads), 0, st, g, ntn);
   return hipGetLastError();
 }
@@ -453,6 +607,22 @@ hipError_t go_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
 // than folding every step, and no pipeline drain of a fold at block ends.
 template <int BITS, int EPI>
 hipError_t pick_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
+  if (g.seg_scale != nullptr) {
+    if constexpr (EPI == EPI_STORE) {
+      // FC2: whole spans (two K steps with column scales), each within one
+      // segment of at least 128 codes
+      if (g.seg_shift < 7 || (g.bs == 0 && g.K % (2 * kTK) != 0)) return hipErrorInvalidValue;
+      if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI, true, 2, true>(g, max_tiles, ntn, st);
+      if (g.bs == 32) return go_tiled<BITS, SC_BLOCK, EPI, true, 0, true>(g, max_tiles, ntn, st);
+      if (g.bs == 64) return go_tiled<BITS, SC_BLOCK, EPI, true, 1, true>(g, max_tiles, ntn, st);
+      return go_tiled<BITS, SC_BLOCK, EPI, true, 2, true>(g, max_tiles, ntn, st);
+    } else {
+      // FC1: a segment is the codes of one column tile, seg_n of them a row
+      const int codes = EPI == EPI_SWIGLU ? kTN / 2 : kTN;
+      if ((1 << g.seg_shift) != codes || g.seg_n != ntn || g.seg_rows == nullptr || g.seg_flag == nullptr)
+        return hipErrorInvalidValue;
+    }
+  }
   if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI, false, 0>(g, max_tiles, ntn, st);
   if (g.bs == 32) return go_tiled<BITS, SC_BLOCK, EPI, true, 0>(g, max_tiles, ntn, st);
   if (g.bs == 64) return go_tiled<BITS, SC_BLOCK, EPI, true, 1>(g, max_tiles, ntn, st);

@@ -119,8 +119,13 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     int* exp2 = reinterpret_cast<int*>(ws + p.off_exp2);
     const float* x = static_cast<const float*>(input->data);
     const bool a_f32 = p.s1.on;
+    // segment scales between the tiled GEMMs (the flag starts each call at
+    // zero: the FC1 operand split clears it)
+    float* seg = reinterpret_cast<float*>(ws + p.off_seg);
+    int* segrows = reinterpret_cast<int*>(ws + p.off_segrows);
+    int* segflag = p.seg_n > 0 ? reinterpret_cast<int*>(ws + p.off_segflag) : nullptr;
     if (!a_f32)
-      QMOE_TRY_HIP(launch_split_rows(d.bits, x, H, H, xa, 4 * (long)p.kp1, (int)p.kp1, T, exp1, s));
+      QMOE_TRY_HIP(launch_split_rows(d.bits, x, H, H, xa, 4 * (long)p.kp1, (int)p.kp1, T, exp1, s, nullptr, segflag));
     else if (!p.s1.one)
       QMOE_TRY_HIP(launch_row_exp(x, H, T, H, exp1, s));
     QMOE_TRY_HIP(mark(1));
@@ -166,19 +171,31 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
                                 s));
       }
     } else if (p.tiled) {
+      if (p.seg_n > 0) {
+        g1.seg_scale = seg;
+        g1.seg_rows = segrows;
+        g1.seg_flag = segflag;
+        g1.seg_n = p.seg_n;
+        g1.seg_shift = p.seg_shift;
+      }
       QMOE_TRY_HIP(launch_tiled(d.bits, epi1, g1, (int)p.max_tiles, s));
       QMOE_TRY_HIP(mark(2));
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, epi1, p.mt, p.aligned, g1, (int)p.max_tiles, s));
       QMOE_TRY_HIP(mark(2));
     }
-    // Operand rows of FC2: FC1 left fp32 rows (stride kp2 codes).  The
-    // streaming FC2 splits them while staging; the other GEMMs take them as
-    // hi/lo rows, converted here in place.
+    // Operand rows of FC2: FC1 left fp32 rows (stride kp2 codes), or with
+    // segment scales the hi/lo rows themselves.  The streaming FC2 splits
+    // fp32 rows while staging; the other GEMMs take them as hi/lo rows,
+    // converted here in place.
     float* act32 = reinterpret_cast<float*>(act);
     // (a share: only the sorted positions of held experts' slots, the first
     // offsets[El], have rows)
-    if (!p.s2.on)
+    if (p.seg_n > 0) {
+      // only when FC1 flagged a row: back to one exponent a row (exp2)
+      QMOE_TRY_HIP(launch_resplit_rows(d.bits, act, 4 * (long)p.kp2, I, S, segrows, p.seg_shift, exp2, segflag, s,
+                                       p.share ? offsets + El : nullptr));
+    } else if (!p.s2.on)
       QMOE_TRY_HIP(launch_split_rows(d.bits, act32, p.kp2, I, act, 4 * (long)p.kp2, (int)p.kp2, S, exp2, s,
                                      p.share ? offsets + El : nullptr));
     else if (!p.s2.one)
@@ -210,6 +227,20 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
       g2.nst = p.s2.nst;
       QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.one, p.s2.splits, p.s2.wg_rows, p.half ? p.s2.stg : 0, g2, (int)p.max_tiles, s));
     } else if (p.tiled) {
+      if (p.seg_n > 0) {
+        // the segment-scale FC2 unless FC1 flagged a row, else the per-row one
+        // (each launch's workgroups exit at once when it is not its turn)
+        GemmArgs gs = g2;
+        gs.a_exp = nullptr;
+        gs.seg_scale = seg;
+        gs.seg_n = p.seg_n;
+        gs.seg_shift = p.seg_shift;
+        gs.gate = segflag;
+        gs.gate_on = 0;
+        QMOE_TRY_HIP(launch_tiled(d.bits, EPI_STORE, gs, (int)p.max_tiles, s));
+        g2.gate = segflag;
+        g2.gate_on = 1;
+      }
       QMOE_TRY_HIP(launch_tiled(d.bits, EPI_STORE, g2, (int)p.max_tiles, s));
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
@@ -349,11 +380,11 @@ qmoe_status qmoe_plan_describe(const qmoe_tensor* input, const qmoe_tensor* rout
   const bool ffn = d.T > 0 && d.I > 0 && d.El > 0;
   std::snprintf(buf, len,
                 "fc1=%s fc2=%s front=%s tile_rows=%lld max_tiles=%lld share=%d "
-                "s1=%d:%d:%d:%d:%d s2=%d:%d:%d:%d:%d workspace=%zu",
+                "s1=%d:%d:%d:%d:%d s2=%d:%d:%d:%d:%d segments=%d segflag=%zu workspace=%zu",
                 ffn ? gemm(p.s1) : "none", ffn ? gemm(p.s2) : "none",
                 p.small_front ? "one-workgroup" : "kernels", (long long)p.bm, (long long)p.max_tiles, p.share ? 1 : 0,
                 p.s1.one, p.s1.stg, p.s1.nst, p.s1.splits, p.s1.wg_rows, p.s2.one, p.s2.stg, p.s2.nst,
-                p.s2.splits, p.s2.wg_rows, p.bytes);
+                p.s2.splits, p.s2.wg_rows, p.seg_n, p.off_segflag, p.bytes);
   return QMOE_OK;
 }
 

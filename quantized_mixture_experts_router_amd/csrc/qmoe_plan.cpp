@@ -97,6 +97,13 @@ int stream_items_override(int gemm) {
   return s == "1" ? 1 : s == "4" ? 4 : s == "8" ? 8 : 0;
 }
 
+// QMOE_TILED_SEGMENTS=0 keeps the per-row operand split between the tiled
+// GEMMs (for measurement and tests); anything else: the plan's own choice.
+bool segments_off() {
+  const char* v = std::getenv("QMOE_TILED_SEGMENTS");
+  return v && std::string(v) == "0";
+}
+
 int path_override() {
   const char* v = std::getenv("QMOE_PATH");
   if (!v) return PATH_AUTO;
@@ -368,6 +375,15 @@ void make_plan(const Dims& d, Plan* p) {
   // With I == 0 only the routing stages run (output is a zero fill).
   p->kp1 = d.I > 0 ? round_up(d.H, 128) : 0;
   p->kp2 = round_up(d.I, 128);
+  // Segment scales between the tiled GEMMs: FC1's epilogue writes FC2's
+  // hi/lo operand rows itself with one power-of-two scale per row tile and
+  // column tile, so no split pass runs between them.  Every span FC2 folds
+  // (a scale block of up to 128 codes, or two 64-code steps with
+  // column-wise scales) lies in one FC1 column tile.
+  if (p->tiled && (d.bs != 0 || d.I % 128 == 0) && !segments_off()) {
+    p->seg_shift = d.act == QMOE_ACT_SWIGLU ? 7 : 8;  // codes of an FC1 column tile of 256 columns
+    p->seg_n = (int)((d.I + (int64_t(1) << p->seg_shift) - 1) >> p->seg_shift);
+  }
   p->aligned = (d.H % 8 == 0) && (d.I % 8 == 0);
   p->nchunks = (p->S + p->chunk - 1) / p->chunk;
   // a share permutes over El + 1 groups (the last: slots of experts not held)
@@ -397,6 +413,9 @@ void make_plan(const Dims& d, Plan* p) {
   p->off_act = take(size_t(4) * p->S * p->kp2);   // fp32 per element, or f16 hi + lo after the split pass
   p->off_exp1 = take(sizeof(int32_t) * d.T);
   p->off_exp2 = take(sizeof(int32_t) * p->S);
+  p->off_seg = take(sizeof(float) * p->max_tiles * p->seg_n);
+  p->off_segrows = take(sizeof(int32_t) * p->S * p->seg_n);
+  p->off_segflag = take(p->seg_n > 0 ? sizeof(int32_t) : 0);
   p->off_local = take(p->share ? sizeof(int32_t) * p->S : 0);
   p->off_slot = take(d.I > 0 ? sizeof(float) * p->splits2 * p->S * d.H : 0); // FC2 rows by slot id
   p->off_part1 = take(p->s1.on && p->s1.splits > 1 ? sizeof(float) * p->s1.splits * p->S * d.F : 0);

@@ -58,6 +58,11 @@ struct Plan {
   int64_t S = 0;         // slots = T * k
   bool decode = false;   // weight-streaming path (every expert's rows fit one M tile)
   bool tiled = false;    // LDS-tiled GEMMs (128-row tiles) for both FC1 and FC2
+  // tiled, segment scales: the FC1 epilogue writes FC2's hi/lo operand rows
+  // itself, one power-of-two scale per row tile and FC1 column tile
+  // (2^seg_shift codes), seg_n segments a row; 0: fp32 rows split per row
+  // afterwards
+  int seg_n = 0, seg_shift = 0;
   int mt = 1;            // 16-row M subtiles per tile
   int64_t bm = 16;       // rows per M tile
   int64_t max_tiles = 0; // ceil(S / bm) + E
@@ -84,6 +89,11 @@ struct Plan {
   size_t off_topk_idx = 0, off_topk_w = 0, off_counts = 0, off_offsets = 0, off_perm = 0;
   size_t off_tiles = 0, off_ntiles = 0, off_hist = 0, off_xa = 0, off_act = 0, off_slot = 0;
   size_t off_exp1 = 0, off_exp2 = 0;  // row scale exponents of the FC1 [T] and FC2 [S] operand rows
+  // segment scales: f32 [max_tiles][seg_n] (2^-e of each row tile and
+  // segment), i32 [seg_n][S] (the exponent each row segment was written
+  // with), i32 flag (a row kept its own exponent: FC2 rows go back to one
+  // exponent a row)
+  size_t off_seg = 0, off_segrows = 0, off_segflag = 0;
   size_t off_local = 0;  // share: local expert of every slot [S] (El = not held)
   size_t bytes = 0;
 };

@@ -23,7 +23,8 @@ def to_dev(arrs, torch):
     return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in arrs.items()}
 
 
-def run_gpu(arrs, attrs, torch, debug=True, stream=None):
+def run_gpu(arrs, attrs, torch, debug=True, stream=None, keep_ws=False):
+    """keep_ws: also return the workspace bytes after the call (res["ws"])."""
     d = to_dev(arrs, torch)
     T = int(np.prod(arrs["input"].shape[:-1]))
     E = arrs["fc1_experts_weights"].shape[0]  # experts the weights hold (counts/offsets are over them)
@@ -45,6 +46,8 @@ def run_gpu(arrs, attrs, torch, debug=True, stream=None):
     qm.forward(*args, attrs, output=out, debug=dbg, stream=stream, workspace=ws)
     torch.cuda.synchronize()
     res = {"out": out.cpu().numpy()}
+    if keep_ws:
+        res["ws"] = ws.cpu().numpy()
     if dbg:
         res.update({kk: v.cpu().numpy() for kk, v in dbg.items()})
     return res

@@ -165,6 +165,9 @@ void check_plan(const qmoe::Dims& d, const qmoe::Plan& p) {
       {p.off_act, 4 * (size_t)(S * p.kp2), "act"},
       {p.off_exp1, 4 * (size_t)d.T, "exp1"},
       {p.off_exp2, 4 * (size_t)S, "exp2"},
+      {p.off_seg, 4 * (size_t)p.max_tiles * p.seg_n, "seg"},
+      {p.off_segrows, 4 * (size_t)S * p.seg_n, "segrows"},
+      {p.off_segflag, p.seg_n > 0 ? (size_t)4 : 0, "segflag"},
       {p.off_slot, d.I > 0 ? sizeof(float) * p.splits2 * S * d.H : 0, "slot"},
       {p.off_part1, stream_part, "part1"},
       {p.off_trows, p.s1.on || p.s2.on ? 4 * (size_t)(p.max_tiles * p.bm) : 0, "trows"},
@@ -195,6 +198,14 @@ void check_plan(const qmoe::Dims& d, const qmoe::Plan& p) {
   split_ok(p.s1, d.H, "FC1");
   split_ok(p.s2, d.I, "FC2");
   EXPECT(!p.small_front || (!p.share && S <= 1024 && d.E <= 1024), "small front end");
+  // segment scales: tiled GEMMs whose FC2 spans (a scale block, or 128
+  // codes with column scales) lie in one FC1 column tile; one segment per
+  // column tile
+  if (p.seg_n > 0) {
+    EXPECT(p.tiled && (d.bs != 0 || d.I % 128 == 0), "segments on this shape");
+    EXPECT(p.seg_shift == (d.act == QMOE_ACT_SWIGLU ? 7 : 8), "segment shift %d", p.seg_shift);
+    EXPECT(p.seg_n == (d.I + (int64_t(1) << p.seg_shift) - 1) >> p.seg_shift, "segments %d", p.seg_n);
+  }
 }
 
 }  // namespace

@@ -90,6 +90,12 @@ def test_kernel_choice_per_workload():
     assert "tile_rows=8 " in plan and "s1=1:8:1:2:0" in plan and "s2=1:4:1:14:0" in plan
     for name in ("prefill", "fine", "large_e"):
         assert bench.gemm_kernel(W.WORKLOADS[name]) == "qmoe_tiled"
+    # segment scales between the tiled GEMMs: one segment per FC1 column tile
+    # (128 SwiGLU codes, 256 ReLU codes)
+    assert "segments=112 " in bench.plan_of(W.WORKLOADS["prefill"])
+    assert "segments=11 " in bench.plan_of(W.WORKLOADS["fine"])
+    assert "segments=12 " in bench.plan_of(W.WORKLOADS["large_e"])
+    assert "segments=1 " in bench.plan_of(W.WORKLOADS["tiny"])
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1"]) == "qmoe_gmm_f32_rows16"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_fine_fc1"]) == "qmoe_gmm_f32"
 

@@ -16,7 +16,7 @@ from oracle import qmoe_oracle as Q
 from quantized_mixture_experts_router_amd import workloads as W
 
 from conftest import GOLDEN
-from gpu_util import check_output, check_routing, run_gpu, say
+from gpu_util import OUT_TOL, check_output, check_routing, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -414,6 +414,84 @@ def test_tiled_scale_block_spans(torch, bs, bits):
         w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=5, inter=I, k=2, bits=bits, block_size=bs,
                              activation=act)
         _full_check(w, a, torch, f"tiled bs{bs} bits{bits} {act} T{T} H{H} I{I}")
+
+
+# Segment scales between the tiled GEMMs: the FC1 epilogue writes FC2's hi/lo
+# operand rows with one power-of-two scale per row tile and FC1 column tile;
+# a row more than 2^12 below its tile's bound keeps its own exponent, which
+# raises a flag, and FC2 then takes its rows back to one exponent each.
+# (T, H, E, I, k, bits, bs, act, segments a row, FC1 scale factor per
+# segment, extra attributes, decades of spread between token rows[, input
+# scale])
+SEGMENTS = [
+    (300, 512, 4, 384, 2, 4, 128, "swiglu", 3, None, None, 0),
+    (300, 512, 4, 640, 2, 4, 0, "relu", 3, None, None, 0),       # last FC1 column tile half empty
+    (257, 1024, 6, 256, 2, 4, 256, "swiglu", 2, None, None, 0),
+    (300, 512, 3, 512, 2, 4, 128, "swiglu", 4, (1e-4, 1e3, 1.0, 3e-2), None, 0),  # segments far apart
+    (400, 256, 2, 256, 1, 4, 0, "relu", 1, (1e-6,), None, 0),
+    (300, 512, 4, 320, 2, 4, 32, "swiglu", 3, None, None, 0),    # 32-code blocks, a partial column tile
+    (300, 512, 4, 448, 2, 8, 64, "relu", 2, None, None, 0),
+    (300, 512, 4, 384, 2, 8, 0, "swiglu", 3, (1e3, 1e-3, 1.0), None, 0),
+    (260, 256, 3, 256, 2, 8, 128, "swiglu", 2, None, None, 0),
+    (300, 512, 4, 384, 2, 4, 128, "swiglu", 3, None, dict(activation_alpha=1.702, activation_beta=1.0,
+                                                          swiglu_limit=0.05), 0),
+    (300, 512, 4, 384, 2, 4, 128, "swiglu", 3, None, None, 8),   # rows far apart: per-row exponents
+    (300, 512, 4, 640, 2, 8, 0, "relu", 3, None, None, 8),
+    (300, 512, 4, 320, 2, 4, 32, "relu", 2, None, None, 6),
+    (300, 512, 4, 384, 2, 4, 128, "swiglu", 3, None, None, 0, 3e17),  # SwiGLU values past 2^113
+]
+
+
+@pytest.mark.parametrize("case", SEGMENTS)
+def test_tiled_segment_scales(torch, monkeypatch, case):
+    import re
+    import quantized_mixture_experts_router_amd as qm
+    T, H, E, I, k, bits, bs, act, nseg, factors, extra, spread = case[:12]
+    xscale = case[12] if len(case) > 12 else 1.0
+    rng = np.random.default_rng(1700 + T + I + bs + bits + spread)
+    w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=E, inter=I, k=k, bits=bits, block_size=bs,
+                         activation=act)
+    if factors:
+        # FC1 columns of segment t (256 of them, the interleaved gate/linear
+        # pairs of 128 codes with SwiGLU) scaled by factors[t]
+        s1 = a["fc1_scales"].copy()
+        for t, f in enumerate(factors):
+            s1[:, 256 * t:256 * (t + 1)] *= np.float32(f)
+        a["fc1_scales"] = s1
+    if spread:
+        a["input"] = (a["input"] * 10.0 ** rng.uniform(-spread, 0, size=(T, 1))).astype(np.float32)
+    if xscale != 1.0:
+        a["input"] = (a["input"].astype(np.float64) * xscale).astype(np.float32)
+    attrs = dict(w.attrs(), **(extra or {}))
+    label = (f"segments T{T} H{H} E{E} I{I} k{k} bits{bits} bs{bs} {act} factors={factors} {extra} spread={spread} "
+             f"x{xscale:g}")
+    for off in (False, True):
+        # segment scales, then the per-row split between the GEMMs
+        if off:
+            monkeypatch.setenv("QMOE_TILED_SEGMENTS", "0")
+        else:
+            monkeypatch.delenv("QMOE_TILED_SEGMENTS", raising=False)
+        plan = qm.qmoe_plan_describe(*a.values(), attrs=attrs)
+        assert "fc1=tiled fc2=tiled" in plan and f"segments={0 if off else nseg} " in plan, plan
+        say(f"[case] {label} {'per-row split' if off else ''}")
+        res = run_gpu(a, attrs, torch, keep_ws=not off)
+        ref, inter = oracle.qmoe(*a.values(), attrs=attrs, return_intermediates=True)
+        check_routing(res, inter["sel"], inter["w"], inter["counts"], inter["offsets"], inter["perm"])
+        assert np.all(np.isfinite(res["out"])), f"{label}: non-finite output"
+        if spread or xscale != 1.0:
+            # the bar per token row: a small row is held to its own magnitude
+            out = res["out"].reshape(T, H).astype(np.float64)
+            ref2 = np.asarray(ref, dtype=np.float64).reshape(T, H)
+            err = np.max(np.abs(out - ref2), axis=1)
+            rms = np.sqrt(np.mean(ref2 ** 2, axis=1))
+            assert np.all(err <= OUT_TOL * rms), f"{label}: worst row {np.max(err / rms)}"
+        else:
+            check_output(res["out"], ref, label)
+        if not off:
+            # which FC2 ran: the flag FC1 raises for rows far below their tile
+            at = int(re.search(r"segflag=(\d+)", plan).group(1))
+            flag = int(res["ws"][at:at + 4].view(np.int32)[0])
+            assert flag == (1 if spread or xscale > 1e16 else 0), f"{label}: flag {flag}"
 
 
 @pytest.mark.parametrize("case", [
