@@ -79,12 +79,11 @@ struct GemmArgs {
   // FC1 with segment scales: a row whose largest magnitude in the segment is
   // more than 2^12 below the tile's bound keeps its own exponent instead
   // (and sets *seg_flag); seg_rows [seg_n][S] gets the exponent each row
-  // segment was written with
+  // segment was written with.  FC2 with segment scales reads *seg_flag: when
+  // set, its rows carry one exponent each again (a_exp) and the segment
+  // factors are not applied.
   int* seg_rows;
   int* seg_flag;
-  // the kernel runs only when (gate[0] != 0) == (gate_on != 0); nullptr: always
-  const int* gate;
-  int gate_on;
   long act_stride;
   float* slot_out;      // FC2 output [splits][S][N] by slot id
   const int* perm;      // FC2: sorted position -> slot

@@ -102,7 +102,9 @@ __device__ __forceinline__ void wait_vm() {
 // one per row.  A span never straddles a segment, so the segment's factor
 // g.seg_scale joins the span's block scales when the span closes (with
 // column-wise scales the spans are two K steps, folded with that factor
-// alone).
+// alone).  When FC1 raised *g.seg_flag the rows were taken back to one
+// exponent each (g.a_exp): the factors are then 1 and the epilogue undoes
+// the row exponents as without SEG.
 template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT, bool SEG = false>
 __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   static_assert(!SEG || (EPI == EPI_STORE && STEPFOLD && (SCALE == SC_BLOCK || STEPFOLD_KT == 2)),
@@ -123,7 +125,6 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   // sized for the most tiles routing can produce; only the first
   // ntiles * ntn linear ids carry work, and they are the ones dealt out, so
   // every XCD gets its share of the real tiles.
-  if (g.gate != nullptr && (g.gate[0] != 0) != (g.gate_on != 0)) return;
   const int mtiles = g.ntiles[0];
   const int total = mtiles * ntn;
   const int lin = blockIdx.x;
@@ -152,7 +153,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     const long ar = g.a_map ? (long)(g.a_map[p] / g.a_div) : (long)p;
     s_arow[tid] = ar * g.a_stride;
     s_orow[tid] = g.store_by_slot ? g.perm[p] : p;
-    s_rexp[tid] = SEG ? 0 : g.a_exp[ar];
+    s_rexp[tid] = (SEG && g.seg_flag[0] == 0) ? 0 : g.a_exp[ar];
   }
   __syncthreads();
 
@@ -254,6 +255,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   // through the scalar cache)
   const __attribute__((address_space(4))) float* segs =
       SEG ? (const __attribute__((address_space(4))) float*)(g.seg_scale + (long)tile * g.seg_n) : nullptr;
+  const bool segrow = SEG && g.seg_flag[0] != 0;  // rows back to one exponent each: factors 1
   // Fragment tick of half j of the step in buffer base: the packed weight
   // words of the wavefront's four column subtiles, the activation hi/lo
   // fragments of its four row subtiles and the closing span's scales come
@@ -272,7 +274,10 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     float nsc[4] = {1.f, 1.f, 1.f, 1.f};
     float fseg = 1.f;
     if constexpr (SEG) {
-      if (close) fseg = segs[(kt * kTK) >> g.seg_shift];
+      if (close) {
+        const float f = segs[(kt * kTK) >> g.seg_shift];
+        fseg = segrow ? 1.f : f;
+      }
     }
     if constexpr (SCALE == SC_BLOCK) {
       if (close) {
@@ -611,7 +616,8 @@ hipError_t pick_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st)
     if constexpr (EPI == EPI_STORE) {
       // FC2: whole spans (two K steps with column scales), each within one
       // segment of at least 128 codes
-      if (g.seg_shift < 7 || (g.bs == 0 && g.K % (2 * kTK) != 0)) return hipErrorInvalidValue;
+      if (g.seg_shift < 7 || (g.bs == 0 && g.K % (2 * kTK) != 0) || g.seg_flag == nullptr || g.a_exp == nullptr)
+        return hipErrorInvalidValue;
       if (g.bs == 0) return go_tiled<BITS, SC_COL, EPI, true, 2, true>(g, max_tiles, ntn, st);
       if (g.bs == 32) return go_tiled<BITS, SC_BLOCK, EPI, true, 0, true>(g, max_tiles, ntn, st);
       if (g.bs == 64) return go_tiled<BITS, SC_BLOCK, EPI, true, 1, true>(g, max_tiles, ntn, st);

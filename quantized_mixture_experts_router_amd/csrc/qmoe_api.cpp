@@ -228,18 +228,12 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
       QMOE_TRY_HIP(launch_stream(d.bits, p.mt, p.s2.one, p.s2.splits, p.s2.wg_rows, p.half ? p.s2.stg : 0, g2, (int)p.max_tiles, s));
     } else if (p.tiled) {
       if (p.seg_n > 0) {
-        // the segment-scale FC2 unless FC1 flagged a row, else the per-row one
-        // (each launch's workgroups exit at once when it is not its turn)
-        GemmArgs gs = g2;
-        gs.a_exp = nullptr;
-        gs.seg_scale = seg;
-        gs.seg_n = p.seg_n;
-        gs.seg_shift = p.seg_shift;
-        gs.gate = segflag;
-        gs.gate_on = 0;
-        QMOE_TRY_HIP(launch_tiled(d.bits, EPI_STORE, gs, (int)p.max_tiles, s));
-        g2.gate = segflag;
-        g2.gate_on = 1;
+        // segment factors, or (when FC1 flagged a row) the per-row exponents
+        // the re-split pass wrote
+        g2.seg_scale = seg;
+        g2.seg_flag = segflag;
+        g2.seg_n = p.seg_n;
+        g2.seg_shift = p.seg_shift;
       }
       QMOE_TRY_HIP(launch_tiled(d.bits, EPI_STORE, g2, (int)p.max_tiles, s));
     } else {
