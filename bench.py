@@ -253,9 +253,17 @@ def traffic_for(key, kernel, plan=None):
     ent = rec.get(key)
     if not ent or ent.get("kernel") != kernel:
         return None
-    if ent.get("source_sha") != _sha(KERNEL_SRC[kernel]) or ent.get("plan") != plan:
+    if ent.get("source_sha") != _sha(KERNEL_SRC[kernel]) or launch_fields(ent.get("plan")) != launch_fields(plan):
         return None
     return ent.get("bytes")
+
+
+def launch_fields(plan):
+    """A plan description without its workspace layout (the total size and
+    the offset of the segment flag), which moves no HBM bytes."""
+    if plan is None:
+        return None
+    return " ".join(t for t in plan.split() if not t.startswith(("workspace=", "segflag=")))
 
 
 def copy_calibration(nbytes, reps=3):

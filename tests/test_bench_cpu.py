@@ -113,5 +113,8 @@ def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
     assert bench.traffic_for("decode:fc2", "qmoe_stream", plan) is None      # never measured
     assert bench.traffic_for("decode:fc1", "qmoe_tiled", plan) is None       # another kernel
     assert bench.traffic_for("decode:fc1", "qmoe_stream", "fc1=stream s1=1:4:1:8:0") is None  # another plan
+    # the workspace layout moves no bytes: a record stays valid across it
+    assert bench.traffic_for("decode:fc1", "qmoe_stream", plan + " segflag=512 workspace=4096") == 123
+    assert bench.traffic_for("decode:fc1", "qmoe_stream", plan + " segments=3 workspace=4096") is None
     src.write_text("// kernel source, changed\n")
     assert bench.traffic_for("decode:fc1", "qmoe_stream", plan) is None      # source changed since
