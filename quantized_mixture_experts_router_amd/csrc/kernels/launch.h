@@ -10,16 +10,18 @@ hipError_t launch_router(const float* logits, int T, int E, int k, int routing, 
 
 // Router, counts, offsets, tile table and stable permutation in one launch
 // (T * k <= 1024 and E <= 1024); with trows given, also the tile-row table
-// (see launch_tile_rows).
+// (see launch_tile_rows).  split (the LDS-tiled GEMMs): each expert's last
+// tile of at most bm / 2 rows goes after all the other tiles, and
+// ntiles[1] = the count of the others (no tile-row table then).
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int routing, int normalize, int bm,
                               int* topk_idx, float* topk_w, int* counts, int* offsets, int* perm, int* tiles,
-                              int* ntiles, int* trows, hipStream_t st);
+                              int* ntiles, int* trows, hipStream_t st, int split = 0);
 
 // Counts, offsets, stable permutation and M-tile table over E groups; only
-// the first tile_groups groups (all when negative) get tiles.
+// the first tile_groups groups (all when negative) get tiles; split as above.
 hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchunks, int bm, int* hist,
                           int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st,
-                          int tile_groups = -1);
+                          int tile_groups = -1, int split = 0);
 
 // A share of the experts: local[s] = topk_idx[s] - first for the experts
 // [first, first + El) the weights hold, else El.
@@ -62,7 +64,8 @@ struct GemmArgs {
   int a_div;            // FC1: k (slot -> token)
   long a_stride;
   const int* tiles;     // [max_tiles][4] = expert, first position, rows, 0
-  const int* ntiles;
+  const int* ntiles;    // [0] = tiles; [1] (split_small) = tiles before the small ones
+  int split_small;      // tiled GEMMs: the table ends with tiles of at most 64 rows (half tiles)
   int N, K, kb, nblk, bs;
   int store_by_slot;     // stream kernel: partial rows by slot id (1) or by sorted position (0)
   int S;                 // slots (stride between split partials, in rows)

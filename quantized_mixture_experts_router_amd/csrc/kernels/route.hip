@@ -124,64 +124,93 @@ __global__ void __launch_bounds__(256) qmoe_hist(const int* __restrict__ topk_id
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
+// Tile split (the LDS-tiled GEMMs): an expert's last tile with at most
+// bm / 2 rows is small.  Small tiles go after all the others, in expert
+// order, and ntiles[1] = the count of the others.
+__device__ __forceinline__ int small_tile(int c, int nt, int bm, int split) {
+  return (split && nt > 0 && c - (nt - 1) * bm <= bm / 2) ? 1 : 0;
+}
+
+// Tile i (< nt) of expert e with first sorted position off_e: written at its
+// place in the table (big tiles from tileb0, the small one at small_at).
+__device__ __forceinline__ void write_expert_tiles(int e, int c, int nt, int small, int bm, int off_e, int tileb0,
+                                                   int small_at, int* __restrict__ tiles) {
+  for (int i = 0; i < nt; ++i) {
+    int* tp = tiles + 4 * (small && i == nt - 1 ? small_at : tileb0 + i);
+    tp[0] = e;
+    tp[1] = off_e + i * bm;
+    tp[2] = min(bm, c - i * bm);
+    tp[3] = 0;
+  }
+}
+
 // Block-wide (1024 threads, thread e = expert e < E <= 1024): given each
 // expert's slot count c, write counts, exclusive offsets and the M-tile table
-//   tiles[4*i .. 4*i+3] = (expert, first sorted position, rows, 0), ntiles[0] = count;
-// returns the expert's first sorted position (and in *first_tile its first tile).
-// Only the first tile_groups groups get tiles (a share of the experts: the
-// last group holds the slots of experts the weights do not hold).
+//   tiles[4*i .. 4*i+3] = (expert, first sorted position, rows, 0), ntiles[0] = count
+// (with split, small tiles last and ntiles[1] = the count of the others);
+// returns the expert's first sorted position (and in *first_tile its first
+// tile; without split).  Only the first tile_groups groups get tiles (a share
+// of the experts: the last group holds the slots of experts the weights do
+// not hold).
 __device__ __forceinline__ int scan_experts(int c, int E, int S, int bm, int* __restrict__ counts,
                                             int* __restrict__ offsets, int* __restrict__ tiles,
                                             int* __restrict__ ntiles, int* first_tile = nullptr,
-                                            int tile_groups = 1 << 30) {
+                                            int tile_groups = 1 << 30, int split = 0) {
   __shared__ int s_warp[16];
   __shared__ int s_warp2[16];
+  __shared__ int s_warp3[16];
+  __shared__ int s_tot[2];
   const int e = threadIdx.x;
   if (e < E) counts[e] = c;
   const int nt = threadIdx.x < tile_groups ? (c + bm - 1) / bm : 0;
-  // Inclusive scans of counts and tile counts (wave scan, then wave totals).
-  int inc = c, inct = nt;
+  const int sm = small_tile(c, nt, bm, split);
+  // Inclusive scans of counts, big-tile counts and small-tile counts (wave
+  // scan, then wave totals).
+  int inc = c, inct = nt - sm, incs = sm;
   const int lane = lane_id(), w = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int a = __shfl_up(inc, off);
     const int b = __shfl_up(inct, off);
+    const int d = __shfl_up(incs, off);
     if (lane >= off) {
       inc += a;
       inct += b;
+      incs += d;
     }
   }
   if (lane == 63) {
     s_warp[w] = inc;
     s_warp2[w] = inct;
+    s_warp3[w] = incs;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int a = 0, b = 0;
+    int a = 0, b = 0, d = 0;
     for (int i = 0; i < 16; ++i) {
-      const int x = s_warp[i], y = s_warp2[i];
+      const int x = s_warp[i], y = s_warp2[i], z = s_warp3[i];
       s_warp[i] = a;
       s_warp2[i] = b;
+      s_warp3[i] = d;
       a += x;
       b += y;
+      d += z;
     }
+    s_tot[0] = b;
+    s_tot[1] = d;
   }
   __syncthreads();
   const int off_e = inc - c + s_warp[w];
-  const int tile0 = inct - nt + s_warp2[w];
+  const int tile0 = inct - (nt - sm) + s_warp2[w];
+  const int nbig = s_tot[0];
   if (e < E) {
     offsets[e] = off_e;
-    for (int i = 0; i < nt; ++i) {
-      int* tp = tiles + 4 * (tile0 + i);
-      tp[0] = e;
-      tp[1] = off_e + i * bm;
-      tp[2] = min(bm, c - i * bm);
-      tp[3] = 0;
-    }
+    write_expert_tiles(e, c, nt, sm, bm, off_e, tile0, nbig + incs - sm + s_warp3[w], tiles);
   }
   if (e == E - 1) {
     offsets[E] = S;
-    ntiles[0] = tile0 + nt;
+    ntiles[0] = nbig + s_tot[1];
+    if (split) ntiles[1] = nbig;
   }
   if (first_tile) *first_tile = tile0;
   return off_e;
@@ -204,7 +233,7 @@ __device__ __forceinline__ void write_tile_rows(const int* perm, int off_e, int 
 __global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nchunks, int E, int S, int bm,
                                                   int* __restrict__ counts, int* __restrict__ offsets,
                                                   int* __restrict__ tiles, int* __restrict__ ntiles,
-                                                  int tile_groups) {
+                                                  int tile_groups, int split) {
   const int e = threadIdx.x;
   int c = 0;
   // eight chunks' counts in flight at a time (one round trip per eight)
@@ -221,7 +250,7 @@ __global__ void __launch_bounds__(1024) qmoe_scan(int* __restrict__ hist, int nc
         }
     }
   }
-  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles, nullptr, tile_groups);
+  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles, nullptr, tile_groups, split);
   if (e < E)
     for (int ch0 = 0; ch0 < nchunks; ch0 += 8) {
       int v[8];
@@ -294,7 +323,8 @@ __global__ void __launch_bounds__(1024) qmoe_route_small(const float* __restrict
                                                          int* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                          int* __restrict__ counts, int* __restrict__ offsets,
                                                          int* __restrict__ perm, int* __restrict__ tiles,
-                                                         int* __restrict__ ntiles, int* __restrict__ trows) {
+                                                         int* __restrict__ ntiles, int* __restrict__ trows,
+                                                         int split) {
   __shared__ int s_idx[1024];
   __shared__ int s_cnt[1024];  // counts, then each expert's next sorted position
   __shared__ int s_perm[1024];
@@ -307,7 +337,7 @@ __global__ void __launch_bounds__(1024) qmoe_route_small(const float* __restrict
   __syncthreads();
   const int c = threadIdx.x < E ? s_cnt[threadIdx.x] : 0;
   int tile0 = 0;
-  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles, &tile0);  // synchronises
+  const int off_e = scan_experts(c, E, S, bm, counts, offsets, tiles, ntiles, &tile0, 1 << 30, split);  // synchronises
   if (threadIdx.x < E) s_cnt[threadIdx.x] = off_e;
   __syncthreads();
   const int nw = (S + 63) / 64;
@@ -333,7 +363,7 @@ __global__ void __launch_bounds__(1024) qmoe_route_small(const float* __restrict
     }
     __syncthreads();
   }
-  if (trows && threadIdx.x < E) write_tile_rows(s_perm, off_e, c, tile0, bm, trows);
+  if (trows && !split && threadIdx.x < E) write_tile_rows(s_perm, off_e, c, tile0, bm, trows);
 }
 
 // The whole front end in one wavefront when every token fits a lane and the
@@ -351,7 +381,7 @@ __global__ void __launch_bounds__(64) qmoe_route_wave(const float* __restrict__ 
                                                       int* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                       int* __restrict__ counts, int* __restrict__ offsets,
                                                       int* __restrict__ perm, int* __restrict__ tiles,
-                                                      int* __restrict__ ntiles, int* __restrict__ trows) {
+                                                      int* __restrict__ ntiles, int* __restrict__ trows, int split) {
   // k <= min(E, 64 / E) <= 8, so S <= 512 slots; with tiles of at least 8
   // rows at most S / 8 + E <= 64 + 64 tiles
   __shared__ int s_cnt[64];
@@ -417,34 +447,36 @@ __global__ void __launch_bounds__(64) qmoe_route_wave(const float* __restrict__ 
   // Counts, exclusive offsets and tile counts of expert e in lane e.
   const int c = lane < E ? s_cnt[lane] : 0;
   const int nt = (c + bm - 1) / bm;
-  int inc = c, inct = nt;
+  const int sm = small_tile(c, nt, bm, split);
+  int inc = c, inct = nt - sm, incs = sm;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int a = __shfl_up(inc, off);
     const int b = __shfl_up(inct, off);
+    const int d = __shfl_up(incs, off);
     if (lane >= off) {
       inc += a;
       inct += b;
+      incs += d;
     }
   }
-  const int off_e = inc - c, tile0 = inct - nt;
-  const int ntot = __shfl(inct, 63);
+  const int off_e = inc - c, tile0 = inct - (nt - sm);
+  const int nbig = __shfl(inct, 63);
+  const int ntot = nbig + __shfl(incs, 63);
   if (lane < E) {
     counts[lane] = c;
     offsets[lane] = off_e;
-    for (int i = 0; i < nt; ++i) {
-      int* tp = tiles + 4 * (tile0 + i);
-      tp[0] = lane;
-      tp[1] = off_e + i * bm;
-      tp[2] = min(bm, c - i * bm);
-      tp[3] = 0;
-      s_tile[2 * (tile0 + i)] = off_e + i * bm;
-      s_tile[2 * (tile0 + i) + 1] = min(bm, c - i * bm);
-    }
+    write_expert_tiles(lane, c, nt, sm, bm, off_e, tile0, nbig + incs - sm, tiles);
+    if (!split)
+      for (int i = 0; i < nt; ++i) {
+        s_tile[2 * (tile0 + i)] = off_e + i * bm;
+        s_tile[2 * (tile0 + i) + 1] = min(bm, c - i * bm);
+      }
   }
   if (lane == 0) {
     offsets[E] = S;
     ntiles[0] = ntot;
+    if (split) ntiles[1] = nbig;
   }
   // Stable scatter: slots of expert e in token order.
   const unsigned long long below = (1ull << lane) - 1ull;
@@ -464,7 +496,7 @@ __global__ void __launch_bounds__(64) qmoe_route_wave(const float* __restrict__ 
   }
   __syncthreads();
   // Tile rows: rows past a tile's count repeat its last row.
-  if (trows)
+  if (trows && !split)
     for (int j = lane; j < ntot * bm; j += 64) {
       const int t = j / bm, r = j - t * bm;
       trows[j] = s_perm[s_tile[2 * t] + min(r, s_tile[2 * t + 1] - 1)];
@@ -510,12 +542,12 @@ hipError_t launch_router(const float* logits, int T, int E, int k, int routing, 
 
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int routing, int normalize, int bm,
                               int* topk_idx, float* topk_w, int* counts, int* offsets, int* perm, int* tiles,
-                              int* ntiles, int* trows, hipStream_t st) {
+                              int* ntiles, int* trows, hipStream_t st, int split) {
   if (T * k > 1024 || E > 1024) return hipErrorInvalidValue;
   if (T <= 64 && E <= 64 && E * k <= 64 && bm >= 8) {
 #define QMOE_ROUTE_WAVE(EVV)                                                                                      \
   hipLaunchKernelGGL(qmoe_route_wave<EVV>, dim3(1), dim3(64), 0, st, logits, T, E, k, routing, normalize, bm,     \
-                     topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows)
+                     topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows, split)
     if (E <= 8) QMOE_ROUTE_WAVE(8);
     else if (E <= 16) QMOE_ROUTE_WAVE(16);
     else if (E <= 32) QMOE_ROUTE_WAVE(32);
@@ -526,7 +558,7 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int rout
   const int V = (E + 63) / 64;
 #define QMOE_ROUTE_SMALL(VV)                                                                                       \
   hipLaunchKernelGGL(qmoe_route_small<VV>, dim3(1), dim3(1024), 0, st, logits, T, E, k, routing, normalize, bm,  \
-                     topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows)
+                     topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows, split)
   if (V <= 1) QMOE_ROUTE_SMALL(1);
   else if (V <= 2) QMOE_ROUTE_SMALL(2);
   else if (V <= 4) QMOE_ROUTE_SMALL(4);
@@ -538,10 +570,10 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int rout
 
 hipError_t launch_permute(const int* topk_idx, int S, int E, int chunk, int nchunks, int bm, int* hist,
                           int* counts, int* offsets, int* perm, int* tiles, int* ntiles, hipStream_t st,
-                          int tile_groups) {
+                          int tile_groups, int split) {
   hipLaunchKernelGGL(qmoe_hist, dim3(nchunks), dim3(256), E * sizeof(int), st, topk_idx, S, E, chunk, hist);
   hipLaunchKernelGGL(qmoe_scan, dim3(1), dim3(1024), 0, st, hist, nchunks, E, S, bm, counts, offsets, tiles, ntiles,
-                     tile_groups < 0 ? E : tile_groups);
+                     tile_groups < 0 ? E : tile_groups, split);
   hipLaunchKernelGGL(qmoe_scatter, dim3(nchunks), dim3(64 * kScatterWaves), (1 + kScatterWaves) * E * sizeof(int), st,
                      topk_idx, hist, S, E, chunk, perm);
   return hipGetLastError();

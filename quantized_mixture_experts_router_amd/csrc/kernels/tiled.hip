@@ -105,37 +105,13 @@ __device__ __forceinline__ void wait_vm() {
 // alone).  When FC1 raised *g.seg_flag the rows were taken back to one
 // exponent each (g.a_exp): the factors are then 1 and the epilogue undoes
 // the row exponents as without SEG.
-template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT, bool SEG = false>
-__global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
-  static_assert(!SEG || (EPI == EPI_STORE && STEPFOLD && (SCALE == SC_BLOCK || STEPFOLD_KT == 2)),
-                "segment scales: FC2, folded spans");
+// The work of one tile: 128 rows x 256 columns, or (HALF) 64 rows x 512
+// columns, staged through the kernel's LDS arrays.
+template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT, bool SEG, bool HALF>
+__device__ __forceinline__ void tiled_tile(const GemmArgs& g, int ntn, int tile, int ntile, uint8_t* st0, uint8_t* st1,
+                                           uint8_t* st2, long* s_arow, int* s_orow, int* s_rexp) {
   using L = TiledLayout<BITS>;
-  // Three stage buffers: a step's operands arrive by direct-to-LDS loads two
-  // steps ahead of their use.
-  __shared__ __align__(16) uint8_t st0[L::kStage];
-  __shared__ __align__(16) uint8_t st1[L::kStage];
-  __shared__ __align__(16) uint8_t st2[L::kStage];
-  __shared__ long s_arow[kTM];
-  __shared__ int s_orow[kTM];
-  __shared__ int s_rexp[kTM];  // row scale exponent of each tile row
-
-  // Tile order: each XCD (workgroups are dealt round robin by linear id)
-  // takes a contiguous run of work ids; work ids run over groups of kGroupM
-  // row tiles, column tile by column tile, row tile fastest.  The grid is
-  // sized for the most tiles routing can produce; only the first
-  // ntiles * ntn linear ids carry work, and they are the ones dealt out, so
-  // every XCD gets its share of the real tiles.
-  const int mtiles = g.ntiles[0];
-  const int total = mtiles * ntn;
-  const int lin = blockIdx.x;
-  if (lin >= total) return;
-  const int xcd = lin & 7, per = total >> 3, extra = total & 7;
-  const int w = xcd * per + min(xcd, extra) + (lin >> 3);
-  const int grp0 = (w / (kGroupM * ntn)) * kGroupM;
-  const int gsize = min(kGroupM, mtiles - grp0);
-  const int wr = w % (kGroupM * ntn);
-  const int tile = grp0 + wr % gsize;
-  const int ntile = wr / gsize;
+  constexpr bool half = HALF;
   const int e = g.tiles[4 * tile + 0];
   const int p0 = g.tiles[4 * tile + 1];
   const int rows = g.tiles[4 * tile + 2];
@@ -145,6 +121,11 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
+  // this wavefront's first tile row and first column (half tiles: every
+  // wavefront has rows 0..63, the second row of wavefronts the second 256
+  // columns)
+  const int rbase = half ? 0 : wm * 64;
+  const int cbase = half ? wm * kTN : 0;
   const int col = lane & 15, grp = lane >> 4;
   const long ebase = (long)e * g.N;
 
@@ -164,13 +145,25 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   //  B: the step's weight rows, GPR granules a row, granule g of row n in
   //     slot g ^ swz(n);
   //  S (block scales): wavefronts 0-3 the first 32-code half, 4-7 the second.
+  //  Half tiles (column-wise scales only): wavefront w fills rows 8w ..
+  //     8w + 7 (two instructions), and the weight rows of the second 256
+  //     columns go to the second half of the activation buffer (kABuf / 2
+  //     on; sources in asrc[2], asrc[3]).
   constexpr int BPW = L::kGPR * kTN / 64 / kTWaves;  // weight load instructions per wavefront
-  constexpr int NV = 4 + BPW + (SCALE == SC_BLOCK ? 1 : 0);
+  static_assert(!HALF || (SCALE == SC_COL && BPW <= 2 && L::kBBuf <= kABuf / 2),
+                "half tiles: column scales, second weight half in the activation buffer");
+  constexpr int NV = HALF ? 2 + 2 * BPW : 4 + BPW + (SCALE == SC_BLOCK ? 1 : 0);
   const uint8_t* asrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (wave * 4 + i) * 4 + (lane >> 4);
-    asrc[i] = g.a + s_arow[r] + (((lane & 15) ^ (r & 15)) * 16);
+    if (!HALF || i < 2) {
+      const int r = HALF ? (wave * 2 + i) * 4 + (lane >> 4) : (wave * 4 + i) * 4 + (lane >> 4);
+      asrc[i] = g.a + s_arow[r] + (((lane & 15) ^ (r & 15)) * 16);
+    } else {
+      const int G = (wave * BPW + min(i - 2, BPW - 1)) * 64 + lane;
+      const int n = G / L::kGPR, gs = G % L::kGPR;
+      asrc[i] = g.wq + (ebase + min(n0 + kTN + n, g.N - 1)) * (long)g.kb + ((gs ^ bswz<BITS>(n)) * 16);
+    }
   }
   const uint8_t* bsrc[BPW];
 #pragma unroll
@@ -183,19 +176,34 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   const int shalf = (wave >> 2) * 32;
   const int nk = g.K / kTK;
   auto issue = [&](uint8_t* sb, int kt) QMOE_INLINE {
+    if constexpr (HALF) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(asrc[i] + (long)kt * (kTK * 4)), QMOE_LOCAL(sb + (wave * 4 + i) * 1024),
-                                       16, 0, 0);
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(asrc[i] + (long)kt * (kTK * 4)),
+                                         QMOE_LOCAL(sb + (wave * 2 + i) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i)
-      __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(bsrc[i] + (long)kt * L::kBRow),
-                                       QMOE_LOCAL(sb + kABuf + (wave * BPW + i) * 1024), 16, 0, 0);
-    if constexpr (SCALE == SC_BLOCK)
-      __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(ssrc + (kt * kTK + shalf) / g.bs),
-                                       QMOE_LOCAL(sb + kABuf + L::kBBuf + (wave >> 2) * (kTN * 4) + (wave & 3) * 256),
-                                       4, 0, 0);
+      for (int i = 0; i < BPW; ++i) {
+        __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(bsrc[i] + (long)kt * L::kBRow),
+                                         QMOE_LOCAL(sb + kABuf + (wave * BPW + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(asrc[2 + i] + (long)kt * L::kBRow),
+                                         QMOE_LOCAL(sb + kABuf / 2 + (wave * BPW + i) * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(asrc[i] + (long)kt * (kTK * 4)),
+                                         QMOE_LOCAL(sb + (wave * 4 + i) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < BPW; ++i)
+        __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(bsrc[i] + (long)kt * L::kBRow),
+                                         QMOE_LOCAL(sb + kABuf + (wave * BPW + i) * 1024), 16, 0, 0);
+      if constexpr (SCALE == SC_BLOCK)
+        __builtin_amdgcn_global_load_lds(QMOE_GLOBAL(ssrc + (kt * kTK + shalf) / g.bs),
+                                         QMOE_LOCAL(sb + kABuf + L::kBBuf + (wave >> 2) * (kTN * 4) + (wave & 3) * 256),
+                                         4, 0, 0);
+    }
   };
+  auto wait_loads = [&]() QMOE_INLINE { wait_vm<NV>(); };
 
   f32x4 acc[4][4];
   f32x4 blk[4][4];  // block-scale spans: the span's sum, folded into acc when it closes
@@ -256,6 +264,9 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   const __attribute__((address_space(4))) float* segs =
       SEG ? (const __attribute__((address_space(4))) float*)(g.seg_scale + (long)tile * g.seg_n) : nullptr;
   const bool segrow = SEG && g.seg_flag[0] != 0;  // rows back to one exponent each: factors 1
+  // this wavefront's weight rows of a stage (half tiles, second row of
+  // wavefronts: the second column half, staged in the activation buffer)
+  auto bsel = [&](const uint8_t* base) QMOE_INLINE { return (half && wm == 1) ? base + kABuf / 2 : base + kABuf; };
   // Fragment tick of half j of the step in buffer base: the packed weight
   // words of the wavefront's four column subtiles, the activation hi/lo
   // fragments of its four row subtiles and the closing span's scales come
@@ -264,10 +275,10 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   auto frag = [&](const uint8_t* base, int j, bool fold_first, bool close, int kt) QMOE_INLINE {
     const uint8_t* bbuf = base + kABuf;
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) raw[ns] = tile_raw<BITS>(bbuf, wn * 64 + ns * 16 + col, j, cg);
+    for (int ns = 0; ns < 4; ++ns) raw[ns] = tile_raw<BITS>(bsel(base), wn * 64 + ns * 16 + col, j, cg);
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) {
-      const uint8_t* arow = base + (wm * 64 + ms * 16 + col) * 256;  // row & 15 == col
+      const uint8_t* arow = base + (rbase + ms * 16 + col) * 256;  // row & 15 == col
       ah[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp) ^ col) * 16));
       al[ms] = *(const f16x8*)(arow + (((8 * j + 2 * grp + 1) ^ col) * 16));
     }
@@ -348,7 +359,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   uint8_t* const sts[3] = {st0, st1, st2};
   issue(st0, 0);
   issue(st1, min(1, nk - 1));
-  wait_vm<NV>();
+  wait_loads();
   if (trail) bar();
   // one K step; D = kt modulo the unroll, so buffers and span parity are static
   auto step_d = [&](int kt, auto d_tag) QMOE_INLINE {
@@ -364,7 +375,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     mma(span(ODD, 0, false));
     bar();  // p2
     frag(base, 1, span(ODD, 0, true), span(ODD, 1, true), kt);
-    wait_vm<NV>();
+    wait_loads();
     bar();  // p3
     mma(span(ODD, 1, false));
   };
@@ -393,7 +404,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   if constexpr (SCALE == SC_COL) {
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
-      const float sc = g.ws[ebase + min(n0 + wn * 64 + ns * 16 + col, g.N - 1)];
+      const float sc = g.ws[ebase + min(n0 + cbase + wn * 64 + ns * 16 + col, g.N - 1)];
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms) acc[ms][ns] *= sc;
     }
@@ -424,7 +435,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
           float r = 0.f;
 #pragma unroll
           for (int ns = 0; ns < 4; ++ns) r = fmaxf(r, EPI == EPI_RELU ? acc[ms][ns][i] : fabsf(acc[ms][ns][i]));
-          m = fmaxf(m, __builtin_ldexpf(r, -s_rexp[wm * 64 + ms * 16 + 4 * grp + i]));
+          m = fmaxf(m, __builtin_ldexpf(r, -s_rexp[rbase + ms * 16 + 4 * grp + i]));
         }
 #pragma unroll
       for (int o = EPI == EPI_SWIGLU ? 2 : 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -434,38 +445,45 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   // every load has landed and every wavefront is done with the stages
   wait_vm<0>();
   __syncthreads();
-  int tile_e = 0;
-  bool tile_own = false;  // every nonzero row takes its own exponent
+  // (half tiles: one exponent per column half, from its row of wavefronts)
+  int tile_e[2] = {0, 0};
+  bool tile_own[2] = {false, false};  // every nonzero row takes its own exponent
   if constexpr (seg1) {
     if (g.seg_scale != nullptr) {
-      float G = 0.f, Lm = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < kTWaves; ++w2) {
-        G = fmaxf(G, s_red[2 * w2]);
-        Lm = fmaxf(Lm, s_red[2 * w2 + 1]);
-      }
-      int e = 0;
-      if constexpr (EPI == EPI_SWIGLU) {
-        if (g.limit < 0.f) {
-          G = fmaxf(G, -g.limit);
-          Lm = fmaxf(Lm, -g.limit);
+      for (int h = 0; h < 2; ++h) {
+        float G = 0.f, Lm = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kTWaves; ++w2)
+          if (!half || (w2 >> 2) == h) {
+            G = fmaxf(G, s_red[2 * w2]);
+            Lm = fmaxf(Lm, s_red[2 * w2 + 1]);
+          }
+        int e = 0;
+        if constexpr (EPI == EPI_SWIGLU) {
+          if (g.limit < 0.f) {
+            G = fmaxf(G, -g.limit);
+            Lm = fmaxf(Lm, -g.limit);
+          }
+          const float Lb = Lm + fabsf(g.beta);
+          if (G > 0.f && Lb > 0.f && G <= 3.4028235e38f && Lb <= 3.4028235e38f)
+            e = kRowTop - (__builtin_amdgcn_frexp_expf(G) + __builtin_amdgcn_frexp_expf(Lb));
+        } else {
+          e = row_exp(G);
         }
-        const float Lb = Lm + fabsf(g.beta);
-        if (G > 0.f && Lb > 0.f && G <= 3.4028235e38f && Lb <= 3.4028235e38f)
-          e = kRowTop - (__builtin_amdgcn_frexp_expf(G) + __builtin_amdgcn_frexp_expf(Lb));
-      } else {
-        e = row_exp(G);
+        tile_own[h] = e < -100;
+        tile_e[h] = max(min(e, 64), -100);
       }
-      tile_own = e < -100;
-      tile_e = max(min(e, 64), -100);
-      if (tid == 0) g.seg_scale[(long)tile * g.seg_n + ntile] = __builtin_ldexpf(1.f, -tile_e);
+      if (tid < (half ? 2 : 1) && ntile + tid < ntn)
+        g.seg_scale[(long)tile * g.seg_n + ntile + tid] = __builtin_ldexpf(1.f, -(tid == 0 ? tile_e[0] : tile_e[1]));
     }
   }
 
   // Epilogue in four rounds of 32 rows: the wavefronts holding those rows put
   // them (row scales undone) in an fp32 LDS tile [32][256] (columns
   // XOR-swizzled by 16 * ((row / 4) % 4)), then the workgroup writes whole
-  // rows.
+  // rows.  (Half tiles: rows 0-31 and 32-63 of the first column half, then
+  // of the second.)
   float* otile = reinterpret_cast<float*>(st0);
   auto tix = [](int rr, int c) { return rr * kTN + (c ^ (16 * ((rr >> 2) & 3))); };
 #pragma unroll
@@ -479,17 +497,20 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
           for (int i = 0; i < 4; ++i) {
             const int ms = (round & 1) * 2 + m2;
             const int rr = m2 * 16 + 4 * grp + i;
-            otile[tix(rr, wn * 64 + ns * 16 + col)] = __builtin_ldexpf(acc[ms][ns][i], -s_rexp[round * 32 + rr]);
+            otile[tix(rr, wn * 64 + ns * 16 + col)] =
+                __builtin_ldexpf(acc[ms][ns][i], -s_rexp[(half ? (round & 1) * 32 : round * 32) + rr]);
           }
     }
     __syncthreads();
-    const int r0 = round * 32;
-    const int rlim = min(32, rows - r0);  // valid rows of this round
+    const int r0 = half ? (round & 1) * 32 : round * 32;
+    const int ch = half ? round >> 1 : 0;  // column half
+    const int nc0 = n0 + ch * kTN;         // first column of this round
+    const int rlim = min(32, rows - r0);   // valid rows of this round
     if constexpr (EPI == EPI_STORE) {
       for (int idx = tid; idx < rlim * (kTN / 4); idx += kTThreads) {
         const int rr = idx / (kTN / 4), c = 4 * (idx % (kTN / 4));
-        if (n0 + c < g.N)
-          *(f32x4*)(g.slot_out + (long)s_orow[r0 + rr] * g.N + n0 + c) = *(const f32x4*)(otile + tix(rr, c));
+        if (nc0 + c < g.N)
+          *(f32x4*)(g.slot_out + (long)s_orow[r0 + rr] * g.N + nc0 + c) = *(const f32x4*)(otile + tix(rr, c));
       }
     } else if (g.seg_scale != nullptr) {
       // FC2 operand rows as f16 hi/lo groups of v * 2^e (the layout of the
@@ -507,8 +528,10 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
       constexpr int jw = swiglu ? kTN / 2 : kTN;  // codes of this tile
       constexpr int GR = jw / 8;                  // 8-code groups a row
       static_assert(GR <= 64 && (64 % GR) == 0, "a row's groups lie in one wavefront");
-      const int jbase = swiglu ? n0 / 2 : n0;
-      const float thr = __builtin_ldexpf(1.f, 1 - tile_e);
+      const int jbase = swiglu ? nc0 / 2 : nc0;
+      const int te = ch ? tile_e[1] : tile_e[0];
+      const bool town = ch ? tile_own[1] : tile_own[0];
+      const float thr = __builtin_ldexpf(1.f, 1 - te);
 #pragma unroll
       for (int b = 0; b < 32 * GR; b += kTThreads) {
         const int idx = b + tid;
@@ -539,8 +562,8 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
         }
         const unsigned long long rowm = (GR == 64 ? ~0ull : ((1ull << GR) - 1)) << (lane & (64 - GR));
         const unsigned long long big = __ballot(m >= thr), nz = __ballot(m > 0.f);
-        const bool own = (nz & rowm) != 0 && (tile_own || (big & rowm) == 0);
-        int e = tile_e;
+        const bool own = (nz & rowm) != 0 && (town || (big & rowm) == 0);
+        int e = te;
         if (__ballot(own) != 0) {
           const float mr = seg_max<GR>(m);
           if (own) e = row_exp(mr);
@@ -557,7 +580,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
             *(f16x8*)(dst + 16) = lo;
           }
           if (gq == 0) {
-            g.seg_rows[(long)ntile * g.S + prow] = e;
+            if (ntile + ch < ntn) g.seg_rows[(long)(ntile + ch) * g.S + prow] = e;
             if (own) *g.seg_flag = 1;
           }
         }
@@ -569,7 +592,7 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
       constexpr bool swiglu = EPI == EPI_SWIGLU;
       const int I = swiglu ? g.N / 2 : g.N;
       constexpr int jw = swiglu ? kTN / 2 : kTN;  // codes of this tile
-      const int jbase = swiglu ? n0 / 2 : n0;
+      const int jbase = swiglu ? nc0 / 2 : nc0;
       for (int idx = tid; idx < rlim * (jw / 4); idx += kTThreads) {
         const int rr = idx / (jw / 4);
         const int j0 = jbase + 4 * (idx % (jw / 4));
@@ -592,6 +615,59 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
     }
     __syncthreads();
   }
+}
+
+template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT, bool SEG = false>
+__global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
+  static_assert(!SEG || (EPI == EPI_STORE && STEPFOLD && (SCALE == SC_BLOCK || STEPFOLD_KT == 2)),
+                "segment scales: FC2, folded spans");
+  using L = TiledLayout<BITS>;
+  // Three stage buffers: a step's operands arrive by direct-to-LDS loads two
+  // steps ahead of their use.
+  __shared__ __align__(16) uint8_t st0[L::kStage];
+  __shared__ __align__(16) uint8_t st1[L::kStage];
+  __shared__ __align__(16) uint8_t st2[L::kStage];
+  __shared__ long s_arow[kTM];
+  __shared__ int s_orow[kTM];
+  __shared__ int s_rexp[kTM];  // row scale exponent of each tile row
+
+  // Tile order: each XCD (workgroups are dealt round robin by linear id)
+  // takes a contiguous run of work ids; work ids run over groups of kGroupM
+  // row tiles, column tile by column tile, row tile fastest.  The grid is
+  // sized for the most tiles routing can produce; only the first linear ids
+  // carry work, and they are the ones dealt out, so every XCD gets its share
+  // of the real tiles.  With g.split_small the table ends with the experts'
+  // last tiles of at most 64 rows (ntiles[1] tiles before them): each of
+  // those is a half tile, 64 rows x 512 columns, whose second wavefront row
+  // takes the second 256 columns (work ids after the full tiles').
+  const int mtiles = g.ntiles[0];
+  const int nfull = g.split_small ? g.ntiles[1] : mtiles;
+  const int ntn2 = (ntn + 1) >> 1;
+  const int totf = nfull * ntn;
+  const int total = totf + (mtiles - nfull) * ntn2;
+  const int lin = blockIdx.x;
+  if (lin >= total) return;
+  const int xcd = lin & 7, per = total >> 3, extra = total & 7;
+  const int w = xcd * per + min(xcd, extra) + (lin >> 3);
+  const bool half = w >= totf;  // workgroup-uniform
+  const int wh = half ? w - totf : w;
+  const int nt_ = half ? ntn2 : ntn, t0_ = half ? nfull : 0, nm_ = half ? mtiles - nfull : nfull;
+  const int grp0 = (wh / (kGroupM * nt_)) * kGroupM;
+  const int gsize = min(kGroupM, nm_ - grp0);
+  const int wr = wh % (kGroupM * nt_);
+  const int tile = t0_ + grp0 + wr % gsize;
+  const int ntile = half ? 2 * (wr / gsize) : wr / gsize;  // first 256-column tile
+  // the two kinds of tile are separate instantiations of the tile's code
+  // (a mode known only at run time inside the K loop makes the compiler
+  // wait for every load before LDS reads it cannot separate from them)
+  if (half) {
+    // (the host sets split_small only with column-wise scales)
+    if constexpr (SCALE == SC_COL)
+      tiled_tile<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT, SEG, true>(g, ntn, tile, ntile, st0, st1, st2, s_arow, s_orow,
+                                                                     s_rexp);
+  } else
+    tiled_tile<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT, SEG, false>(g, ntn, tile, ntile, st0, st1, st2, s_arow, s_orow,
+                                                                    s_rexp);
 }
 
 #undef QMOE_GLOBAL

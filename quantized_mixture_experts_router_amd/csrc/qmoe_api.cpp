@@ -93,7 +93,8 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
   QMOE_TRY_HIP(mark(0));
   if (p.small_front) {
     QMOE_TRY_HIP(launch_route_small(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize,
-                                    (int)p.bm, topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows, s));
+                                    (int)p.bm, topk_idx, topk_w, counts, offsets, perm, tiles, ntiles, trows, s,
+                                    p.half_tiles));
   } else if (p.share) {
     // routing over all E logits; the permutation groups the slots by the
     // held experts, with one more group (no tiles) for the others
@@ -101,13 +102,13 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
                                topk_w, s));
     QMOE_TRY_HIP(launch_local_index(topk_idx, S, (int)d.first, El, local, s));
     QMOE_TRY_HIP(launch_permute(local, S, El + 1, (int)p.chunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets,
-                                perm, tiles, ntiles, s, El));
+                                perm, tiles, ntiles, s, El, p.half_tiles));
     if (trows) QMOE_TRY_HIP(launch_tile_rows(perm, tiles, ntiles, (int)p.max_tiles, (int)p.bm, trows, s));
   } else {
     QMOE_TRY_HIP(launch_router(static_cast<const float*>(router->data), T, E, k, d.routing, d.normalize, topk_idx,
                                topk_w, s));
     QMOE_TRY_HIP(launch_permute(topk_idx, S, E, (int)p.chunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets,
-                                perm, tiles, ntiles, s));
+                                perm, tiles, ntiles, s, -1, p.half_tiles));
     if (trows) QMOE_TRY_HIP(launch_tile_rows(perm, tiles, ntiles, (int)p.max_tiles, (int)p.bm, trows, s));
   }
   if (ffn) {
@@ -140,6 +141,7 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g1.a_stride = a_f32 ? 4 * H : 4 * p.kp1;
     g1.tiles = tiles;
     g1.ntiles = ntiles;
+    g1.split_small = p.half_tiles;
     g1.trows = trows;
     g1.N = (int)d.F;
     g1.K = H;
@@ -212,6 +214,7 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
     g2.a_stride = 4 * p.kp2;
     g2.tiles = tiles;
     g2.ntiles = ntiles;
+    g2.split_small = p.half_tiles;
     g2.trows = trows;
     g2.N = H;
     g2.K = I;
@@ -374,11 +377,11 @@ qmoe_status qmoe_plan_describe(const qmoe_tensor* input, const qmoe_tensor* rout
   const bool ffn = d.T > 0 && d.I > 0 && d.El > 0;
   std::snprintf(buf, len,
                 "fc1=%s fc2=%s front=%s tile_rows=%lld max_tiles=%lld share=%d "
-                "s1=%d:%d:%d:%d:%d s2=%d:%d:%d:%d:%d segments=%d segflag=%zu workspace=%zu",
+                "s1=%d:%d:%d:%d:%d s2=%d:%d:%d:%d:%d segments=%d half_tiles=%d segflag=%zu workspace=%zu",
                 ffn ? gemm(p.s1) : "none", ffn ? gemm(p.s2) : "none",
                 p.small_front ? "one-workgroup" : "kernels", (long long)p.bm, (long long)p.max_tiles, p.share ? 1 : 0,
                 p.s1.one, p.s1.stg, p.s1.nst, p.s1.splits, p.s1.wg_rows, p.s2.one, p.s2.stg, p.s2.nst,
-                p.s2.splits, p.s2.wg_rows, p.seg_n, p.off_segflag, p.bytes);
+                p.s2.splits, p.s2.wg_rows, p.seg_n, p.half_tiles, p.off_segflag, p.bytes);
   return QMOE_OK;
 }
 

@@ -97,6 +97,13 @@ int stream_items_override(int gemm) {
   return s == "1" ? 1 : s == "4" ? 4 : s == "8" ? 8 : 0;
 }
 
+// QMOE_TILED_HALF=0 runs every tiled GEMM tile at 128 rows (for measurement
+// and tests); anything else: the plan's own choice.
+bool half_tiles_off() {
+  const char* v = std::getenv("QMOE_TILED_HALF");
+  return v && std::string(v) == "0";
+}
+
 // QMOE_TILED_SEGMENTS=0 keeps the per-row operand split between the tiled
 // GEMMs (for measurement and tests); anything else: the plan's own choice.
 bool segments_off() {
@@ -369,6 +376,9 @@ void make_plan(const Dims& d, Plan* p) {
   p->tiled = !p->decode && force != PATH_GEMM && d.I > 0 && aligned8 && d.H % 64 == 0 && d.I % 64 == 0 &&
              (d.bs == 0 || d.bs >= 32);
   if (p->tiled) p->bm = 128;
+  // Half tiles with column-wise scales only (with block scales the tiled
+  // kernel's half-tile code path was measured slower than whole tiles)
+  p->half_tiles = p->tiled && d.bs == 0 && !half_tiles_off() ? 1 : 0;
   // Sum over experts of ceil(count / bm) <= ceil(S / bm) + E; when one tile
   // holds any expert's rows it is at most E (one tile per used expert).
   p->max_tiles = (p->decode && d.T <= p->bm) ? d.El : (p->S + p->bm - 1) / p->bm + d.El;

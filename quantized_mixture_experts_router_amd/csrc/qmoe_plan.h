@@ -63,6 +63,10 @@ struct Plan {
   // (2^seg_shift codes), seg_n segments a row; 0: fp32 rows split per row
   // afterwards
   int seg_n = 0, seg_shift = 0;
+  // tiled, column-wise scales: each expert's last tile of at most 64 rows
+  // runs as a half tile (64 rows x 512 columns; the tile table lists those
+  // tiles last)
+  int half_tiles = 0;
   int mt = 1;            // 16-row M subtiles per tile
   int64_t bm = 16;       // rows per M tile
   int64_t max_tiles = 0; // ceil(S / bm) + E

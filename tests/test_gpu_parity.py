@@ -494,6 +494,46 @@ def test_tiled_segment_scales(torch, monkeypatch, case):
             assert flag == (1 if spread or xscale > 1e16 else 0), f"{label}: flag {flag}"
 
 
+# Half tiles (column-wise scales): each expert's last tile of at most 64
+# rows runs as 64 rows x 512 columns (the second row of wavefronts takes the
+# second 256 columns).  (T, H, E, I, k, bits, bs, act, logit bias of expert
+# 0, extra environment): ragged expert counts, column-tile counts odd and
+# even on both GEMMs (FC1 2I or I over 256, FC2 H / 256), both widths, with
+# and without segment scales.
+HALF_TILES = [
+    (300, 768, 10, 384, 2, 4, 0, "swiglu", 0.0, {}),
+    (300, 768, 10, 384, 2, 4, 0, "swiglu", 2.5, {"QMOE_TILED_SEGMENTS": "0"}),
+    (280, 1280, 9, 640, 2, 8, 0, "relu", 0.0, {}),
+    (333, 512, 16, 320, 3, 8, 0, "swiglu", 3.0, {}),
+    (290, 256, 10, 256, 2, 8, 0, "swiglu", 0.0, {}),
+    (400, 768, 7, 896, 1, 4, 0, "relu", 2.0, {"QMOE_TILED_SEGMENTS": "0"}),
+]
+
+
+@pytest.mark.parametrize("case", HALF_TILES)
+def test_tiled_half_tiles(torch, monkeypatch, case):
+    import quantized_mixture_experts_router_amd as qm
+    T, H, E, I, k, bits, bs, act, bias, env = case
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
+    rng = np.random.default_rng(2100 + T + E + I + bits)
+    w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=E, inter=I, k=k, bits=bits, block_size=bs,
+                         activation=act)
+    # a bias makes expert 0 take several tiles (full ones, then a remainder)
+    a["router_probs"] = a["router_probs"].copy()
+    a["router_probs"][:, 0] += bias
+    sel, _ = oracle.route(a["router_probs"], k)
+    counts = np.bincount(sel.reshape(-1), minlength=E)
+    small = int(np.sum((counts > 0) & (((counts - 1) % 128) < 64)))
+    for off in (False, True):
+        if off:
+            monkeypatch.setenv("QMOE_TILED_HALF", "0")
+        plan = qm.qmoe_plan_describe(*a.values(), attrs=w.attrs())
+        assert "fc1=tiled fc2=tiled" in plan and f"half_tiles={0 if off else 1} " in plan, plan
+        _full_check(w, a, torch, f"half tiles {'off' if off else 'on'} ({small} small tiles) T{T} H{H} E{E} I{I} "
+                                 f"k{k} bits{bits} bs{bs} {act} bias{bias} {env}")
+
+
 @pytest.mark.parametrize("case", [
     # (T, H, E, I, k, bits, bs, act): one 16-row tile per expert with K-range
     # partials on the streaming path, many experts with tokens (dozens of
