@@ -200,9 +200,11 @@ qmoe_status qmoe_validate(const qmoe_tensor* input, const qmoe_tensor* router_pr
 /* Bytes of device workspace qmoe_forward needs for these shapes (validates
  * first).  *bytes receives the size; it is 0 when T == 0.  With I == 0 only
  * the (small) routing part is needed.  The size depends on the kernel plan,
- * which the environment variable QMOE_STREAM_SINGLE_STAGE_MAX_SPLITS (most K
- * ranges of a single-stage streaming GEMM, default 16) can change: query the
- * size under the same environment as the forward call. */
+ * which environment variables can change (QMOE_STREAM_SINGLE_STAGE_MAX_SPLITS:
+ * most K ranges of a single-stage streaming GEMM, default 16;
+ * QMOE_TILED_KSPLIT: K ranges of the LDS-tiled FC2, 1, 2 or 4, each adding
+ * one set of S x H fp32 partial rows): query the size under the same
+ * environment as the forward call. */
 qmoe_status qmoe_workspace_size(const qmoe_tensor* input, const qmoe_tensor* router_probs,
                                 const qmoe_tensor* fc1_experts_weights, const qmoe_tensor* fc1_scales,
                                 const qmoe_tensor* fc2_experts_weights, const qmoe_tensor* fc2_scales,
@@ -213,7 +215,9 @@ qmoe_status qmoe_workspace_size(const qmoe_tensor* input, const qmoe_tensor* rou
  * (fc1=, fc2= stream | tiled | gemm | none), the routing front end, the
  * M-tile height and count, whether the weights hold a share of the experts,
  * the streaming split of each GEMM (single-stage:items per stage:stages per
- * K range:K ranges:rows per workgroup) and the workspace bytes.  The plan
+ * K range:K ranges:rows per workgroup), for the LDS-tiled GEMMs the segment
+ * scales per operand row (segments=), half tiles (half_tiles=) and FC2's K
+ * ranges (fc2_ranges=), and the workspace bytes.  The plan
  * depends on the environment as qmoe_workspace_size says.  At most len
  * bytes are written to buf, NUL-terminated; NULL buf or len 0 is
  * QMOE_ERR_NULL. */

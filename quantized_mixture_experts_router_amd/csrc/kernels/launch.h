@@ -89,6 +89,7 @@ struct GemmArgs {
   int* seg_flag;
   long act_stride;
   float* slot_out;      // FC2 output [splits][S][N] by slot id
+  int ksplit;           // tiled FC2: K ranges, range z's sums in slot_out[z] (0 or 1: one)
   const int* perm;      // FC2: sorted position -> slot
   float alpha, beta;
   float limit;          // SwiGLU clamp limit (+inf: none); set it, zero clamps everything
@@ -108,6 +109,8 @@ hipError_t launch_gemm(int bits, int epi, int mt, bool aligned, const GemmArgs& 
 
 // LDS-tiled variant (see tiled.hip): 128-row tiles, K a multiple of 64,
 // column-wise or >= 32-code block scales, 8-code-aligned rows, N % 4 == 0.
+// FC2 (EPI_STORE) may take g.ksplit K ranges of a multiple of 256 codes and
+// of the block size each.
 hipError_t launch_tiled(int bits, int epi, const GemmArgs& g, int max_tiles, hipStream_t st);
 
 // Weight-streaming variant for small token counts (see stream.hip).  A rows

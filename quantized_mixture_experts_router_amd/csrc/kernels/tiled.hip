@@ -108,8 +108,8 @@ __device__ __forceinline__ void wait_vm() {
 // The work of one tile: 128 rows x 256 columns, or (HALF) 64 rows x 512
 // columns, staged through the kernel's LDS arrays.
 template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT, bool SEG, bool HALF>
-__device__ __forceinline__ void tiled_tile(const GemmArgs& g, int ntn, int tile, int ntile, uint8_t* st0, uint8_t* st1,
-                                           uint8_t* st2, long* s_arow, int* s_orow, int* s_rexp) {
+__device__ __forceinline__ void tiled_tile(const GemmArgs& g, int ntn, int tile, int ntile, int kz, uint8_t* st0,
+                                           uint8_t* st1, uint8_t* st2, long* s_arow, int* s_orow, int* s_rexp) {
   using L = TiledLayout<BITS>;
   constexpr bool half = HALF;
   const int e = g.tiles[4 * tile + 0];
@@ -129,12 +129,15 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& g, int ntn, int tile,
   const int col = lane & 15, grp = lane >> 4;
   const long ebase = (long)e * g.N;
 
+  // SEG: rows back to one exponent each (segment factors 1), read before
+  // the barrier so that its wait is not one for the first steps' loads
+  const bool segrow = SEG && g.seg_flag[0] != 0;
   if (tid < kTM) {
     const int p = p0 + min(tid, rows - 1);
     const long ar = g.a_map ? (long)(g.a_map[p] / g.a_div) : (long)p;
     s_arow[tid] = ar * g.a_stride;
     s_orow[tid] = g.store_by_slot ? g.perm[p] : p;
-    s_rexp[tid] = (SEG && g.seg_flag[0] == 0) ? 0 : g.a_exp[ar];
+    s_rexp[tid] = (SEG && !segrow) ? 0 : g.a_exp[ar];
   }
   __syncthreads();
 
@@ -174,7 +177,20 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& g, int ntn, int tile,
   }
   const float* ssrc = g.ws + (ebase + min(n0 + (wave & 3) * 64 + lane, g.N - 1)) * (long)g.nblk;
   const int shalf = (wave >> 2) * 32;
-  const int nk = g.K / kTK;
+  // K range kz of g.ksplit (FC2): the sources start at its first step, kt
+  // counts the range's steps (the range is a whole number of scale blocks,
+  // segments and two-step spans)
+  const int nk = g.K / kTK / g.ksplit;
+  if (g.ksplit > 1) {
+    const int kt0 = kz * nk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (!HALF || i < 2) asrc[i] += (long)kt0 * (kTK * 4);
+      else asrc[i] += (long)kt0 * L::kBRow;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) bsrc[i] += (long)kt0 * L::kBRow;
+    if constexpr (SCALE == SC_BLOCK) ssrc += (kt0 * kTK) / g.bs;
+  }
   auto issue = [&](uint8_t* sb, int kt) QMOE_INLINE {
     if constexpr (HALF) {
 #pragma unroll
@@ -262,8 +278,9 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& g, int ntn, int tile,
   // SEG: the factor of the segment holding K step kt (a uniform load, read
   // through the scalar cache)
   const __attribute__((address_space(4))) float* segs =
-      SEG ? (const __attribute__((address_space(4))) float*)(g.seg_scale + (long)tile * g.seg_n) : nullptr;
-  const bool segrow = SEG && g.seg_flag[0] != 0;  // rows back to one exponent each: factors 1
+      SEG ? (const __attribute__((address_space(4))) float*)(g.seg_scale + (long)tile * g.seg_n +
+                                                             ((kz * nk * kTK) >> g.seg_shift))
+          : nullptr;
   // this wavefront's weight rows of a stage (half tiles, second row of
   // wavefronts: the second column half, staged in the activation buffer)
   auto bsel = [&](const uint8_t* base) QMOE_INLINE { return (half && wm == 1) ? base + kABuf / 2 : base + kABuf; };
@@ -510,7 +527,7 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& g, int ntn, int tile,
       for (int idx = tid; idx < rlim * (kTN / 4); idx += kTThreads) {
         const int rr = idx / (kTN / 4), c = 4 * (idx % (kTN / 4));
         if (nc0 + c < g.N)
-          *(f32x4*)(g.slot_out + (long)s_orow[r0 + rr] * g.N + nc0 + c) = *(const f32x4*)(otile + tix(rr, c));
+          *(f32x4*)(g.slot_out + ((long)kz * g.S + s_orow[r0 + rr]) * g.N + nc0 + c) = *(const f32x4*)(otile + tix(rr, c));
       }
     } else if (g.seg_scale != nullptr) {
       // FC2 operand rows as f16 hi/lo groups of v * 2^e (the layout of the
@@ -639,16 +656,20 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   // of the real tiles.  With g.split_small the table ends with the experts'
   // last tiles of at most 64 rows (ntiles[1] tiles before them): each of
   // those is a half tile, 64 rows x 512 columns, whose second wavefront row
-  // takes the second 256 columns (work ids after the full tiles').
+  // takes the second 256 columns (work ids after the full tiles').  With
+  // g.ksplit K ranges (FC2) the whole order repeats once per range.
   const int mtiles = g.ntiles[0];
   const int nfull = g.split_small ? g.ntiles[1] : mtiles;
   const int ntn2 = (ntn + 1) >> 1;
   const int totf = nfull * ntn;
-  const int total = totf + (mtiles - nfull) * ntn2;
+  const int tot1 = totf + (mtiles - nfull) * ntn2;  // tiles of one K range
+  const int total = tot1 * g.ksplit;
   const int lin = blockIdx.x;
   if (lin >= total) return;
   const int xcd = lin & 7, per = total >> 3, extra = total & 7;
-  const int w = xcd * per + min(xcd, extra) + (lin >> 3);
+  const int wk = xcd * per + min(xcd, extra) + (lin >> 3);
+  const int kz = wk / tot1;  // K range (the slowest index)
+  const int w = wk - kz * tot1;
   const bool half = w >= totf;  // workgroup-uniform
   const int wh = half ? w - totf : w;
   const int nt_ = half ? ntn2 : ntn, t0_ = half ? nfull : 0, nm_ = half ? mtiles - nfull : nfull;
@@ -663,11 +684,11 @@ __global__ void __launch_bounds__(kTThreads) qmoe_tiled(GemmArgs g, int ntn) {
   if (half) {
     // (the host sets split_small only with column-wise scales)
     if constexpr (SCALE == SC_COL)
-      tiled_tile<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT, SEG, true>(g, ntn, tile, ntile, st0, st1, st2, s_arow, s_orow,
-                                                                     s_rexp);
+      tiled_tile<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT, SEG, true>(g, ntn, tile, ntile, kz, st0, st1, st2, s_arow,
+                                                                     s_orow, s_rexp);
   } else
-    tiled_tile<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT, SEG, false>(g, ntn, tile, ntile, st0, st1, st2, s_arow, s_orow,
-                                                                    s_rexp);
+    tiled_tile<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT, SEG, false>(g, ntn, tile, ntile, kz, st0, st1, st2, s_arow,
+                                                                    s_orow, s_rexp);
 }
 
 #undef QMOE_GLOBAL
@@ -679,7 +700,7 @@ namespace {
 template <int BITS, int SCALE, int EPI, bool STEPFOLD, int STEPFOLD_KT, bool SEG = false>
 hipError_t go_tiled(const GemmArgs& g, int max_tiles, int ntn, hipStream_t st) {
   auto kern = qmoe_tiled<BITS, SCALE, EPI, STEPFOLD, STEPFOLD_KT, SEG>;
-  hipLaunchKernelGGL(kern, dim3(max_tiles * ntn), dim3(kTThreads), 0, st, g, ntn);
+  hipLaunchKernelGGL(kern, dim3(max_tiles * ntn * g.ksplit), dim3(kTThreads), 0, st, g, ntn);
   return hipGetLastError();
 }
 
@@ -717,8 +738,18 @@ int tiled_rows() { return kTM; }
 
 bool tiled_ok(int64_t K, int64_t bs, bool aligned) { return aligned && K > 0 && K % kTK == 0 && (bs == 0 || bs >= 32); }
 
-hipError_t launch_tiled(int bits, int epi, const GemmArgs& g, int max_tiles, hipStream_t st) {
-  if (!tiled_ok(g.K, g.bs, true) || (g.N & 3) != 0) return hipErrorInvalidValue;
+bool tiled_ksplit_ok(int64_t K, int64_t bs, int ksplit, bool store) {
+  if (ksplit == 1) return true;
+  if (!store || ksplit < 1 || K % ksplit != 0) return false;
+  const int64_t kr = K / ksplit;
+  return kr % 256 == 0 && (bs == 0 || kr % bs == 0);
+}
+
+hipError_t launch_tiled(int bits, int epi, const GemmArgs& g_in, int max_tiles, hipStream_t st) {
+  if (!tiled_ok(g_in.K, g_in.bs, true) || (g_in.N & 3) != 0) return hipErrorInvalidValue;
+  GemmArgs g = g_in;
+  if (g.ksplit < 1) g.ksplit = 1;
+  if (g.ksplit > 1 && !tiled_ksplit_ok(g.K, g.bs, g.ksplit, epi == EPI_STORE)) return hipErrorInvalidValue;
   const int ntn = (g.N + kTN - 1) / kTN;
   if (bits == 4) {
     if (epi == EPI_RELU) return pick_tiled<4, EPI_RELU>(g, max_tiles, ntn, st);

@@ -238,6 +238,7 @@ qmoe_status forward_impl(const qmoe_tensor* input, const qmoe_tensor* router, co
         g2.seg_n = p.seg_n;
         g2.seg_shift = p.seg_shift;
       }
+      g2.ksplit = p.ksplit2;  // K ranges: partial sets the combine sums
       QMOE_TRY_HIP(launch_tiled(d.bits, EPI_STORE, g2, (int)p.max_tiles, s));
     } else {
       QMOE_TRY_HIP(launch_gemm(d.bits, EPI_STORE, p.mt, p.aligned, g2, (int)p.max_tiles, s));
@@ -377,11 +378,12 @@ qmoe_status qmoe_plan_describe(const qmoe_tensor* input, const qmoe_tensor* rout
   const bool ffn = d.T > 0 && d.I > 0 && d.El > 0;
   std::snprintf(buf, len,
                 "fc1=%s fc2=%s front=%s tile_rows=%lld max_tiles=%lld share=%d "
-                "s1=%d:%d:%d:%d:%d s2=%d:%d:%d:%d:%d segments=%d half_tiles=%d segflag=%zu workspace=%zu",
+                "s1=%d:%d:%d:%d:%d s2=%d:%d:%d:%d:%d segments=%d half_tiles=%d fc2_ranges=%d segflag=%zu "
+                "workspace=%zu",
                 ffn ? gemm(p.s1) : "none", ffn ? gemm(p.s2) : "none",
                 p.small_front ? "one-workgroup" : "kernels", (long long)p.bm, (long long)p.max_tiles, p.share ? 1 : 0,
                 p.s1.one, p.s1.stg, p.s1.nst, p.s1.splits, p.s1.wg_rows, p.s2.one, p.s2.stg, p.s2.nst,
-                p.s2.splits, p.s2.wg_rows, p.seg_n, p.half_tiles, p.off_segflag, p.bytes);
+                p.s2.splits, p.s2.wg_rows, p.seg_n, p.half_tiles, p.ksplit2, p.off_segflag, p.bytes);
   return QMOE_OK;
 }
 

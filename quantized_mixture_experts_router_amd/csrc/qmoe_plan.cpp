@@ -111,6 +111,16 @@ bool segments_off() {
   return v && std::string(v) == "0";
 }
 
+// QMOE_TILED_KSPLIT=1, 2 or 4 sets the K ranges of the tiled FC2 (for
+// measurement and tests; a count the shape does not allow gives one range);
+// anything else: the plan's own choice.
+int tiled_ksplit_override() {
+  const char* v = std::getenv("QMOE_TILED_KSPLIT");
+  if (!v) return 0;
+  const std::string s(v);
+  return s == "1" ? 1 : s == "2" ? 2 : s == "4" ? 4 : 0;
+}
+
 int path_override() {
   const char* v = std::getenv("QMOE_PATH");
   if (!v) return PATH_AUTO;
@@ -332,11 +342,13 @@ void make_plan(const Dims& d, Plan* p) {
   // M tile of 16 rows (an expert with more rows takes several tiles); the
   // LDS-tiled kernels use 128-row tiles.  Measured on the decode (8 large
   // experts), large-E (128 int8 experts), fine-grained (64 small experts) and
-  // decode inter-share layers (bench.py --crossover): streaming is faster up
-  // to 256 tokens where both GEMMs stream (up to about 280 and 450 tokens on
-  // the first two); where only FC1 streams (FC2's reduction is not a whole
-  // number of stages) it is faster up to 64 tokens with 8 experts and slower
-  // at every size with 64.  Taller streaming tiles (each weight fragment
+  // decode inter-share layers (bench.py --crossover): where both GEMMs
+  // stream, streaming is faster up to about 240 tokens on the decode layer
+  // and 100 to 160 on the large-E one (whose tiled GEMMs run the experts'
+  // few rows as 64-row half tiles), within 3 to 5 % between them; the switch
+  // is at 224 tokens.  Where only FC1 streams (FC2's reduction is not a
+  // whole number of stages) streaming is faster up to 64 tokens with 8
+  // experts and slower at every size with 64.  Taller streaming tiles (each weight fragment
   // feeding 2 to 4 row subtiles) made the kernel bound by matrix-core and LDS
   // work instead of HBM: 0.36 / 0.63 / 0.72 ms at 32 / 64 / 96 decode tokens
   // against 0.20 / 0.30 / 0.35 ms with 16-row tiles.
@@ -393,6 +405,33 @@ void make_plan(const Dims& d, Plan* p) {
   if (p->tiled && (d.bs != 0 || d.I % 128 == 0) && !segments_off()) {
     p->seg_shift = d.act == QMOE_ACT_SWIGLU ? 7 : 8;  // codes of an FC1 column tile of 256 columns
     p->seg_n = (int)((d.I + (int64_t(1) << p->seg_shift) - 1) >> p->seg_shift);
+  }
+  // K ranges of the tiled FC2: one workgroup runs on a compute unit at a
+  // time, so an FC2 with few tiles leaves units idle in its last round of
+  // tiles (or in its only one).  Each range doubles the workgroups and adds
+  // one partial set (S x H fp32) that the combine sums in range order.
+  // Ranges double while the estimated tile count (the routed rows in
+  // 128-row tiles, half a tile of padding an expert) is under 16 rounds of
+  // 256 and each range keeps at least 1024 codes (shorter ones measured
+  // slower: a tile's fixed costs and the combine's extra reads outweigh the
+  // rounds saved).  The kernel takes ranges of any multiple of 256 codes
+  // and of the scale block.
+  if (p->tiled) {
+    const int64_t rows = p->share ? (p->S * d.El + d.E - 1) / d.E : p->S;
+    const int64_t est = ((rows + p->bm - 1) / p->bm + d.El / 2) * ((d.H + 255) / 256);
+    auto ranges_ok = [&](int ks, int64_t least) {
+      const int64_t kr = d.I / ks;
+      return d.I % ks == 0 && kr % 256 == 0 && kr >= least && (d.bs == 0 || kr % d.bs == 0);
+    };
+    const int force = tiled_ksplit_override();
+    int ks = 1;
+    if (force > 0) {
+      if (ranges_ok(force, 256)) ks = force;
+    } else {
+      while (ks < 4 && est * ks < 16 * 256 && ranges_ok(2 * ks, 1024)) ks *= 2;
+    }
+    p->ksplit2 = ks;
+    p->splits2 = ks;
   }
   p->aligned = (d.H % 8 == 0) && (d.I % 8 == 0);
   p->nchunks = (p->S + p->chunk - 1) / p->chunk;

@@ -36,7 +36,7 @@ constexpr int64_t kMaxExperts = 1024;
 // Token counts up to which the weight-streaming GEMMs run (measured
 // crossovers; see make_plan): when both GEMMs stream, and when only FC1
 // streams (then also at most kStreamMixedMaxExperts experts held).
-constexpr int64_t kStreamMaxTokens = 256;
+constexpr int64_t kStreamMaxTokens = 224;
 constexpr int64_t kStreamMixedMaxTokens = 64;
 constexpr int64_t kStreamMixedMaxExperts = 16;
 
@@ -83,6 +83,7 @@ struct Plan {
   } s1, s2;
   bool half = false;     // streaming tiles of 8 rows (each K range one stage of s.stg items), else 16 * mt rows
   int splits2 = 1;       // FC2 partial sets the combine sums (1 off the stream path)
+  int ksplit2 = 1;       // tiled FC2: K ranges (each writes its own partial set)
   size_t off_part1 = 0;  // FC1 fp32 partials [s1.splits][S][F] (stream path with K ranges)
   size_t off_trows = 0;  // streaming kernels: slot id of every tile row [max_tiles][bm]
   bool small_front = false;  // router + permutation in one workgroup (S, E <= 1024)

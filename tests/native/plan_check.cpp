@@ -206,6 +206,16 @@ void check_plan(const qmoe::Dims& d, const qmoe::Plan& p) {
     EXPECT(p.seg_shift == (d.act == QMOE_ACT_SWIGLU ? 7 : 8), "segment shift %d", p.seg_shift);
     EXPECT(p.seg_n == (d.I + (int64_t(1) << p.seg_shift) - 1) >> p.seg_shift, "segments %d", p.seg_n);
   }
+  // K ranges of the tiled FC2: 1, 2 or 4, each a whole number of 256-code
+  // pieces and scale blocks, at least 1024 codes; the combine sums one
+  // partial set per range
+  EXPECT(p.ksplit2 == 1 || p.ksplit2 == 2 || p.ksplit2 == 4, "FC2 ranges %d", p.ksplit2);
+  if (p.ksplit2 > 1) {
+    const int64_t kr = d.I / p.ksplit2;
+    EXPECT(p.tiled && d.I % p.ksplit2 == 0 && kr % 256 == 0 && kr >= 1024 && (d.bs == 0 || kr % d.bs == 0),
+           "FC2 ranges %d on I %" PRId64, p.ksplit2, d.I);
+    EXPECT(p.splits2 == p.ksplit2, "partial sets %d for %d ranges", p.splits2, p.ksplit2);
+  }
 }
 
 }  // namespace

@@ -96,6 +96,12 @@ def test_kernel_choice_per_workload():
     assert "segments=11 " in bench.plan_of(W.WORKLOADS["fine"])
     assert "segments=12 " in bench.plan_of(W.WORKLOADS["large_e"])
     assert "segments=1 " in bench.plan_of(W.WORKLOADS["tiny"])
+    # K ranges of the tiled FC2: four at prefill (about 1100 tiles of 128 x
+    # 256 for 256 compute units), one where the reduction is too short to
+    # split into ranges of 1024 codes or more
+    assert "fc2_ranges=4 " in bench.plan_of(W.WORKLOADS["prefill"])
+    for name in ("fine", "large_e", "large_e_ep8", "tiny"):
+        assert "fc2_ranges=1 " in bench.plan_of(W.WORKLOADS[name]), name
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1"]) == "qmoe_gmm_f32_rows16"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_fine_fc1"]) == "qmoe_gmm_f32"
 

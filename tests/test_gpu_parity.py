@@ -108,7 +108,7 @@ def test_route_ties_through_gpu(torch):
 
 
 # Small sweeps: every element.  (T, H, E, I, k) chosen to cover one and several
-# M tiles on the weight-streaming path (up to 256 tokens where its stages
+# M tiles on the weight-streaming path (up to 224 tokens where its stages
 # tile both reductions), the LDS-tiled path (larger T,
 # H and I multiples of 64) and the register-tiled path (other shapes), ragged
 # tails in every dimension, unused experts and k = E.
@@ -117,11 +117,11 @@ SHAPES = [
     (33, 128, 6, 64, 6), (64, 192, 8, 128, 2), (70, 128, 5, 96, 2), (200, 64, 16, 64, 4),
     (300, 256, 1, 32, 1), (24, 512, 8, 256, 3), (40, 256, 4, 256, 2), (60, 256, 4, 128, 2),
     (130, 128, 3, 192, 2), (257, 320, 4, 128, 3),
-    # either side of the streaming / tiled switches: 256 tokens where both
+    # either side of the streaming / tiled switches: 224 tokens where both
     # GEMMs stream (16-row streaming tiles, experts spread over many tiles),
     # 64 where only FC1 does (int4: FC2's 256-code reduction is not a whole
     # 512-code stage), then 128-row LDS tiles
-    (256, 512, 4, 512, 2), (257, 512, 4, 512, 2), (64, 512, 8, 256, 2), (65, 512, 8, 256, 2),
+    (224, 512, 4, 512, 2), (225, 512, 4, 512, 2), (64, 512, 8, 256, 2), (65, 512, 8, 256, 2),
 ]
 
 
@@ -532,6 +532,72 @@ def test_tiled_half_tiles(torch, monkeypatch, case):
         assert "fc1=tiled fc2=tiled" in plan and f"half_tiles={0 if off else 1} " in plan, plan
         _full_check(w, a, torch, f"half tiles {'off' if off else 'on'} ({small} small tiles) T{T} H{H} E{E} I{I} "
                                  f"k{k} bits{bits} bs{bs} {act} bias{bias} {env}")
+
+
+# K ranges of the tiled FC2 (a few tiles for 256 compute units): each range
+# writes its own partial rows and the combine sums them in range order.
+# (T, H, E, I, k, bits, bs, act, the plan's ranges, ranges forced through
+# QMOE_TILED_KSPLIT, input spread in decades, extra environment): every
+# scale layout the tiled kernel takes (blocks of 32 to 256 codes,
+# column-wise with half tiles), two and four ranges of 256 codes and more,
+# ReLU (256-code segments) and SwiGLU (128-code ones), rows flagged back to
+# their own exponents (spread), and the per-row split between the GEMMs.
+FC2_RANGES = [
+    (300, 512, 4, 2048, 2, 4, 128, "swiglu", 2, (4, 1), 0, {}),
+    (280, 512, 8, 2048, 2, 4, 32, "swiglu", 2, (4,), 0, {}),
+    (260, 256, 4, 1536, 3, 4, 64, "relu", 1, (2,), 0, {}),
+    (300, 512, 4, 2048, 2, 8, 256, "swiglu", 2, (4,), 0, {}),
+    (300, 768, 6, 1024, 2, 8, 0, "relu", 1, (2, 4), 0, {}),
+    (290, 256, 5, 4096, 2, 4, 0, "swiglu", 4, (1,), 0, {}),
+    (300, 512, 4, 2048, 2, 4, 128, "swiglu", 2, (4,), 3, {}),
+    (300, 512, 4, 2048, 2, 4, 128, "relu", 2, (4,), 0, {"QMOE_TILED_SEGMENTS": "0"}),
+]
+
+
+@pytest.mark.parametrize("case", FC2_RANGES)
+def test_tiled_fc2_k_ranges(torch, monkeypatch, case):
+    import quantized_mixture_experts_router_amd as qm
+    T, H, E, I, k, bits, bs, act, ranges, forced, spread, env = case
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
+    rng = np.random.default_rng(2600 + T + E + I + bits + bs)
+    w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=E, inter=I, k=k, bits=bits, block_size=bs,
+                         activation=act)
+    if spread:
+        a["input"] = (a["input"] * 10.0 ** rng.uniform(-spread, 0, size=(T, 1))).astype(np.float32)
+    attrs = w.attrs()
+    ref, inter = oracle.qmoe(*a.values(), attrs=attrs, return_intermediates=True)
+    outs = []
+    for ks in (None,) + tuple(forced):
+        # the plan's own count, then the forced ones (a count whose ranges
+        # would be under 256 codes leaves one range)
+        if ks is None:
+            monkeypatch.delenv("QMOE_TILED_KSPLIT", raising=False)
+            want = ranges
+        else:
+            monkeypatch.setenv("QMOE_TILED_KSPLIT", str(ks))
+            want = ks if I % (256 * ks) == 0 else 1
+        plan = qm.qmoe_plan_describe(*a.values(), attrs=attrs)
+        assert "fc1=tiled fc2=tiled" in plan and f"fc2_ranges={want} " in plan, plan
+        label = f"FC2 ranges {want}: T{T} H{H} E{E} I{I} k{k} bits{bits} bs{bs} {act} spread={spread} {env}"
+        say(f"[case] {label}")
+        res = run_gpu(a, attrs, torch)
+        check_routing(res, inter["sel"], inter["w"], inter["counts"], inter["offsets"], inter["perm"])
+        assert np.all(np.isfinite(res["out"])), f"{label}: non-finite output"
+        if spread:
+            # the bar per token row: a small row is held to its own magnitude
+            out = res["out"].reshape(T, H).astype(np.float64)
+            ref2 = np.asarray(ref, dtype=np.float64).reshape(T, H)
+            err = np.max(np.abs(out - ref2), axis=1)
+            rms = np.sqrt(np.mean(ref2 ** 2, axis=1))
+            assert np.all(err <= OUT_TOL * rms), f"{label}: worst row {np.max(err / rms)}"
+        else:
+            check_output(res["out"], ref, label)
+        outs.append(res["out"].astype(np.float64))
+    # the ranges split the same sums: the results agree to rounding
+    ref_rms = np.sqrt(np.mean(np.asarray(ref, dtype=np.float64) ** 2))
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-5 * ref_rms
 
 
 @pytest.mark.parametrize("case", [
