@@ -20,88 +20,59 @@
 #include "common.hpp"
 #include "launch.h"
 
+#define QMOE_OPERAND_INLINE __attribute__((always_inline))
+
 namespace qmoe {
 
-namespace {
-
-// 32 fp32 codes [32 b, 32 b + 32) of a row of n codes (zero from n on).
-__device__ __forceinline__ void load_block(const float* __restrict__ s, int b, int n, bool vec, float (&v)[32]) {
-  const int c0 = 32 * b;
-  if (vec && c0 + 32 <= n) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const f32x4 t = *(const f32x4*)(s + c0 + 4 * q);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) v[4 * q + c] = t[c];
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) v[c] = c0 + c < n ? s[c0 + c] : 0.f;
-  }
-}
-
-__device__ __forceinline__ float block_max(const float (&v)[32]) {
-  float m = 0.f;
-#pragma unroll
-  for (int c = 0; c < 32; ++c) m = fmaxf(m, fabsf(v[c]));
-  return m;
-}
-
-// Storage groups 4b .. 4b + 3 (bytes [128 b, 128 b + 128) of the row) from
-// the block's fp32 codes: the same bytes the block's fp32 values occupy in a
-// row of 4-byte codes, so the conversion can run in place.
-template <int BITS>
-__device__ __forceinline__ void store_block(uint8_t* __restrict__ d, int b, int e, const float (&v)[32]) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int cg = BITS == 4 ? g : sigma8(g);  // code group held by storage group g
-    float w[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) w[c] = v[8 * cg + c];
-    f16x8 hi, lo;
-    split_group<BITS>(w, e, hi, lo);
-    uint8_t* dst = d + (long)(4 * b + g) * 32;
-    *(f16x8*)dst = hi;
-    *(f16x8*)(dst + 16) = lo;
-  }
-}
-
-}  // namespace
-
-// One workgroup per row.  Row r: n fp32 codes at src + r * sstride (floats),
-// kp hi/lo codes (kp % 32 == 0, codes from n on are zero) at dst + r *
-// dstride (bytes); exps[r] = e.  src and dst may be the same row of 4-byte
-// codes (every thread reads a block before it writes that block's bytes, and
-// no other thread touches them).  The first RB blocks of a thread stay in
-// registers between the two passes; longer rows read the rest again.  With
-// live given, rows from *live on are not in use and are skipped.
-template <int BITS, int NT>
+// One workgroup of NT threads per row.  Row r: n fp32 codes at src + r *
+// sstride (floats), kp hi/lo codes (kp % 32 == 0, codes from n on are zero)
+// at dst + r * dstride (bytes); exps[r] = e.  Thread t takes the 4-code
+// pieces t, t + NT, ... of the row, so that each load instruction of a
+// wavefront reads 1 KB of it; the first RB pieces stay in registers between
+// the two passes and longer rows read the rest again.  The two lanes
+// holding a storage group's pieces (2j and 2j + 1, codes 0-3 and 4-7 of the
+// group) swap halves, and the first writes the group's 16 bytes of hi
+// parts, the second its 16 bytes of lo parts.  src and dst may be the same
+// row of 4-byte codes: a storage group lies in the bytes of its own 32-code
+// block, whose 8 pieces are read by 8 lanes of one wavefront in the same
+// step before any of them is written.  With live given, rows from *live on
+// are not in use and are skipped.
+template <int BITS, int NT, int RB>
 __global__ void __launch_bounds__(NT) qmoe_split_rows(const float* src, long sstride, int n, int vec, uint8_t* dst,
                                                       long dstride, int kp, int* __restrict__ exps,
                                                       const int* __restrict__ live, int* __restrict__ zero_flag) {
-  constexpr int RB = 2;
   const long row = blockIdx.x;
   if (zero_flag != nullptr && row == 0 && threadIdx.x == 0) *zero_flag = 0;
   if (live != nullptr && row >= live[0]) return;
   const float* s = src + row * sstride;
   uint8_t* d = dst + row * dstride;
-  const int nb = kp / 32;
+  const int np = kp / 4;  // pieces: a whole number of storage groups and blocks
   const int tid = threadIdx.x;
-  float cache[RB][32];
+  auto load = [&](int p) QMOE_OPERAND_INLINE {
+    const int c0 = 4 * p;
+    f32x4 v;
+    if (vec && c0 + 4 <= n) {
+      v = *(const f32x4*)(s + c0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = c0 + c < n ? s[c0 + c] : 0.f;
+    }
+    return v;
+  };
+  auto vmax = [](float m, const f32x4& v) QMOE_OPERAND_INLINE {
+    return fmaxf(fmaxf(m, fmaxf(fabsf(v[0]), fabsf(v[1]))), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  };
+  f32x4 cache[RB];
   float m = 0.f;
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
-    const int b = tid + i * NT;
-    if (b < nb) {
-      load_block(s, b, n, vec != 0, cache[i]);
-      m = fmaxf(m, block_max(cache[i]));
+    const int p = tid + i * NT;
+    if (p < np) {
+      cache[i] = load(p);
+      m = vmax(m, cache[i]);
     }
   }
-  for (int b = tid + RB * NT; b < nb; b += NT) {
-    float v[32];
-    load_block(s, b, n, vec != 0, v);
-    m = fmaxf(m, block_max(v));
-  }
+  for (int p = tid + RB * NT; p < np; p += NT) m = vmax(m, load(p));
   m = seg_max<64>(m);
   if constexpr (NT > 64) {
     __shared__ float red[NT / 64];
@@ -112,16 +83,45 @@ __global__ void __launch_bounds__(NT) qmoe_split_rows(const float* src, long sst
   }
   const int e = row_exp(m);
   if (tid == 0) exps[row] = e;
+  // piece p's part of its storage group (both lanes of a group run this
+  // together: np is even and NT a multiple of 64)
+  auto put = [&](int p, const f32x4& v) QMOE_OPERAND_INLINE {
+    const bool odd = (p & 1) != 0;  // codes 4-7 of the group: writes the lo parts
+    _Float16 h[4], l[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) split_f16(v[c], e, h[c], l[c]);
+    // send the other kind: the even lane its lo parts, the odd one its hi parts
+    uint32_t x[2], y[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const _Float16 a = odd ? h[2 * k] : l[2 * k], b = odd ? h[2 * k + 1] : l[2 * k + 1];
+      x[k] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+      y[k] = (uint32_t)__shfl_xor((int)x[k], 1);
+    }
+    // the 8 codes' parts of this lane's kind, in code order
+    _Float16 g8[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const _Float16 r0 = __builtin_bit_cast(_Float16, (uint16_t)(y[k] & 0xFFFF));
+      const _Float16 r1 = __builtin_bit_cast(_Float16, (uint16_t)(y[k] >> 16));
+      g8[2 * k] = odd ? r0 : h[2 * k];
+      g8[2 * k + 1] = odd ? r1 : h[2 * k + 1];
+      g8[4 + 2 * k] = odd ? l[2 * k] : r0;
+      g8[4 + 2 * k + 1] = odd ? l[2 * k + 1] : r1;
+    }
+    f16x8 out;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) out[sl] = g8[BITS == 4 ? perm4_of_slot(sl) : sl];
+    const int q = p >> 1;                               // code group of the row
+    const int sg = BITS == 4 ? (q & 3) : sigma8(q & 3);  // its storage group in the 32-code block
+    *(f16x8*)(d + (long)(4 * (q >> 2) + sg) * 32 + (odd ? 16 : 0)) = out;
+  };
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
-    const int b = tid + i * NT;
-    if (b < nb) store_block<BITS>(d, b, e, cache[i]);
+    const int p = tid + i * NT;
+    if (p < np) put(p, cache[i]);
   }
-  for (int b = tid + RB * NT; b < nb; b += NT) {
-    float v[32];
-    load_block(s, b, n, vec != 0, v);
-    store_block<BITS>(d, b, e, v);
-  }
+  for (int p = tid + RB * NT; p < np; p += NT) put(p, load(p));
 }
 
 // One wavefront per row: exps[r] = e of the n fp32 codes at src + r * stride.
@@ -213,15 +213,22 @@ hipError_t launch_split_rows(int bits, const float* src, long sstride, int n, ui
   if (kp % 32 != 0 || n > kp) return hipErrorInvalidValue;
   // 16-byte loads need 16-byte aligned rows
   const int vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && (sstride & 3) == 0) ? 1 : 0;
-  const int nb = kp / 32;
   const dim3 grid((unsigned)rows);
-  if (nb <= 128) {
-    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live, zero_flag);
-    else hipLaunchKernelGGL((qmoe_split_rows<8, 64>), grid, dim3(64), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live, zero_flag);
-  } else {
-    if (bits == 4) hipLaunchKernelGGL((qmoe_split_rows<4, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live, zero_flag);
-    else hipLaunchKernelGGL((qmoe_split_rows<8, 256>), grid, dim3(256), 0, st, src, sstride, n, vec, dst, dstride, kp, exps, live, zero_flag);
-  }
+  // threads and registered pieces a row: rows up to 1024, 4096 and 16384
+  // codes stay in registers between the passes
+#define QMOE_SPLIT(NT, RB)                                                                                     \
+  do {                                                                                                         \
+    if (bits == 4)                                                                                             \
+      hipLaunchKernelGGL((qmoe_split_rows<4, NT, RB>), grid, dim3(NT), 0, st, src, sstride, n, vec, dst, dstride, \
+                         kp, exps, live, zero_flag);                                                           \
+    else                                                                                                       \
+      hipLaunchKernelGGL((qmoe_split_rows<8, NT, RB>), grid, dim3(NT), 0, st, src, sstride, n, vec, dst, dstride, \
+                         kp, exps, live, zero_flag);                                                           \
+  } while (0)
+  if (kp <= 1024) QMOE_SPLIT(64, 4);
+  else if (kp <= 4096) QMOE_SPLIT(256, 4);
+  else QMOE_SPLIT(256, 16);
+#undef QMOE_SPLIT
   return hipGetLastError();
 }
 
