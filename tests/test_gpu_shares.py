@@ -38,17 +38,22 @@ def _expert_share(a, first, held):
 
 
 CASES = [
-    # (T, H, E, I, k, bits, bs, act, cuts): one case per GEMM path
-    (16, 512, 8, 256, 2, 4, 64, "swiglu", [0, 3, 4, 8]),        # weight streaming
-    (40, 256, 12, 128, 3, 8, 0, "relu", [0, 5, 12]),            # weight streaming, int8
-    (200, 256, 8, 192, 2, 4, 32, "swiglu", [0, 1, 6, 8]),       # LDS-tiled
-    (130, 256, 6, 128, 2, 8, 16, "relu", [0, 2, 6]),            # register-tiled (16-code blocks)
+    # (T, H, E, I, k, bits, bs, act, cuts, environment): one case per GEMM
+    # path, and the LDS-tiled FC2 in four K ranges (partial sets of the held
+    # slots only)
+    (16, 512, 8, 256, 2, 4, 64, "swiglu", [0, 3, 4, 8], {}),        # weight streaming
+    (40, 256, 12, 128, 3, 8, 0, "relu", [0, 5, 12], {}),            # weight streaming, int8
+    (200, 256, 8, 192, 2, 4, 32, "swiglu", [0, 1, 6, 8], {}),       # LDS-tiled
+    (130, 256, 6, 128, 2, 8, 16, "relu", [0, 2, 6], {}),            # register-tiled (16-code blocks)
+    (300, 256, 8, 2048, 2, 4, 128, "swiglu", [0, 3, 8], {"QMOE_TILED_KSPLIT": "4"}),  # tiled, FC2 ranges
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=["stream", "stream-int8", "tiled", "gemm"])
-def test_expert_shares(torch, case):
-    T, H, E, I, k, bits, bs, act, cuts = case
+@pytest.mark.parametrize("case", CASES, ids=["stream", "stream-int8", "tiled", "gemm", "tiled-fc2-ranges"])
+def test_expert_shares(torch, monkeypatch, case):
+    T, H, E, I, k, bits, bs, act, cuts, env = case
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
     rng = np.random.default_rng(800 + T + E)
     w, a = W.random_case(rng, tokens_shape=(T,), hidden=H, experts=E, inter=I, k=k, bits=bits, block_size=bs,
                          activation=act)
@@ -57,7 +62,7 @@ def test_expert_shares(torch, case):
         b = _expert_share(a, first, last - first)
         attrs = dict(w.attrs(), first_expert=first)
         label = f"share [{first}, {last}) of {E} T{T} bits{bits} bs{bs} {act}"
-        say(f"[case] {label}")
+        say(f"[case] {label} {env}")
         res = run_gpu(b, attrs, torch)
         ref, inter = oracle.qmoe(*b.values(), attrs=attrs, return_intermediates=True)
         check_routing(res, inter["sel"], inter["w"], inter["counts"], inter["offsets"], inter["perm"])
