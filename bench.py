@@ -716,8 +716,8 @@ def main_crossover(args):
 def main():
     args = _args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every run here uses a single MI355X); use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the layer on one MI355X "
+              "(no collectives or sharding across GPUs); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
