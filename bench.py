@@ -43,6 +43,15 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 F16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense f16 matrix peak, TFLOP/s
 F32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X fp32 matrix (and vector) peak, TFLOP/s
+F64_MATRIX_PEAK_TFLOPS = 78.6   # MI355X fp64 matrix peak, TFLOP/s
+# GroupedMatMul element types: bytes, matrix peak of the instruction the
+# library runs them on, and the short name of the JSON line
+GMM_TYPES = {
+    "float32": (4, F32_MATRIX_PEAK_TFLOPS, "f32"),
+    "float16": (2, F16_DENSE_PEAK_TFLOPS, "f16"),
+    "bfloat16": (2, F16_DENSE_PEAK_TFLOPS, "bf16"),  # bf16 dense MFMA: the f16 rate
+    "float64": (8, F64_MATRIX_PEAK_TFLOPS, "f64"),
+}
 METRIC = "QMoE layer tokens/s + achieved HBM GB/s vs peak (int4 decode & prefill)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -182,16 +191,21 @@ KERNEL_SRC = {
     "qmoe_gmm_f32": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm.hip"),
     "qmoe_gmm_f32_rows16": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm.hip"),
     "qmoe_gmm_typed": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
+    "qmoe_gmm16_rows16": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
 }
 
 
 def gmm_kernel(w):
     """The library's GroupedMatMul kernel for this shape: the weight-streaming
     one over 16-row tiles when the rows average at most 16 per group (and K, N
-    are multiples of 4; bench tensors are 16-byte aligned), else the LDS-tiled
-    one over 64-row tiles."""
+    are multiples of 4; bench tensors are aligned) in float32, float16 and
+    bfloat16, else the LDS-tiled ones over 64-row tiles (double always)."""
     R = w.M * w.S
     rows16 = w.K % 4 == 0 and w.N % 4 == 0 and R <= 16 * max(1, min(w.G, R))
+    if w.dtype == "float64":
+        return "qmoe_gmm_typed"
+    if w.dtype != "float32":
+        return "qmoe_gmm16_rows16" if rows16 else "qmoe_gmm_typed"
     return "qmoe_gmm_f32_rows16" if rows16 else "qmoe_gmm_f32"
 
 
@@ -280,11 +294,13 @@ def copy_calibration(nbytes, reps=3):
 
 def gmm_work(w, idx):
     """Algorithmic bytes and FLOPs of one GroupedMatMul call: weights (and
-    bias rows) of the groups that receive a row, input rows, output rows."""
+    bias rows) of the groups that receive a row, input rows, output rows, in
+    the workload's element type."""
     import numpy as np
+    eb = GMM_TYPES[w.dtype][0]
     used = int(np.unique(idx).size)
-    wb = used * w.K * w.N * 4 + (used * w.N * 4 if w.bias else 0)
-    return dict(bytes=wb + w.M * w.K * 4 + w.M * w.S * w.N * 4, flops=2.0 * w.M * w.S * w.K * w.N,
+    wb = used * w.K * w.N * eb + (used * w.N * eb if w.bias else 0)
+    return dict(bytes=wb + w.M * w.K * eb + w.M * w.S * w.N * eb, flops=2.0 * w.M * w.S * w.K * w.N,
                 weight_bytes=wb, used_groups=used)
 
 
@@ -312,8 +328,9 @@ def gmm_cpu_baseline(w, a, budget_s=12.0, max_reps=64):
 
 
 def main_gmm(args):
-    """GroupedMatMul (float32) on one of its workloads: one step = one
-    qmoe_grouped_matmul call (index conversion, group permutation, tile GEMM)."""
+    """GroupedMatMul on one of its workloads (float32, float16, bfloat16 or
+    double): one step = one qmoe_grouped_matmul call (index conversion, group
+    permutation, tile GEMM)."""
     import numpy as np
     import torch
 
@@ -323,8 +340,13 @@ def main_gmm(args):
     w = W.GMM_WORKLOADS[args.workload]
     a = W.gmm_generate(w)
     torch.cuda.set_device(0)
+    tdt = getattr(torch, w.dtype)
+    # floating tensors: the float32 draws rounded to the element type
     d = {k: (torch.from_numpy(v).cuda() if v is not None else None) for k, v in a.items()}
-    out = torch.empty((w.M, w.S, w.N), dtype=torch.float32, device="cuda")
+    for k in ("input", "weights", "bias"):
+        if d[k] is not None:
+            d[k] = d[k].to(tdt).contiguous()
+    out = torch.empty((w.M, w.S, w.N), dtype=tdt, device="cuda")
     need = qm.qmoe_grouped_matmul_workspace_size(d["input"], d["weights"], d["group_indices"], d["bias"], out)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -364,7 +386,7 @@ def main_gmm(args):
         for e in evs:
             hip.hipEventDestroy(e)
         stages = dict(permutation=sums[0] / args.steps, gemm=sums[1] / args.steps)
-        roofline = roofline_for(work, stages["gemm"], F32_MATRIX_PEAK_TFLOPS)
+        roofline = roofline_for(work, stages["gemm"], GMM_TYPES[w.dtype][1])
         kernel = gmm_kernel(w)
         roofline["kernel"] = kernel
         roofline["avg_ms"] = round(stages["gemm"], 5)
@@ -374,7 +396,7 @@ def main_gmm(args):
 
     cpu = None if args.no_cpu_baseline else gmm_cpu_baseline(w, a)
     line = {
-        "metric": "GroupedMatMul float32 tokens/s + achieved GB/s or TFLOP/s vs peak",
+        "metric": f"GroupedMatMul {w.dtype} tokens/s + achieved GB/s or TFLOP/s vs peak",
         "value": round(w.M * args.steps / elapsed, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -384,11 +406,11 @@ def main_gmm(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": GMM_TYPES[w.dtype][2],
         "data": "synthetic (seeded numpy draws: input N(0,1), weights and bias N(0,1)*wscale, "
-                "Zipf or uniform distinct group indices)",
+                "rounded to the element type; Zipf or uniform distinct group indices)",
         "config": {"workload": w.name, "M": w.M, "K": w.K, "G": w.G, "N": w.N, "S": w.S, "bias": w.bias,
-                   "zipf": w.zipf},
+                   "zipf": w.zipf, "element_type": w.dtype},
         "gbs": round(work["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
         "tflops": round(work["flops"] / (ms_per_step * 1e-3) / 1e12, 2),
         "stage_ms": {k: round(v, 5) for k, v in stages.items()} if stages else None,

@@ -25,6 +25,8 @@
 // reads its 8 consecutive K values of a column as one 16-byte load; the
 // double kernel's 16x16x4 instruction takes one K value a lane and reads the
 // slice as stored.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.h"
 
@@ -246,6 +248,157 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, i
         if (r < rows) out[(long)s_orow[r] * N + n] = (ET)(acc[ms][ns][i] + bv);
       }
   }
+}
+
+// 16-bit element types on 16-row tiles (groups averaging at most 16 rows),
+// the weight streaming of gmm.hip's qmoe_gmm_f32_rows16 for [K, N] weights:
+// each wavefront owns 64 columns of one tile and streams that strip of W[g]
+// from HBM into matrix-core operands (no LDS, no barriers), 8 K groups of 16
+// rows in flight, every 16-bit value widened to fp32 (exactly) for
+// v_mfma_f32_16x16x4_f32: exact products, fp32 sums, bias added in fp32 and
+// the sum rounded once to the element type (the arithmetic of the tile
+// kernel above).  Lane (c, kq): columns n0 + 4c .. + 3, output rows 4kq ..
+// 4kq + 3, K values 4kq .. 4kq + 3 of each group.  KSPLIT > 1: the four
+// wavefronts take K ranges of the same 64 columns and add their sums through
+// LDS in wavefront order.  Needs K % 4 == 0, N % 4 == 0 and 8-byte aligned
+// input, weights, bias and output.
+template <typename ET>
+__device__ __forceinline__ float widen16(const u32x2& v, int j) {
+  const uint16_t h = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+  if constexpr (std::is_same<ET, _Float16>::value) return (float)__builtin_bit_cast(_Float16, h);
+  else return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+template <typename ET, int KSPLIT>
+__global__ void __launch_bounds__(256) qmoe_gmm16_rows16(const TypedGemm g, int nblk) {
+  constexpr int KG = 16, SD = 8;
+  const int tile = blockIdx.x / nblk;
+  if (tile >= g.ntiles[0]) return;
+  const int grp = g.tiles[4 * tile + 0];
+  const int p0 = g.tiles[4 * tile + 1];
+  const int rows = g.tiles[4 * tile + 2];
+  const int K = g.K, N = g.N;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int n0 = KSPLIT == 1 ? (blockIdx.x % nblk) * 256 + wave * 64 : (blockIdx.x % nblk) * 64;
+  if (n0 >= N) return;  // whole wavefront (whole workgroup when KSPLIT > 1): before any barrier
+  const int c = lane & 15, kq = lane >> 4;
+  int orow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) orow[t] = 4 * kq + t < rows ? g.perm[p0 + 4 * kq + t] : -1;
+  const bool cok = n0 + 4 * c < N;  // all four columns or none (N % 4 == 0)
+  ET* out = static_cast<ET*>(g.out);
+  if (grp >= g.G) {  // index outside [0, G): zero rows
+    if (KSPLIT > 1 && wave > 0) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (orow[t] >= 0 && cok) *(u32x2*)(out + (long)orow[t] * N + n0 + 4 * c) = u32x2{0u, 0u};
+    return;
+  }
+  const int nfull = K / KG;
+  const int g0 = KSPLIT == 1 ? 0 : (int)((long)nfull * wave / KSPLIT);
+  const int g1 = KSPLIT == 1 ? nfull : (int)((long)nfull * (wave + 1) / KSPLIT);
+  const bool tail = nfull * KG < K && (KSPLIT == 1 || wave == KSPLIT - 1);
+  const ET* arow = static_cast<const ET*>(g.a) + (long)(g.a_perm[p0 + min(c, rows - 1)] / g.a_div) * K + 4 * kq;
+  // this lane's columns at k row 4 kq (lanes past N re-read column 0)
+  const ET* wp = static_cast<const ET*>(g.w) + (long)grp * K * N + (cok ? n0 + 4 * c : 0) + (long)(4 * kq) * N;
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ra[d]: operand k KG kg + 4 kq .. + 3; rb[d][j]: columns n0 + 4c .. + 3 at
+  // k row KG kg + 4 kq + j (four 16-bit values each)
+  u32x2 ra[SD], rb[SD][4];
+  auto load = [&](int slot, int kg) {
+    const long k = (long)kg * KG;
+    ra[slot] = *(const u32x2*)(arow + k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rb[slot][j] = *(const u32x2*)(wp + (k + j) * N);
+  };
+  auto mma = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float av = widen16<ET>(ra[slot], j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, widen16<ET>(rb[slot][j], i), acc[i], 0, 0, 0);
+    }
+  };
+  // branch-free pipeline as in gmm.hip (past the range's last group the
+  // loads repeat it, unused)
+  if (g1 > g0) {
+    int kg = g0;
+#pragma unroll
+    for (int d = 0; d < SD; ++d) load(d, min(g0 + d, g1 - 1));
+    for (; kg + SD <= g1; kg += SD) {
+#pragma unroll
+      for (int d = 0; d < SD; ++d) {
+        mma(d);
+        load(d, min(kg + SD + d, g1 - 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < SD; ++d)
+      if (kg + d < g1) mma(d);
+  }
+  if (tail) {
+    // tail group: k past K reads as zero on both operands (K % 4 == 0, so a
+    // lane's four k are all in or all out)
+    const int kb = nfull * KG;
+    const bool ok = kb + 4 * kq < K;
+    ra[0] = ok ? *(const u32x2*)(arow + kb) : u32x2{0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rb[0][j] = ok ? *(const u32x2*)(wp + (long)(kb + j) * N) : u32x2{0u, 0u};
+    mma(0);
+  }
+  if (KSPLIT > 1) {
+    __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT - 1 : 1][4][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave - 1][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KSPLIT - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += red[w][i][lane];
+  }
+  if (!cok) return;
+  const int n = n0 + 4 * c;
+  float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (g.bias) {
+    const u32x2 b = *(const u32x2*)(static_cast<const ET*>(g.bias) + (long)grp * N + n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bv[i] = widen16<ET>(b, i);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (orow[t] < 0) continue;
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = __builtin_bit_cast(uint16_t, (ET)(acc[i][t] + bv[i]));
+    *(u32x2*)(out + (long)orow[t] * N + n) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  }
+}
+
+hipError_t launch_gmm16_rows16(int type, const TypedGemm& g, int ksplit, int max_tiles, hipStream_t st) {
+  if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  if (g.K % 4 != 0 || g.N % 4 != 0 || (ksplit != 1 && ksplit != 4)) return hipErrorInvalidValue;
+  const int cols = ksplit == 1 ? 256 : 64;  // columns per workgroup
+  const int nblk = (g.N + cols - 1) / cols;
+  const dim3 grid((unsigned)((long)max_tiles * nblk)), block(256);
+#define QMOE_R16(ET)                                                                                  \
+  do {                                                                                                \
+    if (ksplit == 1) hipLaunchKernelGGL((qmoe_gmm16_rows16<ET, 1>), grid, block, 0, st, g, nblk);     \
+    else hipLaunchKernelGGL((qmoe_gmm16_rows16<ET, 4>), grid, block, 0, st, g, nblk);                 \
+  } while (0)
+  switch (type) {
+    case GMM_F16: QMOE_R16(_Float16); break;
+    case GMM_BF16: QMOE_R16(__bf16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef QMOE_R16
+  return hipGetLastError();
 }
 
 hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tiles, hipStream_t st) {

@@ -188,6 +188,10 @@ struct TypedGemm {
   void* out;
 };
 hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tiles, hipStream_t st);
+// float16 / bfloat16 on 16-row tiles, weight streaming (gmm_typed.hip): K %
+// 4 == 0, N % 4 == 0, 8-byte aligned input, weights, bias and output; ksplit
+// 1 or 4 (K ranges of one workgroup's four wavefronts).
+hipError_t launch_gmm16_rows16(int type, const TypedGemm& g, int ksplit, int max_tiles, hipStream_t st);
 
 // Float MoE activation pass (see moe.hip): act[p][j], p < S, j < I, from
 // FC1 rows h (F floats) and FC3 rows u3 (I floats, or nullptr).  Codes

@@ -71,8 +71,9 @@ qmoe_status check(const qmoe_tensor* input, const qmoe_tensor* weights, const qm
   // LDS-tiled 64-row tiles.  With misaligned pointers the tiled kernel also
   // runs the 16-row tiles.
   const int64_t spread = std::max<int64_t>(1, std::min(p->G, p->R));
-  // (float32 only; the other types take the 64-row tiles of gmm_typed.hip)
-  p->rows16 = T == QMOE_F32 && p->K % 4 == 0 && p->N % 4 == 0 && p->R <= 16 * spread;
+  // (float32, float16 and bfloat16; double takes the 64-row tiles of
+  // gmm_typed.hip)
+  p->rows16 = T != QMOE_F64 && p->K % 4 == 0 && p->N % 4 == 0 && p->R <= 16 * spread;
   p->bm = p->rows16 ? gmm_rows16_tile_rows() : gmm_tile_rows();
   p->has_bias = bias != nullptr;
   p->max_tiles = (p->R + p->bm - 1) / p->bm + p->G + 1;
@@ -175,7 +176,14 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
     const bool tvec = (p.K * (int64_t)es) % 16 == 0 && (p.N * (int64_t)es) % 16 == 0 &&
                       aligned_to(input->data, 16) && aligned_to(weights->data, 16);
     const int ty = p.dtype == QMOE_F16 ? GMM_F16 : p.dtype == QMOE_BF16 ? GMM_BF16 : GMM_F64;
-    if (launch_gmm_typed(ty, tg, tvec, (int)p.max_tiles, s) != hipSuccess) return QMOE_ERR_HIP;
+    // 16-row tiles stream the weights when every pointer allows 8-byte loads
+    // (else the tile kernel takes them: its tiles hold up to 64 rows)
+    const bool stream16 = p.rows16 && aligned_to(input->data, 8) && aligned_to(weights->data, 8) &&
+                          aligned_to(output->data, 8) && (!bias || aligned_to(bias->data, 8));
+    const long est_tiles = std::max<int64_t>(1, std::min<int64_t>(p.G, p.R));  // groups in use, at most
+    const hipError_t e = stream16 ? launch_gmm16_rows16(ty, tg, gmm_rows16_ksplit(est_tiles, tg.N), (int)p.max_tiles, s)
+                                  : launch_gmm_typed(ty, tg, tvec, (int)p.max_tiles, s);
+    if (e != hipSuccess) return QMOE_ERR_HIP;
     if (mark(2) != hipSuccess) return QMOE_ERR_HIP;
     return QMOE_OK;
   }

@@ -179,6 +179,9 @@ class GmmWorkload:
     zipf: bool = False
     wscale: float = 0.01
     seed: int = 0
+    # element type of input, weights, bias and output (the page's Type
+    # Constraints): the float32 draws below rounded to it
+    dtype: str = "float32"
 
     def describe(self) -> dict:
         return asdict(self)
@@ -188,6 +191,12 @@ GMM_WORKLOADS = {
     "gmm_decode_fc1": GmmWorkload("gmm_decode_fc1", 16, 4096, 8, 28672, 2),
     "gmm_fine_fc1": GmmWorkload("gmm_fine_fc1", 2048, 2048, 64, 2816, 6, zipf=True),
 }
+# the same two shapes in the page's other element types
+for _dt, _sfx in (("float16", "f16"), ("bfloat16", "bf16"), ("float64", "f64")):
+    for _base in ("gmm_decode_fc1", "gmm_fine_fc1"):
+        _w = GMM_WORKLOADS[_base]
+        GMM_WORKLOADS[f"{_base}_{_sfx}"] = GmmWorkload(f"{_base}_{_sfx}", _w.M, _w.K, _w.G, _w.N, _w.S, zipf=_w.zipf,
+                                                        dtype=_dt)
 
 
 def gmm_generate(w: GmmWorkload, seed: Optional[int] = None, index_dtype=np.int64) -> dict:

@@ -39,6 +39,19 @@ def test_decode_algorithmic_bytes():
     assert fc1["flops"] == 2.0 * T * k * 2 * I * H
 
 
+def test_grouped_matmul_bytes_follow_the_element_type():
+    import numpy as np
+    w32 = W.GMM_WORKLOADS["gmm_decode_fc1"]
+    idx = np.arange(w32.M * w32.S).reshape(w32.M, w32.S) % 5  # 5 of the 8 groups used
+    b32 = bench.gmm_work(w32, idx)
+    for sfx, eb in (("f16", 2), ("bf16", 2), ("f64", 8)):
+        w = W.GMM_WORKLOADS[f"gmm_decode_fc1_{sfx}"]
+        b = bench.gmm_work(w, idx)
+        assert b["bytes"] * 4 == b32["bytes"] * eb and b["flops"] == b32["flops"]
+    used = int(np.unique(idx).size)
+    assert b32["weight_bytes"] == used * (w32.K * w32.N + w32.N) * 4
+
+
 def test_unused_experts_are_not_counted():
     w = W.WORKLOADS["decode"]
     counts = np.array([3, 0, 5, 0, 0, 8, 16, 0])
@@ -104,6 +117,11 @@ def test_kernel_choice_per_workload():
         assert "fc2_ranges=1 " in bench.plan_of(W.WORKLOADS[name]), name
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1"]) == "qmoe_gmm_f32_rows16"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_fine_fc1"]) == "qmoe_gmm_f32"
+    for sfx in ("f16", "bf16", "f64"):
+        assert bench.gmm_kernel(W.GMM_WORKLOADS[f"gmm_fine_fc1_{sfx}"]) == "qmoe_gmm_typed"
+    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f16"]) == "qmoe_gmm16_rows16"
+    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_bf16"]) == "qmoe_gmm16_rows16"
+    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f64"]) == "qmoe_gmm_typed"
 
 
 def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):

@@ -236,7 +236,7 @@ def test_degenerate_sizes(torch):
         assert got.shape == (M, S, N)
 
 
-@pytest.mark.parametrize("name", sorted(W.GMM_WORKLOADS))
+@pytest.mark.parametrize("name", sorted(n for n, w in W.GMM_WORKLOADS.items() if w.dtype == "float32"))
 def test_full_size_workloads_sampled(torch, name):
     w = W.GMM_WORKLOADS[name]
     a = W.gmm_generate(w)

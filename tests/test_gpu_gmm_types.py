@@ -12,6 +12,7 @@ the output type by half a unit in its last place (2^-11 or 2^-8 relative
 for normal results; 2^-25 absolute below the float16 normal range).
 Rows with an index outside [0, G) must be zero (the library's choice).
 """
+import functools
 import json
 import os
 
@@ -165,6 +166,25 @@ def test_invalid_indices_misaligned_and_empty(torch, dt):
     idx = rng.integers(0, G, size=(9, 2))
     got, _, _, fb = _run(torch, np.zeros((9, 0)), np.zeros((G, 0, N)), idx, b, dt, label="K0")
     np.testing.assert_array_equal(got, fb[idx])
+
+
+@functools.lru_cache(maxsize=1)
+def _decode_case():
+    # drawn once for the three types (940 M weights)
+    return W.gmm_generate(W.GMM_WORKLOADS["gmm_decode_fc1"])
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dt", TYPES)
+def test_decode_workload_sampled(torch, dt):
+    # the decode layer's FC1 as a GroupedMatMul (16 x 4096 -> 28672, 8 groups,
+    # 2 a row): the weight slices of every used group once, inputs rounded to
+    # the type
+    w = W.GMM_WORKLOADS["gmm_decode_fc1"]
+    a = _decode_case()
+    got, fx, fw, fb = _run(torch, a["input"], a["weights"], a["group_indices"], a["bias"], dt, label=w.name)
+    assert np.isfinite(got).all()
+    _check(dt, got, fx, fw, a["group_indices"], fb, rows=np.arange(w.M), label=w.name)
 
 
 @pytest.mark.timeout(600)
