@@ -250,6 +250,191 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, i
   }
 }
 
+// 16-bit element types on 64-row tiles with 16-byte aligned input and
+// weights and K, N multiples of 8: the tile kernel above with deeper K steps
+// (KS = 64: two matrix instructions a row subtile between barriers), loads
+// two steps ahead in registers, and the weight slice transposed in registers
+// instead of element by element in LDS: thread t loads rows 4kb .. 4kb + 3
+// (kb = t / 16) of columns 8cb .. 8cb + 7 (cb = t % 16) of the step's
+// [KS, 128] slice, regroups them into eight columns of four K values with
+// byte permutes, and writes each as one 8-byte LDS store (columns of K
+// contiguous, padded by 8 elements to spread the fragment reads over the
+// banks).  A rows are staged as 16-byte pieces.
+template <typename ET, int KS>
+__global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g, int nblk) {
+  using T = Ty<ET>;
+  static_assert(sizeof(ET) == 2 && KS % 64 == 0, "16-bit types, whole 64-K steps");
+  constexpr int AST = KS + 8;  // LDS elements per A row and per B column
+  constexpr int AP = KS / 32;  // 16-byte A pieces per thread and step
+  constexpr int BP = KS / 64;  // 4 x 8 B blocks per thread and step
+  __shared__ __attribute__((aligned(16))) ET sa[2][kYM * AST];
+  __shared__ __attribute__((aligned(16))) ET sb[2][kYN * AST];
+  __shared__ int s_arow[kYM];
+  __shared__ int s_orow[kYM];
+
+  // Tile order: each XCD (workgroups are dealt round robin by linear id)
+  // takes a contiguous run of work ids; work ids run over runs of GM row
+  // tiles (consecutive tiles mostly share a group, hence weight columns),
+  // column tile by column tile, row tile fastest.  Only the first linear ids
+  // carry work, so every XCD gets its share of the real tiles.
+  constexpr int GM = 8;
+  const int mt = g.ntiles[0];
+  const int total = mt * nblk;
+  const int lin = blockIdx.x;
+  if (lin >= total) return;
+  const int per = total >> 3, extra = total & 7, xcd = lin & 7;
+  const int wk = xcd * per + min(xcd, extra) + (lin >> 3);
+  const int r0 = (wk / (GM * nblk)) * GM;
+  const int gs = min(GM, mt - r0);
+  const int wr = wk - r0 * nblk;
+  const int tile = r0 + wr % gs;
+  const int n0 = (wr / gs) * kYN;
+  const int grp = g.tiles[4 * tile + 0];
+  const int p0 = g.tiles[4 * tile + 1];
+  const int rows = g.tiles[4 * tile + 2];
+  const int K = g.K, N = g.N;
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int col = lane & 15, kq = lane >> 4;
+  ET* out = static_cast<ET*>(g.out);
+
+  if (tid < kYM) {
+    const int p = p0 + min(tid, rows - 1);
+    s_arow[tid] = g.a_perm[p] / g.a_div;
+    s_orow[tid] = g.perm[p];
+  }
+  __syncthreads();
+
+  if (grp >= g.G) {  // index outside [0, G): zero rows
+    for (int idx = tid; idx < rows * kYN; idx += kYThreads) {
+      const int rr = idx / kYN, c = idx % kYN;
+      if (n0 + c < N) out[(long)s_orow[rr] * N + n0 + c] = (ET)0.f;
+    }
+    return;
+  }
+
+  const ET* x = static_cast<const ET*>(g.a);
+  const ET* wg = static_cast<const ET*>(g.w) + (long)grp * K * N;
+  const ET* arow = x + (long)s_arow[tid >> 2] * K;
+  const int cb = tid & 15;
+  const bool bcol = n0 + 8 * cb < N;  // all eight columns or none (N % 8 == 0)
+  const ET* bcolp = wg + min(n0 + 8 * cb, N - 8);
+  // B chunk swizzle: the 8-value K chunk c of column n sits at chunk
+  // c ^ ((n / 16) % 8), so one store instruction's 64 lanes (16 column
+  // blocks) spread over all banks; a fragment read's 16 columns share n / 16.
+  const int bsw = (cb >> 1) & 7;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  // Loads are unconditional (addresses clamped into the row and the matrix)
+  // so that the wait before a register set's LDS store counts only the loads
+  // issued after it; values outside K or N become zeros when stored.
+  auto load = [&](int kt, u32x4(&ra)[AP], u32x4(&rb)[BP][4]) {
+    const int k0 = kt * KS;
+#pragma unroll
+    for (int q = 0; q < AP; ++q) ra[q] = *(const u32x4*)(arow + min(k0 + 8 * ((tid & 3) + 4 * q), K - 8));
+#pragma unroll
+    for (int q = 0; q < BP; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        rb[q][r] = *(const u32x4*)(bcolp + (long)min(k0 + 4 * ((tid >> 4) + 16 * q) + r, K - 1) * N);
+  };
+  auto store = [&](int kt, int buf, const u32x4(&ra)[AP], const u32x4(&rb)[BP][4]) {
+    const int k0 = kt * KS;
+#pragma unroll
+    for (int q = 0; q < AP; ++q)
+      *(u32x4*)(sa[buf] + (tid >> 2) * AST + 8 * ((tid & 3) + 4 * q)) =
+          k0 + 8 * ((tid & 3) + 4 * q) < K ? ra[q] : z4;  // K % 8 == 0: a piece is all in or out
+#pragma unroll
+    for (int q = 0; q < BP; ++q) {
+      const int kb = (tid >> 4) + 16 * q;
+      u32x4 v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (bcol && k0 + 4 * kb + r < K) ? rb[q][r] : z4;
+      const int koff = 8 * ((kb >> 1) ^ bsw) + 4 * (kb & 1);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        // column 8cb + c: its values in rows 0..3 are the low (c even) or
+        // high (c odd) halves of dword c / 2
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(v[3][c >> 1], v[2][c >> 1], sel);
+        *(u32x2*)(sb[buf] + (8 * cb + c) * AST + koff) = u32x2{lo, hi};
+      }
+    }
+  };
+
+  typename T::Acc acc[2][4];
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = typename T::Acc{};
+  auto compute = [&](int buf) {
+    const ET* a = sa[buf];
+    const ET* b = sb[buf];
+#pragma unroll
+    for (int s = 0; s < KS / 32; ++s) {
+      // lane holds A[row col][k 32s + 8kq .. + 7] and B[k ..][column col]
+      typename T::Frag af[2], bf[4];
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms)
+        af[ms] = *(const typename T::Frag*)(a + (wm * 32 + ms * 16 + col) * AST + 32 * s + 8 * kq);
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        const int n = wn * 64 + ns * 16 + col;
+        bf[ns] = *(const typename T::Frag*)(b + n * AST + 8 * ((4 * s + kq) ^ ((n >> 4) & 7)));
+      }
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = T::mma(af[ms], bf[ns], acc[ms][ns]);
+    }
+  };
+
+  // Register sets 0 and 1 hold the steps of even and odd index, loaded two
+  // steps ahead of their use; the step count is rounded up to even (a step
+  // past K is all zeros).
+  const int nk = (K + KS - 1) / KS;
+  const int nk2 = (nk + 1) & ~1;
+  u32x4 ra0[AP], ra1[AP];
+  u32x4 rb0[BP][4], rb1[BP][4];
+  if (nk2 > 0) {
+    load(0, ra0, rb0);
+    load(1, ra1, rb1);
+    store(0, 0, ra0, rb0);
+    __syncthreads();
+    for (int kt = 0; kt < nk2; kt += 2) {
+      // the scheduling barriers keep each step's loads issued before its
+      // matrix instructions
+      load(kt + 2, ra0, rb0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0);
+      store(kt + 1, 1, ra1, rb1);
+      __syncthreads();
+      load(kt + 3, ra1, rb1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1);
+      store(kt + 2, 0, ra0, rb0);
+      __syncthreads();
+    }
+  }
+
+  // acc[ms][ns][i]: column wn*64 + ns*16 + col of row wm*32 + ms*16 + 4*kq + i
+  const ET* bias = static_cast<const ET*>(g.bias);
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    const int n = n0 + wn * 64 + ns * 16 + col;
+    if (n >= N) continue;
+    const float bv = bias ? (float)bias[(long)grp * N + n] : 0.f;
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 32 + ms * 16 + 4 * kq + i;
+        if (r < rows) out[(long)s_orow[r] * N + n] = (ET)(acc[ms][ns][i] + bv);
+      }
+  }
+}
+
 // 16-bit element types on 16-row tiles (groups averaging at most 16 rows),
 // the weight streaming of gmm.hip's qmoe_gmm_f32_rows16 for [K, N] weights:
 // each wavefront owns 64 columns of one tile and streams that strip of W[g]
@@ -410,9 +595,18 @@ hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tile
     if (vec) hipLaunchKernelGGL((qmoe_gmm_typed<ET, true>), grid, block, 0, st, g, nblk);   \
     else hipLaunchKernelGGL((qmoe_gmm_typed<ET, false>), grid, block, 0, st, g, nblk);      \
   } while (0)
+  // 16-bit types with whole 16-byte runs of 8 K values and 8 columns: the
+  // register-transposed kernel
+  const bool t16 = vec && g.K % 8 == 0 && g.N % 8 == 0;
   switch (type) {
-    case GMM_F16: QMOE_TYPED(_Float16); break;
-    case GMM_BF16: QMOE_TYPED(__bf16); break;
+    case GMM_F16:
+      if (t16) hipLaunchKernelGGL((qmoe_gmm16_tiled<_Float16, 64>), grid, block, 0, st, g, nblk);
+      else QMOE_TYPED(_Float16);
+      break;
+    case GMM_BF16:
+      if (t16) hipLaunchKernelGGL((qmoe_gmm16_tiled<__bf16, 64>), grid, block, 0, st, g, nblk);
+      else QMOE_TYPED(__bf16);
+      break;
     case GMM_F64: QMOE_TYPED(double); break;
     default: return hipErrorInvalidValue;
   }

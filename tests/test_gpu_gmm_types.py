@@ -127,6 +127,7 @@ def test_page_additional_types_example(torch, dt):
 SHAPES = [  # M, K, G, N, S: one tile, several tiles, ragged K / N / M tails
     (1, 1, 1, 1, 1), (5, 3, 2, 7, 2), (16, 256, 8, 512, 2), (64, 32, 1, 128, 1), (100, 64, 4, 200, 3),
     (257, 96, 3, 384, 1), (300, 130, 7, 257, 2), (129, 260, 5, 132, 4), (33, 1000, 9, 96, 3),
+    (200, 1000, 3, 136, 2),
 ]
 
 
