@@ -25,6 +25,8 @@
 // reads its 8 consecutive K values of a column as one 16-byte load; the
 // double kernel's 16x16x4 instruction takes one K value a lane and reads the
 // slice as stored.
+#include <cstdlib>
+#include <string>
 #include <type_traits>
 
 #include "common.hpp"
@@ -250,9 +252,10 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, i
   }
 }
 
-// 16-bit element types on 64-row tiles with 16-byte aligned input and
-// weights and K, N multiples of 8: the tile kernel above with deeper K steps
-// (KS = 64: two matrix instructions a row subtile between barriers), loads
+// 16-bit element types on MT-row tiles (64 or 128) with 16-byte aligned
+// input and weights and K, N multiples of 8: the tile kernel above with
+// deeper K steps (KS = 64: two matrix instructions a row subtile between
+// barriers, 2 x 2 wavefronts of MT / 2 rows x 64 columns), loads
 // two steps ahead in registers, and the weight slice transposed in registers
 // instead of element by element in LDS: thread t loads rows 4kb .. 4kb + 3
 // (kb = t / 16) of columns 8cb .. 8cb + 7 (cb = t % 16) of the step's
@@ -260,17 +263,19 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, i
 // byte permutes, and writes each as one 8-byte LDS store (columns of K
 // contiguous, padded by 8 elements to spread the fragment reads over the
 // banks).  A rows are staged as 16-byte pieces.
-template <typename ET, int KS>
+template <typename ET, int KS, int MT>
 __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g, int nblk) {
   using T = Ty<ET>;
-  static_assert(sizeof(ET) == 2 && KS % 64 == 0, "16-bit types, whole 64-K steps");
-  constexpr int AST = KS + 8;  // LDS elements per A row and per B column
-  constexpr int AP = KS / 32;  // 16-byte A pieces per thread and step
-  constexpr int BP = KS / 64;  // 4 x 8 B blocks per thread and step
-  __shared__ __attribute__((aligned(16))) ET sa[2][kYM * AST];
+  static_assert(sizeof(ET) == 2 && KS % 64 == 0 && (MT == 64 || MT == 128), "16-bit types, whole 64-K steps");
+  constexpr int AST = KS + 8;   // LDS elements per A row and per B column
+  constexpr int AH = MT / 64;   // 64-row halves of the A tile
+  constexpr int AP = KS / 32;   // 16-byte A pieces per thread, step and half
+  constexpr int BP = KS / 64;   // 4 x 8 B blocks per thread and step
+  constexpr int MS = MT / 32;   // 16-row subtiles per wavefront
+  __shared__ __attribute__((aligned(16))) ET sa[2][MT * AST];
   __shared__ __attribute__((aligned(16))) ET sb[2][kYN * AST];
-  __shared__ int s_arow[kYM];
-  __shared__ int s_orow[kYM];
+  __shared__ int s_arow[MT];
+  __shared__ int s_orow[MT];
 
   // Tile order: each XCD (workgroups are dealt round robin by linear id)
   // takes a contiguous run of work ids; work ids run over runs of GM row
@@ -299,7 +304,7 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g,
   const int col = lane & 15, kq = lane >> 4;
   ET* out = static_cast<ET*>(g.out);
 
-  if (tid < kYM) {
+  if (tid < MT) {
     const int p = p0 + min(tid, rows - 1);
     s_arow[tid] = g.a_perm[p] / g.a_div;
     s_orow[tid] = g.perm[p];
@@ -316,7 +321,9 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g,
 
   const ET* x = static_cast<const ET*>(g.a);
   const ET* wg = static_cast<const ET*>(g.w) + (long)grp * K * N;
-  const ET* arow = x + (long)s_arow[tid >> 2] * K;
+  const ET* arow[AH];
+#pragma unroll
+  for (int h = 0; h < AH; ++h) arow[h] = x + (long)s_arow[(tid >> 2) + 64 * h] * K;
   const int cb = tid & 15;
   const bool bcol = n0 + 8 * cb < N;  // all eight columns or none (N % 8 == 0)
   const ET* bcolp = wg + min(n0 + 8 * cb, N - 8);
@@ -328,22 +335,27 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g,
   // Loads are unconditional (addresses clamped into the row and the matrix)
   // so that the wait before a register set's LDS store counts only the loads
   // issued after it; values outside K or N become zeros when stored.
-  auto load = [&](int kt, u32x4(&ra)[AP], u32x4(&rb)[BP][4]) {
+  auto load = [&](int kt, u32x4(&ra)[AH * AP], u32x4(&rb)[BP][4]) {
     const int k0 = kt * KS;
 #pragma unroll
-    for (int q = 0; q < AP; ++q) ra[q] = *(const u32x4*)(arow + min(k0 + 8 * ((tid & 3) + 4 * q), K - 8));
+    for (int h = 0; h < AH; ++h)
+#pragma unroll
+      for (int q = 0; q < AP; ++q)
+        ra[h * AP + q] = *(const u32x4*)(arow[h] + min(k0 + 8 * ((tid & 3) + 4 * q), K - 8));
 #pragma unroll
     for (int q = 0; q < BP; ++q)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         rb[q][r] = *(const u32x4*)(bcolp + (long)min(k0 + 4 * ((tid >> 4) + 16 * q) + r, K - 1) * N);
   };
-  auto store = [&](int kt, int buf, const u32x4(&ra)[AP], const u32x4(&rb)[BP][4]) {
+  auto store = [&](int kt, int buf, const u32x4(&ra)[AH * AP], const u32x4(&rb)[BP][4]) {
     const int k0 = kt * KS;
 #pragma unroll
-    for (int q = 0; q < AP; ++q)
-      *(u32x4*)(sa[buf] + (tid >> 2) * AST + 8 * ((tid & 3) + 4 * q)) =
-          k0 + 8 * ((tid & 3) + 4 * q) < K ? ra[q] : z4;  // K % 8 == 0: a piece is all in or out
+    for (int h = 0; h < AH; ++h)
+#pragma unroll
+      for (int q = 0; q < AP; ++q)
+        *(u32x4*)(sa[buf] + ((tid >> 2) + 64 * h) * AST + 8 * ((tid & 3) + 4 * q)) =
+            k0 + 8 * ((tid & 3) + 4 * q) < K ? ra[h * AP + q] : z4;  // K % 8 == 0: a piece is all in or out
 #pragma unroll
     for (int q = 0; q < BP; ++q) {
       const int kb = (tid >> 4) + 16 * q;
@@ -363,9 +375,9 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g,
     }
   };
 
-  typename T::Acc acc[2][4];
+  typename T::Acc acc[MS][4];
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms)
+  for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = typename T::Acc{};
   auto compute = [&](int buf) {
@@ -374,17 +386,17 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g,
 #pragma unroll
     for (int s = 0; s < KS / 32; ++s) {
       // lane holds A[row col][k 32s + 8kq .. + 7] and B[k ..][column col]
-      typename T::Frag af[2], bf[4];
+      typename T::Frag af[MS], bf[4];
 #pragma unroll
-      for (int ms = 0; ms < 2; ++ms)
-        af[ms] = *(const typename T::Frag*)(a + (wm * 32 + ms * 16 + col) * AST + 32 * s + 8 * kq);
+      for (int ms = 0; ms < MS; ++ms)
+        af[ms] = *(const typename T::Frag*)(a + (wm * (MT / 2) + ms * 16 + col) * AST + 32 * s + 8 * kq);
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) {
         const int n = wn * 64 + ns * 16 + col;
         bf[ns] = *(const typename T::Frag*)(b + n * AST + 8 * ((4 * s + kq) ^ ((n >> 4) & 7)));
       }
 #pragma unroll
-      for (int ms = 0; ms < 2; ++ms)
+      for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = T::mma(af[ms], bf[ns], acc[ms][ns]);
     }
@@ -395,7 +407,7 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g,
   // past K is all zeros).
   const int nk = (K + KS - 1) / KS;
   const int nk2 = (nk + 1) & ~1;
-  u32x4 ra0[AP], ra1[AP];
+  u32x4 ra0[AH * AP], ra1[AH * AP];
   u32x4 rb0[BP][4], rb1[BP][4];
   if (nk2 > 0) {
     load(0, ra0, rb0);
@@ -418,7 +430,7 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g,
     }
   }
 
-  // acc[ms][ns][i]: column wn*64 + ns*16 + col of row wm*32 + ms*16 + 4*kq + i
+  // acc[ms][ns][i]: column wn*64 + ns*16 + col of row wm*MT/2 + ms*16 + 4*kq + i
   const ET* bias = static_cast<const ET*>(g.bias);
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns) {
@@ -426,10 +438,10 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g,
     if (n >= N) continue;
     const float bv = bias ? (float)bias[(long)grp * N + n] : 0.f;
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms)
+    for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = wm * 32 + ms * 16 + 4 * kq + i;
+        const int r = wm * (MT / 2) + ms * 16 + 4 * kq + i;
         if (r < rows) out[(long)s_orow[r] * N + n] = (ET)(acc[ms][ns][i] + bv);
       }
   }
@@ -586,7 +598,19 @@ hipError_t launch_gmm16_rows16(int type, const TypedGemm& g, int ksplit, int max
   return hipGetLastError();
 }
 
-hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tiles, hipStream_t st) {
+int gmm16_tile_rows(long R, long spread) {
+  // QMOE_GMM16_TILE_ROWS = 64 or 128 forces the choice (timing comparisons)
+  if (const char* v = std::getenv("QMOE_GMM16_TILE_ROWS")) {
+    const std::string s(v);
+    if (s == "64") return 64;
+    if (s == "128") return 128;
+  }
+  // groups averaging at least 128 rows: 128-row tiles read each weight
+  // column slice half as often
+  return R >= 128 * spread ? 128 : 64;
+}
+
+hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tiles, hipStream_t st, int tile_rows) {
   if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
   const int nblk = (g.N + kYN - 1) / kYN;
   const dim3 grid((unsigned)((long)max_tiles * nblk)), block(kYThreads);
@@ -597,20 +621,30 @@ hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tile
   } while (0)
   // 16-bit types with whole 16-byte runs of 8 K values and 8 columns: the
   // register-transposed kernel
+  // register-transposed kernel, on tiles of at most tile_rows rows (64, or
+  // 128 for that kernel alone)
   const bool t16 = vec && g.K % 8 == 0 && g.N % 8 == 0;
+  if (tile_rows > kYM && !(t16 && tile_rows == 128 && (type == GMM_F16 || type == GMM_BF16)))
+    return hipErrorInvalidValue;
+#define QMOE_T16(ET)                                                                                  \
+  do {                                                                                                \
+    if (tile_rows == 128) hipLaunchKernelGGL((qmoe_gmm16_tiled<ET, 64, 128>), grid, block, 0, st, g, nblk); \
+    else hipLaunchKernelGGL((qmoe_gmm16_tiled<ET, 64, 64>), grid, block, 0, st, g, nblk);            \
+  } while (0)
   switch (type) {
     case GMM_F16:
-      if (t16) hipLaunchKernelGGL((qmoe_gmm16_tiled<_Float16, 64>), grid, block, 0, st, g, nblk);
+      if (t16) QMOE_T16(_Float16);
       else QMOE_TYPED(_Float16);
       break;
     case GMM_BF16:
-      if (t16) hipLaunchKernelGGL((qmoe_gmm16_tiled<__bf16, 64>), grid, block, 0, st, g, nblk);
+      if (t16) QMOE_T16(__bf16);
       else QMOE_TYPED(__bf16);
       break;
     case GMM_F64: QMOE_TYPED(double); break;
     default: return hipErrorInvalidValue;
   }
 #undef QMOE_TYPED
+#undef QMOE_T16
   return hipGetLastError();
 }
 

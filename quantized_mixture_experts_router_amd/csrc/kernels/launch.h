@@ -187,7 +187,12 @@ struct TypedGemm {
   int K, N, G;          // tiles of group >= G write zero rows
   void* out;
 };
-hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tiles, hipStream_t st);
+// tile_rows: most rows a tile of the table holds, at most 64, or 128 for
+// float16 / bfloat16 with vec, K % 8 == 0 and N % 8 == 0 (gmm16_tile_rows()).
+hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tiles, hipStream_t st, int tile_rows = 64);
+// Rows per tile for the float16 / bfloat16 tile kernel on R rows over
+// `spread` groups.
+int gmm16_tile_rows(long R, long spread);
 // float16 / bfloat16 on 16-row tiles, weight streaming (gmm_typed.hip): K %
 // 4 == 0, N % 4 == 0, 8-byte aligned input, weights, bias and output; ksplit
 // 1 or 4 (K ranges of one workgroup's four wavefronts).

@@ -153,9 +153,25 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
     if (events && events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s);
     return hipSuccess;
   };
+  // float16 / bfloat16 on the register-transposed tile kernel (16-byte
+  // aligned input and weights, K and N multiples of 8, not the 16-row
+  // streaming kernel) may take 128-row tiles: fewer tiles than the
+  // workspace's table was sized for
+  const bool tvec = (p.K * (int64_t)es) % 16 == 0 && (p.N * (int64_t)es) % 16 == 0 &&
+                    aligned_to(input->data, 16) && aligned_to(weights->data, 16);
+  const bool tstream16 = p.dtype != QMOE_F32 && p.rows16 && aligned_to(input->data, 8) &&
+                        aligned_to(weights->data, 8) && aligned_to(output->data, 8) &&
+                        (!bias || aligned_to(bias->data, 8));
+  const int64_t spread = std::max<int64_t>(1, std::min<int64_t>(p.G, p.R));  // groups in use, at most
+  int bm = (int)p.bm;
+  int64_t max_tiles = p.max_tiles;
+  if ((p.dtype == QMOE_F16 || p.dtype == QMOE_BF16) && tvec && !tstream16) {
+    bm = gmm16_tile_rows((long)p.R, (long)spread);
+    max_tiles = (p.R + bm - 1) / bm + p.G + 1;
+  }
   if (mark(0) != hipSuccess) return QMOE_ERR_HIP;
   if (launch_gmm_index(group_indices->data, p.idx64, R, G, idx, s) != hipSuccess) return QMOE_ERR_HIP;
-  if (launch_permute(idx, R, G + 1, (int)kChunk, (int)p.nchunks, (int)p.bm, hist, counts, offsets, perm, tiles,
+  if (launch_permute(idx, R, G + 1, (int)kChunk, (int)p.nchunks, bm, hist, counts, offsets, perm, tiles,
                      ntiles, s) != hipSuccess)
     return QMOE_ERR_HIP;
   if (mark(1) != hipSuccess) return QMOE_ERR_HIP;
@@ -173,16 +189,11 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
     tg.N = (int)p.N;
     tg.G = G;
     tg.out = const_cast<void*>(output->data);
-    const bool tvec = (p.K * (int64_t)es) % 16 == 0 && (p.N * (int64_t)es) % 16 == 0 &&
-                      aligned_to(input->data, 16) && aligned_to(weights->data, 16);
     const int ty = p.dtype == QMOE_F16 ? GMM_F16 : p.dtype == QMOE_BF16 ? GMM_BF16 : GMM_F64;
     // 16-row tiles stream the weights when every pointer allows 8-byte loads
     // (else the tile kernel takes them: its tiles hold up to 64 rows)
-    const bool stream16 = p.rows16 && aligned_to(input->data, 8) && aligned_to(weights->data, 8) &&
-                          aligned_to(output->data, 8) && (!bias || aligned_to(bias->data, 8));
-    const long est_tiles = std::max<int64_t>(1, std::min<int64_t>(p.G, p.R));  // groups in use, at most
-    const hipError_t e = stream16 ? launch_gmm16_rows16(ty, tg, gmm_rows16_ksplit(est_tiles, tg.N), (int)p.max_tiles, s)
-                                  : launch_gmm_typed(ty, tg, tvec, (int)p.max_tiles, s);
+    const hipError_t e = tstream16 ? launch_gmm16_rows16(ty, tg, gmm_rows16_ksplit(spread, tg.N), (int)max_tiles, s)
+                                   : launch_gmm_typed(ty, tg, tvec, (int)max_tiles, s, bm);
     if (e != hipSuccess) return QMOE_ERR_HIP;
     if (mark(2) != hipSuccess) return QMOE_ERR_HIP;
     return QMOE_OK;

@@ -169,6 +169,25 @@ def test_invalid_indices_misaligned_and_empty(torch, dt):
     np.testing.assert_array_equal(got, fb[idx])
 
 
+@pytest.mark.parametrize("dt", ["float16", "bfloat16"])
+@pytest.mark.parametrize("tile_rows", ["64", "128"])
+def test_tile_rows_choices(torch, dt, tile_rows, monkeypatch):
+    # the 16-bit tile kernel on 64- and 128-row tiles (the library picks by
+    # rows per group; the variable forces either): ragged M, K and N tails,
+    # invalid indices, one group with most of the rows
+    monkeypatch.setenv("QMOE_GMM16_TILE_ROWS", tile_rows)
+    rng = np.random.default_rng(41)
+    for M, K, G, N, S in [(257, 96, 3, 384, 1), (300, 200, 5, 136, 2), (40, 520, 2, 264, 4)]:
+        x = rng.standard_normal((M, K))
+        w = rng.standard_normal((G, K, N)) * 0.1
+        b = rng.standard_normal((G, N))
+        idx = np.where(rng.random((M, S)) < 0.6, 0, rng.integers(0, G, size=(M, S))).astype(np.int64)
+        idx[rng.random((M, S)) < 0.1] = G + 2
+        label = f"rows{tile_rows}-{M}x{K}x{G}x{N}x{S}"
+        got, fx, fw, fb = _run(torch, x, w, idx, b, dt, label=label)
+        _check(dt, got, fx, fw, idx, fb, label=label)
+
+
 @functools.lru_cache(maxsize=1)
 def _decode_case():
     # drawn once for the three types (940 M weights)
