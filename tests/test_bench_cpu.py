@@ -117,8 +117,9 @@ def test_kernel_choice_per_workload():
         assert "fc2_ranges=1 " in bench.plan_of(W.WORKLOADS[name]), name
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1"]) == "qmoe_gmm_f32_rows16"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_fine_fc1"]) == "qmoe_gmm_f32"
-    for sfx in ("f16", "bf16", "f64"):
-        assert bench.gmm_kernel(W.GMM_WORKLOADS[f"gmm_fine_fc1_{sfx}"]) == "qmoe_gmm_typed"
+    for sfx in ("f16", "bf16"):
+        assert bench.gmm_kernel(W.GMM_WORKLOADS[f"gmm_fine_fc1_{sfx}"]) == "qmoe_gmm16_tiled"
+    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_fine_fc1_f64"]) == "qmoe_gmm_typed"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f16"]) == "qmoe_gmm16_rows16"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_bf16"]) == "qmoe_gmm16_rows16"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f64"]) == "qmoe_gmm_typed"
