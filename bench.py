@@ -193,19 +193,21 @@ KERNEL_SRC = {
     "qmoe_gmm_typed": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
     "qmoe_gmm16_rows16": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
     "qmoe_gmm16_tiled": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
+    "qmoe_gmm64_rows16": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
 }
 
 
 def gmm_kernel(w):
     """The library's GroupedMatMul kernel for this shape: the weight-streaming
-    one over 16-row tiles when the rows average at most 16 per group (and K, N
-    are multiples of 4; bench tensors are aligned) in float32, float16 and
-    bfloat16, else the LDS-tiled ones (double always; float16 and bfloat16
-    with K and N multiples of 8 on the register-transposed kernel)."""
+    ones over 16-row tiles when the rows average at most 16 per group (K a
+    multiple of 4, N of 4, or of 2 in double; bench tensors are aligned),
+    else the LDS-tiled ones (float16 and bfloat16 with K and N multiples of 8
+    on the register-transposed kernel)."""
     R = w.M * w.S
-    rows16 = w.K % 4 == 0 and w.N % 4 == 0 and R <= 16 * max(1, min(w.G, R))
+    few = R <= 16 * max(1, min(w.G, R))
+    rows16 = w.K % 4 == 0 and w.N % 4 == 0 and few
     if w.dtype == "float64":
-        return "qmoe_gmm_typed"
+        return "qmoe_gmm64_rows16" if w.K % 4 == 0 and w.N % 2 == 0 and few else "qmoe_gmm_typed"
     if w.dtype != "float32":
         if rows16:
             return "qmoe_gmm16_rows16"

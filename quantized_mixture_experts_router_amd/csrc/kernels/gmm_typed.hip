@@ -578,6 +578,138 @@ __global__ void __launch_bounds__(256) qmoe_gmm16_rows16(const TypedGemm g, int 
   }
 }
 
+// double on 16-row tiles (groups averaging at most 16 rows): the same weight
+// streaming with 16-byte loads (two adjacent columns of one K row a lane) on
+// v_mfma_f64_16x16x4_f64 (fp64 products and sums, bias added in fp64).  A
+// wavefront owns 32 columns: lane (c, kq) holds columns n0 + 2c and
+// n0 + 2c + 1 (accumulators 0 and 1, each the instruction's column c) and K
+// values 4kq .. 4kq + 3 of each 16-value group, one per instruction j (the
+// instruction's k index kq stands for k = 4kq + j); the fp64 result leaves
+// row kq + 4t of the tile in register t of lane 16kq + c.  4 K groups in
+// flight.  KSPLIT > 1: the four wavefronts take K ranges of the same 32
+// columns and add their sums through LDS in wavefront order.  Needs
+// K % 4 == 0, N % 2 == 0 and 16-byte aligned input, weights, bias and output.
+template <int KSPLIT>
+__global__ void __launch_bounds__(256) qmoe_gmm64_rows16(const TypedGemm g, int nblk) {
+  constexpr int KG = 16, SD = 4;
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  const int tile = blockIdx.x / nblk;
+  if (tile >= g.ntiles[0]) return;
+  const int grp = g.tiles[4 * tile + 0];
+  const int p0 = g.tiles[4 * tile + 1];
+  const int rows = g.tiles[4 * tile + 2];
+  const int K = g.K, N = g.N;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int n0 = KSPLIT == 1 ? (blockIdx.x % nblk) * 128 + wave * 32 : (blockIdx.x % nblk) * 32;
+  if (n0 >= N) return;  // whole wavefront (whole workgroup when KSPLIT > 1): before any barrier
+  const int c = lane & 15, kq = lane >> 4;
+  int orow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) orow[t] = kq + 4 * t < rows ? g.perm[p0 + kq + 4 * t] : -1;
+  const bool cok = n0 + 2 * c < N;  // both columns or none (N % 2 == 0)
+  double* out = static_cast<double*>(g.out);
+  if (grp >= g.G) {  // index outside [0, G): zero rows
+    if (KSPLIT > 1 && wave > 0) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (orow[t] >= 0 && cok) *(f64x2*)(out + (long)orow[t] * N + n0 + 2 * c) = f64x2{0.0, 0.0};
+    return;
+  }
+  const int nfull = K / KG;
+  const int g0 = KSPLIT == 1 ? 0 : (int)((long)nfull * wave / KSPLIT);
+  const int g1 = KSPLIT == 1 ? nfull : (int)((long)nfull * (wave + 1) / KSPLIT);
+  const bool tail = nfull * KG < K && (KSPLIT == 1 || wave == KSPLIT - 1);
+  const double* arow =
+      static_cast<const double*>(g.a) + (long)(g.a_perm[p0 + min(c, rows - 1)] / g.a_div) * K + 4 * kq;
+  // this lane's columns at k row 4 kq (lanes past N re-read column 0)
+  const double* wp =
+      static_cast<const double*>(g.w) + (long)grp * K * N + (cok ? n0 + 2 * c : 0) + (long)(4 * kq) * N;
+  f64x4 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // ra[d]: operand k KG kg + 4 kq .. + 3; rb[d][j]: columns n0 + 2c, + 1 at
+  // k row KG kg + 4 kq + j
+  f64x2 ra[SD][2], rb[SD][4];
+  auto load = [&](int slot, int kg) {
+    const long k = (long)kg * KG;
+    ra[slot][0] = *(const f64x2*)(arow + k);
+    ra[slot][1] = *(const f64x2*)(arow + k + 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rb[slot][j] = *(const f64x2*)(wp + (k + j) * N);
+  };
+  auto mma = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f64_16x16x4f64(ra[slot][j >> 1][j & 1], rb[slot][j][i], acc[i], 0, 0, 0);
+  };
+  // branch-free pipeline (past the range's last group the loads repeat it,
+  // unused)
+  if (g1 > g0) {
+    int kg = g0;
+#pragma unroll
+    for (int d = 0; d < SD; ++d) load(d, min(g0 + d, g1 - 1));
+    for (; kg + SD <= g1; kg += SD) {
+#pragma unroll
+      for (int d = 0; d < SD; ++d) {
+        mma(d);
+        load(d, min(kg + SD + d, g1 - 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < SD; ++d)
+      if (kg + d < g1) mma(d);
+  }
+  if (tail) {
+    // tail group: k past K reads as zero on both operands (K % 4 == 0, so a
+    // lane's four k are all in or all out)
+    const int kb = nfull * KG;
+    const bool ok = kb + 4 * kq < K;
+    const f64x2 z = {0.0, 0.0};
+    ra[0][0] = ok ? *(const f64x2*)(arow + kb) : z;
+    ra[0][1] = ok ? *(const f64x2*)(arow + kb + 2) : z;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rb[0][j] = ok ? *(const f64x2*)(wp + (long)(kb + j) * N) : z;
+    mma(0);
+  }
+  if (KSPLIT > 1) {
+    __shared__ f64x4 red[KSPLIT > 1 ? KSPLIT - 1 : 1][2][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) red[wave - 1][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KSPLIT - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i] += red[w][i][lane];
+  }
+  if (!cok) return;
+  const int n = n0 + 2 * c;
+  f64x2 bv = {0.0, 0.0};
+  if (g.bias) bv = *(const f64x2*)(static_cast<const double*>(g.bias) + (long)grp * N + n);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    if (orow[t] >= 0) *(f64x2*)(out + (long)orow[t] * N + n) = f64x2{acc[0][t] + bv[0], acc[1][t] + bv[1]};
+}
+
+hipError_t launch_gmm64_rows16(const TypedGemm& g, long est_tiles, int max_tiles, hipStream_t st) {
+  if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  if (g.K % 4 != 0 || g.N % 2 != 0) return hipErrorInvalidValue;
+  // one 32-column strip a wavefront; below about two thousand wavefronts
+  // (eight per compute unit) the K ranges are split four ways
+  const int ksplit = est_tiles * ((g.N + 31) / 32) < 2048 ? 4 : 1;
+  const int cols = ksplit == 1 ? 128 : 32;  // columns per workgroup
+  const int nblk = (g.N + cols - 1) / cols;
+  const dim3 grid((unsigned)((long)max_tiles * nblk)), block(256);
+  if (ksplit == 1) hipLaunchKernelGGL((qmoe_gmm64_rows16<1>), grid, block, 0, st, g, nblk);
+  else hipLaunchKernelGGL((qmoe_gmm64_rows16<4>), grid, block, 0, st, g, nblk);
+  return hipGetLastError();
+}
+
 hipError_t launch_gmm16_rows16(int type, const TypedGemm& g, int ksplit, int max_tiles, hipStream_t st) {
   if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
   if (g.K % 4 != 0 || g.N % 4 != 0 || (ksplit != 1 && ksplit != 4)) return hipErrorInvalidValue;

@@ -197,6 +197,10 @@ int gmm16_tile_rows(long R, long spread);
 // 4 == 0, N % 4 == 0, 8-byte aligned input, weights, bias and output; ksplit
 // 1 or 4 (K ranges of one workgroup's four wavefronts).
 hipError_t launch_gmm16_rows16(int type, const TypedGemm& g, int ksplit, int max_tiles, hipStream_t st);
+// double on 16-row tiles, weight streaming (gmm_typed.hip): K % 4 == 0,
+// N % 2 == 0, 16-byte aligned input, weights, bias and output; est_tiles:
+// the tiles to expect (groups in use) for the K-range choice.
+hipError_t launch_gmm64_rows16(const TypedGemm& g, long est_tiles, int max_tiles, hipStream_t st);
 
 // Float MoE activation pass (see moe.hip): act[p][j], p < S, j < I, from
 // FC1 rows h (F floats) and FC3 rows u3 (I floats, or nullptr).  Codes

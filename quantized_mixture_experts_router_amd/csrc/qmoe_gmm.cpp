@@ -71,9 +71,8 @@ qmoe_status check(const qmoe_tensor* input, const qmoe_tensor* weights, const qm
   // LDS-tiled 64-row tiles.  With misaligned pointers the tiled kernel also
   // runs the 16-row tiles.
   const int64_t spread = std::max<int64_t>(1, std::min(p->G, p->R));
-  // (float32, float16 and bfloat16; double takes the 64-row tiles of
-  // gmm_typed.hip)
-  p->rows16 = T != QMOE_F64 && p->K % 4 == 0 && p->N % 4 == 0 && p->R <= 16 * spread;
+  // (double streams two columns a lane: N even suffices)
+  p->rows16 = p->K % 4 == 0 && p->N % (T == QMOE_F64 ? 2 : 4) == 0 && p->R <= 16 * spread;
   p->bm = p->rows16 ? gmm_rows16_tile_rows() : gmm_tile_rows();
   p->has_bias = bias != nullptr;
   p->max_tiles = (p->R + p->bm - 1) / p->bm + p->G + 1;
@@ -159,9 +158,10 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
   // workspace's table was sized for
   const bool tvec = (p.K * (int64_t)es) % 16 == 0 && (p.N * (int64_t)es) % 16 == 0 &&
                     aligned_to(input->data, 16) && aligned_to(weights->data, 16);
-  const bool tstream16 = p.dtype != QMOE_F32 && p.rows16 && aligned_to(input->data, 8) &&
-                        aligned_to(weights->data, 8) && aligned_to(output->data, 8) &&
-                        (!bias || aligned_to(bias->data, 8));
+  const uintptr_t sal = p.dtype == QMOE_F64 ? 16 : 8;  // the streaming kernels' access width
+  const bool tstream16 = p.dtype != QMOE_F32 && p.rows16 && aligned_to(input->data, sal) &&
+                         aligned_to(weights->data, sal) && aligned_to(output->data, sal) &&
+                         (!bias || aligned_to(bias->data, sal));
   const int64_t spread = std::max<int64_t>(1, std::min<int64_t>(p.G, p.R));  // groups in use, at most
   int bm = (int)p.bm;
   int64_t max_tiles = p.max_tiles;
@@ -190,10 +190,13 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
     tg.G = G;
     tg.out = const_cast<void*>(output->data);
     const int ty = p.dtype == QMOE_F16 ? GMM_F16 : p.dtype == QMOE_BF16 ? GMM_BF16 : GMM_F64;
-    // 16-row tiles stream the weights when every pointer allows 8-byte loads
-    // (else the tile kernel takes them: its tiles hold up to 64 rows)
-    const hipError_t e = tstream16 ? launch_gmm16_rows16(ty, tg, gmm_rows16_ksplit(spread, tg.N), (int)max_tiles, s)
-                                   : launch_gmm_typed(ty, tg, tvec, (int)max_tiles, s, bm);
+    // 16-row tiles stream the weights when every pointer allows 8-byte
+    // (16-bit types) or 16-byte (double) accesses (else the tile kernel takes
+    // them: its tiles hold up to 64 rows)
+    hipError_t e;
+    if (!tstream16) e = launch_gmm_typed(ty, tg, tvec, (int)max_tiles, s, bm);
+    else if (p.dtype == QMOE_F64) e = launch_gmm64_rows16(tg, (long)spread, (int)max_tiles, s);
+    else e = launch_gmm16_rows16(ty, tg, gmm_rows16_ksplit(spread, tg.N), (int)max_tiles, s);
     if (e != hipSuccess) return QMOE_ERR_HIP;
     if (mark(2) != hipSuccess) return QMOE_ERR_HIP;
     return QMOE_OK;

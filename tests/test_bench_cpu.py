@@ -122,7 +122,7 @@ def test_kernel_choice_per_workload():
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_fine_fc1_f64"]) == "qmoe_gmm_typed"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f16"]) == "qmoe_gmm16_rows16"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_bf16"]) == "qmoe_gmm16_rows16"
-    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f64"]) == "qmoe_gmm_typed"
+    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f64"]) == "qmoe_gmm64_rows16"
 
 
 def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
