@@ -194,6 +194,7 @@ KERNEL_SRC = {
     "qmoe_gmm16_rows16": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
     "qmoe_gmm16_tiled": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
     "qmoe_gmm64_rows16": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
+    "qmoe_gmm16_stream": os.path.join(ROOT, "quantized_mixture_experts_router_amd", "csrc", "kernels", "gmm_typed.hip"),
 }
 
 
@@ -210,7 +211,7 @@ def gmm_kernel(w):
         return "qmoe_gmm64_rows16" if w.K % 4 == 0 and w.N % 2 == 0 and few else "qmoe_gmm_typed"
     if w.dtype != "float32":
         if rows16:
-            return "qmoe_gmm16_rows16"
+            return "qmoe_gmm16_stream" if w.K % 8 == 0 and w.N % 8 == 0 else "qmoe_gmm16_rows16"
         return "qmoe_gmm16_tiled" if w.K % 8 == 0 and w.N % 8 == 0 else "qmoe_gmm_typed"
     return "qmoe_gmm_f32_rows16" if rows16 else "qmoe_gmm_f32"
 

@@ -578,6 +578,160 @@ __global__ void __launch_bounds__(256) qmoe_gmm16_rows16(const TypedGemm g, int 
   }
 }
 
+// 16-bit element types on 16-row tiles, weight streaming on the 16-bit
+// matrix instruction (v_mfma_f32_16x16x32_f16 / _bf16: exact products, fp32
+// sums, the arithmetic of the tile kernels) for K and N multiples of 8 and
+// 16-byte aligned tensors.  Lane (c, kq) loads the 8 x 8 block of W[g] at K
+// rows 8kq .. 8kq + 7 of each 32-value group and columns n0 + 8c .. + 7 (one
+// 16-byte load a row) and transposes it in registers with byte permutes into
+// eight operands, one per column: instruction i takes column n0 + 8c + i as
+// its column c (accumulator i), so a wavefront covers 128 columns and each
+// lane ends with 8 consecutive columns of rows 4kq .. 4kq + 3, stored as
+// 16-byte rows.  The input rows are already 16-bit operands (lane (c, kq):
+// row c, K values 8kq .. 8kq + 7).  Two K groups in flight; KSPLIT > 1 as in
+// qmoe_gmm16_rows16.
+template <typename ET, int KSPLIT>
+__global__ void __launch_bounds__(256) qmoe_gmm16_stream(const TypedGemm g, int nblk) {
+  using T = Ty<ET>;
+  constexpr int KG = 32, SD = 2;
+  const int tile = blockIdx.x / nblk;
+  if (tile >= g.ntiles[0]) return;
+  const int grp = g.tiles[4 * tile + 0];
+  const int p0 = g.tiles[4 * tile + 1];
+  const int rows = g.tiles[4 * tile + 2];
+  const int K = g.K, N = g.N;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int n0 = KSPLIT == 1 ? (blockIdx.x % nblk) * 512 + wave * 128 : (blockIdx.x % nblk) * 128;
+  if (n0 >= N) return;  // whole wavefront (whole workgroup when KSPLIT > 1): before any barrier
+  const int c = lane & 15, kq = lane >> 4;
+  int orow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) orow[t] = 4 * kq + t < rows ? g.perm[p0 + 4 * kq + t] : -1;
+  const bool cok = n0 + 8 * c < N;  // all eight columns or none (N % 8 == 0)
+  ET* out = static_cast<ET*>(g.out);
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  if (grp >= g.G) {  // index outside [0, G): zero rows
+    if (KSPLIT > 1 && wave > 0) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (orow[t] >= 0 && cok) *(u32x4*)(out + (long)orow[t] * N + n0 + 8 * c) = z4;
+    return;
+  }
+  const int nfull = K / KG;
+  const int g0 = KSPLIT == 1 ? 0 : (int)((long)nfull * wave / KSPLIT);
+  const int g1 = KSPLIT == 1 ? nfull : (int)((long)nfull * (wave + 1) / KSPLIT);
+  const bool tail = nfull * KG < K && (KSPLIT == 1 || wave == KSPLIT - 1);
+  const ET* arow = static_cast<const ET*>(g.a) + (long)(g.a_perm[p0 + min(c, rows - 1)] / g.a_div) * K + 8 * kq;
+  // this lane's columns at k row 8 kq (lanes past N re-read column 0)
+  const ET* wp = static_cast<const ET*>(g.w) + (long)grp * K * N + (cok ? n0 + 8 * c : 0) + (long)(8 * kq) * N;
+  typename T::Acc acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = typename T::Acc{};
+  // ra[d]: row c, k KG kg + 8 kq .. + 7; rb[d][r]: columns n0 + 8c .. + 7 at
+  // k row KG kg + 8 kq + r
+  u32x4 ra[SD], rb[SD][8];
+  auto load = [&](int slot, int kg) {
+    const long k = (long)kg * KG;
+    ra[slot] = *(const u32x4*)(arow + k);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) rb[slot][r] = *(const u32x4*)(wp + (k + r) * N);
+  };
+  auto mma = [&](const u32x4& a, const u32x4 (&b)[8]) {
+    const typename T::Frag af = __builtin_bit_cast(typename T::Frag, a);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // column 8c + i: rows r are the low (i even) or high (i odd) halves of
+      // dword i / 2 of b[r]
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f[q] = __builtin_amdgcn_perm(b[2 * q + 1][i >> 1], b[2 * q][i >> 1], sel);
+      acc[i] = T::mma(af, __builtin_bit_cast(typename T::Frag, f), acc[i]);
+    }
+  };
+  // branch-free pipeline (past the range's last group the loads repeat it,
+  // unused)
+  if (g1 > g0) {
+    int kg = g0;
+#pragma unroll
+    for (int d = 0; d < SD; ++d) load(d, min(g0 + d, g1 - 1));
+    for (; kg + SD <= g1; kg += SD) {
+#pragma unroll
+      for (int d = 0; d < SD; ++d) {
+        mma(ra[d], rb[d]);
+        load(d, min(kg + SD + d, g1 - 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < SD; ++d)
+      if (kg + d < g1) mma(ra[d], rb[d]);
+  }
+  if (tail) {
+    // tail group: k past K reads as zero on both operands (K % 8 == 0, so a
+    // lane's eight k are all in or all out)
+    const int kb = nfull * KG;
+    const bool ok = kb + 8 * kq < K;
+    ra[0] = ok ? *(const u32x4*)(arow + kb) : z4;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) rb[0][r] = ok ? *(const u32x4*)(wp + (long)(kb + r) * N) : z4;
+    mma(ra[0], rb[0]);
+  }
+  if (KSPLIT > 1) {
+    __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT - 1 : 1][8][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wave - 1][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KSPLIT - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += red[w][i][lane];
+  }
+  if (!cok) return;
+  const int n = n0 + 8 * c;
+  float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (g.bias) {
+    const u32x4 b = *(const u32x4*)(static_cast<const ET*>(g.bias) + (long)grp * N + n);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bv[i] = widen16<ET>(u32x2{b[(i >> 2) * 2], b[(i >> 2) * 2 + 1]}, i & 3);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (orow[t] < 0) continue;
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = __builtin_bit_cast(uint16_t, (ET)(acc[i][t] + bv[i]));
+    *(u32x4*)(out + (long)orow[t] * N + n) =
+        u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  }
+}
+
+hipError_t launch_gmm16_stream(int type, const TypedGemm& g, long est_tiles, int max_tiles, hipStream_t st) {
+  if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  if (g.K % 8 != 0 || g.N % 8 != 0) return hipErrorInvalidValue;
+  // one 128-column strip a wavefront; below about two thousand wavefronts
+  // (eight per compute unit) the K ranges are split four ways
+  const int ksplit = est_tiles * ((g.N + 127) / 128) < 2048 ? 4 : 1;
+  const int cols = ksplit == 1 ? 512 : 128;  // columns per workgroup
+  const int nblk = (g.N + cols - 1) / cols;
+  const dim3 grid((unsigned)((long)max_tiles * nblk)), block(256);
+#define QMOE_S16(ET)                                                                                  \
+  do {                                                                                                \
+    if (ksplit == 1) hipLaunchKernelGGL((qmoe_gmm16_stream<ET, 1>), grid, block, 0, st, g, nblk);     \
+    else hipLaunchKernelGGL((qmoe_gmm16_stream<ET, 4>), grid, block, 0, st, g, nblk);                 \
+  } while (0)
+  switch (type) {
+    case GMM_F16: QMOE_S16(_Float16); break;
+    case GMM_BF16: QMOE_S16(__bf16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef QMOE_S16
+  return hipGetLastError();
+}
+
 // double on 16-row tiles (groups averaging at most 16 rows): the same weight
 // streaming with 16-byte loads (two adjacent columns of one K row a lane) on
 // v_mfma_f64_16x16x4_f64 (fp64 products and sums, bias added in fp64).  A

@@ -197,6 +197,10 @@ int gmm16_tile_rows(long R, long spread);
 // 4 == 0, N % 4 == 0, 8-byte aligned input, weights, bias and output; ksplit
 // 1 or 4 (K ranges of one workgroup's four wavefronts).
 hipError_t launch_gmm16_rows16(int type, const TypedGemm& g, int ksplit, int max_tiles, hipStream_t st);
+// float16 / bfloat16 on 16-row tiles, weight streaming on the 16-bit matrix
+// instruction (gmm_typed.hip): K % 8 == 0, N % 8 == 0, 16-byte aligned input,
+// weights, bias and output; est_tiles as below.
+hipError_t launch_gmm16_stream(int type, const TypedGemm& g, long est_tiles, int max_tiles, hipStream_t st);
 // double on 16-row tiles, weight streaming (gmm_typed.hip): K % 4 == 0,
 // N % 2 == 0, 16-byte aligned input, weights, bias and output; est_tiles:
 // the tiles to expect (groups in use) for the K-range choice.

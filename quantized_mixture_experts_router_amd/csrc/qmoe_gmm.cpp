@@ -196,6 +196,9 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
     hipError_t e;
     if (!tstream16) e = launch_gmm_typed(ty, tg, tvec, (int)max_tiles, s, bm);
     else if (p.dtype == QMOE_F64) e = launch_gmm64_rows16(tg, (long)spread, (int)max_tiles, s);
+    else if (p.K % 8 == 0 && p.N % 8 == 0 && aligned_to(input->data, 16) && aligned_to(weights->data, 16) &&
+             aligned_to(output->data, 16) && (!bias || aligned_to(bias->data, 16)))
+      e = launch_gmm16_stream(ty, tg, (long)spread, (int)max_tiles, s);  // 16-byte accesses
     else e = launch_gmm16_rows16(ty, tg, gmm_rows16_ksplit(spread, tg.N), (int)max_tiles, s);
     if (e != hipSuccess) return QMOE_ERR_HIP;
     if (mark(2) != hipSuccess) return QMOE_ERR_HIP;

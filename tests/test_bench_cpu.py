@@ -120,8 +120,8 @@ def test_kernel_choice_per_workload():
     for sfx in ("f16", "bf16"):
         assert bench.gmm_kernel(W.GMM_WORKLOADS[f"gmm_fine_fc1_{sfx}"]) == "qmoe_gmm16_tiled"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_fine_fc1_f64"]) == "qmoe_gmm_typed"
-    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f16"]) == "qmoe_gmm16_rows16"
-    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_bf16"]) == "qmoe_gmm16_rows16"
+    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f16"]) == "qmoe_gmm16_stream"
+    assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_bf16"]) == "qmoe_gmm16_stream"
     assert bench.gmm_kernel(W.GMM_WORKLOADS["gmm_decode_fc1_f64"]) == "qmoe_gmm64_rows16"
 
 

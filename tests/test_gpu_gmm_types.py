@@ -64,7 +64,7 @@ def _run(torch, x, w, idx, bias, dt, misalign=False, label=""):
         v = buf[off:].view(t.shape)
         v.copy_(t.cuda())
         return v
-    off = 1 if misalign else 0
+    off = int(misalign)  # elements: True = 1
     dx, dw, db = dev(tx, off), dev(tw, off), dev(tb)
     di = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
     M, S, N = x.shape[0], idx.shape[1], w.shape[2]
@@ -185,6 +185,27 @@ def test_tile_rows_choices(torch, dt, tile_rows, monkeypatch):
         idx[rng.random((M, S)) < 0.1] = G + 2
         label = f"rows{tile_rows}-{M}x{K}x{G}x{N}x{S}"
         got, fx, fw, fb = _run(torch, x, w, idx, b, dt, label=label)
+        _check(dt, got, fx, fw, idx, fb, label=label)
+
+
+@pytest.mark.parametrize("dt", TYPES)
+def test_streaming_variants(torch, dt):
+    # groups of at most 16 rows take the weight-streaming kernels: the 16-bit
+    # matrix-instruction one (K, N multiples of 8, 16-byte aligned), with and
+    # without K ranges, the widening one (K or N only multiples of 4, or
+    # 8-byte aligned), the double one (N even, 16-byte aligned); ragged K
+    # groups, invalid indices
+    rng = np.random.default_rng(43)
+    cases = [((24, 260, 6, 132, 2), 0), ((16, 64, 16, 16384, 2), 0), ((16, 264, 8, 256, 2), 4),
+             ((20, 1000, 4, 520, 3), 0), ((18, 72, 3, 136, 2), 0)]
+    for (M, K, G, N, S), off in cases:
+        x = rng.standard_normal((M, K))
+        w = rng.standard_normal((G, K, N)) * 0.1
+        b = rng.standard_normal((G, N))
+        idx = rng.integers(0, G, size=(M, S)).astype(np.int64)
+        idx[rng.random((M, S)) < 0.15] = -3
+        label = f"stream-{M}x{K}x{G}x{N}x{S}-off{off}"
+        got, fx, fw, fb = _run(torch, x, w, idx, b, dt, misalign=off, label=label)
         _check(dt, got, fx, fw, idx, fb, label=label)
 
 
