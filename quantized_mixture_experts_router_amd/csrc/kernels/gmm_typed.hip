@@ -137,8 +137,23 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, i
   const int ak = (tid & 3) * AQ;
   ET ra[AQ];
   ET rb[BR][EV];
+  // VEC: unconditional 16-byte loads (addresses clamped into the row and the
+  // matrix; K and N are whole runs of EV), the pieces past K or N zeroed at
+  // the LDS store, so that no load waits on a branch
+  u32x4 va[AQ / EV], vb[BR];
   auto load = [&](int kt) {
     const int k0 = kt * KS;
+    if constexpr (VEC) {
+#pragma unroll
+      for (int h = 0; h < AQ / EV; ++h) va[h] = *(const u32x4*)(arow + min(k0 + ak + h * EV, K - EV));
+#pragma unroll
+      for (int r = 0; r < BR; ++r) {
+        const int idx = tid + r * kYThreads;
+        const int k = idx / (kYN / EV), n = (idx % (kYN / EV)) * EV;
+        vb[r] = *(const u32x4*)(wg + (long)min(k0 + k, K - 1) * N + min(n0 + n, N - EV));
+      }
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < AQ / EV; ++h) {
       const int kk = k0 + ak + h * EV;
@@ -169,7 +184,27 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, i
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, int kt) {
+    if constexpr (VEC) {
+      const int k0 = kt * KS;
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int h = 0; h < AQ / EV; ++h) {
+        const u32x4 v = k0 + ak + h * EV < K ? va[h] : z4;
+        const ET* e = reinterpret_cast<const ET*>(&v);
+#pragma unroll
+        for (int i = 0; i < EV; ++i) ra[h * EV + i] = e[i];
+      }
+#pragma unroll
+      for (int r = 0; r < BR; ++r) {
+        const int idx = tid + r * kYThreads;
+        const int k = idx / (kYN / EV), n = (idx % (kYN / EV)) * EV;
+        const u32x4 v = (k0 + k < K && n0 + n < N) ? vb[r] : z4;
+        const ET* e = reinterpret_cast<const ET*>(&v);
+#pragma unroll
+        for (int i = 0; i < EV; ++i) rb[r][i] = e[i];
+      }
+    }
     ET* a = sa[buf] + (tid >> 2) * AST + ak;
 #pragma unroll
     for (int i = 0; i < AQ; ++i) a[i] = ra[i];
@@ -194,7 +229,7 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, i
   const int nk = (K + KS - 1) / KS;
   if (nk > 0) {
     load(0);
-    store(0);
+    store(0, 0);
   }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
@@ -228,7 +263,7 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, i
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = T::mma(af[ms], bf[ns], acc[ms][ns]);
     }
-    if (kt + 1 < nk) store(buf ^ 1);
+    if (kt + 1 < nk) store(buf ^ 1, kt + 1);
     __syncthreads();
   }
 
