@@ -96,10 +96,10 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm_typed(const TypedGemm g, i
 
   const int tile = blockIdx.x / nblk;
   if (tile >= g.ntiles[0]) return;
+  const int n0 = (blockIdx.x % nblk) * kYN;
   const int grp = g.tiles[4 * tile + 0];
   const int p0 = g.tiles[4 * tile + 1];
   const int rows = g.tiles[4 * tile + 2];
-  const int n0 = (blockIdx.x % nblk) * kYN;
   const int K = g.K, N = g.N;
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = tid >> 6;
@@ -747,9 +747,10 @@ __global__ void __launch_bounds__(256) qmoe_gmm16_stream(const TypedGemm g, int 
 hipError_t launch_gmm16_stream(int type, const TypedGemm& g, long est_tiles, int max_tiles, hipStream_t st) {
   if (max_tiles <= 0 || g.N <= 0) return hipSuccess;
   if (g.K % 8 != 0 || g.N % 8 != 0) return hipErrorInvalidValue;
-  // one 128-column strip a wavefront; below about two thousand wavefronts
-  // (eight per compute unit) the K ranges are split four ways
-  const int ksplit = est_tiles * ((g.N + 127) / 128) < 2048 ? 4 : 1;
+  // one 128-column strip a wavefront; below about a thousand wavefronts
+  // (four per compute unit) the K ranges are split four ways (at 1792, the
+  // decode-shaped workload, whole K ranges measured 5 % faster)
+  const int ksplit = est_tiles * ((g.N + 127) / 128) < 1024 ? 4 : 1;
   const int cols = ksplit == 1 ? 512 : 128;  // columns per workgroup
   const int nblk = (g.N + cols - 1) / cols;
   const dim3 grid((unsigned)((long)max_tiles * nblk)), block(256);
