@@ -104,8 +104,25 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const F32Gemm g, int n
   const int bn = NK ? tid >> 1 : (tid & 15) * 8;
   f32x4 ra;
   f32x4 rb[2];
+  // VEC: unconditional 16-byte loads (addresses clamped into the row and the
+  // matrix), the pieces past K or N zeroed at the LDS store, so that no load
+  // waits on a branch (per-lane conditional loads with a scalar fallback
+  // made each load wait on the one before)
   auto load = [&](int kt) {
     const int k0 = kt * kGK;
+    if constexpr (VEC) {
+      ra = *(const f32x4*)(arow + min(k0 + ak, K - 4));
+      if (NK) {
+        const float* brow = wg + (long)min(n0 + bn, N - 1) * K;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) rb[h] = *(const f32x4*)(brow + min(k0 + bk + 4 * h, K - 4));
+      } else {
+        const float* brow = wg + (long)min(k0 + bk, K - 1) * N;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) rb[h] = *(const f32x4*)(brow + min(n0 + bn + 4 * h, N - 4));
+      }
+      return;
+    }
     if (VEC && k0 + ak + 4 <= K) {
       ra = *(const f32x4*)(arow + k0 + ak);
     } else {
@@ -140,7 +157,17 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const F32Gemm g, int n
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, int kt) {
+    if constexpr (VEC) {
+      const int k0 = kt * kGK;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      if (k0 + ak >= K) ra = z;  // K % 4 == 0: a piece is all in or out
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool ok = NK ? (n0 + bn < N && k0 + bk + 4 * h < K) : (k0 + bk < K && n0 + bn + 4 * h < N);
+        if (!ok) rb[h] = z;
+      }
+    }
     float* a = sa[buf] + (tid >> 2) * kAStride + ak;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = ra[i];
@@ -180,7 +207,7 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const F32Gemm g, int n
     constexpr int MSN = MSR < 0 ? 2 : MSR;
     if (nk > 0) {
       load(0);
-      store(0);
+      store(0, 0);
     }
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
@@ -208,7 +235,7 @@ __global__ void __launch_bounds__(kGThreads) qmoe_gmm_f32(const F32Gemm g, int n
       }
       // the other buffer was last read in the previous step, finished by every
       // wavefront before the last barrier
-      if (kt + 1 < nk) store(buf ^ 1);
+      if (kt + 1 < nk) store(buf ^ 1, kt + 1);
       __syncthreads();
     }
   };
