@@ -465,20 +465,30 @@ __global__ void __launch_bounds__(kYThreads) qmoe_gmm16_tiled(const TypedGemm g,
     }
   }
 
-  // acc[ms][ns][i]: column wn*64 + ns*16 + col of row wm*MT/2 + ms*16 + 4*kq + i
+  // acc[ms][ns][i]: column wn*64 + ns*16 + col of row wm*MT/2 + ms*16 + 4*kq + i.
+  // The rounded tile goes through LDS (the A buffers, free after the last
+  // barrier of the K loop, or never used when K == 0) so that each output
+  // row leaves as 16-byte pieces of whole 256-byte runs.
+  constexpr int OST = kYN + 8;  // elements per staged row
+  static_assert(MT * OST <= 2 * MT * AST, "the staged tile fits the A buffers");
+  ET* so = &sa[0][0];
   const ET* bias = static_cast<const ET*>(g.bias);
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns) {
-    const int n = n0 + wn * 64 + ns * 16 + col;
-    if (n >= N) continue;
+    const int cn = wn * 64 + ns * 16 + col;
+    const int n = min(n0 + cn, N - 1);  // columns past N are staged, not stored
     const float bv = bias ? (float)bias[(long)grp * N + n] : 0.f;
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * (MT / 2) + ms * 16 + 4 * kq + i;
-        if (r < rows) out[(long)s_orow[r] * N + n] = (ET)(acc[ms][ns][i] + bv);
-      }
+      for (int i = 0; i < 4; ++i)
+        so[(wm * (MT / 2) + ms * 16 + 4 * kq + i) * OST + cn] = (ET)(acc[ms][ns][i] + bv);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < rows * (kYN / 8); idx += kYThreads) {
+    const int r = idx / (kYN / 8), c8 = 8 * (idx % (kYN / 8));
+    if (n0 + c8 < N)  // N % 8 == 0: all eight columns or none
+      *(u32x4*)(out + (long)s_orow[r] * N + n0 + c8) = *(const u32x4*)(so + r * OST + c8);
   }
 }
 
@@ -945,7 +955,7 @@ hipError_t launch_gmm_typed(int type, const TypedGemm& g, bool vec, int max_tile
   // register-transposed kernel
   // register-transposed kernel, on tiles of at most tile_rows rows (64, or
   // 128 for that kernel alone)
-  const bool t16 = vec && g.K % 8 == 0 && g.N % 8 == 0;
+  const bool t16 = vec && g.K % 8 == 0 && g.N % 8 == 0 && reinterpret_cast<uintptr_t>(g.out) % 16 == 0;
   if (tile_rows > kYM && !(t16 && tile_rows == 128 && (type == GMM_F16 || type == GMM_BF16)))
     return hipErrorInvalidValue;
 #define QMOE_T16(ET)                                                                                  \

@@ -153,8 +153,8 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
     return hipSuccess;
   };
   // float16 / bfloat16 on the register-transposed tile kernel (16-byte
-  // aligned input and weights, K and N multiples of 8, not the 16-row
-  // streaming kernel) may take 128-row tiles: fewer tiles than the
+  // aligned input, weights and output, K and N multiples of 8, not the
+  // 16-row streaming kernel) may take 128-row tiles: fewer tiles than the
   // workspace's table was sized for
   const bool tvec = (p.K * (int64_t)es) % 16 == 0 && (p.N * (int64_t)es) % 16 == 0 &&
                     aligned_to(input->data, 16) && aligned_to(weights->data, 16);
@@ -165,7 +165,7 @@ qmoe_status gmm_impl(const qmoe_tensor* input, const qmoe_tensor* weights, const
   const int64_t spread = std::max<int64_t>(1, std::min<int64_t>(p.G, p.R));  // groups in use, at most
   int bm = (int)p.bm;
   int64_t max_tiles = p.max_tiles;
-  if ((p.dtype == QMOE_F16 || p.dtype == QMOE_BF16) && tvec && !tstream16) {
+  if ((p.dtype == QMOE_F16 || p.dtype == QMOE_BF16) && tvec && aligned_to(output->data, 16) && !tstream16) {
     bm = gmm16_tile_rows((long)p.R, (long)spread);
     max_tiles = (p.R + bm - 1) / bm + p.G + 1;
   }
